@@ -1,0 +1,77 @@
+"""The oracle's pins must catch plausible mistakes.  Each case plants one
+mistake (a dropped term, a wrong sign, a swapped index, a wrong block size,
+...) into a private copy of the oracle source, builds it on the CPU, and runs
+the oracle pin suite against it in a subprocess; the suite has to fail."""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
+PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_route.py", "tests/test_oracle_layer.py"]
+
+MUTANTS = {
+    "up rows read from the gate half": ("orc_mat_row(w13, H, I + n, wrow);", "orc_mat_row(w13, H, n, wrow);"),
+    "silu dropped": ("h[n] = (g / (1.0 + exp(-g))) * u;", "h[n] = g * u;"),
+    "sigmoid sign flipped": ("s[e] = 1.0 / (1.0 + exp(-(double)logits_row[e]));",
+                             "s[e] = 1.0 / (1.0 + exp((double)logits_row[e]));"),
+    "bias leaks into weights": ("w[j] = (float)((scale * s[ids[j]]) / sum);",
+                                "w[j] = (float)((scale * key[ids[j]]) / sum);"),
+    "ties to the higher id": ("if (best < 0 || key[e] > key[best])", "if (best < 0 || key[e] >= key[best])"),
+    "routed scale dropped": ("w[j] = (float)((scale * s[ids[j]]) / sum);", "w[j] = (float)((s[ids[j]]) / sum);"),
+    "MX shared exponent off by one": ("shared = (e - 1) - 8;", "shared = (e - 1) - 7;"),
+    "nibble order swapped": ("int code = (k & 1) ? (byte >> 4) : (byte & 15);",
+                             "int code = (k & 1) ? (byte & 15) : (byte >> 4);"),
+    "NVFP4 block of 32": ("scale = T_E4M3[m->scales[(size_t)n * (K / 16) + k / 16]] * (double)m->gscale;",
+                          "scale = T_E4M3[m->scales[(size_t)n * (K / 16) + k / 32]] * (double)m->gscale;"),
+    "NVFP4 global dropped": ("scale = T_E4M3[m->scales[(size_t)n * (K / 16) + k / 16]] * (double)m->gscale;",
+                             "scale = T_E4M3[m->scales[(size_t)n * (K / 16) + k / 16]];"),
+    "E2M1 subnormal wrong": ("double mag = (e == 0) ? m * 0.5 : ldexp(1.0 + m * 0.5, e - 1);",
+                             "double mag = (e == 0) ? m * 1.0 : ldexp(1.0 + m * 0.5, e - 1);"),
+    "E4M3 bias 8": ("mag = ldexp(1.0 + m / 8.0, e - 7);", "mag = ldexp(1.0 + m / 8.0, e - 8);"),
+    "round toward zero": ("return rint(a / quantum) * quantum;", "return floor(a / quantum) * quantum;"),
+    "requant skipped before down": ("orc_down(w2, H, I, hd, y);", "orc_down(w2, H, I, h, y);"),
+    "bf16 shared intermediate not rounded": ("h[n] = orc_bf16_value(orc_bf16_rne(h[n]));", "h[n] = h[n];"),
+    "residual dropped": ("double t = orc_bf16_value(residual[c]) + (y_sh ? y_sh[c] : 0.0);",
+                         "double t = (y_sh ? y_sh[c] : 0.0);"),
+    "shared expert dropped": ("double t = orc_bf16_value(residual[c]) + (y_sh ? y_sh[c] : 0.0);",
+                              "double t = orc_bf16_value(residual[c]);"),
+    "RMS without the mean": ("double inv = 1.0 / sqrt(ss / H + eps);", "double inv = 1.0 / sqrt(ss + eps);"),
+    "norm on the unrounded sum": ("rr[c] = orc_bf16_value(rb);", "rr[c] = t;"),
+    "tiles of 7": ("tile_rows[t] = (n - 8 * i < 8) ? (n - 8 * i) : 8;", "tile_rows[t] = (n - 8 * i < 8) ? (n - 8 * i) : 7;"),
+    "bucket rows descending": ("        for (int r = 0; r < M; ++r)\n            for (int j = 0; j < k; ++j)\n                if (ids[(size_t)r * k + j] == e)",
+                               "        for (int r = M - 1; r >= 0; --r)\n            for (int j = 0; j < k; ++j)\n                if (ids[(size_t)r * k + j] == e)"),
+    "E4M3 not saturating": ("    if (r > 448.0)\n        r = 448.0;\n", ""),
+}
+
+
+def _run(name, old, new, tmp):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor for {name!r} not found"
+    mutated = src.replace(old, new, 1)
+    d = os.path.join(tmp, "m%d" % abs(hash(name)))
+    os.makedirs(d, exist_ok=True)
+    c = os.path.join(d, "moe_oracle.c")
+    open(c, "w").write(mutated)
+    for hdr in ("moe_oracle.h",):
+        open(os.path.join(d, hdr), "w").write(open(os.path.join(ROOT, "oracle", hdr)).read())
+    so = os.path.join(d, "liboracle.so")
+    subprocess.run(["gcc", "-O1", "-std=c11", "-D_GNU_SOURCE", "-shared", "-fPIC", "-o", so, c,
+                    "-lm", "-lpthread"], check=True)
+    env = dict(os.environ, MOE_ORACLE_LIB=so)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] + PINS,
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return name, r.returncode
+
+
+@pytest.mark.slow
+def test_every_planted_mistake_fails_a_pin():
+    with tempfile.TemporaryDirectory() as tmp:
+        with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 2)) as ex:
+            res = list(ex.map(lambda kv: _run(kv[0], kv[1][0], kv[1][1], tmp), MUTANTS.items()))
+    survivors = [n for n, rc in res if rc == 0]
+    assert not survivors, f"mistakes no pin caught: {survivors}"
