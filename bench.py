@@ -1,0 +1,270 @@
+"""Benchmark of the MoE layer step on one MI355X.
+
+Prints ONE JSON line on stdout:
+  metric/value/unit  — effective weight GB/s (unique selected experts' weight
+                       bytes / step time) at the measured workload, with
+                       ms_per_step beside it;
+  roofline           — the dominant kernel (routed gate_up) timed on its own
+                       with HIP events: algorithmic bytes per launch / mean
+                       duration, against the 8 TB/s HBM peak;
+  cpu_baseline       — the oracle (plain fp64 C) timed on the host cores on
+                       the same inputs (a baseline only).
+Inputs are seeded synthetic data already resident in HBM; each step reads a
+different copy of the weights (rotation over enough copies that no step
+finds the previous step's weights in the 256 MB Infinity Cache).
+
+Only --gpus 1 is supported: the layer runs on one GPU (one GPU's share of an
+expert-parallel / tensor-parallel layer at its real shape).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "verify-m8-h7168-e256-k8-nvfp4"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def expert_bytes(s, fmt, N, K):
+    """Packed weights + scales (+ fp32 global for NVFP4) of one [N, K] matrix."""
+    from block_scaled_fp4_sigmoid_amd import synth
+    if fmt == synth.BF16:
+        return 2 * N * K
+    if fmt == synth.MXFP4:
+        return N * K // 2 + N * K // 32
+    return N * K // 2 + N * K // 16 + 4
+
+
+def byte_model(s, U):
+    from block_scaled_fp4_sigmoid_amd import synth
+    per_expert = expert_bytes(s, s.wfmt, 2 * s.I, s.H) + expert_bytes(s, s.wfmt, s.H, s.I)
+    shared = 0
+    if s.sfmt != synth.NONE:
+        shared = expert_bytes(s, s.sfmt, 2 * s.I_sh, s.H) + expert_bytes(s, s.sfmt, s.H, s.I_sh)
+    router = 4 * s.E * s.H
+    acts = 8 * s.M * s.H  # x, residual in; out, residual_out
+    gate_up_launch = (U * expert_bytes(s, s.wfmt, 2 * s.I, s.H)
+                      + s.M * s.H * 33 // 32            # MXFP8 activations in
+                      + s.M * s.k * s.I * 33 // 32)     # MXFP8 h out
+    return dict(per_expert=per_expert, routed=U * per_expert, shared=shared, router=router,
+                acts=acts, total=U * per_expert + shared + router + acts,
+                gate_up_launch=gate_up_launch)
+
+
+def timed(fn, steps, warmup, stream):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms
+
+
+def cpu_baseline(inp, logits):
+    from oracle import oracle as orc
+    s = inp.shape
+    rows = np.arange(s.M)
+    need = set()
+    for r in rows:
+        ids, _, _ = orc.topk_row(logits[r], inp.bias, s.k, s.routed_scale)
+        need.update(int(e) for e in ids)
+    L = orc.Layer(inp, experts=need)
+    items = s.M * (s.k + (1 if s.sfmt else 0))
+    threads = min(orc.num_cores(), items)
+    L.rows(rows, logits=logits, nthreads=threads)  # warm
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        L.rows(rows, logits=logits, nthreads=threads)
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), threads
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-gate-up", type=int, default=0,
+                    help="only launch the routed gate_up kernel N times (for counter runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the layer is one "
+              "GPU's share of an expert/tensor-parallel MoE layer and this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_scaled_fp4_sigmoid_amd import moe, staging, synth
+
+    dev = "cuda"
+    name = args.workload
+    s = synth.WORKLOADS[name]
+    seed = args.seed if args.seed is not None else synth.WORKLOAD_ORDER.index(name) + 1
+    t0 = time.time()
+    inp = synth.make_inputs(name, seed=seed)
+    d = staging.to_device(inp, dev)
+    log(f"[bench] {name}: inputs drawn and staged in {time.time() - t0:.1f}s")
+
+    # routing of this input (deterministic), for U and the byte model
+    layer0 = d.layer()
+    out = torch.empty((s.M, s.H), dtype=torch.int16, device=dev)
+    res = torch.empty_like(out)
+    logits = torch.empty((s.M, s.E), dtype=torch.float32, device=dev)
+    ids = torch.empty((s.M, s.k), dtype=torch.int32, device=dev)
+    layer0(d.x, d.x, out, res, logits, ids)
+    torch.cuda.synchronize()
+    U = int(np.unique(ids.cpu().numpy()).size)
+    bm = byte_model(s, U)
+    copies = args.copies or max(1, math.ceil((1 << 30) / bm["total"]))
+    log(f"[bench] U={U} unique experts, routed bytes {bm['routed'] / 1e6:.1f} MB, "
+        f"total {bm['total'] / 1e6:.1f} MB, rotating {copies} weight copies")
+
+    layers = [layer0]
+    keep = []
+    for c in range(1, copies):
+        w13, w2 = staging.clone_weights(d.w13), staging.clone_weights(d.w2)
+        sh13, sh2 = staging.clone_weights(d.sh13), staging.clone_weights(d.sh2)
+        Wr = d.Wr.clone()
+        keep.append((w13, w2, sh13, sh2, Wr))
+        layers.append(moe.Layer(s.M, s.H, s.E, s.k, s.I, s.I_sh, s.routed_scale, s.eps, Wr, d.bias,
+                                w13, w2, sh13, sh2, d.gamma))
+    stream = torch.cuda.current_stream()
+
+    if args.profile_gate_up:
+        rt = moe.Routing(s.M, s.E, s.k, dev)
+        moe.route_topk(rt, x=d.x, w_router=d.Wr, bias=d.bias, routed_scale=s.routed_scale,
+                       logits_out=logits)
+        xq = torch.empty((s.M, s.H), dtype=torch.uint8, device=dev)
+        xs = torch.empty((s.M, s.H // 32), dtype=torch.uint8, device=dev)
+        moe.quant_act_mxfp8(d.x, xq, xs)
+        hq = torch.empty((s.M * s.k, s.I), dtype=torch.uint8, device=dev)
+        hs = torch.empty((s.M * s.k, s.I // 32), dtype=torch.uint8, device=dev)
+        for i in range(args.profile_gate_up):
+            w13 = d.w13 if i % copies == 0 else keep[i % copies - 1][0]
+            moe.expert_gate_up(w13, s.M, s.H, s.I, s.E, s.k, routing=rt, a_q=xq, a_s=xs, h_q=hq, h_s=hs)
+        torch.cuda.synchronize()
+        log(f"[bench] launched routed gate_up {args.profile_gate_up} times")
+        return
+
+    def step_eager(i):
+        layers[i % copies](d.x, d.x, out, res)
+
+    ms_eager = timed(step_eager, args.steps, args.warmup, stream)
+    log(f"[bench] eager: {ms_eager * 1e3:.2f} us/step")
+
+    ms_graph = None
+    if not args.no_graph:
+        graphs = []
+        gs = torch.cuda.Stream()
+        with torch.cuda.stream(gs):
+            for c in range(copies):
+                layers[c](d.x, d.x, out, res, stream=gs)
+            gs.synchronize()
+            for c in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=gs):
+                    layers[c](d.x, d.x, out, res, stream=gs)
+                graphs.append(g)
+        torch.cuda.synchronize()
+        ms_graph = timed(lambda i: graphs[i % copies].replay(), args.steps, args.warmup, stream)
+        log(f"[bench] graph replay: {ms_graph * 1e3:.2f} us/step")
+    ms = ms_graph if ms_graph is not None else ms_eager
+
+    # dominant kernel alone: routed gate_up, timed with HIP events on its stream
+    rt = moe.Routing(s.M, s.E, s.k, dev)
+    moe.route_topk(rt, x=d.x, w_router=d.Wr, bias=d.bias, routed_scale=s.routed_scale,
+                   logits_out=logits)
+    xq = torch.empty((s.M, s.H), dtype=torch.uint8, device=dev)
+    xs = torch.empty((s.M, s.H // 32), dtype=torch.uint8, device=dev)
+    moe.quant_act_mxfp8(d.x, xq, xs)
+    hq = torch.empty((s.M * s.k, s.I), dtype=torch.uint8, device=dev)
+    hs = torch.empty((s.M * s.k, s.I // 32), dtype=torch.uint8, device=dev)
+    w13s = [d.w13] + [k_[0] for k_ in keep]
+
+    def gate_up(i):
+        moe.expert_gate_up(w13s[i % copies], s.M, s.H, s.I, s.E, s.k, routing=rt, a_q=xq, a_s=xs,
+                           h_q=hq, h_s=hs)
+
+    ms_gu = timed(gate_up, args.steps, args.warmup, stream)
+    gu_gbps = bm["gate_up_launch"] / (ms_gu * 1e-3) / 1e9
+    log(f"[bench] routed gate_up alone: {ms_gu * 1e3:.2f} us, {gu_gbps:.0f} GB/s")
+
+    # plain device copy for the achievable stream rate (context)
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    buf2 = torch.empty_like(buf)
+    ms_copy = timed(lambda i: buf2.copy_(buf), 20, 3, stream)
+    copy_gbps = 2 * buf.numel() / (ms_copy * 1e-3) / 1e9
+    del buf, buf2
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        lg = logits.cpu().numpy()
+        t_cpu, threads = cpu_baseline(inp, lg)
+        cpu = {"value": round(bm["routed"] / t_cpu / 1e9, 4), "unit": "GB/s",
+               "us_per_step": round(t_cpu * 1e6, 1), "cores": threads, "kind": "oracle",
+               "sample": f"the whole {s.M}-row step (all rows, all {U} routed experts + shared), "
+                         "1 warm run then the median of 3"}
+        log(f"[bench] oracle on host: {t_cpu * 1e3:.1f} ms/step with {threads} threads")
+
+    value = bm["routed"] / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "MoE layer effective weight GB/s (unique selected experts' weight bytes / step time) "
+                  "at 1-384 rows, with us/step",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1e3, 2),
+        "us_per_step_eager": round(ms_eager * 1e3, 2),
+        "us_per_step_graph": None if ms_graph is None else round(ms_graph * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4xfp8->fp32",
+        "data": "synthetic (seeded; weights drawn N(0,0.02) and encoded offline)",
+        "config": {"workload": name, "rows": s.M, "hidden": s.H, "experts": s.E, "top_k": s.k,
+                   "intermediate": s.I, "weights": synth.FMT_NAMES[s.wfmt],
+                   "shared": synth.FMT_NAMES[s.sfmt], "unique_experts": U,
+                   "weight_copies": copies, "parallelism": "single GPU"},
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "total_alg_GBps": round(bm["total"] / (ms * 1e-3) / 1e9, 2),
+        "copy_GBps": round(copy_gbps, 1),
+        "roofline": {"kernel": "k_gate_up_fp4 (routed)", "bound": "hbm",
+                     "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "us_per_launch": round(ms_gu * 1e3, 2),
+                     "alg_bytes_per_launch": bm["gate_up_launch"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

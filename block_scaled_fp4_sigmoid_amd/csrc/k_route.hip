@@ -1,0 +1,355 @@
+// k_route.hip — router GEMV, sigmoid top-k with renormalized weights, and the
+// route step that groups each expert's rows into 8-row tiles (gfx950).
+//
+// Pages: sgl-nvidia-mega PR #24, "Modifications / Target spec" (one expert
+// group, sigmoid scores, renormalized top-k); SGLang-NVIDIA-Mega README,
+// DeepSeek-V4.1 slot table, rows "Router top-k" (one CTA per row) and "Routed
+// experts (moe)" (8-row tiles; an expert with more than 8 rows takes several).
+#include "moe_device.h"
+#include "moe_internal.h"
+
+#include <algorithm>
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Router GEMV on the matrix cores.  x is bf16 and w_router fp32; w is split
+// exactly into three bf16 pieces (w = w1 + w2 + w3: truncation keeps the top 8
+// significant bits, the remainder is exact in fp32 and splits again), so every
+// product x*wi is exact and the bf16 MFMA's fp32 accumulation gives the fp32
+// dot product.  Units (one wave each) are (16-expert tile, K chunk, 64-row
+// group); each writes partial logits for its K chunk, which the top-k step
+// sums in chunk order (deterministic, no atomics).
+
+RouterPlan router_plan(int M, int H, int E) {
+    const int et = (E + 15) / 16;
+    const int rg = (M + 63) / 64;
+    const int nsteps = H / 32;
+    const int want = std::max(1, 1024 / (et * rg));
+    int splits = 1;
+    for (int d = 1; d <= nsteps; ++d)
+        if (nsteps % d == 0 && d <= want) splits = d;
+    return RouterPlan{splits, H / splits, rg};
+}
+
+__device__ __forceinline__ void split3(float w, uint32_t& b1, uint32_t& b2, uint32_t& b3) {
+    const uint32_t u = __float_as_uint(w);
+    const float w1 = __uint_as_float(u & 0xffff0000u);
+    const float r = w - w1;
+    const uint32_t ur = __float_as_uint(r);
+    const float w2 = __uint_as_float(ur & 0xffff0000u);
+    const float w3 = r - w2;
+    b1 = u >> 16;
+    b2 = ur >> 16;
+    b3 = __float_as_uint(w3) >> 16;
+}
+
+__global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restrict__ x,
+                                                         const float* __restrict__ w_router,
+                                                         int M, int H, int E, int splits,
+                                                         int kchunk, int units,
+                                                         float* __restrict__ partials,
+                                                         int* __restrict__ counters, int ncounters) {
+    if (blockIdx.x == 0)
+        for (int c = threadIdx.x; c < ncounters; c += blockDim.x) counters[c] = 0;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int unit = blockIdx.x * 4 + wave;
+    if (unit >= units) return;
+    const int et = (E + 15) / 16;
+    const int te = unit % et;
+    const int kc = (unit / et) % splits;
+    const int rgi = unit / (et * splits);
+    const int i = lane & 15, g = lane >> 4;
+    const int e = te * 16 + i;
+    const bool ev = e < E;
+    const float* wrow = w_router + (size_t)(ev ? e : 0) * H;
+    const int r0 = rgi * 64;
+    const int nb = min(4, (M - r0 + 15) / 16);
+    const uint16_t* xr[4];
+    bool xv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = r0 + j * 16 + i;
+        xv[j] = (j < nb) && (r < M);
+        xr[j] = x + (size_t)(xv[j] ? r : 0) * H;
+    }
+    v4f acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int kbeg = kc * kchunk;
+    for (int k0 = kbeg; k0 < kbeg + kchunk; k0 += 32) {
+        const int kk = k0 + 8 * g;
+        float wv[8];
+        if (ev) {
+            const float4 w0 = *reinterpret_cast<const float4*>(wrow + kk);
+            const float4 w1 = *reinterpret_cast<const float4*>(wrow + kk + 4);
+            wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
+            wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) wv[t] = 0.f;
+        }
+        uint32_t p1[4], p2[4], p3[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            uint32_t a1, a2, a3, c1, c2, c3;
+            split3(wv[2 * t], a1, a2, a3);
+            split3(wv[2 * t + 1], c1, c2, c3);
+            p1[t] = a1 | (c1 << 16);
+            p2[t] = a2 | (c2 << 16);
+            p3[t] = a3 | (c3 << 16);
+        }
+        v4i A1 = {(int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
+        v4i A2 = {(int)p2[0], (int)p2[1], (int)p2[2], (int)p2[3]};
+        v4i A3 = {(int)p3[0], (int)p3[1], (int)p3[2], (int)p3[3]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j < nb) {
+                v4i B = xv[j] ? load16(xr[j] + kk) : v4i{0, 0, 0, 0};
+                const v8bf b = __builtin_bit_cast(v8bf, B);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, A1), b, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, A2), b, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, A3), b, acc[j], 0, 0, 0);
+            }
+        }
+    }
+    // lane holds D[4g + t][i]: expert te*16 + 4g + t, row r0 + 16j + i
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = r0 + j * 16 + i;
+        if (j < nb && r < M) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int ee = te * 16 + 4 * g + t;
+                if (ee < E) partials[((size_t)kc * M + r) * E + ee] = acc[j][t];
+            }
+        }
+    }
+}
+
+hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int M, int H, int E,
+                                  const RouterPlan& plan, float* partials, int* counters,
+                                  int ncounters, hipStream_t stream) {
+    const int units = ((E + 15) / 16) * plan.splits * plan.row_groups;
+    const int blocks = (units + 3) / 4;
+    hipLaunchKernelGGL(k_router_partials, dim3(blocks), dim3(256), 0, stream, x, w_router, M, H, E,
+                       plan.splits, plan.kchunk, units, partials, counters, ncounters);
+    return hipGetLastError();
+}
+
+__global__ void k_zero_ints(int* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+hipError_t launch_zero_ints(int* p, int n, hipStream_t stream) {
+    hipLaunchKernelGGL(k_zero_ints, dim3(1), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Top-k: one wave per row (the pages' one CTA per row).  Each lane holds up to
+// 16 experts (e = lane + 64 t).  Scores are fp64 sigmoids of the fp32 logits;
+// keys add the optional selection bias; k rounds of a wave-wide arg-max with
+// (key descending, expert ascending) order pick the slots.  The last
+// workgroup to finish then builds the expert buckets and 8-row tiles.
+
+__device__ __forceinline__ bool key_better(double ka, int ea, double kb, int eb) {
+    return ka > kb || (ka == kb && ea < eb);
+}
+
+constexpr int kMaxE = 1024;
+constexpr int kBucketThreads = 256;
+
+// Exclusive scan over kMaxE entries held 4 per thread (256 threads).
+__device__ void block_exclusive_scan(int* data, int* scratch, int& total) {
+    const int tid = threadIdx.x;
+    int v0 = data[4 * tid], v1 = data[4 * tid + 1], v2 = data[4 * tid + 2], v3 = data[4 * tid + 3];
+    int sum = v0 + v1 + v2 + v3;
+    scratch[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < kBucketThreads; off <<= 1) {
+        int add = tid >= off ? scratch[tid - off] : 0;
+        __syncthreads();
+        scratch[tid] += add;
+        __syncthreads();
+    }
+    const int incl = scratch[tid];
+    total = scratch[kBucketThreads - 1];
+    int base = incl - sum;
+    data[4 * tid] = base;
+    data[4 * tid + 1] = base + v0;
+    data[4 * tid + 2] = base + v0 + v1;
+    data[4 * tid + 3] = base + v0 + v1 + v2;
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void k_topk_bucket(const float* __restrict__ partials, int splits,
+                                                     const float* __restrict__ bias, int M, int E,
+                                                     int k, float routed_scale,
+                                                     float* __restrict__ logits_out,
+                                                     moe_routing route, int* __restrict__ counter) {
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + wave;
+    if (r < M) {
+        double key[16], sc[16];
+        uint32_t avail = 0;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int e = lane + 64 * t;
+            key[t] = 0.0;
+            sc[t] = 0.0;
+            if (e < E) {
+                float lg = partials[(size_t)r * E + e];
+                for (int c = 1; c < splits; ++c) lg += partials[((size_t)c * M + r) * E + e];
+                if (logits_out) logits_out[(size_t)r * E + e] = lg;
+                const double s = 1.0 / (1.0 + exp(-(double)lg));
+                sc[t] = s;
+                key[t] = s + (bias ? (double)bias[e] : 0.0);
+                avail |= 1u << t;
+            }
+        }
+        int my_id = 0;
+        double my_s = 0.0;
+        for (int j = 0; j < k; ++j) {
+            bool have = false;
+            double bk = 0.0;
+            int be = 0x7fffffff;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                if ((avail >> t) & 1u) {
+                    const int e = lane + 64 * t;
+                    if (!have || key_better(key[t], e, bk, be)) {
+                        have = true;
+                        bk = key[t];
+                        be = e;
+                    }
+                }
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const double ok = __shfl_xor(bk, off, 64);
+                const int oe = __shfl_xor(be, off, 64);
+                const int oh = __shfl_xor((int)have, off, 64);
+                if (oh && (!have || key_better(ok, oe, bk, be))) {
+                    have = true;
+                    bk = ok;
+                    be = oe;
+                }
+            }
+            double s_sel = 0.0;
+            if ((be & 63) == lane) {
+                const int tt = be >> 6;
+#pragma unroll
+                for (int t = 0; t < 16; ++t)
+                    if (t == tt) s_sel = sc[t];
+                avail &= ~(1u << tt);
+            }
+            const double sj = __shfl(s_sel, be & 63, 64);
+            if (lane == j) {
+                my_id = be;
+                my_s = sj;
+            }
+        }
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j) sum += __shfl(my_s, j, 64);
+        if (lane < k) {
+            route.topk_ids[(size_t)r * k + lane] = my_id;
+            route.topk_w[(size_t)r * k + lane] = (float)(((double)routed_scale * my_s) / sum);
+        }
+    }
+
+    // ---- last workgroup: buckets and tiles ----
+    __shared__ int s_last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = (atomicAdd(counter, 1) == (int)gridDim.x - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+
+    __shared__ int s_cnt[kMaxE], s_off[kMaxE], s_tile[kMaxE], s_act[kMaxE], s_run[kMaxE];
+    __shared__ uint32_t s_bm[kMaxE * 4];
+    __shared__ int s_scan[kBucketThreads];
+    const int tid = threadIdx.x;
+    const int P = M * k;
+    for (int e = tid; e < kMaxE; e += kBucketThreads) {
+        s_cnt[e] = 0;
+        s_run[e] = 0;
+    }
+    __syncthreads();
+    for (int p = tid; p < P; p += kBucketThreads) atomicAdd(&s_cnt[load_agent(route.topk_ids + p)], 1);
+    __syncthreads();
+    for (int e = tid; e < kMaxE; e += kBucketThreads) {
+        const int c = s_cnt[e];
+        s_off[e] = c;
+        s_tile[e] = (c + 7) / 8;
+        s_act[e] = c > 0 ? 1 : 0;
+    }
+    __syncthreads();
+    int tot_pairs, tot_tiles, tot_act;
+    block_exclusive_scan(s_off, s_scan, tot_pairs);
+    block_exclusive_scan(s_tile, s_scan, tot_tiles);
+    block_exclusive_scan(s_act, s_scan, tot_act);
+    for (int e = tid; e < E; e += kBucketThreads) {
+        const int c = s_cnt[e];
+        route.expert_offsets[e] = s_off[e];
+        if (c > 0) route.active_experts[s_act[e]] = e;
+        for (int t = 0; 8 * t < c; ++t) {
+            const int ti = s_tile[e] + t;
+            route.tile_expert[ti] = e;
+            route.tile_begin[ti] = s_off[e] + 8 * t;
+            route.tile_rows[ti] = min(8, c - 8 * t);
+        }
+    }
+    if (tid == 0) {
+        route.expert_offsets[E] = P;
+        *route.num_tiles = tot_tiles;
+        *route.num_active = tot_act;
+    }
+    // Stable placement: chunks of R rows; a bitmap per expert marks the chunk's
+    // rows that chose it, and a pair's rank within its expert is the number of
+    // earlier rows (previous chunks + lower bits of this chunk's bitmap).
+    const int R = min(128, kBucketThreads / k);
+    const int W = (R + 31) / 32;
+    for (int r0 = 0; r0 < M; r0 += R) {
+        for (int w = tid; w < E * W; w += kBucketThreads) s_bm[w] = 0u;
+        __syncthreads();
+        const int p = r0 * k + tid;
+        const bool valid = tid < R * k && p < P;
+        int e = 0, rl = 0;
+        if (valid) {
+            e = load_agent(route.topk_ids + p);
+            rl = p / k - r0;
+            atomicOr(&s_bm[e * W + (rl >> 5)], 1u << (rl & 31));
+        }
+        __syncthreads();
+        if (valid) {
+            int rank = 0;
+            for (int w = 0; w < (rl >> 5); ++w) rank += __popc(s_bm[e * W + w]);
+            rank += __popc(s_bm[e * W + (rl >> 5)] & ((1u << (rl & 31)) - 1u));
+            route.bucket[s_off[e] + s_run[e] + rank] = p;
+        }
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += kBucketThreads) {
+            int c = 0;
+            for (int w = 0; w < W; ++w) c += __popc(s_bm[ee * W + w]);
+            s_run[ee] += c;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) *counter = 0;
+}
+
+hipError_t launch_topk_bucket(const float* partials, int splits, const float* bias, int M, int E,
+                              int k, float routed_scale, float* logits_out,
+                              const moe_routing& route, int* counter, hipStream_t stream) {
+    const int blocks = (M + 3) / 4;
+    hipLaunchKernelGGL(k_topk_bucket, dim3(blocks), dim3(256), 0, stream, partials, splits, bias,
+                       M, E, k, routed_scale, logits_out, route, counter);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,383 @@
+// moe_api.cpp — the C ABI of the MoE layer: argument validation, workspace
+// layout and launch sequencing (host only; the kernels live in k_*.hip).
+//
+// Every argument is checked before anything is enqueued, so an error return
+// means nothing was launched (the pages' no-silent-fallback rule: an
+// unsupported setup is refused with a reason, SGLang-NVIDIA-Mega README,
+// "Design").  Grid sizes depend only on shapes (README "Design": coverage is
+// decided by row count alone, so captured graphs replay the decision).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxM = 4096;
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+constexpr int kMaxH = 16384;
+constexpr int kMaxI = 8192;
+constexpr int kRouteCounters = 16;  // ints reserved for the route step's counter
+
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+int check_dims(int M, int H, int E, int k) {
+    if (M < 1 || H < 1 || E < 1 || k < 1) return MOE_ERR_INVALID_ARG;
+    if (M > kMaxM || E > kMaxE || k > std::min(E, kMaxK)) return MOE_ERR_UNSUPPORTED;
+    if (H % 128 != 0 || H > kMaxH) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int check_routing(const moe_routing* r) {
+    if (!r || !r->topk_ids || !r->topk_w || !r->expert_offsets || !r->bucket || !r->tile_expert ||
+        !r->tile_begin || !r->tile_rows || !r->num_tiles || !r->active_experts || !r->num_active)
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+int check_fp4_weights(const moe_weights* w) {
+    if (!w || !w->w || !w->scales) return MOE_ERR_INVALID_ARG;
+    if (w->fmt == MOE_FMT_NVFP4 && !w->global_scale) return MOE_ERR_INVALID_ARG;
+    if (w->fmt != MOE_FMT_MXFP4 && w->fmt != MOE_FMT_NVFP4) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return MOE_OK;
+    (void)hipGetLastError();
+    return MOE_ERR_HIP;
+}
+
+// Sequential carve of a workspace at 256-byte boundaries.
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    template <typename T>
+    T* take(size_t count) {
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += align_up(count * sizeof(T));
+        return p;
+    }
+};
+
+struct RouteWs {
+    int* counters;
+    float* partials;
+};
+
+RouteWs carve_route(Carver& c, int M, int H, int E, int extra_counters) {
+    RouteWs w;
+    w.counters = c.take<int>(kRouteCounters + extra_counters);
+    const RouterPlan p = router_plan(M, H, E);
+    w.partials = c.take<float>((size_t)p.splits * M * E);
+    return w;
+}
+
+ExpertJob routed_job(const moe_weights& w, int N_out, int K, const moe_routing& r, int M, int E,
+                     int k) {
+    ExpertJob j;
+    j.w = w;
+    j.N_out = N_out;
+    j.K = K;
+    j.dense = false;
+    j.offsets = r.expert_offsets;
+    j.bucket = r.bucket;
+    j.active = r.active_experts;
+    j.num_active = r.num_active;
+    j.slots = std::min(E, M * k);
+    j.k = k;
+    j.M = M;
+    return j;
+}
+
+ExpertJob dense_job(const moe_weights& w, int N_out, int K, int M) {
+    ExpertJob j;
+    j.w = w;
+    j.N_out = N_out;
+    j.K = K;
+    j.dense = true;
+    j.offsets = j.bucket = j.active = j.num_active = nullptr;
+    j.slots = 1;
+    j.k = 1;
+    j.M = M;
+    return j;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument (null pointer, bad size or inconsistent shape)";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or format (see the limits in moe.h)";
+        case MOE_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+        case MOE_ERR_HIP: return "a HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+int moe_tile_capacity(int M, int E, int k) {
+    if (M < 1 || E < 1 || k < 1) return 0;
+    const int P = M * k;
+    return (P + 7) / 8 + std::min(E, P);
+}
+
+size_t moe_route_workspace_bytes(int M, int H, int E, int k) {
+    const int Hc = H == 0 ? 128 : H;  // H = 0: routing from logits_in
+    if (check_dims(M, Hc, E, k) != MOE_OK) return 0;
+    Carver c(nullptr);
+    carve_route(c, M, Hc, E, 0);
+    return c.off;
+}
+
+int moe_route_topk(const uint16_t* x, const float* logits_in, const float* w_router,
+                   const float* bias, int M, int H, int E, int k, float routed_scale,
+                   float* logits_out, const moe_routing* route, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+    if ((x == nullptr) == (logits_in == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (x && (!w_router || !logits_out)) return MOE_ERR_INVALID_ARG;
+    const int Hc = x ? H : 128;
+    if (int st = check_dims(M, Hc, E, k)) return st;
+    if (int st = check_routing(route)) return st;
+    if (!workspace || !aligned256(workspace)) return MOE_ERR_WORKSPACE;
+    Carver c(workspace);
+    RouteWs w = carve_route(c, M, Hc, E, 0);
+    if (c.off > workspace_bytes) return MOE_ERR_WORKSPACE;
+    hipError_t e;
+    if (x) {
+        const RouterPlan p = router_plan(M, H, E);
+        e = launch_router_partials(x, w_router, M, H, E, p, w.partials, w.counters, kRouteCounters, stream);
+        if (e == hipSuccess)
+            e = launch_topk_bucket(w.partials, p.splits, bias, M, E, k, routed_scale, logits_out, *route,
+                                   w.counters, stream);
+    } else {
+        e = launch_zero_ints(w.counters, kRouteCounters, stream);
+        if (e == hipSuccess)
+            e = launch_topk_bucket(logits_in, 1, bias, M, E, k, routed_scale, nullptr, *route, w.counters,
+                                   stream);
+    }
+    return hip_status(e);
+}
+
+int moe_quant_act_mxfp8(const uint16_t* x, int M, int K, uint8_t* q, uint8_t* s,
+                        hipStream_t stream) {
+    if (!x || !q || !s || M < 1 || K < 32) return MOE_ERR_INVALID_ARG;
+    if (K % 32 != 0 || M > kMaxM * kMaxK || K > kMaxH) return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_quant_mxfp8(x, M, K, q, s, stream));
+}
+
+size_t moe_gate_up_workspace_bytes(int fmt, int M, int H, int I, int E, int k, int dense) {
+    (void)E;
+    (void)k;
+    if (fmt != MOE_FMT_BF16 || !dense || M < 1 || H < 128 || I < 32) return 0;
+    return align_up((size_t)(I / 32) * sizeof(int)) + gate_up_bf16_partials_bytes(M, H, I);
+}
+
+int moe_expert_gate_up(const moe_weights* w13, const uint8_t* a_q, const uint8_t* a_s,
+                       const uint16_t* a_bf16, const moe_routing* route, int M, int H, int I,
+                       int E, int k, uint8_t* h_q, uint8_t* h_s, uint16_t* h_bf16,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!w13) return MOE_ERR_INVALID_ARG;
+    const bool dense = route == nullptr;
+    if (int st = check_dims(M, H, dense ? 1 : E, dense ? 1 : k)) return st;
+    if (I < 128 || I % 128 != 0 || I > kMaxI) return MOE_ERR_UNSUPPORTED;
+    if (w13->fmt == MOE_FMT_BF16) {
+        if (!dense) return MOE_ERR_UNSUPPORTED;  // bf16 weights: shared expert only
+        if (!w13->w || !a_bf16 || !h_bf16) return MOE_ERR_INVALID_ARG;
+        const size_t need = moe_gate_up_workspace_bytes(MOE_FMT_BF16, M, H, I, 1, 1, 1);
+        if (!workspace || !aligned256(workspace) || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+        Carver c(workspace);
+        int* counters = c.take<int>(I / 32);
+        float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + c.off);
+        hipError_t e = launch_zero_ints(counters, I / 32, stream);
+        if (e == hipSuccess)
+            e = launch_gate_up_bf16(dense_job(*w13, I, H, M), a_bf16, h_bf16, part, counters, stream);
+        return hip_status(e);
+    }
+    if (int st = check_fp4_weights(w13)) return st;
+    if (!a_q || !a_s || !h_q || !h_s) return MOE_ERR_INVALID_ARG;
+    if (!dense)
+        if (int st = check_routing(route)) return st;
+    const ExpertJob job = dense ? dense_job(*w13, I, H, M) : routed_job(*w13, I, H, *route, M, E, k);
+    return hip_status(launch_gate_up_fp4(job, a_q, a_s, h_q, h_s, stream));
+}
+
+int moe_expert_down(const moe_weights* w2, const uint8_t* h_q, const uint8_t* h_s,
+                    const uint16_t* h_bf16, const moe_routing* route, int M, int H, int I,
+                    int E, int k, float* y, hipStream_t stream) {
+    if (!w2 || !y) return MOE_ERR_INVALID_ARG;
+    const bool dense = route == nullptr;
+    if (int st = check_dims(M, H, dense ? 1 : E, dense ? 1 : k)) return st;
+    if (I < 128 || I % 128 != 0 || I > kMaxI) return MOE_ERR_UNSUPPORTED;
+    if (w2->fmt == MOE_FMT_BF16) {
+        if (!dense) return MOE_ERR_UNSUPPORTED;
+        if (!w2->w || !h_bf16) return MOE_ERR_INVALID_ARG;
+        return hip_status(launch_down_bf16(dense_job(*w2, H, I, M), h_bf16, y, stream));
+    }
+    if (int st = check_fp4_weights(w2)) return st;
+    if (!h_q || !h_s) return MOE_ERR_INVALID_ARG;
+    if (!dense)
+        if (int st = check_routing(route)) return st;
+    const ExpertJob job = dense ? dense_job(*w2, H, I, M) : routed_job(*w2, H, I, *route, M, E, k);
+    return hip_status(launch_down_fp4(job, h_q, h_s, y, stream));
+}
+
+int moe_finalize_rmsnorm(const float* y, const float* topk_w, const float* y_sh,
+                         const uint16_t* residual, const uint16_t* gamma, float eps, int M, int H,
+                         int k, uint16_t* out, uint16_t* residual_out, hipStream_t stream) {
+    if (!y || !topk_w || !residual || !gamma || !out || M < 1 || H < 1 || k < 1)
+        return MOE_ERR_INVALID_ARG;
+    if (H % 128 != 0 || H > kMaxH || k > kMaxK || M > kMaxM) return MOE_ERR_UNSUPPORTED;
+    if (!(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_finalize(y, topk_w, y_sh, residual, gamma, eps, M, H, k, out, residual_out, stream));
+}
+
+// ---- the whole layer --------------------------------------------------------
+
+namespace {
+
+int check_desc(const moe_layer_desc* d) {
+    if (!d) return MOE_ERR_INVALID_ARG;
+    if (int st = check_dims(d->M, d->H, d->E, d->k)) return st;
+    if (d->I < 128 || d->I % 128 != 0 || d->I > kMaxI) return MOE_ERR_UNSUPPORTED;
+    if (!d->w_router || !d->gamma) return MOE_ERR_INVALID_ARG;
+    if (!(d->eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+    if (int st = check_fp4_weights(&d->w13)) return st;
+    if (int st = check_fp4_weights(&d->w2)) return st;
+    if (d->w13.fmt != d->w2.fmt) return MOE_ERR_UNSUPPORTED;
+    const int sf = d->sh13.fmt;
+    if (sf != d->sh2.fmt) return MOE_ERR_INVALID_ARG;
+    if (sf != MOE_FMT_NONE) {
+        if (d->I_sh < 128 || d->I_sh % 128 != 0 || d->I_sh > kMaxI) return MOE_ERR_UNSUPPORTED;
+        if (sf == MOE_FMT_BF16) {
+            if (!d->sh13.w || !d->sh2.w) return MOE_ERR_INVALID_ARG;
+        } else {
+            if (int st = check_fp4_weights(&d->sh13)) return st;
+            if (int st = check_fp4_weights(&d->sh2)) return st;
+        }
+    }
+    return MOE_OK;
+}
+
+struct LayerWs {
+    RouteWs route;
+    int* sh_counters;
+    int32_t *ids, *offsets, *bucket, *tile_e, *tile_b, *tile_r, *num_tiles, *active, *num_active;
+    float* w;
+    uint8_t *xq, *xs, *hq, *hs, *hsq, *hss;
+    uint16_t* hsb;
+    float* sh_part;
+    float *y, *ysh;
+};
+
+LayerWs carve_layer(Carver& c, const moe_layer_desc* d) {
+    LayerWs L;
+    const int M = d->M, H = d->H, E = d->E, k = d->k, I = d->I, Ish = d->I_sh;
+    const int P = M * k;
+    const int T = moe_tile_capacity(M, E, k);
+    const bool sh = d->sh13.fmt != MOE_FMT_NONE;
+    const bool shb = d->sh13.fmt == MOE_FMT_BF16;
+    L.route = carve_route(c, M, H, E, shb ? Ish / 32 : 0);
+    L.sh_counters = L.route.counters ? L.route.counters + kRouteCounters : nullptr;
+    L.ids = c.take<int32_t>(P);
+    L.w = c.take<float>(P);
+    L.offsets = c.take<int32_t>(E + 1);
+    L.bucket = c.take<int32_t>(P);
+    L.tile_e = c.take<int32_t>(T);
+    L.tile_b = c.take<int32_t>(T);
+    L.tile_r = c.take<int32_t>(T);
+    L.num_tiles = c.take<int32_t>(1);
+    L.active = c.take<int32_t>(std::min(E, P));
+    L.num_active = c.take<int32_t>(1);
+    L.xq = c.take<uint8_t>((size_t)M * H);
+    L.xs = c.take<uint8_t>((size_t)M * H / 32);
+    L.hq = c.take<uint8_t>((size_t)P * I);
+    L.hs = c.take<uint8_t>((size_t)P * I / 32);
+    L.hsq = L.hss = nullptr;
+    L.hsb = nullptr;
+    L.sh_part = nullptr;
+    if (sh && !shb) {
+        L.hsq = c.take<uint8_t>((size_t)M * Ish);
+        L.hss = c.take<uint8_t>((size_t)M * Ish / 32);
+    }
+    if (shb) {
+        L.hsb = c.take<uint16_t>((size_t)M * Ish);
+        L.sh_part = c.take<float>(gate_up_bf16_partials_bytes(M, H, Ish) / sizeof(float));
+    }
+    L.y = c.take<float>((size_t)P * H);
+    L.ysh = sh ? c.take<float>((size_t)M * H) : nullptr;
+    return L;
+}
+
+}  // namespace
+
+size_t moe_layer_workspace_bytes(const moe_layer_desc* desc) {
+    if (check_desc(desc) != MOE_OK) return 0;
+    Carver c(nullptr);
+    carve_layer(c, desc);
+    return c.off;
+}
+
+int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residual,
+              uint16_t* out, uint16_t* residual_out, float* logits_out, int32_t* topk_ids_out,
+              float* topk_w_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (int st = check_desc(d)) return st;
+    if (!x || !residual || !out) return MOE_ERR_INVALID_ARG;
+    if (!workspace || !aligned256(workspace)) return MOE_ERR_WORKSPACE;
+    Carver c(workspace);
+    LayerWs L = carve_layer(c, d);
+    if (c.off > workspace_bytes) return MOE_ERR_WORKSPACE;
+    const int M = d->M, H = d->H, E = d->E, k = d->k, I = d->I, Ish = d->I_sh;
+    const int sf = d->sh13.fmt;
+
+    moe_routing r;
+    r.topk_ids = topk_ids_out ? topk_ids_out : L.ids;
+    r.topk_w = topk_w_out ? topk_w_out : L.w;
+    r.expert_offsets = L.offsets;
+    r.bucket = L.bucket;
+    r.tile_expert = L.tile_e;
+    r.tile_begin = L.tile_b;
+    r.tile_rows = L.tile_r;
+    r.num_tiles = L.num_tiles;
+    r.active_experts = L.active;
+    r.num_active = L.num_active;
+
+    const RouterPlan p = router_plan(M, H, E);
+    const int ncount = kRouteCounters + (sf == MOE_FMT_BF16 ? Ish / 32 : 0);
+    hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials,
+                                          L.route.counters, ncount, stream);
+    if (e == hipSuccess)
+        e = launch_topk_bucket(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale,
+                               logits_out, r, L.route.counters, stream);
+    if (e == hipSuccess) e = launch_quant_mxfp8(x, M, H, L.xq, L.xs, stream);
+    const ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
+    if (e == hipSuccess) e = launch_gate_up_fp4(gu, L.xq, L.xs, L.hq, L.hs, stream);
+    if (e == hipSuccess && sf == MOE_FMT_BF16)
+        e = launch_gate_up_bf16(dense_job(d->sh13, Ish, H, M), x, L.hsb, L.sh_part, L.sh_counters, stream);
+    else if (e == hipSuccess && sf != MOE_FMT_NONE)
+        e = launch_gate_up_fp4(dense_job(d->sh13, Ish, H, M), L.xq, L.xs, L.hsq, L.hss, stream);
+    const ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);
+    if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream);
+    if (e == hipSuccess && sf == MOE_FMT_BF16)
+        e = launch_down_bf16(dense_job(d->sh2, H, Ish, M), L.hsb, L.ysh, stream);
+    else if (e == hipSuccess && sf != MOE_FMT_NONE)
+        e = launch_down_fp4(dense_job(d->sh2, H, Ish, M), L.hsq, L.hss, L.ysh, stream);
+    if (e == hipSuccess)
+        e = launch_finalize(L.y, r.topk_w, L.ysh, residual, d->gamma, d->eps, M, H, k, out, residual_out,
+                            stream);
+    return hip_status(e);
+}
+
+}  // extern "C"

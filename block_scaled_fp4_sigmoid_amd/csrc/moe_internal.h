@@ -1,0 +1,71 @@
+// moe_internal.h — host-side launchers of the layer's kernels (private).
+// Every launcher assumes its arguments were validated by the C ABI layer and
+// returns the HIP error of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// Workspace pieces are carved at 256-byte boundaries.
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+struct RouterPlan {
+    int splits;     // K chunks whose partial logits the top-k step sums
+    int kchunk;     // elements of H per chunk (multiple of 32)
+    int row_groups; // groups of up to 64 rows
+};
+RouterPlan router_plan(int M, int H, int E);
+
+hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int M, int H, int E,
+                                  const RouterPlan& plan, float* partials, int* counters,
+                                  int ncounters, hipStream_t stream);
+// Zeroes n ints with a kernel (no memset node, so it is safe in captured graphs).
+hipError_t launch_zero_ints(int* p, int n, hipStream_t stream);
+// partials == nullptr: logits_in is read as the single partial.
+hipError_t launch_topk_bucket(const float* partials, int splits, const float* bias, int M, int E,
+                              int k, float routed_scale, float* logits_out,
+                              const moe_routing& route, int* counter, hipStream_t stream);
+
+hipError_t launch_quant_mxfp8(const uint16_t* x, int M, int K, uint8_t* q, uint8_t* s,
+                              hipStream_t stream);
+
+// Expert GEMM jobs.  A routed job covers slots [0, U_max) of the active-expert
+// list; a dense job is one expert over all M rows.
+struct ExpertJob {
+    moe_weights w;          // weights (E experts or one)
+    int N_out;              // gate_up: I ; down: H (output features)
+    int K;                  // reduction length (gate_up: H ; down: I)
+    bool dense;
+    // routed
+    const int32_t* offsets;
+    const int32_t* bucket;
+    const int32_t* active;
+    const int32_t* num_active;
+    int slots;              // U_max for routed, 1 for dense
+    int k;                  // top-k (pair id -> row)
+    int M;
+};
+
+hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const uint8_t* a_s,
+                              uint8_t* h_q, uint8_t* h_s, hipStream_t stream);
+hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8_t* h_s,
+                           float* y, hipStream_t stream);
+
+// bf16 split-K partials; the counters (I/32 ints) live separately and must be
+// zero when the kernel starts (the last workgroup of each block re-zeroes its own).
+size_t gate_up_bf16_partials_bytes(int M, int H, int I);
+hipError_t launch_gate_up_bf16(const ExpertJob& job, const uint16_t* a, uint16_t* h,
+                               float* partials, int* counters, hipStream_t stream);
+hipError_t launch_down_bf16(const ExpertJob& job, const uint16_t* h, float* y, hipStream_t stream);
+
+hipError_t launch_finalize(const float* y, const float* topk_w, const float* y_sh,
+                           const uint16_t* residual, const uint16_t* gamma, float eps, int M,
+                           int H, int k, uint16_t* out, uint16_t* residual_out,
+                           hipStream_t stream);
+
+}  // namespace moe

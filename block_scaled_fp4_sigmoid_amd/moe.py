@@ -1,0 +1,239 @@
+"""Python binding of the C ABI in include/moe.h (ctypes; argument marshalling only).
+
+Every step of the layer runs in the HIP library libmoe_mi355.so; this module
+only turns torch tensors (device memory) and torch streams into the plain
+pointers the C ABI takes.  There is no fallback: if the library is missing or
+a call returns an error, a RuntimeError is raised.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_mi355.so")
+
+MOE_FMT_NONE, MOE_FMT_MXFP4, MOE_FMT_NVFP4, MOE_FMT_BF16 = 0, 1, 2, 3
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
+
+EXPORTS = ["moe_status_str", "moe_abi_version", "moe_tile_capacity", "moe_route_workspace_bytes",
+           "moe_route_topk", "moe_quant_act_mxfp8", "moe_gate_up_workspace_bytes",
+           "moe_expert_gate_up", "moe_expert_down", "moe_finalize_rmsnorm",
+           "moe_layer_workspace_bytes", "moe_layer"]
+
+
+class moe_weights(C.Structure):
+    _fields_ = [("fmt", C.c_int), ("w", C.c_void_p), ("scales", C.c_void_p),
+                ("global_scale", C.c_void_p)]
+
+
+class moe_routing(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("topk_ids", "topk_w", "expert_offsets", "bucket",
+                                          "tile_expert", "tile_begin", "tile_rows", "num_tiles",
+                                          "active_experts", "num_active")]
+
+
+class moe_layer_desc(C.Structure):
+    _fields_ = [("M", C.c_int), ("H", C.c_int), ("E", C.c_int), ("k", C.c_int), ("I", C.c_int),
+                ("I_sh", C.c_int), ("routed_scale", C.c_float), ("eps", C.c_float),
+                ("w_router", C.c_void_p), ("router_bias", C.c_void_p),
+                ("w13", moe_weights), ("w2", moe_weights), ("sh13", moe_weights),
+                ("sh2", moe_weights), ("gamma", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -m "
+                               "block_scaled_fp4_sigmoid_amd.build or __graft_entry__.build())")
+        L = C.CDLL(LIB_PATH)
+        vp, i, f, sz = C.c_void_p, C.c_int, C.c_float, C.c_size_t
+        L.moe_status_str.restype = C.c_char_p
+        L.moe_status_str.argtypes = [i]
+        L.moe_abi_version.restype = i
+        L.moe_tile_capacity.restype = i
+        L.moe_tile_capacity.argtypes = [i, i, i]
+        L.moe_route_workspace_bytes.restype = sz
+        L.moe_route_workspace_bytes.argtypes = [i, i, i, i]
+        L.moe_route_topk.restype = i
+        L.moe_route_topk.argtypes = [vp, vp, vp, vp, i, i, i, i, f, vp, C.POINTER(moe_routing), vp, sz, vp]
+        L.moe_quant_act_mxfp8.restype = i
+        L.moe_quant_act_mxfp8.argtypes = [vp, i, i, vp, vp, vp]
+        L.moe_gate_up_workspace_bytes.restype = sz
+        L.moe_gate_up_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        L.moe_expert_gate_up.restype = i
+        L.moe_expert_gate_up.argtypes = [C.POINTER(moe_weights), vp, vp, vp, C.POINTER(moe_routing),
+                                         i, i, i, i, i, vp, vp, vp, vp, sz, vp]
+        L.moe_expert_down.restype = i
+        L.moe_expert_down.argtypes = [C.POINTER(moe_weights), vp, vp, vp, C.POINTER(moe_routing),
+                                      i, i, i, i, i, vp, vp]
+        L.moe_finalize_rmsnorm.restype = i
+        L.moe_finalize_rmsnorm.argtypes = [vp, vp, vp, vp, vp, f, i, i, i, vp, vp, vp]
+        L.moe_layer_workspace_bytes.restype = sz
+        L.moe_layer_workspace_bytes.argtypes = [C.POINTER(moe_layer_desc)]
+        L.moe_layer.restype = i
+        L.moe_layer.argtypes = [C.POINTER(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the C ABI must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(rc: int, what: str):
+    if rc != MOE_OK:
+        raise RuntimeError(f"{what} failed: {lib().moe_status_str(rc).decode()} (status {rc})")
+
+
+def status_str(rc: int) -> str:
+    return lib().moe_status_str(rc).decode()
+
+
+def abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def tile_capacity(M: int, E: int, k: int) -> int:
+    return lib().moe_tile_capacity(M, E, k)
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A 256-byte aligned device buffer (torch's allocator aligns to 512)."""
+    t = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    assert t.data_ptr() % 256 == 0
+    return t
+
+
+@dataclass
+class Weights:
+    """One projection of E experts in the canonical layout (see moe.h)."""
+    fmt: int
+    w: Optional[torch.Tensor] = None
+    scales: Optional[torch.Tensor] = None
+    global_scale: Optional[torch.Tensor] = None
+
+    def c(self) -> moe_weights:
+        return moe_weights(self.fmt, _p(self.w), _p(self.scales), _p(self.global_scale))
+
+
+class Routing:
+    """Device buffers of a routing result (moe_routing)."""
+
+    def __init__(self, M: int, E: int, k: int, device):
+        P = M * k
+        T = tile_capacity(M, E, k)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.M, self.E, self.k = M, E, k
+        self.topk_ids = torch.empty((M, k), **i32)
+        self.topk_w = torch.empty((M, k), dtype=torch.float32, device=device)
+        self.expert_offsets = torch.empty(E + 1, **i32)
+        self.bucket = torch.empty(P, **i32)
+        self.tile_expert = torch.empty(T, **i32)
+        self.tile_begin = torch.empty(T, **i32)
+        self.tile_rows = torch.empty(T, **i32)
+        self.num_tiles = torch.empty(1, **i32)
+        self.active_experts = torch.empty(min(E, P), **i32)
+        self.num_active = torch.empty(1, **i32)
+
+    def c(self) -> moe_routing:
+        return moe_routing(*[_p(getattr(self, n)) for n, _ in moe_routing._fields_])
+
+
+def route_topk(routing: Routing, x=None, logits_in=None, w_router=None, bias=None,
+               routed_scale: float = 1.0, logits_out=None, ws=None, stream=None):
+    M, E, k = routing.M, routing.E, routing.k
+    H = x.shape[1] if x is not None else 0
+    dev = (x if x is not None else logits_in).device
+    need = lib().moe_route_workspace_bytes(M, H, E, k)
+    if ws is None:
+        ws = workspace(need, dev)
+    r = routing.c()
+    rc = lib().moe_route_topk(_p(x), _p(logits_in), _p(w_router), _p(bias), M, H, E, k,
+                              float(routed_scale), _p(logits_out), C.byref(r), _p(ws), ws.numel(),
+                              _stream(stream))
+    _check(rc, "moe_route_topk")
+
+
+def quant_act_mxfp8(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream=None):
+    M, K = x.shape
+    _check(lib().moe_quant_act_mxfp8(_p(x), M, K, _p(q), _p(s), _stream(stream)), "moe_quant_act_mxfp8")
+
+
+def expert_gate_up(w13: Weights, M, H, I, E, k, routing: Optional[Routing] = None, a_q=None,
+                   a_s=None, a_bf16=None, h_q=None, h_s=None, h_bf16=None, ws=None, stream=None):
+    dense = routing is None
+    dev = (a_q if a_q is not None else a_bf16).device
+    need = lib().moe_gate_up_workspace_bytes(w13.fmt, M, H, I, E, k, int(dense))
+    if ws is None and need:
+        ws = workspace(need, dev)
+    wc = w13.c()
+    r = None if dense else routing.c()
+    rc = lib().moe_expert_gate_up(C.byref(wc), _p(a_q), _p(a_s), _p(a_bf16),
+                                  None if dense else C.byref(r), M, H, I, E, k, _p(h_q), _p(h_s),
+                                  _p(h_bf16), _p(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(rc, "moe_expert_gate_up")
+
+
+def expert_down(w2: Weights, M, H, I, E, k, y, routing: Optional[Routing] = None, h_q=None,
+                h_s=None, h_bf16=None, stream=None):
+    wc = w2.c()
+    r = None if routing is None else routing.c()
+    rc = lib().moe_expert_down(C.byref(wc), _p(h_q), _p(h_s), _p(h_bf16),
+                               None if routing is None else C.byref(r), M, H, I, E, k, _p(y),
+                               _stream(stream))
+    _check(rc, "moe_expert_down")
+
+
+def finalize_rmsnorm(y, topk_w, y_sh, residual, gamma, eps, out, residual_out=None, stream=None):
+    M, H = residual.shape
+    k = topk_w.shape[1]
+    rc = lib().moe_finalize_rmsnorm(_p(y), _p(topk_w), _p(y_sh), _p(residual), _p(gamma),
+                                    float(eps), M, H, k, _p(out), _p(residual_out), _stream(stream))
+    _check(rc, "moe_finalize_rmsnorm")
+
+
+class Layer:
+    """The fused layer (moe_layer) over weights held in torch device tensors."""
+
+    def __init__(self, M, H, E, k, I, I_sh, routed_scale, eps, w_router, router_bias,
+                 w13: Weights, w2: Weights, sh13: Weights, sh2: Weights, gamma):
+        self._keep = (w_router, router_bias, w13, w2, sh13, sh2, gamma)
+        self.M, self.H, self.E, self.k = M, H, E, k
+        self.desc = moe_layer_desc(M, H, E, k, I, I_sh, float(routed_scale), float(eps),
+                                   _p(w_router), _p(router_bias), w13.c(), w2.c(), sh13.c(),
+                                   sh2.c(), _p(gamma))
+        self.ws_bytes = lib().moe_layer_workspace_bytes(C.byref(self.desc))
+        if self.ws_bytes == 0:
+            raise RuntimeError("moe_layer_workspace_bytes rejected the layer description")
+        self.ws = workspace(self.ws_bytes, w_router.device)
+
+    def set_weights(self, w13: Weights, w2: Weights, sh13: Weights, sh2: Weights):
+        """Point the layer at another copy of its weights (same shapes)."""
+        self.desc.w13, self.desc.w2, self.desc.sh13, self.desc.sh2 = w13.c(), w2.c(), sh13.c(), sh2.c()
+        self._keep = self._keep[:2] + (w13, w2, sh13, sh2) + self._keep[6:]
+
+    def __call__(self, x, residual, out, residual_out=None, logits_out=None, topk_ids_out=None,
+                 topk_w_out=None, stream=None):
+        rc = lib().moe_layer(C.byref(self.desc), _p(x), _p(residual), _p(out), _p(residual_out),
+                             _p(logits_out), _p(topk_ids_out), _p(topk_w_out), _p(self.ws),
+                             self.ws.numel(), _stream(stream))
+        _check(rc, "moe_layer")

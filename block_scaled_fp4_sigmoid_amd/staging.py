@@ -1,0 +1,83 @@
+"""Places synthetic inputs (synth.MoEInputs) in device memory for the C ABI.
+
+Pure data movement: host arrays are copied to the GPU and each expert matrix
+is assembled there from the generator's row pool with index_select, giving
+the canonical layouts of include/moe.h ([E, N, K/2] packed, [E, N, K/32|K/16]
+scales, [E] globals).  Nothing here computes a step of the layer.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import synth
+from .moe import (MOE_FMT_BF16, MOE_FMT_NONE, Layer, Weights)
+
+
+def _t(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def pooled_on(pe: synth.PooledExperts, device) -> Weights:
+    pool = _t(pe.pool_packed, device)
+    pool_s = _t(pe.pool_scales, device)
+    idx = torch.from_numpy(pe.idx.astype(np.int64).reshape(-1)).to(device)
+    packed = pool.index_select(0, idx).reshape(pe.E, pe.N, -1).contiguous()
+    scales = pool_s.index_select(0, idx).reshape(pe.E, pe.N, -1).contiguous()
+    g = _t(pe.gscale.astype(np.float32), device)
+    return Weights(pe.fmt, packed, scales, g)
+
+
+def matrix_on(m: Optional[synth.Matrix], device) -> Weights:
+    if m is None:
+        return Weights(MOE_FMT_NONE)
+    if m.fmt == synth.BF16:
+        return Weights(MOE_FMT_BF16, _t(m.bf16, device))
+    g = torch.tensor([m.gscale], dtype=torch.float32, device=device)
+    return Weights(m.fmt, _t(m.packed, device), _t(m.scales, device), g)
+
+
+def clone_weights(w: Weights) -> Weights:
+    c = lambda t: None if t is None else t.clone()
+    return Weights(w.fmt, c(w.w), c(w.scales), c(w.global_scale))
+
+
+@dataclass
+class DeviceInputs:
+    shape: synth.Shape
+    x: torch.Tensor
+    Wr: torch.Tensor
+    bias: Optional[torch.Tensor]
+    gamma: torch.Tensor
+    w13: Weights
+    w2: Weights
+    sh13: Weights
+    sh2: Weights
+
+    def layer(self) -> Layer:
+        s = self.shape
+        return Layer(s.M, s.H, s.E, s.k, s.I, s.I_sh, s.routed_scale, s.eps, self.Wr, self.bias,
+                     self.w13, self.w2, self.sh13, self.sh2, self.gamma)
+
+    def weight_bytes_per_expert(self) -> int:
+        s = self.shape
+        per = lambda w: (w.w[0].numel() + w.scales[0].numel() + (4 if w.global_scale is not None
+                                                                 and s.wfmt == synth.NVFP4 else 0))
+        return per(self.w13) + per(self.w2)
+
+
+def to_device(inp: synth.MoEInputs, device="cuda") -> DeviceInputs:
+    return DeviceInputs(
+        inp.shape,
+        _t(inp.x, device),
+        _t(inp.Wr, device),
+        None if inp.bias is None else _t(inp.bias, device),
+        _t(inp.gamma, device),
+        pooled_on(inp.w13, device),
+        pooled_on(inp.w2, device),
+        matrix_on(inp.sh13, device),
+        matrix_on(inp.sh2, device),
+    )

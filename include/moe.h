@@ -1,0 +1,237 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) small-M block-scaled-FP4 sigmoid-routed
+ * mixture-of-experts layer.
+ *
+ * The layer (one decode / verify step of 1 to a few hundred rows):
+ *   1. router GEMV and sigmoid top-k with renormalized weights;
+ *   2. route step: each expert's rows grouped into 8-row tiles;
+ *   3. one-pass MXFP8 quantization of the activations;
+ *   4. block-scaled FP4 gate_up GEMM + SwiGLU + MXFP8 requantization;
+ *   5. block-scaled FP4 down GEMM;
+ *   6. top-k weighted finalize + shared-expert add + residual add + RMSNorm.
+ * Where each step is described (page, section): see the comment of each entry.
+ *
+ * Conventions shared by every entry point
+ *   - Memory: every data pointer is device memory owned by the caller.  The
+ *     library never allocates, frees or synchronizes, and keeps no global
+ *     mutable state; calls are thread-safe.
+ *   - Streams: every call enqueues work on `stream` and returns immediately.
+ *     Grid sizes depend on shape arguments only, so calls can be captured in
+ *     a HIP graph; data-dependent counts stay on the device.
+ *   - Types: bf16 is passed as uint16_t bit patterns; FP4 (E2M1) as packed
+ *     bytes, two codes per byte, low nibble = even K index; E4M3 and E8M0 as
+ *     uint8_t codes.  All arrays are row-major and contiguous.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued, so a call that returns an error enqueued nothing.  No C++
+ *     exception crosses the ABI.  moe_status_str() describes a code.
+ *   - Limits (MOE_ERR_UNSUPPORTED otherwise): H % 128 == 0, I % 128 == 0,
+ *     1 <= k <= min(E, 32), 1 <= E <= 1024, 1 <= M <= 4096, H <= 16384,
+ *     I <= 8192, and a format pair this build implements.
+ *
+ * Number formats (the pages name them; their definitions are those of the
+ * OCP Microscaling Formats v1.0 specification): E2M1 elements; MXFP4 = E2M1
+ * with one E8M0 scale 2^(c-127) per 32 consecutive K; NVFP4 = E2M1 with one
+ * E4M3 scale per 16 consecutive K and one fp32 global per expert and
+ * projection; MXFP8 = E4M3 elements with one E8M0 scale per 32 along K.
+ */
+#ifndef MOE_MI355_H
+#define MOE_MI355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shape */
+    MOE_ERR_UNSUPPORTED = 2, /* outside the limits above or an unimplemented format */
+    MOE_ERR_WORKSPACE = 3,   /* workspace null, too small or misaligned */
+    MOE_ERR_HIP = 4          /* a launch failed; the HIP error was cleared */
+};
+
+/* Weight formats. */
+enum moe_fmt {
+    MOE_FMT_NONE = 0,  /* no shared expert */
+    MOE_FMT_MXFP4 = 1, /* packed E2M1 + E8M0 per 32 along K */
+    MOE_FMT_NVFP4 = 2, /* packed E2M1 + E4M3 per 16 along K + fp32 global per expert */
+    MOE_FMT_BF16 = 3   /* bf16 (shared expert only) */
+};
+
+/* One projection of E experts (or of the shared expert, E = 1), each a
+ * matrix [N, K] with K contiguous:
+ *   MXFP4: w = packed [E, N, K/2], scales = E8M0 [E, N, K/32], global unused;
+ *   NVFP4: w = packed [E, N, K/2], scales = E4M3 [E, N, K/16], global = fp32 [E];
+ *   BF16:  w = bf16 [E, N, K], scales and global unused.
+ * Gate_up weights (W13) have N = 2I with rows [0, I) the gate projection and
+ * rows [I, 2I) the up projection; down weights (W2) have N = H, K = I. */
+typedef struct moe_weights {
+    int fmt;
+    const void *w;
+    const uint8_t *scales;
+    const float *global_scale;
+} moe_weights;
+
+/* Routing of M rows with top-k over E experts (P = M*k (row, slot) pairs,
+ * pair id p = r*k + j).  Produced by moe_route_topk, read by the expert GEMMs.
+ *   topk_ids       int32 [M, k]  chosen experts, slot order = rank
+ *   topk_w         fp32  [M, k]  renormalized, scaled routing weights
+ *   expert_offsets int32 [E + 1] start of each expert's entries in `bucket`
+ *   bucket         int32 [P]     pair ids, expert by expert (ascending id),
+ *                                ascending row within an expert
+ *   tile_expert, tile_begin, tile_rows  int32 [moe_tile_capacity(M,E,k)]
+ *                                8-row tiles of consecutive bucket entries in
+ *                                (expert, tile) order; entries past
+ *                                num_tiles are unspecified
+ *   num_tiles      int32 [1]
+ *   active_experts int32 [min(E, P)]  experts with at least one row, ascending;
+ *                                entries past num_active are unspecified
+ *   num_active     int32 [1] */
+typedef struct moe_routing {
+    int32_t *topk_ids;
+    float *topk_w;
+    int32_t *expert_offsets;
+    int32_t *bucket;
+    int32_t *tile_expert;
+    int32_t *tile_begin;
+    int32_t *tile_rows;
+    int32_t *num_tiles;
+    int32_t *active_experts;
+    int32_t *num_active;
+} moe_routing;
+
+/* The whole layer's parameters. */
+typedef struct moe_layer_desc {
+    int M, H, E, k, I, I_sh;     /* I_sh: shared-expert intermediate (0 when none) */
+    float routed_scale;          /* routed scaling factor applied to topk_w */
+    float eps;                   /* RMSNorm epsilon */
+    const float *w_router;       /* fp32 [E, H] */
+    const float *router_bias;    /* fp32 [E] selection bias, or NULL */
+    moe_weights w13, w2;         /* routed experts: [E, 2I, H] and [E, H, I] */
+    moe_weights sh13, sh2;       /* shared expert: [2I_sh, H] and [H, I_sh]; fmt NONE = absent */
+    const uint16_t *gamma;       /* bf16 [H] RMSNorm weight */
+} moe_layer_desc;
+
+const char *moe_status_str(int status);
+int moe_abi_version(void);
+
+/* Upper bound on the number of 8-row tiles: sum_e ceil(n_e/8) <= ceil(P/8) + min(E, P). */
+int moe_tile_capacity(int M, int E, int k);
+
+/* ---------------------------------------------------------------------------
+ * moe_route_topk — router GEMV, sigmoid top-k with renormalized weights, and
+ * the route step that groups each expert's rows into 8-row tiles.
+ *   Pages: sgl-nvidia-mega PR #24, "Modifications / Target spec" (one expert
+ *   group, sigmoid scores, renormalized top-8); SGLang-NVIDIA-Mega README,
+ *   DeepSeek-V4.1 slot table, rows "Router top-k" (one CTA per row) and
+ *   "Routed experts (moe)" (8-row tiles, several tiles for an expert with more
+ *   than 8 rows); README Qwen3.5 slot table, row "route" (router GEMM).
+ * Arithmetic: logits[r,e] = sum_h x[r,h] * w_router[e,h] with fp32 products
+ *   and fp32 accumulation; score s = 1/(1+exp(-logit)) in fp64; selection key
+ *   = s + bias[e] (fp64; bias only selects); top-k by key descending, equal keys
+ *   by ascending expert id; w_j = routed_scale * s_j / sum_j s_j (fp64, sum in
+ *   slot order) rounded to fp32.
+ * Inputs: exactly one of x (bf16 [M, H]) or logits_in (fp32 [M, E]); with x,
+ *   w_router (fp32 [E, H]) is required and logits_out (fp32 [M, E]) receives
+ *   the logits (required with x, ignored with logits_in).  bias: fp32 [E] or
+ *   NULL.  Outputs: every pointer of *route.
+ * Workspace: moe_route_workspace_bytes(M, H, E, k) bytes (H = 0 when routing
+ *   from logits_in), 256-byte aligned, contents need no initialization. */
+size_t moe_route_workspace_bytes(int M, int H, int E, int k);
+int moe_route_topk(const uint16_t *x, const float *logits_in, const float *w_router,
+                   const float *bias, int M, int H, int E, int k, float routed_scale,
+                   float *logits_out, const moe_routing *route, void *workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_quant_act_mxfp8 — one-pass MXFP8 quantization of bf16 rows.
+ *   Pages: SGLang-NVIDIA-Mega README, DeepSeek-V4.1 slot table, row "Shared
+ *   expert gate_up (shared_ll)" (one-pass MXFP8 quant of the activations).
+ * Rule (OCP MX v1.0; the pages do not state one): per 32 consecutive values,
+ *   shared exponent = floor(log2 amax) - 8 clamped to [-127, 127], scale code
+ *   = shared + 127; elements = E4M3 of x / 2^shared, round to nearest even,
+ *   saturated to +-448, sign kept (-0 -> 0x80).  A block holding NaN or Inf
+ *   gets scale 0xFF and NaN codes.
+ * x: bf16 [M, K]; q: uint8 [M, K]; s: uint8 [M, K/32].  K % 32 == 0. */
+int moe_quant_act_mxfp8(const uint16_t *x, int M, int K, uint8_t *q, uint8_t *s,
+                        hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_gate_up — gate_up GEMM of every routed expert over its rows,
+ * SwiGLU, and requantization of the result for the down GEMM.
+ *   Pages: README Qwen3.5 slot table, row "mkm" (FC1, SwiGLU, requant, FC2);
+ *   README DeepSeek-V4.1 slot table, row "Routed experts (moe)" (block-scaled
+ *   GEMMs over 8-row tiles); sgl-nvidia-mega PR #33 appended table, row
+ *   "shared act quant" (SiLU-and-mul fused with the down input's quant);
+ *   SGLang Spark GB10 Optimizations, section 1 (NVFP4 K-groups of 16).
+ * g = A W13[:I]^T, u = A W13[I:]^T with exact products and fp32 sums; h =
+ * silu(g) * u in fp32.  FP4 weights: A is MXFP8 (a_q, a_s) [M, H] and h is
+ * written as MXFP8 (h_q [Pr, I], h_s [Pr, I/32]) with the rule of
+ * moe_quant_act_mxfp8.  BF16 weights: A is bf16 a_bf16 [M, H] and h is written
+ * rounded to bf16 (h_bf16 [Pr, I]).
+ * route != NULL: experts e of w13 over their routed rows; output row b of h is
+ *   bucket position b (Pr = M*k).  route == NULL ("dense"): one expert (w13
+ *   holds E = 1) over all M rows in order (Pr = M); used for the shared expert.
+ * Workspace: moe_gate_up_workspace_bytes(...) bytes (may be 0), 256-byte
+ *   aligned; no initialization needed. */
+size_t moe_gate_up_workspace_bytes(int fmt, int M, int H, int I, int E, int k, int dense);
+int moe_expert_gate_up(const moe_weights *w13, const uint8_t *a_q, const uint8_t *a_s,
+                       const uint16_t *a_bf16, const moe_routing *route, int M, int H, int I,
+                       int E, int k, uint8_t *h_q, uint8_t *h_s, uint16_t *h_bf16,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_down — down GEMM y = h W2^T per routed pair (or per row, dense).
+ *   Pages: README DeepSeek-V4.1 slot table, row "Routed experts (moe)" (the
+ *   second block-scaled GEMM); README Qwen3.5 slot table, row "mkm" (FC2).
+ * h is what moe_expert_gate_up wrote (MXFP8 h_q/h_s for FP4 weights, h_bf16
+ * for BF16).  y: fp32 [M*k, H] indexed by pair id (route != NULL) or fp32
+ * [M, H] by row (dense).  Exact products, fp32 sums. */
+int moe_expert_down(const moe_weights *w2, const uint8_t *h_q, const uint8_t *h_s,
+                    const uint16_t *h_bf16, const moe_routing *route, int M, int H, int I,
+                    int E, int k, float *y, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_finalize_rmsnorm — top-k weighted sum of the expert outputs fused with
+ * the shared-expert add, the residual add and RMSNorm.
+ *   Pages: README DeepSeek-V4.1 slot table, rows "MoE all-reduce + mHC post +
+ *   next norm (hop_b)" and "two_shot" (finalize folded with the shared-expert
+ *   add); README Qwen3.5 slot table, row "hop" (fused residual add + RMSNorm);
+ *   SGLang Spark GB10 Optimizations, section 1 (routed scaling in the MoE sum).
+ * t = residual + y_sh + sum_j topk_w[r,j] * y[r*k+j] (fp32); residual_out =
+ * bf16(t) (round to nearest even); out = bf16(r' * rsqrt(mean(r'^2) + eps) *
+ * gamma) with r' = residual_out.
+ * y: fp32 [M*k, H]; topk_w: fp32 [M, k]; y_sh: fp32 [M, H] or NULL; residual,
+ * out: bf16 [M, H] (residual may alias out or residual_out, row by row); gamma:
+ * bf16 [H]; residual_out: bf16 [M, H] or NULL. */
+int moe_finalize_rmsnorm(const float *y, const float *topk_w, const float *y_sh,
+                         const uint16_t *residual, const uint16_t *gamma, float eps, int M,
+                         int H, int k, uint16_t *out, uint16_t *residual_out,
+                         hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_layer — the whole layer (all steps above) in one call on one stream.
+ *   Pages: README Qwen3.5 slot table, row "mkm" (top-k, FC1, SwiGLU, requant
+ *   and FC2 as one unit); README "Design" (built at load, nothing allocated
+ *   in a step, coverage decided by row count alone).
+ * x: bf16 [M, H]; residual: bf16 [M, H] (may equal x); out: bf16 [M, H];
+ * residual_out: bf16 [M, H] or NULL.  Optional debug outputs (NULL to skip):
+ * logits_out fp32 [M, E], topk_ids_out int32 [M, k], topk_w_out fp32 [M, k].
+ * Workspace: moe_layer_workspace_bytes(desc) bytes, 256-byte aligned; no
+ * initialization needed; one workspace must not be used by two calls that
+ * overlap in time. */
+size_t moe_layer_workspace_bytes(const moe_layer_desc *desc);
+int moe_layer(const moe_layer_desc *desc, const uint16_t *x, const uint16_t *residual,
+              uint16_t *out, uint16_t *residual_out, float *logits_out, int32_t *topk_ids_out,
+              float *topk_w_out, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,125 @@
+"""CPU-side checks of the C ABI: the HIP library loads, exports every symbol
+include/moe.h declares, and its host-side validation refuses bad arguments
+before touching the GPU (no compute call is made here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from block_scaled_fp4_sigmoid_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.fail("libmoe_mi355.so is not built (run __graft_entry__.build())")
+    return moe.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    declared = _declared()
+    assert set(declared) == set(moe.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(L):
+    assert moe.abi_version() == 1
+    for rc in range(5):
+        assert len(moe.status_str(rc)) > 0
+    assert "unknown" in moe.status_str(99)
+
+
+def test_tile_capacity_bound():
+    for M, E, k in [(4, 16, 4), (8, 256, 8), (384, 256, 8), (48, 512, 10), (1, 1, 1)]:
+        P = M * k
+        assert moe.tile_capacity(M, E, k) == (P + 7) // 8 + min(E, P)
+    assert moe.tile_capacity(0, 4, 1) == 0
+
+
+def test_workspace_sizes(L):
+    assert L.moe_route_workspace_bytes(8, 7168, 256, 8) > 0
+    assert L.moe_route_workspace_bytes(8, 100, 256, 8) == 0          # H % 128
+    assert L.moe_route_workspace_bytes(8, 7168, 2048, 8) == 0        # E > 1024
+    assert L.moe_route_workspace_bytes(8, 7168, 16, 17) == 0         # k > E
+    assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_BF16, 8, 7168, 256, 1, 1, 1) > 0
+    assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_MXFP4, 8, 7168, 256, 1, 1, 1) == 0
+
+
+def _desc(**over):
+    d = dict(M=8, H=1024, E=16, k=4, I=512, I_sh=0, routed_scale=1.0, eps=1e-6,
+             w_router=0x1000, router_bias=None,
+             w13=moe.moe_weights(moe.MOE_FMT_MXFP4, 0x1000, 0x1000, None),
+             w2=moe.moe_weights(moe.MOE_FMT_MXFP4, 0x1000, 0x1000, None),
+             sh13=moe.moe_weights(0, None, None, None), sh2=moe.moe_weights(0, None, None, None),
+             gamma=0x1000)
+    d.update(over)
+    return moe.moe_layer_desc(**d)
+
+
+def test_layer_desc_validation(L):
+    ok = _desc()
+    assert L.moe_layer_workspace_bytes(C.byref(ok)) > 0
+    bad = [
+        _desc(H=1000),                                   # H % 128
+        _desc(I=500),                                    # I % 128
+        _desc(k=0),
+        _desc(k=17),                                     # k > E
+        _desc(E=1025),
+        _desc(M=5000),
+        _desc(w_router=None),
+        _desc(gamma=None),
+        _desc(w13=moe.moe_weights(moe.MOE_FMT_NVFP4, 0x1000, 0x1000, None)),  # NV without global
+        _desc(w13=moe.moe_weights(moe.MOE_FMT_NVFP4, 0x1000, 0x1000, 0x1000)),  # w13/w2 formats differ
+        _desc(I_sh=256, sh13=moe.moe_weights(moe.MOE_FMT_BF16, 0x1000, None, None)),  # sh13/sh2 differ
+        _desc(I_sh=100, sh13=moe.moe_weights(moe.MOE_FMT_BF16, 0x1000, None, None),
+              sh2=moe.moe_weights(moe.MOE_FMT_BF16, 0x1000, None, None)),
+        _desc(w13=moe.moe_weights(moe.MOE_FMT_BF16, 0x1000, None, None),
+              w2=moe.moe_weights(moe.MOE_FMT_BF16, 0x1000, None, None)),  # bf16 routed experts
+    ]
+    for d in bad:
+        assert L.moe_layer_workspace_bytes(C.byref(d)) == 0
+
+
+def test_calls_refuse_before_enqueueing(L):
+    """Every refusal returns before any HIP call, so these run without a GPU."""
+    d = _desc()
+    rc = L.moe_layer(C.byref(d), None, None, None, None, None, None, None, None, 0, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+    rc = L.moe_layer(C.byref(d), 0x1000, 0x1000, 0x1000, None, None, None, None, None, 0, None)
+    assert rc == moe.MOE_ERR_WORKSPACE
+    rc = L.moe_layer(C.byref(d), 0x1000, 0x1000, 0x1000, None, None, None, None, 0x1010, 1 << 30, None)
+    assert rc == moe.MOE_ERR_WORKSPACE                     # misaligned
+    rc = L.moe_layer(C.byref(d), 0x1000, 0x1000, 0x1000, None, None, None, None, 0x1000, 16, None)
+    assert rc == moe.MOE_ERR_WORKSPACE                     # too small
+    assert L.moe_quant_act_mxfp8(None, 4, 64, 0x1000, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quant_act_mxfp8(0x1000, 4, 48, 0x1000, 0x1000, None) == moe.MOE_ERR_UNSUPPORTED
+    r = moe.moe_routing(*([0x1000] * 10))
+    # both x and logits_in, or neither
+    assert L.moe_route_topk(None, None, None, None, 4, 128, 8, 2, 1.0, None, C.byref(r), 0x1000,
+                            1 << 20, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(0x1000, 0x1000, 0x1000, None, 4, 128, 8, 2, 1.0, 0x1000, C.byref(r),
+                            0x1000, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
+    # x without logits_out
+    assert L.moe_route_topk(0x1000, None, 0x1000, None, 4, 128, 8, 2, 1.0, None, C.byref(r), 0x1000,
+                            1 << 20, None) == moe.MOE_ERR_INVALID_ARG
+    r_bad = moe.moe_routing(*([0x1000] * 9 + [None]))
+    assert L.moe_route_topk(None, 0x1000, None, None, 4, 128, 8, 2, 1.0, None, C.byref(r_bad),
+                            0x1000, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
+    w = moe.moe_weights(moe.MOE_FMT_BF16, 0x1000, None, None)
+    # bf16 weights are only supported densely (shared expert)
+    assert L.moe_expert_gate_up(C.byref(w), None, None, 0x1000, C.byref(r), 4, 128, 128, 8, 2, None,
+                                None, 0x1000, 0x1000, 1 << 20, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_down(C.byref(w), None, None, 0x1000, None, 4, 128, 100, 1, 1, 0x1000,
+                             None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_finalize_rmsnorm(0x1000, 0x1000, None, 0x1000, 0x1000, -1.0, 4, 128, 2, 0x1000,
+                                  None, None) == moe.MOE_ERR_INVALID_ARG

@@ -1,0 +1,140 @@
+"""GPU parity of the fused layer (moe_layer) against the oracle at the five
+workload shapes and at edge shapes, plus the layer's invariants: repeated
+launches bitwise identical, any row order gives the same bytes per row, and
+HIP-graph replay equals eager execution."""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_fp4_sigmoid_amd import moe, staging, synth
+from tests.parity import (DEV, MAX_ABS_MAX, REL_L2_MAX, LayerRun, compare_layer, np_of,
+                          sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+# rows the oracle recomputes per workload (all rows where that is cheap)
+SAMPLES = {
+    "tiny-m4-h1024-e16-k4-mxfp4": 4,
+    "verify-m8-h7168-e256-k8-nvfp4": 8,
+    "decode-m16-h7168-e384-k8-mxfp4": 6,
+    "skew-m48-h4096-e512-k10-nvfp4": 10,
+    "wide-m384-h7168-e256-k8-mxfp4": 6,
+}
+
+_cache = {}
+
+
+def _workload(name):
+    if name not in _cache:
+        _cache.clear()
+        torch.cuda.empty_cache()
+        inp = synth.make_inputs(name, seed=synth.WORKLOAD_ORDER.index(name) + 1)
+        _cache[name] = (inp, staging.to_device(inp, DEV))
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_layer_parity_workload(name):
+    inp, d = _workload(name)
+    print(f"[layer parity] {name}", flush=True)
+    run = LayerRun(d)
+    rows = sample_rows(inp.shape.M, SAMPLES[name], seed=1)
+    if name.startswith("skew"):
+        # include the rows of the hottest experts (multi-tile experts)
+        ids = np_of(run.ids)
+        hot = np.bincount(ids.ravel(), minlength=inp.shape.E).argsort()[::-1][:2]
+        extra = [int(np.nonzero((ids == e).any(axis=1))[0][0]) for e in hot]
+        rows = np.array(sorted(set(rows.tolist()) | set(extra)))
+    c = compare_layer(inp, run, rows)
+    print(f"  rows={len(rows)} rel_l2={c['rel_l2']:.3e} max_abs={c['max_abs']:.3e} "
+          f"res_rel_l2={c['res_rel_l2']:.3e} w_rel={c['w_rel']:.2e}", flush=True)
+    assert c["ids_ok"], (c["ids_gpu"], c["ids_ref"])
+    assert c["w_rel"] <= 1e-6
+    assert c["rel_l2"] <= REL_L2_MAX and c["max_abs"] <= MAX_ABS_MAX
+    assert c["res_rel_l2"] <= REL_L2_MAX
+
+
+EDGE = [
+    dict(M=1, H=128, E=1, k=1, I=128),                                  # smallest layer
+    dict(M=5, H=256, E=4, k=4, I=128, bias="normal:0.05"),               # top-k = all experts
+    dict(M=37, H=384, E=8, k=2, I=256, sfmt=synth.MXFP4, I_sh=128),     # ragged rows, shared MX
+    dict(M=70, H=256, E=3, k=2, I=128, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=256),  # >64 rows per expert
+    dict(M=9, H=512, E=64, k=6, I=384, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=128, routed_scale=2.5),
+    dict(M=130, H=128, E=2, k=1, I=128, bias="zipf:2.0"),               # one expert takes ~all rows
+]
+
+
+@pytest.mark.parametrize("case", range(len(EDGE)))
+def test_layer_parity_edge(case):
+    sh = synth.custom_shape(**EDGE[case])
+    inp = synth.make_inputs(sh, seed=100 + case, pool_rows=4096)
+    inp = synth.vary_globals(inp, 7)
+    print(f"[layer edge] {sh.name}", flush=True)
+    d = staging.to_device(inp, DEV)
+    run = LayerRun(d)
+    c = compare_layer(inp, run, np.arange(sh.M))
+    print(f"  rel_l2={c['rel_l2']:.3e} max_abs={c['max_abs']:.3e}", flush=True)
+    assert c["ids_ok"]
+    assert c["rel_l2"] <= REL_L2_MAX and c["max_abs"] <= MAX_ABS_MAX
+    assert c["res_rel_l2"] <= REL_L2_MAX
+
+
+def _small_layer(seed=3):
+    sh = synth.custom_shape(M=24, H=512, E=12, k=3, I=256, wfmt=synth.MXFP4, sfmt=synth.MXFP4,
+                            I_sh=128, bias="zipf:1.2")
+    inp = synth.make_inputs(sh, seed=seed, pool_rows=2048)
+    return inp, staging.to_device(inp, DEV)
+
+
+def test_repeated_launches_bitwise_identical():
+    inp, d = _small_layer()
+    first = LayerRun(d)
+    ref = first.host()
+    for i in range(400):
+        first.layer(d.x, d.x, first.out, first.res, first.logits, first.ids, first.w)
+    torch.cuda.synchronize()
+    h = first.host()
+    for k in ref:
+        assert np.array_equal(h[k], ref[k]), k
+    # and every one of a set of separate launches
+    for i in range(20):
+        assert np.array_equal(LayerRun(d, layer=first.layer).host()["out"], ref["out"])
+
+
+def test_row_permutation_invariance():
+    """Any order of the same rows gives the same bytes per row (different
+    8-row tile maps of the same rows)."""
+    inp, d = _small_layer(seed=4)
+    base = LayerRun(d).host()
+    rng = np.random.default_rng(0)
+    for _ in range(3):
+        perm = rng.permutation(inp.shape.M)
+        xp = d.x.view(torch.int16)[torch.from_numpy(perm).to(DEV)].contiguous()
+        run = LayerRun(d, x=xp).host()
+        assert np.array_equal(run["out"], base["out"][perm])
+        assert np.array_equal(run["res"], base["res"][perm])
+        assert np.array_equal(run["ids"], base["ids"][perm])
+
+
+def test_graph_replay_equals_eager():
+    inp, d = _small_layer(seed=5)
+    run = LayerRun(d)
+    eager = run.host()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        run.layer(d.x, d.x, run.out, run.res, run.logits, run.ids, run.w, stream=s)  # warm up on s
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            run.layer(d.x, d.x, run.out, run.res, run.logits, run.ids, run.w, stream=s)
+    for i in range(5):
+        run.out.zero_()
+        run.res.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        h = run.host()
+        for k in eager:
+            assert np.array_equal(h[k], eager[k]), (i, k)
+        # eager work between replays
+        LayerRun(d, layer=run.layer)

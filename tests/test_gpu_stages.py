@@ -1,0 +1,236 @@
+"""GPU parity of each step of the layer against the oracle, through the C ABI,
+on identical seeded inputs: quant bytes and routing bit-exact, expert GEMMs
+and finalize within bars derived from their arithmetic."""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_fp4_sigmoid_amd import moe, staging, synth
+from oracle import oracle as orc
+from tests.parity import DEV, bf16_to_f64, np_of, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16(a):
+    return torch.from_numpy(synth._bf16_trunc(np.asarray(a, np.float32)).view(np.int16)).to(DEV)
+
+
+def test_quant_mxfp8_bitexact():
+    rng = np.random.default_rng(0)
+    M, K = 37, 1024  # ragged row count
+    x = rng.standard_normal((M, K)).astype(np.float32) * np.exp2(rng.integers(-30, 30, (M, K // 32, 1))).repeat(32, 2).reshape(M, K)
+    x[0, :32] = 0.0
+    x[0, 32:64] = -0.0
+    x[1, :32] = 1e-39               # bf16 subnormals
+    x[2, 5] = np.nan
+    x[3, 70] = np.inf
+    x[4, :32] = 448 * 2.0 ** 10     # exactly at the saturation edge after scaling
+    xb = synth._bf16_trunc(x)
+    xt = torch.from_numpy(xb.view(np.int16)).to(DEV)
+    q = torch.empty((M, K), dtype=torch.uint8, device=DEV)
+    s = torch.empty((M, K // 32), dtype=torch.uint8, device=DEV)
+    moe.quant_act_mxfp8(xt, q, s)
+    torch.cuda.synchronize()
+    rq, rs = orc.mxfp8_quant_bf16(xb)
+    assert np.array_equal(np_of(s), rs)
+    assert np.array_equal(np_of(q), rq)
+
+
+ROUTE_CASES = [
+    # M, H, E, k, bias, scale
+    (4, 1024, 16, 4, "normal:0.01", 1.0),
+    (8, 7168, 256, 8, "none", 2.5),
+    (48, 4096, 512, 10, "zipf:1.2", 1.0),
+    (384, 7168, 256, 8, "none", 1.0),
+    (1, 128, 1, 1, "none", 1.0),       # E = k = 1
+    (5, 256, 7, 7, "normal:0.05", 1.0),  # k = E
+    (100, 384, 3, 2, "none", 1.0),     # few experts, many rows per expert
+    (37, 640, 1024, 32, "none", 1.0),  # largest E and k
+]
+
+
+@pytest.mark.parametrize("M,H,E,k,bias,scale", ROUTE_CASES)
+def test_route_topk_parity(M, H, E, k, bias, scale):
+    sh = synth.custom_shape(M=M, H=H, E=E, k=k, I=128, bias=bias, routed_scale=scale)
+    inp = synth.make_inputs(sh, seed=M + E, pool_rows=16)
+    x = torch.from_numpy(inp.x.view(np.int16)).to(DEV)
+    Wr = torch.from_numpy(inp.Wr).to(DEV)
+    bias_t = None if inp.bias is None else torch.from_numpy(inp.bias).to(DEV)
+    rt = moe.Routing(M, E, k, DEV)
+    logits = torch.empty((M, E), dtype=torch.float32, device=DEV)
+    moe.route_topk(rt, x=x, w_router=Wr, bias=bias_t, routed_scale=scale, logits_out=logits)
+    torch.cuda.synchronize()
+    lg = np_of(logits)
+    ref64 = orc.router_logits(inp.x, inp.Wr)
+    assert np.max(np.abs(lg - ref64)) <= 1e-5
+    r = orc.route(lg, inp.bias, k, scale)  # oracle routing on identical fp32 logits
+    assert np.array_equal(np_of(rt.topk_ids), r["ids"])
+    assert np.max(np.abs(np_of(rt.topk_w) - r["w"]) / np.abs(r["w"])) <= 1e-6
+    assert np.array_equal(np_of(rt.expert_offsets), r["offsets"])
+    assert np.array_equal(np_of(rt.bucket), r["bucket"])
+    nt = int(np_of(rt.num_tiles)[0])
+    assert nt == r["num_tiles"]
+    assert np.array_equal(np_of(rt.tile_expert)[:nt], r["tile_expert"])
+    assert np.array_equal(np_of(rt.tile_begin)[:nt], r["tile_begin"])
+    assert np.array_equal(np_of(rt.tile_rows)[:nt], r["tile_rows"])
+    counts = np.diff(r["offsets"])
+    act = np.nonzero(counts)[0]
+    na = int(np_of(rt.num_active)[0])
+    assert na == len(act) and np.array_equal(np_of(rt.active_experts)[:na], act)
+    # routing from logits_in gives the same result
+    rt2 = moe.Routing(M, E, k, DEV)
+    moe.route_topk(rt2, logits_in=logits, bias=bias_t, routed_scale=scale)
+    torch.cuda.synchronize()
+    for name in ("topk_ids", "topk_w", "expert_offsets", "bucket"):
+        assert torch.equal(getattr(rt, name), getattr(rt2, name)), name
+
+
+def _routed_setup(wfmt, M=40, H=512, E=6, k=3, I=256, seed=3, bias="zipf:1.0"):
+    sh = synth.custom_shape(M=M, H=H, E=E, k=k, I=I, wfmt=wfmt, bias=bias)
+    inp = synth.make_inputs(sh, seed=seed, pool_rows=2048)
+    inp = synth.vary_globals(inp, seed + 1)
+    d = staging.to_device(inp, DEV)
+    rt = moe.Routing(M, E, k, DEV)
+    logits = torch.empty((M, E), dtype=torch.float32, device=DEV)
+    moe.route_topk(rt, x=d.x, w_router=d.Wr, bias=d.bias, routed_scale=sh.routed_scale, logits_out=logits)
+    xq = torch.empty((M, H), dtype=torch.uint8, device=DEV)
+    xs = torch.empty((M, H // 32), dtype=torch.uint8, device=DEV)
+    moe.quant_act_mxfp8(d.x, xq, xs)
+    torch.cuda.synchronize()
+    return sh, inp, d, rt, xq, xs
+
+
+@pytest.mark.parametrize("wfmt", [synth.MXFP4, synth.NVFP4])
+def test_gate_up_routed_parity(wfmt):
+    sh, inp, d, rt, xq, xs = _routed_setup(wfmt)
+    M, H, E, k, I = sh.M, sh.H, sh.E, sh.k, sh.I
+    P = M * k
+    hq = torch.empty((P, I), dtype=torch.uint8, device=DEV)
+    hs = torch.empty((P, I // 32), dtype=torch.uint8, device=DEV)
+    moe.expert_gate_up(d.w13, M, H, I, E, k, routing=rt, a_q=xq, a_s=xs, h_q=hq, h_s=hs)
+    torch.cuda.synchronize()
+    bucket, ids = np_of(rt.bucket), np_of(rt.topk_ids).ravel()
+    a = orc.mxfp8_dequant(np_of(xq), np_of(xs))
+    ghq, ghs = np_of(hq), np_of(hs)
+    eq_bytes, tot = 0, 0
+    worst = 0.0
+    for b in range(P):
+        p = bucket[b]
+        e, r = ids[p], p // k
+        m13 = inp.w13.expert(e)
+        h = orc.gate_up(orc.Mat(m13.fmt, m13.packed, m13.scales, m13.gscale), H, I, a[r])
+        rq, rs = orc.mxfp8_quant_f64(h[None, :])
+        eq_bytes += int(np.sum(rq[0] == ghq[b])) + int(np.sum(rs[0] == ghs[b]))
+        tot += I + I // 32
+        # a flipped code is one E4M3 step at a rounding midpoint of fp32 vs fp64 h
+        hd = orc.mxfp8_dequant(ghq[b:b + 1], ghs[b:b + 1])[0]
+        worst = max(worst, rel_l2(hd, orc.mxfp8_dequant(rq, rs)[0]))
+    assert eq_bytes / tot >= 0.999, eq_bytes / tot
+    assert worst < 1e-2, worst
+
+
+@pytest.mark.parametrize("wfmt", [synth.MXFP4, synth.NVFP4])
+def test_down_routed_parity(wfmt):
+    sh, inp, d, rt, xq, xs = _routed_setup(wfmt, seed=5)
+    M, H, E, k, I = sh.M, sh.H, sh.E, sh.k, sh.I
+    P = M * k
+    hq = torch.empty((P, I), dtype=torch.uint8, device=DEV)
+    hs = torch.empty((P, I // 32), dtype=torch.uint8, device=DEV)
+    moe.expert_gate_up(d.w13, M, H, I, E, k, routing=rt, a_q=xq, a_s=xs, h_q=hq, h_s=hs)
+    y = torch.full((P, H), float("nan"), dtype=torch.float32, device=DEV)
+    moe.expert_down(d.w2, M, H, I, E, k, y, routing=rt, h_q=hq, h_s=hs)
+    torch.cuda.synchronize()
+    bucket, ids = np_of(rt.bucket), np_of(rt.topk_ids).ravel()
+    hd = orc.mxfp8_dequant(np_of(hq), np_of(hs))
+    gy = np_of(y)
+    worst = 0.0
+    for b in range(P):
+        p = bucket[b]
+        m2 = inp.w2.expert(ids[p])
+        yr = orc.down(orc.Mat(m2.fmt, m2.packed, m2.scales, m2.gscale), H, I, hd[b])
+        worst = max(worst, rel_l2(gy[p], yr))
+    assert worst < 2e-3, worst
+
+
+@pytest.mark.parametrize("sfmt", [synth.MXFP4, synth.NVFP4])
+def test_dense_fp4_expert_parity(sfmt):
+    """The shared-expert path: one FP4 expert over all rows in order."""
+    M, H, I = 23, 384, 256
+    sh = synth.custom_shape(M=M, H=H, E=1, k=1, I=128, wfmt=synth.MXFP4, sfmt=sfmt, I_sh=I)
+    inp = synth.make_inputs(sh, seed=8, pool_rows=64)
+    d = staging.to_device(inp, DEV)
+    xq = torch.empty((M, H), dtype=torch.uint8, device=DEV)
+    xs = torch.empty((M, H // 32), dtype=torch.uint8, device=DEV)
+    moe.quant_act_mxfp8(d.x, xq, xs)
+    hq = torch.empty((M, I), dtype=torch.uint8, device=DEV)
+    hs = torch.empty((M, I // 32), dtype=torch.uint8, device=DEV)
+    moe.expert_gate_up(d.sh13, M, H, I, 1, 1, routing=None, a_q=xq, a_s=xs, h_q=hq, h_s=hs)
+    y = torch.empty((M, H), dtype=torch.float32, device=DEV)
+    moe.expert_down(d.sh2, M, H, I, 1, 1, y, routing=None, h_q=hq, h_s=hs)
+    torch.cuda.synchronize()
+    a = orc.mxfp8_dequant(np_of(xq), np_of(xs))
+    m13 = orc.Mat.from_synth(inp.sh13)
+    m2 = orc.Mat.from_synth(inp.sh2)
+    ghq, ghs, gy = np_of(hq), np_of(hs), np_of(y)
+    hd = orc.mxfp8_dequant(ghq, ghs)
+    eq = 0
+    for r in range(M):
+        h = orc.gate_up(m13, H, I, a[r])
+        rq, rs = orc.mxfp8_quant_f64(h[None, :])
+        eq += int(np.sum(rq[0] == ghq[r]))
+        yr = orc.down(m2, H, I, hd[r])
+        assert rel_l2(gy[r], yr) < 2e-3
+    assert eq / (M * I) >= 0.999
+
+
+def test_dense_bf16_expert_parity():
+    M, H, I = 48, 1024, 256
+    sh = synth.custom_shape(M=M, H=H, E=1, k=1, I=128, sfmt=synth.BF16, I_sh=I)
+    inp = synth.make_inputs(sh, seed=9, pool_rows=64)
+    d = staging.to_device(inp, DEV)
+    hb = torch.empty((M, I), dtype=torch.int16, device=DEV)
+    moe.expert_gate_up(d.sh13, M, H, I, 1, 1, routing=None, a_bf16=d.x, h_bf16=hb)
+    y = torch.empty((M, H), dtype=torch.float32, device=DEV)
+    moe.expert_down(d.sh2, M, H, I, 1, 1, y, routing=None, h_bf16=hb)
+    torch.cuda.synchronize()
+    m13 = orc.Mat.from_synth(inp.sh13)
+    m2 = orc.Mat.from_synth(inp.sh2)
+    ghb = np_of(hb).view(np.uint16)
+    gy = np_of(y)
+    eq = 0
+    for r in range(M):
+        h = orc.gate_up_bf16(m13, H, I, inp.x[r])
+        hb_ref = orc.bf16_rne_n(h)
+        eq += int(np.sum(hb_ref == ghb[r]))
+        yr = orc.down(m2, H, I, bf16_to_f64(ghb[r]))
+        assert rel_l2(gy[r], yr) < 1e-5
+    assert eq / (M * I) >= 0.99
+
+
+def test_finalize_parity():
+    rng = np.random.default_rng(4)
+    M, H, k = 19, 2048 + 128, 5
+    y = rng.standard_normal((M * k, H)).astype(np.float32)
+    w = rng.random((M, k)).astype(np.float32)
+    ysh = rng.standard_normal((M, H)).astype(np.float32)
+    res = synth._bf16_trunc(rng.standard_normal((M, H)).astype(np.float32))
+    gamma = synth._bf16_trunc((1 + 0.1 * rng.standard_normal(H)).astype(np.float32))
+    t = lambda a: torch.from_numpy(a).to(DEV)
+    out = torch.empty((M, H), dtype=torch.int16, device=DEV)
+    ro = torch.empty((M, H), dtype=torch.int16, device=DEV)
+    moe.finalize_rmsnorm(t(y), t(w), t(ysh), t(res.view(np.int16)), t(gamma.view(np.int16)), 1e-6, out, ro)
+    torch.cuda.synchronize()
+    go, gr = np_of(out).view(np.uint16), np_of(ro).view(np.uint16)
+    for r in range(M):
+        o64, ob, rb = orc.finalize_row(y[r * k:(r + 1) * k].astype(np.float64), w[r],
+                                       ysh[r].astype(np.float64), res[r], gamma, 1e-6)
+        # the fp32 sum differs from the fp64 one by ~1e-7 of the summed magnitudes,
+        # so residual_out may take the neighbouring bf16 value at a rounding
+        # midpoint, or differ more where the sum cancels to near zero
+        mag = np.abs(bf16_to_f64(res[r])) + np.abs(ysh[r]) + np.abs(w[r]) @ np.abs(y[r * k:(r + 1) * k])
+        diff = np.abs(bf16_to_f64(gr[r]) - bf16_to_f64(rb))
+        allowed = np.abs(bf16_to_f64(rb)) * 2.0 ** -7 + 1e-6 * mag
+        assert np.all(diff <= allowed) and (gr[r] != rb).mean() < 0.01
+        assert rel_l2(bf16_to_f64(go[r]), o64) < 4e-3
+        assert np.max(np.abs(bf16_to_f64(go[r]) - o64)) < 3e-2
