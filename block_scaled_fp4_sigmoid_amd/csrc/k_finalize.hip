@@ -7,13 +7,14 @@
 // RMSNorm).  t = residual + y_sh + sum_j w_j y_j (fp32, slot order);
 // residual_out = bf16_rne(t); out = bf16_rne(r' * rsqrt(mean(r'^2) + eps) * gamma).
 //
-// One workgroup per row; each thread owns 8 consecutive columns per 2048.
+// One workgroup per row; each thread owns 8 consecutive columns per 8192.
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int kFinThreads = 256;
+constexpr int kFinThreads = 1024;
+constexpr int kFinChunk = kFinThreads * 8;  // columns per pass of the workgroup
 
 __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restrict__ y,
                                                           const float* __restrict__ topk_w,
@@ -24,16 +25,16 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restric
                                                           uint16_t* out, uint16_t* residual_out) {
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
-    constexpr int kMaxChunks = 8;  // H <= 16384 = 8 * 2048
+    constexpr int kMaxChunks = 2;  // H <= 16384
     float rv[kMaxChunks][8];
     float ss = 0.f;
     const float* wr = topk_w + (size_t)r * k;
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
-        const int col = c * 2048 + tid * 8;
+        const int col = c * kFinChunk + tid * 8;
         if (col < H) {
             const v4i rb = load16(residual + (size_t)r * H + col);
-            uint32_t rw[4] = {(uint32_t)rb.x, (uint32_t)rb.y, (uint32_t)rb.z, (uint32_t)rb.w};
+            const uint32_t rw[4] = {(uint32_t)rb.x, (uint32_t)rb.y, (uint32_t)rb.z, (uint32_t)rb.w};
             float t[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -46,15 +47,29 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restric
                 t[0] += a.x; t[1] += a.y; t[2] += a.z; t[3] += a.w;
                 t[4] += b.x; t[5] += b.y; t[6] += b.z; t[7] += b.w;
             }
-            for (int j = 0; j < k; ++j) {
-                const float wj = wr[j];
-                const float* yr = y + ((size_t)r * k + j) * H + col;
-                const float4 a = *reinterpret_cast<const float4*>(yr);
-                const float4 b = *reinterpret_cast<const float4*>(yr + 4);
-                t[0] = fmaf(wj, a.x, t[0]); t[1] = fmaf(wj, a.y, t[1]);
-                t[2] = fmaf(wj, a.z, t[2]); t[3] = fmaf(wj, a.w, t[3]);
-                t[4] = fmaf(wj, b.x, t[4]); t[5] = fmaf(wj, b.y, t[5]);
-                t[6] = fmaf(wj, b.z, t[6]); t[7] = fmaf(wj, b.w, t[7]);
+            // slot order; loads of four slots are issued before their adds
+            for (int j0 = 0; j0 < k; j0 += 4) {
+                float4 ya[4], yb[4];
+                float wj[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int j = j0 + u;
+                    if (j < k) {
+                        const float* yr = y + ((size_t)r * k + j) * H + col;
+                        ya[u] = *reinterpret_cast<const float4*>(yr);
+                        yb[u] = *reinterpret_cast<const float4*>(yr + 4);
+                        wj[u] = wr[j];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (j0 + u < k) {
+                        t[0] = fmaf(wj[u], ya[u].x, t[0]); t[1] = fmaf(wj[u], ya[u].y, t[1]);
+                        t[2] = fmaf(wj[u], ya[u].z, t[2]); t[3] = fmaf(wj[u], ya[u].w, t[3]);
+                        t[4] = fmaf(wj[u], yb[u].x, t[4]); t[5] = fmaf(wj[u], yb[u].y, t[5]);
+                        t[6] = fmaf(wj[u], yb[u].z, t[6]); t[7] = fmaf(wj[u], yb[u].w, t[7]);
+                    }
+                }
             }
             uint32_t ob[4];
 #pragma unroll
@@ -70,19 +85,21 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restric
                     v4i{(int)ob[0], (int)ob[1], (int)ob[2], (int)ob[3]};
         }
     }
-    // fixed-order reduction: wave butterfly, then the 4 wave sums in order
+    // fixed-order reduction: wave butterfly, then the wave sums in order
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
     __shared__ float s_part[kFinThreads / 64];
     if ((tid & 63) == 0) s_part[tid >> 6] = ss;
     __syncthreads();
-    const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kFinThreads / 64; ++w) tot += s_part[w];
     const float inv = rsqrtf(tot / (float)H + eps);
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
-        const int col = c * 2048 + tid * 8;
+        const int col = c * kFinChunk + tid * 8;
         if (col < H) {
             const v4i gb = load16(gamma + col);
-            uint32_t gw[4] = {(uint32_t)gb.x, (uint32_t)gb.y, (uint32_t)gb.z, (uint32_t)gb.w};
+            const uint32_t gw[4] = {(uint32_t)gb.x, (uint32_t)gb.y, (uint32_t)gb.z, (uint32_t)gb.w};
             uint32_t ob[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {

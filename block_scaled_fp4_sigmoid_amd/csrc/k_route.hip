@@ -24,11 +24,11 @@ namespace moe {
 RouterPlan router_plan(int M, int H, int E) {
     const int et = (E + 15) / 16;
     const int rg = (M + 63) / 64;
-    const int nsteps = H / 32;
+    const int nsteps = H / 128;  // chunks are whole multiples of 4 K-steps of 32
     const int want = std::max(1, 1024 / (et * rg));
     int splits = 1;
     for (int d = 1; d <= nsteps; ++d)
-        if (nsteps % d == 0 && d <= want) splits = d;
+        if (nsteps % d == 0 && d <= want && d <= 32) splits = d;
     return RouterPlan{splits, H / splits, rg};
 }
 
@@ -79,39 +79,48 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
     for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     const int kbeg = kc * kchunk;
-    for (int k0 = kbeg; k0 < kbeg + kchunk; k0 += 32) {
-        const int kk = k0 + 8 * g;
-        float wv[8];
-        if (ev) {
-            const float4 w0 = *reinterpret_cast<const float4*>(wrow + kk);
-            const float4 w1 = *reinterpret_cast<const float4*>(wrow + kk + 4);
-            wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
-            wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
-        } else {
+    constexpr int U = 4;  // K-steps of 32 whose loads are issued together
+    for (int k0 = kbeg; k0 < kbeg + kchunk; k0 += 32 * U) {
+        float4 wl[U][2];
+        v4i xb[U][4];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) wv[t] = 0.f;
+        for (int u = 0; u < U; ++u) {
+            const int kk = k0 + 32 * u + 8 * g;
+            if (ev) {
+                wl[u][0] = *reinterpret_cast<const float4*>(wrow + kk);
+                wl[u][1] = *reinterpret_cast<const float4*>(wrow + kk + 4);
+            } else {
+                wl[u][0] = wl[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                xb[u][j] = (j < nb && xv[j]) ? load16(xr[j] + kk) : v4i{0, 0, 0, 0};
         }
-        uint32_t p1[4], p2[4], p3[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            uint32_t a1, a2, a3, c1, c2, c3;
-            split3(wv[2 * t], a1, a2, a3);
-            split3(wv[2 * t + 1], c1, c2, c3);
-            p1[t] = a1 | (c1 << 16);
-            p2[t] = a2 | (c2 << 16);
-            p3[t] = a3 | (c3 << 16);
-        }
-        v4i A1 = {(int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
-        v4i A2 = {(int)p2[0], (int)p2[1], (int)p2[2], (int)p2[3]};
-        v4i A3 = {(int)p3[0], (int)p3[1], (int)p3[2], (int)p3[3]};
+        for (int u = 0; u < U; ++u) {
+            const float wv[8] = {wl[u][0].x, wl[u][0].y, wl[u][0].z, wl[u][0].w,
+                                 wl[u][1].x, wl[u][1].y, wl[u][1].z, wl[u][1].w};
+            uint32_t p1[4], p2[4], p3[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j < nb) {
-                v4i B = xv[j] ? load16(xr[j] + kk) : v4i{0, 0, 0, 0};
-                const v8bf b = __builtin_bit_cast(v8bf, B);
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, A1), b, acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, A2), b, acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, A3), b, acc[j], 0, 0, 0);
+            for (int t = 0; t < 4; ++t) {
+                uint32_t a1, a2, a3, c1, c2, c3;
+                split3(wv[2 * t], a1, a2, a3);
+                split3(wv[2 * t + 1], c1, c2, c3);
+                p1[t] = a1 | (c1 << 16);
+                p2[t] = a2 | (c2 << 16);
+                p3[t] = a3 | (c3 << 16);
+            }
+            const v8bf A1 = __builtin_bit_cast(v8bf, v4i{(int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]});
+            const v8bf A2 = __builtin_bit_cast(v8bf, v4i{(int)p2[0], (int)p2[1], (int)p2[2], (int)p2[3]});
+            const v8bf A3 = __builtin_bit_cast(v8bf, v4i{(int)p3[0], (int)p3[1], (int)p3[2], (int)p3[3]});
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j < nb) {
+                    const v8bf b = __builtin_bit_cast(v8bf, xb[u][j]);
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, b, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3, b, acc[j], 0, 0, 0);
+                }
             }
         }
     }
@@ -152,8 +161,7 @@ hipError_t launch_zero_ints(int* p, int n, hipStream_t stream) {
 // Top-k: one wave per row (the pages' one CTA per row).  Each lane holds up to
 // 16 experts (e = lane + 64 t).  Scores are fp64 sigmoids of the fp32 logits;
 // keys add the optional selection bias; k rounds of a wave-wide arg-max with
-// (key descending, expert ascending) order pick the slots.  The last
-// workgroup to finish then builds the expert buckets and 8-row tiles.
+// (key descending, expert ascending) order pick the slots.
 
 __device__ __forceinline__ bool key_better(double ka, int ea, double kb, int eb) {
     return ka > kb || (ka == kb && ea < eb);
@@ -185,45 +193,54 @@ __device__ void block_exclusive_scan(int* data, int* scratch, int& total) {
     __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void k_topk_bucket(const float* __restrict__ partials, int splits,
-                                                     const float* __restrict__ bias, int M, int E,
-                                                     int k, float routed_scale,
-                                                     float* __restrict__ logits_out,
-                                                     moe_routing route, int* __restrict__ counter) {
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int r = blockIdx.x * 4 + wave;
-    if (r < M) {
-        double key[16], sc[16];
-        uint32_t avail = 0;
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials, int splits,
+                                              const float* __restrict__ bias, int M, int E, int k,
+                                              float routed_scale, float* __restrict__ logits_out,
+                                              moe_routing route) {
+    // One workgroup per row.  Phase 1: every thread owns experts tid + 256q,
+    // sums their partial logits in chunk order (loads issued 8 at a time) and
+    // stores the fp64 score and key in LDS.  Phase 2: wave 0 picks the k slots.
+    __shared__ double s_key[kMaxE];
+    __shared__ double s_sc[kMaxE];
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += 256) {
+        float lg = 0.f;
+        for (int c0 = 0; c0 < splits; c0 += 8) {
+            float p[8];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const int e = lane + 64 * t;
-            key[t] = 0.0;
-            sc[t] = 0.0;
-            if (e < E) {
-                float lg = partials[(size_t)r * E + e];
-                for (int c = 1; c < splits; ++c) lg += partials[((size_t)c * M + r) * E + e];
-                if (logits_out) logits_out[(size_t)r * E + e] = lg;
-                const double s = 1.0 / (1.0 + exp(-(double)lg));
-                sc[t] = s;
-                key[t] = s + (bias ? (double)bias[e] : 0.0);
-                avail |= 1u << t;
+            for (int u = 0; u < 8; ++u) {
+                const int c = c0 + u;
+                p[u] = c < splits ? partials[((size_t)c * M + r) * E + e] : 0.f;
             }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (c0 + u < splits) lg = (c0 + u == 0) ? p[u] : lg + p[u];
         }
+        if (logits_out) logits_out[(size_t)r * E + e] = lg;
+        const double sc = 1.0 / (1.0 + exp(-(double)lg));
+        s_sc[e] = sc;
+        s_key[e] = sc + (bias ? (double)bias[e] : 0.0);
+    }
+    __syncthreads();
+    if (tid < 64) {
+        const int lane = tid;
+        uint32_t avail = 0;
+        for (int t = 0; t < 16; ++t)
+            if (lane + 64 * t < E) avail |= 1u << t;
         int my_id = 0;
         double my_s = 0.0;
         for (int j = 0; j < k; ++j) {
             bool have = false;
             double bk = 0.0;
             int be = 0x7fffffff;
-#pragma unroll
             for (int t = 0; t < 16; ++t) {
                 if ((avail >> t) & 1u) {
                     const int e = lane + 64 * t;
-                    if (!have || key_better(key[t], e, bk, be)) {
+                    const double kv = s_key[e];
+                    if (!have || key_better(kv, e, bk, be)) {
                         have = true;
-                        bk = key[t];
+                        bk = kv;
                         be = e;
                     }
                 }
@@ -239,18 +256,10 @@ __global__ __launch_bounds__(256) void k_topk_bucket(const float* __restrict__ p
                     be = oe;
                 }
             }
-            double s_sel = 0.0;
-            if ((be & 63) == lane) {
-                const int tt = be >> 6;
-#pragma unroll
-                for (int t = 0; t < 16; ++t)
-                    if (t == tt) s_sel = sc[t];
-                avail &= ~(1u << tt);
-            }
-            const double sj = __shfl(s_sel, be & 63, 64);
+            if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
             if (lane == j) {
                 my_id = be;
-                my_s = sj;
+                my_s = s_sc[be];
             }
         }
         double sum = 0.0;
@@ -261,26 +270,27 @@ __global__ __launch_bounds__(256) void k_topk_bucket(const float* __restrict__ p
         }
     }
 
-    // ---- last workgroup: buckets and tiles ----
-    __shared__ int s_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = (atomicAdd(counter, 1) == (int)gridDim.x - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+}
+
+
+
+// ---------------------------------------------------------------------------
+// Route step: one workgroup builds the expert buckets, 8-row tiles and the
+// active-expert list from topk_ids (a separate launch, so the ids written by
+// the top-k workgroups are visible without a device-scope fence).
+__global__ __launch_bounds__(kBucketThreads) void k_bucket(int M, int E, int k, moe_routing route) {
+    const int tid = threadIdx.x;
 
     __shared__ int s_cnt[kMaxE], s_off[kMaxE], s_tile[kMaxE], s_act[kMaxE], s_run[kMaxE];
     __shared__ uint32_t s_bm[kMaxE * 4];
     __shared__ int s_scan[kBucketThreads];
-    const int tid = threadIdx.x;
     const int P = M * k;
     for (int e = tid; e < kMaxE; e += kBucketThreads) {
         s_cnt[e] = 0;
         s_run[e] = 0;
     }
     __syncthreads();
-    for (int p = tid; p < P; p += kBucketThreads) atomicAdd(&s_cnt[load_agent(route.topk_ids + p)], 1);
+    for (int p = tid; p < P; p += kBucketThreads) atomicAdd(&s_cnt[route.topk_ids[p]], 1);
     __syncthreads();
     for (int e = tid; e < kMaxE; e += kBucketThreads) {
         const int c = s_cnt[e];
@@ -321,7 +331,7 @@ __global__ __launch_bounds__(256) void k_topk_bucket(const float* __restrict__ p
         const bool valid = tid < R * k && p < P;
         int e = 0, rl = 0;
         if (valid) {
-            e = load_agent(route.topk_ids + p);
+            e = route.topk_ids[p];
             rl = p / k - r0;
             atomicOr(&s_bm[e * W + (rl >> 5)], 1u << (rl & 31));
         }
@@ -340,15 +350,17 @@ __global__ __launch_bounds__(256) void k_topk_bucket(const float* __restrict__ p
         }
         __syncthreads();
     }
-    if (tid == 0) *counter = 0;
 }
 
 hipError_t launch_topk_bucket(const float* partials, int splits, const float* bias, int M, int E,
                               int k, float routed_scale, float* logits_out,
                               const moe_routing& route, int* counter, hipStream_t stream) {
-    const int blocks = (M + 3) / 4;
-    hipLaunchKernelGGL(k_topk_bucket, dim3(blocks), dim3(256), 0, stream, partials, splits, bias,
-                       M, E, k, routed_scale, logits_out, route, counter);
+    (void)counter;
+    hipLaunchKernelGGL(k_topk, dim3(M), dim3(256), 0, stream, partials, splits, bias,
+                       M, E, k, routed_scale, logits_out, route);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBucketThreads), 0, stream, M, E, k, route);
     return hipGetLastError();
 }
 

@@ -182,7 +182,7 @@ size_t moe_gate_up_workspace_bytes(int fmt, int M, int H, int I, int E, int k, i
     (void)E;
     (void)k;
     if (fmt != MOE_FMT_BF16 || !dense || M < 1 || H < 128 || I < 32) return 0;
-    return align_up((size_t)(I / 32) * sizeof(int)) + gate_up_bf16_partials_bytes(M, H, I);
+    return gate_up_bf16_partials_bytes(M, H, I);
 }
 
 int moe_expert_gate_up(const moe_weights* w13, const uint8_t* a_q, const uint8_t* a_s,
@@ -198,13 +198,8 @@ int moe_expert_gate_up(const moe_weights* w13, const uint8_t* a_q, const uint8_t
         if (!w13->w || !a_bf16 || !h_bf16) return MOE_ERR_INVALID_ARG;
         const size_t need = moe_gate_up_workspace_bytes(MOE_FMT_BF16, M, H, I, 1, 1, 1);
         if (!workspace || !aligned256(workspace) || workspace_bytes < need) return MOE_ERR_WORKSPACE;
-        Carver c(workspace);
-        int* counters = c.take<int>(I / 32);
-        float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + c.off);
-        hipError_t e = launch_zero_ints(counters, I / 32, stream);
-        if (e == hipSuccess)
-            e = launch_gate_up_bf16(dense_job(*w13, I, H, M), a_bf16, h_bf16, part, counters, stream);
-        return hip_status(e);
+        float* part = static_cast<float*>(workspace);
+        return hip_status(launch_gate_up_bf16(dense_job(*w13, I, H, M), a_bf16, h_bf16, part, stream));
     }
     if (int st = check_fp4_weights(w13)) return st;
     if (!a_q || !a_s || !h_q || !h_s) return MOE_ERR_INVALID_ARG;
@@ -273,7 +268,6 @@ int check_desc(const moe_layer_desc* d) {
 
 struct LayerWs {
     RouteWs route;
-    int* sh_counters;
     int32_t *ids, *offsets, *bucket, *tile_e, *tile_b, *tile_r, *num_tiles, *active, *num_active;
     float* w;
     uint8_t *xq, *xs, *hq, *hs, *hsq, *hss;
@@ -289,8 +283,7 @@ LayerWs carve_layer(Carver& c, const moe_layer_desc* d) {
     const int T = moe_tile_capacity(M, E, k);
     const bool sh = d->sh13.fmt != MOE_FMT_NONE;
     const bool shb = d->sh13.fmt == MOE_FMT_BF16;
-    L.route = carve_route(c, M, H, E, shb ? Ish / 32 : 0);
-    L.sh_counters = L.route.counters ? L.route.counters + kRouteCounters : nullptr;
+    L.route = carve_route(c, M, H, E, 0);
     L.ids = c.take<int32_t>(P);
     L.w = c.take<float>(P);
     L.offsets = c.take<int32_t>(E + 1);
@@ -355,9 +348,8 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
     r.num_active = L.num_active;
 
     const RouterPlan p = router_plan(M, H, E);
-    const int ncount = kRouteCounters + (sf == MOE_FMT_BF16 ? Ish / 32 : 0);
     hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials,
-                                          L.route.counters, ncount, stream);
+                                          L.route.counters, kRouteCounters, stream);
     if (e == hipSuccess)
         e = launch_topk_bucket(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale,
                                logits_out, r, L.route.counters, stream);
@@ -365,7 +357,7 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
     const ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
     if (e == hipSuccess) e = launch_gate_up_fp4(gu, L.xq, L.xs, L.hq, L.hs, stream);
     if (e == hipSuccess && sf == MOE_FMT_BF16)
-        e = launch_gate_up_bf16(dense_job(d->sh13, Ish, H, M), x, L.hsb, L.sh_part, L.sh_counters, stream);
+        e = launch_gate_up_bf16(dense_job(d->sh13, Ish, H, M), x, L.hsb, L.sh_part, stream);
     else if (e == hipSuccess && sf != MOE_FMT_NONE)
         e = launch_gate_up_fp4(dense_job(d->sh13, Ish, H, M), L.xq, L.xs, L.hsq, L.hss, stream);
     const ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);

@@ -56,11 +56,10 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
 hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8_t* h_s,
                            float* y, hipStream_t stream);
 
-// bf16 split-K partials; the counters (I/32 ints) live separately and must be
-// zero when the kernel starts (the last workgroup of each block re-zeroes its own).
+// bf16 shared expert: split-K partials (workspace), reduced by a second launch.
 size_t gate_up_bf16_partials_bytes(int M, int H, int I);
 hipError_t launch_gate_up_bf16(const ExpertJob& job, const uint16_t* a, uint16_t* h,
-                               float* partials, int* counters, hipStream_t stream);
+                               float* partials, hipStream_t stream);
 hipError_t launch_down_bf16(const ExpertJob& job, const uint16_t* h, float* y, hipStream_t stream);
 
 hipError_t launch_finalize(const float* y, const float* topk_w, const float* y_sh,

@@ -101,9 +101,11 @@ def _routed_setup(wfmt, M=40, H=512, E=6, k=3, I=256, seed=3, bias="zipf:1.0"):
     return sh, inp, d, rt, xq, xs
 
 
-@pytest.mark.parametrize("wfmt", [synth.MXFP4, synth.NVFP4])
-def test_gate_up_routed_parity(wfmt):
-    sh, inp, d, rt, xq, xs = _routed_setup(wfmt)
+@pytest.mark.parametrize("wfmt,H", [(synth.MXFP4, 512), (synth.NVFP4, 512),
+                                    (synth.MXFP4, 2560), (synth.NVFP4, 2560)])
+def test_gate_up_routed_parity(wfmt, H):
+    # H = 512 is one K chunk; 2560 is five (exercises the weight ring and LDS buffers)
+    sh, inp, d, rt, xq, xs = _routed_setup(wfmt, H=H)
     M, H, E, k, I = sh.M, sh.H, sh.E, sh.k, sh.I
     P = M * k
     hq = torch.empty((P, I), dtype=torch.uint8, device=DEV)
@@ -130,9 +132,11 @@ def test_gate_up_routed_parity(wfmt):
     assert worst < 1e-2, worst
 
 
-@pytest.mark.parametrize("wfmt", [synth.MXFP4, synth.NVFP4])
-def test_down_routed_parity(wfmt):
-    sh, inp, d, rt, xq, xs = _routed_setup(wfmt, seed=5)
+@pytest.mark.parametrize("wfmt,I", [(synth.MXFP4, 256), (synth.NVFP4, 256),
+                                    (synth.MXFP4, 1536), (synth.NVFP4, 1536)])
+def test_down_routed_parity(wfmt, I):
+    # I = 256 fits one chunk (two row blocks per wave); 1536 is three chunks
+    sh, inp, d, rt, xq, xs = _routed_setup(wfmt, seed=5, I=I)
     M, H, E, k, I = sh.M, sh.H, sh.E, sh.k, sh.I
     P = M * k
     hq = torch.empty((P, I), dtype=torch.uint8, device=DEV)
@@ -184,8 +188,8 @@ def test_dense_fp4_expert_parity(sfmt):
     assert eq / (M * I) >= 0.999
 
 
-def test_dense_bf16_expert_parity():
-    M, H, I = 48, 1024, 256
+@pytest.mark.parametrize("M,H,I", [(48, 1024, 256), (8, 7168, 256), (48, 4096, 512)])
+def test_dense_bf16_expert_parity(M, H, I):
     sh = synth.custom_shape(M=M, H=H, E=1, k=1, I=128, sfmt=synth.BF16, I_sh=I)
     inp = synth.make_inputs(sh, seed=9, pool_rows=64)
     d = staging.to_device(inp, DEV)
