@@ -179,10 +179,15 @@ int moe_quant_act_mxfp8(const uint16_t* x, int M, int K, uint8_t* q, uint8_t* s,
 }
 
 size_t moe_gate_up_workspace_bytes(int fmt, int M, int H, int I, int E, int k, int dense) {
-    (void)E;
-    (void)k;
-    if (fmt != MOE_FMT_BF16 || !dense || M < 1 || H < 128 || I < 32) return 0;
-    return gate_up_bf16_partials_bytes(M, H, I);
+    if (check_dims(M, H, dense ? 1 : E, dense ? 1 : k) != MOE_OK) return 0;
+    if (I < 128 || I % 128 != 0 || I > kMaxI) return 0;
+    if (fmt == MOE_FMT_BF16) return dense ? gate_up_bf16_partials_bytes(M, H, I) : 0;
+    if (fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_NVFP4) return 0;
+    moe_weights w{};
+    w.fmt = fmt;
+    moe_routing r{};
+    const ExpertJob job = dense ? dense_job(w, I, H, M) : routed_job(w, I, H, r, M, E, k);
+    return gate_up_fp4_partials_bytes(job);
 }
 
 int moe_expert_gate_up(const moe_weights* w13, const uint8_t* a_q, const uint8_t* a_s,
@@ -206,7 +211,9 @@ int moe_expert_gate_up(const moe_weights* w13, const uint8_t* a_q, const uint8_t
     if (!dense)
         if (int st = check_routing(route)) return st;
     const ExpertJob job = dense ? dense_job(*w13, I, H, M) : routed_job(*w13, I, H, *route, M, E, k);
-    return hip_status(launch_gate_up_fp4(job, a_q, a_s, h_q, h_s, stream));
+    const size_t need = gate_up_fp4_partials_bytes(job);
+    if (need && (!workspace || !aligned256(workspace) || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+    return hip_status(launch_gate_up_fp4(job, a_q, a_s, h_q, h_s, static_cast<float*>(workspace), stream));
 }
 
 int moe_expert_down(const moe_weights* w2, const uint8_t* h_q, const uint8_t* h_s,
@@ -273,6 +280,8 @@ struct LayerWs {
     uint8_t *xq, *xs, *hq, *hs, *hsq, *hss;
     uint16_t* hsb;
     float* sh_part;
+    float* part;     // routed gate_up split-K partials
+    float* sh_fpart; // FP4 shared gate_up split-K partials
     float *y, *ysh;
 };
 
@@ -309,6 +318,14 @@ LayerWs carve_layer(Carver& c, const moe_layer_desc* d) {
         L.hsb = c.take<uint16_t>((size_t)M * Ish);
         L.sh_part = c.take<float>(gate_up_bf16_partials_bytes(M, H, Ish) / sizeof(float));
     }
+    {
+        moe_weights w = d->w13;
+        moe_routing r{};
+        L.part = c.take<float>(gate_up_fp4_partials_bytes(routed_job(w, I, H, r, M, E, k)) / sizeof(float));
+    }
+    L.sh_fpart = nullptr;
+    if (sh && !shb)
+        L.sh_fpart = c.take<float>(gate_up_fp4_partials_bytes(dense_job(d->sh13, Ish, H, M)) / sizeof(float));
     L.y = c.take<float>((size_t)P * H);
     L.ysh = sh ? c.take<float>((size_t)M * H) : nullptr;
     return L;
@@ -355,11 +372,11 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
                                logits_out, r, L.route.counters, stream);
     if (e == hipSuccess) e = launch_quant_mxfp8(x, M, H, L.xq, L.xs, stream);
     const ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
-    if (e == hipSuccess) e = launch_gate_up_fp4(gu, L.xq, L.xs, L.hq, L.hs, stream);
+    if (e == hipSuccess) e = launch_gate_up_fp4(gu, L.xq, L.xs, L.hq, L.hs, L.part, stream);
     if (e == hipSuccess && sf == MOE_FMT_BF16)
         e = launch_gate_up_bf16(dense_job(d->sh13, Ish, H, M), x, L.hsb, L.sh_part, stream);
     else if (e == hipSuccess && sf != MOE_FMT_NONE)
-        e = launch_gate_up_fp4(dense_job(d->sh13, Ish, H, M), L.xq, L.xs, L.hsq, L.hss, stream);
+        e = launch_gate_up_fp4(dense_job(d->sh13, Ish, H, M), L.xq, L.xs, L.hsq, L.hss, L.sh_fpart, stream);
     const ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);
     if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream);
     if (e == hipSuccess && sf == MOE_FMT_BF16)

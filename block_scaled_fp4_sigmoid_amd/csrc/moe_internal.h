@@ -51,8 +51,12 @@ struct ExpertJob {
     int M;
 };
 
+// gate_up over FP4 experts.  When the plan splits K, fp32 partials go to
+// `partials` (gate_up_fp4_partials_bytes; 0 means no split and no buffer) and a
+// second launch reduces them, applies SwiGLU and requantizes h.
+size_t gate_up_fp4_partials_bytes(const ExpertJob& job);
 hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const uint8_t* a_s,
-                              uint8_t* h_q, uint8_t* h_s, hipStream_t stream);
+                              uint8_t* h_q, uint8_t* h_s, float* partials, hipStream_t stream);
 hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8_t* h_s,
                            float* y, hipStream_t stream);
 

@@ -52,7 +52,13 @@ def test_workspace_sizes(L):
     assert L.moe_route_workspace_bytes(8, 7168, 2048, 8) == 0        # E > 1024
     assert L.moe_route_workspace_bytes(8, 7168, 16, 17) == 0         # k > E
     assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_BF16, 8, 7168, 256, 1, 1, 1) > 0
-    assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_MXFP4, 8, 7168, 256, 1, 1, 1) == 0
+    # FP4: a K split (few items) needs fp32 partials [splits][rows][2I]; one split needs none
+    few = L.moe_gate_up_workspace_bytes(moe.MOE_FMT_MXFP4, 8, 7168, 256, 1, 1, 1)
+    assert few > 0 and few % (8 * 2 * 256 * 4) == 0 and few % 256 == 0
+    assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_NVFP4, 8, 7168, 256, 256, 8, 0) > 0
+    assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_MXFP4, 4, 1024, 512, 16, 4, 0) == 0
+    assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_MXFP4, 8, 100, 256, 1, 1, 1) == 0   # H % 128
+    assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_BF16, 8, 7168, 256, 256, 8, 0) == 0  # bf16 routed
 
 
 def _desc(**over):
