@@ -15,8 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_mi355.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["k_route.hip", "k_quant.hip", "k_stream.hip", "k_dense_bf16.hip", "k_finalize.hip",
-           "moe_api.cpp"]
+SOURCES = ["k_route.hip", "k_quant.hip", "k_pack.hip", "k_stream.hip", "k_dense_bf16.hip",
+           "k_finalize.hip", "moe_api.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -9,17 +9,19 @@
 // One thread per 32-value block: 64 bytes in (four 16-byte loads), 32 bytes +
 // one scale byte out.  amax comes from the bf16 bit patterns (integer max of
 // the magnitudes, exact for subnormals too).
+//
+// The layer quantizes straight into bucket order (row of bucket position b =
+// the token of pair bucket[b]), so the expert GEMMs find an expert's rows
+// contiguous; a gather does the same for token-ordered codes.
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 
-__global__ __launch_bounds__(256) void k_quant_mxfp8(const uint16_t* __restrict__ x, int nblocks,
-                                                     uint8_t* __restrict__ q,
-                                                     uint8_t* __restrict__ s) {
-    const int b = blockIdx.x * 256 + threadIdx.x;
-    if (b >= nblocks) return;
-    const v4i* src = reinterpret_cast<const v4i*>(x + (size_t)b * 32);
+// One 32-value block: src -> 32 codes at q, scale code at *s.
+__device__ __forceinline__ void quant_block32(const uint16_t* __restrict__ xsrc, uint8_t* __restrict__ qdst,
+                                              uint8_t* __restrict__ sdst) {
+    const v4i* src = reinterpret_cast<const v4i*>(xsrc);
     uint32_t w[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -60,16 +62,75 @@ __global__ __launch_bounds__(256) void k_quant_mxfp8(const uint16_t* __restrict_
             out[i] = c0 | (c1 << 16);
         }
     }
-    v4i* dst = reinterpret_cast<v4i*>(q + (size_t)b * 32);
+    v4i* dst = reinterpret_cast<v4i*>(qdst);
     dst[0] = v4i{(int)out[0], (int)out[1], (int)out[2], (int)out[3]};
     dst[1] = v4i{(int)out[4], (int)out[5], (int)out[6], (int)out[7]};
-    s[b] = scale;
+    *sdst = scale;
+}
+
+__global__ __launch_bounds__(256) void k_quant_mxfp8(const uint16_t* __restrict__ x, int nblocks,
+                                                     uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+    const int b = blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblocks) return;
+    quant_block32(x + (size_t)b * 32, q + (size_t)b * 32, s + b);
+}
+
+// Rows [0, P): bucket order (row b = token bucket[b] / k); rows [P, P + Mt):
+// token order into qt/st (Mt = M, or 0 when no token-ordered copy is wanted).
+__global__ __launch_bounds__(256) void k_quant_pairs(const uint16_t* __restrict__ x,
+                                                     const int32_t* __restrict__ bucket, int k, int P, int Mt,
+                                                     int K, uint8_t* __restrict__ qp, uint8_t* __restrict__ sp,
+                                                     uint8_t* __restrict__ qt, uint8_t* __restrict__ st) {
+    const int bpr = K / 32;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    const int row = idx / bpr, blk = idx - row * bpr;
+    if (row >= P + Mt) return;
+    if (row < P) {
+        const int tok = bucket[row] / k;
+        quant_block32(x + (size_t)tok * K + 32 * blk, qp + (size_t)row * K + 32 * blk, sp + (size_t)row * bpr + blk);
+    } else {
+        const int tok = row - P;
+        quant_block32(x + (size_t)tok * K + 32 * blk, qt + (size_t)tok * K + 32 * blk, st + (size_t)tok * bpr + blk);
+    }
+}
+
+// Token-ordered MXFP8 rows -> bucket order (row b = token bucket[b] / k).
+// Thread = 16 code bytes of a row; the first K/32 threads of the row also
+// copy one scale byte each.
+__global__ __launch_bounds__(256) void k_gather_pairs(const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_s,
+                                                      const int32_t* __restrict__ bucket, int k, int P, int K,
+                                                      uint8_t* __restrict__ qp, uint8_t* __restrict__ sp) {
+    const int cpr = K / 16;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    const int row = idx / cpr, c = idx - row * cpr;
+    if (row >= P) return;
+    const int tok = bucket[row] / k;
+    *reinterpret_cast<v4i*>(qp + (size_t)row * K + 16 * c) = load16(a_q + (size_t)tok * K + 16 * c);
+    if (c < K / 32) sp[(size_t)row * (K / 32) + c] = a_s[(size_t)tok * (K / 32) + c];
 }
 
 hipError_t launch_quant_mxfp8(const uint16_t* x, int M, int K, uint8_t* q, uint8_t* s,
                               hipStream_t stream) {
     const int nblocks = M * (K / 32);
     hipLaunchKernelGGL(k_quant_mxfp8, dim3((nblocks + 255) / 256), dim3(256), 0, stream, x, nblocks, q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_pairs(const uint16_t* x, const int32_t* bucket, int k, int M, int K, uint8_t* qp,
+                              uint8_t* sp, uint8_t* qt, uint8_t* st, hipStream_t stream) {
+    const int P = M * k, Mt = qt ? M : 0;
+    const long n = (long)(P + Mt) * (K / 32);
+    hipLaunchKernelGGL(k_quant_pairs, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, x, bucket, k, P, Mt, K,
+                       qp, sp, qt, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_pairs(const uint8_t* a_q, const uint8_t* a_s, const int32_t* bucket, int k, int M, int K,
+                               uint8_t* qp, uint8_t* sp, hipStream_t stream) {
+    const int P = M * k;
+    const long n = (long)P * (K / 16);
+    hipLaunchKernelGGL(k_gather_pairs, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a_q, a_s, bucket, k,
+                       P, K, qp, sp);
     return hipGetLastError();
 }
 

@@ -306,7 +306,10 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(int M, int E, int k, 
     for (int e = tid; e < E; e += kBucketThreads) {
         const int c = s_cnt[e];
         route.expert_offsets[e] = s_off[e];
-        if (c > 0) route.active_experts[s_act[e]] = e;
+        if (c > 0) {
+            route.active_experts[s_act[e]] = e;
+            route.active_offsets[s_act[e]] = s_off[e];
+        }
         for (int t = 0; 8 * t < c; ++t) {
             const int ti = s_tile[e] + t;
             route.tile_expert[ti] = e;
@@ -319,6 +322,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(int M, int E, int k, 
         *route.num_tiles = tot_tiles;
         *route.num_active = tot_act;
     }
+    for (int sl = tot_act + tid; sl <= min(E, P); sl += kBucketThreads) route.active_offsets[sl] = P;
     // Stable placement: chunks of R rows; a bitmap per expert marks the chunk's
     // rows that chose it, and a pair's rank within its expert is the number of
     // earlier rows (previous chunks + lower bits of this chunk's bitmap).

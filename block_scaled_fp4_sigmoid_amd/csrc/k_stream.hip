@@ -10,22 +10,26 @@
 // sparse FP4 GEMV for MoE decode).
 //
 // Work decomposition (weight streaming, HBM-bound).  An item is (active
-// expert, block of weight rows, K range).  Its workgroup
-//   1. issues the first D 128-K steps of its weight loads as soon as the
-//      expert is known,
-//   2. copies the expert's activation rows (up to R rows per pass) for its K
-//      range into LDS,
-//   3. streams its weight rows through a per-wave register ring D steps deep,
-//      with no barrier inside the K loop (the B operands come from LDS),
-//   4. writes the result: gate_up over the whole K fuses SwiGLU and the
-//      MXFP8 requant; gate_up split over K writes fp32 partials that a second
-//      launch adds in split order; down writes fp32 per (row, slot).
-// Every expert weight byte is read once per call however many 8-row tiles the
-// expert has (up to R rows per pass).  Ring refills past the item's K range
-// read through a buffer resource at an offset past its record count, which
-// returns zeros without touching memory, so the ring has no branches (a
-// branch between an MFMA and the read of its accumulator is also what the
-// compiler does not always pad correctly on this target).
+// expert, block of weight rows, K range); activations arrive in bucket order,
+// so an expert's rows are contiguous.  After one memory round trip (slot ->
+// expert and bucket range) every wave streams its weight rows AND the
+// activation rows of its pass through one register ring D steps deep: per
+// 128-K step a lane loads its 16 weight bytes, their scales, its 32
+// activation bytes and their scale.  No LDS stage, no barrier and no other
+// dependent load sits between the expert lookup and the K loop (under load a
+// dependent load waits behind every request already queued on the CU, so each
+// one costs several microseconds).  The activation bytes of an expert are
+// read by all of its workgroups and come from the L2.
+//   gate_up over the whole K fuses SwiGLU and the MXFP8 requant; a gate_up
+//   split over K (used only when too few items would fill the GPU) writes
+//   fp32 partials that a second launch adds in split order; down writes fp32
+//   per (row, slot).  Every expert weight byte is read once per call for up
+//   to 32 rows per expert; more rows take more passes.
+// Loads of rows past the pass, and ring refills past the K range, go through
+// a buffer resource at an offset past its record count: they return zeros
+// without touching memory, so the loop has no branches (a branch between an
+// MFMA and the read of its accumulator is also what the compiler does not
+// always pad correctly on this target).
 //
 // Operand layouts (checked on the hardware):
 //   v_mfma_scale_f32_16x16x128_f8f6f4, FP4 operand: lane (row i, group g)
@@ -35,6 +39,10 @@
 //   v_mfma_f32_16x16x32_f16: lane (i, g) holds K [8g, 8g+8).
 //   Output D (16x16): lane l holds D[4(l/16)+r][l%16], r = 0..3.
 // Weights are the M side (16 rows per block), activation rows the N side.
+// Weights come in the load-order layout of moe_pack_fp4: the 1 KB of A
+// operands of a (16-row block, step) is contiguous in lane order, and one
+// dword (MX) or two (NV) per lane carry the weight scales of 4 steps (the
+// MFMA's op_sel picks an MX scale byte), so each load instruction is dense.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -47,13 +55,17 @@ namespace {
 constexpr int kFmtMX = MOE_FMT_MXFP4;
 constexpr int kFmtNV = MOE_FMT_NVFP4;
 constexpr int kThreads = 256;
+constexpr int kPassRows = 32;           // activation rows per pass (two 16-row N-blocks)
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every record count
 
-#ifndef MOE_STREAM_LDS_BUDGET
-#define MOE_STREAM_LDS_BUDGET 65024  // bytes of activation stage per workgroup
-#endif
 #ifndef MOE_STREAM_TARGET_ITEMS
 #define MOE_STREAM_TARGET_ITEMS 1024  // gate_up splits K until about this many items
+#endif
+#ifndef MOE_MIN_BLOCKS
+#define MOE_MIN_BLOCKS 2  // workgroups per CU the register budget must allow
+#endif
+#ifndef MOE_WEIGHT_AUX
+#define MOE_WEIGHT_AUX 2  // cache policy of the weight loads: non-temporal (streamed once)
 #endif
 
 struct StreamJob {
@@ -62,13 +74,14 @@ struct StreamJob {
     const float* gscale;    // NV: per-expert fp32 global
     int N, K;               // weight rows per expert, reduction length
     int dense;              // one expert over all M rows
-    const int32_t* offsets;
     const int32_t* bucket;
     const int32_t* active;
-    const int32_t* num_active;
-    int k, M;
-    int R;                  // activation rows per pass (16 or 32)
-    int span;               // K per split (multiple of 128 * D)
+    const int32_t* active_offsets;  // bucket range of each slot
+    int M;
+    const uint8_t* a_q;     // activation codes [rows][K] (bucket order; token order when dense)
+    const uint8_t* a_s;     // activation scales [rows][K/32]
+    uint32_t a_rows;        // rows of a_q / a_s (record counts)
+    int span;               // K per split (multiple of 128)
     int splits;
     int nblk;               // row blocks per expert
     int out_rows;           // rows of the partial buffer (gate_up split)
@@ -78,6 +91,8 @@ struct Tokens {
     int e, base, n;
 };
 
+// Slot -> (expert, bucket range).  The three loads are independent; unused
+// slots have no rows.
 __device__ __forceinline__ bool resolve(const StreamJob& J, int slot, Tokens& t) {
     if (J.dense) {
         t.e = 0;
@@ -85,11 +100,12 @@ __device__ __forceinline__ bool resolve(const StreamJob& J, int slot, Tokens& t)
         t.n = J.M;
         return true;
     }
-    if (slot >= *J.num_active) return false;
+    const int b0 = J.active_offsets[slot], b1 = J.active_offsets[slot + 1];
     const int e = J.active[slot];
+    if (b1 <= b0) return false;
     t.e = e;
-    t.base = J.offsets[e];
-    t.n = J.offsets[e + 1] - t.base;
+    t.base = b0;
+    t.n = b1 - b0;
     return true;
 }
 
@@ -136,154 +152,119 @@ __device__ __forceinline__ v8h fp8x8_to_f16(uint32_t d0, uint32_t d1, float sf) 
 // 2^(smax - 127) (activation offset) * global.
 __device__ __forceinline__ float nv_row_factor(int smax, float gs) { return ldexpf(gs, smax - 127); }
 
-// ---- activation stage -------------------------------------------------------
-// LDS: q[R][span + 16] (E4M3 codes, padded rows), s[R][span / 32] (E8M0).
+// ---- coordinates and the ring -------------------------------------------------
 
-struct Stage {
-    uint8_t* q;
-    uint8_t* s;
-    int rs;   // q row stride
-    int ss;   // s row stride
+// Per-lane coordinates: MB blocks of 16 weight rows (packed layout), NB blocks
+// of 16 activation rows.
+template <int FMT, int MB, int NB>
+struct Coord {
+    __amdgpu_buffer_rsrc_t rw, rs, ra, ras;
+    uint32_t vw[MB];   // the lane's 16 bytes of step 0 of its weight block
+    uint32_t vs[MB];   // the lane's scale entry of quad 0 of its weight block
+    uint32_t va[NB];   // activation bytes of the lane's row (kOOB past the pass)
+    uint32_t vas[NB];  // activation scale dword of step 0 of the lane's row (kOOB past the pass)
 };
 
-__device__ __forceinline__ Stage stage_layout(uint8_t* lds, int R, int span) {
-    Stage S;
-    S.rs = span + 16;
-    S.ss = span / 32;
-    S.q = lds;
-    S.s = lds + (size_t)R * S.rs;
-    return S;
-}
-
-// Copies rows s_arow[0..npass) x K [k0, k0 + len) into the stage and zeroes
-// rows [npass, rows_z) (the padding columns of the last MFMA N-block).
-__device__ void stage_rows(const Stage& S, const uint8_t* __restrict__ a_q,
-                           const uint8_t* __restrict__ a_s, int K, int k0, int len,
-                           const int* s_arow, int npass, int rows_z) {
-    const int tid = threadIdx.x;
-    const int cpr = len / 16;  // 16-byte chunks per row
-    for (int idx = tid; idx < rows_z * cpr; idx += kThreads) {
-        const int t = idx / cpr, c = idx - t * cpr;
-        v4i v = v4i{0, 0, 0, 0};
-        if (t < npass) v = load16(a_q + (size_t)s_arow[t] * K + k0 + 16 * c);
-        *reinterpret_cast<v4i*>(S.q + t * S.rs + 16 * c) = v;
-    }
-    const int dpr = len / 128;  // scale dwords per row
-    for (int idx = tid; idx < rows_z * dpr; idx += kThreads) {
-        const int t = idx / dpr, c = idx - t * dpr;
-        uint32_t v = 0;
-        if (t < npass)
-            v = *reinterpret_cast<const uint32_t*>(a_s + (size_t)s_arow[t] * (K / 32) + k0 / 32 + 4 * c);
-        *reinterpret_cast<uint32_t*>(S.s + t * S.ss + 4 * c) = v;
-    }
-}
-
-// NVFP4: largest E8M0 code of each staged row over the staged K range
-// (activations enter the f16 MFMA as E4M3 * 2^(s - smax), inside f16 range);
-// zero for padding rows.
-__device__ void stage_row_smax(const Stage& S, int len, int npass, int rows_z, int* s_smax) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int dpr = len / 128;
-    for (int t = wave; t < rows_z; t += kThreads / 64) {
-        uint32_t mx = 0;
-        if (t < npass) {
-            for (int d = lane; d < dpr; d += 64) {
-                const uint32_t v = *reinterpret_cast<const uint32_t*>(S.s + t * S.ss + 4 * d);
-                mx = max(mx, max(max(v & 0xffu, (v >> 8) & 0xffu), max((v >> 16) & 0xffu, v >> 24)));
-            }
-            for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-        }
-        if (lane == 0) s_smax[t] = (int)mx;
-    }
-}
-
-// ---- weight ring ------------------------------------------------------------
-
-template <int MB, int D>
-struct Ring {
-    v4i a[D][MB];
-    uint32_t s[D][MB];
-};
-
-// Per-lane weight coordinates of MB blocks of 16 rows.
-template <int MB>
-struct WCoord {
-    __amdgpu_buffer_rsrc_t rw, rs;
-    uint32_t vw[MB];  // byte offset of (row, 16g) in the expert's packed matrix
-    uint32_t vs[MB];  // byte offset of the lane's scale word in the scale matrix
-};
-
-template <int FMT, int MB>
-__device__ __forceinline__ WCoord<MB> wcoord(const StreamJob& J, int e, const int (&row)[MB]) {
-    const int g = (threadIdx.x & 63) >> 4;
-    const uint32_t wbytes = (uint32_t)J.N * (J.K / 2);
-    const uint32_t sbytes = (uint32_t)J.N * (J.K / (FMT == kFmtMX ? 32 : 16));
-    WCoord<MB> c;
+// wblk: first row of each weight block (a multiple of 16).
+template <int FMT, int MB, int NB>
+__device__ __forceinline__ Coord<FMT, MB, NB> make_coord(const StreamJob& J, int e, const int (&wblk)[MB],
+                                                          int arow0, int npass) {
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 15, g = lane >> 4;
+    const int K = J.K, S = K / 128, Q = (S + 3) / 4;
+    constexpr int SQ = FMT == kFmtMX ? 256 : 512;  // scale bytes per (block, quad)
+    const uint32_t wbytes = (uint32_t)J.N * (K / 2);
+    const uint32_t sbytes = (uint32_t)(J.N / 16) * Q * SQ;
+    Coord<FMT, MB, NB> c;
     c.rw = make_rsrc(J.w + (size_t)e * wbytes, wbytes);
     c.rs = make_rsrc(J.sc + (size_t)e * sbytes, sbytes);
+    // activation resources cover the pass's rows only (offsets stay small)
+    const uint32_t prow = (uint32_t)min(kPassRows, (int)J.a_rows - arow0);
+    c.ra = make_rsrc(J.a_q + (size_t)arow0 * K, prow * (uint32_t)K);
+    c.ras = make_rsrc(J.a_s + (size_t)arow0 * (K / 32), prow * (uint32_t)(K / 32));
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        c.vw[mb] = (uint32_t)row[mb] * (J.K / 2) + 16 * g;
-        c.vs[mb] = FMT == kFmtMX ? (uint32_t)row[mb] * (J.K / 32) : (uint32_t)row[mb] * (J.K / 16) + 2 * g;
+        const uint32_t rb = (uint32_t)wblk[mb] / 16;
+        c.vw[mb] = rb * S * 1024 + 16 * lane;
+        c.vs[mb] = rb * Q * SQ + (SQ / 64) * lane;
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int t = 16 * j + i;
+        const bool ok = t < npass;
+        // MX: bytes [16g, +16) and [64 + 16g, +16) of the step; NV: [32g, +32)
+        c.va[j] = ok ? (uint32_t)t * K + (FMT == kFmtMX ? 16 : 32) * g : kOOB;
+        c.vas[j] = ok ? (uint32_t)t * (K / 32) : kOOB;
     }
     return c;
 }
 
-// Loads absolute K step `st` into ring slot u; ok == false loads zeros.
-template <int FMT, int MB, int D>
-__device__ __forceinline__ void ring_load(Ring<MB, D>& R, int u, const WCoord<MB>& c, int st, bool ok) {
+// A ring slot holds one quad (4 K steps).
+template <int MB, int NB, int DQ>
+struct Ring {
+    v4i a[DQ][4][MB];
+    uint32_t as[DQ][MB][2];
+    v4i b[DQ][4][NB][2];
+    uint32_t bs[DQ][4][NB];
+};
+
+// Loads quad q (absolute) into slot v; steps at or past s_end load zeros.
+template <int FMT, int MB, int NB, int DQ>
+__device__ __forceinline__ void ring_load(Ring<MB, NB, DQ>& R, int v, const Coord<FMT, MB, NB>& c, int q,
+                                          int s_end) {
+    const bool okq = 4 * q < s_end;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        R.a[u][mb] = __builtin_amdgcn_raw_buffer_load_b128(c.rw, ok ? c.vw[mb] : kOOB, 64 * st, 2);
-        if constexpr (FMT == kFmtMX)
-            R.s[u][mb] = __builtin_amdgcn_raw_buffer_load_b32(c.rs, ok ? c.vs[mb] : kOOB, 4 * st, 0);
-        else
-            R.s[u][mb] = __builtin_amdgcn_raw_buffer_load_b16(c.rs, ok ? c.vs[mb] : kOOB, 8 * st, 0);
+        if constexpr (FMT == kFmtMX) {
+            R.as[v][mb][0] = __builtin_amdgcn_raw_buffer_load_b32(c.rs, okq ? c.vs[mb] : kOOB, 256 * q, 0);
+        } else {
+            const auto sv = __builtin_amdgcn_raw_buffer_load_b64(c.rs, okq ? c.vs[mb] : kOOB, 512 * q, 0);
+            R.as[v][mb][0] = sv[0];
+            R.as[v][mb][1] = sv[1];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int st = 4 * q + u;
+        const bool ok = st < s_end;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            R.a[v][u][mb] = __builtin_amdgcn_raw_buffer_load_b128(c.rw, ok ? c.vw[mb] : kOOB, 1024 * st, MOE_WEIGHT_AUX);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const uint32_t va = ok ? c.va[j] : kOOB;
+            R.b[v][u][j][0] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, va, 128 * st, 0);
+            R.b[v][u][j][1] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, va + (FMT == kFmtMX ? 64 : 16), 128 * st, 0);
+            R.bs[v][u][j] = __builtin_amdgcn_raw_buffer_load_b32(c.ras, ok ? c.vas[j] : kOOB, 4 * st, 0);
+        }
     }
 }
 
-template <int FMT, int MB, int D>
-__device__ __forceinline__ void ring_prologue(Ring<MB, D>& R, const WCoord<MB>& c, int s0, int nst) {
-#pragma unroll
-    for (int u = 0; u < D; ++u) ring_load<FMT, MB, D>(R, u, c, s0 + u, u < nst);
-}
-
-// One 128-K step: MB weight blocks x NB activation blocks (staged step ls).
-template <int FMT, int MB, int NB>
-__device__ __forceinline__ void step_mfma(const v4i (&a)[MB], const uint32_t (&ws)[MB], const Stage& S,
-                                          int ls, const int (&sfo)[NB], v4f (&acc)[MB][2]) {
-    const int lane = threadIdx.x & 63;
-    const int i = lane & 15, g = lane >> 4;
+// Step u of the quad in slot v.
+template <int FMT, int MB, int NB, int DQ, int U>
+__device__ __forceinline__ void step_mfma(const Ring<MB, NB, DQ>& R, int v, const int (&sfo)[NB],
+                                          v4f (&acc)[MB][2]) {
+    const int g = (threadIdx.x & 63) >> 4;
     if constexpr (FMT == kFmtMX) {
-        v8i B[NB];
-        int sb[NB];
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int t = 16 * j + i;
-            const uint8_t* rp = S.q + t * S.rs + 128 * ls;
-            const v4i b0 = *reinterpret_cast<const v4i*>(rp + 16 * g);
-            const v4i b1 = *reinterpret_cast<const v4i*>(rp + 64 + 16 * g);
-            B[j] = v8i{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-            sb[j] = S.s[t * S.ss + 4 * ls + g];
-        }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const v8i A = {a[mb].x, a[mb].y, a[mb].z, a[mb].w, 0, 0, 0, 0};
-            const int sa = (int)(ws[mb] >> (8 * g));
+            const v4i a = R.a[v][U][mb];
+            const v8i A = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
-                acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[j], acc[mb][j], 4, 0, 0, sa,
-                                                                              0, sb[j]);
+            for (int j = 0; j < NB; ++j) {
+                const v4i b0 = R.b[v][U][j][0], b1 = R.b[v][U][j][1];
+                const v8i B = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                // A scale: byte U of the quad's dword; B scale: byte g of the step's dword
+                acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    A, B, acc[mb][j], 4, 0, U, (int)R.as[v][mb][0], 0, (int)(R.bs[v][U][j] >> (8 * g)));
+            }
         }
     } else {
         v8h B[NB][4];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            const int t = 16 * j + i;
-            const uint8_t* rp = S.q + t * S.rs + 128 * ls + 32 * g;
-            const v4i b0 = *reinterpret_cast<const v4i*>(rp);
-            const v4i b1 = *reinterpret_cast<const v4i*>(rp + 16);
-            const int sb = S.s[t * S.ss + 4 * ls + g];
+            const v4i b0 = R.b[v][U][j][0], b1 = R.b[v][U][j][1];
+            const int sb = (int)((R.bs[v][U][j] >> (8 * g)) & 0xffu);
             const float sf = exp2i(max(sb + sfo[j], -126));
             B[j][0] = fp8x8_to_f16((uint32_t)b0.x, (uint32_t)b0.y, sf);
             B[j][1] = fp8x8_to_f16((uint32_t)b0.z, (uint32_t)b0.w, sf);
@@ -292,14 +273,16 @@ __device__ __forceinline__ void step_mfma(const v4i (&a)[MB], const uint32_t (&w
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
+            const v4i a = R.a[v][U][mb];
+            const uint32_t ws = R.as[v][mb][U >> 1] >> (16 * (U & 1));
             float sv0, sv1;
             _Float16 m0, m1;
-            nv_scale_split(ws[mb] & 0xffu, sv0, m0);
-            nv_scale_split((ws[mb] >> 8) & 0xffu, sv1, m1);
-            const v8h A0 = nv_dequant8((uint32_t)a[mb].x, sv0, m0);
-            const v8h A1 = nv_dequant8((uint32_t)a[mb].y, sv0, m0);
-            const v8h A2 = nv_dequant8((uint32_t)a[mb].z, sv1, m1);
-            const v8h A3 = nv_dequant8((uint32_t)a[mb].w, sv1, m1);
+            nv_scale_split(ws & 0xffu, sv0, m0);
+            nv_scale_split((ws >> 8) & 0xffu, sv1, m1);
+            const v8h A0 = nv_dequant8((uint32_t)a.x, sv0, m0);
+            const v8h A1 = nv_dequant8((uint32_t)a.y, sv0, m0);
+            const v8h A2 = nv_dequant8((uint32_t)a.z, sv1, m1);
+            const v8h A3 = nv_dequant8((uint32_t)a.w, sv1, m1);
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, B[j][0], acc[mb][j], 0, 0, 0);
@@ -311,38 +294,85 @@ __device__ __forceinline__ void step_mfma(const v4i (&a)[MB], const uint32_t (&w
     }
 }
 
-// The K loop of one pass: nst staged steps (a multiple of D) starting at
-// absolute step s0; the ring holds the first D steps on entry.  Every slot is
-// refilled D steps ahead (zeros past the range).  NB is a compile-time
-// constant, so no branch separates an MFMA from the read of its accumulator.
-template <int FMT, int MB, int D, int NB>
-__device__ __forceinline__ void stream_k(Ring<MB, D>& R, const WCoord<MB>& c, const Stage& S, int s0, int nst,
-                                         const int* s_smax, v4f (&acc)[MB][2]) {
-    const int i = threadIdx.x & 15;
-    int sfo[NB];  // NVFP4: -smax of the lane's activation row
+// NVFP4: largest E8M0 code of the lane's activation row(s) over K steps
+// [s0, s0 + nst) (activations enter the f16 MFMA as E4M3 * 2^(s - smax),
+// inside f16 range); 0 for rows past the pass.  Issued before the ring, so
+// it returns first.
+template <int FMT, int MB, int NB>
+__device__ __forceinline__ void row_smax(const Coord<FMT, MB, NB>& c, int s0, int nst, int (&smax)[NB]) {
+    const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) sfo[j] = FMT == kFmtNV ? -s_smax[16 * j + i] : 0;
+    for (int j = 0; j < NB; ++j) {
+        // the row's scale dwords of the range (dword d = blocks 4(s0+d) .. +3);
+        // lane group g takes dwords g, g+4, ...
+        const bool ok = c.vas[j] != kOOB;
+        const uint32_t base = ok ? c.vas[j] + 4 * s0 : kOOB;
+        uint32_t mx = 0;
+        for (int d = g; d < nst; d += 4) {
+            const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(c.ras, ok ? base + 4 * d : kOOB, 0, 0);
+            mx = max(mx, max(max(v & 0xffu, (v >> 8) & 0xffu), max((v >> 16) & 0xffu, v >> 24)));
+        }
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16, 64));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
+        smax[j] = (int)mx;
+    }
+}
+
+// All of one pass: K steps [s0, s0 + nst) (s0 a multiple of 4) of MB weight
+// blocks against NB blocks of activation rows arow0 + [0, npass).  The ring
+// holds DQ quads and is refilled DQ quads ahead; steps past the range load
+// zeros for both operands.
+template <int FMT, int MB, int NB, int DQ>
+__device__ __forceinline__ void stream_pass(const StreamJob& J, int e, const int (&wblk)[MB], int arow0, int npass,
+                                            int s0, int nst, int (&smax)[NB], v4f (&acc)[MB][2]) {
+    const Coord<FMT, MB, NB> c = make_coord<FMT, MB, NB>(J, e, wblk, arow0, npass);
+    int sfo[NB];
+    if constexpr (FMT == kFmtNV) {
+        row_smax<FMT, MB, NB>(c, s0, nst, smax);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) sfo[j] = -smax[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            sfo[j] = 0;
+            smax[j] = 0;
+        }
+    }
+    const int q0 = s0 / 4, nq = (nst + 3) / 4, s_end = s0 + nst;
+    Ring<MB, NB, DQ> R;
+#pragma unroll
+    for (int v = 0; v < DQ; ++v) ring_load<FMT, MB, NB, DQ>(R, v, c, q0 + v, s_end);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[mb][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int l0 = 0; l0 < nst; l0 += D) {
+    for (int l0 = 0; l0 < nq; l0 += DQ) {
 #pragma unroll
-        for (int u = 0; u < D; ++u) {
-            step_mfma<FMT, MB, NB>(R.a[u], R.s[u], S, l0 + u, sfo, acc);
-            const int ln = l0 + u + D;
-            ring_load<FMT, MB, D>(R, u, c, s0 + ln, ln < nst);
+        for (int v = 0; v < DQ; ++v) {
+            // keep each step's instructions in place: hoisting the use of a
+            // later slot would wait for that slot's loads and drain the ring
+            __builtin_amdgcn_sched_barrier(0);
+            step_mfma<FMT, MB, NB, DQ, 0>(R, v, sfo, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            step_mfma<FMT, MB, NB, DQ, 1>(R, v, sfo, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            step_mfma<FMT, MB, NB, DQ, 2>(R, v, sfo, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            step_mfma<FMT, MB, NB, DQ, 3>(R, v, sfo, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            ring_load<FMT, MB, NB, DQ>(R, v, c, q0 + l0 + v + DQ, s_end);
         }
     }
 }
 
-template <int FMT, int MB, int D>
-__device__ __forceinline__ void stream_pass(Ring<MB, D>& R, const WCoord<MB>& c, const Stage& S, int s0, int nst,
-                                            int npass, const int* s_smax, v4f (&acc)[MB][2]) {
-    if (npass > 16)
-        stream_k<FMT, MB, D, 2>(R, c, S, s0, nst, s_smax, acc);
-    else
-        stream_k<FMT, MB, D, 1>(R, c, S, s0, nst, s_smax, acc);
+// Ring depth in quads for MB weight blocks and NB activation blocks (about
+// 32 loads of 16 bytes per lane in flight for MXFP4, fewer for NVFP4, whose
+// dequantization needs registers).
+template <int FMT, int MB, int NB>
+constexpr int ring_quads() {
+    constexpr int per_quad = 4 * (MB + 2 * NB);
+    constexpr int budget = FMT == kFmtMX ? 32 : 24;
+    return budget / per_quad < 1 ? 1 : budget / per_quad;
 }
 
 // MXFP8 of 4 consecutive values (part of a 32-value block shared by 8
@@ -377,20 +407,21 @@ __device__ __forceinline__ uint32_t mx_quant4_group8(const float hv[4], uint8_t&
 
 __device__ __forceinline__ float silu_mul(float gt, float up) { return gt / (1.0f + __expf(-gt)) * up; }
 
-extern __shared__ __align__(16) uint8_t g_lds[];
-
 // ---- gate_up ----------------------------------------------------------------
-// Item = (slot, 32 output columns, K split).  Waves 0/1 stream gate rows
-// cb*32 + [0,16) / [16,32), waves 2/3 the matching up rows (rows I + ...).
-// FUSED (one split): SwiGLU + MXFP8 requant in the epilogue, h rows are
-// bucket positions (routed) or token rows (dense).  Otherwise fp32 partials
-// part[split][row][2I] (already multiplied by the NVFP4 row factor).
+// Item = (slot, 32*GMB output columns, K split).  Waves 0/1 stream the gate
+// rows of the two halves of the columns, waves 2/3 the matching up rows
+// (rows I + ...); each wave owns GMB blocks of 16 rows.  FUSED (one split):
+// SwiGLU + MXFP8 requant in the epilogue; h rows are bucket positions
+// (routed) or token rows (dense).  Otherwise fp32 partials part[split][row][2I]
+// (already multiplied by the NVFP4 row factor).
 
-template <int FMT, int D, bool FUSED>
-__global__ __launch_bounds__(kThreads, 2) void k_gate_up(StreamJob J, const uint8_t* __restrict__ a_q,
-                                                         const uint8_t* __restrict__ a_s,
-                                                         uint8_t* __restrict__ h_q, uint8_t* __restrict__ h_s,
-                                                         float* __restrict__ part) {
+constexpr int GMB = 2;           // 16-row weight blocks per wave in gate_up
+constexpr int GCOLS = 32 * GMB;  // output columns per workgroup
+
+template <int FMT, bool FUSED>
+__global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_gate_up(StreamJob J, uint8_t* __restrict__ h_q,
+                                                                      uint8_t* __restrict__ h_s,
+                                                                      float* __restrict__ part) {
     const int I = J.N / 2, K = J.K;
     const int ks = blockIdx.x % J.splits;
     const int blk = (blockIdx.x / J.splits) % J.nblk;
@@ -399,93 +430,92 @@ __global__ __launch_bounds__(kThreads, 2) void k_gate_up(StreamJob J, const uint
     if (!resolve(J, slot, tk)) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int i = lane & 15, g = lane >> 4;
-    const int col0 = blk * 32 + (wave & 1) * 16;         // first of the wave's 16 output columns
-    const int wrow[1] = {(wave >> 1) * I + col0 + i};     // gate or up row of the lane
-    const WCoord<1> wc = wcoord<FMT, 1>(J, tk.e, wrow);
+    const int half = (wave & 1) * (16 * GMB);  // column offset of the wave within the item
+    const int col0 = blk * GCOLS + half;       // first output column of the wave
+    int wblk[GMB];  // first W13 row of each of the wave's 16-row blocks
+#pragma unroll
+    for (int mb = 0; mb < GMB; ++mb) wblk[mb] = (wave >> 1) * I + col0 + 16 * mb;
     const int k0 = ks * J.span;
-    const int len = min(J.span, K - k0);
-    const int s0 = k0 / 128, nst = len / 128;
-
-    Ring<1, D> R;
-    ring_prologue<FMT, 1, D>(R, wc, s0, nst);
-
-    const Stage S = stage_layout(g_lds, J.R, J.span);
-    __shared__ int s_arow[32];
-    __shared__ int s_orow[32];
-    __shared__ int s_smax[32];
+    const int s0 = k0 / 128, nst = min(J.span, K - k0) / 128;
     const float gs = FMT == kFmtNV ? J.gscale[tk.e] : 1.0f;
 
-    for (int t0 = 0; t0 < tk.n; t0 += J.R) {
-        const int npass = min(J.R, tk.n - t0);
-        const int rows_z = npass > 16 ? 32 : 16;
-        if (t0 > 0) ring_prologue<FMT, 1, D>(R, wc, s0, nst);
-        if (threadIdx.x < 32) {
-            const int t = threadIdx.x;
-            int ar = -1, orow = -1;
-            if (t < npass) {
-                const int b = tk.base + t0 + t;
-                ar = J.dense ? b : J.bucket[b] / J.k;
-                orow = b;
-            }
-            s_arow[t] = ar;
-            s_orow[t] = orow;
-        }
-        __syncthreads();
-        stage_rows(S, a_q, a_s, K, k0, len, s_arow, npass, rows_z);
-        __syncthreads();
-        if (FMT == kFmtNV) {
-            stage_row_smax(S, len, npass, rows_z, s_smax);
-            __syncthreads();
-        }
-        v4f acc[1][2];
-        stream_pass<FMT, 1, D>(R, wc, S, s0, nst, npass, s_smax, acc);
-        if constexpr (FUSED) {
-            __syncthreads();  // the stage is reused for the gate/up tile
-            float* sG = reinterpret_cast<float*>(g_lds);  // [32][65]
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int t = 16 * j + i;
-                if (t < npass) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sG[t * 65 + wave * 16 + 4 * g + r] = acc[0][j][r];
-                }
-            }
-            __syncthreads();
-            // SwiGLU + MXFP8 requant: 8 lanes per row, 4 columns each.
-            const int t = threadIdx.x >> 3, q8 = threadIdx.x & 7;
-            float hv[4];
-            float fac = 1.0f;
-            if (FMT == kFmtNV && t < npass) fac = nv_row_factor(s_smax[t], gs);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int col = 4 * q8 + c;
-                float gt = 0.f, up = 0.f;
-                if (t < npass) {
-                    gt = sG[t * 65 + col] * fac;
-                    up = sG[t * 65 + 32 + col] * fac;
-                }
-                hv[c] = silu_mul(gt, up);
-            }
-            uint8_t sc;
-            const uint32_t codes = mx_quant4_group8(hv, sc);
-            if (t < npass) {
-                const size_t orow = (size_t)s_orow[t];
-                *reinterpret_cast<uint32_t*>(h_q + orow * I + blk * 32 + 4 * q8) = codes;
-                if (q8 == 0) h_s[orow * (I / 32) + blk] = sc;
-            }
+    __shared__ float sG[kPassRows][2 * GCOLS + 1];  // fused: gate [0, GCOLS), up [GCOLS, 2*GCOLS)
+    __shared__ int s_smax[kPassRows];
+
+    for (int t0 = 0; t0 < tk.n; t0 += kPassRows) {
+        const int npass = min(kPassRows, tk.n - t0);
+        const int arow0 = tk.base + t0;
+        v4f acc[GMB][2];
+        int smax[2] = {0, 0};
+        if (npass > 16) {
+            int sm[2];
+            stream_pass<FMT, GMB, 2, ring_quads<FMT, GMB, 2>()>(J, tk.e, wblk, arow0, npass, s0, nst, sm, acc);
+            smax[0] = sm[0];
+            smax[1] = sm[1];
         } else {
-            const int colw = (wave >> 1) * I + col0 + 4 * g;
+            int sm[1];
+            stream_pass<FMT, GMB, 1, ring_quads<FMT, GMB, 1>()>(J, tk.e, wblk, arow0, npass, s0, nst, sm, acc);
+            smax[0] = sm[0];
+        }
+        if constexpr (FUSED) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int t = 16 * j + i;
+            for (int mb = 0; mb < GMB; ++mb) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int t = 16 * j + i;
+                    if (t < npass) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            sG[t][(wave >> 1) * GCOLS + half + 16 * mb + 4 * g + r] = acc[mb][j][r];
+                    }
+                }
+            }
+            if (FMT == kFmtNV && wave == 0 && g == 0) {
+                s_smax[i] = smax[0];
+                s_smax[16 + i] = smax[1];
+            }
+            __syncthreads();
+            // SwiGLU + MXFP8 requant: 8 lanes per 32-column block, 4 columns each
+            // (whole waves take part in every round, the row check is per lane).
+            for (int idx = threadIdx.x; idx < kPassRows * (GCOLS / 4); idx += kThreads) {
+                const int t = idx / (GCOLS / 4), q = idx % (GCOLS / 4);
+                float hv[4];
+                float fac = 1.0f;
+                if (FMT == kFmtNV && t < npass) fac = nv_row_factor(s_smax[t], gs);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int col = 4 * q + c;
+                    float gt = 0.f, up = 0.f;
+                    if (t < npass) {
+                        gt = sG[t][col] * fac;
+                        up = sG[t][GCOLS + col] * fac;
+                    }
+                    hv[c] = silu_mul(gt, up);
+                }
+                uint8_t sc;
+                const uint32_t codes = mx_quant4_group8(hv, sc);
                 if (t < npass) {
-                    v4f v = acc[0][j];
-                    if (FMT == kFmtNV) v = v * nv_row_factor(s_smax[t], gs);
-                    *reinterpret_cast<v4f*>(part + ((size_t)ks * J.out_rows + s_orow[t]) * (2 * I) + colw) = v;
+                    const size_t orow = (size_t)(arow0 + t);
+                    *reinterpret_cast<uint32_t*>(h_q + orow * I + blk * GCOLS + 4 * q) = codes;
+                    if ((q & 7) == 0) h_s[orow * (I / 32) + blk * (GCOLS / 32) + (q >> 3)] = sc;
+                }
+            }
+            __syncthreads();
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < GMB; ++mb) {
+                const int colw = (wave >> 1) * I + col0 + 16 * mb + 4 * g;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int t = 16 * j + i;
+                    if (t < npass) {
+                        v4f v = acc[mb][j];
+                        if (FMT == kFmtNV) v = v * nv_row_factor(smax[j], gs);
+                        *reinterpret_cast<v4f*>(part + ((size_t)ks * J.out_rows + arow0 + t) * (2 * I) + colw) = v;
+                    }
                 }
             }
         }
-        __syncthreads();
     }
 }
 
@@ -517,12 +547,11 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_quant(const float* __restri
 
 // ---- down -------------------------------------------------------------------
 // Item = (slot, 64*MB output features); wave w owns MB blocks of 16 features.
-// Activations are h rows (bucket positions for routed experts); the output
-// row of bucket position b is its pair id bucket[b].
+// Activations are h rows in bucket order; the output row of bucket position b
+// is its pair id bucket[b] (the token row for a dense expert).
 
-template <int FMT, int D, int MB>
-__global__ __launch_bounds__(kThreads, 2) void k_down(StreamJob J, const uint8_t* __restrict__ h_q,
-                                                      const uint8_t* __restrict__ h_s, float* __restrict__ y) {
+template <int FMT, int MB>
+__global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J, float* __restrict__ y) {
     const int H = J.N, I = J.K;
     constexpr int RB = 64 * MB;
     const int blk = blockIdx.x % J.nblk;
@@ -532,123 +561,83 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(StreamJob J, const uint8_t
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int i = lane & 15, g = lane >> 4;
     const int f0 = blk * RB + wave * (16 * MB);
-    int wrow[MB];
+    int wblk[MB];  // first W2 row of each of the wave's 16-row blocks
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) wrow[mb] = f0 + 16 * mb + i;
-    const WCoord<MB> wc = wcoord<FMT, MB>(J, tk.e, wrow);
+    for (int mb = 0; mb < MB; ++mb) wblk[mb] = f0 + 16 * mb;
     const int nst = I / 128;
-
-    Ring<MB, D> R;
-    ring_prologue<FMT, MB, D>(R, wc, 0, nst);
-
-    const Stage S = stage_layout(g_lds, J.R, I);
-    __shared__ int s_arow[32];
-    __shared__ int s_orow[32];
-    __shared__ int s_smax[32];
     const float gs = FMT == kFmtNV ? J.gscale[tk.e] : 1.0f;
 
-    for (int t0 = 0; t0 < tk.n; t0 += J.R) {
-        const int npass = min(J.R, tk.n - t0);
-        const int rows_z = npass > 16 ? 32 : 16;
-        if (t0 > 0) ring_prologue<FMT, MB, D>(R, wc, 0, nst);
-        if (threadIdx.x < 32) {
-            const int t = threadIdx.x;
-            int ar = -1, orow = -1;
-            if (t < npass) {
-                const int b = tk.base + t0 + t;
-                ar = b;
-                orow = J.dense ? b : J.bucket[b];
-            }
-            s_arow[t] = ar;
-            s_orow[t] = orow;
-        }
-        __syncthreads();
-        stage_rows(S, h_q, h_s, I, 0, I, s_arow, npass, rows_z);
-        __syncthreads();
-        if (FMT == kFmtNV) {
-            stage_row_smax(S, I, npass, rows_z, s_smax);
-            __syncthreads();
+    for (int t0 = 0; t0 < tk.n; t0 += kPassRows) {
+        const int npass = min(kPassRows, tk.n - t0);
+        const int arow0 = tk.base + t0;
+        // output rows of the lane's activation rows: loaded before the ring so
+        // they return first
+        int orow[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int t = 16 * j + i;
+            orow[j] = t < npass ? (J.dense ? arow0 + t : J.bucket[arow0 + t]) : 0;
         }
         v4f acc[MB][2];
-        stream_pass<FMT, MB, D>(R, wc, S, 0, nst, npass, s_smax, acc);
+        int smax[2] = {0, 0};
+        if (npass > 16) {
+            int sm[2];
+            stream_pass<FMT, MB, 2, ring_quads<FMT, MB, 2>()>(J, tk.e, wblk, arow0, npass, 0, nst, sm, acc);
+            smax[0] = sm[0];
+            smax[1] = sm[1];
+        } else {
+            int sm[1];
+            stream_pass<FMT, MB, 1, ring_quads<FMT, MB, 1>()>(J, tk.e, wblk, arow0, npass, 0, nst, sm, acc);
+            smax[0] = sm[0];
+        }
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+        for (int j = 0; j < 2; ++j) {
+            const int t = 16 * j + i;
+            if (t < npass) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int t = 16 * j + i;
-                if (t < npass) {
+                for (int mb = 0; mb < MB; ++mb) {
                     v4f v = acc[mb][j];
-                    if (FMT == kFmtNV) v = v * nv_row_factor(s_smax[t], gs);
-                    *reinterpret_cast<v4f*>(y + (size_t)s_orow[t] * H + f0 + 16 * mb + 4 * g) = v;
+                    if (FMT == kFmtNV) v = v * nv_row_factor(smax[j], gs);
+                    *reinterpret_cast<v4f*>(y + (size_t)orow[j] * H + f0 + 16 * mb + 4 * g) = v;
                 }
             }
         }
-        __syncthreads();
     }
 }
 
 // ---- host plans -------------------------------------------------------------
 
-int pow2_divisor(int n, int cap) {
-    int d = 1;
-    while (d * 2 <= cap && n % (d * 2) == 0) d *= 2;
-    return d;
-}
-
-// Stage rows: the MFMA N-block is 16 rows, and no expert has more than M rows
-// (a row picks an expert once).
-int rows_for(int M) { return M <= 16 ? 16 : 32; }
-
-size_t stage_bytes(int R, int span) { return (size_t)R * (span + 16) + (size_t)R * (span / 32); }
-
-// Longest K range (a multiple of unit) whose stage of R rows fits the budget.
-int max_span(int R, int unit) {
-    int span = unit;
-    while (stage_bytes(R, span + unit) <= (size_t)MOE_STREAM_LDS_BUDGET) span += unit;
-    return span;
-}
-
 struct GatePlan {
-    int R, D, span, splits, nblk;
-    size_t lds;
+    int span, splits, nblk;
 };
 
 GatePlan gate_plan(const ExpertJob& j) {
     GatePlan p;
     const int K = j.K, steps = K / 128;
-    p.D = pow2_divisor(steps, 8);
-    p.R = rows_for(j.M);
-    p.nblk = j.N_out / 32;
-    const int unit = 128 * p.D;
+    p.nblk = j.N_out / GCOLS;
     const long items = (long)j.slots * p.nblk;
-    const int want = (int)std::max<long>(1, (MOE_STREAM_TARGET_ITEMS + items - 1) / items);
-    int span = (K + want - 1) / want;
-    span = (span + unit - 1) / unit * unit;
-    p.span = std::min(std::min(span, max_span(p.R, unit)), K);
-    p.splits = (K + p.span - 1) / p.span;
-    p.lds = std::max(stage_bytes(p.R, p.span), (size_t)32 * 65 * sizeof(float));
+    int want = (int)std::max<long>(1, (MOE_STREAM_TARGET_ITEMS + items - 1) / items);
+    want = std::min(want, std::max(1, steps / 8));  // at least 8 steps per split
+    int sps = (steps + want - 1) / want;             // steps per split: whole quads
+    if (sps < steps) sps = (sps + 3) / 4 * 4;
+    p.span = 128 * sps;
+    p.splits = (steps + sps - 1) / sps;
     return p;
 }
 
 struct DownPlan {
-    int R, D, MB, nblk;
-    size_t lds;
+    int MB, nblk;
 };
 
 DownPlan down_plan(const ExpertJob& j) {
     DownPlan p;
-    const int I = j.K, steps = I / 128;
-    p.D = pow2_divisor(steps, 8);
-    // weight loads in flight per lane: MB * D <= 8 (16 bytes each)
-    p.MB = p.D == 8 ? 1 : (p.D == 4 || j.N_out % 256 != 0 ? 2 : 4);
-    p.R = rows_for(j.M);
-    if (p.R == 32 && stage_bytes(32, I) > (size_t)MOE_STREAM_LDS_BUDGET) p.R = 16;
+    // a short K gets more 16-row blocks per wave
+    p.MB = (j.K <= 512 && j.N_out % 256 == 0) ? 4 : 2;
     p.nblk = j.N_out / (64 * p.MB);
-    p.lds = stage_bytes(p.R, I);
     return p;
 }
 
-StreamJob stream_job(const ExpertJob& j, int N, int R, int span, int splits, int nblk, int out_rows) {
+StreamJob stream_job(const ExpertJob& j, int N, const uint8_t* a_q, const uint8_t* a_s, int a_rows) {
     StreamJob s;
     s.w = static_cast<const uint8_t*>(j.w.w);
     s.sc = j.w.scales;
@@ -656,60 +645,18 @@ StreamJob stream_job(const ExpertJob& j, int N, int R, int span, int splits, int
     s.N = N;
     s.K = j.K;
     s.dense = j.dense ? 1 : 0;
-    s.offsets = j.offsets;
     s.bucket = j.bucket;
     s.active = j.active;
-    s.num_active = j.num_active;
-    s.k = j.k;
+    s.active_offsets = j.active_offsets;
     s.M = j.M;
-    s.R = R;
-    s.span = span;
-    s.splits = splits;
-    s.nblk = nblk;
-    s.out_rows = out_rows;
+    s.a_q = a_q;
+    s.a_s = a_s;
+    s.a_rows = (uint32_t)a_rows;
+    s.span = j.K;
+    s.splits = 1;
+    s.nblk = 1;
+    s.out_rows = a_rows;
     return s;
-}
-
-template <int FMT, int D>
-hipError_t launch_gate_up_d(const StreamJob& J, const GatePlan& p, int blocks, const uint8_t* a_q,
-                            const uint8_t* a_s, uint8_t* h_q, uint8_t* h_s, float* part, hipStream_t stream) {
-    if (p.splits == 1)
-        hipLaunchKernelGGL((k_gate_up<FMT, D, true>), dim3(blocks), dim3(kThreads), p.lds, stream, J, a_q, a_s, h_q,
-                           h_s, part);
-    else
-        hipLaunchKernelGGL((k_gate_up<FMT, D, false>), dim3(blocks), dim3(kThreads), p.lds, stream, J, a_q, a_s,
-                           h_q, h_s, part);
-    return hipGetLastError();
-}
-
-template <int FMT>
-hipError_t launch_gate_up_f(const StreamJob& J, const GatePlan& p, int blocks, const uint8_t* a_q,
-                            const uint8_t* a_s, uint8_t* h_q, uint8_t* h_s, float* part, hipStream_t stream) {
-    switch (p.D) {
-        case 8: return launch_gate_up_d<FMT, 8>(J, p, blocks, a_q, a_s, h_q, h_s, part, stream);
-        case 4: return launch_gate_up_d<FMT, 4>(J, p, blocks, a_q, a_s, h_q, h_s, part, stream);
-        case 2: return launch_gate_up_d<FMT, 2>(J, p, blocks, a_q, a_s, h_q, h_s, part, stream);
-        default: return launch_gate_up_d<FMT, 1>(J, p, blocks, a_q, a_s, h_q, h_s, part, stream);
-    }
-}
-
-template <int FMT, int D, int MB>
-hipError_t launch_down_k(const StreamJob& J, const DownPlan& p, int blocks, const uint8_t* h_q,
-                         const uint8_t* h_s, float* y, hipStream_t stream) {
-    hipLaunchKernelGGL((k_down<FMT, D, MB>), dim3(blocks), dim3(kThreads), p.lds, stream, J, h_q, h_s, y);
-    return hipGetLastError();
-}
-
-template <int FMT>
-hipError_t launch_down_f(const StreamJob& J, const DownPlan& p, int blocks, const uint8_t* h_q,
-                         const uint8_t* h_s, float* y, hipStream_t stream) {
-    if (p.D == 8) return launch_down_k<FMT, 8, 1>(J, p, blocks, h_q, h_s, y, stream);
-    if (p.D == 4) return launch_down_k<FMT, 4, 2>(J, p, blocks, h_q, h_s, y, stream);
-    if (p.D == 2)
-        return p.MB == 4 ? launch_down_k<FMT, 2, 4>(J, p, blocks, h_q, h_s, y, stream)
-                         : launch_down_k<FMT, 2, 2>(J, p, blocks, h_q, h_s, y, stream);
-    return p.MB == 4 ? launch_down_k<FMT, 1, 4>(J, p, blocks, h_q, h_s, y, stream)
-                     : launch_down_k<FMT, 1, 2>(J, p, blocks, h_q, h_s, y, stream);
 }
 
 int out_rows_of(const ExpertJob& j) { return j.dense ? j.M : j.M * j.k; }
@@ -726,12 +673,29 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
                               uint8_t* h_s, float* partials, hipStream_t stream) {
     const GatePlan p = gate_plan(job);
     const int rows = out_rows_of(job);
-    const StreamJob J = stream_job(job, 2 * job.N_out, p.R, p.span, p.splits, p.nblk, rows);
+    StreamJob J = stream_job(job, 2 * job.N_out, a_q, a_s, rows);
+    J.span = p.span;
+    J.splits = p.splits;
+    J.nblk = p.nblk;
     const int blocks = job.slots * p.nblk * p.splits;
-    hipError_t e = job.w.fmt == MOE_FMT_MXFP4
-                       ? launch_gate_up_f<kFmtMX>(J, p, blocks, a_q, a_s, h_q, h_s, partials, stream)
-                       : launch_gate_up_f<kFmtNV>(J, p, blocks, a_q, a_s, h_q, h_s, partials, stream);
-    if (e != hipSuccess || p.splits == 1) return e;
+    const bool mx = job.w.fmt == MOE_FMT_MXFP4;
+    if (p.splits == 1) {
+        if (mx)
+            hipLaunchKernelGGL((k_gate_up<kFmtMX, true>), dim3(blocks), dim3(kThreads), 0, stream, J, h_q, h_s,
+                               partials);
+        else
+            hipLaunchKernelGGL((k_gate_up<kFmtNV, true>), dim3(blocks), dim3(kThreads), 0, stream, J, h_q, h_s,
+                               partials);
+        return hipGetLastError();
+    }
+    if (mx)
+        hipLaunchKernelGGL((k_gate_up<kFmtMX, false>), dim3(blocks), dim3(kThreads), 0, stream, J, h_q, h_s,
+                           partials);
+    else
+        hipLaunchKernelGGL((k_gate_up<kFmtNV, false>), dim3(blocks), dim3(kThreads), 0, stream, J, h_q, h_s,
+                           partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const int threads = rows * (job.N_out / 32) * 8;
     hipLaunchKernelGGL(k_swiglu_quant, dim3((threads + kThreads - 1) / kThreads), dim3(kThreads), 0, stream,
                        partials, p.splits, rows, job.N_out, h_q, h_s);
@@ -741,10 +705,22 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
 hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8_t* h_s, float* y,
                            hipStream_t stream) {
     const DownPlan p = down_plan(job);
-    const StreamJob J = stream_job(job, job.N_out, p.R, job.K, 1, p.nblk, out_rows_of(job));
+    StreamJob J = stream_job(job, job.N_out, h_q, h_s, out_rows_of(job));
+    J.nblk = p.nblk;
     const int blocks = job.slots * p.nblk;
-    return job.w.fmt == MOE_FMT_MXFP4 ? launch_down_f<kFmtMX>(J, p, blocks, h_q, h_s, y, stream)
-                                      : launch_down_f<kFmtNV>(J, p, blocks, h_q, h_s, y, stream);
+    const bool mx = job.w.fmt == MOE_FMT_MXFP4;
+    if (p.MB == 4) {
+        if (mx)
+            hipLaunchKernelGGL((k_down<kFmtMX, 4>), dim3(blocks), dim3(kThreads), 0, stream, J, y);
+        else
+            hipLaunchKernelGGL((k_down<kFmtNV, 4>), dim3(blocks), dim3(kThreads), 0, stream, J, y);
+    } else {
+        if (mx)
+            hipLaunchKernelGGL((k_down<kFmtMX, 2>), dim3(blocks), dim3(kThreads), 0, stream, J, y);
+        else
+            hipLaunchKernelGGL((k_down<kFmtNV, 2>), dim3(blocks), dim3(kThreads), 0, stream, J, y);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace moe

@@ -37,7 +37,8 @@ int check_dims(int M, int H, int E, int k) {
 
 int check_routing(const moe_routing* r) {
     if (!r || !r->topk_ids || !r->topk_w || !r->expert_offsets || !r->bucket || !r->tile_expert ||
-        !r->tile_begin || !r->tile_rows || !r->num_tiles || !r->active_experts || !r->num_active)
+        !r->tile_begin || !r->tile_rows || !r->num_tiles || !r->active_experts || !r->num_active ||
+        !r->active_offsets)
         return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
@@ -92,6 +93,7 @@ ExpertJob routed_job(const moe_weights& w, int N_out, int K, const moe_routing& 
     j.bucket = r.bucket;
     j.active = r.active_experts;
     j.num_active = r.num_active;
+    j.active_offsets = r.active_offsets;
     j.slots = std::min(E, M * k);
     j.k = k;
     j.M = M;
@@ -104,11 +106,28 @@ ExpertJob dense_job(const moe_weights& w, int N_out, int K, int M) {
     j.N_out = N_out;
     j.K = K;
     j.dense = true;
-    j.offsets = j.bucket = j.active = j.num_active = nullptr;
+    j.offsets = j.bucket = j.active = j.num_active = j.active_offsets = nullptr;
     j.slots = 1;
     j.k = 1;
     j.M = M;
     return j;
+}
+
+// FP4 gate_up workspace: [bucket-ordered activation codes P*H][their scales
+// P*H/32] (routed only) [split-K partials].
+struct GateUpWs {
+    uint8_t *aq, *as;
+    float* part;
+};
+
+GateUpWs carve_gate_up(Carver& c, const ExpertJob& job, int M, int H, int k, bool dense) {
+    GateUpWs w{nullptr, nullptr, nullptr};
+    if (!dense) {
+        w.aq = c.take<uint8_t>((size_t)M * k * H);
+        w.as = c.take<uint8_t>((size_t)M * k * (H / 32));
+    }
+    w.part = c.take<float>(gate_up_fp4_partials_bytes(job) / sizeof(float));
+    return w;
 }
 
 }  // namespace
@@ -132,6 +151,21 @@ int moe_tile_capacity(int M, int E, int k) {
     if (M < 1 || E < 1 || k < 1) return 0;
     const int P = M * k;
     return (P + 7) / 8 + std::min(E, P);
+}
+
+size_t moe_packed_scale_bytes(int fmt, int E, int N, int K) {
+    if ((fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_NVFP4) || E < 1 || N < 16 || N % 16 != 0 || K < 128 ||
+        K % 128 != 0)
+        return 0;
+    return packed_scale_bytes(fmt, E, N, K);
+}
+
+int moe_pack_fp4(int fmt, int E, int N, int K, const uint8_t* w, const uint8_t* scales, uint8_t* w_out,
+                 uint8_t* scales_out, hipStream_t stream) {
+    if (fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_NVFP4) return MOE_ERR_UNSUPPORTED;
+    if (!w || !scales || !w_out || !scales_out || E < 1 || N < 16 || K < 128) return MOE_ERR_INVALID_ARG;
+    if (N % 16 != 0 || K % 128 != 0 || (long)E * N > (1L << 28) || K > kMaxH) return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_pack_fp4(fmt, E, N, K, w, scales, w_out, scales_out, stream));
 }
 
 size_t moe_route_workspace_bytes(int M, int H, int E, int k) {
@@ -187,7 +221,9 @@ size_t moe_gate_up_workspace_bytes(int fmt, int M, int H, int I, int E, int k, i
     w.fmt = fmt;
     moe_routing r{};
     const ExpertJob job = dense ? dense_job(w, I, H, M) : routed_job(w, I, H, r, M, E, k);
-    return gate_up_fp4_partials_bytes(job);
+    Carver c(nullptr);
+    carve_gate_up(c, job, M, H, k, dense);
+    return c.off;
 }
 
 int moe_expert_gate_up(const moe_weights* w13, const uint8_t* a_q, const uint8_t* a_s,
@@ -211,9 +247,20 @@ int moe_expert_gate_up(const moe_weights* w13, const uint8_t* a_q, const uint8_t
     if (!dense)
         if (int st = check_routing(route)) return st;
     const ExpertJob job = dense ? dense_job(*w13, I, H, M) : routed_job(*w13, I, H, *route, M, E, k);
-    const size_t need = gate_up_fp4_partials_bytes(job);
+    Carver c(nullptr);
+    carve_gate_up(c, job, M, H, k, dense);
+    const size_t need = c.off;
     if (need && (!workspace || !aligned256(workspace) || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
-    return hip_status(launch_gate_up_fp4(job, a_q, a_s, h_q, h_s, static_cast<float*>(workspace), stream));
+    Carver cw(workspace);
+    const GateUpWs w = carve_gate_up(cw, job, M, H, k, dense);
+    hipError_t e = hipSuccess;
+    if (!dense) {  // the kernel reads an expert's rows contiguously: bucket order
+        e = launch_gather_pairs(a_q, a_s, route->bucket, k, M, H, w.aq, w.as, stream);
+        a_q = w.aq;
+        a_s = w.as;
+    }
+    if (e == hipSuccess) e = launch_gate_up_fp4(job, a_q, a_s, h_q, h_s, w.part, stream);
+    return hip_status(e);
 }
 
 int moe_expert_down(const moe_weights* w2, const uint8_t* h_q, const uint8_t* h_s,
@@ -275,9 +322,9 @@ int check_desc(const moe_layer_desc* d) {
 
 struct LayerWs {
     RouteWs route;
-    int32_t *ids, *offsets, *bucket, *tile_e, *tile_b, *tile_r, *num_tiles, *active, *num_active;
+    int32_t *ids, *offsets, *bucket, *tile_e, *tile_b, *tile_r, *num_tiles, *active, *num_active, *act_off;
     float* w;
-    uint8_t *xq, *xs, *hq, *hs, *hsq, *hss;
+    uint8_t *xq, *xs, *xqt, *xst, *hq, *hs, *hsq, *hss;
     uint16_t* hsb;
     float* sh_part;
     float* part;     // routed gate_up split-K partials
@@ -303,8 +350,14 @@ LayerWs carve_layer(Carver& c, const moe_layer_desc* d) {
     L.num_tiles = c.take<int32_t>(1);
     L.active = c.take<int32_t>(std::min(E, P));
     L.num_active = c.take<int32_t>(1);
-    L.xq = c.take<uint8_t>((size_t)M * H);
-    L.xs = c.take<uint8_t>((size_t)M * H / 32);
+    L.act_off = c.take<int32_t>(std::min(E, P) + 1);
+    L.xq = c.take<uint8_t>((size_t)P * H);       // bucket order
+    L.xs = c.take<uint8_t>((size_t)P * H / 32);
+    L.xqt = L.xst = nullptr;
+    if (sh && !shb) {                            // token order for the FP4 shared expert
+        L.xqt = c.take<uint8_t>((size_t)M * H);
+        L.xst = c.take<uint8_t>((size_t)M * H / 32);
+    }
     L.hq = c.take<uint8_t>((size_t)P * I);
     L.hs = c.take<uint8_t>((size_t)P * I / 32);
     L.hsq = L.hss = nullptr;
@@ -363,6 +416,7 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
     r.num_tiles = L.num_tiles;
     r.active_experts = L.active;
     r.num_active = L.num_active;
+    r.active_offsets = L.act_off;
 
     const RouterPlan p = router_plan(M, H, E);
     hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials,
@@ -370,13 +424,13 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
     if (e == hipSuccess)
         e = launch_topk_bucket(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale,
                                logits_out, r, L.route.counters, stream);
-    if (e == hipSuccess) e = launch_quant_mxfp8(x, M, H, L.xq, L.xs, stream);
+    if (e == hipSuccess) e = launch_quant_pairs(x, r.bucket, k, M, H, L.xq, L.xs, L.xqt, L.xst, stream);
     const ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
     if (e == hipSuccess) e = launch_gate_up_fp4(gu, L.xq, L.xs, L.hq, L.hs, L.part, stream);
     if (e == hipSuccess && sf == MOE_FMT_BF16)
         e = launch_gate_up_bf16(dense_job(d->sh13, Ish, H, M), x, L.hsb, L.sh_part, stream);
     else if (e == hipSuccess && sf != MOE_FMT_NONE)
-        e = launch_gate_up_fp4(dense_job(d->sh13, Ish, H, M), L.xq, L.xs, L.hsq, L.hss, L.sh_fpart, stream);
+        e = launch_gate_up_fp4(dense_job(d->sh13, Ish, H, M), L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart, stream);
     const ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);
     if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream);
     if (e == hipSuccess && sf == MOE_FMT_BF16)

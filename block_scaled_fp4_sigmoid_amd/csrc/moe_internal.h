@@ -31,8 +31,20 @@ hipError_t launch_topk_bucket(const float* partials, int splits, const float* bi
                               int k, float routed_scale, float* logits_out,
                               const moe_routing& route, int* counter, hipStream_t stream);
 
+// FP4 weights in the load-order layout (moe_pack_fp4).
+size_t packed_scale_bytes(int fmt, int E, int N, int K);
+hipError_t launch_pack_fp4(int fmt, int E, int N, int K, const uint8_t* w, const uint8_t* sc, uint8_t* w_out,
+                           uint8_t* sc_out, hipStream_t stream);
+
 hipError_t launch_quant_mxfp8(const uint16_t* x, int M, int K, uint8_t* q, uint8_t* s,
                               hipStream_t stream);
+// MXFP8 rows in bucket order: qp/sp row b holds token bucket[b] / k (P = M*k
+// rows); with qt != nullptr also the M token-ordered rows into qt/st.
+hipError_t launch_quant_pairs(const uint16_t* x, const int32_t* bucket, int k, int M, int K, uint8_t* qp,
+                              uint8_t* sp, uint8_t* qt, uint8_t* st, hipStream_t stream);
+// Token-ordered MXFP8 rows -> bucket order.
+hipError_t launch_gather_pairs(const uint8_t* a_q, const uint8_t* a_s, const int32_t* bucket, int k, int M, int K,
+                               uint8_t* qp, uint8_t* sp, hipStream_t stream);
 
 // Expert GEMM jobs.  A routed job covers slots [0, U_max) of the active-expert
 // list; a dense job is one expert over all M rows.
@@ -46,6 +58,7 @@ struct ExpertJob {
     const int32_t* bucket;
     const int32_t* active;
     const int32_t* num_active;
+    const int32_t* active_offsets;  // [slots + 1] bucket range of each slot
     int slots;              // U_max for routed, 1 for dense
     int k;                  // top-k (pair id -> row)
     int M;

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355.so")
 MOE_FMT_NONE, MOE_FMT_MXFP4, MOE_FMT_NVFP4, MOE_FMT_BF16 = 0, 1, 2, 3
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
 
-EXPORTS = ["moe_status_str", "moe_abi_version", "moe_tile_capacity", "moe_route_workspace_bytes",
+EXPORTS = ["moe_status_str", "moe_abi_version", "moe_tile_capacity", "moe_packed_scale_bytes",
+           "moe_pack_fp4", "moe_route_workspace_bytes",
            "moe_route_topk", "moe_quant_act_mxfp8", "moe_gate_up_workspace_bytes",
            "moe_expert_gate_up", "moe_expert_down", "moe_finalize_rmsnorm",
            "moe_layer_workspace_bytes", "moe_layer"]
@@ -34,7 +35,7 @@ class moe_weights(C.Structure):
 class moe_routing(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("topk_ids", "topk_w", "expert_offsets", "bucket",
                                           "tile_expert", "tile_begin", "tile_rows", "num_tiles",
-                                          "active_experts", "num_active")]
+                                          "active_experts", "num_active", "active_offsets")]
 
 
 class moe_layer_desc(C.Structure):
@@ -62,6 +63,10 @@ def lib() -> C.CDLL:
         L.moe_abi_version.restype = i
         L.moe_tile_capacity.restype = i
         L.moe_tile_capacity.argtypes = [i, i, i]
+        L.moe_packed_scale_bytes.restype = sz
+        L.moe_packed_scale_bytes.argtypes = [i, i, i, i]
+        L.moe_pack_fp4.restype = i
+        L.moe_pack_fp4.argtypes = [i, i, i, i, vp, vp, vp, vp, vp]
         L.moe_route_workspace_bytes.restype = sz
         L.moe_route_workspace_bytes.argtypes = [i, i, i, i]
         L.moe_route_topk.restype = i
@@ -130,9 +135,33 @@ class Weights:
     w: Optional[torch.Tensor] = None
     scales: Optional[torch.Tensor] = None
     global_scale: Optional[torch.Tensor] = None
+    packed: bool = False  # FP4: in the load-order layout of moe_pack_fp4
 
     def c(self) -> moe_weights:
         return moe_weights(self.fmt, _p(self.w), _p(self.scales), _p(self.global_scale))
+
+
+def _need_packed(*ws: "Weights"):
+    for w in ws:
+        if w.fmt in (MOE_FMT_MXFP4, MOE_FMT_NVFP4) and not w.packed:
+            raise ValueError("FP4 weights must be in the load-order layout: pass them through pack_fp4")
+
+
+def pack_fp4(w: "Weights", stream=None) -> "Weights":
+    """Standard-layout FP4 weights -> the load-order layout the expert GEMMs
+    take (moe_pack_fp4); bf16 and absent weights are returned unchanged."""
+    if w.fmt not in (MOE_FMT_MXFP4, MOE_FMT_NVFP4):
+        return w
+    E, N = w.w.shape[0], w.w.shape[1]
+    K = 2 * w.w.shape[2]
+    nb = lib().moe_packed_scale_bytes(w.fmt, E, N, K)
+    if nb == 0:
+        raise ValueError(f"unsupported FP4 matrix shape E={E} N={N} K={K}")
+    w_out = torch.empty_like(w.w)
+    s_out = torch.empty(nb, dtype=torch.uint8, device=w.w.device)
+    _check(lib().moe_pack_fp4(w.fmt, E, N, K, _p(w.w), _p(w.scales), _p(w_out), _p(s_out), _stream(stream)),
+           "moe_pack_fp4")
+    return Weights(w.fmt, w_out, s_out, w.global_scale, packed=True)
 
 
 class Routing:
@@ -153,6 +182,7 @@ class Routing:
         self.num_tiles = torch.empty(1, **i32)
         self.active_experts = torch.empty(min(E, P), **i32)
         self.num_active = torch.empty(1, **i32)
+        self.active_offsets = torch.empty(min(E, P) + 1, **i32)
 
     def c(self) -> moe_routing:
         return moe_routing(*[_p(getattr(self, n)) for n, _ in moe_routing._fields_])
@@ -180,6 +210,7 @@ def quant_act_mxfp8(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream=No
 
 def expert_gate_up(w13: Weights, M, H, I, E, k, routing: Optional[Routing] = None, a_q=None,
                    a_s=None, a_bf16=None, h_q=None, h_s=None, h_bf16=None, ws=None, stream=None):
+    _need_packed(w13)
     dense = routing is None
     dev = (a_q if a_q is not None else a_bf16).device
     need = lib().moe_gate_up_workspace_bytes(w13.fmt, M, H, I, E, k, int(dense))
@@ -195,6 +226,7 @@ def expert_gate_up(w13: Weights, M, H, I, E, k, routing: Optional[Routing] = Non
 
 def expert_down(w2: Weights, M, H, I, E, k, y, routing: Optional[Routing] = None, h_q=None,
                 h_s=None, h_bf16=None, stream=None):
+    _need_packed(w2)
     wc = w2.c()
     r = None if routing is None else routing.c()
     rc = lib().moe_expert_down(C.byref(wc), _p(h_q), _p(h_s), _p(h_bf16),
@@ -216,6 +248,7 @@ class Layer:
 
     def __init__(self, M, H, E, k, I, I_sh, routed_scale, eps, w_router, router_bias,
                  w13: Weights, w2: Weights, sh13: Weights, sh2: Weights, gamma):
+        _need_packed(w13, w2, sh13, sh2)
         self._keep = (w_router, router_bias, w13, w2, sh13, sh2, gamma)
         self.M, self.H, self.E, self.k = M, H, E, k
         self.desc = moe_layer_desc(M, H, E, k, I, I_sh, float(routed_scale), float(eps),
@@ -228,6 +261,7 @@ class Layer:
 
     def set_weights(self, w13: Weights, w2: Weights, sh13: Weights, sh2: Weights):
         """Point the layer at another copy of its weights (same shapes)."""
+        _need_packed(w13, w2, sh13, sh2)
         self.desc.w13, self.desc.w2, self.desc.sh13, self.desc.sh2 = w13.c(), w2.c(), sh13.c(), sh2.c()
         self._keep = self._keep[:2] + (w13, w2, sh13, sh2) + self._keep[6:]
 

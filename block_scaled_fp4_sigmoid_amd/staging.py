@@ -2,8 +2,10 @@
 
 Pure data movement: host arrays are copied to the GPU and each expert matrix
 is assembled there from the generator's row pool with index_select, giving
-the canonical layouts of include/moe.h ([E, N, K/2] packed, [E, N, K/32|K/16]
-scales, [E] globals).  Nothing here computes a step of the layer.
+the standard layouts of include/moe.h ([E, N, K/2] packed, [E, N, K/32|K/16]
+scales, [E] globals); FP4 matrices are then put into the GEMMs' load order
+with moe_pack_fp4 (a permutation of bytes).  Nothing here computes a step of
+the layer.
 """
 from __future__ import annotations
 
@@ -14,7 +16,7 @@ import numpy as np
 import torch
 
 from . import synth
-from .moe import (MOE_FMT_BF16, MOE_FMT_NONE, Layer, Weights)
+from .moe import (MOE_FMT_BF16, MOE_FMT_NONE, Layer, Weights, pack_fp4)
 
 
 def _t(a: np.ndarray, device) -> torch.Tensor:
@@ -28,7 +30,7 @@ def pooled_on(pe: synth.PooledExperts, device) -> Weights:
     packed = pool.index_select(0, idx).reshape(pe.E, pe.N, -1).contiguous()
     scales = pool_s.index_select(0, idx).reshape(pe.E, pe.N, -1).contiguous()
     g = _t(pe.gscale.astype(np.float32), device)
-    return Weights(pe.fmt, packed, scales, g)
+    return pack_fp4(Weights(pe.fmt, packed, scales, g))
 
 
 def matrix_on(m: Optional[synth.Matrix], device) -> Weights:
@@ -37,12 +39,13 @@ def matrix_on(m: Optional[synth.Matrix], device) -> Weights:
     if m.fmt == synth.BF16:
         return Weights(MOE_FMT_BF16, _t(m.bf16, device))
     g = torch.tensor([m.gscale], dtype=torch.float32, device=device)
-    return Weights(m.fmt, _t(m.packed, device), _t(m.scales, device), g)
+    w = Weights(m.fmt, _t(m.packed, device)[None], _t(m.scales, device)[None], g)
+    return pack_fp4(w)
 
 
 def clone_weights(w: Weights) -> Weights:
     c = lambda t: None if t is None else t.clone()
-    return Weights(w.fmt, c(w.w), c(w.scales), c(w.global_scale))
+    return Weights(w.fmt, c(w.w), c(w.scales), c(w.global_scale), packed=w.packed)
 
 
 @dataclass
@@ -64,8 +67,8 @@ class DeviceInputs:
 
     def weight_bytes_per_expert(self) -> int:
         s = self.shape
-        per = lambda w: (w.w[0].numel() + w.scales[0].numel() + (4 if w.global_scale is not None
-                                                                 and s.wfmt == synth.NVFP4 else 0))
+        per = lambda w: (w.w[0].numel() + w.scales.numel() // w.w.shape[0]
+                         + (4 if w.global_scale is not None and s.wfmt == synth.NVFP4 else 0))
         return per(self.w13) + per(self.w2)
 
 

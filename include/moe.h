@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 3
 
 enum moe_status {
     MOE_OK = 0,
@@ -65,10 +65,14 @@ enum moe_fmt {
 };
 
 /* One projection of E experts (or of the shared expert, E = 1), each a
- * matrix [N, K] with K contiguous:
- *   MXFP4: w = packed [E, N, K/2], scales = E8M0 [E, N, K/32], global unused;
+ * matrix [N, K].  Standard layout, K contiguous:
+ *   MXFP4: w = packed [E, N, K/2] (two E2M1 per byte, low nibble first),
+ *          scales = E8M0 [E, N, K/32], global unused;
  *   NVFP4: w = packed [E, N, K/2], scales = E4M3 [E, N, K/16], global = fp32 [E];
  *   BF16:  w = bf16 [E, N, K], scales and global unused.
+ * The expert GEMMs and moe_layer take FP4 weights in the load-order layout
+ * that moe_pack_fp4 produces from the standard one (same values, other
+ * places); bf16 weights are taken as they are.
  * Gate_up weights (W13) have N = 2I with rows [0, I) the gate projection and
  * rows [I, 2I) the up projection; down weights (W2) have N = H, K = I. */
 typedef struct moe_weights {
@@ -92,7 +96,12 @@ typedef struct moe_weights {
  *   num_tiles      int32 [1]
  *   active_experts int32 [min(E, P)]  experts with at least one row, ascending;
  *                                entries past num_active are unspecified
- *   num_active     int32 [1] */
+ *   num_active     int32 [1]
+ *   active_offsets int32 [min(E, P) + 1]  active_offsets[s] =
+ *                                expert_offsets[active_experts[s]] for s <
+ *                                num_active, P from num_active on (so slot s
+ *                                holds bucket entries [active_offsets[s],
+ *                                active_offsets[s+1]) and unused slots none) */
 typedef struct moe_routing {
     int32_t *topk_ids;
     float *topk_w;
@@ -104,6 +113,7 @@ typedef struct moe_routing {
     int32_t *num_tiles;
     int32_t *active_experts;
     int32_t *num_active;
+    int32_t *active_offsets;
 } moe_routing;
 
 /* The whole layer's parameters. */
@@ -123,6 +133,27 @@ int moe_abi_version(void);
 
 /* Upper bound on the number of 8-row tiles: sum_e ceil(n_e/8) <= ceil(P/8) + min(E, P). */
 int moe_tile_capacity(int M, int E, int k);
+
+/* ---------------------------------------------------------------------------
+ * moe_pack_fp4 — puts FP4 expert weights into the order in which the gfx950
+ * expert GEMMs load them; done once, when the weights are loaded.
+ *   Pages: SGLang Spark GB10 Optimizations, section 1 (NVFP4 weights with one
+ *   FP8 scale per 16 values along K); README DeepSeek-V4.1 slot table, row
+ *   "Routed experts (moe)" (block-scaled expert GEMMs).
+ * In: fmt MXFP4 or NVFP4; w, scales in the standard layout above (device).
+ * Out: w_out (E*N*K/2 bytes) and scales_out (moe_packed_scale_bytes bytes),
+ *   device memory not overlapping the inputs.  With S = K/128, Q = ceil(S/4),
+ *   rb a block of 16 rows and lane l = 16g + i (row 16rb + i):
+ *     w_out      [E][N/16][S][64][16]: lane l of step s holds the row's bytes
+ *                [64s + 16g, +16);
+ *     MX scales  [E][N/16][Q][64][4]: byte u = E8M0 of K block 4(4q+u) + g;
+ *     NV scales  [E][N/16][Q][64][8]: bytes 2u, 2u+1 = E4M3 of K blocks
+ *                8(4q+u) + 2g and + 1;
+ *   entries of steps past S are zero.  NVFP4 global scales are not touched.
+ * Limits: E >= 1, N % 16 == 0, K % 128 == 0. */
+size_t moe_packed_scale_bytes(int fmt, int E, int N, int K);
+int moe_pack_fp4(int fmt, int E, int N, int K, const uint8_t *w, const uint8_t *scales,
+                 uint8_t *w_out, uint8_t *scales_out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_route_topk — router GEMV, sigmoid top-k with renormalized weights, and

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert moe.abi_version() == 1
+    assert moe.abi_version() == 3
     for rc in range(5):
         assert len(moe.status_str(rc)) > 0
     assert "unknown" in moe.status_str(99)
@@ -56,7 +56,10 @@ def test_workspace_sizes(L):
     few = L.moe_gate_up_workspace_bytes(moe.MOE_FMT_MXFP4, 8, 7168, 256, 1, 1, 1)
     assert few > 0 and few % (8 * 2 * 256 * 4) == 0 and few % 256 == 0
     assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_NVFP4, 8, 7168, 256, 256, 8, 0) > 0
-    assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_MXFP4, 4, 1024, 512, 16, 4, 0) == 0
+    # routed FP4: the activations in bucket order (P*H codes, P*H/32 scales), no split here
+    al = lambda n: (n + 255) // 256 * 256
+    P = 64 * 8
+    assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_MXFP4, 64, 512, 2048, 64, 8, 0) == al(P * 512) + al(P * 16)
     assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_MXFP4, 8, 100, 256, 1, 1, 1) == 0   # H % 128
     assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_BF16, 8, 7168, 256, 256, 8, 0) == 0  # bf16 routed
 

@@ -78,6 +78,11 @@ def test_route_topk_parity(M, H, E, k, bias, scale):
     act = np.nonzero(counts)[0]
     na = int(np_of(rt.num_active)[0])
     assert na == len(act) and np.array_equal(np_of(rt.active_experts)[:na], act)
+    # slot ranges: the active experts' offsets, then P for every unused slot
+    U = min(E, M * k)
+    want = np.full(U + 1, M * k, dtype=np.int64)
+    want[:na] = r["offsets"][act]
+    assert np.array_equal(np_of(rt.active_offsets), want)
     # routing from logits_in gives the same result
     rt2 = moe.Routing(M, E, k, DEV)
     moe.route_topk(rt2, logits_in=logits, bias=bias_t, routed_scale=scale)
@@ -238,3 +243,40 @@ def test_finalize_parity():
         assert np.all(diff <= allowed) and (gr[r] != rb).mean() < 0.01
         assert rel_l2(bf16_to_f64(go[r]), o64) < 4e-3
         assert np.max(np.abs(bf16_to_f64(go[r]) - o64)) < 3e-2
+
+
+@pytest.mark.parametrize("fmt,N,K", [(synth.MXFP4, 48, 640), (synth.NVFP4, 32, 384),
+                                     (synth.MXFP4, 16, 1024), (synth.NVFP4, 64, 2048)])
+def test_pack_fp4_layout(fmt, N, K):
+    """moe_pack_fp4 against the layout written out in moe.h (numpy, byte by byte);
+    K = 640 and 384 leave a partial last quad (zero entries)."""
+    E = 3
+    S, Q = K // 128, (K // 128 + 3) // 4
+    rng = np.random.default_rng(N + K)
+    nb = K // (32 if fmt == synth.MXFP4 else 16)
+    w = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    sc = rng.integers(0, 256, (E, N, nb), dtype=np.uint8)
+    g = torch.ones(E, dtype=torch.float32, device=DEV)
+    P = moe.pack_fp4(moe.Weights(fmt, torch.from_numpy(w).to(DEV), torch.from_numpy(sc).to(DEV), g))
+    torch.cuda.synchronize()
+    pw = np_of(P.w).reshape(E, N // 16, S, 64, 16)
+    ps = np_of(P.scales)
+    for e in range(E):
+        for rb in range(N // 16):
+            for l in range(64):
+                i, gg = l % 16, l // 16
+                row = 16 * rb + i
+                for st in range(S):
+                    assert np.array_equal(pw[e, rb, st, l], w[e, row, 64 * st + 16 * gg:64 * st + 16 * gg + 16])
+    if fmt == synth.MXFP4:
+        ps = ps.reshape(E, N // 16, Q, 64, 4)
+        for e, rb, q, l, u in np.ndindex(E, N // 16, Q, 64, 4):
+            i, gg = l % 16, l // 16
+            want = sc[e, 16 * rb + i, 4 * (4 * q + u) + gg] if 4 * q + u < S else 0
+            assert ps[e, rb, q, l, u] == want
+    else:
+        ps = ps.reshape(E, N // 16, Q, 64, 8)
+        for e, rb, q, l, u, h in np.ndindex(E, N // 16, Q, 64, 4, 2):
+            i, gg = l % 16, l // 16
+            want = sc[e, 16 * rb + i, 8 * (4 * q + u) + 2 * gg + h] if 4 * q + u < S else 0
+            assert ps[e, rb, q, l, 2 * u + h] == want
