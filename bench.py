@@ -159,9 +159,9 @@ def main():
         rt = moe.Routing(s.M, s.E, s.k, dev)
         moe.route_topk(rt, x=d.x, w_router=d.Wr, bias=d.bias, routed_scale=s.routed_scale,
                        logits_out=logits)
-        xq = torch.empty((s.M, s.H), dtype=torch.uint8, device=dev)
-        xs = torch.empty((s.M, s.H // 32), dtype=torch.uint8, device=dev)
-        moe.quant_act_mxfp8(d.x, xq, xs)
+        xq = torch.empty((s.M * s.k, s.H), dtype=torch.uint8, device=dev)
+        xs = torch.empty((s.M * s.k, s.H // 32), dtype=torch.uint8, device=dev)
+        moe.quant_act_mxfp8(d.x, xq, xs, routing=rt)
         hq = torch.empty((s.M * s.k, s.I), dtype=torch.uint8, device=dev)
         hs = torch.empty((s.M * s.k, s.I // 32), dtype=torch.uint8, device=dev)
         for i in range(args.profile_gate_up):
@@ -199,16 +199,18 @@ def main():
     rt = moe.Routing(s.M, s.E, s.k, dev)
     moe.route_topk(rt, x=d.x, w_router=d.Wr, bias=d.bias, routed_scale=s.routed_scale,
                    logits_out=logits)
-    xq = torch.empty((s.M, s.H), dtype=torch.uint8, device=dev)
-    xs = torch.empty((s.M, s.H // 32), dtype=torch.uint8, device=dev)
-    moe.quant_act_mxfp8(d.x, xq, xs)
+    xq = torch.empty((s.M * s.k, s.H), dtype=torch.uint8, device=dev)
+    xs = torch.empty((s.M * s.k, s.H // 32), dtype=torch.uint8, device=dev)
+    moe.quant_act_mxfp8(d.x, xq, xs, routing=rt)
     hq = torch.empty((s.M * s.k, s.I), dtype=torch.uint8, device=dev)
     hs = torch.empty((s.M * s.k, s.I // 32), dtype=torch.uint8, device=dev)
     w13s = [d.w13] + [k_[0] for k_ in keep]
+    gu_ws = moe.workspace(max(256, moe.lib().moe_gate_up_workspace_bytes(d.w13.fmt, s.M, s.H, s.I, s.E,
+                                                                         s.k, 0)), dev)
 
     def gate_up(i):
         moe.expert_gate_up(w13s[i % copies], s.M, s.H, s.I, s.E, s.k, routing=rt, a_q=xq, a_s=xs,
-                           h_q=hq, h_s=hs)
+                           h_q=hq, h_s=hs, ws=gu_ws)
 
     ms_gu = timed(gate_up, args.steps, args.warmup, stream)
     gu_gbps = bm["gate_up_launch"] / (ms_gu * 1e-3) / 1e9

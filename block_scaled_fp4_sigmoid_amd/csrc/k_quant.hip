@@ -10,9 +10,9 @@
 // one scale byte out.  amax comes from the bf16 bit patterns (integer max of
 // the magnitudes, exact for subnormals too).
 //
-// The layer quantizes straight into bucket order (row of bucket position b =
-// the token of pair bucket[b]), so the expert GEMMs find an expert's rows
-// contiguous; a gather does the same for token-ordered codes.
+// With a routing the rows are written in bucket order (row of bucket position
+// b = the token of pair bucket[b]), so the expert GEMMs find an expert's rows
+// contiguous.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -94,21 +94,6 @@ __global__ __launch_bounds__(256) void k_quant_pairs(const uint16_t* __restrict_
     }
 }
 
-// Token-ordered MXFP8 rows -> bucket order (row b = token bucket[b] / k).
-// Thread = 16 code bytes of a row; the first K/32 threads of the row also
-// copy one scale byte each.
-__global__ __launch_bounds__(256) void k_gather_pairs(const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_s,
-                                                      const int32_t* __restrict__ bucket, int k, int P, int K,
-                                                      uint8_t* __restrict__ qp, uint8_t* __restrict__ sp) {
-    const int cpr = K / 16;
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    const int row = idx / cpr, c = idx - row * cpr;
-    if (row >= P) return;
-    const int tok = bucket[row] / k;
-    *reinterpret_cast<v4i*>(qp + (size_t)row * K + 16 * c) = load16(a_q + (size_t)tok * K + 16 * c);
-    if (c < K / 32) sp[(size_t)row * (K / 32) + c] = a_s[(size_t)tok * (K / 32) + c];
-}
-
 hipError_t launch_quant_mxfp8(const uint16_t* x, int M, int K, uint8_t* q, uint8_t* s,
                               hipStream_t stream) {
     const int nblocks = M * (K / 32);
@@ -122,15 +107,6 @@ hipError_t launch_quant_pairs(const uint16_t* x, const int32_t* bucket, int k, i
     const long n = (long)(P + Mt) * (K / 32);
     hipLaunchKernelGGL(k_quant_pairs, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, x, bucket, k, P, Mt, K,
                        qp, sp, qt, st);
-    return hipGetLastError();
-}
-
-hipError_t launch_gather_pairs(const uint8_t* a_q, const uint8_t* a_s, const int32_t* bucket, int k, int M, int K,
-                               uint8_t* qp, uint8_t* sp, hipStream_t stream) {
-    const int P = M * k;
-    const long n = (long)P * (K / 16);
-    hipLaunchKernelGGL(k_gather_pairs, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a_q, a_s, bucket, k,
-                       P, K, qp, sp);
     return hipGetLastError();
 }
 

@@ -59,7 +59,7 @@ constexpr int kPassRows = 32;           // activation rows per pass (two 16-row 
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every record count
 
 #ifndef MOE_STREAM_TARGET_ITEMS
-#define MOE_STREAM_TARGET_ITEMS 1024  // gate_up splits K until about this many items
+#define MOE_STREAM_TARGET_ITEMS 256  // gate_up splits K until about this many items
 #endif
 #ifndef MOE_MIN_BLOCKS
 #define MOE_MIN_BLOCKS 2  // workgroups per CU the register budget must allow
@@ -199,19 +199,38 @@ __device__ __forceinline__ Coord<FMT, MB, NB> make_coord(const StreamJob& J, int
     return c;
 }
 
-// A ring slot holds one quad (4 K steps).
-template <int MB, int NB, int DQ>
+// A ring slot holds one quad: QS K steps (4, or fewer when the whole K is
+// shorter than a quad) and the weight scales of the quad.
+template <int MB, int NB, int DQ, int QS>
 struct Ring {
-    v4i a[DQ][4][MB];
+    v4i a[DQ][QS][MB];
     uint32_t as[DQ][MB][2];
-    v4i b[DQ][4][NB][2];
-    uint32_t bs[DQ][4][NB];
+    v4i b[DQ][QS][NB][2];
+    uint32_t bs[DQ][QS][NB];
 };
 
-// Loads quad q (absolute) into slot v; steps at or past s_end load zeros.
-template <int FMT, int MB, int NB, int DQ>
-__device__ __forceinline__ void ring_load(Ring<MB, NB, DQ>& R, int v, const Coord<FMT, MB, NB>& c, int q,
-                                          int s_end) {
+// Loads step u of quad q (absolute) into slot v; steps at or past s_end load zeros.
+template <int FMT, int MB, int NB, int DQ, int QS>
+__device__ __forceinline__ void ring_load_step(Ring<MB, NB, DQ, QS>& R, int v, int u, const Coord<FMT, MB, NB>& c,
+                                               int q, int s_end) {
+    const int st = 4 * q + u;
+    const bool ok = st < s_end;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        R.a[v][u][mb] = __builtin_amdgcn_raw_buffer_load_b128(c.rw, ok ? c.vw[mb] : kOOB, 1024 * st, MOE_WEIGHT_AUX);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const uint32_t va = ok ? c.va[j] : kOOB;
+        R.b[v][u][j][0] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, va, 128 * st, 0);
+        R.b[v][u][j][1] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, va + (FMT == kFmtMX ? 64 : 16), 128 * st, 0);
+        R.bs[v][u][j] = __builtin_amdgcn_raw_buffer_load_b32(c.ras, ok ? c.vas[j] : kOOB, 4 * st, 0);
+    }
+}
+
+// Loads the weight scales of quad q (absolute) into slot v.
+template <int FMT, int MB, int NB, int DQ, int QS>
+__device__ __forceinline__ void ring_load_scales(Ring<MB, NB, DQ, QS>& R, int v, const Coord<FMT, MB, NB>& c, int q,
+                                                 int s_end) {
     const bool okq = 4 * q < s_end;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -223,26 +242,11 @@ __device__ __forceinline__ void ring_load(Ring<MB, NB, DQ>& R, int v, const Coor
             R.as[v][mb][1] = sv[1];
         }
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int st = 4 * q + u;
-        const bool ok = st < s_end;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            R.a[v][u][mb] = __builtin_amdgcn_raw_buffer_load_b128(c.rw, ok ? c.vw[mb] : kOOB, 1024 * st, MOE_WEIGHT_AUX);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const uint32_t va = ok ? c.va[j] : kOOB;
-            R.b[v][u][j][0] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, va, 128 * st, 0);
-            R.b[v][u][j][1] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, va + (FMT == kFmtMX ? 64 : 16), 128 * st, 0);
-            R.bs[v][u][j] = __builtin_amdgcn_raw_buffer_load_b32(c.ras, ok ? c.vas[j] : kOOB, 4 * st, 0);
-        }
-    }
 }
 
 // Step u of the quad in slot v.
-template <int FMT, int MB, int NB, int DQ, int U>
-__device__ __forceinline__ void step_mfma(const Ring<MB, NB, DQ>& R, int v, const int (&sfo)[NB],
+template <int FMT, int MB, int NB, int DQ, int QS, int U>
+__device__ __forceinline__ void step_mfma(const Ring<MB, NB, DQ, QS>& R, int v, const int (&sfo)[NB],
                                           v4f (&acc)[MB][2]) {
     const int g = (threadIdx.x & 63) >> 4;
     if constexpr (FMT == kFmtMX) {
@@ -318,11 +322,29 @@ __device__ __forceinline__ void row_smax(const Coord<FMT, MB, NB>& c, int s0, in
     }
 }
 
+// Steps U..QS-1 of the quad in slot v, each followed by its refill with quad
+// qn; the quad's scales are refilled after its last step, before that step's
+// refill.
+template <int FMT, int MB, int NB, int DQ, int QS, int U>
+__device__ __forceinline__ void quad_steps(Ring<MB, NB, DQ, QS>& R, int v, const Coord<FMT, MB, NB>& c, int qn,
+                                           int s_end, const int (&sfo)[NB], v4f (&acc)[MB][2]) {
+    if constexpr (U < QS) {
+        // keep each step's instructions in place: hoisting the use of a later
+        // slot would wait for that slot's loads and drain the ring
+        __builtin_amdgcn_sched_barrier(0);
+        step_mfma<FMT, MB, NB, DQ, QS, U>(R, v, sfo, acc);
+        if constexpr (U == QS - 1) ring_load_scales<FMT, MB, NB, DQ, QS>(R, v, c, qn, s_end);
+        ring_load_step<FMT, MB, NB, DQ, QS>(R, v, U, c, qn, s_end);
+        quad_steps<FMT, MB, NB, DQ, QS, U + 1>(R, v, c, qn, s_end, sfo, acc);
+    }
+}
+
 // All of one pass: K steps [s0, s0 + nst) (s0 a multiple of 4) of MB weight
 // blocks against NB blocks of activation rows arow0 + [0, npass).  The ring
-// holds DQ quads and is refilled DQ quads ahead; steps past the range load
-// zeros for both operands.
-template <int FMT, int MB, int NB, int DQ>
+// holds DQ quads; each step's slot is refilled right after its MFMAs, so
+// DQ*QS - 1 steps stay in flight.  Steps past the range load zeros for both
+// operands.  QS < 4 only when all of K is one quad of QS steps.
+template <int FMT, int MB, int NB, int DQ, int QS>
 __device__ __forceinline__ void stream_pass(const StreamJob& J, int e, const int (&wblk)[MB], int arow0, int npass,
                                             int s0, int nst, int (&smax)[NB], v4f (&acc)[MB][2]) {
     const Coord<FMT, MB, NB> c = make_coord<FMT, MB, NB>(J, e, wblk, arow0, npass);
@@ -339,39 +361,31 @@ __device__ __forceinline__ void stream_pass(const StreamJob& J, int e, const int
         }
     }
     const int q0 = s0 / 4, nq = (nst + 3) / 4, s_end = s0 + nst;
-    Ring<MB, NB, DQ> R;
+    Ring<MB, NB, DQ, QS> R;
 #pragma unroll
-    for (int v = 0; v < DQ; ++v) ring_load<FMT, MB, NB, DQ>(R, v, c, q0 + v, s_end);
+    for (int v = 0; v < DQ; ++v) {
+        ring_load_scales<FMT, MB, NB, DQ, QS>(R, v, c, q0 + v, s_end);
+#pragma unroll
+        for (int u = 0; u < QS; ++u) ring_load_step<FMT, MB, NB, DQ, QS>(R, v, u, c, q0 + v, s_end);
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[mb][j] = v4f{0.f, 0.f, 0.f, 0.f};
     for (int l0 = 0; l0 < nq; l0 += DQ) {
 #pragma unroll
-        for (int v = 0; v < DQ; ++v) {
-            // keep each step's instructions in place: hoisting the use of a
-            // later slot would wait for that slot's loads and drain the ring
-            __builtin_amdgcn_sched_barrier(0);
-            step_mfma<FMT, MB, NB, DQ, 0>(R, v, sfo, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            step_mfma<FMT, MB, NB, DQ, 1>(R, v, sfo, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            step_mfma<FMT, MB, NB, DQ, 2>(R, v, sfo, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            step_mfma<FMT, MB, NB, DQ, 3>(R, v, sfo, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            ring_load<FMT, MB, NB, DQ>(R, v, c, q0 + l0 + v + DQ, s_end);
-        }
+        for (int v = 0; v < DQ; ++v)
+            quad_steps<FMT, MB, NB, DQ, QS, 0>(R, v, c, q0 + l0 + v + DQ, s_end, sfo, acc);
     }
 }
 
-// Ring depth in quads for MB weight blocks and NB activation blocks (about
-// 32 loads of 16 bytes per lane in flight for MXFP4, fewer for NVFP4, whose
-// dequantization needs registers).
+// Ring depth in quads for MB weight blocks and NB activation blocks: about
+// 32 loads of 16 bytes per lane in flight (the registers allow two quads
+// with two weight blocks and one activation block).
 template <int FMT, int MB, int NB>
 constexpr int ring_quads() {
     constexpr int per_quad = 4 * (MB + 2 * NB);
-    constexpr int budget = FMT == kFmtMX ? 32 : 24;
+    constexpr int budget = 32;
     return budget / per_quad < 1 ? 1 : budget / per_quad;
 }
 
@@ -449,12 +463,14 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_gate_up(StreamJob 
         int smax[2] = {0, 0};
         if (npass > 16) {
             int sm[2];
-            stream_pass<FMT, GMB, 2, ring_quads<FMT, GMB, 2>()>(J, tk.e, wblk, arow0, npass, s0, nst, sm, acc);
+            stream_pass<FMT, GMB, 2, ring_quads<FMT, GMB, 2>(), 4>(J, tk.e, wblk, arow0, npass, s0, nst, sm,
+                                                                     acc);
             smax[0] = sm[0];
             smax[1] = sm[1];
         } else {
             int sm[1];
-            stream_pass<FMT, GMB, 1, ring_quads<FMT, GMB, 1>()>(J, tk.e, wblk, arow0, npass, s0, nst, sm, acc);
+            stream_pass<FMT, GMB, 1, ring_quads<FMT, GMB, 1>(), 4>(J, tk.e, wblk, arow0, npass, s0, nst, sm,
+                                                                     acc);
             smax[0] = sm[0];
         }
         if constexpr (FUSED) {
@@ -550,7 +566,7 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_quant(const float* __restri
 // Activations are h rows in bucket order; the output row of bucket position b
 // is its pair id bucket[b] (the token row for a dense expert).
 
-template <int FMT, int MB>
+template <int FMT, int MB, int QS, int DQ>
 __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J, float* __restrict__ y) {
     const int H = J.N, I = J.K;
     constexpr int RB = 64 * MB;
@@ -582,12 +598,14 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J, 
         int smax[2] = {0, 0};
         if (npass > 16) {
             int sm[2];
-            stream_pass<FMT, MB, 2, ring_quads<FMT, MB, 2>()>(J, tk.e, wblk, arow0, npass, 0, nst, sm, acc);
+            stream_pass<FMT, MB, 2, DQ == 1 ? 1 : ring_quads<FMT, MB, 2>(), QS>(J, tk.e, wblk, arow0, npass, 0,
+                                                                                 nst, sm, acc);
             smax[0] = sm[0];
             smax[1] = sm[1];
         } else {
             int sm[1];
-            stream_pass<FMT, MB, 1, ring_quads<FMT, MB, 1>()>(J, tk.e, wblk, arow0, npass, 0, nst, sm, acc);
+            stream_pass<FMT, MB, 1, DQ == 1 ? 1 : ring_quads<FMT, MB, 1>(), QS>(J, tk.e, wblk, arow0, npass, 0,
+                                                                                 nst, sm, acc);
             smax[0] = sm[0];
         }
 #pragma unroll
@@ -626,13 +644,22 @@ GatePlan gate_plan(const ExpertJob& j) {
 }
 
 struct DownPlan {
-    int MB, nblk;
+    int MB, QS, DQ, nblk;
 };
 
+// A K of one quad or less runs a one-quad ring (nothing to prefetch) and
+// gets more 16-row blocks per wave: its items are otherwise too small to pay
+// for their start.
 DownPlan down_plan(const ExpertJob& j) {
     DownPlan p;
-    // a short K gets more 16-row blocks per wave
-    p.MB = (j.K <= 512 && j.N_out % 256 == 0) ? 4 : 2;
+    const int steps = j.K / 128;
+    p.QS = steps <= 2 ? 2 : 4;
+    p.DQ = steps <= 4 ? 1 : 2;
+    p.MB = 2;
+    if (steps <= 2)
+        p.MB = j.N_out % 512 == 0 ? 8 : (j.N_out % 256 == 0 ? 4 : 2);
+    else if (steps <= 4 && j.N_out % 256 == 0 && j.w.fmt == MOE_FMT_MXFP4)
+        p.MB = 4;  // (NVFP4's dequantization needs the registers)
     p.nblk = j.N_out / (64 * p.MB);
     return p;
 }
@@ -702,25 +729,37 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
     return hipGetLastError();
 }
 
+template <int FMT>
+hipError_t launch_down_f(const StreamJob& J, const DownPlan& p, int blocks, float* y, hipStream_t stream) {
+    const dim3 g(blocks), b(kThreads);
+    if (p.QS == 2) {
+        if (p.MB == 8)
+            hipLaunchKernelGGL((k_down<FMT, 8, 2, 1>), g, b, 0, stream, J, y);
+        else if (p.MB == 4)
+            hipLaunchKernelGGL((k_down<FMT, 4, 2, 1>), g, b, 0, stream, J, y);
+        else
+            hipLaunchKernelGGL((k_down<FMT, 2, 2, 1>), g, b, 0, stream, J, y);
+    } else if (p.DQ == 1) {
+        if constexpr (FMT == kFmtMX)
+            if (p.MB == 4) {
+                hipLaunchKernelGGL((k_down<FMT, 4, 4, 1>), g, b, 0, stream, J, y);
+                return hipGetLastError();
+            }
+        hipLaunchKernelGGL((k_down<FMT, 2, 4, 1>), g, b, 0, stream, J, y);
+    } else {
+        hipLaunchKernelGGL((k_down<FMT, 2, 4, 2>), g, b, 0, stream, J, y);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8_t* h_s, float* y,
                            hipStream_t stream) {
     const DownPlan p = down_plan(job);
     StreamJob J = stream_job(job, job.N_out, h_q, h_s, out_rows_of(job));
     J.nblk = p.nblk;
     const int blocks = job.slots * p.nblk;
-    const bool mx = job.w.fmt == MOE_FMT_MXFP4;
-    if (p.MB == 4) {
-        if (mx)
-            hipLaunchKernelGGL((k_down<kFmtMX, 4>), dim3(blocks), dim3(kThreads), 0, stream, J, y);
-        else
-            hipLaunchKernelGGL((k_down<kFmtNV, 4>), dim3(blocks), dim3(kThreads), 0, stream, J, y);
-    } else {
-        if (mx)
-            hipLaunchKernelGGL((k_down<kFmtMX, 2>), dim3(blocks), dim3(kThreads), 0, stream, J, y);
-        else
-            hipLaunchKernelGGL((k_down<kFmtNV, 2>), dim3(blocks), dim3(kThreads), 0, stream, J, y);
-    }
-    return hipGetLastError();
+    return job.w.fmt == MOE_FMT_MXFP4 ? launch_down_f<kFmtMX>(J, p, blocks, y, stream)
+                                      : launch_down_f<kFmtNV>(J, p, blocks, y, stream);
 }
 
 }  // namespace moe

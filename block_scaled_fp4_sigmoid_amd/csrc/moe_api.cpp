@@ -113,23 +113,6 @@ ExpertJob dense_job(const moe_weights& w, int N_out, int K, int M) {
     return j;
 }
 
-// FP4 gate_up workspace: [bucket-ordered activation codes P*H][their scales
-// P*H/32] (routed only) [split-K partials].
-struct GateUpWs {
-    uint8_t *aq, *as;
-    float* part;
-};
-
-GateUpWs carve_gate_up(Carver& c, const ExpertJob& job, int M, int H, int k, bool dense) {
-    GateUpWs w{nullptr, nullptr, nullptr};
-    if (!dense) {
-        w.aq = c.take<uint8_t>((size_t)M * k * H);
-        w.as = c.take<uint8_t>((size_t)M * k * (H / 32));
-    }
-    w.part = c.take<float>(gate_up_fp4_partials_bytes(job) / sizeof(float));
-    return w;
-}
-
 }  // namespace
 
 extern "C" {
@@ -205,11 +188,17 @@ int moe_route_topk(const uint16_t* x, const float* logits_in, const float* w_rou
     return hip_status(e);
 }
 
-int moe_quant_act_mxfp8(const uint16_t* x, int M, int K, uint8_t* q, uint8_t* s,
-                        hipStream_t stream) {
+int moe_quant_act_mxfp8(const uint16_t* x, int M, int K, const moe_routing* route, int k, uint8_t* q,
+                        uint8_t* s, hipStream_t stream) {
     if (!x || !q || !s || M < 1 || K < 32) return MOE_ERR_INVALID_ARG;
-    if (K % 32 != 0 || M > kMaxM * kMaxK || K > kMaxH) return MOE_ERR_UNSUPPORTED;
-    return hip_status(launch_quant_mxfp8(x, M, K, q, s, stream));
+    if (K % 32 != 0 || K > kMaxH) return MOE_ERR_UNSUPPORTED;
+    if (!route) {
+        if (M > kMaxM * kMaxK) return MOE_ERR_UNSUPPORTED;
+        return hip_status(launch_quant_mxfp8(x, M, K, q, s, stream));
+    }
+    if (!route->bucket) return MOE_ERR_INVALID_ARG;
+    if (k < 1 || k > kMaxK || M > kMaxM) return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_quant_pairs(x, route->bucket, k, M, K, q, s, nullptr, nullptr, stream));
 }
 
 size_t moe_gate_up_workspace_bytes(int fmt, int M, int H, int I, int E, int k, int dense) {
@@ -221,9 +210,7 @@ size_t moe_gate_up_workspace_bytes(int fmt, int M, int H, int I, int E, int k, i
     w.fmt = fmt;
     moe_routing r{};
     const ExpertJob job = dense ? dense_job(w, I, H, M) : routed_job(w, I, H, r, M, E, k);
-    Carver c(nullptr);
-    carve_gate_up(c, job, M, H, k, dense);
-    return c.off;
+    return gate_up_fp4_partials_bytes(job);
 }
 
 int moe_expert_gate_up(const moe_weights* w13, const uint8_t* a_q, const uint8_t* a_s,
@@ -247,20 +234,9 @@ int moe_expert_gate_up(const moe_weights* w13, const uint8_t* a_q, const uint8_t
     if (!dense)
         if (int st = check_routing(route)) return st;
     const ExpertJob job = dense ? dense_job(*w13, I, H, M) : routed_job(*w13, I, H, *route, M, E, k);
-    Carver c(nullptr);
-    carve_gate_up(c, job, M, H, k, dense);
-    const size_t need = c.off;
+    const size_t need = gate_up_fp4_partials_bytes(job);
     if (need && (!workspace || !aligned256(workspace) || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
-    Carver cw(workspace);
-    const GateUpWs w = carve_gate_up(cw, job, M, H, k, dense);
-    hipError_t e = hipSuccess;
-    if (!dense) {  // the kernel reads an expert's rows contiguously: bucket order
-        e = launch_gather_pairs(a_q, a_s, route->bucket, k, M, H, w.aq, w.as, stream);
-        a_q = w.aq;
-        a_s = w.as;
-    }
-    if (e == hipSuccess) e = launch_gate_up_fp4(job, a_q, a_s, h_q, h_s, w.part, stream);
-    return hip_status(e);
+    return hip_status(launch_gate_up_fp4(job, a_q, a_s, h_q, h_s, static_cast<float*>(workspace), stream));
 }
 
 int moe_expert_down(const moe_weights* w2, const uint8_t* h_q, const uint8_t* h_s,

@@ -42,9 +42,7 @@ hipError_t launch_quant_mxfp8(const uint16_t* x, int M, int K, uint8_t* q, uint8
 // rows); with qt != nullptr also the M token-ordered rows into qt/st.
 hipError_t launch_quant_pairs(const uint16_t* x, const int32_t* bucket, int k, int M, int K, uint8_t* qp,
                               uint8_t* sp, uint8_t* qt, uint8_t* st, hipStream_t stream);
-// Token-ordered MXFP8 rows -> bucket order.
-hipError_t launch_gather_pairs(const uint8_t* a_q, const uint8_t* a_s, const int32_t* bucket, int k, int M, int K,
-                               uint8_t* qp, uint8_t* sp, hipStream_t stream);
+
 
 // Expert GEMM jobs.  A routed job covers slots [0, U_max) of the active-expert
 // list; a dense job is one expert over all M rows.

@@ -72,7 +72,7 @@ def lib() -> C.CDLL:
         L.moe_route_topk.restype = i
         L.moe_route_topk.argtypes = [vp, vp, vp, vp, i, i, i, i, f, vp, C.POINTER(moe_routing), vp, sz, vp]
         L.moe_quant_act_mxfp8.restype = i
-        L.moe_quant_act_mxfp8.argtypes = [vp, i, i, vp, vp, vp]
+        L.moe_quant_act_mxfp8.argtypes = [vp, i, i, C.POINTER(moe_routing), i, vp, vp, vp]
         L.moe_gate_up_workspace_bytes.restype = sz
         L.moe_gate_up_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         L.moe_expert_gate_up.restype = i
@@ -203,9 +203,14 @@ def route_topk(routing: Routing, x=None, logits_in=None, w_router=None, bias=Non
     _check(rc, "moe_route_topk")
 
 
-def quant_act_mxfp8(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream=None):
+def quant_act_mxfp8(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, routing: Optional["Routing"] = None,
+                    stream=None):
+    """MXFP8 of the rows of x: row order, or bucket order [M*k, K] with a routing."""
     M, K = x.shape
-    _check(lib().moe_quant_act_mxfp8(_p(x), M, K, _p(q), _p(s), _stream(stream)), "moe_quant_act_mxfp8")
+    r = None if routing is None else routing.c()
+    k = 0 if routing is None else routing.k
+    _check(lib().moe_quant_act_mxfp8(_p(x), M, K, None if r is None else C.byref(r), k, _p(q), _p(s),
+                                     _stream(stream)), "moe_quant_act_mxfp8")
 
 
 def expert_gate_up(w13: Weights, M, H, I, E, k, routing: Optional[Routing] = None, a_q=None,

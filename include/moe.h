@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 enum moe_status {
     MOE_OK = 0,
@@ -189,9 +189,14 @@ int moe_route_topk(const uint16_t *x, const float *logits_in, const float *w_rou
  *   = shared + 127; elements = E4M3 of x / 2^shared, round to nearest even,
  *   saturated to +-448, sign kept (-0 -> 0x80).  A block holding NaN or Inf
  *   gets scale 0xFF and NaN codes.
- * x: bf16 [M, K]; q: uint8 [M, K]; s: uint8 [M, K/32].  K % 32 == 0. */
-int moe_quant_act_mxfp8(const uint16_t *x, int M, int K, uint8_t *q, uint8_t *s,
-                        hipStream_t stream);
+ * x: bf16 [M, K]; K % 32 == 0.
+ * route == NULL: q: uint8 [M, K], s: uint8 [M, K/32] in row order.
+ * route != NULL (a routing of the M rows with top-k k): q [M*k, K], s
+ *   [M*k, K/32] in bucket order, row b holding x row bucket[b] / k (each row's
+ *   codes are the same as in row order), which is the order the routed
+ *   expert GEMMs read. */
+int moe_quant_act_mxfp8(const uint16_t *x, int M, int K, const moe_routing *route, int k,
+                        uint8_t *q, uint8_t *s, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_expert_gate_up — gate_up GEMM of every routed expert over its rows,
@@ -202,13 +207,15 @@ int moe_quant_act_mxfp8(const uint16_t *x, int M, int K, uint8_t *q, uint8_t *s,
  *   "shared act quant" (SiLU-and-mul fused with the down input's quant);
  *   SGLang Spark GB10 Optimizations, section 1 (NVFP4 K-groups of 16).
  * g = A W13[:I]^T, u = A W13[I:]^T with exact products and fp32 sums; h =
- * silu(g) * u in fp32.  FP4 weights: A is MXFP8 (a_q, a_s) [M, H] and h is
- * written as MXFP8 (h_q [Pr, I], h_s [Pr, I/32]) with the rule of
- * moe_quant_act_mxfp8.  BF16 weights: A is bf16 a_bf16 [M, H] and h is written
- * rounded to bf16 (h_bf16 [Pr, I]).
- * route != NULL: experts e of w13 over their routed rows; output row b of h is
- *   bucket position b (Pr = M*k).  route == NULL ("dense"): one expert (w13
- *   holds E = 1) over all M rows in order (Pr = M); used for the shared expert.
+ * silu(g) * u in fp32.  FP4 weights (packed by moe_pack_fp4): A is MXFP8
+ * (a_q, a_s) [Pr, H] and h is written as MXFP8 (h_q [Pr, I], h_s [Pr, I/32])
+ * with the rule of moe_quant_act_mxfp8.  BF16 weights: A is bf16 a_bf16
+ * [M, H] and h is written rounded to bf16 (h_bf16 [Pr, I]).
+ * route != NULL: experts e of w13 over their routed rows; A and h are in
+ *   bucket order (row b = bucket position b, Pr = M*k; moe_quant_act_mxfp8
+ *   with the same route writes A so).  route == NULL ("dense"): one expert
+ *   (w13 holds E = 1) over all M rows in order (Pr = M); used for the shared
+ *   expert.
  * Workspace: moe_gate_up_workspace_bytes(...) bytes (may be 0), 256-byte
  *   aligned; no initialization needed. */
 size_t moe_gate_up_workspace_bytes(int fmt, int M, int H, int I, int E, int k, int dense);

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert moe.abi_version() == 3
+    assert moe.abi_version() == 4
     for rc in range(5):
         assert len(moe.status_str(rc)) > 0
     assert "unknown" in moe.status_str(99)
@@ -55,11 +55,9 @@ def test_workspace_sizes(L):
     # FP4: a K split (few items) needs fp32 partials [splits][rows][2I]; one split needs none
     few = L.moe_gate_up_workspace_bytes(moe.MOE_FMT_MXFP4, 8, 7168, 256, 1, 1, 1)
     assert few > 0 and few % (8 * 2 * 256 * 4) == 0 and few % 256 == 0
-    assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_NVFP4, 8, 7168, 256, 256, 8, 0) > 0
-    # routed FP4: the activations in bucket order (P*H codes, P*H/32 scales), no split here
-    al = lambda n: (n + 255) // 256 * 256
-    P = 64 * 8
-    assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_MXFP4, 64, 512, 2048, 64, 8, 0) == al(P * 512) + al(P * 16)
+    assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_NVFP4, 2, 7168, 256, 8, 2, 0) > 0    # 4 experts x 4 blocks
+    # enough items for the GPU: one K split, no partials
+    assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_MXFP4, 64, 512, 2048, 64, 8, 0) == 0
     assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_MXFP4, 8, 100, 256, 1, 1, 1) == 0   # H % 128
     assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_BF16, 8, 7168, 256, 256, 8, 0) == 0  # bf16 routed
 
@@ -110,8 +108,21 @@ def test_calls_refuse_before_enqueueing(L):
     assert rc == moe.MOE_ERR_WORKSPACE                     # misaligned
     rc = L.moe_layer(C.byref(d), 0x1000, 0x1000, 0x1000, None, None, None, None, 0x1000, 16, None)
     assert rc == moe.MOE_ERR_WORKSPACE                     # too small
-    assert L.moe_quant_act_mxfp8(None, 4, 64, 0x1000, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_quant_act_mxfp8(0x1000, 4, 48, 0x1000, 0x1000, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_quant_act_mxfp8(None, 4, 64, None, 0, 0x1000, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quant_act_mxfp8(0x1000, 4, 48, None, 0, 0x1000, 0x1000, None) == moe.MOE_ERR_UNSUPPORTED
+    r = moe.moe_routing()  # bucket missing
+    assert L.moe_quant_act_mxfp8(0x1000, 4, 64, C.byref(r), 2, 0x1000, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
+    r.bucket = 0x1000
+    assert L.moe_quant_act_mxfp8(0x1000, 4, 64, C.byref(r), 33, 0x1000, 0x1000, None) == moe.MOE_ERR_UNSUPPORTED
+    # packing: format, shape and pointer checks
+    assert L.moe_packed_scale_bytes(moe.MOE_FMT_MXFP4, 2, 32, 640) == 2 * 2 * 2 * 64 * 4
+    assert L.moe_packed_scale_bytes(moe.MOE_FMT_NVFP4, 1, 16, 128) == 64 * 8
+    assert L.moe_packed_scale_bytes(moe.MOE_FMT_MXFP4, 1, 24, 128) == 0     # N % 16
+    assert L.moe_packed_scale_bytes(moe.MOE_FMT_BF16, 1, 16, 128) == 0
+    assert L.moe_pack_fp4(moe.MOE_FMT_BF16, 1, 16, 128, 0x1000, 0x1000, 0x1000, 0x1000, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_fp4(moe.MOE_FMT_MXFP4, 1, 16, 100, 0x1000, 0x1000, 0x1000, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_fp4(moe.MOE_FMT_MXFP4, 1, 16, 192, 0x1000, 0x1000, 0x1000, 0x1000, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_fp4(moe.MOE_FMT_MXFP4, 1, 16, 128, None, 0x1000, 0x1000, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
     r = moe.moe_routing(*([0x1000] * 10))
     # both x and logits_in, or neither
     assert L.moe_route_topk(None, None, None, None, 4, 128, 8, 2, 1.0, None, C.byref(r), 0x1000,

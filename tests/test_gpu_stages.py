@@ -99,23 +99,30 @@ def _routed_setup(wfmt, M=40, H=512, E=6, k=3, I=256, seed=3, bias="zipf:1.0"):
     rt = moe.Routing(M, E, k, DEV)
     logits = torch.empty((M, E), dtype=torch.float32, device=DEV)
     moe.route_topk(rt, x=d.x, w_router=d.Wr, bias=d.bias, routed_scale=sh.routed_scale, logits_out=logits)
+    # row order (what the oracle reads) and bucket order (what the routed GEMMs read)
     xq = torch.empty((M, H), dtype=torch.uint8, device=DEV)
     xs = torch.empty((M, H // 32), dtype=torch.uint8, device=DEV)
     moe.quant_act_mxfp8(d.x, xq, xs)
+    xqp = torch.empty((M * k, H), dtype=torch.uint8, device=DEV)
+    xsp = torch.empty((M * k, H // 32), dtype=torch.uint8, device=DEV)
+    moe.quant_act_mxfp8(d.x, xqp, xsp, routing=rt)
     torch.cuda.synchronize()
-    return sh, inp, d, rt, xq, xs
+    # bucket order is row order permuted: row b = row bucket[b] // k, bit for bit
+    tok = torch.div(rt.bucket.long(), k, rounding_mode="floor")
+    assert torch.equal(xqp, xq[tok]) and torch.equal(xsp, xs[tok])
+    return sh, inp, d, rt, (xq, xs), (xqp, xsp)
 
 
 @pytest.mark.parametrize("wfmt,H", [(synth.MXFP4, 512), (synth.NVFP4, 512),
                                     (synth.MXFP4, 2560), (synth.NVFP4, 2560)])
 def test_gate_up_routed_parity(wfmt, H):
     # H = 512 is one K chunk; 2560 is five (exercises the weight ring and LDS buffers)
-    sh, inp, d, rt, xq, xs = _routed_setup(wfmt, H=H)
+    sh, inp, d, rt, (xq, xs), (xqp, xsp) = _routed_setup(wfmt, H=H)
     M, H, E, k, I = sh.M, sh.H, sh.E, sh.k, sh.I
     P = M * k
     hq = torch.empty((P, I), dtype=torch.uint8, device=DEV)
     hs = torch.empty((P, I // 32), dtype=torch.uint8, device=DEV)
-    moe.expert_gate_up(d.w13, M, H, I, E, k, routing=rt, a_q=xq, a_s=xs, h_q=hq, h_s=hs)
+    moe.expert_gate_up(d.w13, M, H, I, E, k, routing=rt, a_q=xqp, a_s=xsp, h_q=hq, h_s=hs)
     torch.cuda.synchronize()
     bucket, ids = np_of(rt.bucket), np_of(rt.topk_ids).ravel()
     a = orc.mxfp8_dequant(np_of(xq), np_of(xs))
@@ -141,12 +148,12 @@ def test_gate_up_routed_parity(wfmt, H):
                                     (synth.MXFP4, 1536), (synth.NVFP4, 1536)])
 def test_down_routed_parity(wfmt, I):
     # I = 256 fits one chunk (two row blocks per wave); 1536 is three chunks
-    sh, inp, d, rt, xq, xs = _routed_setup(wfmt, seed=5, I=I)
+    sh, inp, d, rt, (xq, xs), (xqp, xsp) = _routed_setup(wfmt, seed=5, I=I)
     M, H, E, k, I = sh.M, sh.H, sh.E, sh.k, sh.I
     P = M * k
     hq = torch.empty((P, I), dtype=torch.uint8, device=DEV)
     hs = torch.empty((P, I // 32), dtype=torch.uint8, device=DEV)
-    moe.expert_gate_up(d.w13, M, H, I, E, k, routing=rt, a_q=xq, a_s=xs, h_q=hq, h_s=hs)
+    moe.expert_gate_up(d.w13, M, H, I, E, k, routing=rt, a_q=xqp, a_s=xsp, h_q=hq, h_s=hs)
     y = torch.full((P, H), float("nan"), dtype=torch.float32, device=DEV)
     moe.expert_down(d.w2, M, H, I, E, k, y, routing=rt, h_q=hq, h_s=hs)
     torch.cuda.synchronize()
