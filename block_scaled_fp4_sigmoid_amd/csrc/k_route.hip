@@ -5,6 +5,7 @@
 // group, sigmoid scores, renormalized top-k); SGLang-NVIDIA-Mega README,
 // DeepSeek-V4.1 slot table, rows "Router top-k" (one CTA per row) and "Routed
 // experts (moe)" (8-row tiles; an expert with more than 8 rows takes several).
+#include "dense_bf16_dev.h"
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -47,11 +48,13 @@ __device__ __forceinline__ void split3(float w, uint32_t& b1, uint32_t& b2, uint
 __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restrict__ x,
                                                          const float* __restrict__ w_router,
                                                          int M, int H, int E, int splits,
-                                                         int kchunk, int units,
-                                                         float* __restrict__ partials,
-                                                         int* __restrict__ counters, int ncounters) {
-    if (blockIdx.x == 0)
-        for (int c = threadIdx.x; c < ncounters; c += blockDim.x) counters[c] = 0;
+                                                         int kchunk, int units, int nmain,
+                                                         float* __restrict__ partials, Bf16Side side,
+                                                         int stage) {
+    if ((int)blockIdx.x >= nmain) {  // a bf16 shared-expert stage riding along
+        bf16_side_block(side, stage, blockIdx.x - nmain);
+        return;
+    }
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int unit = blockIdx.x * 4 + wave;
@@ -139,21 +142,13 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
 }
 
 hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int M, int H, int E,
-                                  const RouterPlan& plan, float* partials, int* counters,
-                                  int ncounters, hipStream_t stream) {
+                                  const RouterPlan& plan, float* partials, const Bf16Side& side1, int stage1,
+                                  hipStream_t stream) {
     const int units = ((E + 15) / 16) * plan.splits * plan.row_groups;
     const int blocks = (units + 3) / 4;
-    hipLaunchKernelGGL(k_router_partials, dim3(blocks), dim3(256), 0, stream, x, w_router, M, H, E,
-                       plan.splits, plan.kchunk, units, partials, counters, ncounters);
-    return hipGetLastError();
-}
-
-__global__ void k_zero_ints(int* p, int n) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
-}
-
-hipError_t launch_zero_ints(int* p, int n, hipStream_t stream) {
-    hipLaunchKernelGGL(k_zero_ints, dim3(1), dim3(256), 0, stream, p, n);
+    const int extra = stage1 == kBf16None ? 0 : side1.blocks;
+    hipLaunchKernelGGL(k_router_partials, dim3(blocks + extra), dim3(256), 0, stream, x, w_router, M, H, E,
+                       plan.splits, plan.kchunk, units, blocks, partials, side1, stage1);
     return hipGetLastError();
 }
 
@@ -196,7 +191,11 @@ __device__ void block_exclusive_scan(int* data, int* scratch, int& total) {
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials, int splits,
                                               const float* __restrict__ bias, int M, int E, int k,
                                               float routed_scale, float* __restrict__ logits_out,
-                                              moe_routing route) {
+                                              moe_routing route, Bf16Side side, int stage) {
+    if ((int)blockIdx.x >= M) {  // a bf16 shared-expert stage riding along
+        bf16_side_block(side, stage, blockIdx.x - M);
+        return;
+    }
     // One workgroup per row.  Phase 1: every thread owns experts tid + 256q,
     // sums their partial logits in chunk order (loads issued 8 at a time) and
     // stores the fp64 score and key in LDS.  Phase 2: wave 0 picks the k slots.
@@ -205,18 +204,14 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += 256) {
-        float lg = 0.f;
-        for (int c0 = 0; c0 < splits; c0 += 8) {
-            float p[8];
+        // all partials of the expert in one round of loads (splits <= 32)
+        float p[32];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int c = c0 + u;
-                p[u] = c < splits ? partials[((size_t)c * M + r) * E + e] : 0.f;
-            }
+        for (int u = 0; u < 32; ++u) p[u] = u < splits ? partials[((size_t)u * M + r) * E + e] : 0.f;
+        float lg = p[0];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (c0 + u < splits) lg = (c0 + u == 0) ? p[u] : lg + p[u];
-        }
+        for (int u = 1; u < 32; ++u)
+            if (u < splits) lg = lg + p[u];
         if (logits_out) logits_out[(size_t)r * E + e] = lg;
         const double sc = 1.0 / (1.0 + exp(-(double)lg));
         s_sc[e] = sc;
@@ -278,7 +273,12 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials
 // Route step: one workgroup builds the expert buckets, 8-row tiles and the
 // active-expert list from topk_ids (a separate launch, so the ids written by
 // the top-k workgroups are visible without a device-scope fence).
-__global__ __launch_bounds__(kBucketThreads) void k_bucket(int M, int E, int k, moe_routing route) {
+__global__ __launch_bounds__(kBucketThreads) void k_bucket(int M, int E, int k, moe_routing route, Bf16Side side,
+                                                          int stage) {
+    if (blockIdx.x > 0) {  // a bf16 shared-expert stage riding along
+        bf16_side_block(side, stage, blockIdx.x - 1);
+        return;
+    }
     const int tid = threadIdx.x;
 
     __shared__ int s_cnt[kMaxE], s_off[kMaxE], s_tile[kMaxE], s_act[kMaxE], s_run[kMaxE];
@@ -358,13 +358,15 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(int M, int E, int k, 
 
 hipError_t launch_topk_bucket(const float* partials, int splits, const float* bias, int M, int E,
                               int k, float routed_scale, float* logits_out,
-                              const moe_routing& route, int* counter, hipStream_t stream) {
-    (void)counter;
-    hipLaunchKernelGGL(k_topk, dim3(M), dim3(256), 0, stream, partials, splits, bias,
-                       M, E, k, routed_scale, logits_out, route);
+                              const moe_routing& route, const Bf16Side& side2, int stage2,
+                              const Bf16Side& side3, int stage3, hipStream_t stream) {
+    const int extra2 = stage2 == kBf16None ? 0 : side2.blocks;
+    hipLaunchKernelGGL(k_topk, dim3(M + extra2), dim3(256), 0, stream, partials, splits, bias,
+                       M, E, k, routed_scale, logits_out, route, side2, stage2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBucketThreads), 0, stream, M, E, k, route);
+    const int extra3 = stage3 == kBf16None ? 0 : side3.blocks;
+    hipLaunchKernelGGL(k_bucket, dim3(1 + extra3), dim3(kBucketThreads), 0, stream, M, E, k, route, side3, stage3);
     return hipGetLastError();
 }
 

@@ -24,7 +24,6 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
 constexpr int kMaxH = 16384;
 constexpr int kMaxI = 8192;
-constexpr int kRouteCounters = 16;  // ints reserved for the route step's counter
 
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
@@ -70,13 +69,11 @@ struct Carver {
 };
 
 struct RouteWs {
-    int* counters;
     float* partials;
 };
 
-RouteWs carve_route(Carver& c, int M, int H, int E, int extra_counters) {
+RouteWs carve_route(Carver& c, int M, int H, int E) {
     RouteWs w;
-    w.counters = c.take<int>(kRouteCounters + extra_counters);
     const RouterPlan p = router_plan(M, H, E);
     w.partials = c.take<float>((size_t)p.splits * M * E);
     return w;
@@ -155,7 +152,7 @@ size_t moe_route_workspace_bytes(int M, int H, int E, int k) {
     const int Hc = H == 0 ? 128 : H;  // H = 0: routing from logits_in
     if (check_dims(M, Hc, E, k) != MOE_OK) return 0;
     Carver c(nullptr);
-    carve_route(c, M, Hc, E, 0);
+    carve_route(c, M, Hc, E);
     return c.off;
 }
 
@@ -170,20 +167,18 @@ int moe_route_topk(const uint16_t* x, const float* logits_in, const float* w_rou
     if (int st = check_routing(route)) return st;
     if (!workspace || !aligned256(workspace)) return MOE_ERR_WORKSPACE;
     Carver c(workspace);
-    RouteWs w = carve_route(c, M, Hc, E, 0);
+    RouteWs w = carve_route(c, M, Hc, E);
     if (c.off > workspace_bytes) return MOE_ERR_WORKSPACE;
     hipError_t e;
     if (x) {
         const RouterPlan p = router_plan(M, H, E);
-        e = launch_router_partials(x, w_router, M, H, E, p, w.partials, w.counters, kRouteCounters, stream);
+        e = launch_router_partials(x, w_router, M, H, E, p, w.partials, no_side(), kBf16None, stream);
         if (e == hipSuccess)
-            e = launch_topk_bucket(w.partials, p.splits, bias, M, E, k, routed_scale, logits_out, *route,
-                                   w.counters, stream);
+            e = launch_topk_bucket(w.partials, p.splits, bias, M, E, k, routed_scale, logits_out, *route, no_side(),
+                                   kBf16None, no_side(), kBf16None, stream);
     } else {
-        e = launch_zero_ints(w.counters, kRouteCounters, stream);
-        if (e == hipSuccess)
-            e = launch_topk_bucket(logits_in, 1, bias, M, E, k, routed_scale, nullptr, *route, w.counters,
-                                   stream);
+        e = launch_topk_bucket(logits_in, 1, bias, M, E, k, routed_scale, nullptr, *route, no_side(), kBf16None,
+                               no_side(), kBf16None, stream);
     }
     return hip_status(e);
 }
@@ -315,7 +310,7 @@ LayerWs carve_layer(Carver& c, const moe_layer_desc* d) {
     const int T = moe_tile_capacity(M, E, k);
     const bool sh = d->sh13.fmt != MOE_FMT_NONE;
     const bool shb = d->sh13.fmt == MOE_FMT_BF16;
-    L.route = carve_route(c, M, H, E, 0);
+    L.route = carve_route(c, M, H, E);
     L.ids = c.take<int32_t>(P);
     L.w = c.take<float>(P);
     L.offsets = c.take<int32_t>(E + 1);
@@ -394,24 +389,33 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
     r.num_active = L.num_active;
     r.active_offsets = L.act_off;
 
+    // A bf16 shared expert does not depend on the routing: its three stages
+    // run as extra workgroups of the router, top-k and bucketing launches.
+    const bool shb = sf == MOE_FMT_BF16;
+    const Bf16Side s1 = shb ? bf16_side(dense_job(d->sh13, Ish, H, M), Ish, H, M, x, L.sh_part, L.hsb, L.ysh,
+                                        kBf16GateUp)
+                            : no_side();
+    const Bf16Side s2 = shb ? bf16_side(dense_job(d->sh13, Ish, H, M), Ish, H, M, x, L.sh_part, L.hsb, L.ysh,
+                                        kBf16Swiglu)
+                            : no_side();
+    const Bf16Side s3 = shb ? bf16_side(dense_job(d->sh2, H, Ish, M), Ish, H, M, x, L.sh_part, L.hsb, L.ysh,
+                                        kBf16Down)
+                            : no_side();
     const RouterPlan p = router_plan(M, H, E);
-    hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials,
-                                          L.route.counters, kRouteCounters, stream);
+    hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, s1,
+                                          shb ? kBf16GateUp : kBf16None, stream);
     if (e == hipSuccess)
         e = launch_topk_bucket(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale,
-                               logits_out, r, L.route.counters, stream);
+                               logits_out, r, s2, shb ? kBf16Swiglu : kBf16None, s3, shb ? kBf16Down : kBf16None,
+                               stream);
     if (e == hipSuccess) e = launch_quant_pairs(x, r.bucket, k, M, H, L.xq, L.xs, L.xqt, L.xst, stream);
     const ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
     if (e == hipSuccess) e = launch_gate_up_fp4(gu, L.xq, L.xs, L.hq, L.hs, L.part, stream);
-    if (e == hipSuccess && sf == MOE_FMT_BF16)
-        e = launch_gate_up_bf16(dense_job(d->sh13, Ish, H, M), x, L.hsb, L.sh_part, stream);
-    else if (e == hipSuccess && sf != MOE_FMT_NONE)
+    if (e == hipSuccess && sf != MOE_FMT_NONE && !shb)
         e = launch_gate_up_fp4(dense_job(d->sh13, Ish, H, M), L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart, stream);
     const ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);
     if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream);
-    if (e == hipSuccess && sf == MOE_FMT_BF16)
-        e = launch_down_bf16(dense_job(d->sh2, H, Ish, M), L.hsb, L.ysh, stream);
-    else if (e == hipSuccess && sf != MOE_FMT_NONE)
+    if (e == hipSuccess && sf != MOE_FMT_NONE && !shb)
         e = launch_down_fp4(dense_job(d->sh2, H, Ish, M), L.hsq, L.hss, L.ysh, stream);
     if (e == hipSuccess)
         e = launch_finalize(L.y, r.topk_w, L.ysh, residual, d->gamma, d->eps, M, H, k, out, residual_out,

@@ -14,6 +14,25 @@ namespace moe {
 // Workspace pieces are carved at 256-byte boundaries.
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
+// bf16 shared expert: split-K partials (workspace), reduced by a second stage.
+// A Bf16Side describes one stage, which the routing launches can run as extra
+// workgroups (the stages do not depend on the routing).
+struct Bf16Side {
+    const uint16_t* w;  // bf16 weights [N][K]: W13 (N = 2I, K = H) or W2 (N = H, K = I)
+    int I, H, M;        // intermediate, hidden, rows
+    int splits;         // gate_up K splits
+    const uint16_t* x;  // bf16 [M][H] (gate_up input)
+    float* part;        // fp32 [splits][M][2I] (gate_up partials)
+    uint16_t* h;        // bf16 [M][I] (SwiGLU output, down input)
+    float* y;           // fp32 [M][H] (down output)
+    int blocks;         // workgroups of the stage
+};
+enum Bf16Stage { kBf16None = 0, kBf16GateUp = 1, kBf16Swiglu = 2, kBf16Down = 3 };
+// An empty side: no extra workgroups.
+inline Bf16Side no_side() {
+    Bf16Side s{};
+    return s;
+}
 struct RouterPlan {
     int splits;     // K chunks whose partial logits the top-k step sums
     int kchunk;     // elements of H per chunk (multiple of 32)
@@ -21,15 +40,17 @@ struct RouterPlan {
 };
 RouterPlan router_plan(int M, int H, int E);
 
+// The routing launches optionally run one bf16 shared-expert stage each as
+// extra workgroups: side1 with the router, side2 with the top-k, side3 with
+// the bucketing (stage kBf16None and blocks 0 for none).
 hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int M, int H, int E,
-                                  const RouterPlan& plan, float* partials, int* counters,
-                                  int ncounters, hipStream_t stream);
-// Zeroes n ints with a kernel (no memset node, so it is safe in captured graphs).
-hipError_t launch_zero_ints(int* p, int n, hipStream_t stream);
-// partials == nullptr: logits_in is read as the single partial.
+                                  const RouterPlan& plan, float* partials, const Bf16Side& side1, int stage1,
+                                  hipStream_t stream);
+// logits: the router partials (splits of them), or given logits (splits = 1).
 hipError_t launch_topk_bucket(const float* partials, int splits, const float* bias, int M, int E,
                               int k, float routed_scale, float* logits_out,
-                              const moe_routing& route, int* counter, hipStream_t stream);
+                              const moe_routing& route, const Bf16Side& side2, int stage2,
+                              const Bf16Side& side3, int stage3, hipStream_t stream);
 
 // FP4 weights in the load-order layout (moe_pack_fp4).
 size_t packed_scale_bytes(int fmt, int E, int N, int K);
@@ -71,8 +92,9 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
 hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8_t* h_s,
                            float* y, hipStream_t stream);
 
-// bf16 shared expert: split-K partials (workspace), reduced by a second launch.
 size_t gate_up_bf16_partials_bytes(int M, int H, int I);
+Bf16Side bf16_side(const ExpertJob& gate_up_or_down, int I, int H, int M, const uint16_t* x, float* part,
+                   uint16_t* h, float* y, int stage);
 hipError_t launch_gate_up_bf16(const ExpertJob& job, const uint16_t* a, uint16_t* h,
                                float* partials, hipStream_t stream);
 hipError_t launch_down_bf16(const ExpertJob& job, const uint16_t* h, float* y, hipStream_t stream);
