@@ -110,22 +110,20 @@ __device__ inline void bf16_swiglu_block(const Bf16Side& S, int bid) {
     const int idx = bid * 256 + threadIdx.x;
     if (idx >= M * I) return;
     const int t = idx / I, col = idx % I;
-    float gt = 0.f, up = 0.f;
-    for (int s0 = 0; s0 < splits; s0 += 8) {
-        float pg[8], pu[8];
+    // all partials in one round of loads (splits <= 32), added in split order
+    float pg[32], pu[32];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int sp = s0 + u;
-            const float* pr = S.part + ((size_t)(sp < splits ? sp : 0) * M + t) * (2 * I);
-            pg[u] = sp < splits ? pr[col] : 0.f;
-            pu[u] = sp < splits ? pr[I + col] : 0.f;
-        }
+    for (int u = 0; u < 32; ++u) {
+        const float* pr = S.part + ((size_t)(u < splits ? u : 0) * M + t) * (2 * I);
+        pg[u] = u < splits ? pr[col] : 0.f;
+        pu[u] = u < splits ? pr[I + col] : 0.f;
+    }
+    float gt = pg[0], up = pu[0];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (s0 + u < splits) {
-                gt += pg[u];
-                up += pu[u];
-            }
+    for (int u = 1; u < 32; ++u) {
+        if (u < splits) {
+            gt += pg[u];
+            up += pu[u];
         }
     }
     const float hv = gt / (1.0f + __expf(-gt)) * up;

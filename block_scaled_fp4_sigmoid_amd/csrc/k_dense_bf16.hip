@@ -10,12 +10,14 @@
 
 namespace moe {
 
+// gate_up K splits: about 256 workgroups, at most 32 splits (the SwiGLU stage
+// loads all of a value's partials in one round).
 int bf16_splits(int H, int I) {
     const int cbs = I / 32;
     const int nsteps = H / 32;
     int splits = 1;
-    for (int d = 1; d <= nsteps; ++d)
-        if (nsteps % d == 0 && cbs * d <= 512) splits = d;
+    for (int d = 1; d <= nsteps && d <= 32; ++d)
+        if (nsteps % d == 0 && cbs * d <= 256) splits = d;
     return splits;
 }
 

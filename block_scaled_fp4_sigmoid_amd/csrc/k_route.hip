@@ -153,16 +153,13 @@ hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int 
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: one wave per row (the pages' one CTA per row).  Each lane holds up to
-// 16 experts (e = lane + 64 t).  Scores are fp64 sigmoids of the fp32 logits;
-// keys add the optional selection bias; k rounds of a wave-wide arg-max with
-// (key descending, expert ascending) order pick the slots.
+// Top-k: one workgroup per row (the pages' one CTA per row).  Scores are fp64
+// sigmoids of the fp32 logits; keys add the optional selection bias; the
+// order is key descending, then expert ascending.
 
-__device__ __forceinline__ bool key_better(double ka, int ea, double kb, int eb) {
-    return ka > kb || (ka == kb && ea < eb);
-}
 
 constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
 constexpr int kBucketThreads = 256;
 
 // Exclusive scan over kMaxE entries held 4 per thread (256 threads).
@@ -188,6 +185,28 @@ __device__ void block_exclusive_scan(int* data, int* scratch, int& total) {
     __syncthreads();
 }
 
+// fp64 key -> unsigned integer with the same order (+0 and -0 equal).
+__device__ __forceinline__ uint64_t ordered_key(double v) {
+    if (v == 0.0) v = 0.0;
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// (hi, lo) key and expert id; better = larger key, then smaller id.
+__device__ __forceinline__ bool better3(uint32_t ah, uint32_t al, int ae, uint32_t bh, uint32_t bl, int be) {
+    return ah > bh || (ah == bh && (al > bl || (al == bl && ae < be)));
+}
+
+// DPP move within a row of 16 lanes.
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v, int ctrl_id) {
+    switch (ctrl_id) {
+        case 0: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+        case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+        case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+        default: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false); // row_mirror
+    }
+}
+
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials, int splits,
                                               const float* __restrict__ bias, int M, int E, int k,
                                               float routed_scale, float* __restrict__ logits_out,
@@ -197,9 +216,13 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials
         return;
     }
     // One workgroup per row.  Phase 1: every thread owns experts tid + 256q,
-    // sums their partial logits in chunk order (loads issued 8 at a time) and
-    // stores the fp64 score and key in LDS.  Phase 2: wave 0 picks the k slots.
-    __shared__ double s_key[kMaxE];
+    // sums their partial logits in chunk order and stores the fp64 score and
+    // the order-preserving integer form of the key in LDS.  Phase 2: wave 0
+    // holds 16 keys per lane in registers (expert lane + 64t) and picks the k
+    // slots in k rounds of a wave-wide arg-max: DPP moves inside each row of
+    // 16 lanes, then the four rows through readlane.  Phase 3: the weights,
+    // with the chosen scores summed in slot order.
+    __shared__ uint64_t s_ord[kMaxE];
     __shared__ double s_sc[kMaxE];
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
@@ -215,59 +238,76 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials
         if (logits_out) logits_out[(size_t)r * E + e] = lg;
         const double sc = 1.0 / (1.0 + exp(-(double)lg));
         s_sc[e] = sc;
-        s_key[e] = sc + (bias ? (double)bias[e] : 0.0);
+        s_ord[e] = ordered_key(sc + (bias ? (double)bias[e] : 0.0));
     }
     __syncthreads();
-    if (tid < 64) {
-        const int lane = tid;
-        uint32_t avail = 0;
-        for (int t = 0; t < 16; ++t)
-            if (lane + 64 * t < E) avail |= 1u << t;
-        int my_id = 0;
-        double my_s = 0.0;
-        for (int j = 0; j < k; ++j) {
-            bool have = false;
-            double bk = 0.0;
-            int be = 0x7fffffff;
-            for (int t = 0; t < 16; ++t) {
-                if ((avail >> t) & 1u) {
-                    const int e = lane + 64 * t;
-                    const double kv = s_key[e];
-                    if (!have || key_better(kv, e, bk, be)) {
-                        have = true;
-                        bk = kv;
-                        be = e;
-                    }
-                }
-            }
+    if (tid >= 64) return;
+    const int lane = tid;
+    constexpr int kT = kMaxE / 64;
+    uint32_t kh[kT], kl[kT];
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                const double ok = __shfl_xor(bk, off, 64);
-                const int oe = __shfl_xor(be, off, 64);
-                const int oh = __shfl_xor((int)have, off, 64);
-                if (oh && (!have || key_better(ok, oe, bk, be))) {
-                    have = true;
-                    bk = ok;
-                    be = oe;
-                }
-            }
-            if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
-            if (lane == j) {
-                my_id = be;
-                my_s = s_sc[be];
-            }
-        }
-        double sum = 0.0;
-        for (int j = 0; j < k; ++j) sum += __shfl(my_s, j, 64);
-        if (lane < k) {
-            route.topk_ids[(size_t)r * k + lane] = my_id;
-            route.topk_w[(size_t)r * k + lane] = (float)(((double)routed_scale * my_s) / sum);
-        }
+    for (int t = 0; t < kT; ++t) {
+        const int e = lane + 64 * t;
+        const uint64_t o = e < E ? s_ord[e] : 0;  // 0: no expert (below every key)
+        kh[t] = (uint32_t)(o >> 32);
+        kl[t] = (uint32_t)o;
     }
-
+    int my_id = 0;
+    for (int j = 0; j < k; ++j) {
+        // the lane's best remaining expert
+        uint32_t bh = 0, bl = 0;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+            const int e = lane + 64 * t;
+            if (better3(kh[t], kl[t], e, bh, bl, be) && (kh[t] | kl[t])) {
+                bh = kh[t];
+                bl = kl[t];
+                be = e;
+            }
+        }
+        // best of each row of 16 lanes (every lane of the row ends with it)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t oh = dpp_u(bh, c), ol = dpp_u(bl, c);
+            const int oe = (int)dpp_u((uint32_t)be, c);
+            if (better3(oh, ol, oe, bh, bl, be)) {
+                bh = oh;
+                bl = ol;
+                be = oe;
+            }
+        }
+        // best of the four rows (uniform)
+        uint32_t wh = __builtin_amdgcn_readlane(bh, 0), wl = __builtin_amdgcn_readlane(bl, 0);
+        int we = __builtin_amdgcn_readlane(be, 0);
+#pragma unroll
+        for (int rr = 1; rr < 4; ++rr) {
+            const uint32_t oh = __builtin_amdgcn_readlane(bh, 16 * rr), ol = __builtin_amdgcn_readlane(bl, 16 * rr);
+            const int oe = __builtin_amdgcn_readlane(be, 16 * rr);
+            if (better3(oh, ol, oe, wh, wl, we)) {
+                wh = oh;
+                wl = ol;
+                we = oe;
+            }
+        }
+        // the owner lane retires the winner
+        if ((we & 63) == lane) {
+#pragma unroll
+            for (int t = 0; t < kT; ++t)
+                if (t == (we >> 6)) {
+                    kh[t] = 0;
+                    kl[t] = 0;
+                }
+        }
+        if (lane == j) my_id = we;
+    }
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) sum += s_sc[__shfl(my_id, j, 64)];
+    if (lane < k) {
+        route.topk_ids[(size_t)r * k + lane] = my_id;
+        route.topk_w[(size_t)r * k + lane] = (float)(((double)routed_scale * s_sc[my_id]) / sum);
+    }
 }
-
-
 
 // ---------------------------------------------------------------------------
 // Route step: one workgroup builds the expert buckets, 8-row tiles and the
