@@ -192,19 +192,95 @@ __device__ __forceinline__ uint64_t ordered_key(double v) {
     return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
-// (hi, lo) key and expert id; better = larger key, then smaller id.
-__device__ __forceinline__ bool better3(uint32_t ah, uint32_t al, int ae, uint32_t bh, uint32_t bl, int be) {
-    return ah > bh || (ah == bh && (al > bl || (al == bl && ae < be)));
+// A candidate: order-preserving key and expert id.  Better = larger key, then
+// smaller id (the expert order among equal scores).  Branch-free, so the
+// selection below runs without divergence.
+struct Cand {
+    uint64_t key;
+    int id;
+};
+__device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
+    return (a.key > b.key) | ((a.key == b.key) & (a.id < b.id));
+}
+__device__ __forceinline__ void take_if(Cand& dst, const Cand& src, bool c) {
+    dst.key = c ? src.key : dst.key;
+    dst.id = c ? src.id : dst.id;
 }
 
-// DPP move within a row of 16 lanes.
-__device__ __forceinline__ uint32_t dpp_u(uint32_t v, int ctrl_id) {
-    switch (ctrl_id) {
-        case 0: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
-        case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
-        case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);  // row_half_mirror
-        default: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false); // row_mirror
+// The candidate of another lane through one DPP move (all three words);
+// lanes outside row_mask keep their own.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ Cand dpp_cand(const Cand& c) {
+    const int h = (int)(uint32_t)(c.key >> 32), l = (int)(uint32_t)c.key;
+    Cand o;
+    o.key = ((uint64_t)(uint32_t)__builtin_amdgcn_update_dpp(h, h, CTRL, ROW_MASK, 0xF, false) << 32) |
+            (uint32_t)__builtin_amdgcn_update_dpp(l, l, CTRL, ROW_MASK, 0xF, false);
+    o.id = __builtin_amdgcn_update_dpp(c.id, c.id, CTRL, ROW_MASK, 0xF, false);
+    return o;
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_best(Cand& c) {
+    const Cand o = dpp_cand<CTRL, ROW_MASK>(c);
+    take_if(c, o, better(o, c));
+}
+
+// Best candidate of the wave, returned uniform.  Inside each row of 16 lanes
+// four DPP exchanges (pair swap, quad half swap, half-row mirror, row mirror)
+// leave the row's best in every lane of the row; two row broadcasts then carry
+// it to lane 63 (rows 1 and 3 take lane 15 of the row before them, rows 2 and
+// 3 take lane 31).
+__device__ __forceinline__ Cand wave_best(Cand c) {
+    dpp_best<0xB1, 0xF>(c);   // quad_perm [1,0,3,2]
+    dpp_best<0x4E, 0xF>(c);   // quad_perm [2,3,0,1]
+    dpp_best<0x141, 0xF>(c);  // row_half_mirror
+    dpp_best<0x140, 0xF>(c);  // row_mirror
+    dpp_best<0x142, 0xA>(c);  // row_bcast:15
+    dpp_best<0x143, 0xC>(c);  // row_bcast:31
+    Cand w;
+    w.key = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(c.key >> 32), 63) << 32) |
+            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)c.key, 63);
+    w.id = __builtin_amdgcn_readlane(c.id, 63);
+    return w;
+}
+
+// Top-k of one row by wave 0: lane l holds experts l + 64t (t < KT) sorted
+// best first (a bitonic network in registers), then k rounds of a wave-wide
+// arg-max over the list heads; the winning lane drops its head.  Experts
+// past E carry key 0, below every score.  Returns, in lane j < k, the j-th
+// chosen expert.
+template <int KT>
+__device__ int select_topk(const uint64_t* s_ord, int E, int k, int lane) {
+    Cand c[KT];
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+        const int e = lane + 64 * t;
+        c[t].key = e < E ? s_ord[e] : 0;
+        c[t].id = e;
     }
+#pragma unroll
+    for (int size = 2; size <= KT; size <<= 1)
+#pragma unroll
+        for (int stride = size / 2; stride > 0; stride >>= 1)
+#pragma unroll
+            for (int i = 0; i < KT; ++i) {
+                const int j = i ^ stride;
+                if (j <= i) continue;
+                // (i & size) == 0: this pair ends best-first
+                const bool swap = ((i & size) == 0) ? better(c[j], c[i]) : better(c[i], c[j]);
+                const Cand ci = c[i];
+                take_if(c[i], c[j], swap);
+                take_if(c[j], ci, swap);
+            }
+    int my_id = 0;
+    for (int j = 0; j < k; ++j) {
+        const Cand w = wave_best(c[0]);
+        const bool mine = (w.id & 63) == lane;
+#pragma unroll
+        for (int t = 0; t + 1 < KT; ++t) take_if(c[t], c[t + 1], mine);
+        c[KT - 1].key = mine ? 0 : c[KT - 1].key;
+        my_id = lane == j ? w.id : my_id;
+    }
+    return my_id;
 }
 
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials, int splits,
@@ -215,13 +291,10 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials
         bf16_side_block(side, stage, blockIdx.x - M);
         return;
     }
-    // One workgroup per row.  Phase 1: every thread owns experts tid + 256q,
-    // sums their partial logits in chunk order and stores the fp64 score and
-    // the order-preserving integer form of the key in LDS.  Phase 2: wave 0
-    // holds 16 keys per lane in registers (expert lane + 64t) and picks the k
-    // slots in k rounds of a wave-wide arg-max: DPP moves inside each row of
-    // 16 lanes, then the four rows through readlane.  Phase 3: the weights,
-    // with the chosen scores summed in slot order.
+    // Phase 1: every thread owns experts tid + 256q, sums their partial
+    // logits in chunk order and stores the fp64 score and the order-preserving
+    // integer form of the key in LDS.  Phase 2: wave 0 picks the k slots.
+    // Phase 3: the weights, with the chosen scores summed in slot order.
     __shared__ uint64_t s_ord[kMaxE];
     __shared__ double s_sc[kMaxE];
     const int r = blockIdx.x;
@@ -243,69 +316,24 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials
     __syncthreads();
     if (tid >= 64) return;
     const int lane = tid;
-    constexpr int kT = kMaxE / 64;
-    uint32_t kh[kT], kl[kT];
-#pragma unroll
-    for (int t = 0; t < kT; ++t) {
-        const int e = lane + 64 * t;
-        const uint64_t o = e < E ? s_ord[e] : 0;  // 0: no expert (below every key)
-        kh[t] = (uint32_t)(o >> 32);
-        kl[t] = (uint32_t)o;
-    }
-    int my_id = 0;
-    for (int j = 0; j < k; ++j) {
-        // the lane's best remaining expert
-        uint32_t bh = 0, bl = 0;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int t = 0; t < kT; ++t) {
-            const int e = lane + 64 * t;
-            if (better3(kh[t], kl[t], e, bh, bl, be) && (kh[t] | kl[t])) {
-                bh = kh[t];
-                bl = kl[t];
-                be = e;
-            }
-        }
-        // best of each row of 16 lanes (every lane of the row ends with it)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t oh = dpp_u(bh, c), ol = dpp_u(bl, c);
-            const int oe = (int)dpp_u((uint32_t)be, c);
-            if (better3(oh, ol, oe, bh, bl, be)) {
-                bh = oh;
-                bl = ol;
-                be = oe;
-            }
-        }
-        // best of the four rows (uniform)
-        uint32_t wh = __builtin_amdgcn_readlane(bh, 0), wl = __builtin_amdgcn_readlane(bl, 0);
-        int we = __builtin_amdgcn_readlane(be, 0);
-#pragma unroll
-        for (int rr = 1; rr < 4; ++rr) {
-            const uint32_t oh = __builtin_amdgcn_readlane(bh, 16 * rr), ol = __builtin_amdgcn_readlane(bl, 16 * rr);
-            const int oe = __builtin_amdgcn_readlane(be, 16 * rr);
-            if (better3(oh, ol, oe, wh, wl, we)) {
-                wh = oh;
-                wl = ol;
-                we = oe;
-            }
-        }
-        // the owner lane retires the winner
-        if ((we & 63) == lane) {
-#pragma unroll
-            for (int t = 0; t < kT; ++t)
-                if (t == (we >> 6)) {
-                    kh[t] = 0;
-                    kl[t] = 0;
-                }
-        }
-        if (lane == j) my_id = we;
-    }
+    int my_id;
+    if (E <= 256)
+        my_id = select_topk<4>(s_ord, E, k, lane);
+    else if (E <= 512)
+        my_id = select_topk<8>(s_ord, E, k, lane);
+    else
+        my_id = select_topk<16>(s_ord, E, k, lane);
+    const double my_sc = lane < k ? s_sc[my_id] : 0.0;
     double sum = 0.0;
-    for (int j = 0; j < k; ++j) sum += s_sc[__shfl(my_id, j, 64)];
+    for (int j = 0; j < k; ++j) {
+        const uint64_t b = __double_as_longlong(my_sc);
+        const uint64_t v = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), j) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, j);
+        sum += __longlong_as_double((long long)v);
+    }
     if (lane < k) {
         route.topk_ids[(size_t)r * k + lane] = my_id;
-        route.topk_w[(size_t)r * k + lane] = (float)(((double)routed_scale * s_sc[my_id]) / sum);
+        route.topk_w[(size_t)r * k + lane] = (float)(((double)routed_scale * my_sc) / sum);
     }
 }
 

@@ -91,6 +91,33 @@ def test_route_topk_parity(M, H, E, k, bias, scale):
         assert torch.equal(getattr(rt, name), getattr(rt2, name)), name
 
 
+TIE_CASES = [
+    # E, k: list lengths per lane of 1..16 keys and their edges
+    (16, 4), (64, 8), (65, 8), (200, 8), (256, 8), (257, 10), (384, 8), (512, 32), (513, 8),
+    (1000, 32), (1024, 32), (1024, 1),
+]
+
+
+@pytest.mark.parametrize("E,k", TIE_CASES)
+def test_route_topk_ties(E, k):
+    """Top-k on logits with many exactly equal scores, negative keys (a
+    bias below -1) and keys that tie across the bias: equal keys go to the
+    smaller expert id, as in the oracle."""
+    M = 5
+    rng = np.random.default_rng(E * 100 + k)
+    lg = rng.choice(np.array([-1.0, 0.0, 0.5, 2.0], np.float32), size=(M, E)).astype(np.float32)
+    bias = rng.choice(np.array([-2.0, 0.0, 0.25], np.float32), size=E).astype(np.float32)
+    for b in (None, bias):
+        rt = moe.Routing(M, E, k, DEV)
+        moe.route_topk(rt, logits_in=torch.from_numpy(lg).to(DEV),
+                       bias=None if b is None else torch.from_numpy(b).to(DEV), routed_scale=1.0)
+        torch.cuda.synchronize()
+        r = orc.route(lg, b, k, 1.0)
+        assert np.array_equal(np_of(rt.topk_ids), r["ids"])
+        assert np.max(np.abs(np_of(rt.topk_w) - r["w"]) / np.abs(r["w"])) <= 1e-6
+        assert np.array_equal(np_of(rt.bucket), r["bucket"])
+
+
 def _routed_setup(wfmt, M=40, H=512, E=6, k=3, I=256, seed=3, bias="zipf:1.0"):
     sh = synth.custom_shape(M=M, H=H, E=E, k=k, I=I, wfmt=wfmt, bias=bias)
     inp = synth.make_inputs(sh, seed=seed, pool_rows=2048)
