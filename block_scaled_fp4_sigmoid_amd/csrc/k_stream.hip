@@ -61,6 +61,9 @@ constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every record count
 #ifndef MOE_STREAM_TARGET_ITEMS
 #define MOE_STREAM_TARGET_ITEMS 256  // gate_up splits K until about this many items
 #endif
+#ifndef MOE_RING_LOADS
+#define MOE_RING_LOADS 32  // 16-byte loads per lane the register ring may hold
+#endif
 #ifndef MOE_MIN_BLOCKS
 #define MOE_MIN_BLOCKS 2  // workgroups per CU the register budget must allow
 #endif
@@ -115,18 +118,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 
 // ---- NVFP4 helpers ----------------------------------------------------------
 
-// E4M3 scale code -> (fp32 value whose exponent is used, f16 mantissa factor):
-// value = 2^floor(log2 v) * m, m in [1, 2); zero -> m = 0; NaN -> m = NaN.
-__device__ __forceinline__ void nv_scale_split(uint32_t code, float& sv, _Float16& m) {
-    sv = __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
-    const uint32_t b = __float_as_uint(sv);
-    if ((b & 0x7fffffffu) == 0u) {
-        m = (_Float16)0.0f;
-    } else if ((b & 0x7f800000u) == 0x7f800000u) {
-        m = (_Float16)__uint_as_float(0x7fc00000u);
-    } else {
-        m = (_Float16)__uint_as_float((b & 0x007fffffu) | 0x3f800000u);
-    }
+// The two E4M3 block scales of one step (bytes 2h, 2h+1 of the dword) ->
+// exponent carriers sv0, sv1 for the scaled E2M1 conversion and an f16 pair of
+// mantissa factors carrying the scales' signs.  The conversion uses only the
+// exponent field of its fp32 scale (its sign and mantissa are ignored, and an
+// all-ones exponent, i.e. a NaN scale, makes every output NaN; checked on the
+// hardware), so value = conv(e2m1, sv) * m is exact: the E4M3 scale is exact
+// in f16, its mantissa field with exponent 0 and the sign kept is m.
+template <int H>
+__device__ __forceinline__ void nv_scales2(uint32_t dw, float& sv0, float& sv1, v2h& m) {
+    sv0 = __builtin_amdgcn_cvt_f32_fp8((int)dw, 2 * H);
+    sv1 = __builtin_amdgcn_cvt_f32_fp8((int)dw, 2 * H + 1);
+    const v2h sf = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(dw, 1.0f, H != 0);
+    m = __builtin_bit_cast(v2h, (__builtin_bit_cast(uint32_t, sf) & 0x83FF83FFu) | 0x3C003C00u);
 }
 
 // 8 packed E2M1 (one dword) -> 8 f16 = e2m1 * 2^floor(log2 sv) * m (exact).
@@ -278,15 +282,13 @@ __device__ __forceinline__ void step_mfma(const Ring<MB, NB, DQ, QS>& R, int v, 
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const v4i a = R.a[v][U][mb];
-            const uint32_t ws = R.as[v][mb][U >> 1] >> (16 * (U & 1));
             float sv0, sv1;
-            _Float16 m0, m1;
-            nv_scale_split(ws & 0xffu, sv0, m0);
-            nv_scale_split((ws >> 8) & 0xffu, sv1, m1);
-            const v8h A0 = nv_dequant8((uint32_t)a.x, sv0, m0);
-            const v8h A1 = nv_dequant8((uint32_t)a.y, sv0, m0);
-            const v8h A2 = nv_dequant8((uint32_t)a.z, sv1, m1);
-            const v8h A3 = nv_dequant8((uint32_t)a.w, sv1, m1);
+            v2h m;
+            nv_scales2<U & 1>(R.as[v][mb][U >> 1], sv0, sv1, m);
+            const v8h A0 = nv_dequant8((uint32_t)a.x, sv0, m[0]);
+            const v8h A1 = nv_dequant8((uint32_t)a.y, sv0, m[0]);
+            const v8h A2 = nv_dequant8((uint32_t)a.z, sv1, m[1]);
+            const v8h A3 = nv_dequant8((uint32_t)a.w, sv1, m[1]);
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, B[j][0], acc[mb][j], 0, 0, 0);
@@ -362,11 +364,26 @@ __device__ __forceinline__ void stream_pass(const StreamJob& J, int e, const int
     }
     const int q0 = s0 / 4, nq = (nst + 3) / 4, s_end = s0 + nst;
     Ring<MB, NB, DQ, QS> R;
+    // Fill the ring in the order the loop refills it (a quad's scales with its
+    // last step).  The wait counts at the loop head are merged over the entry
+    // and the back edge; an entry order with the scales issued last would
+    // make the first use of a quad's scales wait for every load in flight.
+    if constexpr (QS == 4) {
 #pragma unroll
-    for (int v = 0; v < DQ; ++v) {
-        ring_load_scales<FMT, MB, NB, DQ, QS>(R, v, c, q0 + v, s_end);
+        for (int v = 0; v < DQ; ++v) {
 #pragma unroll
-        for (int u = 0; u < QS; ++u) ring_load_step<FMT, MB, NB, DQ, QS>(R, v, u, c, q0 + v, s_end);
+            for (int u = 0; u < QS; ++u) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (u == QS - 1) ring_load_scales<FMT, MB, NB, DQ, QS>(R, v, c, q0 + v, s_end);
+                ring_load_step<FMT, MB, NB, DQ, QS>(R, v, u, c, q0 + v, s_end);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    } else {  // all of K in one quad: the loop runs once, the order is free
+        static_assert(DQ == 1, "a short ring holds one quad");
+        ring_load_scales<FMT, MB, NB, DQ, QS>(R, 0, c, q0, s_end);
+#pragma unroll
+        for (int u = 0; u < QS; ++u) ring_load_step<FMT, MB, NB, DQ, QS>(R, 0, u, c, q0, s_end);
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -385,7 +402,7 @@ __device__ __forceinline__ void stream_pass(const StreamJob& J, int e, const int
 template <int FMT, int MB, int NB>
 constexpr int ring_quads() {
     constexpr int per_quad = 4 * (MB + 2 * NB);
-    constexpr int budget = 32;
+    constexpr int budget = MOE_RING_LOADS;
     return budget / per_quad < 1 ? 1 : budget / per_quad;
 }
 

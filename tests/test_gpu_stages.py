@@ -118,10 +118,22 @@ def test_route_topk_ties(E, k):
         assert np.array_equal(np_of(rt.bucket), r["bucket"])
 
 
-def _routed_setup(wfmt, M=40, H=512, E=6, k=3, I=256, seed=3, bias="zipf:1.0"):
+def _negate_some_scales(inp, seed):
+    """Set the sign bit of about a quarter of the NVFP4 block-scale codes: a
+    negative E4M3 scale is a legal code and negates its block."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    for pe in (inp.w13, inp.w2):
+        flip = rng.random(pe.pool_scales.shape) < 0.25
+        pe.pool_scales = np.where(flip, pe.pool_scales | np.uint8(0x80), pe.pool_scales).astype(np.uint8)
+    return inp
+
+
+def _routed_setup(wfmt, M=40, H=512, E=6, k=3, I=256, seed=3, bias="zipf:1.0", neg_scales=False):
     sh = synth.custom_shape(M=M, H=H, E=E, k=k, I=I, wfmt=wfmt, bias=bias)
     inp = synth.make_inputs(sh, seed=seed, pool_rows=2048)
     inp = synth.vary_globals(inp, seed + 1)
+    if neg_scales:
+        inp = _negate_some_scales(inp, seed + 2)
     d = staging.to_device(inp, DEV)
     rt = moe.Routing(M, E, k, DEV)
     logits = torch.empty((M, E), dtype=torch.float32, device=DEV)
@@ -140,11 +152,12 @@ def _routed_setup(wfmt, M=40, H=512, E=6, k=3, I=256, seed=3, bias="zipf:1.0"):
     return sh, inp, d, rt, (xq, xs), (xqp, xsp)
 
 
-@pytest.mark.parametrize("wfmt,H", [(synth.MXFP4, 512), (synth.NVFP4, 512),
-                                    (synth.MXFP4, 2560), (synth.NVFP4, 2560)])
-def test_gate_up_routed_parity(wfmt, H):
+@pytest.mark.parametrize("wfmt,H,neg", [(synth.MXFP4, 512, False), (synth.NVFP4, 512, False),
+                                        (synth.MXFP4, 2560, False), (synth.NVFP4, 2560, False),
+                                        (synth.NVFP4, 2560, True)])
+def test_gate_up_routed_parity(wfmt, H, neg):
     # H = 512 is one K chunk; 2560 is five (exercises the weight ring and LDS buffers)
-    sh, inp, d, rt, (xq, xs), (xqp, xsp) = _routed_setup(wfmt, H=H)
+    sh, inp, d, rt, (xq, xs), (xqp, xsp) = _routed_setup(wfmt, H=H, neg_scales=neg)
     M, H, E, k, I = sh.M, sh.H, sh.E, sh.k, sh.I
     P = M * k
     hq = torch.empty((P, I), dtype=torch.uint8, device=DEV)
@@ -171,11 +184,12 @@ def test_gate_up_routed_parity(wfmt, H):
     assert worst < 1e-2, worst
 
 
-@pytest.mark.parametrize("wfmt,I", [(synth.MXFP4, 256), (synth.NVFP4, 256),
-                                    (synth.MXFP4, 1536), (synth.NVFP4, 1536)])
-def test_down_routed_parity(wfmt, I):
+@pytest.mark.parametrize("wfmt,I,neg", [(synth.MXFP4, 256, False), (synth.NVFP4, 256, False),
+                                        (synth.MXFP4, 1536, False), (synth.NVFP4, 1536, False),
+                                        (synth.NVFP4, 256, True), (synth.NVFP4, 1536, True)])
+def test_down_routed_parity(wfmt, I, neg):
     # I = 256 fits one chunk (two row blocks per wave); 1536 is three chunks
-    sh, inp, d, rt, (xq, xs), (xqp, xsp) = _routed_setup(wfmt, seed=5, I=I)
+    sh, inp, d, rt, (xq, xs), (xqp, xsp) = _routed_setup(wfmt, seed=5, I=I, neg_scales=neg)
     M, H, E, k, I = sh.M, sh.H, sh.E, sh.k, sh.I
     P = M * k
     hq = torch.empty((P, I), dtype=torch.uint8, device=DEV)
