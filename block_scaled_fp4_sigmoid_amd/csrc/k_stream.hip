@@ -64,6 +64,12 @@ constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every record count
 #ifndef MOE_RING_LOADS
 #define MOE_RING_LOADS 32  // 16-byte loads per lane the register ring may hold
 #endif
+#ifndef MOE_ROWS_TARGET_WGS
+#define MOE_ROWS_TARGET_WGS 512  // down by rows: workgroups to spread an expert set over
+#endif
+#ifndef MOE_ROWS_MAX_KB
+#define MOE_ROWS_MAX_KB 32  // down by rows: most weight KB per wave
+#endif
 #ifndef MOE_MIN_BLOCKS
 #define MOE_MIN_BLOCKS 2  // workgroups per CU the register budget must allow
 #endif
@@ -345,7 +351,7 @@ __device__ __forceinline__ void quad_steps(Ring<MB, NB, DQ, QS>& R, int v, const
 // blocks against NB blocks of activation rows arow0 + [0, npass).  The ring
 // holds DQ quads; each step's slot is refilled right after its MFMAs, so
 // DQ*QS - 1 steps stay in flight.  Steps past the range load zeros for both
-// operands.  QS < 4 only when all of K is one quad of QS steps.
+// operands.
 template <int FMT, int MB, int NB, int DQ, int QS>
 __device__ __forceinline__ void stream_pass(const StreamJob& J, int e, const int (&wblk)[MB], int arow0, int npass,
                                             int s0, int nst, int (&smax)[NB], v4f (&acc)[MB][2]) {
@@ -368,23 +374,17 @@ __device__ __forceinline__ void stream_pass(const StreamJob& J, int e, const int
     // last step).  The wait counts at the loop head are merged over the entry
     // and the back edge; an entry order with the scales issued last would
     // make the first use of a quad's scales wait for every load in flight.
-    if constexpr (QS == 4) {
+    static_assert(QS == 4, "the ring streams whole quads");
 #pragma unroll
-        for (int v = 0; v < DQ; ++v) {
+    for (int v = 0; v < DQ; ++v) {
 #pragma unroll
-            for (int u = 0; u < QS; ++u) {
-                __builtin_amdgcn_sched_barrier(0);
-                if (u == QS - 1) ring_load_scales<FMT, MB, NB, DQ, QS>(R, v, c, q0 + v, s_end);
-                ring_load_step<FMT, MB, NB, DQ, QS>(R, v, u, c, q0 + v, s_end);
-            }
+        for (int u = 0; u < QS; ++u) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (u == QS - 1) ring_load_scales<FMT, MB, NB, DQ, QS>(R, v, c, q0 + v, s_end);
+            ring_load_step<FMT, MB, NB, DQ, QS>(R, v, u, c, q0 + v, s_end);
         }
-        __builtin_amdgcn_sched_barrier(0);
-    } else {  // all of K in one quad: the loop runs once, the order is free
-        static_assert(DQ == 1, "a short ring holds one quad");
-        ring_load_scales<FMT, MB, NB, DQ, QS>(R, 0, c, q0, s_end);
-#pragma unroll
-        for (int u = 0; u < QS; ++u) ring_load_step<FMT, MB, NB, DQ, QS>(R, 0, u, c, q0, s_end);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -578,12 +578,14 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_quant(const float* __restri
     if (q8 == 0) h_s[(size_t)row * cbs + cb] = sc;
 }
 
-// ---- down -------------------------------------------------------------------
+// ---- down along K (K above one quad) ------------------------------------------
 // Item = (slot, 64*MB output features); wave w owns MB blocks of 16 features.
 // Activations are h rows in bucket order; the output row of bucket position b
 // is its pair id bucket[b] (the token row for a dense expert).
 
-template <int FMT, int MB, int QS, int DQ>
+constexpr int kDownMB = 2;  // 16-row weight blocks per wave in down along K
+
+template <int FMT, int MB>
 __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J, float* __restrict__ y) {
     const int H = J.N, I = J.K;
     constexpr int RB = 64 * MB;
@@ -615,13 +617,13 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J, 
         int smax[2] = {0, 0};
         if (npass > 16) {
             int sm[2];
-            stream_pass<FMT, MB, 2, DQ == 1 ? 1 : ring_quads<FMT, MB, 2>(), QS>(J, tk.e, wblk, arow0, npass, 0,
+            stream_pass<FMT, MB, 2, ring_quads<FMT, MB, 2>(), 4>(J, tk.e, wblk, arow0, npass, 0,
                                                                                  nst, sm, acc);
             smax[0] = sm[0];
             smax[1] = sm[1];
         } else {
             int sm[1];
-            stream_pass<FMT, MB, 1, DQ == 1 ? 1 : ring_quads<FMT, MB, 1>(), QS>(J, tk.e, wblk, arow0, npass, 0,
+            stream_pass<FMT, MB, 1, ring_quads<FMT, MB, 1>(), 4>(J, tk.e, wblk, arow0, npass, 0,
                                                                                  nst, sm, acc);
             smax[0] = sm[0];
         }
@@ -635,6 +637,147 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J, 
                     if (FMT == kFmtNV) v = v * nv_row_factor(smax[j], gs);
                     *reinterpret_cast<v4f*>(y + (size_t)orow[j] * H + f0 + 16 * mb + 4 * g) = v;
                 }
+            }
+        }
+    }
+}
+
+// The S steps of one 16-row block in down-by-rows (step U at a time; the
+// MFMA's scale byte selects are immediates).
+template <int FMT, int S, int D, int U>
+__device__ __forceinline__ void rows_steps(v4f& acc, const v4i (&wa)[D][S], const uint32_t (&wsc)[D][FMT == kFmtMX ? 1 : 2],
+                                           int d, const v4i (&b)[S][2], const uint32_t (&bs)[S],
+                                           const v8h (&B16)[FMT == kFmtNV ? S : 1][4], int g) {
+    if constexpr (U < S) {
+        const v4i a = wa[d][U];
+        if constexpr (FMT == kFmtMX) {
+            const v8i A = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+            const v8i Bm = {b[U][0].x, b[U][0].y, b[U][0].z, b[U][0].w, b[U][1].x, b[U][1].y, b[U][1].z, b[U][1].w};
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bm, acc, 4, 0, U, (int)wsc[d][0], 0,
+                                                                   (int)(bs[U] >> (8 * g)));
+        } else {
+            float sv0, sv1;
+            v2h m;
+            nv_scales2<U & 1>(wsc[d][U >> 1], sv0, sv1, m);
+            const v8h A0 = nv_dequant8((uint32_t)a.x, sv0, m[0]);
+            const v8h A1 = nv_dequant8((uint32_t)a.y, sv0, m[0]);
+            const v8h A2 = nv_dequant8((uint32_t)a.z, sv1, m[1]);
+            const v8h A3 = nv_dequant8((uint32_t)a.w, sv1, m[1]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, B16[U][0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, B16[U][1], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2, B16[U][2], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3, B16[U][3], acc, 0, 0, 0);
+        }
+        rows_steps<FMT, S, D, U + 1>(acc, wa, wsc, d, b, bs, B16, g);
+    }
+}
+
+// ---- down for a short K: streaming along the output rows ---------------------
+// When all of K is one quad (S = K/128 <= 4 steps) there is nothing to stream
+// along K, so an item streams its weight rows instead: each wave converts its
+// pass's activation rows once and keeps them in registers, keeps D blocks of 16
+// weight rows in flight, and writes a block's outputs as soon as its S steps
+// are done (stores past the wave's blocks or the pass's rows are dropped by the
+// buffer range check, so the loop has no branches).  Item = (slot, run of
+// 4 * bpw blocks); wave w takes blocks [w * bpw, (w + 1) * bpw) of the run.
+// Passes of 16 activation rows; a later pass reads the item's weights again.
+template <int FMT, int S, int D>
+__global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down_rows(StreamJob J, float* __restrict__ y) {
+    const int H = J.N, K = J.K;
+    const int bpw = J.span;
+    const int item = blockIdx.x % J.nblk;
+    const int slot = blockIdx.x / J.nblk;
+    Tokens tk;
+    if (!resolve(J, slot, tk)) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int i = lane & 15, g = lane >> 4;
+    const int nbr = H / 16;
+    const int rb0 = (item * 4 + wave) * bpw;
+    const int nb = max(0, min(bpw, nbr - rb0));
+    constexpr int SQ = FMT == kFmtMX ? 256 : 512;  // scale bytes per block (one quad)
+    const uint32_t wbytes = (uint32_t)H * (K / 2), sbytes = (uint32_t)nbr * SQ;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(J.w + (size_t)tk.e * wbytes, wbytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(J.sc + (size_t)tk.e * sbytes, sbytes);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(y, (uint32_t)J.out_rows * (uint32_t)H * 4u);
+    const float gs = FMT == kFmtNV ? J.gscale[tk.e] : 1.0f;
+
+    for (int t0 = 0; t0 < tk.n; t0 += 16) {
+        const int npass = min(16, tk.n - t0);
+        const int arow0 = tk.base + t0;
+        const bool okr = i < npass;
+        const int orow = okr ? (J.dense ? arow0 + i : J.bucket[arow0 + i]) : 0;
+        // the lane's activation row (column i of the MFMAs), all S steps
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(J.a_q + (size_t)arow0 * K, (uint32_t)npass * (uint32_t)K);
+        const __amdgpu_buffer_rsrc_t ras = make_rsrc(J.a_s + (size_t)arow0 * (K / 32), (uint32_t)npass * (uint32_t)(K / 32));
+        const uint32_t va = okr ? (uint32_t)i * K + (FMT == kFmtMX ? 16 : 32) * g : kOOB;
+        const uint32_t vas = okr ? (uint32_t)i * (K / 32) : kOOB;
+        v4i b[S][2];
+        uint32_t bs[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            b[s][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, va, 128 * s, 0);
+            b[s][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, va + (FMT == kFmtMX ? 64 : 16), 128 * s, 0);
+            bs[s] = __builtin_amdgcn_raw_buffer_load_b32(ras, vas, 4 * s, 0);
+        }
+        // weight ring: slot d holds one block (S steps and its scale entry)
+        v4i wa[D][S];
+        uint32_t wsc[D][FMT == kFmtMX ? 1 : 2];
+        auto load_block = [&](int d, int blk) {
+            const bool ok = blk < nb;
+            const uint32_t rb = (uint32_t)(rb0 + blk);
+            const uint32_t vw = ok ? rb * S * 1024 + 16 * lane : kOOB;
+            const uint32_t vs = ok ? rb * SQ + (SQ / 64) * lane : kOOB;
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                wa[d][s] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw, 1024 * s, MOE_WEIGHT_AUX);
+            if constexpr (FMT == kFmtMX) {
+                wsc[d][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs, 0, 0);
+            } else {
+                const auto sv = __builtin_amdgcn_raw_buffer_load_b64(rs, vs, 0, 0);
+                wsc[d][0] = sv[0];
+                wsc[d][1] = sv[1];
+            }
+        };
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            __builtin_amdgcn_sched_barrier(0);
+            load_block(d, d);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // activations as MFMA operands: MX keeps the codes; NV converts to f16
+        // scaled by 2^(s - smax) with smax the row's largest scale code
+        int smax = 0;
+        float fac = 1.0f;
+        v8h B16[FMT == kFmtNV ? S : 1][4];
+        if constexpr (FMT == kFmtNV) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const uint32_t v = bs[s];
+                smax = max(smax, (int)max(max(v & 0xffu, (v >> 8) & 0xffu), max((v >> 16) & 0xffu, v >> 24)));
+            }
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const int sb = (int)((bs[s] >> (8 * g)) & 0xffu);
+                const float sf = exp2i(max(sb - smax, -126));
+                B16[s][0] = fp8x8_to_f16((uint32_t)b[s][0].x, (uint32_t)b[s][0].y, sf);
+                B16[s][1] = fp8x8_to_f16((uint32_t)b[s][0].z, (uint32_t)b[s][0].w, sf);
+                B16[s][2] = fp8x8_to_f16((uint32_t)b[s][1].x, (uint32_t)b[s][1].y, sf);
+                B16[s][3] = fp8x8_to_f16((uint32_t)b[s][1].z, (uint32_t)b[s][1].w, sf);
+            }
+            fac = nv_row_factor(smax, gs);
+        }
+        const uint32_t ybase = okr ? (uint32_t)orow * (uint32_t)H * 4u + 16u * g : kOOB;
+        for (int b0 = 0; b0 < nb; b0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                __builtin_amdgcn_sched_barrier(0);
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+                rows_steps<FMT, S, D, 0>(acc, wa, wsc, d, b, bs, B16, g);
+                const int blk = b0 + d;
+                const uint32_t vo = blk < nb ? ybase + (uint32_t)(rb0 + blk) * 64u : kOOB;
+                const v4f v = acc * fac;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), ry, vo, 0, 0);
+                load_block(d, blk + D);
             }
         }
     }
@@ -657,27 +800,6 @@ GatePlan gate_plan(const ExpertJob& j) {
     if (sps < steps) sps = (sps + 3) / 4 * 4;
     p.span = 128 * sps;
     p.splits = (steps + sps - 1) / sps;
-    return p;
-}
-
-struct DownPlan {
-    int MB, QS, DQ, nblk;
-};
-
-// A K of one quad or less runs a one-quad ring (nothing to prefetch) and
-// gets more 16-row blocks per wave: its items are otherwise too small to pay
-// for their start.
-DownPlan down_plan(const ExpertJob& j) {
-    DownPlan p;
-    const int steps = j.K / 128;
-    p.QS = steps <= 2 ? 2 : 4;
-    p.DQ = steps <= 4 ? 1 : 2;
-    p.MB = 2;
-    if (steps <= 2)
-        p.MB = j.N_out % 512 == 0 ? 8 : (j.N_out % 256 == 0 ? 4 : 2);
-    else if (steps <= 4 && j.N_out % 256 == 0 && j.w.fmt == MOE_FMT_MXFP4)
-        p.MB = 4;  // (NVFP4's dequantization needs the registers)
-    p.nblk = j.N_out / (64 * p.MB);
     return p;
 }
 
@@ -746,37 +868,47 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
     return hipGetLastError();
 }
 
-template <int FMT>
-hipError_t launch_down_f(const StreamJob& J, const DownPlan& p, int blocks, float* y, hipStream_t stream) {
-    const dim3 g(blocks), b(kThreads);
-    if (p.QS == 2) {
-        if (p.MB == 8)
-            hipLaunchKernelGGL((k_down<FMT, 8, 2, 1>), g, b, 0, stream, J, y);
-        else if (p.MB == 4)
-            hipLaunchKernelGGL((k_down<FMT, 4, 2, 1>), g, b, 0, stream, J, y);
-        else
-            hipLaunchKernelGGL((k_down<FMT, 2, 2, 1>), g, b, 0, stream, J, y);
-    } else if (p.DQ == 1) {
-        if constexpr (FMT == kFmtMX)
-            if (p.MB == 4) {
-                hipLaunchKernelGGL((k_down<FMT, 4, 4, 1>), g, b, 0, stream, J, y);
-                return hipGetLastError();
-            }
-        hipLaunchKernelGGL((k_down<FMT, 2, 4, 1>), g, b, 0, stream, J, y);
-    } else {
-        hipLaunchKernelGGL((k_down<FMT, 2, 4, 2>), g, b, 0, stream, J, y);
-    }
+// Down by rows (K of at most one quad): blocks per wave and items per slot so
+// that about two workgroups per CU stream runs of equal length.
+template <int FMT, int S>
+hipError_t launch_down_rows_s(StreamJob J, int slots, float* y, hipStream_t stream) {
+    constexpr int D = S <= 2 ? 8 : 4;
+    const int nbr = J.N / 16;
+    int items = std::max(1, std::min(MOE_ROWS_TARGET_WGS / std::max(1, slots), nbr / (4 * D)));
+    // a run short enough that an expert with many passes still spreads out
+    constexpr int max_bpw = MOE_ROWS_MAX_KB / S;
+    items = std::max(items, (nbr + 4 * max_bpw - 1) / (4 * max_bpw));
+    const int bpw = (nbr + 4 * items - 1) / (4 * items);
+    items = (nbr + 4 * bpw - 1) / (4 * bpw);
+    J.span = bpw;
+    J.nblk = items;
+    hipLaunchKernelGGL((k_down_rows<FMT, S, D>), dim3(slots * items), dim3(kThreads), 0, stream, J, y);
     return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_down_rows(const StreamJob& J, int slots, float* y, hipStream_t stream) {
+    switch (J.K / 128) {
+        case 1: return launch_down_rows_s<FMT, 1>(J, slots, y, stream);
+        case 2: return launch_down_rows_s<FMT, 2>(J, slots, y, stream);
+        case 3: return launch_down_rows_s<FMT, 3>(J, slots, y, stream);
+        default: return launch_down_rows_s<FMT, 4>(J, slots, y, stream);
+    }
 }
 
 hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8_t* h_s, float* y,
                            hipStream_t stream) {
-    const DownPlan p = down_plan(job);
     StreamJob J = stream_job(job, job.N_out, h_q, h_s, out_rows_of(job));
-    J.nblk = p.nblk;
-    const int blocks = job.slots * p.nblk;
-    return job.w.fmt == MOE_FMT_MXFP4 ? launch_down_f<kFmtMX>(J, p, blocks, y, stream)
-                                      : launch_down_f<kFmtNV>(J, p, blocks, y, stream);
+    if (job.K <= 512)  // all of K in one quad: stream along the rows
+        return job.w.fmt == MOE_FMT_MXFP4 ? launch_down_rows<kFmtMX>(J, job.slots, y, stream)
+                                          : launch_down_rows<kFmtNV>(J, job.slots, y, stream);
+    J.nblk = job.N_out / (64 * kDownMB);
+    const dim3 g(job.slots * J.nblk), b(kThreads);
+    if (job.w.fmt == MOE_FMT_MXFP4)
+        hipLaunchKernelGGL((k_down<kFmtMX, kDownMB>), g, b, 0, stream, J, y);
+    else
+        hipLaunchKernelGGL((k_down<kFmtNV, kDownMB>), g, b, 0, stream, J, y);
+    return hipGetLastError();
 }
 
 }  // namespace moe

@@ -186,9 +186,11 @@ def test_gate_up_routed_parity(wfmt, H, neg):
 
 @pytest.mark.parametrize("wfmt,I,neg", [(synth.MXFP4, 256, False), (synth.NVFP4, 256, False),
                                         (synth.MXFP4, 1536, False), (synth.NVFP4, 1536, False),
-                                        (synth.NVFP4, 256, True), (synth.NVFP4, 1536, True)])
+                                        (synth.NVFP4, 256, True), (synth.NVFP4, 1536, True),
+                                        (synth.MXFP4, 128, False), (synth.NVFP4, 384, False),
+                                        (synth.MXFP4, 512, False), (synth.NVFP4, 512, True)])
 def test_down_routed_parity(wfmt, I, neg):
-    # I = 256 fits one chunk (two row blocks per wave); 1536 is three chunks
+    # I <= 512 (one quad of K steps) streams along the output rows; 1536 along K
     sh, inp, d, rt, (xq, xs), (xqp, xsp) = _routed_setup(wfmt, seed=5, I=I, neg_scales=neg)
     M, H, E, k, I = sh.M, sh.H, sh.E, sh.k, sh.I
     P = M * k
