@@ -26,33 +26,39 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restric
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
     constexpr int kMaxChunks = 2;  // H <= 16384
+    constexpr int kBatch = 8;      // slots whose loads are in flight together
     float rv[kMaxChunks][8];
+    uint32_t gw[kMaxChunks][4];
     float ss = 0.f;
     const float* wr = topk_w + (size_t)r * k;
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
         const int col = c * kFinChunk + tid * 8;
         if (col < H) {
+            // every operand of the column group is requested before the first add
             const v4i rb = load16(residual + (size_t)r * H + col);
-            const uint32_t rw[4] = {(uint32_t)rb.x, (uint32_t)rb.y, (uint32_t)rb.z, (uint32_t)rb.w};
+            const v4i gb = load16(gamma + col);
+            float4 sa = {0.f, 0.f, 0.f, 0.f}, sb = sa;
+            if (y_sh) {
+                sa = *reinterpret_cast<const float4*>(y_sh + (size_t)r * H + col);
+                sb = *reinterpret_cast<const float4*>(y_sh + (size_t)r * H + col + 4);
+            }
+            gw[c][0] = (uint32_t)gb.x; gw[c][1] = (uint32_t)gb.y; gw[c][2] = (uint32_t)gb.z; gw[c][3] = (uint32_t)gb.w;
             float t[8];
+            const uint32_t rw[4] = {(uint32_t)rb.x, (uint32_t)rb.y, (uint32_t)rb.z, (uint32_t)rb.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 t[2 * i] = bf16_to_f32(rw[i] & 0xffffu);
                 t[2 * i + 1] = bf16_to_f32(rw[i] >> 16);
             }
-            if (y_sh) {
-                const float4 a = *reinterpret_cast<const float4*>(y_sh + (size_t)r * H + col);
-                const float4 b = *reinterpret_cast<const float4*>(y_sh + (size_t)r * H + col + 4);
-                t[0] += a.x; t[1] += a.y; t[2] += a.z; t[3] += a.w;
-                t[4] += b.x; t[5] += b.y; t[6] += b.z; t[7] += b.w;
-            }
-            // slot order; loads of four slots are issued before their adds
-            for (int j0 = 0; j0 < k; j0 += 4) {
-                float4 ya[4], yb[4];
-                float wj[4];
+            t[0] += sa.x; t[1] += sa.y; t[2] += sa.z; t[3] += sa.w;
+            t[4] += sb.x; t[5] += sb.y; t[6] += sb.z; t[7] += sb.w;
+            // slot order
+            for (int j0 = 0; j0 < k; j0 += kBatch) {
+                float4 ya[kBatch], yb[kBatch];
+                float wj[kBatch];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < kBatch; ++u) {
                     const int j = j0 + u;
                     if (j < k) {
                         const float* yr = y + ((size_t)r * k + j) * H + col;
@@ -62,7 +68,7 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restric
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < kBatch; ++u) {
                     if (j0 + u < k) {
                         t[0] = fmaf(wj[u], ya[u].x, t[0]); t[1] = fmaf(wj[u], ya[u].y, t[1]);
                         t[2] = fmaf(wj[u], ya[u].z, t[2]); t[3] = fmaf(wj[u], ya[u].w, t[3]);
@@ -98,13 +104,11 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restric
     for (int c = 0; c < kMaxChunks; ++c) {
         const int col = c * kFinChunk + tid * 8;
         if (col < H) {
-            const v4i gb = load16(gamma + col);
-            const uint32_t gw[4] = {(uint32_t)gb.x, (uint32_t)gb.y, (uint32_t)gb.z, (uint32_t)gb.w};
             uint32_t ob[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float o0 = rv[c][2 * i] * inv * bf16_to_f32(gw[i] & 0xffffu);
-                const float o1 = rv[c][2 * i + 1] * inv * bf16_to_f32(gw[i] >> 16);
+                const float o0 = rv[c][2 * i] * inv * bf16_to_f32(gw[c][i] & 0xffffu);
+                const float o1 = rv[c][2 * i + 1] * inv * bf16_to_f32(gw[c][i] >> 16);
                 ob[i] = f32_to_bf16_rne(o0) | (f32_to_bf16_rne(o1) << 16);
             }
             *reinterpret_cast<v4i*>(out + (size_t)r * H + col) = v4i{(int)ob[0], (int)ob[1], (int)ob[2], (int)ob[3]};

@@ -404,11 +404,20 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
     const RouterPlan p = router_plan(M, H, E);
     hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, s1,
                                           shb ? kBf16GateUp : kBf16None, stream);
-    if (e == hipSuccess)
-        e = launch_topk_bucket(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale,
-                               logits_out, r, s2, shb ? kBf16Swiglu : kBf16None, s3, shb ? kBf16Down : kBf16None,
-                               stream);
-    if (e == hipSuccess) e = launch_quant_pairs(x, r.bucket, k, M, H, L.xq, L.xs, L.xqt, L.xst, stream);
+    if (M * k <= kSmallPairs) {  // route step and activation quant share a launch
+        if (e == hipSuccess)
+            e = launch_topk(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale, logits_out, r, s2,
+                            shb ? kBf16Swiglu : kBf16None, stream);
+        if (e == hipSuccess)
+            e = launch_bucket_quant(M, E, k, r, x, H, L.xq, L.xs, L.xqt, L.xst, s3, shb ? kBf16Down : kBf16None,
+                                    stream);
+    } else {
+        if (e == hipSuccess)
+            e = launch_topk_bucket(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale,
+                                   logits_out, r, s2, shb ? kBf16Swiglu : kBf16None, s3,
+                                   shb ? kBf16Down : kBf16None, stream);
+        if (e == hipSuccess) e = launch_quant_pairs(x, r.bucket, k, M, H, L.xq, L.xs, L.xqt, L.xst, stream);
+    }
     const ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
     if (e == hipSuccess) e = launch_gate_up_fp4(gu, L.xq, L.xs, L.hq, L.hs, L.part, stream);
     if (e == hipSuccess && sf != MOE_FMT_NONE && !shb)

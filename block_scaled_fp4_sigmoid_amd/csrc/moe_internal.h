@@ -47,6 +47,9 @@ hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int 
                                   const RouterPlan& plan, float* partials, const Bf16Side& side1, int stage1,
                                   hipStream_t stream);
 // logits: the router partials (splits of them), or given logits (splits = 1).
+hipError_t launch_topk(const float* partials, int splits, const float* bias, int M, int E, int k,
+                       float routed_scale, float* logits_out, const moe_routing& route, const Bf16Side& side2,
+                       int stage2, hipStream_t stream);
 hipError_t launch_topk_bucket(const float* partials, int splits, const float* bias, int M, int E,
                               int k, float routed_scale, float* logits_out,
                               const moe_routing& route, const Bf16Side& side2, int stage2,
@@ -63,6 +66,12 @@ hipError_t launch_quant_mxfp8(const uint16_t* x, int M, int K, uint8_t* q, uint8
 // rows); with qt != nullptr also the M token-ordered rows into qt/st.
 hipError_t launch_quant_pairs(const uint16_t* x, const int32_t* bucket, int k, int M, int K, uint8_t* qp,
                               uint8_t* sp, uint8_t* qt, uint8_t* st, hipStream_t stream);
+// The route step (after launch_topk) and launch_quant_pairs in one launch,
+// for M*k <= kSmallPairs pairs; side3 rides along.
+constexpr int kSmallPairs = 256;
+hipError_t launch_bucket_quant(int M, int E, int k, const moe_routing& route, const uint16_t* x, int K,
+                               uint8_t* qp, uint8_t* sp, uint8_t* qt, uint8_t* st, const Bf16Side& side3,
+                               int stage3, hipStream_t stream);
 
 
 // Expert GEMM jobs.  A routed job covers slots [0, U_max) of the active-expert
