@@ -46,6 +46,9 @@ __device__ __forceinline__ void split3(float w, uint32_t& b1, uint32_t& b2, uint
     b3 = __float_as_uint(w3) >> 16;
 }
 
+// U: K-steps of 32 whose loads are issued together (a chunk of 256 takes one
+// round of loads); NBT: 16-row blocks of the row group (1 when M <= 16).
+template <int U, int NBT>
 __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restrict__ x,
                                                          const float* __restrict__ w_router,
                                                          int M, int H, int E, int splits,
@@ -69,24 +72,23 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
     const bool ev = e < E;
     const float* wrow = w_router + (size_t)(ev ? e : 0) * H;
     const int r0 = rgi * 64;
-    const int nb = min(4, (M - r0 + 15) / 16);
-    const uint16_t* xr[4];
-    bool xv[4];
+    const int nb = min(NBT, (M - r0 + 15) / 16);
+    const uint16_t* xr[NBT];
+    bool xv[NBT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NBT; ++j) {
         const int r = r0 + j * 16 + i;
         xv[j] = (j < nb) && (r < M);
         xr[j] = x + (size_t)(xv[j] ? r : 0) * H;
     }
-    v4f acc[4];
+    v4f acc[NBT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NBT; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     const int kbeg = kc * kchunk;
-    constexpr int U = 4;  // K-steps of 32 whose loads are issued together
     for (int k0 = kbeg; k0 < kbeg + kchunk; k0 += 32 * U) {
         float4 wl[U][2];
-        v4i xb[U][4];
+        v4i xb[U][NBT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int kk = k0 + 32 * u + 8 * g;
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
                 wl[u][0] = wl[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NBT; ++j)
                 xb[u][j] = (j < nb && xv[j]) ? load16(xr[j] + kk) : v4i{0, 0, 0, 0};
         }
 #pragma unroll
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
             const v8bf A2 = __builtin_bit_cast(v8bf, v4i{(int)p2[0], (int)p2[1], (int)p2[2], (int)p2[3]});
             const v8bf A3 = __builtin_bit_cast(v8bf, v4i{(int)p3[0], (int)p3[1], (int)p3[2], (int)p3[3]});
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < NBT; ++j) {
                 if (j < nb) {
                     const v8bf b = __builtin_bit_cast(v8bf, xb[u][j]);
                     acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, acc[j], 0, 0, 0);
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
     }
     // lane holds D[4g + t][i]: expert te*16 + 4g + t, row r0 + 16j + i
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NBT; ++j) {
         const int r = r0 + j * 16 + i;
         if (j < nb && r < M) {
 #pragma unroll
@@ -148,8 +150,17 @@ hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int 
     const int units = ((E + 15) / 16) * plan.splits * plan.row_groups;
     const int blocks = (units + 3) / 4;
     const int extra = stage1 == kBf16None ? 0 : side1.blocks;
-    hipLaunchKernelGGL(k_router_partials, dim3(blocks + extra), dim3(256), 0, stream, x, w_router, M, H, E,
-                       plan.splits, plan.kchunk, units, blocks, partials, side1, stage1);
+    const dim3 g(blocks + extra), b(256);
+    const bool wide = plan.kchunk % 256 == 0, one = M <= 16;  // (four row blocks keep U = 4: registers)
+    if (wide && one)
+        hipLaunchKernelGGL((k_router_partials<8, 1>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
+                           units, blocks, partials, side1, stage1);
+    else if (one)
+        hipLaunchKernelGGL((k_router_partials<4, 1>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
+                           units, blocks, partials, side1, stage1);
+    else
+        hipLaunchKernelGGL((k_router_partials<4, 4>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
+                           units, blocks, partials, side1, stage1);
     return hipGetLastError();
 }
 
