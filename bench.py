@@ -32,6 +32,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "verify-m8-h7168-e256-k8-nvfp4"
+DOMINANT = "k_gate_up"
+# sources that decide what the dominant kernel reads and writes
+KERNEL_SOURCES = ("block_scaled_fp4_sigmoid_amd/csrc/k_stream.hip", "block_scaled_fp4_sigmoid_amd/csrc/moe_device.h",
+                  "block_scaled_fp4_sigmoid_amd/csrc/moe_internal.h")
 
 
 def log(*a):
@@ -62,6 +66,98 @@ def byte_model(s, U):
     return dict(per_expert=per_expert, routed=U * per_expert, shared=shared, router=router,
                 acts=acts, total=U * per_expert + shared + router + acts,
                 gate_up_launch=gate_up_launch)
+
+
+def kernel_sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{DOMINANT}_{workload}.md")
+
+
+def read_counter_csv(path, counter):
+    """Per-dispatch values of one counter from a rocprofv3 counter_collection CSV:
+    {kernel name: [(grid, value), ...]} (value in the counter's unit, KiB for
+    FETCH_SIZE / WRITE_SIZE)."""
+    import csv
+    out = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], []).append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return out
+
+
+def traffic_summary(fetch_dir, write_dir, workload, command):
+    """HBM bytes per launch of the routed gate_up from two counter runs
+    (FETCH_SIZE, WRITE_SIZE), each scaled by what the same counter reports for
+    the weight-packing kernel, a plain permuting copy of known size (16 bytes
+    read and 16 written per thread)."""
+    f = read_counter_csv(os.path.join(fetch_dir, "run_counter_collection.csv"), "FETCH_SIZE")
+    w = read_counter_csv(os.path.join(write_dir, "run_counter_collection.csv"), "WRITE_SIZE")
+
+    def pick(d, key):
+        return [v for name, vals in d.items() if key in name for v in vals]
+
+    def copy_factor(d):
+        vals = pick(d, "k_pack_w")
+        known = sum(16 * g for g, _ in vals)
+        counted = sum(1024 * v for _, v in vals)
+        return known / counted, len(vals)
+
+    ff, nf = copy_factor(f)
+    fw, nw = copy_factor(w)
+    gf = [v for _, v in pick(f, DOMINANT)]
+    gw = [v for _, v in pick(w, DOMINANT)]
+    fetch = 1024 * ff * float(np.mean(gf))
+    write = 1024 * fw * float(np.mean(gw))
+    lines = [
+        f"# HBM traffic of the routed gate_up, {workload}",
+        "",
+        "Commands (from the repository root, on one MI355X):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        f"- copy kernel (k_pack_w, 16 B read + 16 B written per thread): FETCH_SIZE x {ff:.4f}, "
+        f"WRITE_SIZE x {fw:.4f} ({nf} and {nw} dispatches)",
+        f"- gate_up dispatches: {len(gf)} (FETCH_SIZE), {len(gw)} (WRITE_SIZE)",
+        f"- FETCH_SIZE mean {np.mean(gf):.1f} KiB -> {fetch / 1e6:.3f} MB read per launch",
+        f"- WRITE_SIZE mean {np.mean(gw):.1f} KiB -> {write / 1e6:.3f} MB written per launch",
+        "",
+        f"traffic_bytes_per_launch: {int(round(fetch + write))}",
+        f"kernel_sources_sha256_16: {kernel_sources_sha()}",
+        "",
+    ]
+    return "\n".join(lines)
+
+
+def stored_traffic(workload):
+    """Traffic per launch from the committed summary, or None when there is
+    none or the kernel's sources changed since the counters were taken."""
+    p = traffic_path(workload)
+    if not os.path.exists(p):
+        return None
+    vals = {}
+    with open(p) as fh:
+        for ln in fh:
+            if ":" in ln and not ln.startswith(("-", "#", " ")):
+                k_, v_ = ln.split(":", 1)
+                vals[k_.strip()] = v_.strip()
+    if vals.get("kernel_sources_sha256_16") != kernel_sources_sha():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def timed(fn, steps, warmup, stream):
@@ -111,7 +207,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-gate-up", type=int, default=0,
                     help="only launch the routed gate_up kernel N times (for counter runs)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary of two rocprofv3 counter runs to stdout")
+    ap.add_argument("--traffic-command", default="", help="the commands to record in the summary")
     args = ap.parse_args()
+    if args.traffic_summary:
+        print(traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload,
+                              args.traffic_command))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the layer is one "
               "GPU's share of an expert/tensor-parallel MoE layer and this build has no "
@@ -260,7 +363,7 @@ def main():
         "copy_GBps": round(copy_gbps, 1),
         "roofline": {"kernel": "k_gate_up_fp4 (routed)", "bound": "hbm",
                      "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(name),
                      "us_per_launch": round(ms_gu * 1e3, 2),
                      "alg_bytes_per_launch": bm["gate_up_launch"]},
         "cpu_baseline": cpu,
