@@ -101,13 +101,14 @@ struct Tokens {
 };
 
 // Slot -> (expert, bucket range).  The three loads are independent; unused
-// slots have no rows.
+// slots have no rows.  A dense job's slots are its passes of kPassRows rows
+// (so many rows spread over workgroups instead of looping in each).
 __device__ __forceinline__ bool resolve(const StreamJob& J, int slot, Tokens& t) {
     if (J.dense) {
         t.e = 0;
-        t.base = 0;
-        t.n = J.M;
-        return true;
+        t.base = slot * kPassRows;
+        t.n = min(kPassRows, J.M - t.base);
+        return t.n > 0;
     }
     const int b0 = J.active_offsets[slot], b1 = J.active_offsets[slot + 1];
     const int e = J.active[slot];
@@ -785,6 +786,9 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down_rows(StreamJo
 
 // ---- host plans -------------------------------------------------------------
 
+// Slot dimension of a launch: the active-expert slots, or a dense job's passes.
+int grid_slots(const ExpertJob& j) { return j.dense ? (j.M + kPassRows - 1) / kPassRows : j.slots; }
+
 struct GatePlan {
     int span, splits, nblk;
 };
@@ -793,7 +797,7 @@ GatePlan gate_plan(const ExpertJob& j) {
     GatePlan p;
     const int K = j.K, steps = K / 128;
     p.nblk = j.N_out / GCOLS;
-    const long items = (long)j.slots * p.nblk;
+    const long items = (long)grid_slots(j) * p.nblk;
     int want = (int)std::max<long>(1, (MOE_STREAM_TARGET_ITEMS + items - 1) / items);
     want = std::min(want, std::max(1, steps / 8));  // at least 8 steps per split
     int sps = (steps + want - 1) / want;             // steps per split: whole quads
@@ -843,7 +847,7 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
     J.span = p.span;
     J.splits = p.splits;
     J.nblk = p.nblk;
-    const int blocks = job.slots * p.nblk * p.splits;
+    const int blocks = grid_slots(job) * p.nblk * p.splits;
     const bool mx = job.w.fmt == MOE_FMT_MXFP4;
     if (p.splits == 1) {
         if (mx)
@@ -872,7 +876,7 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
 // that about two workgroups per CU stream runs of equal length.
 template <int FMT, int S>
 hipError_t launch_down_rows_s(StreamJob J, int slots, float* y, hipStream_t stream) {
-    constexpr int D = S <= 2 ? 8 : 4;
+    constexpr int D = 4;  // blocks in flight per wave (deeper rings measured slower)
     const int nbr = J.N / 16;
     int items = std::max(1, std::min(MOE_ROWS_TARGET_WGS / std::max(1, slots), nbr / (4 * D)));
     // a run short enough that an expert with many passes still spreads out
@@ -900,10 +904,10 @@ hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8
                            hipStream_t stream) {
     StreamJob J = stream_job(job, job.N_out, h_q, h_s, out_rows_of(job));
     if (job.K <= 512)  // all of K in one quad: stream along the rows
-        return job.w.fmt == MOE_FMT_MXFP4 ? launch_down_rows<kFmtMX>(J, job.slots, y, stream)
-                                          : launch_down_rows<kFmtNV>(J, job.slots, y, stream);
+        return job.w.fmt == MOE_FMT_MXFP4 ? launch_down_rows<kFmtMX>(J, grid_slots(job), y, stream)
+                                          : launch_down_rows<kFmtNV>(J, grid_slots(job), y, stream);
     J.nblk = job.N_out / (64 * kDownMB);
-    const dim3 g(job.slots * J.nblk), b(kThreads);
+    const dim3 g(grid_slots(job) * J.nblk), b(kThreads);
     if (job.w.fmt == MOE_FMT_MXFP4)
         hipLaunchKernelGGL((k_down<kFmtMX, kDownMB>), g, b, 0, stream, J, y);
     else

@@ -212,10 +212,11 @@ def test_down_routed_parity(wfmt, I, neg):
     assert worst < 2e-3, worst
 
 
-@pytest.mark.parametrize("sfmt", [synth.MXFP4, synth.NVFP4])
-def test_dense_fp4_expert_parity(sfmt):
-    """The shared-expert path: one FP4 expert over all rows in order."""
-    M, H, I = 23, 384, 256
+@pytest.mark.parametrize("sfmt,M", [(synth.MXFP4, 23), (synth.NVFP4, 23), (synth.MXFP4, 70), (synth.NVFP4, 70)])
+def test_dense_fp4_expert_parity(sfmt, M):
+    """The shared-expert path: one FP4 expert over all rows in order (70 rows:
+    three passes of 32 rows, each its own workgroups)."""
+    H, I = 384, 256
     sh = synth.custom_shape(M=M, H=H, E=1, k=1, I=128, wfmt=synth.MXFP4, sfmt=sfmt, I_sh=I)
     inp = synth.make_inputs(sh, seed=8, pool_rows=64)
     d = staging.to_device(inp, DEV)
