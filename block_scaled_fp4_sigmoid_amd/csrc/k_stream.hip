@@ -255,31 +255,33 @@ __device__ __forceinline__ void ring_load_scales(Ring<MB, NB, DQ, QS>& R, int v,
     }
 }
 
-// Step u of the quad in slot v.
-template <int FMT, int MB, int NB, int DQ, int QS, int U>
-__device__ __forceinline__ void step_mfma(const Ring<MB, NB, DQ, QS>& R, int v, const int (&sfo)[NB],
-                                          v4f (&acc)[MB][2]) {
+// One K step (U of its quad) from operands in registers: a[mb] the weight
+// bytes of block mb, as[mb] its quad scale entry, b[j] the activation bytes of
+// N-block j, bs[j] their scale dword.
+template <int FMT, int MB, int NB, int U>
+__device__ __forceinline__ void mfma_step(const v4i (&a_)[MB], const uint32_t (&as)[MB][2], const v4i (&b)[NB][2],
+                                          const uint32_t (&bs)[NB], const int (&sfo)[NB], v4f (&acc)[MB][2]) {
     const int g = (threadIdx.x & 63) >> 4;
     if constexpr (FMT == kFmtMX) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const v4i a = R.a[v][U][mb];
+            const v4i a = a_[mb];
             const v8i A = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const v4i b0 = R.b[v][U][j][0], b1 = R.b[v][U][j][1];
+                const v4i b0 = b[j][0], b1 = b[j][1];
                 const v8i B = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
                 // A scale: byte U of the quad's dword; B scale: byte g of the step's dword
-                acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    A, B, acc[mb][j], 4, 0, U, (int)R.as[v][mb][0], 0, (int)(R.bs[v][U][j] >> (8 * g)));
+                acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc[mb][j], 4, 0, U, (int)as[mb][0],
+                                                                              0, (int)(bs[j] >> (8 * g)));
             }
         }
     } else {
         v8h B[NB][4];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            const v4i b0 = R.b[v][U][j][0], b1 = R.b[v][U][j][1];
-            const int sb = (int)((R.bs[v][U][j] >> (8 * g)) & 0xffu);
+            const v4i b0 = b[j][0], b1 = b[j][1];
+            const int sb = (int)((bs[j] >> (8 * g)) & 0xffu);
             const float sf = exp2i(max(sb + sfo[j], -126));
             B[j][0] = fp8x8_to_f16((uint32_t)b0.x, (uint32_t)b0.y, sf);
             B[j][1] = fp8x8_to_f16((uint32_t)b0.z, (uint32_t)b0.w, sf);
@@ -288,10 +290,10 @@ __device__ __forceinline__ void step_mfma(const Ring<MB, NB, DQ, QS>& R, int v, 
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const v4i a = R.a[v][U][mb];
+            const v4i a = a_[mb];
             float sv0, sv1;
             v2h m;
-            nv_scales2<U & 1>(R.as[v][mb][U >> 1], sv0, sv1, m);
+            nv_scales2<U & 1>(as[mb][U >> 1], sv0, sv1, m);
             const v8h A0 = nv_dequant8((uint32_t)a.x, sv0, m[0]);
             const v8h A1 = nv_dequant8((uint32_t)a.y, sv0, m[0]);
             const v8h A2 = nv_dequant8((uint32_t)a.z, sv1, m[1]);
@@ -305,6 +307,13 @@ __device__ __forceinline__ void step_mfma(const Ring<MB, NB, DQ, QS>& R, int v, 
             }
         }
     }
+}
+
+// Step u of the quad in slot v.
+template <int FMT, int MB, int NB, int DQ, int QS, int U>
+__device__ __forceinline__ void step_mfma(const Ring<MB, NB, DQ, QS>& R, int v, const int (&sfo)[NB],
+                                          v4f (&acc)[MB][2]) {
+    mfma_step<FMT, MB, NB, U>(R.a[v][U], R.as[v], R.b[v][U], R.bs[v][U], sfo, acc);
 }
 
 // NVFP4: largest E8M0 code of the lane's activation row(s) over K steps
@@ -397,6 +406,188 @@ __device__ __forceinline__ void stream_pass(const StreamJob& J, int e, const int
     }
 }
 
+// ---- streaming with the activation tile of a quad in LDS ---------------------
+// The four waves of a workgroup use the same activation rows.  Instead of each
+// wave loading its B operands every step, the workgroup loads the tile of a
+// quad (16*NB rows x 512 K codes and their 16 scale bytes per row) once, a
+// share per thread, into one of two LDS buffers, and the waves read their
+// operands from there; the register ring then holds weights only.  One barrier
+// per quad: tile q+1 is written while tile q is read, the barrier publishes it.
+constexpr int kTileRow = 528;                   // bytes per row: 512 codes + 16 scale bytes (staggers banks)
+constexpr int kTileBytes = kPassRows * kTileRow;  // one buffer, sized for two N-blocks
+
+template <int NB>
+struct ActShare {
+    v4i c[2 * NB];  // code chunks of the thread (16 B each)
+    v4i s;          // the scale bytes of row t (threads t < 16*NB)
+};
+
+// Requests the thread's share of tile q (absolute quad).  Rows past the pass
+// and steps at or past s_end read zeros.
+template <int NB>
+__device__ __forceinline__ void tile_load(ActShare<NB>& P, const Coord<kFmtMX, 1, NB>& c, int K, int npass, int q,
+                                          int s_end) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 2 * NB; ++k) {
+        const int li = t + kThreads * k, row = li >> 5, ch = li & 31;
+        const bool ok = row < npass && 4 * q + (ch >> 3) < s_end;
+        P.c[k] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, ok ? (uint32_t)(row * K + 512 * q + 16 * ch) : kOOB, 0, 0);
+    }
+    const bool oks = t < 16 * NB && t < npass && 4 * q < s_end;
+    P.s = __builtin_amdgcn_raw_buffer_load_b128(c.ras, oks ? (uint32_t)(t * (K / 32) + 16 * q) : kOOB, 0, 0);
+}
+
+// Writes the thread's share of tile q into an LDS buffer; the scale dwords of
+// steps at or past s_end become 0 (a partial last quad reads the next row's
+// bytes there).
+template <int NB>
+__device__ __forceinline__ void tile_store(const ActShare<NB>& P, uint8_t* buf, int q, int s_end) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 2 * NB; ++k) {
+        const int li = t + kThreads * k, row = li >> 5, ch = li & 31;
+        *reinterpret_cast<v4i*>(buf + row * kTileRow + 16 * ch) = P.c[k];
+    }
+    if (t < 16 * NB) {
+        v4i sc = P.s;
+        sc.x = 4 * q + 0 < s_end ? sc.x : 0;
+        sc.y = 4 * q + 1 < s_end ? sc.y : 0;
+        sc.z = 4 * q + 2 < s_end ? sc.z : 0;
+        sc.w = 4 * q + 3 < s_end ? sc.w : 0;
+        *reinterpret_cast<v4i*>(buf + t * kTileRow + 512) = sc;
+    }
+}
+
+// The lane's B operands of step u of the tile in buf.
+template <int FMT, int NB>
+__device__ __forceinline__ void tile_read(const uint8_t* buf, int u, v4i (&b)[NB][2], uint32_t (&bs)[NB]) {
+    const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const uint8_t* row = buf + (16 * j + i) * kTileRow;
+        bs[j] = *reinterpret_cast<const uint32_t*>(row + 512 + 4 * u);
+        // MX: [16g, +16) and [64 + 16g, +16) of the step; NV: [32g, +32)
+        const uint8_t* p = row + 128 * u + (FMT == kFmtMX ? 16 : 32) * g;
+        b[j][0] = *reinterpret_cast<const v4i*>(p);
+        b[j][1] = *reinterpret_cast<const v4i*>(p + (FMT == kFmtMX ? 64 : 16));
+    }
+}
+
+// Weight ring: DQ quads of MB blocks.
+template <int MB, int DQ>
+struct RingW {
+    v4i a[DQ][4][MB];
+    uint32_t as[DQ][MB][2];
+};
+
+template <int FMT, int MB, int NB, int DQ>
+__device__ __forceinline__ void ringw_load_step(RingW<MB, DQ>& R, int v, int u, const Coord<FMT, MB, NB>& c, int q,
+                                                int s_end) {
+    const int st = 4 * q + u;
+    const bool ok = st < s_end;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        R.a[v][u][mb] = __builtin_amdgcn_raw_buffer_load_b128(c.rw, ok ? c.vw[mb] : kOOB, 1024 * st, MOE_WEIGHT_AUX);
+}
+
+template <int FMT, int MB, int NB, int DQ>
+__device__ __forceinline__ void ringw_load_scales(RingW<MB, DQ>& R, int v, const Coord<FMT, MB, NB>& c, int q,
+                                                  int s_end) {
+    const bool okq = 4 * q < s_end;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        if constexpr (FMT == kFmtMX) {
+            R.as[v][mb][0] = __builtin_amdgcn_raw_buffer_load_b32(c.rs, okq ? c.vs[mb] : kOOB, 256 * q, 0);
+        } else {
+            const auto sv = __builtin_amdgcn_raw_buffer_load_b64(c.rs, okq ? c.vs[mb] : kOOB, 512 * q, 0);
+            R.as[v][mb][0] = sv[0];
+            R.as[v][mb][1] = sv[1];
+        }
+    }
+}
+
+// The four steps of the quad in slot v, the B operands of step U given and
+// those of step U+1 read from the tile meanwhile; each step's weight slot is
+// refilled with quad qn right after its MFMAs.
+template <int FMT, int MB, int NB, int DQ, int U>
+__device__ __forceinline__ void quadw_steps(RingW<MB, DQ>& R, int v, const Coord<FMT, MB, NB>& c, int qn, int s_end,
+                                            const uint8_t* tile, const v4i (&b)[NB][2], const uint32_t (&bs)[NB],
+                                            const int (&sfo)[NB], v4f (&acc)[MB][2]) {
+    if constexpr (U < 4) {
+        __builtin_amdgcn_sched_barrier(0);
+        v4i bn[NB][2];
+        uint32_t bsn[NB];
+        if constexpr (U < 3) tile_read<FMT, NB>(tile, U + 1, bn, bsn);
+        mfma_step<FMT, MB, NB, U>(R.a[v][U], R.as[v], b, bs, sfo, acc);
+        if constexpr (U == 3) ringw_load_scales<FMT, MB, NB, DQ>(R, v, c, qn, s_end);
+        ringw_load_step<FMT, MB, NB, DQ>(R, v, U, c, qn, s_end);
+        quadw_steps<FMT, MB, NB, DQ, U + 1>(R, v, c, qn, s_end, tile, bn, bsn, sfo, acc);
+    }
+}
+
+// A pass as stream_pass, with the activation tiles in LDS (tiles: two
+// kTileBytes buffers).  Every thread of the workgroup must call it with the
+// same arguments apart from the weight blocks (it has barriers).
+template <int FMT, int MB, int NB, int DQ>
+__device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const int (&wblk)[MB], int arow0,
+                                                int npass, int s0, int nst, int ms0, int mnst, int (&smax)[NB],
+                                                v4f (&acc)[MB][2], uint8_t* tiles) {
+    static_assert(DQ % 2 == 0, "slots alternate between the two tile buffers");
+    const Coord<FMT, MB, NB> c = make_coord<FMT, MB, NB>(J, e, wblk, arow0, npass);
+    Coord<kFmtMX, 1, NB> ca;  // the activation resources, for the tile loads
+    ca.ra = c.ra;
+    ca.ras = c.ras;
+    int sfo[NB];
+    if constexpr (FMT == kFmtNV) {
+        row_smax<FMT, MB, NB>(c, ms0, mnst, smax);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) sfo[j] = -smax[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            sfo[j] = 0;
+            smax[j] = 0;
+        }
+    }
+    const int K = J.K;
+    const int q0 = s0 / 4, nq = (nst + 3) / 4, s_end = s0 + nst;
+    ActShare<NB> P;
+    tile_load<NB>(P, ca, K, npass, q0, s_end);
+    RingW<MB, DQ> R;
+#pragma unroll
+    for (int v = 0; v < DQ; ++v) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (u == 3) ringw_load_scales<FMT, MB, NB, DQ>(R, v, c, q0 + v, s_end);
+            ringw_load_step<FMT, MB, NB, DQ>(R, v, u, c, q0 + v, s_end);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[mb][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    tile_store<NB>(P, tiles, q0, s_end);
+    __syncthreads();
+    for (int l0 = 0; l0 < nq; l0 += DQ) {
+#pragma unroll
+        for (int v = 0; v < DQ; ++v) {
+            const int q = q0 + l0 + v;  // the quad of slot v in this round
+            const uint8_t* tile = tiles + (v & 1) * kTileBytes;
+            v4i b[NB][2];
+            uint32_t bs[NB];
+            tile_read<FMT, NB>(tile, 0, b, bs);
+            tile_load<NB>(P, ca, K, npass, q + 1, s_end);  // in flight over the quad's steps
+            quadw_steps<FMT, MB, NB, DQ, 0>(R, v, c, q + DQ, s_end, tile, b, bs, sfo, acc);
+            // tile q+1 into the other buffer (its reads ended at the last barrier)
+            tile_store<NB>(P, tiles + ((v + 1) & 1) * kTileBytes, q + 1, s_end);
+            __syncthreads();
+        }
+    }
+}
+
 // Ring depth in quads for MB weight blocks and NB activation blocks: about
 // 32 loads of 16 bytes per lane in flight (the registers allow two quads
 // with two weight blocks and one activation block).
@@ -473,6 +664,7 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_gate_up(StreamJob 
 
     __shared__ float sG[kPassRows][2 * GCOLS + 1];  // fused: gate [0, GCOLS), up [GCOLS, 2*GCOLS)
     __shared__ int s_smax[kPassRows];
+    __shared__ __align__(16) uint8_t sTiles[FMT == kFmtNV ? 2 * kTileBytes : 16];  // activation tiles of two quads
 
     for (int t0 = 0; t0 < tk.n; t0 += kPassRows) {
         const int npass = min(kPassRows, tk.n - t0);
@@ -481,14 +673,18 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_gate_up(StreamJob 
         int smax[2] = {0, 0};
         if (npass > 16) {
             int sm[2];
-            stream_pass<FMT, GMB, 2, ring_quads<FMT, GMB, 2>(), 4>(J, tk.e, wblk, arow0, npass, s0, nst, sm,
-                                                                     acc);
+            if constexpr (FMT == kFmtNV)
+                stream_pass_lds<FMT, GMB, 2, 2>(J, tk.e, wblk, arow0, npass, s0, nst, s0, nst, sm, acc, sTiles);
+            else
+                stream_pass<FMT, GMB, 2, ring_quads<FMT, GMB, 2>(), 4>(J, tk.e, wblk, arow0, npass, s0, nst, sm, acc);
             smax[0] = sm[0];
             smax[1] = sm[1];
         } else {
             int sm[1];
-            stream_pass<FMT, GMB, 1, ring_quads<FMT, GMB, 1>(), 4>(J, tk.e, wblk, arow0, npass, s0, nst, sm,
-                                                                     acc);
+            if constexpr (FMT == kFmtNV)
+                stream_pass_lds<FMT, GMB, 1, 2>(J, tk.e, wblk, arow0, npass, s0, nst, s0, nst, sm, acc, sTiles);
+            else
+                stream_pass<FMT, GMB, 1, ring_quads<FMT, GMB, 1>(), 4>(J, tk.e, wblk, arow0, npass, s0, nst, sm, acc);
             smax[0] = sm[0];
         }
         if constexpr (FUSED) {
