@@ -9,6 +9,7 @@
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "quant_dev.h"
+#include "route_dev.h"
 
 #include <algorithm>
 
@@ -53,10 +54,16 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
                                                          const float* __restrict__ w_router,
                                                          int M, int H, int E, int splits,
                                                          int kchunk, int units, int nmain,
-                                                         float* __restrict__ partials, Bf16Side side,
-                                                         int stage) {
-    if ((int)blockIdx.x >= nmain) {  // a bf16 shared-expert stage riding along
-        bf16_side_block(side, stage, blockIdx.x - nmain);
+                                                         float* __restrict__ partials, int nquant,
+                                                         uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
+                                                         Bf16Side side, int stage) {
+    if ((int)blockIdx.x >= nmain + nquant) {  // a bf16 shared-expert stage riding along
+        bf16_side_block(side, stage, blockIdx.x - nmain - nquant);
+        return;
+    }
+    if ((int)blockIdx.x >= nmain) {  // MXFP8 of x in token order: 256 blocks of 32 values
+        const int b = (blockIdx.x - nmain) * 256 + threadIdx.x;
+        if (b < M * (H / 32)) quant_block32(x + (size_t)b * 32, xq + (size_t)b * 32, xs + b);
         return;
     }
     const int wave = threadIdx.x >> 6;
@@ -145,22 +152,23 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
 }
 
 hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int M, int H, int E,
-                                  const RouterPlan& plan, float* partials, const Bf16Side& side1, int stage1,
-                                  hipStream_t stream) {
+                                  const RouterPlan& plan, float* partials, uint8_t* xq, uint8_t* xs,
+                                  const Bf16Side& side1, int stage1, hipStream_t stream) {
     const int units = ((E + 15) / 16) * plan.splits * plan.row_groups;
     const int blocks = (units + 3) / 4;
+    const int nquant = xq ? (M * (H / 32) + 255) / 256 : 0;
     const int extra = stage1 == kBf16None ? 0 : side1.blocks;
-    const dim3 g(blocks + extra), b(256);
+    const dim3 g(blocks + nquant + extra), b(256);
     const bool wide = plan.kchunk % 256 == 0, one = M <= 16;  // (four row blocks keep U = 4: registers)
     if (wide && one)
         hipLaunchKernelGGL((k_router_partials<8, 1>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
-                           units, blocks, partials, side1, stage1);
+                           units, blocks, partials, nquant, xq, xs, side1, stage1);
     else if (one)
         hipLaunchKernelGGL((k_router_partials<4, 1>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
-                           units, blocks, partials, side1, stage1);
+                           units, blocks, partials, nquant, xq, xs, side1, stage1);
     else
         hipLaunchKernelGGL((k_router_partials<4, 4>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
-                           units, blocks, partials, side1, stage1);
+                           units, blocks, partials, nquant, xq, xs, side1, stage1);
     return hipGetLastError();
 }
 
@@ -169,33 +177,6 @@ hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int 
 // sigmoids of the fp32 logits; keys add the optional selection bias; the
 // order is key descending, then expert ascending.
 
-
-constexpr int kMaxE = 1024;
-constexpr int kMaxK = 32;
-constexpr int kBucketThreads = 256;
-
-// Exclusive scan over kMaxE entries held 4 per thread (256 threads).
-__device__ void block_exclusive_scan(int* data, int* scratch, int& total) {
-    const int tid = threadIdx.x;
-    int v0 = data[4 * tid], v1 = data[4 * tid + 1], v2 = data[4 * tid + 2], v3 = data[4 * tid + 3];
-    int sum = v0 + v1 + v2 + v3;
-    scratch[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < kBucketThreads; off <<= 1) {
-        int add = tid >= off ? scratch[tid - off] : 0;
-        __syncthreads();
-        scratch[tid] += add;
-        __syncthreads();
-    }
-    const int incl = scratch[tid];
-    total = scratch[kBucketThreads - 1];
-    int base = incl - sum;
-    data[4 * tid] = base;
-    data[4 * tid + 1] = base + v0;
-    data[4 * tid + 2] = base + v0 + v1;
-    data[4 * tid + 3] = base + v0 + v1 + v2;
-    __syncthreads();
-}
 
 // fp64 key -> unsigned integer with the same order (+0 and -0 equal).
 __device__ __forceinline__ uint64_t ordered_key(double v) {
@@ -349,96 +330,14 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials
     }
 }
 
-// ---------------------------------------------------------------------------
-// Route step: one workgroup builds the expert buckets, 8-row tiles and the
-// active-expert list from topk_ids (in a launch after the top-k one, so the
-// ids written by the top-k workgroups are visible without a device-scope
-// fence).
-__device__ void bucket_step(int M, int E, int k, const moe_routing& route) {
-    const int tid = threadIdx.x;
-
-    __shared__ int s_cnt[kMaxE], s_off[kMaxE], s_tile[kMaxE], s_act[kMaxE], s_run[kMaxE];
-    __shared__ uint32_t s_bm[kMaxE * 4];
-    __shared__ int s_scan[kBucketThreads];
-    const int P = M * k;
-    for (int e = tid; e < kMaxE; e += kBucketThreads) {
-        s_cnt[e] = 0;
-        s_run[e] = 0;
-    }
-    __syncthreads();
-    for (int p = tid; p < P; p += kBucketThreads) atomicAdd(&s_cnt[route.topk_ids[p]], 1);
-    __syncthreads();
-    for (int e = tid; e < kMaxE; e += kBucketThreads) {
-        const int c = s_cnt[e];
-        s_off[e] = c;
-        s_tile[e] = (c + 7) / 8;
-        s_act[e] = c > 0 ? 1 : 0;
-    }
-    __syncthreads();
-    int tot_pairs, tot_tiles, tot_act;
-    block_exclusive_scan(s_off, s_scan, tot_pairs);
-    block_exclusive_scan(s_tile, s_scan, tot_tiles);
-    block_exclusive_scan(s_act, s_scan, tot_act);
-    for (int e = tid; e < E; e += kBucketThreads) {
-        const int c = s_cnt[e];
-        route.expert_offsets[e] = s_off[e];
-        if (c > 0) {
-            route.active_experts[s_act[e]] = e;
-            route.active_offsets[s_act[e]] = s_off[e];
-        }
-        for (int t = 0; 8 * t < c; ++t) {
-            const int ti = s_tile[e] + t;
-            route.tile_expert[ti] = e;
-            route.tile_begin[ti] = s_off[e] + 8 * t;
-            route.tile_rows[ti] = min(8, c - 8 * t);
-        }
-    }
-    if (tid == 0) {
-        route.expert_offsets[E] = P;
-        *route.num_tiles = tot_tiles;
-        *route.num_active = tot_act;
-    }
-    for (int sl = tot_act + tid; sl <= min(E, P); sl += kBucketThreads) route.active_offsets[sl] = P;
-    // Stable placement: chunks of R rows; a bitmap per expert marks the chunk's
-    // rows that chose it, and a pair's rank within its expert is the number of
-    // earlier rows (previous chunks + lower bits of this chunk's bitmap).
-    const int R = min(128, kBucketThreads / k);
-    const int W = (R + 31) / 32;
-    for (int r0 = 0; r0 < M; r0 += R) {
-        for (int w = tid; w < E * W; w += kBucketThreads) s_bm[w] = 0u;
-        __syncthreads();
-        const int p = r0 * k + tid;
-        const bool valid = tid < R * k && p < P;
-        int e = 0, rl = 0;
-        if (valid) {
-            e = route.topk_ids[p];
-            rl = p / k - r0;
-            atomicOr(&s_bm[e * W + (rl >> 5)], 1u << (rl & 31));
-        }
-        __syncthreads();
-        if (valid) {
-            int rank = 0;
-            for (int w = 0; w < (rl >> 5); ++w) rank += __popc(s_bm[e * W + w]);
-            rank += __popc(s_bm[e * W + (rl >> 5)] & ((1u << (rl & 31)) - 1u));
-            route.bucket[s_off[e] + s_run[e] + rank] = p;
-        }
-        __syncthreads();
-        for (int ee = tid; ee < E; ee += kBucketThreads) {
-            int c = 0;
-            for (int w = 0; w < W; ++w) c += __popc(s_bm[ee * W + w]);
-            s_run[ee] += c;
-        }
-        __syncthreads();
-    }
-}
-
 __global__ __launch_bounds__(kBucketThreads) void k_bucket(int M, int E, int k, moe_routing route, Bf16Side side,
                                                           int stage) {
     if (blockIdx.x > 0) {  // a bf16 shared-expert stage riding along
         bf16_side_block(side, stage, blockIdx.x - 1);
         return;
     }
-    bucket_step(M, E, k, route);
+    __shared__ __align__(16) uint8_t s_lds[kBucketLdsMax];
+    bucket_step(M, E, k, route, s_lds);
 }
 
 // Route step and the activation quant in one launch, for P = M*k <= 256 pairs.
@@ -454,7 +353,8 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket_quant(int M, int E, i
                                                                 uint8_t* __restrict__ sp, uint8_t* __restrict__ qt,
                                                                 uint8_t* __restrict__ st, Bf16Side side, int stage) {
     if (blockIdx.x == 0) {
-        bucket_step(M, E, k, route);
+        __shared__ __align__(16) uint8_t s_lds[kBucketLdsMax];
+        bucket_step(M, E, k, route, s_lds);
         return;
     }
     if ((int)blockIdx.x > nq) {

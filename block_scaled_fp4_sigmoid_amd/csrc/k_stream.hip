@@ -43,8 +43,10 @@
 // operands of a (16-row block, step) is contiguous in lane order, and one
 // dword (MX) or two (NV) per lane carry the weight scales of 4 steps (the
 // MFMA's op_sel picks an MX scale byte), so each load instruction is dense.
+#include "dense_bf16_dev.h"
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "route_dev.h"
 
 #include <algorithm>
 
@@ -73,6 +75,12 @@ constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every record count
 #ifndef MOE_MIN_BLOCKS
 #define MOE_MIN_BLOCKS 2  // workgroups per CU the register budget must allow
 #endif
+#ifndef MOE_NV_DQ
+#define MOE_NV_DQ 2  // NVFP4 gate_up: weight ring depth in quads
+#endif
+#ifndef MOE_NV_MINB
+#define MOE_NV_MINB MOE_MIN_BLOCKS  // NVFP4 gate_up: workgroups per CU the register budget must allow
+#endif
 #ifndef MOE_WEIGHT_AUX
 #define MOE_WEIGHT_AUX 2  // cache policy of the weight loads: non-temporal (streamed once)
 #endif
@@ -94,6 +102,9 @@ struct StreamJob {
     int splits;
     int nblk;               // row blocks per expert
     int out_rows;           // rows of the partial buffer (gate_up split)
+    const int32_t* ids;     // routed, M*k <= kThreads pairs: slots resolve from the top-k ids
+    int k;                  // top-k (pair id = row * k + slot)
+    int a_tok;              // activations in token order: pair p reads row p / k
 };
 
 struct Tokens {
@@ -117,6 +128,70 @@ __device__ __forceinline__ bool resolve(const StreamJob& J, int slot, Tokens& t)
     t.base = b0;
     t.n = b1 - b0;
     return true;
+}
+
+// Slot -> (expert, bucket range) from the top-k ids, for P = M*k <= kThreads
+// pairs: the slot-th chosen expert in ascending id order, its bucket base
+// (the pairs with a smaller expert) and its pairs in ascending order (list,
+// LDS; tok[t] = list[t] / k), the order the route step writes.  One bitmap of
+// the chosen experts in LDS, a scan of its word counts in one wave, and one
+// ballot per wave for the pairs below and at the expert.  Every thread of the
+// workgroup calls it (it has barriers); the result is uniform.
+static_assert(kSmallPairs == kThreads, "one thread per pair resolves a slot");
+__device__ __forceinline__ bool resolve_ids(const StreamJob& J, int slot, Tokens& t, int* list, int* tok) {
+    __shared__ uint32_t s_bm[kMaxE / 32];
+    __shared__ int s_cnt[kThreads / 64][2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int P = J.M * J.k;
+    const int id = tid < P ? J.ids[tid] : -1;
+    if (tid < kMaxE / 32) s_bm[tid] = 0u;
+    __syncthreads();
+    if (id >= 0) atomicOr(&s_bm[id >> 5], 1u << (id & 31));
+    __syncthreads();
+    const uint32_t word = lane < kMaxE / 32 ? s_bm[lane] : 0u;
+    int incl = __popc(word);  // inclusive count of chosen experts up to this word
+#pragma unroll
+    for (int off = 1; off < kMaxE / 32; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, kMaxE / 32 - 1, 64));
+    if (slot >= total) return false;
+    const uint64_t over = __ballot(lane < kMaxE / 32 && incl > slot);
+    const int w = __ffsll((unsigned long long)over) - 1;  // word holding the expert
+    const int before = __shfl(incl - __popc(word), w, 64);
+    uint32_t bits = (uint32_t)__shfl((int)word, w, 64);
+    for (int r = slot - before; r > 0; --r) bits &= bits - 1u;
+    const int e = 32 * w + __ffs(bits) - 1;
+    const uint64_t lt = __ballot(id >= 0 && id < e), eq = __ballot(id == e);
+    if (lane == 0) {
+        s_cnt[wave][0] = __popcll(lt);
+        s_cnt[wave][1] = __popcll(eq);
+    }
+    __syncthreads();
+    int base = 0, n = 0, pre = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kThreads / 64; ++w2) {
+        base += s_cnt[w2][0];
+        pre += w2 < wave ? s_cnt[w2][1] : 0;
+        n += s_cnt[w2][1];
+    }
+    if (id == e) {
+        const int pos = pre + __popcll(eq & ((1ull << lane) - 1ull));
+        list[pos] = tid;
+        tok[pos] = tid / J.k;
+    }
+    __syncthreads();
+    // uniform, but computed through lane exchanges: say so, or every buffer
+    // load through the expert's resource becomes a readfirstlane loop
+    t.e = __builtin_amdgcn_readfirstlane(e);
+    t.base = __builtin_amdgcn_readfirstlane(base);
+    t.n = __builtin_amdgcn_readfirstlane(n);
+    return true;
+}
+
+__device__ __forceinline__ bool resolve_item(const StreamJob& J, int slot, Tokens& t, int* list, int* tok) {
+    return (J.ids && !J.dense) ? resolve_ids(J, slot, t, list, tok) : resolve(J, slot, t);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
@@ -176,10 +251,11 @@ struct Coord {
     uint32_t vas[NB];  // activation scale dword of step 0 of the lane's row (kOOB past the pass)
 };
 
-// wblk: first row of each weight block (a multiple of 16).
+// wblk: first row of each weight block (a multiple of 16).  src: the a_q row
+// of each pass row (LDS), or nullptr for rows arow0, arow0 + 1, ...
 template <int FMT, int MB, int NB>
 __device__ __forceinline__ Coord<FMT, MB, NB> make_coord(const StreamJob& J, int e, const int (&wblk)[MB],
-                                                          int arow0, int npass) {
+                                                          int arow0, int npass, const int* src) {
     const int lane = threadIdx.x & 63;
     const int i = lane & 15, g = lane >> 4;
     const int K = J.K, S = K / 128, Q = (S + 3) / 4;
@@ -189,10 +265,14 @@ __device__ __forceinline__ Coord<FMT, MB, NB> make_coord(const StreamJob& J, int
     Coord<FMT, MB, NB> c;
     c.rw = make_rsrc(J.w + (size_t)e * wbytes, wbytes);
     c.rs = make_rsrc(J.sc + (size_t)e * sbytes, sbytes);
-    // activation resources cover the pass's rows only (offsets stay small)
-    const uint32_t prow = (uint32_t)min(kPassRows, (int)J.a_rows - arow0);
-    c.ra = make_rsrc(J.a_q + (size_t)arow0 * K, prow * (uint32_t)K);
-    c.ras = make_rsrc(J.a_s + (size_t)arow0 * (K / 32), prow * (uint32_t)(K / 32));
+    if (src) {  // gathered rows: the resources cover all of a_q
+        c.ra = make_rsrc(J.a_q, J.a_rows * (uint32_t)K);
+        c.ras = make_rsrc(J.a_s, J.a_rows * (uint32_t)(K / 32));
+    } else {  // the pass's rows only (offsets stay small)
+        const uint32_t prow = (uint32_t)min(kPassRows, (int)J.a_rows - arow0);
+        c.ra = make_rsrc(J.a_q + (size_t)arow0 * K, prow * (uint32_t)K);
+        c.ras = make_rsrc(J.a_s + (size_t)arow0 * (K / 32), prow * (uint32_t)(K / 32));
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         const uint32_t rb = (uint32_t)wblk[mb] / 16;
@@ -203,9 +283,10 @@ __device__ __forceinline__ Coord<FMT, MB, NB> make_coord(const StreamJob& J, int
     for (int j = 0; j < NB; ++j) {
         const int t = 16 * j + i;
         const bool ok = t < npass;
+        const uint32_t r = ok ? (src ? (uint32_t)src[t] : (uint32_t)t) : 0u;
         // MX: bytes [16g, +16) and [64 + 16g, +16) of the step; NV: [32g, +32)
-        c.va[j] = ok ? (uint32_t)t * K + (FMT == kFmtMX ? 16 : 32) * g : kOOB;
-        c.vas[j] = ok ? (uint32_t)t * (K / 32) : kOOB;
+        c.va[j] = ok ? r * K + (FMT == kFmtMX ? 16 : 32) * g : kOOB;
+        c.vas[j] = ok ? r * (K / 32) : kOOB;
     }
     return c;
 }
@@ -318,21 +399,59 @@ __device__ __forceinline__ void step_mfma(const Ring<MB, NB, DQ, QS>& R, int v, 
 
 // NVFP4: largest E8M0 code of the lane's activation row(s) over K steps
 // [s0, s0 + nst) (activations enter the f16 MFMA as E4M3 * 2^(s - smax),
-// inside f16 range); 0 for rows past the pass.  Issued before the ring, so
-// it returns first.
+// inside f16 range); 0 for rows past the pass.  Two phases: the loads are
+// issued before the operand ring is filled and reduced after it, so their
+// round trip overlaps the ring's instead of preceding it.  The four lanes of a
+// row (g = 0..3) load 16 bytes each per round: dwords 4(g + 4u) .. +3 of the
+// range (dword d = the scale bytes of step s0 + d), u < kSmaxU; a range longer
+// than 16 * kSmaxU dwords finishes with a loop.
+constexpr int kSmaxU = 4;
+
+template <int NB>
+struct SmaxRaw {
+    v4i v[NB][kSmaxU];
+};
+
 template <int FMT, int MB, int NB>
-__device__ __forceinline__ void row_smax(const Coord<FMT, MB, NB>& c, int s0, int nst, int (&smax)[NB]) {
+__device__ __forceinline__ void row_smax_issue(const Coord<FMT, MB, NB>& c, int s0, int nst, SmaxRaw<NB>& R) {
     const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-        // the row's scale dwords of the range (dword d = blocks 4(s0+d) .. +3);
-        // lane group g takes dwords g, g+4, ...
         const bool ok = c.vas[j] != kOOB;
-        const uint32_t base = ok ? c.vas[j] + 4 * s0 : kOOB;
+#pragma unroll
+        for (int u = 0; u < kSmaxU; ++u) {
+            const int d = 4 * (g + 4 * u);
+            R.v[j][u] = __builtin_amdgcn_raw_buffer_load_b128(
+                c.ras, ok && d < nst ? c.vas[j] + 4 * (s0 + d) : kOOB, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t max_byte(uint32_t v) {
+    return max(max(v & 0xffu, (v >> 8) & 0xffu), max((v >> 16) & 0xffu, v >> 24));
+}
+
+template <int FMT, int MB, int NB>
+__device__ __forceinline__ void row_smax_finish(const Coord<FMT, MB, NB>& c, int s0, int nst, const SmaxRaw<NB>& R,
+                                                int (&smax)[NB]) {
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
         uint32_t mx = 0;
-        for (int d = g; d < nst; d += 4) {
-            const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(c.ras, ok ? base + 4 * d : kOOB, 0, 0);
-            mx = max(mx, max(max(v & 0xffu, (v >> 8) & 0xffu), max((v >> 16) & 0xffu, v >> 24)));
+#pragma unroll
+        for (int u = 0; u < kSmaxU; ++u) {
+            const int d = 4 * (g + 4 * u);
+            const v4i v = R.v[j][u];
+            // dwords past the range are ignored (a range may end inside the load)
+            mx = max(mx, d + 0 < nst ? max_byte((uint32_t)v.x) : 0u);
+            mx = max(mx, d + 1 < nst ? max_byte((uint32_t)v.y) : 0u);
+            mx = max(mx, d + 2 < nst ? max_byte((uint32_t)v.z) : 0u);
+            mx = max(mx, d + 3 < nst ? max_byte((uint32_t)v.w) : 0u);
+        }
+        const bool ok = c.vas[j] != kOOB;
+        for (int d = 16 * kSmaxU + g; d < nst; d += 4) {
+            const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(c.ras, ok ? c.vas[j] + 4 * (s0 + d) : kOOB, 0, 0);
+            mx = max(mx, max_byte(v));
         }
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16, 64));
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
@@ -364,20 +483,10 @@ __device__ __forceinline__ void quad_steps(Ring<MB, NB, DQ, QS>& R, int v, const
 // operands.
 template <int FMT, int MB, int NB, int DQ, int QS>
 __device__ __forceinline__ void stream_pass(const StreamJob& J, int e, const int (&wblk)[MB], int arow0, int npass,
-                                            int s0, int nst, int (&smax)[NB], v4f (&acc)[MB][2]) {
-    const Coord<FMT, MB, NB> c = make_coord<FMT, MB, NB>(J, e, wblk, arow0, npass);
-    int sfo[NB];
-    if constexpr (FMT == kFmtNV) {
-        row_smax<FMT, MB, NB>(c, s0, nst, smax);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) sfo[j] = -smax[j];
-    } else {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            sfo[j] = 0;
-            smax[j] = 0;
-        }
-    }
+                                            const int* src, int s0, int nst, int (&smax)[NB], v4f (&acc)[MB][2]) {
+    const Coord<FMT, MB, NB> c = make_coord<FMT, MB, NB>(J, e, wblk, arow0, npass, src);
+    SmaxRaw<NB> SR;
+    if constexpr (FMT == kFmtNV) row_smax_issue<FMT, MB, NB>(c, s0, nst, SR);
     const int q0 = s0 / 4, nq = (nst + 3) / 4, s_end = s0 + nst;
     Ring<MB, NB, DQ, QS> R;
     // Fill the ring in the order the loop refills it (a quad's scales with its
@@ -392,6 +501,19 @@ __device__ __forceinline__ void stream_pass(const StreamJob& J, int e, const int
             __builtin_amdgcn_sched_barrier(0);
             if (u == QS - 1) ring_load_scales<FMT, MB, NB, DQ, QS>(R, v, c, q0 + v, s_end);
             ring_load_step<FMT, MB, NB, DQ, QS>(R, v, u, c, q0 + v, s_end);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int sfo[NB];
+    if constexpr (FMT == kFmtNV) {
+        row_smax_finish<FMT, MB, NB>(c, s0, nst, SR, smax);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) sfo[j] = -smax[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            sfo[j] = 0;
+            smax[j] = 0;
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -422,20 +544,42 @@ struct ActShare {
     v4i s;          // the scale bytes of row t (threads t < 16*NB)
 };
 
-// Requests the thread's share of tile q (absolute quad).  Rows past the pass
-// and steps at or past s_end read zeros.
+// The thread's share of a tile: byte offsets (in a_q, a_s) of its code
+// chunks and of its row's scale bytes at quad 0; kOOB for rows past the pass.
+// src as in make_coord.
 template <int NB>
-__device__ __forceinline__ void tile_load(ActShare<NB>& P, const Coord<kFmtMX, 1, NB>& c, int K, int npass, int q,
-                                          int s_end) {
+struct TileOffs {
+    uint32_t c[2 * NB];
+    uint32_t s;
+};
+
+template <int NB>
+__device__ __forceinline__ TileOffs<NB> tile_offsets(int K, int npass, const int* src) {
     const int t = threadIdx.x;
+    TileOffs<NB> o;
 #pragma unroll
     for (int k = 0; k < 2 * NB; ++k) {
         const int li = t + kThreads * k, row = li >> 5, ch = li & 31;
-        const bool ok = row < npass && 4 * q + (ch >> 3) < s_end;
-        P.c[k] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, ok ? (uint32_t)(row * K + 512 * q + 16 * ch) : kOOB, 0, 0);
+        o.c[k] = row < npass ? (src ? (uint32_t)src[row] : (uint32_t)row) * (uint32_t)K + 16 * ch : kOOB;
     }
-    const bool oks = t < 16 * NB && t < npass && 4 * q < s_end;
-    P.s = __builtin_amdgcn_raw_buffer_load_b128(c.ras, oks ? (uint32_t)(t * (K / 32) + 16 * q) : kOOB, 0, 0);
+    o.s = (t < 16 * NB && t < npass) ? (src ? (uint32_t)src[t] : (uint32_t)t) * (uint32_t)(K / 32) : kOOB;
+    return o;
+}
+
+// Requests the thread's share of tile q (absolute quad).  Rows past the pass
+// and steps at or past s_end read zeros.
+template <int NB>
+__device__ __forceinline__ void tile_load(ActShare<NB>& P, const Coord<kFmtMX, 1, NB>& c, const TileOffs<NB>& o,
+                                          int q, int s_end) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 2 * NB; ++k) {
+        const int ch = (t + kThreads * k) & 31;
+        const bool ok = o.c[k] != kOOB && 4 * q + (ch >> 3) < s_end;
+        P.c[k] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, ok ? o.c[k] + 512 * q : kOOB, 0, 0);
+    }
+    const bool oks = o.s != kOOB && 4 * q < s_end;
+    P.s = __builtin_amdgcn_raw_buffer_load_b128(c.ras, oks ? o.s + 16 * q : kOOB, 0, 0);
 }
 
 // Writes the thread's share of tile q into an LDS buffer; the scale dwords of
@@ -531,29 +675,20 @@ __device__ __forceinline__ void quadw_steps(RingW<MB, DQ>& R, int v, const Coord
 // same arguments apart from the weight blocks (it has barriers).
 template <int FMT, int MB, int NB, int DQ>
 __device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const int (&wblk)[MB], int arow0,
-                                                int npass, int s0, int nst, int ms0, int mnst, int (&smax)[NB],
-                                                v4f (&acc)[MB][2], uint8_t* tiles) {
+                                                int npass, const int* src, int s0, int nst, int ms0, int mnst,
+                                                int (&smax)[NB], v4f (&acc)[MB][2], uint8_t* tiles) {
     static_assert(DQ % 2 == 0, "slots alternate between the two tile buffers");
-    const Coord<FMT, MB, NB> c = make_coord<FMT, MB, NB>(J, e, wblk, arow0, npass);
+    const Coord<FMT, MB, NB> c = make_coord<FMT, MB, NB>(J, e, wblk, arow0, npass, src);
+    const TileOffs<NB> to = tile_offsets<NB>(J.K, npass, src);
     Coord<kFmtMX, 1, NB> ca;  // the activation resources, for the tile loads
     ca.ra = c.ra;
     ca.ras = c.ras;
-    int sfo[NB];
-    if constexpr (FMT == kFmtNV) {
-        row_smax<FMT, MB, NB>(c, ms0, mnst, smax);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) sfo[j] = -smax[j];
-    } else {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            sfo[j] = 0;
-            smax[j] = 0;
-        }
-    }
-    const int K = J.K;
+    SmaxRaw<NB> SR;
+    if constexpr (FMT == kFmtNV) row_smax_issue<FMT, MB, NB>(c, ms0, mnst, SR);
+    __builtin_amdgcn_sched_barrier(0);
     const int q0 = s0 / 4, nq = (nst + 3) / 4, s_end = s0 + nst;
     ActShare<NB> P;
-    tile_load<NB>(P, ca, K, npass, q0, s_end);
+    tile_load<NB>(P, ca, to, q0, s_end);
     RingW<MB, DQ> R;
 #pragma unroll
     for (int v = 0; v < DQ; ++v) {
@@ -562,6 +697,19 @@ __device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const
             __builtin_amdgcn_sched_barrier(0);
             if (u == 3) ringw_load_scales<FMT, MB, NB, DQ>(R, v, c, q0 + v, s_end);
             ringw_load_step<FMT, MB, NB, DQ>(R, v, u, c, q0 + v, s_end);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int sfo[NB];
+    if constexpr (FMT == kFmtNV) {
+        row_smax_finish<FMT, MB, NB>(c, ms0, mnst, SR, smax);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) sfo[j] = -smax[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            sfo[j] = 0;
+            smax[j] = 0;
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -579,7 +727,7 @@ __device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const
             v4i b[NB][2];
             uint32_t bs[NB];
             tile_read<FMT, NB>(tile, 0, b, bs);
-            tile_load<NB>(P, ca, K, npass, q + 1, s_end);  // in flight over the quad's steps
+            tile_load<NB>(P, ca, to, q + 1, s_end);  // in flight over the quad's steps
             quadw_steps<FMT, MB, NB, DQ, 0>(R, v, c, q + DQ, s_end, tile, b, bs, sfo, acc);
             // tile q+1 into the other buffer (its reads ended at the last barrier)
             tile_store<NB>(P, tiles + ((v + 1) & 1) * kTileBytes, q + 1, s_end);
@@ -642,15 +790,20 @@ constexpr int GMB = 2;           // 16-row weight blocks per wave in gate_up
 constexpr int GCOLS = 32 * GMB;  // output columns per workgroup
 
 template <int FMT, bool FUSED>
-__global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_gate_up(StreamJob J, uint8_t* __restrict__ h_q,
-                                                                      uint8_t* __restrict__ h_s,
-                                                                      float* __restrict__ part) {
+__global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLOCKS) void k_gate_up(
+    StreamJob J, uint8_t* __restrict__ h_q, uint8_t* __restrict__ h_s, float* __restrict__ part, int nmain,
+    Bf16Side side, int stage) {
+    if ((int)blockIdx.x >= nmain) {  // a bf16 shared-expert stage riding along
+        bf16_side_block(side, stage, blockIdx.x - nmain);
+        return;
+    }
     const int I = J.N / 2, K = J.K;
     const int ks = blockIdx.x % J.splits;
     const int blk = (blockIdx.x / J.splits) % J.nblk;
     const int slot = blockIdx.x / (J.splits * J.nblk);
     Tokens tk;
-    if (!resolve(J, slot, tk)) return;
+    __shared__ int s_list[kThreads], s_tok[kThreads];
+    if (!resolve_item(J, slot, tk, s_list, s_tok)) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int i = lane & 15, g = lane >> 4;
     const int half = (wave & 1) * (16 * GMB);  // column offset of the wave within the item
@@ -669,22 +822,27 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_gate_up(StreamJob 
     for (int t0 = 0; t0 < tk.n; t0 += kPassRows) {
         const int npass = min(kPassRows, tk.n - t0);
         const int arow0 = tk.base + t0;
+        const int* src = J.a_tok ? s_tok + t0 : nullptr;  // token-ordered activations: gather the rows
         v4f acc[GMB][2];
         int smax[2] = {0, 0};
         if (npass > 16) {
             int sm[2];
             if constexpr (FMT == kFmtNV)
-                stream_pass_lds<FMT, GMB, 2, 2>(J, tk.e, wblk, arow0, npass, s0, nst, s0, nst, sm, acc, sTiles);
+                stream_pass_lds<FMT, GMB, 2, MOE_NV_DQ>(J, tk.e, wblk, arow0, npass, src, s0, nst, s0, nst, sm, acc,
+                                                        sTiles);
             else
-                stream_pass<FMT, GMB, 2, ring_quads<FMT, GMB, 2>(), 4>(J, tk.e, wblk, arow0, npass, s0, nst, sm, acc);
+                stream_pass<FMT, GMB, 2, ring_quads<FMT, GMB, 2>(), 4>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm,
+                                                                         acc);
             smax[0] = sm[0];
             smax[1] = sm[1];
         } else {
             int sm[1];
             if constexpr (FMT == kFmtNV)
-                stream_pass_lds<FMT, GMB, 1, 2>(J, tk.e, wblk, arow0, npass, s0, nst, s0, nst, sm, acc, sTiles);
+                stream_pass_lds<FMT, GMB, 1, MOE_NV_DQ>(J, tk.e, wblk, arow0, npass, src, s0, nst, s0, nst, sm, acc,
+                                                        sTiles);
             else
-                stream_pass<FMT, GMB, 1, ring_quads<FMT, GMB, 1>(), 4>(J, tk.e, wblk, arow0, npass, s0, nst, sm, acc);
+                stream_pass<FMT, GMB, 1, ring_quads<FMT, GMB, 1>(), 4>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm,
+                                                                         acc);
             smax[0] = sm[0];
         }
         if constexpr (FUSED) {
@@ -783,13 +941,20 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_quant(const float* __restri
 constexpr int kDownMB = 2;  // 16-row weight blocks per wave in down along K
 
 template <int FMT, int MB>
-__global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J, float* __restrict__ y) {
+__global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J, float* __restrict__ y, int nmain,
+                                                                   moe_routing ride, int ride_E) {
+    if ((int)blockIdx.x >= nmain) {  // the route step riding along (it writes only the routing arrays)
+        extern __shared__ __align__(16) uint8_t s_dyn[];
+        bucket_step(J.M, ride_E, J.k, ride, s_dyn);
+        return;
+    }
     const int H = J.N, I = J.K;
     constexpr int RB = 64 * MB;
     const int blk = blockIdx.x % J.nblk;
     const int slot = blockIdx.x / J.nblk;
     Tokens tk;
-    if (!resolve(J, slot, tk)) return;
+    __shared__ int s_list[kThreads], s_tok[kThreads];
+    if (!resolve_item(J, slot, tk, s_list, s_tok)) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int i = lane & 15, g = lane >> 4;
     const int f0 = blk * RB + wave * (16 * MB);
@@ -808,19 +973,19 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J, 
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int t = 16 * j + i;
-            orow[j] = t < npass ? (J.dense ? arow0 + t : J.bucket[arow0 + t]) : 0;
+            orow[j] = t < npass ? (J.dense ? arow0 + t : J.ids ? s_list[t0 + t] : J.bucket[arow0 + t]) : 0;
         }
         v4f acc[MB][2];
         int smax[2] = {0, 0};
         if (npass > 16) {
             int sm[2];
-            stream_pass<FMT, MB, 2, ring_quads<FMT, MB, 2>(), 4>(J, tk.e, wblk, arow0, npass, 0,
+            stream_pass<FMT, MB, 2, ring_quads<FMT, MB, 2>(), 4>(J, tk.e, wblk, arow0, npass, nullptr, 0,
                                                                                  nst, sm, acc);
             smax[0] = sm[0];
             smax[1] = sm[1];
         } else {
             int sm[1];
-            stream_pass<FMT, MB, 1, ring_quads<FMT, MB, 1>(), 4>(J, tk.e, wblk, arow0, npass, 0,
+            stream_pass<FMT, MB, 1, ring_quads<FMT, MB, 1>(), 4>(J, tk.e, wblk, arow0, npass, nullptr, 0,
                                                                                  nst, sm, acc);
             smax[0] = sm[0];
         }
@@ -879,13 +1044,20 @@ __device__ __forceinline__ void rows_steps(v4f& acc, const v4i (&wa)[D][S], cons
 // 4 * bpw blocks); wave w takes blocks [w * bpw, (w + 1) * bpw) of the run.
 // Passes of 16 activation rows; a later pass reads the item's weights again.
 template <int FMT, int S, int D>
-__global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down_rows(StreamJob J, float* __restrict__ y) {
+__global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down_rows(StreamJob J, float* __restrict__ y,
+                                                                        int nmain, moe_routing ride, int ride_E) {
+    if ((int)blockIdx.x >= nmain) {  // the route step riding along (it writes only the routing arrays)
+        extern __shared__ __align__(16) uint8_t s_dyn[];
+        bucket_step(J.M, ride_E, J.k, ride, s_dyn);
+        return;
+    }
     const int H = J.N, K = J.K;
     const int bpw = J.span;
     const int item = blockIdx.x % J.nblk;
     const int slot = blockIdx.x / J.nblk;
     Tokens tk;
-    if (!resolve(J, slot, tk)) return;
+    __shared__ int s_list[kThreads], s_tok[kThreads];
+    if (!resolve_item(J, slot, tk, s_list, s_tok)) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int i = lane & 15, g = lane >> 4;
     const int nbr = H / 16;
@@ -902,7 +1074,7 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down_rows(StreamJo
         const int npass = min(16, tk.n - t0);
         const int arow0 = tk.base + t0;
         const bool okr = i < npass;
-        const int orow = okr ? (J.dense ? arow0 + i : J.bucket[arow0 + i]) : 0;
+        const int orow = okr ? (J.dense ? arow0 + i : J.ids ? s_list[t0 + i] : J.bucket[arow0 + i]) : 0;
         // the lane's activation row (column i of the MFMAs), all S steps
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(J.a_q + (size_t)arow0 * K, (uint32_t)npass * (uint32_t)K);
         const __amdgpu_buffer_rsrc_t ras = make_rsrc(J.a_s + (size_t)arow0 * (K / 32), (uint32_t)npass * (uint32_t)(K / 32));
@@ -1022,6 +1194,10 @@ StreamJob stream_job(const ExpertJob& j, int N, const uint8_t* a_q, const uint8_
     s.splits = 1;
     s.nblk = 1;
     s.out_rows = a_rows;
+    s.ids = j.dense ? nullptr : j.ids;
+    s.k = j.k;
+    s.a_tok = (!j.dense && j.ids && j.a_tok) ? 1 : 0;
+    if (s.a_tok) s.a_rows = (uint32_t)j.M;
     return s;
 }
 
@@ -1036,7 +1212,7 @@ size_t gate_up_fp4_partials_bytes(const ExpertJob& job) {
 }
 
 hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const uint8_t* a_s, uint8_t* h_q,
-                              uint8_t* h_s, float* partials, hipStream_t stream) {
+                              uint8_t* h_s, float* partials, hipStream_t stream, const Bf16Side& side, int stage) {
     const GatePlan p = gate_plan(job);
     const int rows = out_rows_of(job);
     StreamJob J = stream_job(job, 2 * job.N_out, a_q, a_s, rows);
@@ -1044,22 +1220,20 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
     J.splits = p.splits;
     J.nblk = p.nblk;
     const int blocks = grid_slots(job) * p.nblk * p.splits;
+    const int extra = stage == kBf16None ? 0 : side.blocks;
+    const dim3 g(blocks + extra), b(kThreads);
     const bool mx = job.w.fmt == MOE_FMT_MXFP4;
     if (p.splits == 1) {
         if (mx)
-            hipLaunchKernelGGL((k_gate_up<kFmtMX, true>), dim3(blocks), dim3(kThreads), 0, stream, J, h_q, h_s,
-                               partials);
+            hipLaunchKernelGGL((k_gate_up<kFmtMX, true>), g, b, 0, stream, J, h_q, h_s, partials, blocks, side, stage);
         else
-            hipLaunchKernelGGL((k_gate_up<kFmtNV, true>), dim3(blocks), dim3(kThreads), 0, stream, J, h_q, h_s,
-                               partials);
+            hipLaunchKernelGGL((k_gate_up<kFmtNV, true>), g, b, 0, stream, J, h_q, h_s, partials, blocks, side, stage);
         return hipGetLastError();
     }
     if (mx)
-        hipLaunchKernelGGL((k_gate_up<kFmtMX, false>), dim3(blocks), dim3(kThreads), 0, stream, J, h_q, h_s,
-                           partials);
+        hipLaunchKernelGGL((k_gate_up<kFmtMX, false>), g, b, 0, stream, J, h_q, h_s, partials, blocks, side, stage);
     else
-        hipLaunchKernelGGL((k_gate_up<kFmtNV, false>), dim3(blocks), dim3(kThreads), 0, stream, J, h_q, h_s,
-                           partials);
+        hipLaunchKernelGGL((k_gate_up<kFmtNV, false>), g, b, 0, stream, J, h_q, h_s, partials, blocks, side, stage);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int threads = rows * (job.N_out / 32) * 8;
@@ -1070,8 +1244,27 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
 
 // Down by rows (K of at most one quad): blocks per wave and items per slot so
 // that about two workgroups per CU stream runs of equal length.
+// The route step rides along as one extra workgroup when ride != nullptr.
+struct DownRide {
+    moe_routing route;
+    int E;
+    int blocks;     // 0 or 1
+    size_t lds;     // dynamic LDS bytes of the launch
+};
+
+DownRide down_ride(const moe_routing* ride, int E, int k) {
+    DownRide d{};
+    if (ride) {
+        d.route = *ride;
+        d.E = E;
+        d.blocks = 1;
+        d.lds = bucket_lds_bytes(E, k);
+    }
+    return d;
+}
+
 template <int FMT, int S>
-hipError_t launch_down_rows_s(StreamJob J, int slots, float* y, hipStream_t stream) {
+hipError_t launch_down_rows_s(StreamJob J, int slots, float* y, const DownRide& dr, hipStream_t stream) {
     constexpr int D = 4;  // blocks in flight per wave (deeper rings measured slower)
     const int nbr = J.N / 16;
     int items = std::max(1, std::min(MOE_ROWS_TARGET_WGS / std::max(1, slots), nbr / (4 * D)));
@@ -1082,32 +1275,36 @@ hipError_t launch_down_rows_s(StreamJob J, int slots, float* y, hipStream_t stre
     items = (nbr + 4 * bpw - 1) / (4 * bpw);
     J.span = bpw;
     J.nblk = items;
-    hipLaunchKernelGGL((k_down_rows<FMT, S, D>), dim3(slots * items), dim3(kThreads), 0, stream, J, y);
+    const int nmain = slots * items;
+    hipLaunchKernelGGL((k_down_rows<FMT, S, D>), dim3(nmain + dr.blocks), dim3(kThreads), dr.lds, stream, J, y, nmain,
+                       dr.route, dr.E);
     return hipGetLastError();
 }
 
 template <int FMT>
-hipError_t launch_down_rows(const StreamJob& J, int slots, float* y, hipStream_t stream) {
+hipError_t launch_down_rows(const StreamJob& J, int slots, float* y, const DownRide& dr, hipStream_t stream) {
     switch (J.K / 128) {
-        case 1: return launch_down_rows_s<FMT, 1>(J, slots, y, stream);
-        case 2: return launch_down_rows_s<FMT, 2>(J, slots, y, stream);
-        case 3: return launch_down_rows_s<FMT, 3>(J, slots, y, stream);
-        default: return launch_down_rows_s<FMT, 4>(J, slots, y, stream);
+        case 1: return launch_down_rows_s<FMT, 1>(J, slots, y, dr, stream);
+        case 2: return launch_down_rows_s<FMT, 2>(J, slots, y, dr, stream);
+        case 3: return launch_down_rows_s<FMT, 3>(J, slots, y, dr, stream);
+        default: return launch_down_rows_s<FMT, 4>(J, slots, y, dr, stream);
     }
 }
 
 hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8_t* h_s, float* y,
-                           hipStream_t stream) {
+                           hipStream_t stream, const moe_routing* ride_route, int E) {
     StreamJob J = stream_job(job, job.N_out, h_q, h_s, out_rows_of(job));
+    const DownRide dr = down_ride(ride_route, E, job.k);
     if (job.K <= 512)  // all of K in one quad: stream along the rows
-        return job.w.fmt == MOE_FMT_MXFP4 ? launch_down_rows<kFmtMX>(J, grid_slots(job), y, stream)
-                                          : launch_down_rows<kFmtNV>(J, grid_slots(job), y, stream);
+        return job.w.fmt == MOE_FMT_MXFP4 ? launch_down_rows<kFmtMX>(J, grid_slots(job), y, dr, stream)
+                                          : launch_down_rows<kFmtNV>(J, grid_slots(job), y, dr, stream);
     J.nblk = job.N_out / (64 * kDownMB);
-    const dim3 g(grid_slots(job) * J.nblk), b(kThreads);
+    const int nmain = grid_slots(job) * J.nblk;
+    const dim3 g(nmain + dr.blocks), b(kThreads);
     if (job.w.fmt == MOE_FMT_MXFP4)
-        hipLaunchKernelGGL((k_down<kFmtMX, kDownMB>), g, b, 0, stream, J, y);
+        hipLaunchKernelGGL((k_down<kFmtMX, kDownMB>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E);
     else
-        hipLaunchKernelGGL((k_down<kFmtNV, kDownMB>), g, b, 0, stream, J, y);
+        hipLaunchKernelGGL((k_down<kFmtNV, kDownMB>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E);
     return hipGetLastError();
 }
 

@@ -172,7 +172,8 @@ int moe_route_topk(const uint16_t* x, const float* logits_in, const float* w_rou
     hipError_t e;
     if (x) {
         const RouterPlan p = router_plan(M, H, E);
-        e = launch_router_partials(x, w_router, M, H, E, p, w.partials, no_side(), kBf16None, stream);
+        e = launch_router_partials(x, w_router, M, H, E, p, w.partials, nullptr, nullptr, no_side(), kBf16None,
+                                   stream);
         if (e == hipSuccess)
             e = launch_topk_bucket(w.partials, p.splits, bias, M, E, k, routed_scale, logits_out, *route, no_side(),
                                    kBf16None, no_side(), kBf16None, stream);
@@ -322,10 +323,13 @@ LayerWs carve_layer(Carver& c, const moe_layer_desc* d) {
     L.active = c.take<int32_t>(std::min(E, P));
     L.num_active = c.take<int32_t>(1);
     L.act_off = c.take<int32_t>(std::min(E, P) + 1);
-    L.xq = c.take<uint8_t>((size_t)P * H);       // bucket order
-    L.xs = c.take<uint8_t>((size_t)P * H / 32);
-    L.xqt = L.xst = nullptr;
-    if (sh && !shb) {                            // token order for the FP4 shared expert
+    const bool small = P <= kSmallPairs;         // gate_up gathers token-order rows
+    L.xq = L.xs = L.xqt = L.xst = nullptr;
+    if (!small) {                                // bucket order
+        L.xq = c.take<uint8_t>((size_t)P * H);
+        L.xs = c.take<uint8_t>((size_t)P * H / 32);
+    }
+    if (small || (sh && !shb)) {                 // token order (and for the FP4 shared expert)
         L.xqt = c.take<uint8_t>((size_t)M * H);
         L.xst = c.take<uint8_t>((size_t)M * H / 32);
     }
@@ -402,29 +406,47 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
                                         kBf16Down)
                             : no_side();
     const RouterPlan p = router_plan(M, H, E);
-    hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, s1,
-                                          shb ? kBf16GateUp : kBf16None, stream);
-    if (M * k <= kSmallPairs) {  // route step and activation quant share a launch
+    const bool fp4_shared = sf != MOE_FMT_NONE && !shb;
+    if (M * k <= kSmallPairs) {
+        // Five launches: (router + token-order MXFP8 of x) -> top-k -> gate_up
+        // (workgroups resolve their expert from the ids and gather token rows)
+        // -> down (the route step rides along) -> finalize.  The bf16 shared
+        // expert's stages ride along the first three.
+        hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, L.xqt, L.xst, s1,
+                                              shb ? kBf16GateUp : kBf16None, stream);
         if (e == hipSuccess)
             e = launch_topk(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale, logits_out, r, s2,
                             shb ? kBf16Swiglu : kBf16None, stream);
+        ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
+        gu.ids = r.topk_ids;
+        gu.a_tok = true;
         if (e == hipSuccess)
-            e = launch_bucket_quant(M, E, k, r, x, H, L.xq, L.xs, L.xqt, L.xst, s3, shb ? kBf16Down : kBf16None,
-                                    stream);
-    } else {
+            e = launch_gate_up_fp4(gu, L.xqt, L.xst, L.hq, L.hs, L.part, stream, s3, shb ? kBf16Down : kBf16None);
+        if (e == hipSuccess && fp4_shared)
+            e = launch_gate_up_fp4(dense_job(d->sh13, Ish, H, M), L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart, stream);
+        ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);
+        dn.ids = r.topk_ids;
+        if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream, &r, E);
+        if (e == hipSuccess && fp4_shared)
+            e = launch_down_fp4(dense_job(d->sh2, H, Ish, M), L.hsq, L.hss, L.ysh, stream);
         if (e == hipSuccess)
-            e = launch_topk_bucket(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale,
-                                   logits_out, r, s2, shb ? kBf16Swiglu : kBf16None, s3,
-                                   shb ? kBf16Down : kBf16None, stream);
-        if (e == hipSuccess) e = launch_quant_pairs(x, r.bucket, k, M, H, L.xq, L.xs, L.xqt, L.xst, stream);
+            e = launch_finalize(L.y, r.topk_w, L.ysh, residual, d->gamma, d->eps, M, H, k, out, residual_out,
+                                stream);
+        return hip_status(e);
     }
+    hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, nullptr, nullptr, s1,
+                                          shb ? kBf16GateUp : kBf16None, stream);
+    if (e == hipSuccess)
+        e = launch_topk_bucket(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale, logits_out, r,
+                               s2, shb ? kBf16Swiglu : kBf16None, s3, shb ? kBf16Down : kBf16None, stream);
+    if (e == hipSuccess) e = launch_quant_pairs(x, r.bucket, k, M, H, L.xq, L.xs, L.xqt, L.xst, stream);
     const ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
     if (e == hipSuccess) e = launch_gate_up_fp4(gu, L.xq, L.xs, L.hq, L.hs, L.part, stream);
-    if (e == hipSuccess && sf != MOE_FMT_NONE && !shb)
+    if (e == hipSuccess && fp4_shared)
         e = launch_gate_up_fp4(dense_job(d->sh13, Ish, H, M), L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart, stream);
     const ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);
     if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream);
-    if (e == hipSuccess && sf != MOE_FMT_NONE && !shb)
+    if (e == hipSuccess && fp4_shared)
         e = launch_down_fp4(dense_job(d->sh2, H, Ish, M), L.hsq, L.hss, L.ysh, stream);
     if (e == hipSuccess)
         e = launch_finalize(L.y, r.topk_w, L.ysh, residual, d->gamma, d->eps, M, H, k, out, residual_out,

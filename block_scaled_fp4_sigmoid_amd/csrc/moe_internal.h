@@ -43,9 +43,11 @@ RouterPlan router_plan(int M, int H, int E);
 // The routing launches optionally run one bf16 shared-expert stage each as
 // extra workgroups: side1 with the router, side2 with the top-k, side3 with
 // the bucketing (stage kBf16None and blocks 0 for none).
+// With xq != nullptr the launch also writes the MXFP8 of x in token order
+// (codes xq [M][H], scales xs [M][H/32]).
 hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int M, int H, int E,
-                                  const RouterPlan& plan, float* partials, const Bf16Side& side1, int stage1,
-                                  hipStream_t stream);
+                                  const RouterPlan& plan, float* partials, uint8_t* xq, uint8_t* xs,
+                                  const Bf16Side& side1, int stage1, hipStream_t stream);
 // logits: the router partials (splits of them), or given logits (splits = 1).
 hipError_t launch_topk(const float* partials, int splits, const float* bias, int M, int E, int k,
                        float routed_scale, float* logits_out, const moe_routing& route, const Bf16Side& side2,
@@ -90,16 +92,26 @@ struct ExpertJob {
     int slots;              // U_max for routed, 1 for dense
     int k;                  // top-k (pair id -> row)
     int M;
+    // Small-pair routed path (M*k <= kSmallPairs): with ids != nullptr every
+    // workgroup resolves its slot from the top-k ids (no route step needed
+    // before it), and with a_tok the gate_up activations are in token order
+    // ([M][K]: pair p reads row p / k).
+    const int32_t* ids = nullptr;
+    bool a_tok = false;
 };
 
 // gate_up over FP4 experts.  When the plan splits K, fp32 partials go to
 // `partials` (gate_up_fp4_partials_bytes; 0 means no split and no buffer) and a
 // second launch reduces them, applies SwiGLU and requantizes h.
+// A bf16 shared-expert stage may ride along the gate_up launch (side, stage),
+// and the route step along the down launch (ride_route != nullptr: it writes
+// the routing arrays from ride_route->topk_ids for E experts).
 size_t gate_up_fp4_partials_bytes(const ExpertJob& job);
 hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const uint8_t* a_s,
-                              uint8_t* h_q, uint8_t* h_s, float* partials, hipStream_t stream);
+                              uint8_t* h_q, uint8_t* h_s, float* partials, hipStream_t stream,
+                              const Bf16Side& side = Bf16Side{}, int stage = 0);
 hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8_t* h_s,
-                           float* y, hipStream_t stream);
+                           float* y, hipStream_t stream, const moe_routing* ride_route = nullptr, int E = 0);
 
 size_t gate_up_bf16_partials_bytes(int M, int H, int I);
 Bf16Side bf16_side(const ExpertJob& gate_up_or_down, int I, int H, int M, const uint16_t* x, float* part,

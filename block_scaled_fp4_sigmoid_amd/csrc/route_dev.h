@@ -1,0 +1,140 @@
+// route_dev.h — the route step as a device function of one workgroup of
+// kBucketThreads threads, so it can run in a launch of its own or as an extra
+// workgroup of a later launch (it reads only topk_ids).
+//
+// Pages: SGLang-NVIDIA-Mega README, DeepSeek-V4.1 slot table, row "Routed
+// experts (moe)": each expert's rows are grouped into tiles of at most 8 rows,
+// an expert with more than 8 rows takes several tiles.
+#pragma once
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+constexpr int kBucketThreads = 256;
+
+// Exclusive scan over kMaxE entries held 4 per thread (256 threads).
+__device__ inline void block_exclusive_scan(int* data, int* scratch, int& total) {
+    const int tid = threadIdx.x;
+    int v0 = data[4 * tid], v1 = data[4 * tid + 1], v2 = data[4 * tid + 2], v3 = data[4 * tid + 3];
+    int sum = v0 + v1 + v2 + v3;
+    scratch[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < kBucketThreads; off <<= 1) {
+        int add = tid >= off ? scratch[tid - off] : 0;
+        __syncthreads();
+        scratch[tid] += add;
+        __syncthreads();
+    }
+    const int incl = scratch[tid];
+    total = scratch[kBucketThreads - 1];
+    int base = incl - sum;
+    data[4 * tid] = base;
+    data[4 * tid + 1] = base + v0;
+    data[4 * tid + 2] = base + v0 + v1;
+    data[4 * tid + 3] = base + v0 + v1 + v2;
+    __syncthreads();
+}
+
+// Rows per placement chunk and bitmap words per expert of the route step.
+__host__ __device__ inline int bucket_chunk_rows(int k) { return 128 < kBucketThreads / k ? 128 : kBucketThreads / k; }
+__host__ __device__ inline int bucket_words(int k) { return (bucket_chunk_rows(k) + 31) / 32; }
+
+// LDS bytes the route step needs: five per-expert int arrays, the scan
+// scratch, and the placement bitmaps.
+__host__ __device__ inline size_t bucket_lds_bytes(int E, int k) {
+    return (size_t)(5 * kMaxE + kBucketThreads) * 4 + (size_t)E * bucket_words(k) * 4;
+}
+constexpr size_t kBucketLdsMax = (size_t)(5 * kMaxE + kBucketThreads) * 4 + (size_t)kMaxE * 4 * 4;
+
+// ---------------------------------------------------------------------------
+// Route step: one workgroup builds the expert buckets, 8-row tiles and the
+// active-expert list from topk_ids (in a launch after the top-k one, so the
+// ids written by the top-k workgroups are visible without a device-scope
+// fence).
+__device__ inline void bucket_step(int M, int E, int k, const moe_routing& route, uint8_t* lds) {
+    const int tid = threadIdx.x;
+
+    int* s_cnt = reinterpret_cast<int*>(lds);
+    int* s_off = s_cnt + kMaxE;
+    int* s_tile = s_off + kMaxE;
+    int* s_act = s_tile + kMaxE;
+    int* s_run = s_act + kMaxE;
+    int* s_scan = s_run + kMaxE;
+    uint32_t* s_bm = reinterpret_cast<uint32_t*>(s_scan + kBucketThreads);  // E * bucket_words(k)
+    const int P = M * k;
+    for (int e = tid; e < kMaxE; e += kBucketThreads) {
+        s_cnt[e] = 0;
+        s_run[e] = 0;
+    }
+    __syncthreads();
+    for (int p = tid; p < P; p += kBucketThreads) atomicAdd(&s_cnt[route.topk_ids[p]], 1);
+    __syncthreads();
+    for (int e = tid; e < kMaxE; e += kBucketThreads) {
+        const int c = s_cnt[e];
+        s_off[e] = c;
+        s_tile[e] = (c + 7) / 8;
+        s_act[e] = c > 0 ? 1 : 0;
+    }
+    __syncthreads();
+    int tot_pairs, tot_tiles, tot_act;
+    block_exclusive_scan(s_off, s_scan, tot_pairs);
+    block_exclusive_scan(s_tile, s_scan, tot_tiles);
+    block_exclusive_scan(s_act, s_scan, tot_act);
+    for (int e = tid; e < E; e += kBucketThreads) {
+        const int c = s_cnt[e];
+        route.expert_offsets[e] = s_off[e];
+        if (c > 0) {
+            route.active_experts[s_act[e]] = e;
+            route.active_offsets[s_act[e]] = s_off[e];
+        }
+        for (int t = 0; 8 * t < c; ++t) {
+            const int ti = s_tile[e] + t;
+            route.tile_expert[ti] = e;
+            route.tile_begin[ti] = s_off[e] + 8 * t;
+            route.tile_rows[ti] = min(8, c - 8 * t);
+        }
+    }
+    if (tid == 0) {
+        route.expert_offsets[E] = P;
+        *route.num_tiles = tot_tiles;
+        *route.num_active = tot_act;
+    }
+    for (int sl = tot_act + tid; sl <= min(E, P); sl += kBucketThreads) route.active_offsets[sl] = P;
+    // Stable placement: chunks of R rows; a bitmap per expert marks the chunk's
+    // rows that chose it, and a pair's rank within its expert is the number of
+    // earlier rows (previous chunks + lower bits of this chunk's bitmap).
+    const int R = bucket_chunk_rows(k);
+    const int W = bucket_words(k);
+    for (int r0 = 0; r0 < M; r0 += R) {
+        for (int w = tid; w < E * W; w += kBucketThreads) s_bm[w] = 0u;
+        __syncthreads();
+        const int p = r0 * k + tid;
+        const bool valid = tid < R * k && p < P;
+        int e = 0, rl = 0;
+        if (valid) {
+            e = route.topk_ids[p];
+            rl = p / k - r0;
+            atomicOr(&s_bm[e * W + (rl >> 5)], 1u << (rl & 31));
+        }
+        __syncthreads();
+        if (valid) {
+            int rank = 0;
+            for (int w = 0; w < (rl >> 5); ++w) rank += __popc(s_bm[e * W + w]);
+            rank += __popc(s_bm[e * W + (rl >> 5)] & ((1u << (rl & 31)) - 1u));
+            route.bucket[s_off[e] + s_run[e] + rank] = p;
+        }
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += kBucketThreads) {
+            int c = 0;
+            for (int w = 0; w < W; ++w) c += __popc(s_bm[ee * W + w]);
+            s_run[ee] += c;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace moe
