@@ -528,29 +528,31 @@ __device__ __forceinline__ void stream_pass(const StreamJob& J, int e, const int
     }
 }
 
-// ---- streaming with the activation tile of a quad in LDS ---------------------
-// The four waves of a workgroup use the same activation rows.  Instead of each
-// wave loading its B operands every step, the workgroup loads the tile of a
-// quad (16*NB rows x 512 K codes and their 16 scale bytes per row) once, a
-// share per thread, into one of two LDS buffers, and the waves read their
-// operands from there; the register ring then holds weights only.  One barrier
-// per quad: tile q+1 is written while tile q is read, the barrier publishes it.
-constexpr int kTileRow = 528;                   // bytes per row: 512 codes + 16 scale bytes (staggers banks)
-constexpr int kTileBytes = kPassRows * kTileRow;  // one buffer, sized for two N-blocks
+// ---- NVFP4: streaming with the activation tile of a quad in LDS --------------
+// The four waves of a workgroup use the same activation rows.  The workgroup
+// loads the tile of a quad (16*NB rows x 512 K) once, a share per thread,
+// converts it to the f16 operand form (E4M3 * 2^(s - smax), smax the row's
+// largest scale code over the item's K range) and stores it into one of two
+// LDS buffers; the waves read ready operands from there, and the register
+// ring holds weights only.  One barrier per quad: tile q+1 is written while
+// tile q is read, the barrier publishes it.
+constexpr int kTileRowH = 1040;                     // bytes per row: 512 f16 + 16 (staggers banks)
+constexpr int kTileBytesH = kPassRows * kTileRowH;  // one buffer, sized for two N-blocks
 
 template <int NB>
 struct ActShare {
-    v4i c[2 * NB];  // code chunks of the thread (16 B each)
-    v4i s;          // the scale bytes of row t (threads t < 16*NB)
+    v4i c[2 * NB];       // code chunks of the thread (16 codes each)
+    uint32_t s[2 * NB];  // the E8M0 code of each chunk's 32-block
 };
 
-// The thread's share of a tile: byte offsets (in a_q, a_s) of its code
-// chunks and of its row's scale bytes at quad 0; kOOB for rows past the pass.
-// src as in make_coord.
+// The thread's share of a tile: byte offsets (in a_q, a_s) of its code chunks
+// and of their scale bytes at quad 0; kOOB for rows past the pass.  Chunk k of
+// thread t is row (t + 256k) / 32, codes [16 ch, +16) of the quad, ch =
+// (t + 256k) % 32.  src as in make_coord.
 template <int NB>
 struct TileOffs {
     uint32_t c[2 * NB];
-    uint32_t s;
+    uint32_t s[2 * NB];
 };
 
 template <int NB>
@@ -560,16 +562,17 @@ __device__ __forceinline__ TileOffs<NB> tile_offsets(int K, int npass, const int
 #pragma unroll
     for (int k = 0; k < 2 * NB; ++k) {
         const int li = t + kThreads * k, row = li >> 5, ch = li & 31;
-        o.c[k] = row < npass ? (src ? (uint32_t)src[row] : (uint32_t)row) * (uint32_t)K + 16 * ch : kOOB;
+        const uint32_t r = row < npass ? (src ? (uint32_t)src[row] : (uint32_t)row) : 0u;
+        o.c[k] = row < npass ? r * (uint32_t)K + 16 * ch : kOOB;
+        o.s[k] = row < npass ? r * (uint32_t)(K / 32) + (ch >> 1) : kOOB;
     }
-    o.s = (t < 16 * NB && t < npass) ? (src ? (uint32_t)src[t] : (uint32_t)t) * (uint32_t)(K / 32) : kOOB;
     return o;
 }
 
 // Requests the thread's share of tile q (absolute quad).  Rows past the pass
 // and steps at or past s_end read zeros.
 template <int NB>
-__device__ __forceinline__ void tile_load(ActShare<NB>& P, const Coord<kFmtMX, 1, NB>& c, const TileOffs<NB>& o,
+__device__ __forceinline__ void tile_load(ActShare<NB>& P, const Coord<kFmtNV, 1, NB>& c, const TileOffs<NB>& o,
                                           int q, int s_end) {
     const int t = threadIdx.x;
 #pragma unroll
@@ -577,44 +580,63 @@ __device__ __forceinline__ void tile_load(ActShare<NB>& P, const Coord<kFmtMX, 1
         const int ch = (t + kThreads * k) & 31;
         const bool ok = o.c[k] != kOOB && 4 * q + (ch >> 3) < s_end;
         P.c[k] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, ok ? o.c[k] + 512 * q : kOOB, 0, 0);
+        P.s[k] = __builtin_amdgcn_raw_buffer_load_b8(c.ras, ok ? o.s[k] + 16 * q : kOOB, 0, 0);
     }
-    const bool oks = o.s != kOOB && 4 * q < s_end;
-    P.s = __builtin_amdgcn_raw_buffer_load_b128(c.ras, oks ? o.s + 16 * q : kOOB, 0, 0);
 }
 
-// Writes the thread's share of tile q into an LDS buffer; the scale dwords of
-// steps at or past s_end become 0 (a partial last quad reads the next row's
-// bytes there).
+// Converts the thread's share of a tile to f16 and writes it into an LDS
+// buffer.  rsmax: the pass rows' smax (LDS).  Codes past the range are zero,
+// and so are their f16 values.
 template <int NB>
-__device__ __forceinline__ void tile_store(const ActShare<NB>& P, uint8_t* buf, int q, int s_end) {
+__device__ __forceinline__ void tile_store(const ActShare<NB>& P, uint8_t* buf, const int* rsmax, int npass) {
     const int t = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < 2 * NB; ++k) {
         const int li = t + kThreads * k, row = li >> 5, ch = li & 31;
-        *reinterpret_cast<v4i*>(buf + row * kTileRow + 16 * ch) = P.c[k];
-    }
-    if (t < 16 * NB) {
-        v4i sc = P.s;
-        sc.x = 4 * q + 0 < s_end ? sc.x : 0;
-        sc.y = 4 * q + 1 < s_end ? sc.y : 0;
-        sc.z = 4 * q + 2 < s_end ? sc.z : 0;
-        sc.w = 4 * q + 3 < s_end ? sc.w : 0;
-        *reinterpret_cast<v4i*>(buf + t * kTileRow + 512) = sc;
+        const int sm = row < npass ? rsmax[row] : 0;
+        const float sf = exp2i(max((int)(P.s[k] & 0xffu) - sm, -126));
+        const v8h h0 = fp8x8_to_f16((uint32_t)P.c[k].x, (uint32_t)P.c[k].y, sf);
+        const v8h h1 = fp8x8_to_f16((uint32_t)P.c[k].z, (uint32_t)P.c[k].w, sf);
+        uint8_t* p = buf + row * kTileRowH + 32 * ch;
+        *reinterpret_cast<v8h*>(p) = h0;
+        *reinterpret_cast<v8h*>(p + 16) = h1;
     }
 }
 
-// The lane's B operands of step u of the tile in buf.
-template <int FMT, int NB>
-__device__ __forceinline__ void tile_read(const uint8_t* buf, int u, v4i (&b)[NB][2], uint32_t (&bs)[NB]) {
+// The lane's B operands of step u of the tile in buf: row 16j + i, K
+// [128u + 32g + 8c, +8) for MFMA c (the order nv_dequant8 gives the weights).
+template <int NB>
+__device__ __forceinline__ void tile_read(const uint8_t* buf, int u, v8h (&B)[NB][4]) {
     const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-        const uint8_t* row = buf + (16 * j + i) * kTileRow;
-        bs[j] = *reinterpret_cast<const uint32_t*>(row + 512 + 4 * u);
-        // MX: [16g, +16) and [64 + 16g, +16) of the step; NV: [32g, +32)
-        const uint8_t* p = row + 128 * u + (FMT == kFmtMX ? 16 : 32) * g;
-        b[j][0] = *reinterpret_cast<const v4i*>(p);
-        b[j][1] = *reinterpret_cast<const v4i*>(p + (FMT == kFmtMX ? 64 : 16));
+        const uint8_t* p = buf + (16 * j + i) * kTileRowH + 256 * u + 64 * g;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) B[j][c] = *reinterpret_cast<const v8h*>(p + 16 * c);
+    }
+}
+
+// One NVFP4 K step with f16 activation operands given.
+template <int MB, int NB, int U>
+__device__ __forceinline__ void mfma_step_h(const v4i (&a_)[MB], const uint32_t (&as)[MB][2], const v8h (&B)[NB][4],
+                                            v4f (&acc)[MB][2]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const v4i a = a_[mb];
+        float sv0, sv1;
+        v2h m;
+        nv_scales2<U & 1>(as[mb][U >> 1], sv0, sv1, m);
+        const v8h A0 = nv_dequant8((uint32_t)a.x, sv0, m[0]);
+        const v8h A1 = nv_dequant8((uint32_t)a.y, sv0, m[0]);
+        const v8h A2 = nv_dequant8((uint32_t)a.z, sv1, m[1]);
+        const v8h A3 = nv_dequant8((uint32_t)a.w, sv1, m[1]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, B[j][0], acc[mb][j], 0, 0, 0);
+            acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, B[j][1], acc[mb][j], 0, 0, 0);
+            acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2, B[j][2], acc[mb][j], 0, 0, 0);
+            acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3, B[j][3], acc[mb][j], 0, 0, 0);
+        }
     }
 }
 
@@ -625,8 +647,8 @@ struct RingW {
     uint32_t as[DQ][MB][2];
 };
 
-template <int FMT, int MB, int NB, int DQ>
-__device__ __forceinline__ void ringw_load_step(RingW<MB, DQ>& R, int v, int u, const Coord<FMT, MB, NB>& c, int q,
+template <int MB, int NB, int DQ>
+__device__ __forceinline__ void ringw_load_step(RingW<MB, DQ>& R, int v, int u, const Coord<kFmtNV, MB, NB>& c, int q,
                                                 int s_end) {
     const int st = 4 * q + u;
     const bool ok = st < s_end;
@@ -635,56 +657,52 @@ __device__ __forceinline__ void ringw_load_step(RingW<MB, DQ>& R, int v, int u, 
         R.a[v][u][mb] = __builtin_amdgcn_raw_buffer_load_b128(c.rw, ok ? c.vw[mb] : kOOB, 1024 * st, MOE_WEIGHT_AUX);
 }
 
-template <int FMT, int MB, int NB, int DQ>
-__device__ __forceinline__ void ringw_load_scales(RingW<MB, DQ>& R, int v, const Coord<FMT, MB, NB>& c, int q,
+template <int MB, int NB, int DQ>
+__device__ __forceinline__ void ringw_load_scales(RingW<MB, DQ>& R, int v, const Coord<kFmtNV, MB, NB>& c, int q,
                                                   int s_end) {
     const bool okq = 4 * q < s_end;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        if constexpr (FMT == kFmtMX) {
-            R.as[v][mb][0] = __builtin_amdgcn_raw_buffer_load_b32(c.rs, okq ? c.vs[mb] : kOOB, 256 * q, 0);
-        } else {
-            const auto sv = __builtin_amdgcn_raw_buffer_load_b64(c.rs, okq ? c.vs[mb] : kOOB, 512 * q, 0);
-            R.as[v][mb][0] = sv[0];
-            R.as[v][mb][1] = sv[1];
-        }
+        const auto sv = __builtin_amdgcn_raw_buffer_load_b64(c.rs, okq ? c.vs[mb] : kOOB, 512 * q, 0);
+        R.as[v][mb][0] = sv[0];
+        R.as[v][mb][1] = sv[1];
     }
 }
 
 // The four steps of the quad in slot v, the B operands of step U given and
 // those of step U+1 read from the tile meanwhile; each step's weight slot is
 // refilled with quad qn right after its MFMAs.
-template <int FMT, int MB, int NB, int DQ, int U>
-__device__ __forceinline__ void quadw_steps(RingW<MB, DQ>& R, int v, const Coord<FMT, MB, NB>& c, int qn, int s_end,
-                                            const uint8_t* tile, const v4i (&b)[NB][2], const uint32_t (&bs)[NB],
-                                            const int (&sfo)[NB], v4f (&acc)[MB][2]) {
+template <int MB, int NB, int DQ, int U>
+__device__ __forceinline__ void quadw_steps(RingW<MB, DQ>& R, int v, const Coord<kFmtNV, MB, NB>& c, int qn,
+                                            int s_end, const uint8_t* tile, const v8h (&B)[NB][4],
+                                            v4f (&acc)[MB][2]) {
     if constexpr (U < 4) {
         __builtin_amdgcn_sched_barrier(0);
-        v4i bn[NB][2];
-        uint32_t bsn[NB];
-        if constexpr (U < 3) tile_read<FMT, NB>(tile, U + 1, bn, bsn);
-        mfma_step<FMT, MB, NB, U>(R.a[v][U], R.as[v], b, bs, sfo, acc);
-        if constexpr (U == 3) ringw_load_scales<FMT, MB, NB, DQ>(R, v, c, qn, s_end);
-        ringw_load_step<FMT, MB, NB, DQ>(R, v, U, c, qn, s_end);
-        quadw_steps<FMT, MB, NB, DQ, U + 1>(R, v, c, qn, s_end, tile, bn, bsn, sfo, acc);
+        v8h Bn[NB][4];
+        if constexpr (U < 3) tile_read<NB>(tile, U + 1, Bn);
+        mfma_step_h<MB, NB, U>(R.a[v][U], R.as[v], B, acc);
+        if constexpr (U == 3) ringw_load_scales<MB, NB, DQ>(R, v, c, qn, s_end);
+        ringw_load_step<MB, NB, DQ>(R, v, U, c, qn, s_end);
+        quadw_steps<MB, NB, DQ, U + 1>(R, v, c, qn, s_end, tile, Bn, acc);
     }
 }
 
-// A pass as stream_pass, with the activation tiles in LDS (tiles: two
-// kTileBytes buffers).  Every thread of the workgroup must call it with the
-// same arguments apart from the weight blocks (it has barriers).
-template <int FMT, int MB, int NB, int DQ>
+// An NVFP4 pass as stream_pass, with the activation tiles in LDS (tiles: two
+// kTileBytesH buffers; rsmax: kPassRows ints).  Every thread of the workgroup
+// must call it with the same arguments apart from the weight blocks (it has
+// barriers).
+template <int MB, int NB, int DQ>
 __device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const int (&wblk)[MB], int arow0,
-                                                int npass, const int* src, int s0, int nst, int ms0, int mnst,
-                                                int (&smax)[NB], v4f (&acc)[MB][2], uint8_t* tiles) {
+                                                int npass, const int* src, int s0, int nst, int (&smax)[NB],
+                                                v4f (&acc)[MB][2], uint8_t* tiles, int* rsmax) {
     static_assert(DQ % 2 == 0, "slots alternate between the two tile buffers");
-    const Coord<FMT, MB, NB> c = make_coord<FMT, MB, NB>(J, e, wblk, arow0, npass, src);
+    const Coord<kFmtNV, MB, NB> c = make_coord<kFmtNV, MB, NB>(J, e, wblk, arow0, npass, src);
     const TileOffs<NB> to = tile_offsets<NB>(J.K, npass, src);
-    Coord<kFmtMX, 1, NB> ca;  // the activation resources, for the tile loads
+    Coord<kFmtNV, 1, NB> ca;  // the activation resources, for the tile loads
     ca.ra = c.ra;
     ca.ras = c.ras;
     SmaxRaw<NB> SR;
-    if constexpr (FMT == kFmtNV) row_smax_issue<FMT, MB, NB>(c, ms0, mnst, SR);
+    row_smax_issue<kFmtNV, MB, NB>(c, s0, nst, SR);
     __builtin_amdgcn_sched_barrier(0);
     const int q0 = s0 / 4, nq = (nst + 3) / 4, s_end = s0 + nst;
     ActShare<NB> P;
@@ -695,42 +713,36 @@ __device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             __builtin_amdgcn_sched_barrier(0);
-            if (u == 3) ringw_load_scales<FMT, MB, NB, DQ>(R, v, c, q0 + v, s_end);
-            ringw_load_step<FMT, MB, NB, DQ>(R, v, u, c, q0 + v, s_end);
+            if (u == 3) ringw_load_scales<MB, NB, DQ>(R, v, c, q0 + v, s_end);
+            ringw_load_step<MB, NB, DQ>(R, v, u, c, q0 + v, s_end);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    int sfo[NB];
-    if constexpr (FMT == kFmtNV) {
-        row_smax_finish<FMT, MB, NB>(c, ms0, mnst, SR, smax);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) sfo[j] = -smax[j];
-    } else {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            sfo[j] = 0;
-            smax[j] = 0;
-        }
-    }
+    row_smax_finish<kFmtNV, MB, NB>(c, s0, nst, SR, smax);
     __builtin_amdgcn_sched_barrier(0);
+    // every wave holds the rows' smax; wave 0 publishes them for the tile stores
+    if (threadIdx.x < 16) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) rsmax[16 * j + threadIdx.x] = smax[j];
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[mb][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    tile_store<NB>(P, tiles, q0, s_end);
+    __syncthreads();
+    tile_store<NB>(P, tiles, rsmax, npass);
     __syncthreads();
     for (int l0 = 0; l0 < nq; l0 += DQ) {
 #pragma unroll
         for (int v = 0; v < DQ; ++v) {
             const int q = q0 + l0 + v;  // the quad of slot v in this round
-            const uint8_t* tile = tiles + (v & 1) * kTileBytes;
-            v4i b[NB][2];
-            uint32_t bs[NB];
-            tile_read<FMT, NB>(tile, 0, b, bs);
+            const uint8_t* tile = tiles + (v & 1) * kTileBytesH;
+            v8h B[NB][4];
+            tile_read<NB>(tile, 0, B);
             tile_load<NB>(P, ca, to, q + 1, s_end);  // in flight over the quad's steps
-            quadw_steps<FMT, MB, NB, DQ, 0>(R, v, c, q + DQ, s_end, tile, b, bs, sfo, acc);
+            quadw_steps<MB, NB, DQ, 0>(R, v, c, q + DQ, s_end, tile, B, acc);
             // tile q+1 into the other buffer (its reads ended at the last barrier)
-            tile_store<NB>(P, tiles + ((v + 1) & 1) * kTileBytes, q + 1, s_end);
+            tile_store<NB>(P, tiles + ((v + 1) & 1) * kTileBytesH, rsmax, npass);
             __syncthreads();
         }
     }
@@ -815,9 +827,14 @@ __global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLO
     const int s0 = k0 / 128, nst = min(J.span, K - k0) / 128;
     const float gs = FMT == kFmtNV ? J.gscale[tk.e] : 1.0f;
 
-    __shared__ float sG[kPassRows][2 * GCOLS + 1];  // fused: gate [0, GCOLS), up [GCOLS, 2*GCOLS)
+    // fused epilogue: gate [0, GCOLS), up [GCOLS, 2*GCOLS) per row.  NVFP4 keeps
+    // the activation tiles of two quads in the same LDS: the epilogue runs
+    // after the pass's last barrier, when no wave reads a tile any more.
+    constexpr int kGBytes = kPassRows * (2 * GCOLS + 1) * 4;
+    constexpr int kLdsBytes = FMT == kFmtNV && 2 * kTileBytesH > kGBytes ? 2 * kTileBytesH : kGBytes;
+    __shared__ __align__(16) uint8_t sLds[kLdsBytes];
+    float(*sG)[2 * GCOLS + 1] = reinterpret_cast<float(*)[2 * GCOLS + 1]>(sLds);
     __shared__ int s_smax[kPassRows];
-    __shared__ __align__(16) uint8_t sTiles[FMT == kFmtNV ? 2 * kTileBytes : 16];  // activation tiles of two quads
 
     for (int t0 = 0; t0 < tk.n; t0 += kPassRows) {
         const int npass = min(kPassRows, tk.n - t0);
@@ -828,8 +845,7 @@ __global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLO
         if (npass > 16) {
             int sm[2];
             if constexpr (FMT == kFmtNV)
-                stream_pass_lds<FMT, GMB, 2, MOE_NV_DQ>(J, tk.e, wblk, arow0, npass, src, s0, nst, s0, nst, sm, acc,
-                                                        sTiles);
+                stream_pass_lds<GMB, 2, MOE_NV_DQ>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm, acc, sLds, s_smax);
             else
                 stream_pass<FMT, GMB, 2, ring_quads<FMT, GMB, 2>(), 4>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm,
                                                                          acc);
@@ -838,8 +854,7 @@ __global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLO
         } else {
             int sm[1];
             if constexpr (FMT == kFmtNV)
-                stream_pass_lds<FMT, GMB, 1, MOE_NV_DQ>(J, tk.e, wblk, arow0, npass, src, s0, nst, s0, nst, sm, acc,
-                                                        sTiles);
+                stream_pass_lds<GMB, 1, MOE_NV_DQ>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm, acc, sLds, s_smax);
             else
                 stream_pass<FMT, GMB, 1, ring_quads<FMT, GMB, 1>(), 4>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm,
                                                                          acc);
