@@ -36,7 +36,8 @@ CHAIN_MIN = 8  # layer steps per graph in the chained graph timing (at least)
 DOMINANT = "k_gate_up"
 # sources that decide what the dominant kernel reads and writes
 KERNEL_SOURCES = ("block_scaled_fp4_sigmoid_amd/csrc/k_stream.hip", "block_scaled_fp4_sigmoid_amd/csrc/moe_device.h",
-                  "block_scaled_fp4_sigmoid_amd/csrc/moe_internal.h")
+                  "block_scaled_fp4_sigmoid_amd/csrc/moe_internal.h", "block_scaled_fp4_sigmoid_amd/csrc/route_dev.h",
+                  "block_scaled_fp4_sigmoid_amd/csrc/dense_bf16_dev.h")
 
 
 def log(*a):
