@@ -839,7 +839,19 @@ __global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLO
     for (int t0 = 0; t0 < tk.n; t0 += kPassRows) {
         const int npass = min(kPassRows, tk.n - t0);
         const int arow0 = tk.base + t0;
-        const int* src = J.a_tok ? s_tok + t0 : nullptr;  // token-ordered activations: gather the rows
+        // token-ordered activations: gather the pass's rows (tokens resolved
+        // with the slot, or read from the bucket here)
+        const int* src = nullptr;
+        if (J.a_tok) {
+            if (J.ids) {
+                src = s_tok + t0;
+            } else {
+                __syncthreads();  // the previous pass's reads of s_tok are done
+                if ((int)threadIdx.x < npass) s_tok[threadIdx.x] = J.bucket[arow0 + threadIdx.x] / J.k;
+                __syncthreads();
+                src = s_tok;
+            }
+        }
         v4f acc[GMB][2];
         int smax[2] = {0, 0};
         if (npass > 16) {
@@ -1211,7 +1223,7 @@ StreamJob stream_job(const ExpertJob& j, int N, const uint8_t* a_q, const uint8_
     s.out_rows = a_rows;
     s.ids = j.dense ? nullptr : j.ids;
     s.k = j.k;
-    s.a_tok = (!j.dense && j.ids && j.a_tok) ? 1 : 0;
+    s.a_tok = (!j.dense && j.a_tok) ? 1 : 0;
     if (s.a_tok) s.a_rows = (uint32_t)j.M;
     return s;
 }

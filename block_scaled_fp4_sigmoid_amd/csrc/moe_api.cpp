@@ -323,16 +323,10 @@ LayerWs carve_layer(Carver& c, const moe_layer_desc* d) {
     L.active = c.take<int32_t>(std::min(E, P));
     L.num_active = c.take<int32_t>(1);
     L.act_off = c.take<int32_t>(std::min(E, P) + 1);
-    const bool small = P <= kSmallPairs;         // gate_up gathers token-order rows
-    L.xq = L.xs = L.xqt = L.xst = nullptr;
-    if (!small) {                                // bucket order
-        L.xq = c.take<uint8_t>((size_t)P * H);
-        L.xs = c.take<uint8_t>((size_t)P * H / 32);
-    }
-    if (small || (sh && !shb)) {                 // token order (and for the FP4 shared expert)
-        L.xqt = c.take<uint8_t>((size_t)M * H);
-        L.xst = c.take<uint8_t>((size_t)M * H / 32);
-    }
+    // token order: gate_up gathers its rows (and the FP4 shared expert reads them)
+    L.xq = L.xs = nullptr;
+    L.xqt = c.take<uint8_t>((size_t)M * H);
+    L.xst = c.take<uint8_t>((size_t)M * H / 32);
     L.hq = c.take<uint8_t>((size_t)P * I);
     L.hs = c.take<uint8_t>((size_t)P * I / 32);
     L.hsq = L.hss = nullptr;
@@ -434,14 +428,17 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
                                 stream);
         return hip_status(e);
     }
-    hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, nullptr, nullptr, s1,
+    // Six launches: (router + token-order MXFP8 of x) -> top-k -> route step
+    // -> gate_up (gathers each pass's token rows through the bucket) -> down
+    // -> finalize.
+    hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, L.xqt, L.xst, s1,
                                           shb ? kBf16GateUp : kBf16None, stream);
     if (e == hipSuccess)
         e = launch_topk_bucket(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale, logits_out, r,
                                s2, shb ? kBf16Swiglu : kBf16None, s3, shb ? kBf16Down : kBf16None, stream);
-    if (e == hipSuccess) e = launch_quant_pairs(x, r.bucket, k, M, H, L.xq, L.xs, L.xqt, L.xst, stream);
-    const ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
-    if (e == hipSuccess) e = launch_gate_up_fp4(gu, L.xq, L.xs, L.hq, L.hs, L.part, stream);
+    ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
+    gu.a_tok = true;
+    if (e == hipSuccess) e = launch_gate_up_fp4(gu, L.xqt, L.xst, L.hq, L.hs, L.part, stream);
     if (e == hipSuccess && fp4_shared)
         e = launch_gate_up_fp4(dense_job(d->sh13, Ish, H, M), L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart, stream);
     const ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);

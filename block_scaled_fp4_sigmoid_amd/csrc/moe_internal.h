@@ -94,8 +94,9 @@ struct ExpertJob {
     int M;
     // Small-pair routed path (M*k <= kSmallPairs): with ids != nullptr every
     // workgroup resolves its slot from the top-k ids (no route step needed
-    // before it), and with a_tok the gate_up activations are in token order
-    // ([M][K]: pair p reads row p / k).
+    // before it).  With a_tok the gate_up activations are in token order
+    // ([M][K]: pair p reads row p / k, the pairs of a pass gathered through
+    // the resolved list or the bucket).
     const int32_t* ids = nullptr;
     bool a_tok = false;
 };
