@@ -801,18 +801,27 @@ __device__ __forceinline__ float silu_mul(float gt, float up) { return gt / (1.0
 constexpr int GMB = 2;           // 16-row weight blocks per wave in gate_up
 constexpr int GCOLS = 32 * GMB;  // output columns per workgroup
 
+// Workgroups [0, n2) take items of a second job J2 of the same format (the
+// FP4 shared expert riding along the routed experts; first, so its few long
+// items do not trail the launch), [n2, nmain) items of job J0, later ones a
+// bf16 shared-expert stage.
 template <int FMT, bool FUSED>
 __global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLOCKS) void k_gate_up(
-    StreamJob J, uint8_t* __restrict__ h_q, uint8_t* __restrict__ h_s, float* __restrict__ part, int nmain,
-    Bf16Side side, int stage) {
+    StreamJob J0, uint8_t* __restrict__ h_q0, uint8_t* __restrict__ h_s0, float* __restrict__ part, int nmain,
+    Bf16Side side, int stage, StreamJob J2, uint8_t* __restrict__ h_q2, uint8_t* __restrict__ h_s2, int n2) {
     if ((int)blockIdx.x >= nmain) {  // a bf16 shared-expert stage riding along
         bf16_side_block(side, stage, blockIdx.x - nmain);
         return;
     }
+    const bool second = (int)blockIdx.x < n2;  // uniform
+    const StreamJob& J = second ? J2 : J0;
+    uint8_t* __restrict__ h_q = second ? h_q2 : h_q0;
+    uint8_t* __restrict__ h_s = second ? h_s2 : h_s0;
+    const int bid = second ? (int)blockIdx.x : (int)blockIdx.x - n2;
     const int I = J.N / 2, K = J.K;
-    const int ks = blockIdx.x % J.splits;
-    const int blk = (blockIdx.x / J.splits) % J.nblk;
-    const int slot = blockIdx.x / (J.splits * J.nblk);
+    const int ks = bid % J.splits;
+    const int blk = (bid / J.splits) % J.nblk;
+    const int slot = bid / (J.splits * J.nblk);
     Tokens tk;
     __shared__ int s_list[kThreads], s_tok[kThreads];
     if (!resolve_item(J, slot, tk, s_list, s_tok)) return;
@@ -968,17 +977,24 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_quant(const float* __restri
 constexpr int kDownMB = 2;  // 16-row weight blocks per wave in down along K
 
 template <int FMT, int MB>
-__global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J, float* __restrict__ y, int nmain,
-                                                                   moe_routing ride, int ride_E) {
+__global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0, float* __restrict__ y0, int nmain,
+                                                                   moe_routing ride, int ride_E, StreamJob J2,
+                                                                   float* __restrict__ y2, int n2) {
     if ((int)blockIdx.x >= nmain) {  // the route step riding along (it writes only the routing arrays)
         extern __shared__ __align__(16) uint8_t s_dyn[];
-        bucket_step(J.M, ride_E, J.k, ride, s_dyn);
+        bucket_step(J0.M, ride_E, J0.k, ride, s_dyn);
         return;
     }
+    // workgroups [0, n2) take items of a second job J2 (first: its few long
+    // items would otherwise trail the launch), [n2, nmain) items of J0
+    const bool second = (int)blockIdx.x < n2;  // uniform
+    const StreamJob& J = second ? J2 : J0;
+    float* __restrict__ y = second ? y2 : y0;
+    const int bid = second ? (int)blockIdx.x : (int)blockIdx.x - n2;
     const int H = J.N, I = J.K;
     constexpr int RB = 64 * MB;
-    const int blk = blockIdx.x % J.nblk;
-    const int slot = blockIdx.x / J.nblk;
+    const int blk = bid % J.nblk;
+    const int slot = bid / J.nblk;
     Tokens tk;
     __shared__ int s_list[kThreads], s_tok[kThreads];
     if (!resolve_item(J, slot, tk, s_list, s_tok)) return;
@@ -1239,7 +1255,8 @@ size_t gate_up_fp4_partials_bytes(const ExpertJob& job) {
 }
 
 hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const uint8_t* a_s, uint8_t* h_q,
-                              uint8_t* h_s, float* partials, hipStream_t stream, const Bf16Side& side, int stage) {
+                              uint8_t* h_s, float* partials, hipStream_t stream, const Bf16Side& side, int stage,
+                              const SecondJob& second) {
     const GatePlan p = gate_plan(job);
     const int rows = out_rows_of(job);
     StreamJob J = stream_job(job, 2 * job.N_out, a_q, a_s, rows);
@@ -1247,20 +1264,42 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
     J.splits = p.splits;
     J.nblk = p.nblk;
     const int blocks = grid_slots(job) * p.nblk * p.splits;
-    const int extra = stage == kBf16None ? 0 : side.blocks;
-    const dim3 g(blocks + extra), b(kThreads);
     const bool mx = job.w.fmt == MOE_FMT_MXFP4;
+    // a second job of the same format rides along when both run over all of K
+    StreamJob J2 = J;
+    int n2 = 0;
+    if (second.job) {
+        const ExpertJob& j2 = *second.job;
+        if (p.splits == 1 && j2.w.fmt == job.w.fmt) {
+            J2 = stream_job(j2, 2 * j2.N_out, second.a_q, second.a_s, out_rows_of(j2));
+            J2.nblk = j2.N_out / GCOLS;  // span = K, one split
+            n2 = grid_slots(j2) * J2.nblk;
+        } else {
+            hipError_t e = launch_gate_up_fp4(j2, second.a_q, second.a_s, second.h_q, second.h_s, second.partials,
+                                              stream);
+            if (e != hipSuccess) return e;
+        }
+    }
+    const int extra = stage == kBf16None ? 0 : side.blocks;
+    const dim3 g(blocks + n2 + extra), b(kThreads);
+    uint8_t* hq2 = n2 ? second.h_q : h_q;
+    uint8_t* hs2 = n2 ? second.h_s : h_s;
+    const int nmain = blocks + n2;
     if (p.splits == 1) {
         if (mx)
-            hipLaunchKernelGGL((k_gate_up<kFmtMX, true>), g, b, 0, stream, J, h_q, h_s, partials, blocks, side, stage);
+            hipLaunchKernelGGL((k_gate_up<kFmtMX, true>), g, b, 0, stream, J, h_q, h_s, partials, nmain, side, stage,
+                               J2, hq2, hs2, n2);
         else
-            hipLaunchKernelGGL((k_gate_up<kFmtNV, true>), g, b, 0, stream, J, h_q, h_s, partials, blocks, side, stage);
+            hipLaunchKernelGGL((k_gate_up<kFmtNV, true>), g, b, 0, stream, J, h_q, h_s, partials, nmain, side, stage,
+                               J2, hq2, hs2, n2);
         return hipGetLastError();
     }
     if (mx)
-        hipLaunchKernelGGL((k_gate_up<kFmtMX, false>), g, b, 0, stream, J, h_q, h_s, partials, blocks, side, stage);
+        hipLaunchKernelGGL((k_gate_up<kFmtMX, false>), g, b, 0, stream, J, h_q, h_s, partials, nmain, side, stage, J2,
+                           hq2, hs2, n2);
     else
-        hipLaunchKernelGGL((k_gate_up<kFmtNV, false>), g, b, 0, stream, J, h_q, h_s, partials, blocks, side, stage);
+        hipLaunchKernelGGL((k_gate_up<kFmtNV, false>), g, b, 0, stream, J, h_q, h_s, partials, nmain, side, stage, J2,
+                           hq2, hs2, n2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int threads = rows * (job.N_out / 32) * 8;
@@ -1319,19 +1358,35 @@ hipError_t launch_down_rows(const StreamJob& J, int slots, float* y, const DownR
 }
 
 hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8_t* h_s, float* y,
-                           hipStream_t stream, const moe_routing* ride_route, int E) {
+                           hipStream_t stream, const moe_routing* ride_route, int E, const SecondDown& second) {
     StreamJob J = stream_job(job, job.N_out, h_q, h_s, out_rows_of(job));
     const DownRide dr = down_ride(ride_route, E, job.k);
+    // a second job rides along when both stream along K with the same format
+    const bool fold = second.job && job.K > 512 && second.job->K > 512 && second.job->w.fmt == job.w.fmt;
+    if (second.job && !fold) {
+        hipError_t e = launch_down_fp4(*second.job, second.h_q, second.h_s, second.y, stream);
+        if (e != hipSuccess) return e;
+    }
     if (job.K <= 512)  // all of K in one quad: stream along the rows
         return job.w.fmt == MOE_FMT_MXFP4 ? launch_down_rows<kFmtMX>(J, grid_slots(job), y, dr, stream)
                                           : launch_down_rows<kFmtNV>(J, grid_slots(job), y, dr, stream);
     J.nblk = job.N_out / (64 * kDownMB);
-    const int nmain = grid_slots(job) * J.nblk;
+    const int n1 = grid_slots(job) * J.nblk;
+    StreamJob J2 = J;
+    int n2 = 0;
+    if (fold) {
+        const ExpertJob& j2 = *second.job;
+        J2 = stream_job(j2, j2.N_out, second.h_q, second.h_s, out_rows_of(j2));
+        J2.nblk = j2.N_out / (64 * kDownMB);
+        n2 = grid_slots(j2) * J2.nblk;
+    }
+    float* y2 = fold ? second.y : y;
+    const int nmain = n1 + n2;
     const dim3 g(nmain + dr.blocks), b(kThreads);
     if (job.w.fmt == MOE_FMT_MXFP4)
-        hipLaunchKernelGGL((k_down<kFmtMX, kDownMB>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E);
+        hipLaunchKernelGGL((k_down<kFmtMX, kDownMB>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E, J2, y2, n2);
     else
-        hipLaunchKernelGGL((k_down<kFmtNV, kDownMB>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E);
+        hipLaunchKernelGGL((k_down<kFmtNV, kDownMB>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E, J2, y2, n2);
     return hipGetLastError();
 }
 

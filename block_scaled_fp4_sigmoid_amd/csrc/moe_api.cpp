@@ -414,15 +414,16 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
         ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
         gu.ids = r.topk_ids;
         gu.a_tok = true;
+        // the FP4 shared expert rides along the routed launches
+        const ExpertJob sgu = dense_job(d->sh13, Ish, H, M), sdn = dense_job(d->sh2, H, Ish, M);
+        const SecondJob s_gu = fp4_shared ? SecondJob{&sgu, L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart} : SecondJob{};
+        const SecondDown s_dn = fp4_shared ? SecondDown{&sdn, L.hsq, L.hss, L.ysh} : SecondDown{};
         if (e == hipSuccess)
-            e = launch_gate_up_fp4(gu, L.xqt, L.xst, L.hq, L.hs, L.part, stream, s3, shb ? kBf16Down : kBf16None);
-        if (e == hipSuccess && fp4_shared)
-            e = launch_gate_up_fp4(dense_job(d->sh13, Ish, H, M), L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart, stream);
+            e = launch_gate_up_fp4(gu, L.xqt, L.xst, L.hq, L.hs, L.part, stream, s3, shb ? kBf16Down : kBf16None,
+                                   s_gu);
         ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);
         dn.ids = r.topk_ids;
-        if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream, &r, E);
-        if (e == hipSuccess && fp4_shared)
-            e = launch_down_fp4(dense_job(d->sh2, H, Ish, M), L.hsq, L.hss, L.ysh, stream);
+        if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream, &r, E, s_dn);
         if (e == hipSuccess)
             e = launch_finalize(L.y, r.topk_w, L.ysh, residual, d->gamma, d->eps, M, H, k, out, residual_out,
                                 stream);
@@ -438,13 +439,13 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
                                s2, shb ? kBf16Swiglu : kBf16None, s3, shb ? kBf16Down : kBf16None, stream);
     ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
     gu.a_tok = true;
-    if (e == hipSuccess) e = launch_gate_up_fp4(gu, L.xqt, L.xst, L.hq, L.hs, L.part, stream);
-    if (e == hipSuccess && fp4_shared)
-        e = launch_gate_up_fp4(dense_job(d->sh13, Ish, H, M), L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart, stream);
+    const ExpertJob sgu = dense_job(d->sh13, Ish, H, M), sdn = dense_job(d->sh2, H, Ish, M);
+    const SecondJob s_gu = fp4_shared ? SecondJob{&sgu, L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart} : SecondJob{};
+    const SecondDown s_dn = fp4_shared ? SecondDown{&sdn, L.hsq, L.hss, L.ysh} : SecondDown{};
+    if (e == hipSuccess)
+        e = launch_gate_up_fp4(gu, L.xqt, L.xst, L.hq, L.hs, L.part, stream, no_side(), kBf16None, s_gu);
     const ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);
-    if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream);
-    if (e == hipSuccess && fp4_shared)
-        e = launch_down_fp4(dense_job(d->sh2, H, Ish, M), L.hsq, L.hss, L.ysh, stream);
+    if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream, nullptr, 0, s_dn);
     if (e == hipSuccess)
         e = launch_finalize(L.y, r.topk_w, L.ysh, residual, d->gamma, d->eps, M, H, k, out, residual_out,
                             stream);

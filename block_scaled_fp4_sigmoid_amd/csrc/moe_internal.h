@@ -104,15 +104,34 @@ struct ExpertJob {
 // gate_up over FP4 experts.  When the plan splits K, fp32 partials go to
 // `partials` (gate_up_fp4_partials_bytes; 0 means no split and no buffer) and a
 // second launch reduces them, applies SwiGLU and requantizes h.
+// A second FP4 job (the shared expert) with its operands: it rides along the
+// launch of the first (its items after the first's) when both have the same
+// format and run over all of K, else it gets a launch of its own.
+struct SecondJob {
+    const ExpertJob* job = nullptr;
+    const uint8_t* a_q = nullptr;
+    const uint8_t* a_s = nullptr;
+    uint8_t* h_q = nullptr;
+    uint8_t* h_s = nullptr;
+    float* partials = nullptr;  // for a launch of its own
+};
+struct SecondDown {
+    const ExpertJob* job = nullptr;
+    const uint8_t* h_q = nullptr;
+    const uint8_t* h_s = nullptr;
+    float* y = nullptr;
+};
+
 // A bf16 shared-expert stage may ride along the gate_up launch (side, stage),
 // and the route step along the down launch (ride_route != nullptr: it writes
 // the routing arrays from ride_route->topk_ids for E experts).
 size_t gate_up_fp4_partials_bytes(const ExpertJob& job);
 hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const uint8_t* a_s,
                               uint8_t* h_q, uint8_t* h_s, float* partials, hipStream_t stream,
-                              const Bf16Side& side = Bf16Side{}, int stage = 0);
+                              const Bf16Side& side = Bf16Side{}, int stage = 0, const SecondJob& second = SecondJob{});
 hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8_t* h_s,
-                           float* y, hipStream_t stream, const moe_routing* ride_route = nullptr, int E = 0);
+                           float* y, hipStream_t stream, const moe_routing* ride_route = nullptr, int E = 0,
+                           const SecondDown& second = SecondDown{});
 
 size_t gate_up_bf16_partials_bytes(int M, int H, int I);
 Bf16Side bf16_side(const ExpertJob& gate_up_or_down, int I, int H, int M, const uint16_t* x, float* part,
