@@ -105,10 +105,15 @@ struct StreamJob {
     const int32_t* ids;     // routed, M*k <= kThreads pairs: slots resolve from the top-k ids
     int k;                  // top-k (pair id = row * k + slot)
     int a_tok;              // activations in token order: pair p reads row p / k
+    const int32_t* count;   // with the active list: the number of active slots (later entries are stale)
+    // gate_up resolving from the ids: record the resolved slots here for the
+    // down launch (active experts, bucket ranges, count, bucket), or nullptr
+    int32_t *r_act, *r_off, *r_na, *r_bkt;
 };
 
 struct Tokens {
     int e, base, n;
+    int na;  // active experts (resolve_ids)
 };
 
 // Slot -> (expert, bucket range).  The three loads are independent; unused
@@ -123,6 +128,7 @@ __device__ __forceinline__ bool resolve(const StreamJob& J, int slot, Tokens& t)
     }
     const int b0 = J.active_offsets[slot], b1 = J.active_offsets[slot + 1];
     const int e = J.active[slot];
+    if (J.count && slot >= *J.count) return false;
     if (b1 <= b0) return false;
     t.e = e;
     t.base = b0;
@@ -187,6 +193,7 @@ __device__ __forceinline__ bool resolve_ids(const StreamJob& J, int slot, Tokens
     t.e = __builtin_amdgcn_readfirstlane(e);
     t.base = __builtin_amdgcn_readfirstlane(base);
     t.n = __builtin_amdgcn_readfirstlane(n);
+    t.na = total;
     return true;
 }
 
@@ -825,6 +832,18 @@ __global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLO
     Tokens tk;
     __shared__ int s_list[kThreads], s_tok[kThreads];
     if (!resolve_item(J, slot, tk, s_list, s_tok)) return;
+    if (J.r_act && blk == 0 && ks == 0) {  // one workgroup per slot records it for the down launch
+        const int t = threadIdx.x;
+        if (t < tk.n) J.r_bkt[tk.base + t] = s_list[t];
+        if (t == 0) {
+            J.r_act[slot] = tk.e;
+            J.r_off[slot] = tk.base;
+            if (slot == 0) {
+                *J.r_na = tk.na;
+                J.r_off[tk.na] = J.M * J.k;
+            }
+        }
+    }
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int i = lane & 15, g = lane >> 4;
     const int half = (wave & 1) * (16 * GMB);  // column offset of the wave within the item
@@ -1240,6 +1259,11 @@ StreamJob stream_job(const ExpertJob& j, int N, const uint8_t* a_q, const uint8_
     s.ids = j.dense ? nullptr : j.ids;
     s.k = j.k;
     s.a_tok = (!j.dense && j.a_tok) ? 1 : 0;
+    s.count = j.dense ? nullptr : j.count;
+    s.r_act = j.record ? j.record->act : nullptr;
+    s.r_off = j.record ? j.record->off : nullptr;
+    s.r_na = j.record ? j.record->na : nullptr;
+    s.r_bkt = j.record ? j.record->bkt : nullptr;
     if (s.a_tok) s.a_rows = (uint32_t)j.M;
     return s;
 }

@@ -302,6 +302,7 @@ struct LayerWs {
     float* part;     // routed gate_up split-K partials
     float* sh_fpart; // FP4 shared gate_up split-K partials
     float *y, *ysh;
+    int32_t *r_act, *r_off, *r_na, *r_bkt;  // slots recorded by the few-pairs gate_up
 };
 
 LayerWs carve_layer(Carver& c, const moe_layer_desc* d) {
@@ -350,6 +351,10 @@ LayerWs carve_layer(Carver& c, const moe_layer_desc* d) {
         L.sh_fpart = c.take<float>(gate_up_fp4_partials_bytes(dense_job(d->sh13, Ish, H, M)) / sizeof(float));
     L.y = c.take<float>((size_t)P * H);
     L.ysh = sh ? c.take<float>((size_t)M * H) : nullptr;
+    L.r_act = c.take<int32_t>(std::min(E, P));
+    L.r_off = c.take<int32_t>(std::min(E, P) + 1);
+    L.r_na = c.take<int32_t>(1);
+    L.r_bkt = c.take<int32_t>(P);
     return L;
 }
 
@@ -414,6 +419,8 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
         ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
         gu.ids = r.topk_ids;
         gu.a_tok = true;
+        const SlotRecord rec{L.r_act, L.r_off, L.r_na, L.r_bkt};
+        gu.record = &rec;
         // the FP4 shared expert rides along the routed launches
         const ExpertJob sgu = dense_job(d->sh13, Ish, H, M), sdn = dense_job(d->sh2, H, Ish, M);
         const SecondJob s_gu = fp4_shared ? SecondJob{&sgu, L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart} : SecondJob{};
@@ -421,8 +428,12 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
         if (e == hipSuccess)
             e = launch_gate_up_fp4(gu, L.xqt, L.xst, L.hq, L.hs, L.part, stream, s3, shb ? kBf16Down : kBf16None,
                                    s_gu);
+        // down resolves its slots from gate_up's record (one round of loads)
         ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);
-        dn.ids = r.topk_ids;
+        dn.active = rec.act;
+        dn.active_offsets = rec.off;
+        dn.bucket = rec.bkt;
+        dn.count = rec.na;
         if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream, &r, E, s_dn);
         if (e == hipSuccess)
             e = launch_finalize(L.y, r.topk_w, L.ysh, residual, d->gamma, d->eps, M, H, k, out, residual_out,

@@ -76,6 +76,13 @@ hipError_t launch_bucket_quant(int M, int E, int k, const moe_routing& route, co
                                int stage3, hipStream_t stream);
 
 
+// Slots a gate_up resolved from the top-k ids, recorded for the down launch:
+// active experts ([min(E,P)]), their bucket ranges ([min(E,P) + 1]), their
+// count, and the bucket ([P]) in the route step's order.
+struct SlotRecord {
+    int32_t *act, *off, *na, *bkt;
+};
+
 // Expert GEMM jobs.  A routed job covers slots [0, U_max) of the active-expert
 // list; a dense job is one expert over all M rows.
 struct ExpertJob {
@@ -99,6 +106,8 @@ struct ExpertJob {
     // the resolved list or the bucket).
     const int32_t* ids = nullptr;
     bool a_tok = false;
+    const SlotRecord* record = nullptr;  // gate_up with ids: record the resolved slots
+    const int32_t* count = nullptr;      // active list whose entries past *count are stale
 };
 
 // gate_up over FP4 experts.  When the plan splits K, fp32 partials go to
