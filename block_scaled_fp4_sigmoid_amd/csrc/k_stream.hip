@@ -805,7 +805,7 @@ __device__ __forceinline__ float silu_mul(float gt, float up) { return gt / (1.0
 // (routed) or token rows (dense).  Otherwise fp32 partials part[split][row][2I]
 // (already multiplied by the NVFP4 row factor).
 
-constexpr int GMB = 2;           // 16-row weight blocks per wave in gate_up
+constexpr int GMB = 2;           // 16-row weight blocks per wave in gate_up (four: decode 269 -> 296 us)
 constexpr int GCOLS = 32 * GMB;  // output columns per workgroup
 
 // Workgroups [0, n2) take items of a second job J2 of the same format (the
@@ -993,7 +993,11 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_quant(const float* __restri
 // Activations are h rows in bucket order; the output row of bucket position b
 // is its pair id bucket[b] (the token row for a dense expert).
 
-constexpr int kDownMB = 2;  // 16-row weight blocks per wave in down along K
+// 16-row weight blocks per wave in down along K: MXFP4 takes four when the
+// output rows are a multiple of 256 (each activation load serves twice the
+// weight rows; measured: wide down 478 -> 400 us), else two; NVFP4 two (four
+// would spill: its dequantization needs registers).
+constexpr int kDownMBWide = 4, kDownMB = 2;
 
 template <int FMT, int MB>
 __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0, float* __restrict__ y0, int nmain,
@@ -1394,20 +1398,25 @@ hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8
     if (job.K <= 512)  // all of K in one quad: stream along the rows
         return job.w.fmt == MOE_FMT_MXFP4 ? launch_down_rows<kFmtMX>(J, grid_slots(job), y, dr, stream)
                                           : launch_down_rows<kFmtNV>(J, grid_slots(job), y, dr, stream);
-    J.nblk = job.N_out / (64 * kDownMB);
+    const bool mx = job.w.fmt == MOE_FMT_MXFP4;
+    const bool wide = mx && job.N_out % (64 * kDownMBWide) == 0;
+    const int dmb = wide ? kDownMBWide : kDownMB;
+    J.nblk = job.N_out / (64 * dmb);
     const int n1 = grid_slots(job) * J.nblk;
     StreamJob J2 = J;
     int n2 = 0;
     if (fold) {
         const ExpertJob& j2 = *second.job;
         J2 = stream_job(j2, j2.N_out, second.h_q, second.h_s, out_rows_of(j2));
-        J2.nblk = j2.N_out / (64 * kDownMB);
+        J2.nblk = j2.N_out / (64 * dmb);
         n2 = grid_slots(j2) * J2.nblk;
     }
     float* y2 = fold ? second.y : y;
     const int nmain = n1 + n2;
     const dim3 g(nmain + dr.blocks), b(kThreads);
-    if (job.w.fmt == MOE_FMT_MXFP4)
+    if (wide)
+        hipLaunchKernelGGL((k_down<kFmtMX, kDownMBWide>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E, J2, y2, n2);
+    else if (mx)
         hipLaunchKernelGGL((k_down<kFmtMX, kDownMB>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E, J2, y2, n2);
     else
         hipLaunchKernelGGL((k_down<kFmtNV, kDownMB>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E, J2, y2, n2);

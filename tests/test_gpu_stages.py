@@ -184,14 +184,17 @@ def test_gate_up_routed_parity(wfmt, H, neg):
     assert worst < 1e-2, worst
 
 
-@pytest.mark.parametrize("wfmt,I,neg", [(synth.MXFP4, 256, False), (synth.NVFP4, 256, False),
-                                        (synth.MXFP4, 1536, False), (synth.NVFP4, 1536, False),
-                                        (synth.NVFP4, 256, True), (synth.NVFP4, 1536, True),
-                                        (synth.MXFP4, 128, False), (synth.NVFP4, 384, False),
-                                        (synth.MXFP4, 512, False), (synth.NVFP4, 512, True)])
-def test_down_routed_parity(wfmt, I, neg):
-    # I <= 512 (one quad of K steps) streams along the output rows; 1536 along K
-    sh, inp, d, rt, (xq, xs), (xqp, xsp) = _routed_setup(wfmt, seed=5, I=I, neg_scales=neg)
+@pytest.mark.parametrize("wfmt,I,neg,H", [(synth.MXFP4, 256, False, 512), (synth.NVFP4, 256, False, 512),
+                                          (synth.MXFP4, 1536, False, 512), (synth.NVFP4, 1536, False, 512),
+                                          (synth.NVFP4, 256, True, 512), (synth.NVFP4, 1536, True, 512),
+                                          (synth.MXFP4, 128, False, 512), (synth.NVFP4, 384, False, 512),
+                                          (synth.MXFP4, 512, False, 512), (synth.NVFP4, 512, True, 512),
+                                          (synth.MXFP4, 1536, False, 640)])
+def test_down_routed_parity(wfmt, I, neg, H):
+    # I <= 512 (one quad of K steps) streams along the output rows; 1536 along
+    # K (MXFP4: four 16-row blocks per wave when H is a multiple of 256, else
+    # two, as at H = 640)
+    sh, inp, d, rt, (xq, xs), (xqp, xsp) = _routed_setup(wfmt, H=H, seed=5, I=I, neg_scales=neg)
     M, H, E, k, I = sh.M, sh.H, sh.E, sh.k, sh.I
     P = M * k
     hq = torch.empty((P, I), dtype=torch.uint8, device=DEV)
