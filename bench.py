@@ -219,7 +219,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the layer is one "
-              "GPU's share of an expert/tensor-parallel MoE layer and this build has no "
+              "GPU's share of an expert/tensor-parallel MoE layer and the library has no "
               "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 

@@ -6,10 +6,16 @@
 // next norm); README Qwen3.5 slot table, row "hop" (fused residual add +
 // RMSNorm).  t = residual + y_sh + sum_j w_j y_j (fp32, slot order);
 // residual_out = bf16_rne(t); out = bf16_rne(r' * rsqrt(mean(r'^2) + eps) * gamma).
+// Optionally also the next layer's input as MXFP8 (same slot table, row
+// "hop_b": the next input's MXFP8 scales written by the norm's consumer):
+// the one-pass quant rule applied to the bf16 out, codes [M][H] and scales
+// [M][H/32] as the activation quant lays them out.
 //
-// One workgroup per row; each thread owns 8 consecutive columns per 8192.
+// One workgroup per row; each thread owns 8 consecutive columns per 8192
+// (four neighbouring lanes hold one 32-value block).
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "quant_dev.h"
 
 namespace moe {
 
@@ -22,7 +28,9 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restric
                                                           const uint16_t* residual,
                                                           const uint16_t* __restrict__ gamma,
                                                           float eps, int H, int k,
-                                                          uint16_t* out, uint16_t* residual_out) {
+                                                          uint16_t* out, uint16_t* residual_out,
+                                                          uint8_t* __restrict__ out_q,
+                                                          uint8_t* __restrict__ out_s) {
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
     constexpr int kMaxChunks = 2;  // H <= 16384
@@ -112,16 +120,23 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restric
                 ob[i] = f32_to_bf16_rne(o0) | (f32_to_bf16_rne(o1) << 16);
             }
             *reinterpret_cast<v4i*>(out + (size_t)r * H + col) = v4i{(int)ob[0], (int)ob[1], (int)ob[2], (int)ob[3]};
+            if (out_q) {
+                // H % 32 == 0: the four lanes of a block are all in range
+                uint8_t sc;
+                const uint2 codes = quant_bf16x8_lanes4(ob, sc);
+                *reinterpret_cast<uint2*>(out_q + (size_t)r * H + col) = codes;
+                if ((tid & 3) == 0) out_s[(size_t)r * (H / 32) + col / 32] = sc;
+            }
         }
     }
 }
 
 hipError_t launch_finalize(const float* y, const float* topk_w, const float* y_sh,
                            const uint16_t* residual, const uint16_t* gamma, float eps, int M,
-                           int H, int k, uint16_t* out, uint16_t* residual_out,
-                           hipStream_t stream) {
+                           int H, int k, uint16_t* out, uint16_t* residual_out, uint8_t* out_q,
+                           uint8_t* out_s, hipStream_t stream) {
     hipLaunchKernelGGL(k_finalize, dim3(M), dim3(kFinThreads), 0, stream, y, topk_w, y_sh,
-                       residual, gamma, eps, H, k, out, residual_out);
+                       residual, gamma, eps, H, k, out, residual_out, out_q, out_s);
     return hipGetLastError();
 }
 

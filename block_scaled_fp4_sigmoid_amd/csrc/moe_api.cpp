@@ -255,14 +255,24 @@ int moe_expert_down(const moe_weights* w2, const uint8_t* h_q, const uint8_t* h_
     return hip_status(launch_down_fp4(job, h_q, h_s, y, stream));
 }
 
+int moe_finalize_rmsnorm_mxfp8(const float* y, const float* topk_w, const float* y_sh,
+                               const uint16_t* residual, const uint16_t* gamma, float eps, int M, int H,
+                               int k, uint16_t* out, uint16_t* residual_out, uint8_t* out_q, uint8_t* out_s,
+                               hipStream_t stream) {
+    if (!y || !topk_w || !residual || !gamma || !out || M < 1 || H < 1 || k < 1)
+        return MOE_ERR_INVALID_ARG;
+    if ((out_q == nullptr) != (out_s == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (H % 128 != 0 || H > kMaxH || k > kMaxK || M > kMaxM) return MOE_ERR_UNSUPPORTED;
+    if (!(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+    return hip_status(
+        launch_finalize(y, topk_w, y_sh, residual, gamma, eps, M, H, k, out, residual_out, out_q, out_s, stream));
+}
+
 int moe_finalize_rmsnorm(const float* y, const float* topk_w, const float* y_sh,
                          const uint16_t* residual, const uint16_t* gamma, float eps, int M, int H,
                          int k, uint16_t* out, uint16_t* residual_out, hipStream_t stream) {
-    if (!y || !topk_w || !residual || !gamma || !out || M < 1 || H < 1 || k < 1)
-        return MOE_ERR_INVALID_ARG;
-    if (H % 128 != 0 || H > kMaxH || k > kMaxK || M > kMaxM) return MOE_ERR_UNSUPPORTED;
-    if (!(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
-    return hip_status(launch_finalize(y, topk_w, y_sh, residual, gamma, eps, M, H, k, out, residual_out, stream));
+    return moe_finalize_rmsnorm_mxfp8(y, topk_w, y_sh, residual, gamma, eps, M, H, k, out, residual_out, nullptr,
+                                      nullptr, stream);
 }
 
 // ---- the whole layer --------------------------------------------------------
@@ -367,11 +377,13 @@ size_t moe_layer_workspace_bytes(const moe_layer_desc* desc) {
     return c.off;
 }
 
-int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residual,
-              uint16_t* out, uint16_t* residual_out, float* logits_out, int32_t* topk_ids_out,
-              float* topk_w_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residual,
+                        uint16_t* out, uint16_t* residual_out, uint8_t* out_q, uint8_t* out_s,
+                        float* logits_out, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
     if (int st = check_desc(d)) return st;
     if (!x || !residual || !out) return MOE_ERR_INVALID_ARG;
+    if ((out_q == nullptr) != (out_s == nullptr)) return MOE_ERR_INVALID_ARG;
     if (!workspace || !aligned256(workspace)) return MOE_ERR_WORKSPACE;
     Carver c(workspace);
     LayerWs L = carve_layer(c, d);
@@ -437,7 +449,7 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
         if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream, &r, E, s_dn);
         if (e == hipSuccess)
             e = launch_finalize(L.y, r.topk_w, L.ysh, residual, d->gamma, d->eps, M, H, k, out, residual_out,
-                                stream);
+                                out_q, out_s, stream);
         return hip_status(e);
     }
     // Six launches: (router + token-order MXFP8 of x) -> top-k -> route step
@@ -459,8 +471,15 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
     if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream, nullptr, 0, s_dn);
     if (e == hipSuccess)
         e = launch_finalize(L.y, r.topk_w, L.ysh, residual, d->gamma, d->eps, M, H, k, out, residual_out,
-                            stream);
+                            out_q, out_s, stream);
     return hip_status(e);
+}
+
+int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residual,
+              uint16_t* out, uint16_t* residual_out, float* logits_out, int32_t* topk_ids_out,
+              float* topk_w_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return moe_layer_mxfp8_out(d, x, residual, out, residual_out, nullptr, nullptr, logits_out, topk_ids_out,
+                               topk_w_out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -151,7 +151,7 @@ hipError_t launch_down_bf16(const ExpertJob& job, const uint16_t* h, float* y, h
 
 hipError_t launch_finalize(const float* y, const float* topk_w, const float* y_sh,
                            const uint16_t* residual, const uint16_t* gamma, float eps, int M,
-                           int H, int k, uint16_t* out, uint16_t* residual_out,
-                           hipStream_t stream);
+                           int H, int k, uint16_t* out, uint16_t* residual_out, uint8_t* out_q,
+                           uint8_t* out_s, hipStream_t stream);
 
 }  // namespace moe

@@ -62,3 +62,55 @@ __device__ __forceinline__ void quant_block32(const uint16_t* __restrict__ xsrc,
 }
 
 }  // namespace moe
+
+namespace moe {
+
+// The same rule over a block spread across four neighbouring lanes (lanes
+// 4j..4j+3, eight bf16 values each, packed two per word in w): the amax and
+// the special flag are combined over the four lanes.  All four lanes must be
+// active.  Returns the lane's eight codes (first value in the low byte of .x);
+// *scale is the block's scale code.
+__device__ __forceinline__ uint2 quant_bf16x8_lanes4(const uint32_t w[4], uint8_t& scale) {
+    uint32_t amax = 0;
+    int special = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = w[i] & 0x7fffu, hi = (w[i] >> 16) & 0x7fffu;
+        amax = max(amax, max(lo, hi));
+        special |= ((lo & 0x7f80u) == 0x7f80u || (hi & 0x7f80u) == 0x7f80u) ? 1 : 0;
+    }
+#pragma unroll
+    for (int off = 1; off < 4; off <<= 1) {
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, off, 64));
+        special |= __shfl_xor(special, off, 64);
+    }
+    uint32_t out[2];
+    if (special) {
+        scale = 0xff;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            uint32_t o = 0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t wd = w[2 * i + h];
+                o |= (((wd >> 8) & 0x80u) | 0x7fu) << (16 * h);
+                o |= (((wd >> 24) & 0x80u) | 0x7fu) << (16 * h + 8);
+            }
+            out[i] = o;
+        }
+    } else {
+        const int shared = mx_shared_exp(amax << 16);
+        scale = (uint8_t)(shared + 127);
+        const float f = exp2i(-shared);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t c0 = e4m3x2_sat(bf16_to_f32(w[2 * i] & 0xffffu) * f, bf16_to_f32(w[2 * i] >> 16) * f);
+            const uint32_t c1 =
+                e4m3x2_sat(bf16_to_f32(w[2 * i + 1] & 0xffffu) * f, bf16_to_f32(w[2 * i + 1] >> 16) * f);
+            out[i] = c0 | (c1 << 16);
+        }
+    }
+    return uint2{out[0], out[1]};
+}
+
+}  // namespace moe

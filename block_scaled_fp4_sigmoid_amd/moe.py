@@ -24,7 +24,8 @@ EXPORTS = ["moe_status_str", "moe_abi_version", "moe_tile_capacity", "moe_packed
            "moe_pack_fp4", "moe_route_workspace_bytes",
            "moe_route_topk", "moe_quant_act_mxfp8", "moe_gate_up_workspace_bytes",
            "moe_expert_gate_up", "moe_expert_down", "moe_finalize_rmsnorm",
-           "moe_layer_workspace_bytes", "moe_layer"]
+           "moe_finalize_rmsnorm_mxfp8", "moe_layer_workspace_bytes", "moe_layer",
+           "moe_layer_mxfp8_out"]
 
 
 class moe_weights(C.Structure):
@@ -83,10 +84,15 @@ def lib() -> C.CDLL:
                                       i, i, i, i, i, vp, vp]
         L.moe_finalize_rmsnorm.restype = i
         L.moe_finalize_rmsnorm.argtypes = [vp, vp, vp, vp, vp, f, i, i, i, vp, vp, vp]
+        L.moe_finalize_rmsnorm_mxfp8.restype = i
+        L.moe_finalize_rmsnorm_mxfp8.argtypes = [vp, vp, vp, vp, vp, f, i, i, i, vp, vp, vp, vp, vp]
         L.moe_layer_workspace_bytes.restype = sz
         L.moe_layer_workspace_bytes.argtypes = [C.POINTER(moe_layer_desc)]
         L.moe_layer.restype = i
         L.moe_layer.argtypes = [C.POINTER(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_layer_mxfp8_out.restype = i
+        L.moe_layer_mxfp8_out.argtypes = [C.POINTER(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          sz, vp]
         _lib = L
     return _lib
 
@@ -240,12 +246,20 @@ def expert_down(w2: Weights, M, H, I, E, k, y, routing: Optional[Routing] = None
     _check(rc, "moe_expert_down")
 
 
-def finalize_rmsnorm(y, topk_w, y_sh, residual, gamma, eps, out, residual_out=None, stream=None):
+def finalize_rmsnorm(y, topk_w, y_sh, residual, gamma, eps, out, residual_out=None, stream=None,
+                     out_q=None, out_s=None):
+    """moe_finalize_rmsnorm; with out_q/out_s, moe_finalize_rmsnorm_mxfp8."""
     M, H = residual.shape
     k = topk_w.shape[1]
-    rc = lib().moe_finalize_rmsnorm(_p(y), _p(topk_w), _p(y_sh), _p(residual), _p(gamma),
-                                    float(eps), M, H, k, _p(out), _p(residual_out), _stream(stream))
-    _check(rc, "moe_finalize_rmsnorm")
+    if out_q is None and out_s is None:
+        rc = lib().moe_finalize_rmsnorm(_p(y), _p(topk_w), _p(y_sh), _p(residual), _p(gamma),
+                                        float(eps), M, H, k, _p(out), _p(residual_out), _stream(stream))
+        _check(rc, "moe_finalize_rmsnorm")
+        return
+    rc = lib().moe_finalize_rmsnorm_mxfp8(_p(y), _p(topk_w), _p(y_sh), _p(residual), _p(gamma),
+                                          float(eps), M, H, k, _p(out), _p(residual_out), _p(out_q),
+                                          _p(out_s), _stream(stream))
+    _check(rc, "moe_finalize_rmsnorm_mxfp8")
 
 
 class Layer:
@@ -271,8 +285,15 @@ class Layer:
         self._keep = self._keep[:2] + (w13, w2, sh13, sh2) + self._keep[6:]
 
     def __call__(self, x, residual, out, residual_out=None, logits_out=None, topk_ids_out=None,
-                 topk_w_out=None, stream=None):
-        rc = lib().moe_layer(C.byref(self.desc), _p(x), _p(residual), _p(out), _p(residual_out),
-                             _p(logits_out), _p(topk_ids_out), _p(topk_w_out), _p(self.ws),
-                             self.ws.numel(), _stream(stream))
-        _check(rc, "moe_layer")
+                 topk_w_out=None, stream=None, out_q=None, out_s=None):
+        """moe_layer; with out_q/out_s, moe_layer_mxfp8_out."""
+        if out_q is None and out_s is None:
+            rc = lib().moe_layer(C.byref(self.desc), _p(x), _p(residual), _p(out), _p(residual_out),
+                                 _p(logits_out), _p(topk_ids_out), _p(topk_w_out), _p(self.ws),
+                                 self.ws.numel(), _stream(stream))
+            _check(rc, "moe_layer")
+            return
+        rc = lib().moe_layer_mxfp8_out(C.byref(self.desc), _p(x), _p(residual), _p(out), _p(residual_out),
+                                       _p(out_q), _p(out_s), _p(logits_out), _p(topk_ids_out),
+                                       _p(topk_w_out), _p(self.ws), self.ws.numel(), _stream(stream))
+        _check(rc, "moe_layer_mxfp8_out")

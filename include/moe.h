@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 enum moe_status {
     MOE_OK = 0,
@@ -254,6 +254,24 @@ int moe_finalize_rmsnorm(const float *y, const float *topk_w, const float *y_sh,
                          hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_finalize_rmsnorm_mxfp8 — moe_finalize_rmsnorm that also writes the next
+ * layer's input as MXFP8.
+ *   Pages: README DeepSeek-V4.1 slot table, row "MoE all-reduce + mHC post +
+ *   next norm (hop_b)" (the norm's consumer writes the next input's MXFP8
+ *   scales so the next GEMM runs on its low-latency path) and row "two_shot"
+ *   (the post quantizes the next input to MXFP8); row "Shared expert gate_up
+ *   (shared_ll)" for the one-pass MXFP8 quant.
+ * Arguments as moe_finalize_rmsnorm, plus out_q: uint8 [M, H] E4M3 codes and
+ * out_s: uint8 [M, H/32] E8M0 scale codes, the quant of `out` exactly as
+ * moe_quant_act_mxfp8 would produce it from `out` (both NULL: no quant, the
+ * same as moe_finalize_rmsnorm; one NULL: MOE_ERR_INVALID_ARG).  Caller-owned
+ * device buffers, written in full. */
+int moe_finalize_rmsnorm_mxfp8(const float *y, const float *topk_w, const float *y_sh,
+                               const uint16_t *residual, const uint16_t *gamma, float eps, int M,
+                               int H, int k, uint16_t *out, uint16_t *residual_out, uint8_t *out_q,
+                               uint8_t *out_s, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_layer — the whole layer (all steps above) in one call on one stream.
  *   Pages: README Qwen3.5 slot table, row "mkm" (top-k, FC1, SwiGLU, requant
  *   and FC2 as one unit); README "Design" (built at load, nothing allocated
@@ -268,6 +286,14 @@ size_t moe_layer_workspace_bytes(const moe_layer_desc *desc);
 int moe_layer(const moe_layer_desc *desc, const uint16_t *x, const uint16_t *residual,
               uint16_t *out, uint16_t *residual_out, float *logits_out, int32_t *topk_ids_out,
               float *topk_w_out, void *workspace, size_t workspace_bytes, hipStream_t stream);
+/* moe_layer_mxfp8_out — moe_layer whose finalize also writes the next layer's
+ * input as MXFP8 (out_q uint8 [M, H], out_s uint8 [M, H/32], as in
+ * moe_finalize_rmsnorm_mxfp8; both NULL is moe_layer, one NULL is
+ * MOE_ERR_INVALID_ARG).  Same launches as moe_layer. */
+int moe_layer_mxfp8_out(const moe_layer_desc *desc, const uint16_t *x, const uint16_t *residual,
+                        uint16_t *out, uint16_t *residual_out, uint8_t *out_q, uint8_t *out_s,
+                        float *logits_out, int32_t *topk_ids_out, float *topk_w_out, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

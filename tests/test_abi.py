@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert moe.abi_version() == 4
+    assert moe.abi_version() == 5
     for rc in range(5):
         assert len(moe.status_str(rc)) > 0
     assert "unknown" in moe.status_str(99)
@@ -108,6 +108,17 @@ def test_calls_refuse_before_enqueueing(L):
     assert rc == moe.MOE_ERR_WORKSPACE                     # misaligned
     rc = L.moe_layer(C.byref(d), 0x1000, 0x1000, 0x1000, None, None, None, None, 0x1000, 16, None)
     assert rc == moe.MOE_ERR_WORKSPACE                     # too small
+    # the MXFP8 next-input outputs come as a pair
+    rc = L.moe_layer_mxfp8_out(C.byref(d), 0x1000, 0x1000, 0x1000, None, 0x1000, None, None, None, None,
+                               0x1000, 1 << 30, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+    rc = L.moe_layer_mxfp8_out(C.byref(d), 0x1000, 0x1000, 0x1000, None, None, None, None, None, None,
+                               0x1000, 16, None)
+    assert rc == moe.MOE_ERR_WORKSPACE
+    fin = [0x1000, 0x1000, None, 0x1000, 0x1000, 1e-6, 4, 256, 2, 0x1000, None]
+    assert L.moe_finalize_rmsnorm_mxfp8(*fin, None, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_finalize_rmsnorm_mxfp8(*fin[:7], 200, *fin[8:], 0x1000, 0x1000, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_finalize_rmsnorm_mxfp8(*fin[:5], -1.0, *fin[6:], 0x1000, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_quant_act_mxfp8(None, 4, 64, None, 0, 0x1000, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_quant_act_mxfp8(0x1000, 4, 48, None, 0, 0x1000, 0x1000, None) == moe.MOE_ERR_UNSUPPORTED
     r = moe.moe_routing()  # bucket missing

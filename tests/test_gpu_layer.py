@@ -7,6 +7,7 @@ import pytest
 import torch
 
 from block_scaled_fp4_sigmoid_amd import moe, staging, synth
+from oracle import oracle as orc
 from tests.parity import (DEV, MAX_ABS_MAX, REL_L2_MAX, LayerRun, compare_layer, np_of,
                           sample_rows)
 
@@ -138,3 +139,30 @@ def test_graph_replay_equals_eager():
             assert np.array_equal(h[k], eager[k]), (i, k)
         # eager work between replays
         LayerRun(d, layer=run.layer)
+
+
+@pytest.mark.parametrize("big", [False, True])
+def test_layer_mxfp8_next_input(big):
+    """moe_layer_mxfp8_out: out, residual_out and routing equal moe_layer's
+    bytes, and its MXFP8 output equals the one-pass quant of that out."""
+    if big:   # above 256 (row, expert) pairs: the bucketed launch sequence
+        sh = synth.custom_shape(M=40, H=1024, E=32, k=8, I=256, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=128)
+    else:
+        sh = synth.custom_shape(M=9, H=512, E=64, k=6, I=384, wfmt=synth.MXFP4, sfmt=synth.MXFP4, I_sh=128)
+    inp = synth.make_inputs(sh, seed=77 + big, pool_rows=2048)
+    d = staging.to_device(inp, DEV)
+    print(f"[layer mxfp8 out] {sh.name}", flush=True)
+    run = LayerRun(d)
+    ref = run.host()
+    q = torch.full((sh.M, sh.H), 0x5a, dtype=torch.uint8, device=DEV)
+    s = torch.full((sh.M, sh.H // 32), 0x5a, dtype=torch.uint8, device=DEV)
+    run.out.zero_()
+    run.res.zero_()
+    run.layer(d.x, d.x, run.out, run.res, run.logits, run.ids, run.w, out_q=q, out_s=s)
+    torch.cuda.synchronize()
+    h = run.host()
+    for key in ref:
+        assert np.array_equal(h[key], ref[key]), key
+    rq, rs = orc.mxfp8_quant_bf16(h["out"])
+    assert np.array_equal(np_of(s), rs)
+    assert np.array_equal(np_of(q), rq)

@@ -334,3 +334,45 @@ def test_pack_fp4_layout(fmt, N, K):
             i, gg = l % 16, l // 16
             want = sc[e, 16 * rb + i, 8 * (4 * q + u) + 2 * gg + h] if 4 * q + u < S else 0
             assert ps[e, rb, q, l, 2 * u + h] == want
+
+
+@pytest.mark.parametrize("M,H", [(19, 2048 + 128), (3, 8192 + 384)])
+def test_finalize_mxfp8_next_input(M, H):
+    """The finalize's MXFP8 of its own bf16 output equals the one-pass quant of
+    that output byte for byte; out and residual_out equal the plain call's."""
+    rng = np.random.default_rng(40 + M)
+    k = 5
+    y = rng.standard_normal((M * k, H)).astype(np.float32)
+    w = rng.random((M, k)).astype(np.float32)
+    ysh = rng.standard_normal((M, H)).astype(np.float32)
+    r32 = rng.standard_normal((M, H)).astype(np.float32)
+    r32[1, 40] = np.inf      # the whole normed row turns 0 / NaN: the NaN block's scale is 0xFF
+    res = synth._bf16_trunc(r32)
+    g32 = (1 + 0.1 * rng.standard_normal(H)).astype(np.float32)
+    g32[:32] = 0.0           # an all-zero block
+    g32[64:96] *= 2.0 ** 20
+    gamma = synth._bf16_trunc(g32)
+    t = lambda a: torch.from_numpy(a).to(DEV)
+    out = torch.empty((M, H), dtype=torch.int16, device=DEV)
+    ro = torch.empty((M, H), dtype=torch.int16, device=DEV)
+    out2, ro2 = torch.empty_like(out), torch.empty_like(ro)
+    q = torch.full((M, H), 0x5a, dtype=torch.uint8, device=DEV)
+    s = torch.full((M, H // 32), 0x5a, dtype=torch.uint8, device=DEV)
+    args = (t(y), t(w), t(ysh), t(res.view(np.int16)), t(gamma.view(np.int16)), 1e-6)
+    moe.finalize_rmsnorm(*args, out, ro)
+    moe.finalize_rmsnorm(*args, out2, ro2, out_q=q, out_s=s)
+    torch.cuda.synchronize()
+    go = np_of(out2).view(np.uint16)
+    assert np.array_equal(go, np_of(out).view(np.uint16))
+    assert np.array_equal(np_of(ro2), np_of(ro))
+    rq, rs = orc.mxfp8_quant_bf16(go)
+    assert np.array_equal(np_of(s), rs)
+    assert np.array_equal(np_of(q), rq)
+    assert (rs[1] == 0xFF).any()
+    # E4M3 keeps three mantissa bits: every normal element lies within 2^-4 of
+    # its value relative, so the dequantized row is that close to the oracle's
+    deq = orc.mxfp8_dequant(np_of(q), np_of(s))
+    for r in (0, M - 1):
+        o64 = orc.finalize_row(y[r * k:(r + 1) * k].astype(np.float64), w[r], ysh[r].astype(np.float64),
+                               res[r], gamma, 1e-6)[0]
+        assert rel_l2(deq[r], o64) < 2.0 ** -4
