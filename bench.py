@@ -8,7 +8,11 @@ Prints ONE JSON line on stdout:
                        with HIP events: algorithmic bytes per launch / mean
                        duration, against the 8 TB/s HBM peak;
   cpu_baseline       — the oracle (plain fp64 C) timed on the host cores on
-                       the same inputs (a baseline only).
+                       the same inputs (a baseline only);
+  stream_read_GBps   — a 4 GiB streaming read in the same run (the practical
+                       HBM read rate); fractions are given against it and
+                       against the 8 TB/s peak;
+  *_windows          — the K timed steps split in 5 windows: median, p10, p90.
 Inputs are seeded synthetic data already resident in HBM; each step reads a
 different copy of the weights (rotation over enough copies that no step
 finds the previous step's weights in the 256 MB Infinity Cache).
@@ -162,19 +166,43 @@ def stored_traffic(workload):
         return None
 
 
-def timed(fn, steps, warmup, stream):
+def timed_units(units, stream, windows=5):
+    """Times a sequence of launches given as (callable, steps it covers), with
+    HIP events on `stream`: one event before the first unit and one after each
+    of `windows` groups of consecutive units.  Returns (ms per step over all of
+    them, [ms per step of each window])."""
+    import torch
+    nw = max(1, min(windows, len(units)))
+    cut = [len(units) * w // nw for w in range(nw + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in cut]
+    ev[0].record(stream)
+    w = 1
+    for u, (fn, _) in enumerate(units):
+        fn()
+        if u + 1 == cut[w]:
+            ev[w].record(stream)
+            w += 1
+    torch.cuda.synchronize()
+    steps = [sum(n for _, n in units[cut[j]:cut[j + 1]]) for j in range(nw)]
+    per = [ev[j].elapsed_time(ev[j + 1]) / steps[j] for j in range(nw)]
+    return ev[0].elapsed_time(ev[-1]) / sum(steps), per
+
+
+def timed(fn, steps, warmup, stream, windows=5):
+    """fn(i) for i < warmup untimed, then exactly `steps` calls timed in
+    `windows` windows; returns (ms per step, [ms per step of each window])."""
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        fn(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps  # ms
+    return timed_units([((lambda i=i: fn(i)), 1) for i in range(steps)], stream, windows)
+
+
+def window_stats(per):
+    """median, p10 and p90 (us per step) over the windows."""
+    a = np.asarray(per) * 1e3
+    return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "windows": len(a)}
 
 
 def cpu_baseline(inp, logits):
@@ -224,7 +252,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from block_scaled_fp4_sigmoid_amd import moe, staging, synth
+    from block_scaled_fp4_sigmoid_amd import moe, probe, staging, synth
 
     dev = "cuda"
     name = args.workload
@@ -279,7 +307,7 @@ def main():
     def step_eager(i):
         layers[i % copies](d.x, d.x, out, res)
 
-    ms_eager = timed(step_eager, args.steps, args.warmup, stream)
+    ms_eager, win_eager = timed(step_eager, args.steps, args.warmup, stream)
     log(f"[bench] eager: {ms_eager * 1e3:.2f} us/step")
 
     ms_graph = ms_chain = chain = None
@@ -296,7 +324,7 @@ def main():
                     layers[c](d.x, d.x, out, res, stream=gs)
                 graphs.append(g)
         torch.cuda.synchronize()
-        ms_graph = timed(lambda i: graphs[i % copies].replay(), args.steps, args.warmup, stream)
+        ms_graph, _ = timed(lambda i: graphs[i % copies].replay(), args.steps, args.warmup, stream)
         log(f"[bench] graph replay, one layer step per graph: {ms_graph * 1e3:.2f} us/step")
         # A decode step's graph holds every layer back to back: a chain of G
         # consecutive layer steps (rotating the weight copies, G a multiple of
@@ -310,19 +338,16 @@ def main():
                     layers[j % copies](d.x, d.x, out, res, stream=gs)
         torch.cuda.synchronize()
 
-        def run_chain(_):
-            full, rem = divmod(args.steps, chain)
-            for _ in range(full):
-                gchain.replay()
-            for j in range(rem):
-                graphs[j % copies].replay()
-
-        ms_chain = timed(run_chain, 1, 1, stream) / args.steps
+        full, rem = divmod(args.steps, chain)
+        units = [(gchain.replay, chain)] * full + [(graphs[j % copies].replay, 1) for j in range(rem)]
+        gchain.replay()  # warm
+        torch.cuda.synchronize()
+        ms_chain, win_chain = timed_units(units, stream)
         log(f"[bench] graph replay, {chain} layer steps per graph: {ms_chain * 1e3:.2f} us/step")
     # the layer step as it runs fastest: eager launches or the chained graph
-    ms, timing = ms_eager, "eager launches"
+    ms, timing, win = ms_eager, "eager launches", win_eager
     if ms_chain is not None and ms_chain < ms_eager:
-        ms, timing = ms_chain, "graph of %d consecutive layer steps, replayed" % chain
+        ms, timing, win = ms_chain, "graph of %d consecutive layer steps, replayed" % chain, win_chain
 
     # dominant kernel alone: routed gate_up, timed with HIP events on its stream
     rt = moe.Routing(s.M, s.E, s.k, dev)
@@ -341,16 +366,29 @@ def main():
         moe.expert_gate_up(w13s[i % copies], s.M, s.H, s.I, s.E, s.k, routing=rt, a_q=xq, a_s=xs,
                            h_q=hq, h_s=hs, ws=gu_ws)
 
-    ms_gu = timed(gate_up, args.steps, args.warmup, stream)
+    ms_gu, win_gu = timed(gate_up, args.steps, args.warmup, stream)
     gu_gbps = bm["gate_up_launch"] / (ms_gu * 1e-3) / 1e9
     log(f"[bench] routed gate_up alone: {ms_gu * 1e3:.2f} us, {gu_gbps:.0f} GB/s")
 
-    # plain device copy for the achievable stream rate (context)
+    # calibration: a streaming read of 4 GiB (the practical HBM read rate) and
+    # a plain 1 GiB device copy (context)
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(1, dtype=torch.int32, device=dev)
+    read_gbps, read_row = 0.0, 0
+    for row_bytes in (1152, 3584):  # the GEMMs' row pattern at two row lengths; the faster counts
+        nb = buf.numel() // row_bytes * row_bytes
+        ms_read, _ = timed(lambda i: probe.stream_read(buf, row_bytes, sink), 10, 2, stream)
+        if nb / (ms_read * 1e-3) / 1e9 > read_gbps:
+            read_gbps, read_row = nb / (ms_read * 1e-3) / 1e9, row_bytes
+    del buf
     buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     buf2 = torch.empty_like(buf)
-    ms_copy = timed(lambda i: buf2.copy_(buf), 20, 3, stream)
+    ms_copy, _ = timed(lambda i: buf2.copy_(buf), 20, 3, stream)
     copy_gbps = 2 * buf.numel() / (ms_copy * 1e-3) / 1e9
     del buf, buf2
+    log(f"[bench] stream read 4 GiB: {read_gbps:.0f} GB/s (rows of {read_row} B); "
+        f"device copy 1 GiB: {copy_gbps:.0f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -377,6 +415,7 @@ def main():
         "us_per_step_graph": None if ms_graph is None else round(ms_graph * 1e3, 2),
         "us_per_step_graph_chain": None if ms_chain is None else round(ms_chain * 1e3, 2),
         "timing": timing,
+        "us_per_step_windows": window_stats(win),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -387,12 +426,16 @@ def main():
                    "shared": synth.FMT_NAMES[s.sfmt], "unique_experts": U,
                    "weight_copies": copies, "parallelism": "single GPU"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "stream_read_GBps": round(read_gbps, 1),
+        "frac_of_stream_read": round(value / read_gbps, 4),
         "total_alg_GBps": round(bm["total"] / (ms * 1e-3) / 1e9, 2),
         "copy_GBps": round(copy_gbps, 1),
         "roofline": {"kernel": "k_gate_up_fp4 (routed)", "bound": "hbm",
                      "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(name),
                      "us_per_launch": round(ms_gu * 1e3, 2),
+                     "us_per_launch_windows": window_stats(win_gu),
+                     "frac_of_stream_read": round(gu_gbps / read_gbps, 4),
                      "alg_bytes_per_launch": bm["gate_up_launch"]},
         "cpu_baseline": cpu,
     }

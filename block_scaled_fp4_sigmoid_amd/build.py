@@ -1,4 +1,5 @@
-"""Builds the HIP library libmoe_mi355.so for gfx950 (in-tree, with hipcc).
+"""Builds the HIP library libmoe_mi355.so for gfx950 (in-tree, with hipcc),
+and the measurement helper libmoe_probe_mi355.so (include/moe_probe.h).
 
 Cross-compiles without a GPU.  Every HIP translation unit gets
 ``-Xclang -target-feature -Xclang -packed-fp32-ops`` so the compiler emits no
@@ -14,6 +15,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_mi355.so")
+PROBE_LIB = os.path.join(HERE, "libmoe_probe_mi355.so")
+PROBE_SOURCES = ["k_probe.hip"]
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["k_route.hip", "k_quant.hip", "k_pack.hip", "k_stream.hip", "k_dense_bf16.hip",
            "k_finalize.hip", "moe_api.cpp"]
@@ -32,18 +35,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -12,8 +12,8 @@ from block_scaled_fp4_sigmoid_amd import moe
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared():
-    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+def _declared(header="moe.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
@@ -30,6 +30,24 @@ def test_every_declared_symbol_is_exported(L):
     assert set(declared) == set(moe.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
+
+
+def test_probe_library_exports():
+    from block_scaled_fp4_sigmoid_amd import probe
+    if not os.path.exists(probe.LIB_PATH):
+        pytest.fail("libmoe_probe_mi355.so is not built (run __graft_entry__.build())")
+    declared = _declared("moe_probe.h")
+    assert set(declared) == set(probe.EXPORTS)
+    P = probe.lib()
+    for name in declared:
+        assert hasattr(P, name), name
+    # refusals return before any HIP call
+    assert P.moe_probe_stream_read(None, 1152, 1152, 0x1000, None) == 1
+    assert P.moe_probe_stream_read(0x1000, 1152, 1152, None, None) == 1
+    assert P.moe_probe_stream_read(0x1000, 1152, 100, 0x1000, None) == 1    # row not a multiple of 64
+    assert P.moe_probe_stream_read(0x1000, 1000, 1152, 0x1000, None) == 1   # bytes not whole rows
+    assert P.moe_probe_stream_read(0x1008, 1152, 1152, 0x1000, None) == 1   # misaligned
+    assert P.moe_probe_stream_read(0x1000, 0, 1152, 0x1000, None) == 1
 
 
 def test_version_and_status_strings(L):
