@@ -134,6 +134,7 @@ class Shape:
     bias: str  # "none" | "normal:<std>" | "zipf:<s>"
     eps: float = 1e-6
     desc: str = ""
+    swiglu_limit: float = 0.0  # clamped SwiGLU of every expert; 0: unclamped
 
 
 # The five workloads the layer is measured on (pages: DeepSeek-V4.1 verify
@@ -162,12 +163,15 @@ WORKLOAD_ORDER = list(WORKLOADS)
 
 
 def custom_shape(M, H, E, k, I, wfmt=MXFP4, sfmt=NONE, I_sh=None, routed_scale=1.0,
-                 bias="none", eps=1e-6, name=None) -> Shape:
+                 bias="none", eps=1e-6, name=None, swiglu_limit=0.0) -> Shape:
     I_sh = I if I_sh is None else I_sh
     if sfmt == NONE:
         I_sh = 0
     name = name or f"custom-m{M}-h{H}-e{E}-k{k}-i{I}-{FMT_NAMES[wfmt]}-sh{FMT_NAMES[sfmt]}"
-    return Shape(name, M, H, E, k, I, wfmt, sfmt, I_sh, float(routed_scale), bias, eps)
+    if swiglu_limit:
+        name += f"-clamp{swiglu_limit:g}"
+    return Shape(name, M, H, E, k, I, wfmt, sfmt, I_sh, float(routed_scale), bias, eps,
+                 swiglu_limit=float(swiglu_limit))
 
 
 @dataclass

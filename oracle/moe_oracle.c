@@ -341,11 +341,30 @@ void orc_route(const float *logits, const float *bias, int M, int E, int k, doub
 }
 
 /* ------------------------------------------------------------------------ */
+/* SwiGLU of one gate/up pair.  h = silu(g) * u with silu(g) = g / (1 + e^-g)
+ * (README Qwen3.5 slot table, row "mkm": FC1, SwiGLU, FC2).  With limit > 0 it
+ * is the clamped SwiGLU (README DeepSeek-V4.1 slot table, row "Shared expert
+ * gate_up (shared_ll)": SGLang's clamped SwiGLU); the pages give neither the
+ * limit nor the clamp's form, so the reading is: the gate is capped from
+ * above at limit and the up projection clamped to [-limit, limit], before the
+ * product.  limit <= 0: unclamped. */
+double orc_swiglu(double g, double u, double limit)
+{
+    if (limit > 0.0) {
+        if (g > limit)
+            g = limit;
+        if (u > limit)
+            u = limit;
+        if (u < -limit)
+            u = -limit;
+    }
+    return (g / (1.0 + exp(-g))) * u;
+}
+
 /* One expert's gate_up + SwiGLU on one activation row a[H] (already the
  * dequantized MXFP8 values).  Readings: rows [0, I) of W13 are the gate, rows
- * [I, 2I) the up projection; h = silu(g) * u with silu(g) = g / (1 + e^-g),
- * unclamped (README Qwen3.5 slot table, row "mkm": FC1, SwiGLU, FC2). */
-void orc_gate_up(const orc_mat *w13, int H, int I, const double *a, double *h)
+ * [I, 2I) the up projection; h[n] = orc_swiglu(g[n], u[n], limit). */
+void orc_gate_up(const orc_mat *w13, int H, int I, const double *a, double limit, double *h)
 {
     double *wrow = (double *)malloc(sizeof(double) * H);
     for (int n = 0; n < I; ++n) {
@@ -356,7 +375,7 @@ void orc_gate_up(const orc_mat *w13, int H, int I, const double *a, double *h)
         orc_mat_row(w13, H, I + n, wrow);
         for (int c = 0; c < H; ++c)
             u += a[c] * wrow[c];
-        h[n] = (g / (1.0 + exp(-g))) * u;
+        h[n] = orc_swiglu(g, u, limit);
     }
     free(wrow);
 }
@@ -365,12 +384,12 @@ void orc_gate_up(const orc_mat *w13, int H, int I, const double *a, double *h)
  * expert beside the NVFP4 routed experts).  Reading: the bf16 hidden row is
  * used as is (not quantized), products summed in fp64; the caller rounds h to
  * bf16 before the down projection. */
-void orc_gate_up_bf16(const orc_mat *w13, int H, int I, const uint16_t *x_row, double *h)
+void orc_gate_up_bf16(const orc_mat *w13, int H, int I, const uint16_t *x_row, double limit, double *h)
 {
     double *a = (double *)malloc(sizeof(double) * H);
     for (int c = 0; c < H; ++c)
         a[c] = orc_bf16_value(x_row[c]);
-    orc_gate_up(w13, H, I, a, h);
+    orc_gate_up(w13, H, I, a, limit, h);
     free(a);
 }
 
@@ -450,13 +469,13 @@ typedef struct {
  * I (the pages requantize the SwiGLU output before FC2: README Qwen3.5 slot
  * table, row "mkm"; PR #33 appended table, row "shared act quant"), down. */
 static void expert_fp4(const orc_mat *w13, const orc_mat *w2, int H, int I, const double *a,
-                       double *y, uint8_t *hq, uint8_t *hs)
+                       double limit, double *y, uint8_t *hq, uint8_t *hs)
 {
     double *h = (double *)malloc(sizeof(double) * I);
     double *hd = (double *)malloc(sizeof(double) * I);
     uint8_t *q = (uint8_t *)malloc(I);
     uint8_t *s = (uint8_t *)malloc(I / 32);
-    orc_gate_up(w13, H, I, a, h);
+    orc_gate_up(w13, H, I, a, limit, h);
     orc_mxfp8_quant_f64(h, 1, I, q, s);
     orc_mxfp8_dequant(q, s, I, hd);
     orc_down(w2, H, I, hd, y);
@@ -506,7 +525,7 @@ static void expert_item(rows_job *J, int i, int j)
     const double *a = J->a + (size_t)i * H;
     if (j < k) {
         int e = J->ids[(size_t)i * k + j];
-        expert_fp4(&L->w13[e], &L->w2[e], H, I, a, J->y + ((size_t)i * k + j) * H,
+        expert_fp4(&L->w13[e], &L->w2[e], H, I, a, L->swiglu_limit, J->y + ((size_t)i * k + j) * H,
                    J->hq ? J->hq + ((size_t)i * k + j) * I : NULL,
                    J->hs ? J->hs + ((size_t)i * k + j) * (I / 32) : NULL);
         return;
@@ -514,13 +533,13 @@ static void expert_item(rows_job *J, int i, int j)
     double *ysh = J->ysh + (size_t)i * H;
     if (L->sfmt == ORC_BF16) {
         double *h = (double *)malloc(sizeof(double) * L->I_sh);
-        orc_gate_up_bf16(&L->sh13, H, L->I_sh, L->x + (size_t)r * H, h);
+        orc_gate_up_bf16(&L->sh13, H, L->I_sh, L->x + (size_t)r * H, L->swiglu_limit, h);
         for (int n = 0; n < L->I_sh; ++n)
             h[n] = orc_bf16_value(orc_bf16_rne(h[n]));
         orc_down(&L->sh2, H, L->I_sh, h, ysh);
         free(h);
     } else {
-        expert_fp4(&L->sh13, &L->sh2, H, L->I_sh, a, ysh, NULL, NULL);
+        expert_fp4(&L->sh13, &L->sh2, H, L->I_sh, a, L->swiglu_limit, ysh, NULL, NULL);
     }
 }
 

@@ -59,6 +59,7 @@ typedef struct {
     const orc_mat *w13;        /* E entries */
     const orc_mat *w2;         /* E entries */
     orc_mat sh13, sh2;         /* shared expert (fmt ORC_NONE when absent) */
+    double swiglu_limit;       /* clamped SwiGLU of every expert (orc_swiglu); <= 0: none */
 } orc_layer;
 
 /* ---- formats ---- */
@@ -86,8 +87,9 @@ void orc_route(const float *logits, const float *bias, int M, int E, int k, doub
                int32_t *num_tiles);
 
 /* ---- one expert on one activation row ---- */
-void orc_gate_up(const orc_mat *w13, int H, int I, const double *a, double *h);
-void orc_gate_up_bf16(const orc_mat *w13, int H, int I, const uint16_t *x_row, double *h);
+double orc_swiglu(double g, double u, double limit);
+void orc_gate_up(const orc_mat *w13, int H, int I, const double *a, double limit, double *h);
+void orc_gate_up_bf16(const orc_mat *w13, int H, int I, const uint16_t *x_row, double limit, double *h);
 void orc_down(const orc_mat *w2, int H, int I, const double *h, double *y);
 
 /* ---- finalize ---- */

@@ -45,7 +45,7 @@ class orc_layer(C.Structure):
                 ("x", C.c_void_p), ("residual", C.c_void_p), ("gamma", C.c_void_p),
                 ("Wr", C.c_void_p), ("bias", C.c_void_p),
                 ("w13", C.POINTER(orc_mat)), ("w2", C.POINTER(orc_mat)),
-                ("sh13", orc_mat), ("sh2", orc_mat)]
+                ("sh13", orc_mat), ("sh2", orc_mat), ("swiglu_limit", C.c_double)]
 
 
 _lib = None
@@ -78,8 +78,10 @@ def lib():
         L.orc_router_logits.argtypes = [vp, vp, C.c_int, C.c_int, C.c_int, vp]
         L.orc_topk_row.argtypes = [vp, vp, C.c_int, C.c_int, d, vp, vp, vp]
         L.orc_route.argtypes = [vp, vp, C.c_int, C.c_int, C.c_int, d] + [vp] * 8
-        L.orc_gate_up.argtypes = [C.POINTER(orc_mat), C.c_int, C.c_int, vp, vp]
-        L.orc_gate_up_bf16.argtypes = [C.POINTER(orc_mat), C.c_int, C.c_int, vp, vp]
+        L.orc_gate_up.argtypes = [C.POINTER(orc_mat), C.c_int, C.c_int, vp, d, vp]
+        L.orc_gate_up_bf16.argtypes = [C.POINTER(orc_mat), C.c_int, C.c_int, vp, d, vp]
+        L.orc_swiglu.restype = d
+        L.orc_swiglu.argtypes = [d, d, d]
         L.orc_down.argtypes = [C.POINTER(orc_mat), C.c_int, C.c_int, vp, vp]
         L.orc_finalize_row.argtypes = [C.c_int, C.c_int, vp, vp, vp, vp, vp, d, vp, vp, vp]
         L.orc_moe_rows.argtypes = [C.POINTER(orc_layer), vp, vp, C.c_int, C.c_int] + [vp] * 9
@@ -246,19 +248,23 @@ def topk_row(logits_row, bias, k, scale):
 
 # ---- experts / finalize ----------------------------------------------------
 
-def gate_up(m: Mat, H: int, I: int, a: np.ndarray) -> np.ndarray:
+def swiglu(g: float, u: float, limit: float = 0.0) -> float:
+    return float(lib().orc_swiglu(float(g), float(u), float(limit)))
+
+
+def gate_up(m: Mat, H: int, I: int, a: np.ndarray, limit: float = 0.0) -> np.ndarray:
     a = np.ascontiguousarray(a, np.float64)
     h = np.empty(I, np.float64)
     cm = m.c()
-    lib().orc_gate_up(C.byref(cm), H, I, _p(a), _p(h))
+    lib().orc_gate_up(C.byref(cm), H, I, _p(a), float(limit), _p(h))
     return h
 
 
-def gate_up_bf16(m: Mat, H: int, I: int, x_row: np.ndarray) -> np.ndarray:
+def gate_up_bf16(m: Mat, H: int, I: int, x_row: np.ndarray, limit: float = 0.0) -> np.ndarray:
     x_row = np.ascontiguousarray(x_row, np.uint16)
     h = np.empty(I, np.float64)
     cm = m.c()
-    lib().orc_gate_up_bf16(C.byref(cm), H, I, _p(x_row), _p(h))
+    lib().orc_gate_up_bf16(C.byref(cm), H, I, _p(x_row), float(limit), _p(h))
     return h
 
 
@@ -316,7 +322,7 @@ class Layer:
         self.c = orc_layer(sh.M, sh.H, sh.E, sh.k, sh.I, sh.I_sh, sh.wfmt, sh.sfmt,
                            float(sh.routed_scale), float(sh.eps), _p(self.x), _p(self.x),
                            _p(self.gamma), _p(self.Wr), _p(self.bias), arr13, arr2,
-                           self.sh13.c(), self.sh2.c())
+                           self.sh13.c(), self.sh2.c(), float(sh.swiglu_limit))
 
     def rows(self, rows, logits=None, nthreads=0, want_h=False):
         sh = self.inp.shape

@@ -51,11 +51,17 @@ def mx_dequant(q, s):
     return e4m3v(q) * np.repeat(np.exp2(s.astype(np.float64) - 127), 32, axis=-1)
 
 
-def textbook_expert(orc, m13, m2, I, a):
+def clamp_gu(g, u, limit):
+    """The clamped SwiGLU's inputs: gate capped from above, up clamped both ways."""
+    if limit > 0:
+        g, u = np.minimum(g, limit), np.clip(u, -limit, limit)
+    return g, u
+
+
+def textbook_expert(orc, m13, m2, I, a, limit=0.0):
     """a: dequantized activation [H]; returns y [H] with the layer's requant."""
     W13, W2 = dense(m13), dense(m2)
-    g = W13[:I] @ a
-    u = W13[I:] @ a
+    g, u = clamp_gu(W13[:I] @ a, W13[I:] @ a, limit)
     h = g / (1 + np.exp(-g)) * u
     q, s = orc.mxfp8_quant_f64(h[None, :])
     return W2 @ mx_dequant(q, s)[0]
@@ -92,18 +98,21 @@ def test_single_expert_is_textbook_swiglu_mlp(orc, wfmt):
         assert np.allclose(res["out64"][r], out, rtol=1e-12, atol=1e-14)
 
 
-@pytest.mark.parametrize("wfmt,sfmt", [(synth.MXFP4, synth.NONE), (synth.NVFP4, synth.BF16),
-                                       (synth.MXFP4, synth.MXFP4)])
-def test_sparse_routing_equals_dense_zero_weighted_mixture(orc, wfmt, sfmt):
+@pytest.mark.parametrize("wfmt,sfmt,limit", [(synth.MXFP4, synth.NONE, 0.0), (synth.NVFP4, synth.BF16, 0.0),
+                                             (synth.MXFP4, synth.MXFP4, 0.0), (synth.NVFP4, synth.BF16, 0.06),
+                                             (synth.MXFP4, synth.MXFP4, 0.05)])
+def test_sparse_routing_equals_dense_zero_weighted_mixture(orc, wfmt, sfmt, limit):
+    """Also with the clamped SwiGLU (limit > 0, small enough that most gate and
+    up values of these rows cross it) in the routed and the shared experts."""
     sh = synth.custom_shape(M=4, H=128, E=6, k=3, I=64, wfmt=wfmt, sfmt=sfmt, I_sh=96,
-                            routed_scale=2.5, bias="normal:0.05")
+                            routed_scale=2.5, bias="normal:0.05", swiglu_limit=limit)
     inp, L = _layer(orc, sh, 6)
     inp = synth.vary_globals(inp, 9)
     L = orc.Layer(inp)
     res = L.rows(np.arange(sh.M))
     for r in range(sh.M):
         a = _act(orc, inp, r)
-        ys = np.stack([textbook_expert(orc, inp.w13.expert(e), inp.w2.expert(e), sh.I, a)
+        ys = np.stack([textbook_expert(orc, inp.w13.expert(e), inp.w2.expert(e), sh.I, a, limit)
                        for e in range(sh.E)])
         wd = np.zeros(sh.E)
         wd[res["ids"][r]] = res["w"][r]  # zero weight on unchosen experts
@@ -111,14 +120,32 @@ def test_sparse_routing_equals_dense_zero_weighted_mixture(orc, wfmt, sfmt):
         if sfmt == synth.BF16:
             W13, W2 = dense(inp.sh13), dense(inp.sh2)
             xv = bf16v(inp.x[r])
-            g, u = W13[:sh.I_sh] @ xv, W13[sh.I_sh:] @ xv
+            g, u = clamp_gu(W13[:sh.I_sh] @ xv, W13[sh.I_sh:] @ xv, limit)
             hb = bf16v(orc.bf16_rne_n(g / (1 + np.exp(-g)) * u))
             t = t + W2 @ hb
         elif sfmt == synth.MXFP4:
-            t = t + textbook_expert(orc, inp.sh13, inp.sh2, sh.I_sh, a)
+            t = t + textbook_expert(orc, inp.sh13, inp.sh2, sh.I_sh, a, limit)
         out, rb = textbook_norm(orc, t, inp.gamma, sh.eps)
         assert np.array_equal(res["resid_out"][r], rb)
         assert np.allclose(res["out64"][r], out, rtol=1e-11, atol=1e-13)
+
+
+def test_clamped_swiglu_closed_forms(orc):
+    """Values the algebra fixes: e^-ln3 = 1/3, so silu(ln 3) = (3/4) ln 3; the
+    clamp leaves values inside the limit alone, does not raise a low gate,
+    makes the output constant in a gate above the limit and odd in up."""
+    L = np.log(3.0)
+    assert orc.swiglu(5.0, 7.0, L) == pytest.approx(0.75 * L * L, rel=1e-15)
+    assert orc.swiglu(0.0, 0.9, L) == 0.0
+    for g, u in [(0.3, -0.7), (-10.0, 1.0), (-4.0, -1.05), (L, L)]:
+        assert orc.swiglu(g, u, L) == orc.swiglu(g, u, 0.0)
+    for g in (L, 2.0, 50.0):
+        assert orc.swiglu(g, 0.5, L) == orc.swiglu(L, 0.5, L)
+    for u in (2.0, 9.0):
+        assert orc.swiglu(0.4, u, L) == orc.swiglu(0.4, L, L)
+        assert orc.swiglu(0.4, -u, L) == -orc.swiglu(0.4, u, L)
+    # unclamped: no cap at all
+    assert orc.swiglu(50.0, 9.0, 0.0) == pytest.approx(50.0 * 9.0, rel=1e-15)
 
 
 def test_top_all_experts_is_dense_mixture(orc):

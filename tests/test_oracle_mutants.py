@@ -16,7 +16,17 @@ PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_route.py", "tests/tes
 
 MUTANTS = {
     "up rows read from the gate half": ("orc_mat_row(w13, H, I + n, wrow);", "orc_mat_row(w13, H, n, wrow);"),
-    "silu dropped": ("h[n] = (g / (1.0 + exp(-g))) * u;", "h[n] = g * u;"),
+    "silu dropped": ("return (g / (1.0 + exp(-g))) * u;", "return g * u;"),
+    "clamped gate capped from below too": ("        if (g > limit)\n            g = limit;\n",
+                                           "        if (g > limit)\n            g = limit;\n        if (g < -limit)\n            g = -limit;\n"),
+    "clamped up one-sided": ("        if (u < -limit)\n            u = -limit;\n", ""),
+    "clamped gate not capped": ("        if (g > limit)\n            g = limit;\n", ""),
+    "clamp left out of the routed experts": ("expert_fp4(&L->w13[e], &L->w2[e], H, I, a, L->swiglu_limit,",
+                                             "expert_fp4(&L->w13[e], &L->w2[e], H, I, a, 0.0,"),
+    "clamp left out of the shared expert": ("expert_fp4(&L->sh13, &L->sh2, H, L->I_sh, a, L->swiglu_limit,",
+                                            "expert_fp4(&L->sh13, &L->sh2, H, L->I_sh, a, 0.0,"),
+    "clamp left out of the bf16 shared expert": ("L->x + (size_t)r * H, L->swiglu_limit, h);",
+                                                 "L->x + (size_t)r * H, 0.0, h);"),
     "sigmoid sign flipped": ("s[e] = 1.0 / (1.0 + exp(-(double)logits_row[e]));",
                              "s[e] = 1.0 / (1.0 + exp((double)logits_row[e]));"),
     "bias leaks into weights": ("w[j] = (float)((scale * s[ids[j]]) / sum);",
