@@ -285,7 +285,7 @@ def main():
         Wr = d.Wr.clone()
         keep.append((w13, w2, sh13, sh2, Wr))
         layers.append(moe.Layer(s.M, s.H, s.E, s.k, s.I, s.I_sh, s.routed_scale, s.eps, Wr, d.bias,
-                                w13, w2, sh13, sh2, d.gamma))
+                                w13, w2, sh13, sh2, d.gamma, s.swiglu_limit))
     stream = torch.cuda.current_stream()
 
     if args.profile_gate_up:

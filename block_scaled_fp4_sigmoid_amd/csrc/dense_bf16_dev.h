@@ -126,7 +126,7 @@ __device__ inline void bf16_swiglu_block(const Bf16Side& S, int bid) {
             up += pu[u];
         }
     }
-    const float hv = gt / (1.0f + __expf(-gt)) * up;
+    const float hv = swiglu(gt, up, S.limit);
     S.h[(size_t)t * I + col] = (uint16_t)f32_to_bf16_rne(hv);
 }
 

@@ -37,6 +37,7 @@ Bf16Side bf16_side(const ExpertJob& gate_up_or_down, int I, int H, int M, const 
     S.part = part;
     S.h = h;
     S.y = y;
+    S.limit = gate_up_or_down.swiglu_limit;
     S.blocks = stage == kBf16GateUp ? (I / 32) * S.splits
                : stage == kBf16Swiglu ? (M * I + 255) / 256
                : stage == kBf16Down ? H / 64

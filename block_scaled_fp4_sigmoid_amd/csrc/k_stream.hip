@@ -109,6 +109,7 @@ struct StreamJob {
     // gate_up resolving from the ids: record the resolved slots here for the
     // down launch (active experts, bucket ranges, count, bucket), or nullptr
     int32_t *r_act, *r_off, *r_na, *r_bkt;
+    float limit;            // gate_up: clamped SwiGLU limit (0: unclamped)
 };
 
 struct Tokens {
@@ -795,7 +796,6 @@ __device__ __forceinline__ uint32_t mx_quant4_group8(const float hv[4], uint8_t&
     return w;
 }
 
-__device__ __forceinline__ float silu_mul(float gt, float up) { return gt / (1.0f + __expf(-gt)) * up; }
 
 // ---- gate_up ----------------------------------------------------------------
 // Item = (slot, 32*GMB output columns, K split).  Waves 0/1 stream the gate
@@ -933,7 +933,7 @@ __global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLO
                         gt = sG[t][col] * fac;
                         up = sG[t][GCOLS + col] * fac;
                     }
-                    hv[c] = silu_mul(gt, up);
+                    hv[c] = swiglu(gt, up, J.limit);
                 }
                 uint8_t sc;
                 const uint32_t codes = mx_quant4_group8(hv, sc);
@@ -966,7 +966,7 @@ __global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLO
 // Thread = (row, 4 columns); 8 consecutive threads share a 32-column block.
 __global__ __launch_bounds__(kThreads) void k_swiglu_quant(const float* __restrict__ part, int splits, int rows,
                                                            int I, uint8_t* __restrict__ h_q,
-                                                           uint8_t* __restrict__ h_s) {
+                                                           uint8_t* __restrict__ h_s, float limit) {
     const int idx = blockIdx.x * kThreads + threadIdx.x;
     const int q8 = idx & 7, blk = idx >> 3;
     const int cbs = I / 32;
@@ -981,7 +981,7 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_quant(const float* __restri
     }
     float hv[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) hv[c] = silu_mul(gt[c], up[c]);
+    for (int c = 0; c < 4; ++c) hv[c] = swiglu(gt[c], up[c], limit);
     uint8_t sc;
     const uint32_t codes = mx_quant4_group8(hv, sc);
     *reinterpret_cast<uint32_t*>(h_q + (size_t)row * I + col) = codes;
@@ -1269,6 +1269,7 @@ StreamJob stream_job(const ExpertJob& j, int N, const uint8_t* a_q, const uint8_
     s.r_na = j.record ? j.record->na : nullptr;
     s.r_bkt = j.record ? j.record->bkt : nullptr;
     if (s.a_tok) s.a_rows = (uint32_t)j.M;
+    s.limit = j.swiglu_limit;
     return s;
 }
 
@@ -1332,7 +1333,7 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
     if (e != hipSuccess) return e;
     const int threads = rows * (job.N_out / 32) * 8;
     hipLaunchKernelGGL(k_swiglu_quant, dim3((threads + kThreads - 1) / kThreads), dim3(kThreads), 0, stream,
-                       partials, p.splits, rows, job.N_out, h_q, h_s);
+                       partials, p.splits, rows, job.N_out, h_q, h_s, job.swiglu_limit);
     return hipGetLastError();
 }
 

@@ -211,9 +211,10 @@ size_t moe_gate_up_workspace_bytes(int fmt, int M, int H, int I, int E, int k, i
 
 int moe_expert_gate_up(const moe_weights* w13, const uint8_t* a_q, const uint8_t* a_s,
                        const uint16_t* a_bf16, const moe_routing* route, int M, int H, int I,
-                       int E, int k, uint8_t* h_q, uint8_t* h_s, uint16_t* h_bf16,
+                       int E, int k, float swiglu_limit, uint8_t* h_q, uint8_t* h_s, uint16_t* h_bf16,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!w13) return MOE_ERR_INVALID_ARG;
+    if (!(swiglu_limit >= 0.0f)) return MOE_ERR_INVALID_ARG;
     const bool dense = route == nullptr;
     if (int st = check_dims(M, H, dense ? 1 : E, dense ? 1 : k)) return st;
     if (I < 128 || I % 128 != 0 || I > kMaxI) return MOE_ERR_UNSUPPORTED;
@@ -223,13 +224,16 @@ int moe_expert_gate_up(const moe_weights* w13, const uint8_t* a_q, const uint8_t
         const size_t need = moe_gate_up_workspace_bytes(MOE_FMT_BF16, M, H, I, 1, 1, 1);
         if (!workspace || !aligned256(workspace) || workspace_bytes < need) return MOE_ERR_WORKSPACE;
         float* part = static_cast<float*>(workspace);
-        return hip_status(launch_gate_up_bf16(dense_job(*w13, I, H, M), a_bf16, h_bf16, part, stream));
+        ExpertJob job = dense_job(*w13, I, H, M);
+        job.swiglu_limit = swiglu_limit;
+        return hip_status(launch_gate_up_bf16(job, a_bf16, h_bf16, part, stream));
     }
     if (int st = check_fp4_weights(w13)) return st;
     if (!a_q || !a_s || !h_q || !h_s) return MOE_ERR_INVALID_ARG;
     if (!dense)
         if (int st = check_routing(route)) return st;
-    const ExpertJob job = dense ? dense_job(*w13, I, H, M) : routed_job(*w13, I, H, *route, M, E, k);
+    ExpertJob job = dense ? dense_job(*w13, I, H, M) : routed_job(*w13, I, H, *route, M, E, k);
+    job.swiglu_limit = swiglu_limit;
     const size_t need = gate_up_fp4_partials_bytes(job);
     if (need && (!workspace || !aligned256(workspace) || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
     return hip_status(launch_gate_up_fp4(job, a_q, a_s, h_q, h_s, static_cast<float*>(workspace), stream));
@@ -285,6 +289,7 @@ int check_desc(const moe_layer_desc* d) {
     if (d->I < 128 || d->I % 128 != 0 || d->I > kMaxI) return MOE_ERR_UNSUPPORTED;
     if (!d->w_router || !d->gamma) return MOE_ERR_INVALID_ARG;
     if (!(d->eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+    if (!(d->swiglu_limit >= 0.0f)) return MOE_ERR_INVALID_ARG;
     if (int st = check_fp4_weights(&d->w13)) return st;
     if (int st = check_fp4_weights(&d->w2)) return st;
     if (d->w13.fmt != d->w2.fmt) return MOE_ERR_UNSUPPORTED;
@@ -407,10 +412,12 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
     // A bf16 shared expert does not depend on the routing: its three stages
     // run as extra workgroups of the router, top-k and bucketing launches.
     const bool shb = sf == MOE_FMT_BF16;
-    const Bf16Side s1 = shb ? bf16_side(dense_job(d->sh13, Ish, H, M), Ish, H, M, x, L.sh_part, L.hsb, L.ysh,
+    ExpertJob sh_gu = dense_job(d->sh13, Ish, H, M);
+    sh_gu.swiglu_limit = d->swiglu_limit;
+    const Bf16Side s1 = shb ? bf16_side(sh_gu, Ish, H, M, x, L.sh_part, L.hsb, L.ysh,
                                         kBf16GateUp)
                             : no_side();
-    const Bf16Side s2 = shb ? bf16_side(dense_job(d->sh13, Ish, H, M), Ish, H, M, x, L.sh_part, L.hsb, L.ysh,
+    const Bf16Side s2 = shb ? bf16_side(sh_gu, Ish, H, M, x, L.sh_part, L.hsb, L.ysh,
                                         kBf16Swiglu)
                             : no_side();
     const Bf16Side s3 = shb ? bf16_side(dense_job(d->sh2, H, Ish, M), Ish, H, M, x, L.sh_part, L.hsb, L.ysh,
@@ -429,12 +436,14 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
             e = launch_topk(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale, logits_out, r, s2,
                             shb ? kBf16Swiglu : kBf16None, stream);
         ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
+        gu.swiglu_limit = d->swiglu_limit;
         gu.ids = r.topk_ids;
         gu.a_tok = true;
         const SlotRecord rec{L.r_act, L.r_off, L.r_na, L.r_bkt};
         gu.record = &rec;
         // the FP4 shared expert rides along the routed launches
-        const ExpertJob sgu = dense_job(d->sh13, Ish, H, M), sdn = dense_job(d->sh2, H, Ish, M);
+        const ExpertJob& sgu = sh_gu;
+        const ExpertJob sdn = dense_job(d->sh2, H, Ish, M);
         const SecondJob s_gu = fp4_shared ? SecondJob{&sgu, L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart} : SecondJob{};
         const SecondDown s_dn = fp4_shared ? SecondDown{&sdn, L.hsq, L.hss, L.ysh} : SecondDown{};
         if (e == hipSuccess)
@@ -461,8 +470,10 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
         e = launch_topk_bucket(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale, logits_out, r,
                                s2, shb ? kBf16Swiglu : kBf16None, s3, shb ? kBf16Down : kBf16None, stream);
     ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
+    gu.swiglu_limit = d->swiglu_limit;
     gu.a_tok = true;
-    const ExpertJob sgu = dense_job(d->sh13, Ish, H, M), sdn = dense_job(d->sh2, H, Ish, M);
+    const ExpertJob& sgu = sh_gu;
+    const ExpertJob sdn = dense_job(d->sh2, H, Ish, M);
     const SecondJob s_gu = fp4_shared ? SecondJob{&sgu, L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart} : SecondJob{};
     const SecondDown s_dn = fp4_shared ? SecondDown{&sdn, L.hsq, L.hss, L.ysh} : SecondDown{};
     if (e == hipSuccess)

@@ -19,6 +19,18 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// SwiGLU of one gate/up pair: silu(g) * u with silu(g) = g / (1 + e^-g).
+// limit > 0 is the clamped form (README DeepSeek-V4.1 slot table, row
+// "Shared expert gate_up (shared_ll)"): the gate capped from above at limit
+// and up clamped to [-limit, limit] before the product; NaN passes through.
+__device__ __forceinline__ float swiglu(float g, float u, float limit) {
+    if (limit > 0.0f) {
+        g = g > limit ? limit : g;
+        u = u > limit ? limit : (u < -limit ? -limit : u);
+    }
+    return g / (1.0f + __expf(-g)) * u;
+}
+
 // fp32 -> bf16 bits, round to nearest even (NaN kept quiet, sign kept).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);

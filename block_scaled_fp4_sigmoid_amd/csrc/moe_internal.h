@@ -26,6 +26,7 @@ struct Bf16Side {
     uint16_t* h;        // bf16 [M][I] (SwiGLU output, down input)
     float* y;           // fp32 [M][H] (down output)
     int blocks;         // workgroups of the stage
+    float limit;        // clamped SwiGLU limit (0: unclamped)
 };
 enum Bf16Stage { kBf16None = 0, kBf16GateUp = 1, kBf16Swiglu = 2, kBf16Down = 3 };
 // An empty side: no extra workgroups.
@@ -108,6 +109,7 @@ struct ExpertJob {
     bool a_tok = false;
     const SlotRecord* record = nullptr;  // gate_up with ids: record the resolved slots
     const int32_t* count = nullptr;      // active list whose entries past *count are stale
+    float swiglu_limit = 0.0f;           // gate_up: clamped SwiGLU limit (0: unclamped)
 };
 
 // gate_up over FP4 experts.  When the plan splits K, fp32 partials go to

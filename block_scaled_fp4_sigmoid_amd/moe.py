@@ -44,7 +44,7 @@ class moe_layer_desc(C.Structure):
                 ("I_sh", C.c_int), ("routed_scale", C.c_float), ("eps", C.c_float),
                 ("w_router", C.c_void_p), ("router_bias", C.c_void_p),
                 ("w13", moe_weights), ("w2", moe_weights), ("sh13", moe_weights),
-                ("sh2", moe_weights), ("gamma", C.c_void_p)]
+                ("sh2", moe_weights), ("gamma", C.c_void_p), ("swiglu_limit", C.c_float)]
 
 
 _lib = None
@@ -78,7 +78,7 @@ def lib() -> C.CDLL:
         L.moe_gate_up_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         L.moe_expert_gate_up.restype = i
         L.moe_expert_gate_up.argtypes = [C.POINTER(moe_weights), vp, vp, vp, C.POINTER(moe_routing),
-                                         i, i, i, i, i, vp, vp, vp, vp, sz, vp]
+                                         i, i, i, i, i, f, vp, vp, vp, vp, sz, vp]
         L.moe_expert_down.restype = i
         L.moe_expert_down.argtypes = [C.POINTER(moe_weights), vp, vp, vp, C.POINTER(moe_routing),
                                       i, i, i, i, i, vp, vp]
@@ -220,7 +220,8 @@ def quant_act_mxfp8(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, routing: 
 
 
 def expert_gate_up(w13: Weights, M, H, I, E, k, routing: Optional[Routing] = None, a_q=None,
-                   a_s=None, a_bf16=None, h_q=None, h_s=None, h_bf16=None, ws=None, stream=None):
+                   a_s=None, a_bf16=None, h_q=None, h_s=None, h_bf16=None, ws=None, stream=None,
+                   swiglu_limit=0.0):
     _need_packed(w13)
     dense = routing is None
     dev = (a_q if a_q is not None else a_bf16).device
@@ -230,7 +231,8 @@ def expert_gate_up(w13: Weights, M, H, I, E, k, routing: Optional[Routing] = Non
     wc = w13.c()
     r = None if dense else routing.c()
     rc = lib().moe_expert_gate_up(C.byref(wc), _p(a_q), _p(a_s), _p(a_bf16),
-                                  None if dense else C.byref(r), M, H, I, E, k, _p(h_q), _p(h_s),
+                                  None if dense else C.byref(r), M, H, I, E, k, float(swiglu_limit),
+                                  _p(h_q), _p(h_s),
                                   _p(h_bf16), _p(ws), 0 if ws is None else ws.numel(), _stream(stream))
     _check(rc, "moe_expert_gate_up")
 
@@ -266,13 +268,13 @@ class Layer:
     """The fused layer (moe_layer) over weights held in torch device tensors."""
 
     def __init__(self, M, H, E, k, I, I_sh, routed_scale, eps, w_router, router_bias,
-                 w13: Weights, w2: Weights, sh13: Weights, sh2: Weights, gamma):
+                 w13: Weights, w2: Weights, sh13: Weights, sh2: Weights, gamma, swiglu_limit=0.0):
         _need_packed(w13, w2, sh13, sh2)
         self._keep = (w_router, router_bias, w13, w2, sh13, sh2, gamma)
         self.M, self.H, self.E, self.k = M, H, E, k
         self.desc = moe_layer_desc(M, H, E, k, I, I_sh, float(routed_scale), float(eps),
                                    _p(w_router), _p(router_bias), w13.c(), w2.c(), sh13.c(),
-                                   sh2.c(), _p(gamma))
+                                   sh2.c(), _p(gamma), float(swiglu_limit))
         self.ws_bytes = lib().moe_layer_workspace_bytes(C.byref(self.desc))
         if self.ws_bytes == 0:
             raise RuntimeError("moe_layer_workspace_bytes rejected the layer description")

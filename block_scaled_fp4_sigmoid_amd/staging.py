@@ -63,7 +63,7 @@ class DeviceInputs:
     def layer(self) -> Layer:
         s = self.shape
         return Layer(s.M, s.H, s.E, s.k, s.I, s.I_sh, s.routed_scale, s.eps, self.Wr, self.bias,
-                     self.w13, self.w2, self.sh13, self.sh2, self.gamma)
+                     self.w13, self.w2, self.sh13, self.sh2, self.gamma, s.swiglu_limit)
 
     def weight_bytes_per_expert(self) -> int:
         s = self.shape

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 enum moe_status {
     MOE_OK = 0,
@@ -126,6 +126,7 @@ typedef struct moe_layer_desc {
     moe_weights w13, w2;         /* routed experts: [E, 2I, H] and [E, H, I] */
     moe_weights sh13, sh2;       /* shared expert: [2I_sh, H] and [H, I_sh]; fmt NONE = absent */
     const uint16_t *gamma;       /* bf16 [H] RMSNorm weight */
+    float swiglu_limit;          /* clamped SwiGLU of every expert (see moe_expert_gate_up); 0: unclamped */
 } moe_layer_desc;
 
 const char *moe_status_str(int status);
@@ -207,7 +208,11 @@ int moe_quant_act_mxfp8(const uint16_t *x, int M, int K, const moe_routing *rout
  *   "shared act quant" (SiLU-and-mul fused with the down input's quant);
  *   SGLang Spark GB10 Optimizations, section 1 (NVFP4 K-groups of 16).
  * g = A W13[:I]^T, u = A W13[I:]^T with exact products and fp32 sums; h =
- * silu(g) * u in fp32.  FP4 weights (packed by moe_pack_fp4): A is MXFP8
+ * silu(g) * u in fp32.  swiglu_limit > 0 selects the clamped SwiGLU (README
+ * DeepSeek-V4.1 slot table, row "Shared expert gate_up (shared_ll)"): g is
+ * capped from above at the limit and u clamped to [-limit, limit] before the
+ * product; 0 is the plain SwiGLU; negative or NaN is MOE_ERR_INVALID_ARG.
+ * FP4 weights (packed by moe_pack_fp4): A is MXFP8
  * (a_q, a_s) [Pr, H] and h is written as MXFP8 (h_q [Pr, I], h_s [Pr, I/32])
  * with the rule of moe_quant_act_mxfp8.  BF16 weights: A is bf16 a_bf16
  * [M, H] and h is written rounded to bf16 (h_bf16 [Pr, I]).
@@ -221,7 +226,7 @@ int moe_quant_act_mxfp8(const uint16_t *x, int M, int K, const moe_routing *rout
 size_t moe_gate_up_workspace_bytes(int fmt, int M, int H, int I, int E, int k, int dense);
 int moe_expert_gate_up(const moe_weights *w13, const uint8_t *a_q, const uint8_t *a_s,
                        const uint16_t *a_bf16, const moe_routing *route, int M, int H, int I,
-                       int E, int k, uint8_t *h_q, uint8_t *h_s, uint16_t *h_bf16,
+                       int E, int k, float swiglu_limit, uint8_t *h_q, uint8_t *h_s, uint16_t *h_bf16,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------

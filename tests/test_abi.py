@@ -51,7 +51,7 @@ def test_probe_library_exports():
 
 
 def test_version_and_status_strings(L):
-    assert moe.abi_version() == 5
+    assert moe.abi_version() == 6
     for rc in range(5):
         assert len(moe.status_str(rc)) > 0
     assert "unknown" in moe.status_str(99)
@@ -110,6 +110,8 @@ def test_layer_desc_validation(L):
               sh2=moe.moe_weights(moe.MOE_FMT_BF16, 0x1000, None, None)),
         _desc(w13=moe.moe_weights(moe.MOE_FMT_BF16, 0x1000, None, None),
               w2=moe.moe_weights(moe.MOE_FMT_BF16, 0x1000, None, None)),  # bf16 routed experts
+        _desc(swiglu_limit=-0.5),
+        _desc(swiglu_limit=float("nan")),
     ]
     for d in bad:
         assert L.moe_layer_workspace_bytes(C.byref(d)) == 0
@@ -166,8 +168,12 @@ def test_calls_refuse_before_enqueueing(L):
                             0x1000, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
     w = moe.moe_weights(moe.MOE_FMT_BF16, 0x1000, None, None)
     # bf16 weights are only supported densely (shared expert)
-    assert L.moe_expert_gate_up(C.byref(w), None, None, 0x1000, C.byref(r), 4, 128, 128, 8, 2, None,
+    assert L.moe_expert_gate_up(C.byref(w), None, None, 0x1000, C.byref(r), 4, 128, 128, 8, 2, 0.0, None,
                                 None, 0x1000, 0x1000, 1 << 20, None) == moe.MOE_ERR_UNSUPPORTED
+    # the clamped SwiGLU's limit: negative or NaN refused
+    for bad in (-1.0, float("nan")):
+        assert L.moe_expert_gate_up(C.byref(w), None, None, 0x1000, None, 4, 128, 128, 1, 1, bad, None,
+                                    None, 0x1000, 0x1000, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_expert_down(C.byref(w), None, None, 0x1000, None, 4, 128, 100, 1, 1, 0x1000,
                              None) == moe.MOE_ERR_UNSUPPORTED
     assert L.moe_finalize_rmsnorm(0x1000, 0x1000, None, 0x1000, 0x1000, -1.0, 4, 128, 2, 0x1000,

@@ -152,17 +152,19 @@ def _routed_setup(wfmt, M=40, H=512, E=6, k=3, I=256, seed=3, bias="zipf:1.0", n
     return sh, inp, d, rt, (xq, xs), (xqp, xsp)
 
 
-@pytest.mark.parametrize("wfmt,H,neg", [(synth.MXFP4, 512, False), (synth.NVFP4, 512, False),
-                                        (synth.MXFP4, 2560, False), (synth.NVFP4, 2560, False),
-                                        (synth.NVFP4, 2560, True)])
-def test_gate_up_routed_parity(wfmt, H, neg):
-    # H = 512 is one K chunk; 2560 is five (exercises the weight ring and LDS buffers)
+@pytest.mark.parametrize("wfmt,H,neg,limit", [(synth.MXFP4, 512, False, 0.0), (synth.NVFP4, 512, False, 0.0),
+                                              (synth.MXFP4, 2560, False, 0.0), (synth.NVFP4, 2560, False, 0.0),
+                                              (synth.NVFP4, 2560, True, 0.0), (synth.MXFP4, 512, False, 0.5),
+                                              (synth.NVFP4, 2560, False, 0.5), (synth.MXFP4, 2560, False, 0.5)])
+def test_gate_up_routed_parity(wfmt, H, neg, limit):
+    # H = 512 is one K chunk; 2560 is five (exercises the weight ring and LDS buffers);
+    # limit > 0: the clamped SwiGLU (gate values here have a std of 0.45 to 1)
     sh, inp, d, rt, (xq, xs), (xqp, xsp) = _routed_setup(wfmt, H=H, neg_scales=neg)
     M, H, E, k, I = sh.M, sh.H, sh.E, sh.k, sh.I
     P = M * k
     hq = torch.empty((P, I), dtype=torch.uint8, device=DEV)
     hs = torch.empty((P, I // 32), dtype=torch.uint8, device=DEV)
-    moe.expert_gate_up(d.w13, M, H, I, E, k, routing=rt, a_q=xqp, a_s=xsp, h_q=hq, h_s=hs)
+    moe.expert_gate_up(d.w13, M, H, I, E, k, routing=rt, a_q=xqp, a_s=xsp, h_q=hq, h_s=hs, swiglu_limit=limit)
     torch.cuda.synchronize()
     bucket, ids = np_of(rt.bucket), np_of(rt.topk_ids).ravel()
     a = orc.mxfp8_dequant(np_of(xq), np_of(xs))
@@ -173,7 +175,7 @@ def test_gate_up_routed_parity(wfmt, H, neg):
         p = bucket[b]
         e, r = ids[p], p // k
         m13 = inp.w13.expert(e)
-        h = orc.gate_up(orc.Mat(m13.fmt, m13.packed, m13.scales, m13.gscale), H, I, a[r])
+        h = orc.gate_up(orc.Mat(m13.fmt, m13.packed, m13.scales, m13.gscale), H, I, a[r], limit)
         rq, rs = orc.mxfp8_quant_f64(h[None, :])
         eq_bytes += int(np.sum(rq[0] == ghq[b])) + int(np.sum(rs[0] == ghs[b]))
         tot += I + I // 32
@@ -215,8 +217,9 @@ def test_down_routed_parity(wfmt, I, neg, H):
     assert worst < 2e-3, worst
 
 
-@pytest.mark.parametrize("sfmt,M", [(synth.MXFP4, 23), (synth.NVFP4, 23), (synth.MXFP4, 70), (synth.NVFP4, 70)])
-def test_dense_fp4_expert_parity(sfmt, M):
+@pytest.mark.parametrize("sfmt,M,limit", [(synth.MXFP4, 23, 0.0), (synth.NVFP4, 23, 0.0), (synth.MXFP4, 70, 0.0),
+                                          (synth.NVFP4, 70, 0.0), (synth.MXFP4, 23, 0.3), (synth.NVFP4, 70, 0.3)])
+def test_dense_fp4_expert_parity(sfmt, M, limit):
     """The shared-expert path: one FP4 expert over all rows in order (70 rows:
     three passes of 32 rows, each its own workgroups)."""
     H, I = 384, 256
@@ -228,7 +231,7 @@ def test_dense_fp4_expert_parity(sfmt, M):
     moe.quant_act_mxfp8(d.x, xq, xs)
     hq = torch.empty((M, I), dtype=torch.uint8, device=DEV)
     hs = torch.empty((M, I // 32), dtype=torch.uint8, device=DEV)
-    moe.expert_gate_up(d.sh13, M, H, I, 1, 1, routing=None, a_q=xq, a_s=xs, h_q=hq, h_s=hs)
+    moe.expert_gate_up(d.sh13, M, H, I, 1, 1, routing=None, a_q=xq, a_s=xs, h_q=hq, h_s=hs, swiglu_limit=limit)
     y = torch.empty((M, H), dtype=torch.float32, device=DEV)
     moe.expert_down(d.sh2, M, H, I, 1, 1, y, routing=None, h_q=hq, h_s=hs)
     torch.cuda.synchronize()
@@ -239,7 +242,7 @@ def test_dense_fp4_expert_parity(sfmt, M):
     hd = orc.mxfp8_dequant(ghq, ghs)
     eq = 0
     for r in range(M):
-        h = orc.gate_up(m13, H, I, a[r])
+        h = orc.gate_up(m13, H, I, a[r], limit)
         rq, rs = orc.mxfp8_quant_f64(h[None, :])
         eq += int(np.sum(rq[0] == ghq[r]))
         yr = orc.down(m2, H, I, hd[r])
@@ -247,13 +250,14 @@ def test_dense_fp4_expert_parity(sfmt, M):
     assert eq / (M * I) >= 0.999
 
 
-@pytest.mark.parametrize("M,H,I", [(48, 1024, 256), (8, 7168, 256), (48, 4096, 512)])
-def test_dense_bf16_expert_parity(M, H, I):
+@pytest.mark.parametrize("M,H,I,limit", [(48, 1024, 256, 0.0), (8, 7168, 256, 0.0), (48, 4096, 512, 0.0),
+                                         (8, 7168, 256, 0.8)])
+def test_dense_bf16_expert_parity(M, H, I, limit):
     sh = synth.custom_shape(M=M, H=H, E=1, k=1, I=128, sfmt=synth.BF16, I_sh=I)
     inp = synth.make_inputs(sh, seed=9, pool_rows=64)
     d = staging.to_device(inp, DEV)
     hb = torch.empty((M, I), dtype=torch.int16, device=DEV)
-    moe.expert_gate_up(d.sh13, M, H, I, 1, 1, routing=None, a_bf16=d.x, h_bf16=hb)
+    moe.expert_gate_up(d.sh13, M, H, I, 1, 1, routing=None, a_bf16=d.x, h_bf16=hb, swiglu_limit=limit)
     y = torch.empty((M, H), dtype=torch.float32, device=DEV)
     moe.expert_down(d.sh2, M, H, I, 1, 1, y, routing=None, h_bf16=hb)
     torch.cuda.synchronize()
@@ -263,7 +267,7 @@ def test_dense_bf16_expert_parity(M, H, I):
     gy = np_of(y)
     eq = 0
     for r in range(M):
-        h = orc.gate_up_bf16(m13, H, I, inp.x[r])
+        h = orc.gate_up_bf16(m13, H, I, inp.x[r], limit)
         hb_ref = orc.bf16_rne_n(h)
         eq += int(np.sum(hb_ref == ghb[r]))
         yr = orc.down(m2, H, I, bf16_to_f64(ghb[r]))
