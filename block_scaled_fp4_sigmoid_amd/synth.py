@@ -44,6 +44,13 @@ BF16 = 3
 NONE = 0
 
 FMT_NAMES = {NONE: "none", MXFP4: "mxfp4", NVFP4: "nvfp4", BF16: "bf16"}
+# activation formats of the expert GEMMs
+ACT_MXFP8 = 0
+ACT_NVFP4 = 1
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 POOL_ROWS = 8192
 
@@ -135,6 +142,7 @@ class Shape:
     eps: float = 1e-6
     desc: str = ""
     swiglu_limit: float = 0.0  # clamped SwiGLU of every expert; 0: unclamped
+    act_fmt: int = 0           # ACT_MXFP8, or ACT_NVFP4 (W4A4: NVFP4 experts only)
 
 
 # The five workloads the layer is measured on (pages: DeepSeek-V4.1 verify
@@ -163,15 +171,17 @@ WORKLOAD_ORDER = list(WORKLOADS)
 
 
 def custom_shape(M, H, E, k, I, wfmt=MXFP4, sfmt=NONE, I_sh=None, routed_scale=1.0,
-                 bias="none", eps=1e-6, name=None, swiglu_limit=0.0) -> Shape:
+                 bias="none", eps=1e-6, name=None, swiglu_limit=0.0, act_fmt=0) -> Shape:
     I_sh = I if I_sh is None else I_sh
     if sfmt == NONE:
         I_sh = 0
     name = name or f"custom-m{M}-h{H}-e{E}-k{k}-i{I}-{FMT_NAMES[wfmt]}-sh{FMT_NAMES[sfmt]}"
     if swiglu_limit:
         name += f"-clamp{swiglu_limit:g}"
+    if act_fmt == ACT_NVFP4:
+        name += "-a4"
     return Shape(name, M, H, E, k, I, wfmt, sfmt, I_sh, float(routed_scale), bias, eps,
-                 swiglu_limit=float(swiglu_limit))
+                 swiglu_limit=float(swiglu_limit), act_fmt=int(act_fmt))
 
 
 @dataclass
@@ -228,6 +238,11 @@ class MoEInputs:
     sh13: Optional[Matrix] = None  # [2I_sh, H]
     sh2: Optional[Matrix] = None   # [H, I_sh]
     meta: dict = field(default_factory=dict)
+    # NVFP4 activations (act_fmt ACT_NVFP4): static globals of the layer input,
+    # of each routed expert's h and of the shared expert's h
+    x_gscale: float = 0.0
+    h_gscale: Optional[np.ndarray] = None  # fp32 [E]
+    sh_h_gscale: float = 0.0
 
     @property
     def residual(self) -> np.ndarray:
@@ -290,7 +305,23 @@ def make_inputs(shape: Shape | str, seed: int = 1, pool_rows: int = POOL_ROWS) -
     if shape.sfmt != NONE:
         sh13 = _whole(rng, shape.sfmt, 2 * shape.I_sh, H)
         sh2 = _whole(rng, shape.sfmt, H, shape.I_sh)
-    return MoEInputs(shape, seed, x, Wr, bias, gamma, w13, w2, sh13, sh2)
+    inp = MoEInputs(shape, seed, x, Wr, bias, gamma, w13, w2, sh13, sh2)
+    if shape.act_fmt == ACT_NVFP4:
+        if shape.wfmt != NVFP4 or shape.sfmt == MXFP4:
+            raise ValueError("NVFP4 activations go with NVFP4 experts (shared: none, NVFP4 or bf16)")
+        # Static globals, as an NVFP4 checkpoint ships them (calibrated offline):
+        # the input's from this step's own amax; each h's from the spread that
+        # gate and up have for N(0, 1) rows and N(0, 0.02) weights (std
+        # 0.02 sqrt(H) each, so h = silu(g) u spreads about their product),
+        # times 2^u, u in {-1, 0, 1} per expert.  Drawn after everything else, so
+        # the other inputs of a seed do not change.
+        xa = np.abs(bf16_to_f32(x)).max()
+        inp.x_gscale = float(np.float32(xa) / np.float32(6 * 448))
+        var = np.float32((0.02 * np.sqrt(H)) ** 2)
+        base = np.float32(8.0) * var / np.float32(6 * 448)
+        inp.h_gscale = (base * np.exp2(rng.integers(-1, 2, size=E)).astype(np.float32)).astype(np.float32)
+        inp.sh_h_gscale = float(base)
+    return inp
 
 
 def vary_globals(inp: MoEInputs, seed: int) -> MoEInputs:

@@ -219,6 +219,104 @@ void orc_mxfp8_dequant(const uint8_t *q, const uint8_t *s, int K, double *out)
         out[i] = T_E4M3[q[i]] * T_E8M0[s[i / 32]];
 }
 
+/* ------------------------------------------------------------------------ */
+/* NVFP4 activations (README Qwen3.5 slot table: row "route" quantizes the MoE
+ * input to NVFP4 in the router launch, row "mkm" requantizes the SwiGLU output
+ * to NVFP4 before FC2).  The pages give no activation-scale rule.  Reading,
+ * the NVFP4 weight encoding (E2M1 codes, an E4M3 scale per 16 values, an fp32
+ * global) applied to activations with a static global g given by the caller,
+ * every decision taken in fp32 so that a GPU computing in fp32 takes the same
+ * ones:
+ *   a block of 16 values v (fp32) with a non-finite value: scale byte 0x7F
+ *     (E4M3 NaN), all codes 0;
+ *   else amax = max |v|; s = amax / (6 g) (fp32: the product 6 g rounded, then
+ *     the quotient rounded); scale = E4M3 RNE of s, saturating at 448;
+ *     sd = its value; sd == 0: all codes 0; else each code = E2M1 RNE of
+ *     v / (sd g) (fp32 product, then fp32 quotient), saturating at 6, with
+ *     the sign of the quotient;
+ *   value = E2M1(code) * E4M3(scale) * g.
+ * Codes pack two per byte, the even element in the low nibble (as the
+ * weights); scales are one byte per 16 values. */
+
+/* E2M1 code of v: the nearest of the eight magnitudes, ties to the code whose
+ * mantissa bit is 0 (even), saturating at 6, with v's sign bit. */
+uint8_t orc_e2m1_rne_sat(float v)
+{
+    tables();
+    const int neg = signbit(v) ? 1 : 0;
+    const double a = fabs((double)v);
+    int best = 7;
+    if (a < 6.0) {
+        best = 0;
+        for (int c = 1; c < 8; ++c) {
+            const double dc = fabs(T_E2M1[c] - a), db = fabs(T_E2M1[best] - a);
+            if (dc < db || (dc == db && (c & 1) == 0))
+                best = c;
+        }
+    }
+    return (uint8_t)((neg << 3) | best);
+}
+
+void orc_nvfp4_quant_block(const float *v, float g, uint8_t *q8, uint8_t *sc)
+{
+    tables();
+    float amax = 0.0f;
+    int finite = 1;
+    for (int i = 0; i < 16; ++i) {
+        if (!isfinite(v[i]))
+            finite = 0;
+        else if (fabsf(v[i]) > amax)
+            amax = fabsf(v[i]);
+    }
+    uint8_t codes[16];
+    if (!finite) {
+        *sc = 0x7F;
+        memset(codes, 0, sizeof(codes));
+    } else {
+        const float t = 6.0f * g;
+        const float sq = amax / t;
+        *sc = orc_e4m3_rne_sat((double)sq);
+        const float sd = (float)T_E4M3[*sc];
+        if (sd == 0.0f) {
+            memset(codes, 0, sizeof(codes));
+        } else {
+            const float d = sd * g;
+            for (int i = 0; i < 16; ++i)
+                codes[i] = orc_e2m1_rne_sat(v[i] / d);
+        }
+    }
+    for (int i = 0; i < 8; ++i)
+        q8[i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
+}
+
+void orc_nvfp4_quant_f32(const float *v, int M, int K, float g, uint8_t *q, uint8_t *s)
+{
+    for (int r = 0; r < M; ++r)
+        for (int b = 0; b < K / 16; ++b)
+            orc_nvfp4_quant_block(v + (size_t)r * K + 16 * b, g, q + (size_t)r * (K / 2) + 8 * b,
+                                  s + (size_t)r * (K / 16) + b);
+}
+
+void orc_nvfp4_quant_bf16(const uint16_t *x, int M, int K, float g, uint8_t *q, uint8_t *s)
+{
+    float blk[16];
+    for (int r = 0; r < M; ++r)
+        for (int b = 0; b < K / 16; ++b) {
+            for (int i = 0; i < 16; ++i)
+                blk[i] = (float)orc_bf16_value(x[(size_t)r * K + 16 * b + i]);
+            orc_nvfp4_quant_block(blk, g, q + (size_t)r * (K / 2) + 8 * b, s + (size_t)r * (K / 16) + b);
+        }
+}
+
+void orc_nvfp4_dequant(const uint8_t *q, const uint8_t *s, int K, float g, double *out)
+{
+    tables();
+    for (int i = 0; i < K; ++i) {
+        const int code = (i & 1) ? (q[i / 2] >> 4) : (q[i / 2] & 15);
+        out[i] = T_E2M1[code] * T_E4M3[s[i / 16]] * (double)g;
+    }
+}
+
 /* Decode row n of a weight matrix [N, K] into fp64 (exact for every format).
  * MXFP4: E2M1 * E8M0(per 32 along K).  NVFP4: E2M1 * E4M3(per 16 along K) *
  * fp32 global, the two-level NVFP4 scaling of SGLang Spark GB10 Optimizations,
@@ -469,20 +567,32 @@ typedef struct {
  * I (the pages requantize the SwiGLU output before FC2: README Qwen3.5 slot
  * table, row "mkm"; PR #33 appended table, row "shared act quant"), down. */
 static void expert_fp4(const orc_mat *w13, const orc_mat *w2, int H, int I, const double *a,
-                       double limit, double *y, uint8_t *hq, uint8_t *hs)
+                       double limit, int act_fmt, float h_g, double *y, uint8_t *hq, uint8_t *hs)
 {
     double *h = (double *)malloc(sizeof(double) * I);
     double *hd = (double *)malloc(sizeof(double) * I);
     uint8_t *q = (uint8_t *)malloc(I);
-    uint8_t *s = (uint8_t *)malloc(I / 32);
+    uint8_t *s = (uint8_t *)malloc(I / 16);
     orc_gate_up(w13, H, I, a, limit, h);
-    orc_mxfp8_quant_f64(h, 1, I, q, s);
-    orc_mxfp8_dequant(q, s, I, hd);
+    const int qb = act_fmt == ORC_ACT_NVFP4 ? I / 2 : I;
+    const int sb = act_fmt == ORC_ACT_NVFP4 ? I / 16 : I / 32;
+    if (act_fmt == ORC_ACT_NVFP4) {
+        /* the GPU holds h in fp32: the fp32 rule reads h rounded to fp32 */
+        float *hf = (float *)malloc(sizeof(float) * I);
+        for (int n = 0; n < I; ++n)
+            hf[n] = (float)h[n];
+        orc_nvfp4_quant_f32(hf, 1, I, h_g, q, s);
+        orc_nvfp4_dequant(q, s, I, h_g, hd);
+        free(hf);
+    } else {
+        orc_mxfp8_quant_f64(h, 1, I, q, s);
+        orc_mxfp8_dequant(q, s, I, hd);
+    }
     orc_down(w2, H, I, hd, y);
     if (hq)
-        memcpy(hq, q, I);
+        memcpy(hq, q, qb);
     if (hs)
-        memcpy(hs, s, I / 32);
+        memcpy(hs, s, sb);
     free(h);
     free(hd);
     free(q);
@@ -508,9 +618,14 @@ static void route_row(rows_job *J, int i)
     orc_topk_row(lrow, L->bias, E, k, L->routed_scale, J->ids + (size_t)i * k,
                  J->w + (size_t)i * k, NULL);
     uint8_t *aq = (uint8_t *)malloc(H);
-    uint8_t *as = (uint8_t *)malloc(H / 32);
-    orc_mxfp8_quant_bf16(L->x + (size_t)r * H, 1, H, aq, as);
-    orc_mxfp8_dequant(aq, as, H, J->a + (size_t)i * H);
+    uint8_t *as = (uint8_t *)malloc(H / 16);
+    if (L->act_fmt == ORC_ACT_NVFP4) {
+        orc_nvfp4_quant_bf16(L->x + (size_t)r * H, 1, H, L->x_gscale, aq, as);
+        orc_nvfp4_dequant(aq, as, H, L->x_gscale, J->a + (size_t)i * H);
+    } else {
+        orc_mxfp8_quant_bf16(L->x + (size_t)r * H, 1, H, aq, as);
+        orc_mxfp8_dequant(aq, as, H, J->a + (size_t)i * H);
+    }
     free(lrow);
     free(aq);
     free(as);
@@ -525,9 +640,11 @@ static void expert_item(rows_job *J, int i, int j)
     const double *a = J->a + (size_t)i * H;
     if (j < k) {
         int e = J->ids[(size_t)i * k + j];
-        expert_fp4(&L->w13[e], &L->w2[e], H, I, a, L->swiglu_limit, J->y + ((size_t)i * k + j) * H,
-                   J->hq ? J->hq + ((size_t)i * k + j) * I : NULL,
-                   J->hs ? J->hs + ((size_t)i * k + j) * (I / 32) : NULL);
+        const int nv = L->act_fmt == ORC_ACT_NVFP4;
+        const int qb = nv ? I / 2 : I, sb = nv ? I / 16 : I / 32;
+        expert_fp4(&L->w13[e], &L->w2[e], H, I, a, L->swiglu_limit, L->act_fmt, nv ? L->h_gscale[e] : 0.0f,
+                   J->y + ((size_t)i * k + j) * H, J->hq ? J->hq + ((size_t)i * k + j) * qb : NULL,
+                   J->hs ? J->hs + ((size_t)i * k + j) * sb : NULL);
         return;
     }
     double *ysh = J->ysh + (size_t)i * H;
@@ -539,7 +656,8 @@ static void expert_item(rows_job *J, int i, int j)
         orc_down(&L->sh2, H, L->I_sh, h, ysh);
         free(h);
     } else {
-        expert_fp4(&L->sh13, &L->sh2, H, L->I_sh, a, L->swiglu_limit, ysh, NULL, NULL);
+        expert_fp4(&L->sh13, &L->sh2, H, L->I_sh, a, L->swiglu_limit, L->act_fmt, L->sh_h_gscale, ysh, NULL,
+                   NULL);
     }
 }
 
@@ -592,6 +710,9 @@ int orc_moe_rows(const orc_layer *L, const float *logits, const int32_t *rows, i
     if (L->sfmt != ORC_NONE && L->I_sh % 32)
         return -1;
     if (!logits && !L->Wr)
+        return -1;
+    if (L->act_fmt == ORC_ACT_NVFP4 &&
+        (L->wfmt != ORC_NVFP4 || !L->h_gscale || (L->sfmt != ORC_NONE && L->sfmt != ORC_NVFP4 && L->sfmt != ORC_BF16)))
         return -1;
     for (int i = 0; i < nrows; ++i)
         if (rows[i] < 0 || rows[i] >= L->M)

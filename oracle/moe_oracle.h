@@ -35,6 +35,9 @@ enum { ORC_NONE = 0, ORC_MXFP4 = 1, ORC_NVFP4 = 2, ORC_BF16 = 3 };
 /* One weight matrix [N, K], canonical layout: packed FP4 [N, K/2] (low nibble
  * = even K), scales [N, K/32] E8M0 (MXFP4) or [N, K/16] E4M3 (NVFP4), plus an
  * fp32 per-tensor global (NVFP4); or bf16 [N, K]. */
+/* Activation formats of the expert GEMMs. */
+enum { ORC_ACT_MXFP8 = 0, ORC_ACT_NVFP4 = 1 };
+
 typedef struct {
     int fmt;
     const uint8_t *packed;
@@ -60,6 +63,10 @@ typedef struct {
     const orc_mat *w2;         /* E entries */
     orc_mat sh13, sh2;         /* shared expert (fmt ORC_NONE when absent) */
     double swiglu_limit;       /* clamped SwiGLU of every expert (orc_swiglu); <= 0: none */
+    int act_fmt;               /* ORC_ACT_MXFP8, or ORC_ACT_NVFP4 (NVFP4 experts only) */
+    float x_gscale;            /* NVFP4 activations: global of the layer input */
+    const float *h_gscale;     /* NVFP4 activations: global of each routed expert's h [E] */
+    float sh_h_gscale;         /* NVFP4 activations: global of the shared expert's h */
 } orc_layer;
 
 /* ---- formats ---- */
@@ -75,6 +82,11 @@ void orc_mxfp8_quant_block(const double *v, uint8_t *q, uint8_t *s);
 void orc_mxfp8_quant_bf16(const uint16_t *x, int M, int K, uint8_t *q, uint8_t *s);
 void orc_mxfp8_quant_f64(const double *v, int M, int K, uint8_t *q, uint8_t *s);
 void orc_mxfp8_dequant(const uint8_t *q, const uint8_t *s, int K, double *out);
+uint8_t orc_e2m1_rne_sat(float v);
+void orc_nvfp4_quant_block(const float *v, float g, uint8_t *q8, uint8_t *sc);
+void orc_nvfp4_quant_f32(const float *v, int M, int K, float g, uint8_t *q, uint8_t *s);
+void orc_nvfp4_quant_bf16(const uint16_t *x, int M, int K, float g, uint8_t *q, uint8_t *s);
+void orc_nvfp4_dequant(const uint8_t *q, const uint8_t *s, int K, float g, double *out);
 void orc_mat_row(const orc_mat *m, int K, int n, double *out);
 
 /* ---- router ---- */

@@ -45,7 +45,9 @@ class orc_layer(C.Structure):
                 ("x", C.c_void_p), ("residual", C.c_void_p), ("gamma", C.c_void_p),
                 ("Wr", C.c_void_p), ("bias", C.c_void_p),
                 ("w13", C.POINTER(orc_mat)), ("w2", C.POINTER(orc_mat)),
-                ("sh13", orc_mat), ("sh2", orc_mat), ("swiglu_limit", C.c_double)]
+                ("sh13", orc_mat), ("sh2", orc_mat), ("swiglu_limit", C.c_double),
+                ("act_fmt", C.c_int), ("x_gscale", C.c_float), ("h_gscale", C.c_void_p),
+                ("sh_h_gscale", C.c_float)]
 
 
 _lib = None
@@ -74,6 +76,12 @@ def lib():
         L.orc_mxfp8_quant_bf16.argtypes = [vp, C.c_int, C.c_int, vp, vp]
         L.orc_mxfp8_quant_f64.argtypes = [vp, C.c_int, C.c_int, vp, vp]
         L.orc_mxfp8_dequant.argtypes = [vp, vp, C.c_int, vp]
+        L.orc_e2m1_rne_sat.restype = u8
+        L.orc_e2m1_rne_sat.argtypes = [f32]
+        L.orc_nvfp4_quant_block.argtypes = [vp, f32, vp, vp]
+        L.orc_nvfp4_quant_f32.argtypes = [vp, C.c_int, C.c_int, f32, vp, vp]
+        L.orc_nvfp4_quant_bf16.argtypes = [vp, C.c_int, C.c_int, f32, vp, vp]
+        L.orc_nvfp4_dequant.argtypes = [vp, vp, C.c_int, f32, vp]
         L.orc_mat_row.argtypes = [C.POINTER(orc_mat), C.c_int, C.c_int, vp]
         L.orc_router_logits.argtypes = [vp, vp, C.c_int, C.c_int, C.c_int, vp]
         L.orc_topk_row.argtypes = [vp, vp, C.c_int, C.c_int, d, vp, vp, vp]
@@ -154,6 +162,40 @@ def mxfp8_quant_bf16(x: np.ndarray):
     s = np.empty((M, K // 32), np.uint8)
     lib().orc_mxfp8_quant_bf16(_p(x), M, K, _p(q), _p(s))
     return q, s
+
+
+def e2m1_rne_sat(v: float) -> int:
+    return int(lib().orc_e2m1_rne_sat(float(v)))
+
+
+def nvfp4_quant_f32(v: np.ndarray, g: float):
+    """NVFP4 activation quant of fp32 rows [M, K] with global g: codes [M, K/2]
+    (even element in the low nibble), E4M3 scales [M, K/16]."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    M, K = v.shape
+    q = np.empty((M, K // 2), np.uint8)
+    s = np.empty((M, K // 16), np.uint8)
+    lib().orc_nvfp4_quant_f32(_p(v), M, K, float(g), _p(q), _p(s))
+    return q, s
+
+
+def nvfp4_quant_bf16(x: np.ndarray, g: float):
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    M, K = x.shape
+    q = np.empty((M, K // 2), np.uint8)
+    s = np.empty((M, K // 16), np.uint8)
+    lib().orc_nvfp4_quant_bf16(_p(x), M, K, float(g), _p(q), _p(s))
+    return q, s
+
+
+def nvfp4_dequant(q: np.ndarray, s: np.ndarray, g: float) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    M, K = q.shape[0], 2 * q.shape[1]
+    out = np.empty((M, K), np.float64)
+    for r in range(M):
+        lib().orc_nvfp4_dequant(_p(q[r]), _p(s[r]), K, float(g), _p(out[r]))
+    return out
 
 
 def mxfp8_dequant(q: np.ndarray, s: np.ndarray) -> np.ndarray:
@@ -319,10 +361,12 @@ class Layer:
         self.gamma = np.ascontiguousarray(inp.gamma, np.uint16)
         self.Wr = np.ascontiguousarray(inp.Wr, np.float32)
         self.bias = None if inp.bias is None else np.ascontiguousarray(inp.bias, np.float32)
+        self.h_g = None if inp.h_gscale is None else np.ascontiguousarray(inp.h_gscale, np.float32)
         self.c = orc_layer(sh.M, sh.H, sh.E, sh.k, sh.I, sh.I_sh, sh.wfmt, sh.sfmt,
                            float(sh.routed_scale), float(sh.eps), _p(self.x), _p(self.x),
                            _p(self.gamma), _p(self.Wr), _p(self.bias), arr13, arr2,
-                           self.sh13.c(), self.sh2.c(), float(sh.swiglu_limit))
+                           self.sh13.c(), self.sh2.c(), float(sh.swiglu_limit), int(sh.act_fmt),
+                           float(inp.x_gscale), _p(self.h_g), float(inp.sh_h_gscale))
 
     def rows(self, rows, logits=None, nthreads=0, want_h=False):
         sh = self.inp.shape
@@ -336,8 +380,9 @@ class Layer:
         w = np.empty((n, sh.k), np.float32)
         y = np.empty((n, sh.k, sh.H), np.float64)
         ysh = np.zeros((n, sh.H), np.float64)
-        hq = np.empty((n, sh.k, sh.I), np.uint8) if want_h else None
-        hs = np.empty((n, sh.k, sh.I // 32), np.uint8) if want_h else None
+        a4 = sh.act_fmt == 1
+        hq = np.empty((n, sh.k, sh.I // 2 if a4 else sh.I), np.uint8) if want_h else None
+        hs = np.empty((n, sh.k, sh.I // 16 if a4 else sh.I // 32), np.uint8) if want_h else None
         rc = lib().orc_moe_rows(C.byref(self.c), _p(lg), _p(rows), n, int(nthreads), _p(out64),
                                 _p(ob), _p(ro), _p(ids), _p(w), _p(y), _p(ysh), _p(hq), _p(hs))
         if rc != 0:

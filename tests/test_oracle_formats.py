@@ -250,3 +250,111 @@ def test_mxfp8_zero_and_special_blocks(orc):
     x = np.full((1, 32), 0x0001, np.uint16)  # 2^-133
     q, s = orc.mxfp8_quant_bf16(x)
     assert s[0, 0] == 0 and orc.e4m3_table()[q[0, 0]] == 2.0 ** -6
+
+
+# ---- NVFP4 activations --------------------------------------------------------
+
+def _e2m1_by_quantum(a: np.ndarray) -> np.ndarray:
+    """E2M1 magnitude of |a| as ordinary rounding to the format's spacing:
+    0.5 below 2, 1 below 4, 2 above; numpy's rint rounds halves to even
+    multiples, which are the even codes; saturating at 6."""
+    a = np.abs(a.astype(np.float64))
+    q = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+    return np.minimum(np.rint(a / q) * q, 6.0)
+
+
+E2M1_MAG = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+
+
+def test_e2m1_encoder_matches_quantum_rounding(orc):
+    # every multiple of 1/64 in [0, 8], the midpoints included, and random values
+    rng = np.random.default_rng(7)
+    vals = np.concatenate([np.arange(0, 8.0001, 1 / 64), rng.random(4000) * 9]).astype(np.float32)
+    for v in vals:
+        for sgn in (1.0, -1.0):
+            c = orc.e2m1_rne_sat(sgn * float(v))
+            assert (c >> 3) == (1 if sgn < 0 else 0)
+            assert E2M1_MAG[c & 7] == _e2m1_by_quantum(np.array([v]))[0], (v, c)
+    assert orc.e2m1_rne_sat(-0.0) == 8 and orc.e2m1_rne_sat(1e30) == 7
+
+
+def _nvfp4_block_independent(v: np.ndarray, g: float):
+    """The stated rule re-derived with numpy fp32 arithmetic and torch's E4M3."""
+    v = v.astype(np.float32)
+    g = np.float32(g)
+    if not np.all(np.isfinite(v)):
+        return np.zeros(8, np.uint8), 0x7F
+    amax = np.max(np.abs(v))
+    s = np.float32(amax) / np.float32(np.float32(6.0) * g)
+    s = min(float(s), 448.0)
+    sc = int(torch.tensor([s], dtype=torch.float64).to(torch.float8_e4m3fn).view(torch.uint8)[0])
+    sd = np.float32(torch.tensor([sc], dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)[0])
+    if sd == 0:
+        return np.zeros(8, np.uint8), sc
+    d = np.float32(sd * g)
+    qv = (v / d).astype(np.float32)
+    mag = _e2m1_by_quantum(qv)
+    codes = np.array([E2M1_MAG.index(m) for m in mag]) | (np.signbit(qv).astype(int) << 3)
+    return (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8), sc
+
+
+def test_nvfp4_block_rule_independent(orc):
+    rng = np.random.default_rng(8)
+    for t in range(3000):
+        g = float(np.float32(np.exp2(rng.uniform(-12, 2))))
+        v = (rng.standard_normal(16) * np.exp2(rng.uniform(-8, 8))).astype(np.float32)
+        if t % 7 == 0:
+            v[rng.integers(16)] = 0.0
+        if t % 11 == 0:
+            v = v * np.float32(1e4)          # scales saturate at 448
+        q, s = orc.nvfp4_quant_f32(v[None, :], g)
+        rq, rs = _nvfp4_block_independent(v, g)
+        assert s[0, 0] == rs and np.array_equal(q[0], rq), (t, v, g)
+
+
+def test_nvfp4_roundtrip_on_representable(orc):
+    """Values e2m1 * E4M3 * g whose block holds a +-6 element decode exactly
+    (g a power of two keeps every fp32 step exact)."""
+    rng = np.random.default_rng(9)
+    e4 = torch.arange(1, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for _ in range(500):
+        g = float(np.exp2(rng.integers(-10, 3)))
+        sd = float(e4[rng.integers(len(e4))])
+        mags = np.array(E2M1_MAG)[rng.integers(0, 8, 16)]
+        mags[rng.integers(16)] = 6.0
+        v = (mags * np.where(rng.random(16) < 0.5, -1, 1) * sd * g).astype(np.float32)
+        q, s = orc.nvfp4_quant_f32(v[None, :], g)
+        back = orc.nvfp4_dequant(q, s, g)[0]
+        assert np.array_equal(back, v.astype(np.float64)), (v, back)
+
+
+def test_nvfp4_zero_special_and_saturated_blocks(orc):
+    z = np.zeros((1, 16), np.float32)
+    q, s = orc.nvfp4_quant_f32(z, 0.25)
+    assert s[0, 0] == 0 and not q.any()
+    for bad in (np.nan, np.inf, -np.inf):
+        v = np.ones((1, 32), np.float32)
+        v[0, 3] = bad
+        q, s = orc.nvfp4_quant_f32(v, 1.0)
+        assert s[0, 0] == 0x7F and not q[0, :8].any()       # the block holding it
+        # the other block: amax 1, s = 1/6 = 2^-3 * 1.33.., nearest E4M3 2^-3 * 1.375 = code 0x23
+        assert s[0, 1] == 0x23
+        assert np.isnan(orc.nvfp4_dequant(q, s, 1.0)[0, :16]).all()
+    # amax far above 6 * 448 * g: scale 448, elements clip at 6
+    v = np.full((1, 16), 1e6, np.float32)
+    q, s = orc.nvfp4_quant_f32(v, 1.0)
+    assert s[0, 0] == 0x7E and np.all(q == 0x77)
+    # a block whose scale underflows E4M3 (below half of 2^-9) encodes zeros
+    v = np.full((1, 16), 1e-6, np.float32)
+    q, s = orc.nvfp4_quant_f32(v, 1.0)
+    assert s[0, 0] == 0 and not q.any()
+
+
+def test_nvfp4_bf16_rows_equal_f32_rows(orc):
+    rng = np.random.default_rng(10)
+    x = (rng.standard_normal((5, 256)).astype(np.float32))
+    xb = ((x.view(np.uint32) >> 16).astype(np.uint16))
+    xf = (xb.astype(np.uint32) << 16).view(np.float32)
+    a = orc.nvfp4_quant_bf16(xb, 0.003)
+    b = orc.nvfp4_quant_f32(xf, 0.003)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

@@ -58,11 +58,15 @@ def clamp_gu(g, u, limit):
     return g, u
 
 
-def textbook_expert(orc, m13, m2, I, a, limit=0.0):
-    """a: dequantized activation [H]; returns y [H] with the layer's requant."""
+def textbook_expert(orc, m13, m2, I, a, limit=0.0, h_g=None):
+    """a: dequantized activation [H]; returns y [H] with the layer's requant of
+    h: MXFP8, or NVFP4 with global h_g (the rule reads h in fp32)."""
     W13, W2 = dense(m13), dense(m2)
     g, u = clamp_gu(W13[:I] @ a, W13[I:] @ a, limit)
     h = g / (1 + np.exp(-g)) * u
+    if h_g is not None:
+        q, s = orc.nvfp4_quant_f32(h[None, :].astype(np.float32), h_g)
+        return W2 @ orc.nvfp4_dequant(q, s, h_g)[0]
     q, s = orc.mxfp8_quant_f64(h[None, :])
     return W2 @ mx_dequant(q, s)[0]
 
@@ -79,6 +83,9 @@ def _layer(orc, shape, seed, **kw):
 
 
 def _act(orc, inp, r):
+    if inp.shape.act_fmt == synth.ACT_NVFP4:
+        q, s = orc.nvfp4_quant_bf16(inp.x[r:r + 1], inp.x_gscale)
+        return orc.nvfp4_dequant(q, s, inp.x_gscale)[0]
     q, s = orc.mxfp8_quant_bf16(inp.x[r:r + 1])
     return mx_dequant(q, s)[0]
 
@@ -98,21 +105,27 @@ def test_single_expert_is_textbook_swiglu_mlp(orc, wfmt):
         assert np.allclose(res["out64"][r], out, rtol=1e-12, atol=1e-14)
 
 
-@pytest.mark.parametrize("wfmt,sfmt,limit", [(synth.MXFP4, synth.NONE, 0.0), (synth.NVFP4, synth.BF16, 0.0),
-                                             (synth.MXFP4, synth.MXFP4, 0.0), (synth.NVFP4, synth.BF16, 0.06),
-                                             (synth.MXFP4, synth.MXFP4, 0.05)])
-def test_sparse_routing_equals_dense_zero_weighted_mixture(orc, wfmt, sfmt, limit):
+A4 = synth.ACT_NVFP4
+
+
+@pytest.mark.parametrize("wfmt,sfmt,limit,act", [(synth.MXFP4, synth.NONE, 0.0, 0), (synth.NVFP4, synth.BF16, 0.0, 0),
+                                                 (synth.MXFP4, synth.MXFP4, 0.0, 0), (synth.NVFP4, synth.BF16, 0.06, 0),
+                                                 (synth.MXFP4, synth.MXFP4, 0.05, 0), (synth.NVFP4, synth.NONE, 0.0, A4),
+                                                 (synth.NVFP4, synth.NVFP4, 0.0, A4), (synth.NVFP4, synth.BF16, 0.06, A4)])
+def test_sparse_routing_equals_dense_zero_weighted_mixture(orc, wfmt, sfmt, limit, act):
     """Also with the clamped SwiGLU (limit > 0, small enough that most gate and
-    up values of these rows cross it) in the routed and the shared experts."""
+    up values of these rows cross it) in the routed and the shared experts, and
+    with NVFP4 activations (the input and each h quantized with their globals)."""
     sh = synth.custom_shape(M=4, H=128, E=6, k=3, I=64, wfmt=wfmt, sfmt=sfmt, I_sh=96,
-                            routed_scale=2.5, bias="normal:0.05", swiglu_limit=limit)
+                            routed_scale=2.5, bias="normal:0.05", swiglu_limit=limit, act_fmt=act)
     inp, L = _layer(orc, sh, 6)
     inp = synth.vary_globals(inp, 9)
     L = orc.Layer(inp)
     res = L.rows(np.arange(sh.M))
     for r in range(sh.M):
         a = _act(orc, inp, r)
-        ys = np.stack([textbook_expert(orc, inp.w13.expert(e), inp.w2.expert(e), sh.I, a, limit)
+        hg = (lambda e: float(inp.h_gscale[e])) if act == A4 else (lambda e: None)
+        ys = np.stack([textbook_expert(orc, inp.w13.expert(e), inp.w2.expert(e), sh.I, a, limit, hg(e))
                        for e in range(sh.E)])
         wd = np.zeros(sh.E)
         wd[res["ids"][r]] = res["w"][r]  # zero weight on unchosen experts
@@ -123,8 +136,9 @@ def test_sparse_routing_equals_dense_zero_weighted_mixture(orc, wfmt, sfmt, limi
             g, u = clamp_gu(W13[:sh.I_sh] @ xv, W13[sh.I_sh:] @ xv, limit)
             hb = bf16v(orc.bf16_rne_n(g / (1 + np.exp(-g)) * u))
             t = t + W2 @ hb
-        elif sfmt == synth.MXFP4:
-            t = t + textbook_expert(orc, inp.sh13, inp.sh2, sh.I_sh, a, limit)
+        elif sfmt in (synth.MXFP4, synth.NVFP4):
+            t = t + textbook_expert(orc, inp.sh13, inp.sh2, sh.I_sh, a, limit,
+                                    inp.sh_h_gscale if act == A4 else None)
         out, rb = textbook_norm(orc, t, inp.gamma, sh.eps)
         assert np.array_equal(res["resid_out"][r], rb)
         assert np.allclose(res["out64"][r], out, rtol=1e-11, atol=1e-13)

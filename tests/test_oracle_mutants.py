@@ -55,6 +55,20 @@ MUTANTS = {
     "tiles of 7": ("tile_rows[t] = (n - 8 * i < 8) ? (n - 8 * i) : 8;", "tile_rows[t] = (n - 8 * i < 8) ? (n - 8 * i) : 7;"),
     "bucket rows descending": ("        for (int r = 0; r < M; ++r)\n            for (int j = 0; j < k; ++j)\n                if (ids[(size_t)r * k + j] == e)",
                                "        for (int r = M - 1; r >= 0; --r)\n            for (int j = 0; j < k; ++j)\n                if (ids[(size_t)r * k + j] == e)"),
+    "E2M1 ties to the larger code": ("if (dc < db || (dc == db && (c & 1) == 0))", "if (dc < db || dc == db)"),
+    "NVFP4 scale without the 6": ("const float t = 6.0f * g;", "const float t = g;"),
+    "NVFP4 codes ignore the global": ("const float d = sd * g;", "const float d = sd;"),
+    "NVFP4 nibbles swapped in the encoder": ("q8[i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));",
+                                            "q8[i] = (uint8_t)(codes[2 * i + 1] | (codes[2 * i] << 4));"),
+    "NVFP4 nibbles swapped in the decoder": ("const int code = (i & 1) ? (q[i / 2] >> 4) : (q[i / 2] & 15);",
+                                            "const int code = (i & 1) ? (q[i / 2] & 15) : (q[i / 2] >> 4);"),
+    "NVFP4 non-finite block kept": ("        if (!isfinite(v[i]))\n            finite = 0;\n        else if",
+                                    "        if (0)\n            finite = 0;\n        else if"),
+    "W4A4 input quantized as MXFP8": ("    if (L->act_fmt == ORC_ACT_NVFP4) {\n        orc_nvfp4_quant_bf16(",
+                                      "    if (0) {\n        orc_nvfp4_quant_bf16("),
+    "W4A4 h requant without its global": ("orc_nvfp4_quant_f32(hf, 1, I, h_g, q, s);",
+                                          "orc_nvfp4_quant_f32(hf, 1, I, 1.0f, q, s);"),
+    "W4A4 shared h with a routed global": ("L->act_fmt, L->sh_h_gscale, ysh,", "L->act_fmt, L->h_gscale[0], ysh,"),
     "E4M3 not saturating": ("    if (r > 448.0)\n        r = 448.0;\n", ""),
 }
 
