@@ -45,6 +45,29 @@ __global__ __launch_bounds__(256) void k_quant_pairs(const uint16_t* __restrict_
     }
 }
 
+// NVFP4 activations (rule in quant_dev.h): one thread per 16-value block, 32
+// bytes in, 8 code bytes + one scale byte out.  With a bucket, rows in bucket
+// order (row b = token bucket[b] / k); without, row order.
+__global__ __launch_bounds__(256) void k_quant_nvfp4(const uint16_t* __restrict__ x, const int32_t* __restrict__ bucket,
+                                                     int k, int rows, int K, float g, uint8_t* __restrict__ q,
+                                                     uint8_t* __restrict__ s) {
+    const int bpr = K / 16;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    const int row = idx / bpr, blk = idx - row * bpr;
+    if (row >= rows) return;
+    const int tok = bucket ? bucket[row] / k : row;
+    quant_nvfp4_bf16x16(x + (size_t)tok * K + 16 * blk, g, q + (size_t)row * (K / 2) + 8 * blk,
+                        s + (size_t)row * bpr + blk);
+}
+
+hipError_t launch_quant_nvfp4(const uint16_t* x, const int32_t* bucket, int k, int rows, int K, float g, uint8_t* q,
+                              uint8_t* s, hipStream_t stream) {
+    const long n = (long)rows * (K / 16);
+    hipLaunchKernelGGL(k_quant_nvfp4, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, x, bucket, k, rows, K, g,
+                       q, s);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant_mxfp8(const uint16_t* x, int M, int K, uint8_t* q, uint8_t* s,
                               hipStream_t stream) {
     const int nblocks = M * (K / 32);

@@ -197,6 +197,20 @@ int moe_quant_act_mxfp8(const uint16_t* x, int M, int K, const moe_routing* rout
     return hip_status(launch_quant_pairs(x, route->bucket, k, M, K, q, s, nullptr, nullptr, stream));
 }
 
+int moe_quant_act_nvfp4(const uint16_t* x, int M, int K, float global, const moe_routing* route, int k, uint8_t* q,
+                        uint8_t* s, hipStream_t stream) {
+    if (!x || !q || !s || M < 1 || K < 32) return MOE_ERR_INVALID_ARG;
+    if (!(global > 0.0f) || !(global <= 3.4e38f)) return MOE_ERR_INVALID_ARG;
+    if (K % 32 != 0 || K > kMaxH) return MOE_ERR_UNSUPPORTED;
+    if (!route) {
+        if (M > kMaxM * kMaxK) return MOE_ERR_UNSUPPORTED;
+        return hip_status(launch_quant_nvfp4(x, nullptr, 1, M, K, global, q, s, stream));
+    }
+    if (!route->bucket) return MOE_ERR_INVALID_ARG;
+    if (k < 1 || k > kMaxK || M > kMaxM) return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_quant_nvfp4(x, route->bucket, k, M * k, K, global, q, s, stream));
+}
+
 size_t moe_gate_up_workspace_bytes(int fmt, int M, int H, int I, int E, int k, int dense) {
     if (check_dims(M, H, dense ? 1 : E, dense ? 1 : k) != MOE_OK) return 0;
     if (I < 128 || I % 128 != 0 || I > kMaxI) return 0;

@@ -65,6 +65,10 @@ hipError_t launch_pack_fp4(int fmt, int E, int N, int K, const uint8_t* w, const
 
 hipError_t launch_quant_mxfp8(const uint16_t* x, int M, int K, uint8_t* q, uint8_t* s,
                               hipStream_t stream);
+// NVFP4 activations with global g: codes [rows][K/2], scales [rows][K/16];
+// bucket != nullptr: row b is token bucket[b] / k (rows = M*k), else row order.
+hipError_t launch_quant_nvfp4(const uint16_t* x, const int32_t* bucket, int k, int rows, int K, float g, uint8_t* q,
+                              uint8_t* s, hipStream_t stream);
 // MXFP8 rows in bucket order: qp/sp row b holds token bucket[b] / k (P = M*k
 // rows); with qt != nullptr also the M token-ordered rows into qt/st.
 hipError_t launch_quant_pairs(const uint16_t* x, const int32_t* bucket, int k, int M, int K, uint8_t* qp,

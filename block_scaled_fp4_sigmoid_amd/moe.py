@@ -22,7 +22,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 
 EXPORTS = ["moe_status_str", "moe_abi_version", "moe_tile_capacity", "moe_packed_scale_bytes",
            "moe_pack_fp4", "moe_route_workspace_bytes",
-           "moe_route_topk", "moe_quant_act_mxfp8", "moe_gate_up_workspace_bytes",
+           "moe_route_topk", "moe_quant_act_mxfp8", "moe_quant_act_nvfp4", "moe_gate_up_workspace_bytes",
            "moe_expert_gate_up", "moe_expert_down", "moe_finalize_rmsnorm",
            "moe_finalize_rmsnorm_mxfp8", "moe_layer_workspace_bytes", "moe_layer",
            "moe_layer_mxfp8_out"]
@@ -74,6 +74,8 @@ def lib() -> C.CDLL:
         L.moe_route_topk.argtypes = [vp, vp, vp, vp, i, i, i, i, f, vp, C.POINTER(moe_routing), vp, sz, vp]
         L.moe_quant_act_mxfp8.restype = i
         L.moe_quant_act_mxfp8.argtypes = [vp, i, i, C.POINTER(moe_routing), i, vp, vp, vp]
+        L.moe_quant_act_nvfp4.restype = i
+        L.moe_quant_act_nvfp4.argtypes = [vp, i, i, f, C.POINTER(moe_routing), i, vp, vp, vp]
         L.moe_gate_up_workspace_bytes.restype = sz
         L.moe_gate_up_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         L.moe_expert_gate_up.restype = i
@@ -217,6 +219,16 @@ def quant_act_mxfp8(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, routing: 
     k = 0 if routing is None else routing.k
     _check(lib().moe_quant_act_mxfp8(_p(x), M, K, None if r is None else C.byref(r), k, _p(q), _p(s),
                                      _stream(stream)), "moe_quant_act_mxfp8")
+
+
+def quant_act_nvfp4(x: torch.Tensor, g: float, q: torch.Tensor, s: torch.Tensor,
+                    routing: Optional["Routing"] = None, stream=None):
+    """NVFP4 of bf16 rows with global g: q [rows, K/2], s [rows, K/16]."""
+    M, K = x.shape
+    r = None if routing is None else routing.c()
+    rc = lib().moe_quant_act_nvfp4(_p(x), M, K, float(g), None if r is None else C.byref(r),
+                                   routing.k if routing is not None else 0, _p(q), _p(s), _stream(stream))
+    _check(rc, "moe_quant_act_nvfp4")
 
 
 def expert_gate_up(w13: Weights, M, H, I, E, k, routing: Optional[Routing] = None, a_q=None,

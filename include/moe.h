@@ -200,6 +200,26 @@ int moe_quant_act_mxfp8(const uint16_t *x, int M, int K, const moe_routing *rout
                         uint8_t *q, uint8_t *s, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_quant_act_nvfp4 — one-pass NVFP4 quantization of bf16 rows (the input
+ * of NVFP4 experts run with NVFP4 activations).
+ *   Pages: README Qwen3.5 slot table, row "route" (the MoE input quantized to
+ *   NVFP4 in the router's launch); SGLang Spark GB10 Optimizations, section 1
+ *   (NVFP4 K-groups of 16 with FP8 scales).
+ * Rule (the pages state none; the NVFP4 weight encoding with a static global,
+ * every step in fp32): per 16 values, a block holding a NaN or Inf gets scale
+ * 0x7F and codes 0; else s = amax / (6 * global) (product rounded, then the
+ * quotient), scale = E4M3 RNE of s saturating at 448, sd its value; sd == 0
+ * gives codes 0; else code = E2M1 RNE of x / (sd * global) (product, then the
+ * quotient) saturating at 6, with the quotient's sign.  value = E2M1(code) *
+ * E4M3(scale) * global.
+ * x: bf16 [M, K]; global: fp32 > 0 (finite); q: uint8 [rows, K/2], two codes
+ * per byte, the even element in the low nibble; s: uint8 [rows, K/16].
+ * route == NULL: rows = M, row order; else rows = M*k in bucket order (row b
+ * = token route->bucket[b] / k), as moe_quant_act_mxfp8.  K % 32 == 0. */
+int moe_quant_act_nvfp4(const uint16_t *x, int M, int K, float global, const moe_routing *route, int k,
+                        uint8_t *q, uint8_t *s, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_expert_gate_up — gate_up GEMM of every routed expert over its rows,
  * SwiGLU, and requantization of the result for the down GEMM.
  *   Pages: README Qwen3.5 slot table, row "mkm" (FC1, SwiGLU, requant, FC2);

@@ -141,6 +141,11 @@ def test_calls_refuse_before_enqueueing(L):
     assert L.moe_finalize_rmsnorm_mxfp8(*fin[:5], -1.0, *fin[6:], 0x1000, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_quant_act_mxfp8(None, 4, 64, None, 0, 0x1000, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_quant_act_mxfp8(0x1000, 4, 48, None, 0, 0x1000, 0x1000, None) == moe.MOE_ERR_UNSUPPORTED
+    # NVFP4 activations: the global must be positive and finite
+    for g in (0.0, -1.0, float("nan"), float("inf")):
+        assert L.moe_quant_act_nvfp4(0x1000, 4, 64, g, None, 0, 0x1000, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quant_act_nvfp4(0x1000, 4, 48, 1.0, None, 0, 0x1000, 0x1000, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_quant_act_nvfp4(None, 4, 64, 1.0, None, 0, 0x1000, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
     r = moe.moe_routing()  # bucket missing
     assert L.moe_quant_act_mxfp8(0x1000, 4, 64, C.byref(r), 2, 0x1000, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
     r.bucket = 0x1000

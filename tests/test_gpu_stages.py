@@ -37,6 +37,43 @@ def test_quant_mxfp8_bitexact():
     assert np.array_equal(np_of(q), rq)
 
 
+@pytest.mark.parametrize("routed", [False, True])
+def test_quant_nvfp4_bitexact(routed):
+    """NVFP4 activations, byte for byte against the oracle's rule (both sides
+    decide every code in fp32), in row order and in bucket order."""
+    rng = np.random.default_rng(11)
+    M, K = 37, 1024  # ragged row count
+    x = rng.standard_normal((M, K)).astype(np.float32) * np.exp2(rng.integers(-30, 30, (M, K // 16, 1))).repeat(16, 2).reshape(M, K)
+    x[0, :16] = 0.0
+    x[0, 16:32] = -0.0
+    x[1, :16] = 1e-39               # bf16 subnormals
+    x[2, 5] = np.nan
+    x[3, 70] = np.inf
+    x[4, :16] = 1e30                # scale saturates at 448, codes at 6
+    x[5, 32:48] = np.float32(6 * 448) * np.float32(0.01)
+    xb = synth._bf16_trunc(x)
+    xt = torch.from_numpy(xb.view(np.int16)).to(DEV)
+    g = float(np.float32(0.0123))
+    if routed:
+        E, k = 8, 3
+        rt = moe.Routing(M, E, k, DEV)
+        logits = torch.from_numpy(rng.standard_normal((M, E)).astype(np.float32)).to(DEV)
+        moe.route_topk(rt, logits_in=logits)
+        rows = M * k
+    else:
+        rt, rows = None, M
+    q = torch.full((rows, K // 2), 0x5a, dtype=torch.uint8, device=DEV)
+    s = torch.full((rows, K // 16), 0x5a, dtype=torch.uint8, device=DEV)
+    moe.quant_act_nvfp4(xt, g, q, s, routing=rt)
+    torch.cuda.synchronize()
+    rq, rs = orc.nvfp4_quant_bf16(xb, g)
+    if routed:
+        tok = np_of(rt.bucket) // k
+        rq, rs = rq[tok], rs[tok]
+    assert np.array_equal(np_of(s), rs)
+    assert np.array_equal(np_of(q), rq)
+
+
 ROUTE_CASES = [
     # M, H, E, k, bias, scale
     (4, 1024, 16, 4, "normal:0.01", 1.0),
