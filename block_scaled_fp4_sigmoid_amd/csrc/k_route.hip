@@ -56,14 +56,18 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
                                                          int kchunk, int units, int nmain,
                                                          float* __restrict__ partials, int nquant,
                                                          uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
-                                                         Bf16Side side, int stage) {
+                                                         float xg4, Bf16Side side, int stage) {
     if ((int)blockIdx.x >= nmain + nquant) {  // a bf16 shared-expert stage riding along
         bf16_side_block(side, stage, blockIdx.x - nmain - nquant);
         return;
     }
-    if ((int)blockIdx.x >= nmain) {  // MXFP8 of x in token order: 256 blocks of 32 values
-        const int b = (blockIdx.x - nmain) * 256 + threadIdx.x;
-        if (b < M * (H / 32)) quant_block32(x + (size_t)b * 32, xq + (size_t)b * 32, xs + b);
+    if ((int)blockIdx.x >= nmain) {  // x in token order: MXFP8 (256 blocks of 32 values), or
+        const int b = (blockIdx.x - nmain) * 256 + threadIdx.x;  // NVFP4 with global xg4 > 0 (of 16)
+        if (xg4 > 0.0f) {
+            if (b < M * (H / 16)) quant_nvfp4_bf16x16(x + (size_t)b * 16, xg4, xq + (size_t)b * 8, xs + b);
+        } else if (b < M * (H / 32)) {
+            quant_block32(x + (size_t)b * 32, xq + (size_t)b * 32, xs + b);
+        }
         return;
     }
     const int wave = threadIdx.x >> 6;
@@ -153,22 +157,22 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
 
 hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int M, int H, int E,
                                   const RouterPlan& plan, float* partials, uint8_t* xq, uint8_t* xs,
-                                  const Bf16Side& side1, int stage1, hipStream_t stream) {
+                                  const Bf16Side& side1, int stage1, hipStream_t stream, float xg4) {
     const int units = ((E + 15) / 16) * plan.splits * plan.row_groups;
     const int blocks = (units + 3) / 4;
-    const int nquant = xq ? (M * (H / 32) + 255) / 256 : 0;
+    const int nquant = xq ? (M * (H / (xg4 > 0.0f ? 16 : 32)) + 255) / 256 : 0;
     const int extra = stage1 == kBf16None ? 0 : side1.blocks;
     const dim3 g(blocks + nquant + extra), b(256);
     const bool wide = plan.kchunk % 256 == 0, one = M <= 16;  // (four row blocks keep U = 4: registers)
     if (wide && one)
         hipLaunchKernelGGL((k_router_partials<8, 1>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
-                           units, blocks, partials, nquant, xq, xs, side1, stage1);
+                           units, blocks, partials, nquant, xq, xs, xg4, side1, stage1);
     else if (one)
         hipLaunchKernelGGL((k_router_partials<4, 1>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
-                           units, blocks, partials, nquant, xq, xs, side1, stage1);
+                           units, blocks, partials, nquant, xq, xs, xg4, side1, stage1);
     else
         hipLaunchKernelGGL((k_router_partials<4, 4>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
-                           units, blocks, partials, nquant, xq, xs, side1, stage1);
+                           units, blocks, partials, nquant, xq, xs, xg4, side1, stage1);
     return hipGetLastError();
 }
 

@@ -46,6 +46,7 @@
 #include "dense_bf16_dev.h"
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "quant_dev.h"
 #include "route_dev.h"
 
 #include <algorithm>
@@ -56,6 +57,11 @@ namespace {
 
 constexpr int kFmtMX = MOE_FMT_MXFP4;
 constexpr int kFmtNV = MOE_FMT_NVFP4;
+constexpr int kFmtNV4 = 16;  // NVFP4 weights with NVFP4 activations (FMT of the templates only)
+template <int F>
+constexpr bool kNVW = F == kFmtNV || F == kFmtNV4;  // NVFP4 weights
+template <int F>
+constexpr bool kA4 = F == kFmtNV4;  // NVFP4 activations
 constexpr int kThreads = 256;
 constexpr int kPassRows = 32;           // activation rows per pass (two 16-row N-blocks)
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every record count
@@ -110,7 +116,14 @@ struct StreamJob {
     // down launch (active experts, bucket ranges, count, bucket), or nullptr
     int32_t *r_act, *r_off, *r_na, *r_bkt;
     float limit;            // gate_up: clamped SwiGLU limit (0: unclamped)
+    // NVFP4 activations: their global (ag, or age[e] per expert) and the
+    // global of the h a gate_up writes (hg, or hge[e])
+    float ag, hg;
+    const float *age, *hge;
 };
+
+__device__ __forceinline__ float act_global(const StreamJob& J, int e) { return J.age ? J.age[e] : J.ag; }
+__device__ __forceinline__ float out_global(const StreamJob& J, int e) { return J.hge ? J.hge[e] : J.hg; }
 
 struct Tokens {
     int e, base, n;
@@ -246,6 +259,20 @@ __device__ __forceinline__ v8h fp8x8_to_f16(uint32_t d0, uint32_t d1, float sf) 
 // 2^(smax - 127) (activation offset) * global.
 __device__ __forceinline__ float nv_row_factor(int smax, float gs) { return ldexpf(gs, smax - 127); }
 
+// NVFP4 activations enter the f16 MFMA exactly: E2M1 * E4M3 has at most six
+// significant bits and lies in [2^-10, 2688].  The lane's 32 codes of a step
+// (16 bytes, K [32g, +32)) and the dword holding its two scale bytes (bytes
+// 2(g & 1), +1) -> the four B operands (the order nv_dequant8 gives weights).
+__device__ __forceinline__ void act4_to_f16(const v4i& b, uint32_t sdw, int g, v8h (&B)[4]) {
+    float sv0, sv1;
+    v2h m;
+    nv_scales2<0>(sdw >> (16 * (g & 1)), sv0, sv1, m);
+    B[0] = nv_dequant8((uint32_t)b.x, sv0, m[0]);
+    B[1] = nv_dequant8((uint32_t)b.y, sv0, m[0]);
+    B[2] = nv_dequant8((uint32_t)b.z, sv1, m[1]);
+    B[3] = nv_dequant8((uint32_t)b.w, sv1, m[1]);
+}
+
 // ---- coordinates and the ring -------------------------------------------------
 
 // Per-lane coordinates: MB blocks of 16 weight rows (packed layout), NB blocks
@@ -273,13 +300,15 @@ __device__ __forceinline__ Coord<FMT, MB, NB> make_coord(const StreamJob& J, int
     Coord<FMT, MB, NB> c;
     c.rw = make_rsrc(J.w + (size_t)e * wbytes, wbytes);
     c.rs = make_rsrc(J.sc + (size_t)e * sbytes, sbytes);
+    // activation row bytes: MXFP8 K codes + K/32 scales; NVFP4 K/2 + K/16
+    const int AQ = kA4<FMT> ? K / 2 : K, AS = kA4<FMT> ? K / 16 : K / 32;
     if (src) {  // gathered rows: the resources cover all of a_q
-        c.ra = make_rsrc(J.a_q, J.a_rows * (uint32_t)K);
-        c.ras = make_rsrc(J.a_s, J.a_rows * (uint32_t)(K / 32));
+        c.ra = make_rsrc(J.a_q, J.a_rows * (uint32_t)AQ);
+        c.ras = make_rsrc(J.a_s, J.a_rows * (uint32_t)AS);
     } else {  // the pass's rows only (offsets stay small)
         const uint32_t prow = (uint32_t)min(kPassRows, (int)J.a_rows - arow0);
-        c.ra = make_rsrc(J.a_q + (size_t)arow0 * K, prow * (uint32_t)K);
-        c.ras = make_rsrc(J.a_s + (size_t)arow0 * (K / 32), prow * (uint32_t)(K / 32));
+        c.ra = make_rsrc(J.a_q + (size_t)arow0 * AQ, prow * (uint32_t)AQ);
+        c.ras = make_rsrc(J.a_s + (size_t)arow0 * AS, prow * (uint32_t)AS);
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -292,9 +321,16 @@ __device__ __forceinline__ Coord<FMT, MB, NB> make_coord(const StreamJob& J, int
         const int t = 16 * j + i;
         const bool ok = t < npass;
         const uint32_t r = ok ? (src ? (uint32_t)src[t] : (uint32_t)t) : 0u;
-        // MX: bytes [16g, +16) and [64 + 16g, +16) of the step; NV: [32g, +32)
-        c.va[j] = ok ? r * K + (FMT == kFmtMX ? 16 : 32) * g : kOOB;
-        c.vas[j] = ok ? r * (K / 32) : kOOB;
+        // MX: bytes [16g, +16) and [64 + 16g, +16) of the step; NV: [32g, +32);
+        // NVFP4 activations: [16g, +16) of the step's 64, and the scale dword
+        // holding the lane's two scale bytes (2g, 2g + 1 of the step's 8)
+        if constexpr (kA4<FMT>) {
+            c.va[j] = ok ? r * (uint32_t)(K / 2) + 16 * g : kOOB;
+            c.vas[j] = ok ? r * (uint32_t)(K / 16) + 4 * (g >> 1) : kOOB;
+        } else {
+            c.va[j] = ok ? r * K + (FMT == kFmtMX ? 16 : 32) * g : kOOB;
+            c.vas[j] = ok ? r * (K / 32) : kOOB;
+        }
     }
     return c;
 }
@@ -321,9 +357,14 @@ __device__ __forceinline__ void ring_load_step(Ring<MB, NB, DQ, QS>& R, int v, i
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
         const uint32_t va = ok ? c.va[j] : kOOB;
-        R.b[v][u][j][0] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, va, 128 * st, 0);
-        R.b[v][u][j][1] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, va + (FMT == kFmtMX ? 64 : 16), 128 * st, 0);
-        R.bs[v][u][j] = __builtin_amdgcn_raw_buffer_load_b32(c.ras, ok ? c.vas[j] : kOOB, 4 * st, 0);
+        if constexpr (kA4<FMT>) {
+            R.b[v][u][j][0] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, va, 64 * st, 0);
+            R.bs[v][u][j] = __builtin_amdgcn_raw_buffer_load_b32(c.ras, ok ? c.vas[j] : kOOB, 8 * st, 0);
+        } else {
+            R.b[v][u][j][0] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, va, 128 * st, 0);
+            R.b[v][u][j][1] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, va + (FMT == kFmtMX ? 64 : 16), 128 * st, 0);
+            R.bs[v][u][j] = __builtin_amdgcn_raw_buffer_load_b32(c.ras, ok ? c.vas[j] : kOOB, 4 * st, 0);
+        }
     }
 }
 
@@ -369,13 +410,17 @@ __device__ __forceinline__ void mfma_step(const v4i (&a_)[MB], const uint32_t (&
         v8h B[NB][4];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            const v4i b0 = b[j][0], b1 = b[j][1];
-            const int sb = (int)((bs[j] >> (8 * g)) & 0xffu);
-            const float sf = exp2i(max(sb + sfo[j], -126));
-            B[j][0] = fp8x8_to_f16((uint32_t)b0.x, (uint32_t)b0.y, sf);
-            B[j][1] = fp8x8_to_f16((uint32_t)b0.z, (uint32_t)b0.w, sf);
-            B[j][2] = fp8x8_to_f16((uint32_t)b1.x, (uint32_t)b1.y, sf);
-            B[j][3] = fp8x8_to_f16((uint32_t)b1.z, (uint32_t)b1.w, sf);
+            if constexpr (kA4<FMT>) {
+                act4_to_f16(b[j][0], bs[j], g, B[j]);
+            } else {
+                const v4i b0 = b[j][0], b1 = b[j][1];
+                const int sb = (int)((bs[j] >> (8 * g)) & 0xffu);
+                const float sf = exp2i(max(sb + sfo[j], -126));
+                B[j][0] = fp8x8_to_f16((uint32_t)b0.x, (uint32_t)b0.y, sf);
+                B[j][1] = fp8x8_to_f16((uint32_t)b0.z, (uint32_t)b0.w, sf);
+                B[j][2] = fp8x8_to_f16((uint32_t)b1.x, (uint32_t)b1.y, sf);
+                B[j][3] = fp8x8_to_f16((uint32_t)b1.z, (uint32_t)b1.w, sf);
+            }
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -563,7 +608,9 @@ struct TileOffs {
     uint32_t s[2 * NB];
 };
 
-template <int NB>
+// A4 (NVFP4 activations): a chunk is 8 code bytes (16 values) and its one
+// E4M3 scale byte.
+template <int NB, bool A4>
 __device__ __forceinline__ TileOffs<NB> tile_offsets(int K, int npass, const int* src) {
     const int t = threadIdx.x;
     TileOffs<NB> o;
@@ -571,40 +618,61 @@ __device__ __forceinline__ TileOffs<NB> tile_offsets(int K, int npass, const int
     for (int k = 0; k < 2 * NB; ++k) {
         const int li = t + kThreads * k, row = li >> 5, ch = li & 31;
         const uint32_t r = row < npass ? (src ? (uint32_t)src[row] : (uint32_t)row) : 0u;
-        o.c[k] = row < npass ? r * (uint32_t)K + 16 * ch : kOOB;
-        o.s[k] = row < npass ? r * (uint32_t)(K / 32) + (ch >> 1) : kOOB;
+        if constexpr (A4) {
+            o.c[k] = row < npass ? r * (uint32_t)(K / 2) + 8 * ch : kOOB;
+            o.s[k] = row < npass ? r * (uint32_t)(K / 16) + ch : kOOB;
+        } else {
+            o.c[k] = row < npass ? r * (uint32_t)K + 16 * ch : kOOB;
+            o.s[k] = row < npass ? r * (uint32_t)(K / 32) + (ch >> 1) : kOOB;
+        }
     }
     return o;
 }
 
 // Requests the thread's share of tile q (absolute quad).  Rows past the pass
 // and steps at or past s_end read zeros.
-template <int NB>
-__device__ __forceinline__ void tile_load(ActShare<NB>& P, const Coord<kFmtNV, 1, NB>& c, const TileOffs<NB>& o,
+template <int NB, bool A4, int CF>
+__device__ __forceinline__ void tile_load(ActShare<NB>& P, const Coord<CF, 1, NB>& c, const TileOffs<NB>& o,
                                           int q, int s_end) {
     const int t = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < 2 * NB; ++k) {
         const int ch = (t + kThreads * k) & 31;
         const bool ok = o.c[k] != kOOB && 4 * q + (ch >> 3) < s_end;
-        P.c[k] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, ok ? o.c[k] + 512 * q : kOOB, 0, 0);
-        P.s[k] = __builtin_amdgcn_raw_buffer_load_b8(c.ras, ok ? o.s[k] + 16 * q : kOOB, 0, 0);
+        if constexpr (A4) {
+            const auto cv = __builtin_amdgcn_raw_buffer_load_b64(c.ra, ok ? o.c[k] + 256 * q : kOOB, 0, 0);
+            P.c[k] = v4i{(int)cv[0], (int)cv[1], 0, 0};
+            P.s[k] = __builtin_amdgcn_raw_buffer_load_b8(c.ras, ok ? o.s[k] + 32 * q : kOOB, 0, 0);
+        } else {
+            P.c[k] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, ok ? o.c[k] + 512 * q : kOOB, 0, 0);
+            P.s[k] = __builtin_amdgcn_raw_buffer_load_b8(c.ras, ok ? o.s[k] + 16 * q : kOOB, 0, 0);
+        }
     }
 }
 
 // Converts the thread's share of a tile to f16 and writes it into an LDS
 // buffer.  rsmax: the pass rows' smax (LDS).  Codes past the range are zero,
 // and so are their f16 values.
-template <int NB>
+template <int NB, bool A4>
 __device__ __forceinline__ void tile_store(const ActShare<NB>& P, uint8_t* buf, const int* rsmax, int npass) {
     const int t = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < 2 * NB; ++k) {
         const int li = t + kThreads * k, row = li >> 5, ch = li & 31;
-        const int sm = row < npass ? rsmax[row] : 0;
-        const float sf = exp2i(max((int)(P.s[k] & 0xffu) - sm, -126));
-        const v8h h0 = fp8x8_to_f16((uint32_t)P.c[k].x, (uint32_t)P.c[k].y, sf);
-        const v8h h1 = fp8x8_to_f16((uint32_t)P.c[k].z, (uint32_t)P.c[k].w, sf);
+        v8h h0, h1;
+        if constexpr (A4) {
+            // exact: E2M1 * E4M3 (the scale's exponent carrier times its mantissa factor)
+            float sv0, sv1;
+            v2h m;
+            nv_scales2<0>(P.s[k] & 0xffu, sv0, sv1, m);
+            h0 = nv_dequant8((uint32_t)P.c[k].x, sv0, m[0]);
+            h1 = nv_dequant8((uint32_t)P.c[k].y, sv0, m[0]);
+        } else {
+            const int sm = row < npass ? rsmax[row] : 0;
+            const float sf = exp2i(max((int)(P.s[k] & 0xffu) - sm, -126));
+            h0 = fp8x8_to_f16((uint32_t)P.c[k].x, (uint32_t)P.c[k].y, sf);
+            h1 = fp8x8_to_f16((uint32_t)P.c[k].z, (uint32_t)P.c[k].w, sf);
+        }
         uint8_t* p = buf + row * kTileRowH + 32 * ch;
         *reinterpret_cast<v8h*>(p) = h0;
         *reinterpret_cast<v8h*>(p + 16) = h1;
@@ -655,8 +723,8 @@ struct RingW {
     uint32_t as[DQ][MB][2];
 };
 
-template <int MB, int NB, int DQ>
-__device__ __forceinline__ void ringw_load_step(RingW<MB, DQ>& R, int v, int u, const Coord<kFmtNV, MB, NB>& c, int q,
+template <int MB, int NB, int DQ, int CF>
+__device__ __forceinline__ void ringw_load_step(RingW<MB, DQ>& R, int v, int u, const Coord<CF, MB, NB>& c, int q,
                                                 int s_end) {
     const int st = 4 * q + u;
     const bool ok = st < s_end;
@@ -665,8 +733,8 @@ __device__ __forceinline__ void ringw_load_step(RingW<MB, DQ>& R, int v, int u, 
         R.a[v][u][mb] = __builtin_amdgcn_raw_buffer_load_b128(c.rw, ok ? c.vw[mb] : kOOB, 1024 * st, MOE_WEIGHT_AUX);
 }
 
-template <int MB, int NB, int DQ>
-__device__ __forceinline__ void ringw_load_scales(RingW<MB, DQ>& R, int v, const Coord<kFmtNV, MB, NB>& c, int q,
+template <int MB, int NB, int DQ, int CF>
+__device__ __forceinline__ void ringw_load_scales(RingW<MB, DQ>& R, int v, const Coord<CF, MB, NB>& c, int q,
                                                   int s_end) {
     const bool okq = 4 * q < s_end;
 #pragma unroll
@@ -680,8 +748,8 @@ __device__ __forceinline__ void ringw_load_scales(RingW<MB, DQ>& R, int v, const
 // The four steps of the quad in slot v, the B operands of step U given and
 // those of step U+1 read from the tile meanwhile; each step's weight slot is
 // refilled with quad qn right after its MFMAs.
-template <int MB, int NB, int DQ, int U>
-__device__ __forceinline__ void quadw_steps(RingW<MB, DQ>& R, int v, const Coord<kFmtNV, MB, NB>& c, int qn,
+template <int MB, int NB, int DQ, int U, int CF>
+__device__ __forceinline__ void quadw_steps(RingW<MB, DQ>& R, int v, const Coord<CF, MB, NB>& c, int qn,
                                             int s_end, const uint8_t* tile, const v8h (&B)[NB][4],
                                             v4f (&acc)[MB][2]) {
     if constexpr (U < 4) {
@@ -699,22 +767,23 @@ __device__ __forceinline__ void quadw_steps(RingW<MB, DQ>& R, int v, const Coord
 // kTileBytesH buffers; rsmax: kPassRows ints).  Every thread of the workgroup
 // must call it with the same arguments apart from the weight blocks (it has
 // barriers).
-template <int MB, int NB, int DQ>
+template <int MB, int NB, int DQ, bool A4>
 __device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const int (&wblk)[MB], int arow0,
                                                 int npass, const int* src, int s0, int nst, int (&smax)[NB],
                                                 v4f (&acc)[MB][2], uint8_t* tiles, int* rsmax) {
     static_assert(DQ % 2 == 0, "slots alternate between the two tile buffers");
-    const Coord<kFmtNV, MB, NB> c = make_coord<kFmtNV, MB, NB>(J, e, wblk, arow0, npass, src);
-    const TileOffs<NB> to = tile_offsets<NB>(J.K, npass, src);
-    Coord<kFmtNV, 1, NB> ca;  // the activation resources, for the tile loads
+    constexpr int CF = A4 ? kFmtNV4 : kFmtNV;
+    const Coord<CF, MB, NB> c = make_coord<CF, MB, NB>(J, e, wblk, arow0, npass, src);
+    const TileOffs<NB> to = tile_offsets<NB, A4>(J.K, npass, src);
+    Coord<CF, 1, NB> ca;  // the activation resources, for the tile loads
     ca.ra = c.ra;
     ca.ras = c.ras;
     SmaxRaw<NB> SR;
-    row_smax_issue<kFmtNV, MB, NB>(c, s0, nst, SR);
+    if constexpr (!A4) row_smax_issue<kFmtNV, MB, NB>(c, s0, nst, SR);
     __builtin_amdgcn_sched_barrier(0);
     const int q0 = s0 / 4, nq = (nst + 3) / 4, s_end = s0 + nst;
     ActShare<NB> P;
-    tile_load<NB>(P, ca, to, q0, s_end);
+    tile_load<NB, A4>(P, ca, to, q0, s_end);
     RingW<MB, DQ> R;
 #pragma unroll
     for (int v = 0; v < DQ; ++v) {
@@ -726,19 +795,24 @@ __device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    row_smax_finish<kFmtNV, MB, NB>(c, s0, nst, SR, smax);
-    __builtin_amdgcn_sched_barrier(0);
-    // every wave holds the rows' smax; wave 0 publishes them for the tile stores
-    if (threadIdx.x < 16) {
+    if constexpr (A4) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) rsmax[16 * j + threadIdx.x] = smax[j];
+        for (int j = 0; j < NB; ++j) smax[j] = 0;
+    } else {
+        row_smax_finish<kFmtNV, MB, NB>(c, s0, nst, SR, smax);
+        __builtin_amdgcn_sched_barrier(0);
+        // every wave holds the rows' smax; wave 0 publishes them for the tile stores
+        if (threadIdx.x < 16) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) rsmax[16 * j + threadIdx.x] = smax[j];
+        }
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[mb][j] = v4f{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
-    tile_store<NB>(P, tiles, rsmax, npass);
+    tile_store<NB, A4>(P, tiles, rsmax, npass);
     __syncthreads();
     for (int l0 = 0; l0 < nq; l0 += DQ) {
 #pragma unroll
@@ -747,10 +821,10 @@ __device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const
             const uint8_t* tile = tiles + (v & 1) * kTileBytesH;
             v8h B[NB][4];
             tile_read<NB>(tile, 0, B);
-            tile_load<NB>(P, ca, to, q + 1, s_end);  // in flight over the quad's steps
+            tile_load<NB, A4>(P, ca, to, q + 1, s_end);  // in flight over the quad's steps
             quadw_steps<MB, NB, DQ, 0>(R, v, c, q + DQ, s_end, tile, B, acc);
             // tile q+1 into the other buffer (its reads ended at the last barrier)
-            tile_store<NB>(P, tiles + ((v + 1) & 1) * kTileBytesH, rsmax, npass);
+            tile_store<NB, A4>(P, tiles + ((v + 1) & 1) * kTileBytesH, rsmax, npass);
             __syncthreads();
         }
     }
@@ -813,7 +887,7 @@ constexpr int GCOLS = 32 * GMB;  // output columns per workgroup
 // items do not trail the launch), [n2, nmain) items of job J0, later ones a
 // bf16 shared-expert stage.
 template <int FMT, bool FUSED>
-__global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLOCKS) void k_gate_up(
+__global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS) void k_gate_up(
     StreamJob J0, uint8_t* __restrict__ h_q0, uint8_t* __restrict__ h_s0, float* __restrict__ part, int nmain,
     Bf16Side side, int stage, StreamJob J2, uint8_t* __restrict__ h_q2, uint8_t* __restrict__ h_s2, int n2) {
     if ((int)blockIdx.x >= nmain) {  // a bf16 shared-expert stage riding along
@@ -853,13 +927,17 @@ __global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLO
     for (int mb = 0; mb < GMB; ++mb) wblk[mb] = (wave >> 1) * I + col0 + 16 * mb;
     const int k0 = ks * J.span;
     const int s0 = k0 / 128, nst = min(J.span, K - k0) / 128;
-    const float gs = FMT == kFmtNV ? J.gscale[tk.e] : 1.0f;
+    const float gs = kNVW<FMT> ? J.gscale[tk.e] : 1.0f;
+    // NVFP4 activations: accumulator factor (activation global x weight
+    // global) and the global of the h written
+    const float fa4 = kA4<FMT> ? act_global(J, tk.e) * gs : 0.0f;
+    const float hg4 = kA4<FMT> ? out_global(J, tk.e) : 0.0f;
 
     // fused epilogue: gate [0, GCOLS), up [GCOLS, 2*GCOLS) per row.  NVFP4 keeps
     // the activation tiles of two quads in the same LDS: the epilogue runs
     // after the pass's last barrier, when no wave reads a tile any more.
     constexpr int kGBytes = kPassRows * (2 * GCOLS + 1) * 4;
-    constexpr int kLdsBytes = FMT == kFmtNV && 2 * kTileBytesH > kGBytes ? 2 * kTileBytesH : kGBytes;
+    constexpr int kLdsBytes = kNVW<FMT> && 2 * kTileBytesH > kGBytes ? 2 * kTileBytesH : kGBytes;
     __shared__ __align__(16) uint8_t sLds[kLdsBytes];
     float(*sG)[2 * GCOLS + 1] = reinterpret_cast<float(*)[2 * GCOLS + 1]>(sLds);
     __shared__ int s_smax[kPassRows];
@@ -884,8 +962,9 @@ __global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLO
         int smax[2] = {0, 0};
         if (npass > 16) {
             int sm[2];
-            if constexpr (FMT == kFmtNV)
-                stream_pass_lds<GMB, 2, MOE_NV_DQ>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm, acc, sLds, s_smax);
+            if constexpr (kNVW<FMT>)
+                stream_pass_lds<GMB, 2, MOE_NV_DQ, kA4<FMT>>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm, acc, sLds,
+                                                             s_smax);
             else
                 stream_pass<FMT, GMB, 2, ring_quads<FMT, GMB, 2>(), 4>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm,
                                                                          acc);
@@ -893,8 +972,9 @@ __global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLO
             smax[1] = sm[1];
         } else {
             int sm[1];
-            if constexpr (FMT == kFmtNV)
-                stream_pass_lds<GMB, 1, MOE_NV_DQ>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm, acc, sLds, s_smax);
+            if constexpr (kNVW<FMT>)
+                stream_pass_lds<GMB, 1, MOE_NV_DQ, kA4<FMT>>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm, acc, sLds,
+                                                             s_smax);
             else
                 stream_pass<FMT, GMB, 1, ring_quads<FMT, GMB, 1>(), 4>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm,
                                                                          acc);
@@ -925,6 +1005,7 @@ __global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLO
                 float hv[4];
                 float fac = 1.0f;
                 if (FMT == kFmtNV && t < npass) fac = nv_row_factor(s_smax[t], gs);
+                if (kA4<FMT>) fac = fa4;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int col = 4 * q + c;
@@ -936,11 +1017,22 @@ __global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLO
                     hv[c] = swiglu(gt, up, J.limit);
                 }
                 uint8_t sc;
-                const uint32_t codes = mx_quant4_group8(hv, sc);
-                if (t < npass) {
-                    const size_t orow = (size_t)(arow0 + t);
-                    *reinterpret_cast<uint32_t*>(h_q + orow * I + blk * GCOLS + 4 * q) = codes;
-                    if ((q & 7) == 0) h_s[orow * (I / 32) + blk * (GCOLS / 32) + (q >> 3)] = sc;
+                if constexpr (kA4<FMT>) {
+                    // NVFP4 h: 4 lanes per 16-column block, 2 code bytes per lane
+                    const uint32_t codes = nvfp4_quant4_lanes4(hv, hg4, sc);
+                    if (t < npass) {
+                        const size_t orow = (size_t)(arow0 + t);
+                        const int col = blk * GCOLS + 4 * q;
+                        *reinterpret_cast<uint16_t*>(h_q + orow * (I / 2) + col / 2) = (uint16_t)codes;
+                        if ((q & 3) == 0) h_s[orow * (I / 16) + col / 16] = sc;
+                    }
+                } else {
+                    const uint32_t codes = mx_quant4_group8(hv, sc);
+                    if (t < npass) {
+                        const size_t orow = (size_t)(arow0 + t);
+                        *reinterpret_cast<uint32_t*>(h_q + orow * I + blk * GCOLS + 4 * q) = codes;
+                        if ((q & 7) == 0) h_s[orow * (I / 32) + blk * (GCOLS / 32) + (q >> 3)] = sc;
+                    }
                 }
             }
             __syncthreads();
@@ -954,6 +1046,7 @@ __global__ __launch_bounds__(kThreads, FMT == kFmtNV ? MOE_NV_MINB : MOE_MIN_BLO
                     if (t < npass) {
                         v4f v = acc[mb][j];
                         if (FMT == kFmtNV) v = v * nv_row_factor(smax[j], gs);
+                        if (kA4<FMT>) v = v * fa4;
                         *reinterpret_cast<v4f*>(part + ((size_t)ks * J.out_rows + arow0 + t) * (2 * I) + colw) = v;
                     }
                 }
@@ -1028,7 +1121,8 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0,
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) wblk[mb] = f0 + 16 * mb;
     const int nst = I / 128;
-    const float gs = FMT == kFmtNV ? J.gscale[tk.e] : 1.0f;
+    const float gs = kNVW<FMT> ? J.gscale[tk.e] : 1.0f;
+    const float fa4 = kA4<FMT> ? act_global(J, tk.e) * gs : 0.0f;  // NVFP4 h: its global x the weights'
 
     for (int t0 = 0; t0 < tk.n; t0 += kPassRows) {
         const int npass = min(kPassRows, tk.n - t0);
@@ -1063,6 +1157,7 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0,
                 for (int mb = 0; mb < MB; ++mb) {
                     v4f v = acc[mb][j];
                     if (FMT == kFmtNV) v = v * nv_row_factor(smax[j], gs);
+                    if (kA4<FMT>) v = v * fa4;
                     *reinterpret_cast<v4f*>(y + (size_t)orow[j] * H + f0 + 16 * mb + 4 * g) = v;
                 }
             }
@@ -1075,7 +1170,7 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0,
 template <int FMT, int S, int D, int U>
 __device__ __forceinline__ void rows_steps(v4f& acc, const v4i (&wa)[D][S], const uint32_t (&wsc)[D][FMT == kFmtMX ? 1 : 2],
                                            int d, const v4i (&b)[S][2], const uint32_t (&bs)[S],
-                                           const v8h (&B16)[FMT == kFmtNV ? S : 1][4], int g) {
+                                           const v8h (&B16)[kNVW<FMT> ? S : 1][4], int g) {
     if constexpr (U < S) {
         const v4i a = wa[d][U];
         if constexpr (FMT == kFmtMX) {
@@ -1134,7 +1229,9 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down_rows(StreamJo
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(J.w + (size_t)tk.e * wbytes, wbytes);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(J.sc + (size_t)tk.e * sbytes, sbytes);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(y, (uint32_t)J.out_rows * (uint32_t)H * 4u);
-    const float gs = FMT == kFmtNV ? J.gscale[tk.e] : 1.0f;
+    const float gs = kNVW<FMT> ? J.gscale[tk.e] : 1.0f;
+    // activation row bytes: MXFP8 K codes + K/32 scales; NVFP4 K/2 + K/16
+    constexpr int kAQd = kA4<FMT> ? 2 : 1, kASd = kA4<FMT> ? 16 : 32;
 
     for (int t0 = 0; t0 < tk.n; t0 += 16) {
         const int npass = min(16, tk.n - t0);
@@ -1142,17 +1239,26 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down_rows(StreamJo
         const bool okr = i < npass;
         const int orow = okr ? (J.dense ? arow0 + i : J.ids ? s_list[t0 + i] : J.bucket[arow0 + i]) : 0;
         // the lane's activation row (column i of the MFMAs), all S steps
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(J.a_q + (size_t)arow0 * K, (uint32_t)npass * (uint32_t)K);
-        const __amdgpu_buffer_rsrc_t ras = make_rsrc(J.a_s + (size_t)arow0 * (K / 32), (uint32_t)npass * (uint32_t)(K / 32));
-        const uint32_t va = okr ? (uint32_t)i * K + (FMT == kFmtMX ? 16 : 32) * g : kOOB;
-        const uint32_t vas = okr ? (uint32_t)i * (K / 32) : kOOB;
+        const int AQ = K / kAQd, AS = K / kASd;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(J.a_q + (size_t)arow0 * AQ, (uint32_t)npass * (uint32_t)AQ);
+        const __amdgpu_buffer_rsrc_t ras = make_rsrc(J.a_s + (size_t)arow0 * AS, (uint32_t)npass * (uint32_t)AS);
+        // NVFP4 h: bytes [16g, +16) of each step's 64 and the dword of the
+        // lane's two scale bytes (2g, 2g + 1 of the step's 8)
+        const uint32_t va = okr ? (uint32_t)i * AQ + (kA4<FMT> ? 16 : FMT == kFmtMX ? 16 : 32) * g : kOOB;
+        const uint32_t vas = okr ? (uint32_t)i * AS + (kA4<FMT> ? 4 * (g >> 1) : 0) : kOOB;
         v4i b[S][2];
         uint32_t bs[S];
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            b[s][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, va, 128 * s, 0);
-            b[s][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, va + (FMT == kFmtMX ? 64 : 16), 128 * s, 0);
-            bs[s] = __builtin_amdgcn_raw_buffer_load_b32(ras, vas, 4 * s, 0);
+            if constexpr (kA4<FMT>) {
+                b[s][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, va, 64 * s, 0);
+                b[s][1] = v4i{0, 0, 0, 0};
+                bs[s] = __builtin_amdgcn_raw_buffer_load_b32(ras, vas, 8 * s, 0);
+            } else {
+                b[s][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, va, 128 * s, 0);
+                b[s][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, va + (FMT == kFmtMX ? 64 : 16), 128 * s, 0);
+                bs[s] = __builtin_amdgcn_raw_buffer_load_b32(ras, vas, 4 * s, 0);
+            }
         }
         // weight ring: slot d holds one block (S steps and its scale entry)
         v4i wa[D][S];
@@ -1183,8 +1289,12 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down_rows(StreamJo
         // scaled by 2^(s - smax) with smax the row's largest scale code
         int smax = 0;
         float fac = 1.0f;
-        v8h B16[FMT == kFmtNV ? S : 1][4];
-        if constexpr (FMT == kFmtNV) {
+        v8h B16[kNVW<FMT> ? S : 1][4];
+        if constexpr (kA4<FMT>) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) act4_to_f16(b[s][0], bs[s], g, B16[s]);
+            fac = act_global(J, tk.e) * gs;
+        } else if constexpr (FMT == kFmtNV) {
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 const uint32_t v = bs[s];
@@ -1231,6 +1341,11 @@ GatePlan gate_plan(const ExpertJob& j) {
     GatePlan p;
     const int K = j.K, steps = K / 128;
     p.nblk = j.N_out / GCOLS;
+    if (j.a_nvfp4) {  // NVFP4 activations: all of K in one item (the requant needs the expert's h global)
+        p.span = K;
+        p.splits = 1;
+        return p;
+    }
     const long items = (long)grid_slots(j) * p.nblk;
     int want = (int)std::max<long>(1, (MOE_STREAM_TARGET_ITEMS + items - 1) / items);
     want = std::min(want, std::max(1, steps / 8));  // at least 8 steps per split
@@ -1270,6 +1385,10 @@ StreamJob stream_job(const ExpertJob& j, int N, const uint8_t* a_q, const uint8_
     s.r_bkt = j.record ? j.record->bkt : nullptr;
     if (s.a_tok) s.a_rows = (uint32_t)j.M;
     s.limit = j.swiglu_limit;
+    s.ag = j.a_global;
+    s.age = j.a_globals;
+    s.hg = j.h_global;
+    s.hge = j.h_globals;
     return s;
 }
 
@@ -1294,12 +1413,12 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
     J.nblk = p.nblk;
     const int blocks = grid_slots(job) * p.nblk * p.splits;
     const bool mx = job.w.fmt == MOE_FMT_MXFP4;
-    // a second job of the same format rides along when both run over all of K
+    // a second job of the same formats rides along when both run over all of K
     StreamJob J2 = J;
     int n2 = 0;
     if (second.job) {
         const ExpertJob& j2 = *second.job;
-        if (p.splits == 1 && j2.w.fmt == job.w.fmt) {
+        if (p.splits == 1 && j2.w.fmt == job.w.fmt && j2.a_nvfp4 == job.a_nvfp4) {
             J2 = stream_job(j2, 2 * j2.N_out, second.a_q, second.a_s, out_rows_of(j2));
             J2.nblk = j2.N_out / GCOLS;  // span = K, one split
             n2 = grid_slots(j2) * J2.nblk;
@@ -1315,7 +1434,10 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
     uint8_t* hs2 = n2 ? second.h_s : h_s;
     const int nmain = blocks + n2;
     if (p.splits == 1) {
-        if (mx)
+        if (job.a_nvfp4)
+            hipLaunchKernelGGL((k_gate_up<kFmtNV4, true>), g, b, 0, stream, J, h_q, h_s, partials, nmain, side, stage,
+                               J2, hq2, hs2, n2);
+        else if (mx)
             hipLaunchKernelGGL((k_gate_up<kFmtMX, true>), g, b, 0, stream, J, h_q, h_s, partials, nmain, side, stage,
                                J2, hq2, hs2, n2);
         else
@@ -1391,14 +1513,16 @@ hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8
     StreamJob J = stream_job(job, job.N_out, h_q, h_s, out_rows_of(job));
     const DownRide dr = down_ride(ride_route, E, job.k);
     // a second job rides along when both stream along K with the same format
-    const bool fold = second.job && job.K > 512 && second.job->K > 512 && second.job->w.fmt == job.w.fmt;
+    const bool fold = second.job && job.K > 512 && second.job->K > 512 && second.job->w.fmt == job.w.fmt &&
+                      second.job->a_nvfp4 == job.a_nvfp4;
     if (second.job && !fold) {
         hipError_t e = launch_down_fp4(*second.job, second.h_q, second.h_s, second.y, stream);
         if (e != hipSuccess) return e;
     }
     if (job.K <= 512)  // all of K in one quad: stream along the rows
-        return job.w.fmt == MOE_FMT_MXFP4 ? launch_down_rows<kFmtMX>(J, grid_slots(job), y, dr, stream)
-                                          : launch_down_rows<kFmtNV>(J, grid_slots(job), y, dr, stream);
+        return job.a_nvfp4                 ? launch_down_rows<kFmtNV4>(J, grid_slots(job), y, dr, stream)
+               : job.w.fmt == MOE_FMT_MXFP4 ? launch_down_rows<kFmtMX>(J, grid_slots(job), y, dr, stream)
+                                            : launch_down_rows<kFmtNV>(J, grid_slots(job), y, dr, stream);
     const bool mx = job.w.fmt == MOE_FMT_MXFP4;
     const bool wide = mx && job.N_out % (64 * kDownMBWide) == 0;
     const int dmb = wide ? kDownMBWide : kDownMB;
@@ -1419,6 +1543,8 @@ hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8
         hipLaunchKernelGGL((k_down<kFmtMX, kDownMBWide>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E, J2, y2, n2);
     else if (mx)
         hipLaunchKernelGGL((k_down<kFmtMX, kDownMB>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E, J2, y2, n2);
+    else if (job.a_nvfp4)
+        hipLaunchKernelGGL((k_down<kFmtNV4, kDownMB>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E, J2, y2, n2);
     else
         hipLaunchKernelGGL((k_down<kFmtNV, kDownMB>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E, J2, y2, n2);
     return hipGetLastError();

@@ -273,6 +273,43 @@ int moe_expert_down(const moe_weights* w2, const uint8_t* h_q, const uint8_t* h_
     return hip_status(launch_down_fp4(job, h_q, h_s, y, stream));
 }
 
+int moe_expert_gate_up_nvfp4a(const moe_weights* w13, const uint8_t* a_q, const uint8_t* a_s, float a_global,
+                              const moe_routing* route, int M, int H, int I, int E, int k, float swiglu_limit,
+                              const float* h_globals, uint8_t* h_q, uint8_t* h_s, hipStream_t stream) {
+    if (!w13 || !a_q || !a_s || !h_globals || !h_q || !h_s) return MOE_ERR_INVALID_ARG;
+    if (!(swiglu_limit >= 0.0f)) return MOE_ERR_INVALID_ARG;
+    if (!(a_global > 0.0f) || !(a_global <= 3.4e38f)) return MOE_ERR_INVALID_ARG;
+    const bool dense = route == nullptr;
+    if (int st = check_dims(M, H, dense ? 1 : E, dense ? 1 : k)) return st;
+    if (I < 128 || I % 128 != 0 || I > kMaxI) return MOE_ERR_UNSUPPORTED;
+    if (w13->fmt != MOE_FMT_NVFP4) return MOE_ERR_UNSUPPORTED;
+    if (int st = check_fp4_weights(w13)) return st;
+    if (!dense)
+        if (int st = check_routing(route)) return st;
+    ExpertJob job = dense ? dense_job(*w13, I, H, M) : routed_job(*w13, I, H, *route, M, E, k);
+    job.swiglu_limit = swiglu_limit;
+    job.a_nvfp4 = true;
+    job.a_global = a_global;
+    job.h_globals = h_globals;
+    return hip_status(launch_gate_up_fp4(job, a_q, a_s, h_q, h_s, nullptr, stream));
+}
+
+int moe_expert_down_nvfp4a(const moe_weights* w2, const uint8_t* h_q, const uint8_t* h_s, const float* h_globals,
+                           const moe_routing* route, int M, int H, int I, int E, int k, float* y, hipStream_t stream) {
+    if (!w2 || !h_q || !h_s || !h_globals || !y) return MOE_ERR_INVALID_ARG;
+    const bool dense = route == nullptr;
+    if (int st = check_dims(M, H, dense ? 1 : E, dense ? 1 : k)) return st;
+    if (I < 128 || I % 128 != 0 || I > kMaxI) return MOE_ERR_UNSUPPORTED;
+    if (w2->fmt != MOE_FMT_NVFP4) return MOE_ERR_UNSUPPORTED;
+    if (int st = check_fp4_weights(w2)) return st;
+    if (!dense)
+        if (int st = check_routing(route)) return st;
+    ExpertJob job = dense ? dense_job(*w2, H, I, M) : routed_job(*w2, H, I, *route, M, E, k);
+    job.a_nvfp4 = true;
+    job.a_globals = h_globals;
+    return hip_status(launch_down_fp4(job, h_q, h_s, y, stream));
+}
+
 int moe_finalize_rmsnorm_mxfp8(const float* y, const float* topk_w, const float* y_sh,
                                const uint16_t* residual, const uint16_t* gamma, float eps, int M, int H,
                                int k, uint16_t* out, uint16_t* residual_out, uint8_t* out_q, uint8_t* out_s,
@@ -297,6 +334,21 @@ int moe_finalize_rmsnorm(const float* y, const float* topk_w, const float* y_sh,
 
 namespace {
 
+// NVFP4 activations of a layer job: a gate_up reads x with its global and
+// writes h with the expert's (routed: h_globals[e], shared: *sh_h_global); a
+// down reads h with the same.
+void set_a4(ExpertJob& j, const moe_layer_desc* d, bool shared, bool gate_up) {
+    if (d->act_fmt != MOE_ACT_NVFP4) return;
+    j.a_nvfp4 = true;
+    const float* hg = shared ? d->sh_h_global : d->h_globals;
+    if (gate_up) {
+        j.a_global = d->x_global;
+        j.h_globals = hg;
+    } else {
+        j.a_globals = hg;
+    }
+}
+
 int check_desc(const moe_layer_desc* d) {
     if (!d) return MOE_ERR_INVALID_ARG;
     if (int st = check_dims(d->M, d->H, d->E, d->k)) return st;
@@ -304,6 +356,12 @@ int check_desc(const moe_layer_desc* d) {
     if (!d->w_router || !d->gamma) return MOE_ERR_INVALID_ARG;
     if (!(d->eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
     if (!(d->swiglu_limit >= 0.0f)) return MOE_ERR_INVALID_ARG;
+    if (d->act_fmt != MOE_ACT_MXFP8 && d->act_fmt != MOE_ACT_NVFP4) return MOE_ERR_INVALID_ARG;
+    if (d->act_fmt == MOE_ACT_NVFP4) {
+        if (d->w13.fmt != MOE_FMT_NVFP4 || d->sh13.fmt == MOE_FMT_MXFP4) return MOE_ERR_UNSUPPORTED;
+        if (!(d->x_global > 0.0f) || !(d->x_global <= 3.4e38f) || !d->h_globals) return MOE_ERR_INVALID_ARG;
+        if (d->sh13.fmt == MOE_FMT_NVFP4 && !d->sh_h_global) return MOE_ERR_INVALID_ARG;
+    }
     if (int st = check_fp4_weights(&d->w13)) return st;
     if (int st = check_fp4_weights(&d->w2)) return st;
     if (d->w13.fmt != d->w2.fmt) return MOE_ERR_UNSUPPORTED;
@@ -355,16 +413,18 @@ LayerWs carve_layer(Carver& c, const moe_layer_desc* d) {
     L.act_off = c.take<int32_t>(std::min(E, P) + 1);
     // token order: gate_up gathers its rows (and the FP4 shared expert reads them)
     L.xq = L.xs = nullptr;
+    // scales: one byte per 32 values (MXFP8) or per 16 (NVFP4 activations)
+    const int sdiv = d->act_fmt == MOE_ACT_NVFP4 ? 16 : 32;
     L.xqt = c.take<uint8_t>((size_t)M * H);
-    L.xst = c.take<uint8_t>((size_t)M * H / 32);
+    L.xst = c.take<uint8_t>((size_t)M * H / sdiv);
     L.hq = c.take<uint8_t>((size_t)P * I);
-    L.hs = c.take<uint8_t>((size_t)P * I / 32);
+    L.hs = c.take<uint8_t>((size_t)P * I / sdiv);
     L.hsq = L.hss = nullptr;
     L.hsb = nullptr;
     L.sh_part = nullptr;
     if (sh && !shb) {
         L.hsq = c.take<uint8_t>((size_t)M * Ish);
-        L.hss = c.take<uint8_t>((size_t)M * Ish / 32);
+        L.hss = c.take<uint8_t>((size_t)M * Ish / sdiv);
     }
     if (shb) {
         L.hsb = c.take<uint16_t>((size_t)M * Ish);
@@ -428,6 +488,9 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
     const bool shb = sf == MOE_FMT_BF16;
     ExpertJob sh_gu = dense_job(d->sh13, Ish, H, M);
     sh_gu.swiglu_limit = d->swiglu_limit;
+    const bool a4 = d->act_fmt == MOE_ACT_NVFP4;
+    const float xg4 = a4 ? d->x_global : 0.0f;
+    if (sf == MOE_FMT_NVFP4) set_a4(sh_gu, d, true, true);
     const Bf16Side s1 = shb ? bf16_side(sh_gu, Ish, H, M, x, L.sh_part, L.hsb, L.ysh,
                                         kBf16GateUp)
                             : no_side();
@@ -445,19 +508,21 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
         // -> down (the route step rides along) -> finalize.  The bf16 shared
         // expert's stages ride along the first three.
         hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, L.xqt, L.xst, s1,
-                                              shb ? kBf16GateUp : kBf16None, stream);
+                                              shb ? kBf16GateUp : kBf16None, stream, xg4);
         if (e == hipSuccess)
             e = launch_topk(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale, logits_out, r, s2,
                             shb ? kBf16Swiglu : kBf16None, stream);
         ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
         gu.swiglu_limit = d->swiglu_limit;
+        set_a4(gu, d, false, true);
         gu.ids = r.topk_ids;
         gu.a_tok = true;
         const SlotRecord rec{L.r_act, L.r_off, L.r_na, L.r_bkt};
         gu.record = &rec;
         // the FP4 shared expert rides along the routed launches
         const ExpertJob& sgu = sh_gu;
-        const ExpertJob sdn = dense_job(d->sh2, H, Ish, M);
+        ExpertJob sdn = dense_job(d->sh2, H, Ish, M);
+        if (sf == MOE_FMT_NVFP4) set_a4(sdn, d, true, false);
         const SecondJob s_gu = fp4_shared ? SecondJob{&sgu, L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart} : SecondJob{};
         const SecondDown s_dn = fp4_shared ? SecondDown{&sdn, L.hsq, L.hss, L.ysh} : SecondDown{};
         if (e == hipSuccess)
@@ -465,6 +530,7 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
                                    s_gu);
         // down resolves its slots from gate_up's record (one round of loads)
         ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);
+        set_a4(dn, d, false, false);
         dn.active = rec.act;
         dn.active_offsets = rec.off;
         dn.bucket = rec.bkt;
@@ -479,20 +545,23 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
     // -> gate_up (gathers each pass's token rows through the bucket) -> down
     // -> finalize.
     hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, L.xqt, L.xst, s1,
-                                          shb ? kBf16GateUp : kBf16None, stream);
+                                          shb ? kBf16GateUp : kBf16None, stream, xg4);
     if (e == hipSuccess)
         e = launch_topk_bucket(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale, logits_out, r,
                                s2, shb ? kBf16Swiglu : kBf16None, s3, shb ? kBf16Down : kBf16None, stream);
     ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
     gu.swiglu_limit = d->swiglu_limit;
+    set_a4(gu, d, false, true);
     gu.a_tok = true;
     const ExpertJob& sgu = sh_gu;
-    const ExpertJob sdn = dense_job(d->sh2, H, Ish, M);
+    ExpertJob sdn = dense_job(d->sh2, H, Ish, M);
+    if (sf == MOE_FMT_NVFP4) set_a4(sdn, d, true, false);
     const SecondJob s_gu = fp4_shared ? SecondJob{&sgu, L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart} : SecondJob{};
     const SecondDown s_dn = fp4_shared ? SecondDown{&sdn, L.hsq, L.hss, L.ysh} : SecondDown{};
     if (e == hipSuccess)
         e = launch_gate_up_fp4(gu, L.xqt, L.xst, L.hq, L.hs, L.part, stream, no_side(), kBf16None, s_gu);
-    const ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);
+    ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);
+    set_a4(dn, d, false, false);
     if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream, nullptr, 0, s_dn);
     if (e == hipSuccess)
         e = launch_finalize(L.y, r.topk_w, L.ysh, residual, d->gamma, d->eps, M, H, k, out, residual_out,

@@ -46,9 +46,11 @@ RouterPlan router_plan(int M, int H, int E);
 // the bucketing (stage kBf16None and blocks 0 for none).
 // With xq != nullptr the launch also writes the MXFP8 of x in token order
 // (codes xq [M][H], scales xs [M][H/32]).
+// xg4 > 0: the token-order copy of x is NVFP4 with global xg4 (codes [M][H/2],
+// scales [M][H/16]) instead of MXFP8.
 hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int M, int H, int E,
                                   const RouterPlan& plan, float* partials, uint8_t* xq, uint8_t* xs,
-                                  const Bf16Side& side1, int stage1, hipStream_t stream);
+                                  const Bf16Side& side1, int stage1, hipStream_t stream, float xg4 = 0.0f);
 // logits: the router partials (splits of them), or given logits (splits = 1).
 hipError_t launch_topk(const float* partials, int splits, const float* bias, int M, int E, int k,
                        float routed_scale, float* logits_out, const moe_routing& route, const Bf16Side& side2,
@@ -114,6 +116,14 @@ struct ExpertJob {
     const SlotRecord* record = nullptr;  // gate_up with ids: record the resolved slots
     const int32_t* count = nullptr;      // active list whose entries past *count are stale
     float swiglu_limit = 0.0f;           // gate_up: clamped SwiGLU limit (0: unclamped)
+    // NVFP4 activations (NVFP4 weights only): the activations are NVFP4 codes
+    // [rows][K/2] + E4M3 scales [rows][K/16] with global a_global, or
+    // a_globals[e] per expert (device, [E]; dense: [1]); a gate_up writes h
+    // as NVFP4 with global h_global, or h_globals[e].
+    bool a_nvfp4 = false;
+    float a_global = 0.0f, h_global = 0.0f;
+    const float* a_globals = nullptr;
+    const float* h_globals = nullptr;
 };
 
 // gate_up over FP4 experts.  When the plan splits K, fp32 partials go to

@@ -23,7 +23,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 EXPORTS = ["moe_status_str", "moe_abi_version", "moe_tile_capacity", "moe_packed_scale_bytes",
            "moe_pack_fp4", "moe_route_workspace_bytes",
            "moe_route_topk", "moe_quant_act_mxfp8", "moe_quant_act_nvfp4", "moe_gate_up_workspace_bytes",
-           "moe_expert_gate_up", "moe_expert_down", "moe_finalize_rmsnorm",
+           "moe_expert_gate_up", "moe_expert_down", "moe_expert_gate_up_nvfp4a",
+           "moe_expert_down_nvfp4a", "moe_finalize_rmsnorm",
            "moe_finalize_rmsnorm_mxfp8", "moe_layer_workspace_bytes", "moe_layer",
            "moe_layer_mxfp8_out"]
 
@@ -44,7 +45,9 @@ class moe_layer_desc(C.Structure):
                 ("I_sh", C.c_int), ("routed_scale", C.c_float), ("eps", C.c_float),
                 ("w_router", C.c_void_p), ("router_bias", C.c_void_p),
                 ("w13", moe_weights), ("w2", moe_weights), ("sh13", moe_weights),
-                ("sh2", moe_weights), ("gamma", C.c_void_p), ("swiglu_limit", C.c_float)]
+                ("sh2", moe_weights), ("gamma", C.c_void_p), ("swiglu_limit", C.c_float),
+                ("act_fmt", C.c_int), ("x_global", C.c_float), ("h_globals", C.c_void_p),
+                ("sh_h_global", C.c_void_p)]
 
 
 _lib = None
@@ -84,6 +87,12 @@ def lib() -> C.CDLL:
         L.moe_expert_down.restype = i
         L.moe_expert_down.argtypes = [C.POINTER(moe_weights), vp, vp, vp, C.POINTER(moe_routing),
                                       i, i, i, i, i, vp, vp]
+        L.moe_expert_gate_up_nvfp4a.restype = i
+        L.moe_expert_gate_up_nvfp4a.argtypes = [C.POINTER(moe_weights), vp, vp, f, C.POINTER(moe_routing),
+                                                i, i, i, i, i, f, vp, vp, vp, vp]
+        L.moe_expert_down_nvfp4a.restype = i
+        L.moe_expert_down_nvfp4a.argtypes = [C.POINTER(moe_weights), vp, vp, vp, C.POINTER(moe_routing),
+                                             i, i, i, i, i, vp, vp]
         L.moe_finalize_rmsnorm.restype = i
         L.moe_finalize_rmsnorm.argtypes = [vp, vp, vp, vp, vp, f, i, i, i, vp, vp, vp]
         L.moe_finalize_rmsnorm_mxfp8.restype = i
@@ -260,6 +269,29 @@ def expert_down(w2: Weights, M, H, I, E, k, y, routing: Optional[Routing] = None
     _check(rc, "moe_expert_down")
 
 
+def expert_gate_up_nvfp4a(w13: Weights, M, H, I, E, k, a_q, a_s, a_global: float, h_globals, h_q, h_s,
+                          routing: Optional[Routing] = None, swiglu_limit=0.0, stream=None):
+    """gate_up of NVFP4 experts on NVFP4 activations; h written as NVFP4
+    with h_globals (device fp32 [E], or [1] without a routing)."""
+    _need_packed(w13)
+    wc = w13.c()
+    r = None if routing is None else routing.c()
+    rc = lib().moe_expert_gate_up_nvfp4a(C.byref(wc), _p(a_q), _p(a_s), float(a_global),
+                                         None if r is None else C.byref(r), M, H, I, E, k, float(swiglu_limit),
+                                         _p(h_globals), _p(h_q), _p(h_s), _stream(stream))
+    _check(rc, "moe_expert_gate_up_nvfp4a")
+
+
+def expert_down_nvfp4a(w2: Weights, M, H, I, E, k, h_q, h_s, h_globals, y, routing: Optional[Routing] = None,
+                       stream=None):
+    _need_packed(w2)
+    wc = w2.c()
+    r = None if routing is None else routing.c()
+    rc = lib().moe_expert_down_nvfp4a(C.byref(wc), _p(h_q), _p(h_s), _p(h_globals),
+                                      None if r is None else C.byref(r), M, H, I, E, k, _p(y), _stream(stream))
+    _check(rc, "moe_expert_down_nvfp4a")
+
+
 def finalize_rmsnorm(y, topk_w, y_sh, residual, gamma, eps, out, residual_out=None, stream=None,
                      out_q=None, out_s=None):
     """moe_finalize_rmsnorm; with out_q/out_s, moe_finalize_rmsnorm_mxfp8."""
@@ -280,13 +312,15 @@ class Layer:
     """The fused layer (moe_layer) over weights held in torch device tensors."""
 
     def __init__(self, M, H, E, k, I, I_sh, routed_scale, eps, w_router, router_bias,
-                 w13: Weights, w2: Weights, sh13: Weights, sh2: Weights, gamma, swiglu_limit=0.0):
+                 w13: Weights, w2: Weights, sh13: Weights, sh2: Weights, gamma, swiglu_limit=0.0,
+                 act_fmt=0, x_global=0.0, h_globals=None, sh_h_global=None):
         _need_packed(w13, w2, sh13, sh2)
-        self._keep = (w_router, router_bias, w13, w2, sh13, sh2, gamma)
+        self._keep = (w_router, router_bias, w13, w2, sh13, sh2, gamma, h_globals, sh_h_global)
         self.M, self.H, self.E, self.k = M, H, E, k
         self.desc = moe_layer_desc(M, H, E, k, I, I_sh, float(routed_scale), float(eps),
                                    _p(w_router), _p(router_bias), w13.c(), w2.c(), sh13.c(),
-                                   sh2.c(), _p(gamma), float(swiglu_limit))
+                                   sh2.c(), _p(gamma), float(swiglu_limit), int(act_fmt), float(x_global),
+                                   _p(h_globals), _p(sh_h_global))
         self.ws_bytes = lib().moe_layer_workspace_bytes(C.byref(self.desc))
         if self.ws_bytes == 0:
             raise RuntimeError("moe_layer_workspace_bytes rejected the layer description")

@@ -59,11 +59,17 @@ class DeviceInputs:
     w2: Weights
     sh13: Weights
     sh2: Weights
+    # NVFP4 activations: the input's global (host) and the h globals (device)
+    x_global: float = 0.0
+    h_globals: Optional[torch.Tensor] = None     # fp32 [E]
+    sh_h_global: Optional[torch.Tensor] = None   # fp32 [1]
 
     def layer(self) -> Layer:
         s = self.shape
         return Layer(s.M, s.H, s.E, s.k, s.I, s.I_sh, s.routed_scale, s.eps, self.Wr, self.bias,
-                     self.w13, self.w2, self.sh13, self.sh2, self.gamma, s.swiglu_limit)
+                     self.w13, self.w2, self.sh13, self.sh2, self.gamma, s.swiglu_limit,
+                     s.act_fmt, self.x_global, self.h_globals,
+                     self.sh_h_global if s.sfmt == synth.NVFP4 else None)
 
     def weight_bytes_per_expert(self) -> int:
         s = self.shape
@@ -83,4 +89,7 @@ def to_device(inp: synth.MoEInputs, device="cuda") -> DeviceInputs:
         pooled_on(inp.w2, device),
         matrix_on(inp.sh13, device),
         matrix_on(inp.sh2, device),
+        float(inp.x_gscale),
+        None if inp.h_gscale is None else _t(np.ascontiguousarray(inp.h_gscale, np.float32), device),
+        None if inp.h_gscale is None else _t(np.array([inp.sh_h_gscale], np.float32), device),
     )

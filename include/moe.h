@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 enum moe_status {
     MOE_OK = 0,
@@ -75,6 +75,12 @@ enum moe_fmt {
  * places); bf16 weights are taken as they are.
  * Gate_up weights (W13) have N = 2I with rows [0, I) the gate projection and
  * rows [I, 2I) the up projection; down weights (W2) have N = H, K = I. */
+/* Activation formats of the expert GEMMs (moe_layer_desc.act_fmt). */
+enum {
+    MOE_ACT_MXFP8 = 0, /* E4M3 + E8M0 per 32 (every weight format) */
+    MOE_ACT_NVFP4 = 1  /* E2M1 + E4M3 per 16 + an fp32 global (NVFP4 weights: W4A4) */
+};
+
 typedef struct moe_weights {
     int fmt;
     const void *w;
@@ -127,6 +133,14 @@ typedef struct moe_layer_desc {
     moe_weights sh13, sh2;       /* shared expert: [2I_sh, H] and [H, I_sh]; fmt NONE = absent */
     const uint16_t *gamma;       /* bf16 [H] RMSNorm weight */
     float swiglu_limit;          /* clamped SwiGLU of every expert (see moe_expert_gate_up); 0: unclamped */
+    /* NVFP4 activations (act_fmt MOE_ACT_NVFP4, NVFP4 experts; shared expert
+     * NONE, NVFP4 or BF16): x is quantized with x_global in the router launch
+     * (moe_quant_act_nvfp4), each routed expert's h with h_globals[e] and the
+     * shared expert's h with *sh_h_global (static globals, device fp32). */
+    int act_fmt;
+    float x_global;
+    const float *h_globals;      /* [E] */
+    const float *sh_h_global;    /* [1], or NULL without an NVFP4 shared expert */
 } moe_layer_desc;
 
 const char *moe_status_str(int status);
@@ -259,6 +273,29 @@ int moe_expert_gate_up(const moe_weights *w13, const uint8_t *a_q, const uint8_t
 int moe_expert_down(const moe_weights *w2, const uint8_t *h_q, const uint8_t *h_s,
                     const uint16_t *h_bf16, const moe_routing *route, int M, int H, int I,
                     int E, int k, float *y, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_gate_up_nvfp4a / moe_expert_down_nvfp4a — the expert GEMMs of
+ * NVFP4 experts with NVFP4 activations (W4A4).
+ *   Pages: README Qwen3.5 slot table, row "mkm" (top-10, FC1, SwiGLU, the
+ *   NVFP4 requantization and FC2) and row "route" (the NVFP4 input).
+ * gate_up: as moe_expert_gate_up for NVFP4 weights, with A the NVFP4 codes
+ *   a_q [Pr, H/2] and scales a_s [Pr, H/16] of global a_global (what
+ *   moe_quant_act_nvfp4 writes; route == NULL: Pr = M rows in order, else
+ *   bucket order), and h written as NVFP4 (h_q [Pr, I/2], h_s [Pr, I/16]) by
+ *   the rule of moe_quant_act_nvfp4 applied to the fp32 h, with global
+ *   h_globals[e] of the row's expert (device fp32 [E]; route == NULL: [1]).
+ *   Products exact (the E2M1 x E4M3 operands are exact in f16), fp32 sums.
+ *   No workspace.
+ * down: y as moe_expert_down, with h the NVFP4 codes and scales above and
+ *   h_globals their globals.
+ * Weights must be NVFP4 (else MOE_ERR_UNSUPPORTED); a_global > 0 finite. */
+int moe_expert_gate_up_nvfp4a(const moe_weights *w13, const uint8_t *a_q, const uint8_t *a_s, float a_global,
+                              const moe_routing *route, int M, int H, int I, int E, int k, float swiglu_limit,
+                              const float *h_globals, uint8_t *h_q, uint8_t *h_s, hipStream_t stream);
+int moe_expert_down_nvfp4a(const moe_weights *w2, const uint8_t *h_q, const uint8_t *h_s, const float *h_globals,
+                           const moe_routing *route, int M, int H, int I, int E, int k, float *y,
+                           hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_finalize_rmsnorm — top-k weighted sum of the expert outputs fused with

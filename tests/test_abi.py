@@ -51,7 +51,7 @@ def test_probe_library_exports():
 
 
 def test_version_and_status_strings(L):
-    assert moe.abi_version() == 6
+    assert moe.abi_version() == 7
     for rc in range(5):
         assert len(moe.status_str(rc)) > 0
     assert "unknown" in moe.status_str(99)
@@ -112,6 +112,19 @@ def test_layer_desc_validation(L):
               w2=moe.moe_weights(moe.MOE_FMT_BF16, 0x1000, None, None)),  # bf16 routed experts
         _desc(swiglu_limit=-0.5),
         _desc(swiglu_limit=float("nan")),
+        _desc(act_fmt=2),                                # unknown activation format
+        _desc(act_fmt=1, x_global=1.0, h_globals=0x1000),  # NVFP4 activations with MXFP4 experts
+    ]
+    nv = moe.moe_weights(moe.MOE_FMT_NVFP4, 0x1000, 0x1000, 0x1000)
+    a4 = dict(w13=nv, w2=nv, act_fmt=1, x_global=0.01, h_globals=0x1000)
+    assert L.moe_layer_workspace_bytes(C.byref(_desc(**a4))) > 0
+    bad += [
+        _desc(**dict(a4, x_global=0.0)),
+        _desc(**dict(a4, x_global=float("inf"))),
+        _desc(**dict(a4, h_globals=None)),
+        _desc(**dict(a4, I_sh=256, sh13=nv, sh2=nv)),    # NVFP4 shared expert without its h global
+        _desc(**dict(a4, I_sh=256, sh13=moe.moe_weights(moe.MOE_FMT_MXFP4, 0x1000, 0x1000, None),
+                     sh2=moe.moe_weights(moe.MOE_FMT_MXFP4, 0x1000, 0x1000, None))),  # MXFP4 shared
     ]
     for d in bad:
         assert L.moe_layer_workspace_bytes(C.byref(d)) == 0
@@ -181,5 +194,17 @@ def test_calls_refuse_before_enqueueing(L):
                                     None, 0x1000, 0x1000, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_expert_down(C.byref(w), None, None, 0x1000, None, 4, 128, 100, 1, 1, 0x1000,
                              None) == moe.MOE_ERR_UNSUPPORTED
+    # W4A4: NVFP4 weights only, a positive activation global, the h globals given
+    mx = moe.moe_weights(moe.MOE_FMT_MXFP4, 0x1000, 0x1000, None)
+    nvw = moe.moe_weights(moe.MOE_FMT_NVFP4, 0x1000, 0x1000, 0x1000)
+    gu4 = lambda wt, g, hg: L.moe_expert_gate_up_nvfp4a(C.byref(wt), 0x1000, 0x1000, g, None, 4, 128, 128, 1, 1,
+                                                         0.0, hg, 0x1000, 0x1000, None)
+    assert gu4(mx, 1.0, 0x1000) == moe.MOE_ERR_UNSUPPORTED
+    assert gu4(nvw, 0.0, 0x1000) == moe.MOE_ERR_INVALID_ARG
+    assert gu4(nvw, 1.0, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_down_nvfp4a(C.byref(mx), 0x1000, 0x1000, 0x1000, None, 4, 128, 128, 1, 1, 0x1000,
+                                    None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_down_nvfp4a(C.byref(nvw), 0x1000, 0x1000, None, None, 4, 128, 128, 1, 1, 0x1000,
+                                    None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_finalize_rmsnorm(0x1000, 0x1000, None, 0x1000, 0x1000, -1.0, 4, 128, 2, 0x1000,
                                   None, None) == moe.MOE_ERR_INVALID_ARG

@@ -65,6 +65,12 @@ EDGE = [
     # the clamped SwiGLU in routed and shared experts (few pairs, many pairs; MX, NV and bf16 shared)
     dict(M=9, H=512, E=64, k=6, I=384, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=256, swiglu_limit=0.4),
     dict(M=48, H=1024, E=32, k=8, I=256, wfmt=synth.MXFP4, sfmt=synth.MXFP4, I_sh=256, swiglu_limit=0.5),
+    # NVFP4 activations (W4A4): the 7-row verify shape of the pages' Qwen3.5 row with top-10, bf16
+    # shared; few pairs with an NVFP4 shared expert; many pairs (bucketed launches), K-streamed down
+    dict(M=7, H=1024, E=64, k=10, I=256, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=256, act_fmt=synth.ACT_NVFP4),
+    dict(M=9, H=512, E=16, k=4, I=384, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=256, act_fmt=synth.ACT_NVFP4),
+    dict(M=40, H=768, E=32, k=8, I=640, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=640, act_fmt=synth.ACT_NVFP4,
+         swiglu_limit=0.6),
 ]
 
 

@@ -417,3 +417,95 @@ def test_finalize_mxfp8_next_input(M, H):
         o64 = orc.finalize_row(y[r * k:(r + 1) * k].astype(np.float64), w[r], ysh[r].astype(np.float64),
                                res[r], gamma, 1e-6)[0]
         assert rel_l2(deq[r], o64) < 2.0 ** -4
+
+
+# ---- NVFP4 activations (W4A4) ---------------------------------------------------
+
+def _a4_setup(M, H, E, k, I, seed, I_sh=0, sfmt=synth.NONE, limit=0.0):
+    sh = synth.custom_shape(M=M, H=H, E=E, k=k, I=I, wfmt=synth.NVFP4, sfmt=sfmt, I_sh=I_sh, bias="zipf:1.0",
+                            act_fmt=synth.ACT_NVFP4, swiglu_limit=limit)
+    inp = synth.make_inputs(sh, seed=seed, pool_rows=2048)
+    inp = synth.vary_globals(inp, seed + 1)
+    d = staging.to_device(inp, DEV)
+    rt = moe.Routing(M, E, k, DEV)
+    moe.route_topk(rt, x=d.x, w_router=d.Wr, bias=d.bias, routed_scale=sh.routed_scale,
+                   logits_out=torch.empty((M, E), dtype=torch.float32, device=DEV))
+    xqp = torch.empty((M * k, H // 2), dtype=torch.uint8, device=DEV)
+    xsp = torch.empty((M * k, H // 16), dtype=torch.uint8, device=DEV)
+    moe.quant_act_nvfp4(d.x, inp.x_gscale, xqp, xsp, routing=rt)
+    return sh, inp, d, rt, xqp, xsp
+
+
+def _h4_compare(ghq, ghs, rows_h, hg):
+    """h bytes against the oracle's NVFP4 requant of its own fp64 h (read in
+    fp32): codes equal but at rounding midpoints of fp32 vs fp64 sums."""
+    eq, tot, worst = 0, 0, 0.0
+    for b, (h, g) in enumerate(zip(rows_h, hg)):
+        rq, rs = orc.nvfp4_quant_f32(h[None, :].astype(np.float32), g)
+        eq += int(np.sum(rq[0] == ghq[b])) + int(np.sum(rs[0] == ghs[b]))
+        tot += rq.shape[1] + rs.shape[1]
+        hd = orc.nvfp4_dequant(ghq[b:b + 1], ghs[b:b + 1], g)[0]
+        worst = max(worst, rel_l2(hd, orc.nvfp4_dequant(rq, rs, g)[0]))
+    return eq / tot, worst
+
+
+@pytest.mark.parametrize("H,I,limit", [(512, 256, 0.0), (2560, 256, 0.0), (2560, 768, 0.5)])
+def test_gate_up_down_nvfp4a_routed_parity(H, I, limit):
+    """W4A4 routed experts: gate_up on NVFP4 activations writes NVFP4 h with
+    each expert's global; down reads it (I = 256: along the rows; 768: along K)."""
+    M, E, k = 40, 6, 3
+    sh, inp, d, rt, xqp, xsp = _a4_setup(M, H, E, k, I, seed=21, limit=limit)
+    P = M * k
+    hq = torch.empty((P, I // 2), dtype=torch.uint8, device=DEV)
+    hs = torch.empty((P, I // 16), dtype=torch.uint8, device=DEV)
+    moe.expert_gate_up_nvfp4a(d.w13, M, H, I, E, k, xqp, xsp, inp.x_gscale, d.h_globals, hq, hs, routing=rt,
+                              swiglu_limit=limit)
+    y = torch.full((P, H), float("nan"), dtype=torch.float32, device=DEV)
+    moe.expert_down_nvfp4a(d.w2, M, H, I, E, k, hq, hs, d.h_globals, y, routing=rt)
+    torch.cuda.synchronize()
+    bucket, ids = np_of(rt.bucket), np_of(rt.topk_ids).ravel()
+    xq, xs = orc.nvfp4_quant_bf16(inp.x, inp.x_gscale)
+    a = orc.nvfp4_dequant(xq, xs, inp.x_gscale)
+    hs_ref, hgs = [], []
+    for b in range(P):
+        p = bucket[b]
+        m13 = inp.w13.expert(ids[p])
+        hs_ref.append(orc.gate_up(orc.Mat(m13.fmt, m13.packed, m13.scales, m13.gscale), H, I, a[p // k], limit))
+        hgs.append(float(inp.h_gscale[ids[p]]))
+    frac, worst = _h4_compare(np_of(hq), np_of(hs), hs_ref, hgs)
+    assert frac >= 0.999, frac
+    assert worst < 0.1, worst   # a flipped code is one E2M1 step (up to 1/3 of the value)
+    gy = np_of(y)
+    worst_y = 0.0
+    for b in range(P):
+        p = bucket[b]
+        m2 = inp.w2.expert(ids[p])
+        hd = orc.nvfp4_dequant(np_of(hq)[b:b + 1], np_of(hs)[b:b + 1], float(inp.h_gscale[ids[p]]))[0]
+        yr = orc.down(orc.Mat(m2.fmt, m2.packed, m2.scales, m2.gscale), H, I, hd)
+        worst_y = max(worst_y, rel_l2(gy[p], yr))
+    assert worst_y < 2e-3, worst_y
+
+
+@pytest.mark.parametrize("M", [23, 70])
+def test_dense_nvfp4a_expert_parity(M):
+    """The NVFP4 shared expert on NVFP4 activations (one expert over all rows)."""
+    H, I = 384, 256
+    sh, inp, d, rt, _, _ = _a4_setup(M, H, 4, 2, 128, seed=23, I_sh=I, sfmt=synth.NVFP4)
+    xq = torch.empty((M, H // 2), dtype=torch.uint8, device=DEV)
+    xs = torch.empty((M, H // 16), dtype=torch.uint8, device=DEV)
+    moe.quant_act_nvfp4(d.x, inp.x_gscale, xq, xs)
+    hq = torch.empty((M, I // 2), dtype=torch.uint8, device=DEV)
+    hs = torch.empty((M, I // 16), dtype=torch.uint8, device=DEV)
+    moe.expert_gate_up_nvfp4a(d.sh13, M, H, I, 1, 1, xq, xs, inp.x_gscale, d.sh_h_global, hq, hs)
+    y = torch.empty((M, H), dtype=torch.float32, device=DEV)
+    moe.expert_down_nvfp4a(d.sh2, M, H, I, 1, 1, hq, hs, d.sh_h_global, y)
+    torch.cuda.synchronize()
+    a = orc.nvfp4_dequant(np_of(xq), np_of(xs), inp.x_gscale)
+    m13, m2 = orc.Mat.from_synth(inp.sh13), orc.Mat.from_synth(inp.sh2)
+    frac, _ = _h4_compare(np_of(hq), np_of(hs), [orc.gate_up(m13, H, I, a[r]) for r in range(M)],
+                          [inp.sh_h_gscale] * M)
+    assert frac >= 0.999, frac
+    gy = np_of(y)
+    for r in range(M):
+        hd = orc.nvfp4_dequant(np_of(hq)[r:r + 1], np_of(hs)[r:r + 1], inp.sh_h_gscale)[0]
+        assert rel_l2(gy[r], orc.down(m2, H, I, hd)) < 2e-3
