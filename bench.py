@@ -66,9 +66,11 @@ def byte_model(s, U):
         shared = expert_bytes(s, s.sfmt, 2 * s.I_sh, s.H) + expert_bytes(s, s.sfmt, s.H, s.I_sh)
     router = 4 * s.E * s.H
     acts = 8 * s.M * s.H  # x, residual in; out, residual_out
+    a4 = s.act_fmt == synth.ACT_NVFP4
+    anum, aden = (9, 16) if a4 else (33, 32)  # activation bytes per value: NVFP4 or MXFP8
     gate_up_launch = (U * expert_bytes(s, s.wfmt, 2 * s.I, s.H)
-                      + s.M * s.H * 33 // 32            # MXFP8 activations in
-                      + s.M * s.k * s.I * 33 // 32)     # MXFP8 h out
+                      + s.M * s.H * anum // aden            # activations in
+                      + s.M * s.k * s.I * anum // aden)     # h out
     return dict(per_expert=per_expert, routed=U * per_expert, shared=shared, router=router,
                 acts=acts, total=U * per_expert + shared + router + acts,
                 gate_up_launch=gate_up_launch)
@@ -205,6 +207,33 @@ def window_stats(per):
             "p90": round(float(np.percentile(a, 90)), 2), "windows": len(a)}
 
 
+def gate_up_alone(moe, s, d, logits, dev):
+    """The routed gate_up as one launch on bucket-ordered activations (MXFP8,
+    or NVFP4 for W4A4 workloads): returns a function of the W13 copy."""
+    import torch
+    from block_scaled_fp4_sigmoid_amd import synth
+    rt = moe.Routing(s.M, s.E, s.k, dev)
+    moe.route_topk(rt, x=d.x, w_router=d.Wr, bias=d.bias, routed_scale=s.routed_scale, logits_out=logits)
+    P = s.M * s.k
+    if s.act_fmt == synth.ACT_NVFP4:
+        xq = torch.empty((P, s.H // 2), dtype=torch.uint8, device=dev)
+        xs = torch.empty((P, s.H // 16), dtype=torch.uint8, device=dev)
+        moe.quant_act_nvfp4(d.x, d.x_global, xq, xs, routing=rt)
+        hq = torch.empty((P, s.I // 2), dtype=torch.uint8, device=dev)
+        hs = torch.empty((P, s.I // 16), dtype=torch.uint8, device=dev)
+        return lambda w13: moe.expert_gate_up_nvfp4a(w13, s.M, s.H, s.I, s.E, s.k, xq, xs, d.x_global,
+                                                     d.h_globals, hq, hs, routing=rt)
+    xq = torch.empty((P, s.H), dtype=torch.uint8, device=dev)
+    xs = torch.empty((P, s.H // 32), dtype=torch.uint8, device=dev)
+    moe.quant_act_mxfp8(d.x, xq, xs, routing=rt)
+    hq = torch.empty((P, s.I), dtype=torch.uint8, device=dev)
+    hs = torch.empty((P, s.I // 32), dtype=torch.uint8, device=dev)
+    ws = moe.workspace(max(256, moe.lib().moe_gate_up_workspace_bytes(d.w13.fmt, s.M, s.H, s.I, s.E, s.k, 0)),
+                       dev)
+    return lambda w13: moe.expert_gate_up(w13, s.M, s.H, s.I, s.E, s.k, routing=rt, a_q=xq, a_s=xs, h_q=hq,
+                                          h_s=hs, ws=ws)
+
+
 def cpu_baseline(inp, logits):
     from oracle import oracle as orc
     s = inp.shape
@@ -257,7 +286,7 @@ def main():
     dev = "cuda"
     name = args.workload
     s = synth.WORKLOADS[name]
-    seed = args.seed if args.seed is not None else synth.WORKLOAD_ORDER.index(name) + 1
+    seed = args.seed if args.seed is not None else synth.seed_of(name)
     t0 = time.time()
     inp = synth.make_inputs(name, seed=seed)
     d = staging.to_device(inp, dev)
@@ -285,21 +314,14 @@ def main():
         Wr = d.Wr.clone()
         keep.append((w13, w2, sh13, sh2, Wr))
         layers.append(moe.Layer(s.M, s.H, s.E, s.k, s.I, s.I_sh, s.routed_scale, s.eps, Wr, d.bias,
-                                w13, w2, sh13, sh2, d.gamma, s.swiglu_limit))
+                                w13, w2, sh13, sh2, d.gamma, s.swiglu_limit, s.act_fmt, d.x_global,
+                                d.h_globals, d.sh_h_global if s.sfmt == synth.NVFP4 else None))
     stream = torch.cuda.current_stream()
 
     if args.profile_gate_up:
-        rt = moe.Routing(s.M, s.E, s.k, dev)
-        moe.route_topk(rt, x=d.x, w_router=d.Wr, bias=d.bias, routed_scale=s.routed_scale,
-                       logits_out=logits)
-        xq = torch.empty((s.M * s.k, s.H), dtype=torch.uint8, device=dev)
-        xs = torch.empty((s.M * s.k, s.H // 32), dtype=torch.uint8, device=dev)
-        moe.quant_act_mxfp8(d.x, xq, xs, routing=rt)
-        hq = torch.empty((s.M * s.k, s.I), dtype=torch.uint8, device=dev)
-        hs = torch.empty((s.M * s.k, s.I // 32), dtype=torch.uint8, device=dev)
+        gate_up_w = gate_up_alone(moe, s, d, logits, dev)
         for i in range(args.profile_gate_up):
-            w13 = d.w13 if i % copies == 0 else keep[i % copies - 1][0]
-            moe.expert_gate_up(w13, s.M, s.H, s.I, s.E, s.k, routing=rt, a_q=xq, a_s=xs, h_q=hq, h_s=hs)
+            gate_up_w(d.w13 if i % copies == 0 else keep[i % copies - 1][0])
         torch.cuda.synchronize()
         log(f"[bench] launched routed gate_up {args.profile_gate_up} times")
         return
@@ -350,21 +372,11 @@ def main():
         ms, timing, win = ms_chain, "graph of %d consecutive layer steps, replayed" % chain, win_chain
 
     # dominant kernel alone: routed gate_up, timed with HIP events on its stream
-    rt = moe.Routing(s.M, s.E, s.k, dev)
-    moe.route_topk(rt, x=d.x, w_router=d.Wr, bias=d.bias, routed_scale=s.routed_scale,
-                   logits_out=logits)
-    xq = torch.empty((s.M * s.k, s.H), dtype=torch.uint8, device=dev)
-    xs = torch.empty((s.M * s.k, s.H // 32), dtype=torch.uint8, device=dev)
-    moe.quant_act_mxfp8(d.x, xq, xs, routing=rt)
-    hq = torch.empty((s.M * s.k, s.I), dtype=torch.uint8, device=dev)
-    hs = torch.empty((s.M * s.k, s.I // 32), dtype=torch.uint8, device=dev)
     w13s = [d.w13] + [k_[0] for k_ in keep]
-    gu_ws = moe.workspace(max(256, moe.lib().moe_gate_up_workspace_bytes(d.w13.fmt, s.M, s.H, s.I, s.E,
-                                                                         s.k, 0)), dev)
+    gate_up_w = gate_up_alone(moe, s, d, logits, dev)
 
     def gate_up(i):
-        moe.expert_gate_up(w13s[i % copies], s.M, s.H, s.I, s.E, s.k, routing=rt, a_q=xq, a_s=xs,
-                           h_q=hq, h_s=hs, ws=gu_ws)
+        gate_up_w(w13s[i % copies])
 
     ms_gu, win_gu = timed(gate_up, args.steps, args.warmup, stream)
     gu_gbps = bm["gate_up_launch"] / (ms_gu * 1e-3) / 1e9
@@ -419,10 +431,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4xfp8->fp32",
+        "dtype": "fp4xfp4->fp32" if s.act_fmt == synth.ACT_NVFP4 else "fp4xfp8->fp32",
         "data": "synthetic (seeded; weights drawn N(0,0.02) and encoded offline)",
         "config": {"workload": name, "rows": s.M, "hidden": s.H, "experts": s.E, "top_k": s.k,
                    "intermediate": s.I, "weights": synth.FMT_NAMES[s.wfmt],
+                   "activations": "nvfp4" if s.act_fmt == synth.ACT_NVFP4 else "mxfp8",
                    "shared": synth.FMT_NAMES[s.sfmt], "unique_experts": U,
                    "weight_copies": copies, "parallelism": "single GPU"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),

@@ -169,6 +169,26 @@ WORKLOADS = {
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
+# Further workloads (not among the five): NVFP4 activations (W4A4) at the
+# pages' Qwen3.5 verify step of 7 rows with top-10 (README slot table, rows
+# "route" and "mkm"); the pages give no layer dimensions, so it takes the
+# skewed-routing workload's (hidden 4096, 512 experts, intermediate 512, bf16
+# shared expert of 512) without the bias.
+EXTRA_WORKLOADS = {
+    "verify7-m7-h4096-e512-k10-nvfp4-a4": Shape(
+        "verify7-m7-h4096-e512-k10-nvfp4-a4", 7, 4096, 512, 10, 512, NVFP4, BF16, 512, 1.0, "none",
+        act_fmt=ACT_NVFP4,
+        desc="7-row verify step with top-10, NVFP4 experts on NVFP4 activations (W4A4), bf16 shared expert"),
+}
+WORKLOADS.update(EXTRA_WORKLOADS)
+
+
+def seed_of(name: str) -> int:
+    """Default seed of a named workload: 1-5 for the five, 101.. for the others."""
+    if name in WORKLOAD_ORDER:
+        return WORKLOAD_ORDER.index(name) + 1
+    return 101 + list(EXTRA_WORKLOADS).index(name)
+
 
 def custom_shape(M, H, E, k, I, wfmt=MXFP4, sfmt=NONE, I_sh=None, routed_scale=1.0,
                  bias="none", eps=1e-6, name=None, swiglu_limit=0.0, act_fmt=0) -> Shape:

@@ -55,6 +55,20 @@ def test_layer_parity_workload(name):
     assert c["res_rel_l2"] <= REL_L2_MAX
 
 
+@pytest.mark.parametrize("name", list(synth.EXTRA_WORKLOADS))
+def test_layer_parity_extra_workload(name):
+    """The further workloads (W4A4 7-row verify) at their full shape, sampled rows."""
+    inp = synth.make_inputs(name, seed=synth.seed_of(name))
+    d = staging.to_device(inp, DEV)
+    print(f"[layer parity] {name}", flush=True)
+    run = LayerRun(d)
+    c = compare_layer(inp, run, np.arange(inp.shape.M))
+    print(f"  rel_l2={c['rel_l2']:.3e} max_abs={c['max_abs']:.3e} res_rel_l2={c['res_rel_l2']:.3e}", flush=True)
+    assert c["ids_ok"]
+    assert c["rel_l2"] <= REL_L2_MAX and c["max_abs"] <= MAX_ABS_MAX
+    assert c["res_rel_l2"] <= REL_L2_MAX
+
+
 EDGE = [
     dict(M=1, H=128, E=1, k=1, I=128),                                  # smallest layer
     dict(M=5, H=256, E=4, k=4, I=128, bias="normal:0.05"),               # top-k = all experts
