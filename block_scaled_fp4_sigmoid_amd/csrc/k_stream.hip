@@ -879,14 +879,17 @@ __device__ __forceinline__ uint32_t mx_quant4_group8(const float hv[4], uint8_t&
 // (routed) or token rows (dense).  Otherwise fp32 partials part[split][row][2I]
 // (already multiplied by the NVFP4 row factor).
 
-constexpr int GMB = 2;           // 16-row weight blocks per wave in gate_up (four: decode 269 -> 296 us)
-constexpr int GCOLS = 32 * GMB;  // output columns per workgroup
+// 16-row weight blocks per wave in gate_up: two (four: decode 269 -> 296
+// us), or one for NVFP4 weights when a two-block grid would not reach one
+// workgroup per CU (verify: 26.0 -> 24.8 us alone; MXFP4 decode with one:
+// 269 -> 347 us).  Output columns per workgroup: 32 * blocks.
+constexpr int kGateMB = 2, kGateMBSmall = 1;
 
 // Workgroups [0, n2) take items of a second job J2 of the same format (the
 // FP4 shared expert riding along the routed experts; first, so its few long
 // items do not trail the launch), [n2, nmain) items of job J0, later ones a
 // bf16 shared-expert stage.
-template <int FMT, bool FUSED>
+template <int FMT, bool FUSED, int GMB>
 __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS) void k_gate_up(
     StreamJob J0, uint8_t* __restrict__ h_q0, uint8_t* __restrict__ h_s0, float* __restrict__ part, int nmain,
     Bf16Side side, int stage, StreamJob J2, uint8_t* __restrict__ h_q2, uint8_t* __restrict__ h_s2, int n2) {
@@ -900,6 +903,7 @@ __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS)
     uint8_t* __restrict__ h_s = second ? h_s2 : h_s0;
     const int bid = second ? (int)blockIdx.x : (int)blockIdx.x - n2;
     const int I = J.N / 2, K = J.K;
+    constexpr int GCOLS = 32 * GMB;  // output columns per workgroup
     const int ks = bid % J.splits;
     const int blk = (bid / J.splits) % J.nblk;
     const int slot = bid / (J.splits * J.nblk);
@@ -1337,10 +1341,16 @@ struct GatePlan {
     int span, splits, nblk;
 };
 
-GatePlan gate_plan(const ExpertJob& j) {
+// Weight blocks per wave of a gate_up launch (see kGateMB).
+int gate_mb(const ExpertJob& j) {
+    const bool nv = j.w.fmt == MOE_FMT_NVFP4;
+    return nv && (long)grid_slots(j) * (j.N_out / (32 * kGateMB)) <= 256 ? kGateMBSmall : kGateMB;
+}
+
+GatePlan gate_plan(const ExpertJob& j, int gmb) {
     GatePlan p;
     const int K = j.K, steps = K / 128;
-    p.nblk = j.N_out / GCOLS;
+    p.nblk = j.N_out / (32 * gmb);
     if (j.a_nvfp4) {  // NVFP4 activations: all of K in one item (the requant needs the expert's h global)
         p.span = K;
         p.splits = 1;
@@ -1397,15 +1407,35 @@ int out_rows_of(const ExpertJob& j) { return j.dense ? j.M : j.M * j.k; }
 }  // namespace
 
 size_t gate_up_fp4_partials_bytes(const ExpertJob& job) {
-    const GatePlan p = gate_plan(job);
+    const int gmb = gate_mb(job);
+    const GatePlan p = gate_plan(job, gmb);
     if (p.splits == 1) return 0;
     return align_up((size_t)p.splits * out_rows_of(job) * 2 * job.N_out * sizeof(float));
+}
+
+// One gate_up launch with the kernel of gmb weight blocks per wave (MXFP4
+// always takes kGateMB).
+template <int F, bool FU>
+hipError_t launch_gu(int gmb, dim3 g, hipStream_t stream, const StreamJob& J, uint8_t* h_q, uint8_t* h_s,
+                     float* partials, int nmain, const Bf16Side& side, int stage, const StreamJob& J2, uint8_t* hq2,
+                     uint8_t* hs2, int n2) {
+    if constexpr (F != kFmtMX) {
+        if (gmb == kGateMBSmall) {
+            hipLaunchKernelGGL((k_gate_up<F, FU, kGateMBSmall>), g, dim3(kThreads), 0, stream, J, h_q, h_s, partials,
+                               nmain, side, stage, J2, hq2, hs2, n2);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((k_gate_up<F, FU, kGateMB>), g, dim3(kThreads), 0, stream, J, h_q, h_s, partials, nmain, side,
+                       stage, J2, hq2, hs2, n2);
+    return hipGetLastError();
 }
 
 hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const uint8_t* a_s, uint8_t* h_q,
                               uint8_t* h_s, float* partials, hipStream_t stream, const Bf16Side& side, int stage,
                               const SecondJob& second) {
-    const GatePlan p = gate_plan(job);
+    const int gmb = gate_mb(job);
+    const GatePlan p = gate_plan(job, gmb);
     const int rows = out_rows_of(job);
     StreamJob J = stream_job(job, 2 * job.N_out, a_q, a_s, rows);
     J.span = p.span;
@@ -1420,7 +1450,7 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
         const ExpertJob& j2 = *second.job;
         if (p.splits == 1 && j2.w.fmt == job.w.fmt && j2.a_nvfp4 == job.a_nvfp4) {
             J2 = stream_job(j2, 2 * j2.N_out, second.a_q, second.a_s, out_rows_of(j2));
-            J2.nblk = j2.N_out / GCOLS;  // span = K, one split
+            J2.nblk = j2.N_out / (32 * gmb);  // span = K, one split
             n2 = grid_slots(j2) * J2.nblk;
         } else {
             hipError_t e = launch_gate_up_fp4(j2, second.a_q, second.a_s, second.h_q, second.h_s, second.partials,
@@ -1429,29 +1459,21 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
         }
     }
     const int extra = stage == kBf16None ? 0 : side.blocks;
-    const dim3 g(blocks + n2 + extra), b(kThreads);
+    const dim3 g(blocks + n2 + extra);
     uint8_t* hq2 = n2 ? second.h_q : h_q;
     uint8_t* hs2 = n2 ? second.h_s : h_s;
     const int nmain = blocks + n2;
     if (p.splits == 1) {
         if (job.a_nvfp4)
-            hipLaunchKernelGGL((k_gate_up<kFmtNV4, true>), g, b, 0, stream, J, h_q, h_s, partials, nmain, side, stage,
-                               J2, hq2, hs2, n2);
-        else if (mx)
-            hipLaunchKernelGGL((k_gate_up<kFmtMX, true>), g, b, 0, stream, J, h_q, h_s, partials, nmain, side, stage,
-                               J2, hq2, hs2, n2);
-        else
-            hipLaunchKernelGGL((k_gate_up<kFmtNV, true>), g, b, 0, stream, J, h_q, h_s, partials, nmain, side, stage,
-                               J2, hq2, hs2, n2);
-        return hipGetLastError();
+            return launch_gu<kFmtNV4, true>(gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2, hq2, hs2, n2);
+        if (mx)
+            return launch_gu<kFmtMX, true>(gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2, hq2, hs2, n2);
+        return launch_gu<kFmtNV, true>(gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2, hq2, hs2, n2);
     }
-    if (mx)
-        hipLaunchKernelGGL((k_gate_up<kFmtMX, false>), g, b, 0, stream, J, h_q, h_s, partials, nmain, side, stage, J2,
-                           hq2, hs2, n2);
-    else
-        hipLaunchKernelGGL((k_gate_up<kFmtNV, false>), g, b, 0, stream, J, h_q, h_s, partials, nmain, side, stage, J2,
-                           hq2, hs2, n2);
-    hipError_t e = hipGetLastError();
+    hipError_t e = mx ? launch_gu<kFmtMX, false>(gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2, hq2,
+                                                 hs2, n2)
+                      : launch_gu<kFmtNV, false>(gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2, hq2,
+                                                 hs2, n2);
     if (e != hipSuccess) return e;
     const int threads = rows * (job.N_out / 32) * 8;
     hipLaunchKernelGGL(k_swiglu_quant, dim3((threads + kThreads - 1) / kThreads), dim3(kThreads), 0, stream,
