@@ -880,9 +880,9 @@ __device__ __forceinline__ uint32_t mx_quant4_group8(const float hv[4], uint8_t&
 // (already multiplied by the NVFP4 row factor).
 
 // 16-row weight blocks per wave in gate_up: two (four: decode 269 -> 296
-// us), or one for NVFP4 weights when a two-block grid would not reach one
-// workgroup per CU (verify: 26.0 -> 24.8 us alone; MXFP4 decode with one:
-// 269 -> 347 us).  Output columns per workgroup: 32 * blocks.
+// us), or one when a two-block grid would not reach one workgroup per CU
+// (verify: 26.0 -> 24.8 us alone, tiny 9.1 -> 7.7; decode, whose grid is far
+// larger, with one: 269 -> 347 us).  Output columns per workgroup: 32 * blocks.
 constexpr int kGateMB = 2, kGateMBSmall = 1;
 
 // Workgroups [0, n2) take items of a second job J2 of the same format (the
@@ -1343,8 +1343,7 @@ struct GatePlan {
 
 // Weight blocks per wave of a gate_up launch (see kGateMB).
 int gate_mb(const ExpertJob& j) {
-    const bool nv = j.w.fmt == MOE_FMT_NVFP4;
-    return nv && (long)grid_slots(j) * (j.N_out / (32 * kGateMB)) <= 256 ? kGateMBSmall : kGateMB;
+    return (long)grid_slots(j) * (j.N_out / (32 * kGateMB)) <= 256 ? kGateMBSmall : kGateMB;
 }
 
 GatePlan gate_plan(const ExpertJob& j, int gmb) {
@@ -1413,18 +1412,15 @@ size_t gate_up_fp4_partials_bytes(const ExpertJob& job) {
     return align_up((size_t)p.splits * out_rows_of(job) * 2 * job.N_out * sizeof(float));
 }
 
-// One gate_up launch with the kernel of gmb weight blocks per wave (MXFP4
-// always takes kGateMB).
+// One gate_up launch with the kernel of gmb weight blocks per wave.
 template <int F, bool FU>
 hipError_t launch_gu(int gmb, dim3 g, hipStream_t stream, const StreamJob& J, uint8_t* h_q, uint8_t* h_s,
                      float* partials, int nmain, const Bf16Side& side, int stage, const StreamJob& J2, uint8_t* hq2,
                      uint8_t* hs2, int n2) {
-    if constexpr (F != kFmtMX) {
-        if (gmb == kGateMBSmall) {
-            hipLaunchKernelGGL((k_gate_up<F, FU, kGateMBSmall>), g, dim3(kThreads), 0, stream, J, h_q, h_s, partials,
-                               nmain, side, stage, J2, hq2, hs2, n2);
-            return hipGetLastError();
-        }
+    if (gmb == kGateMBSmall) {
+        hipLaunchKernelGGL((k_gate_up<F, FU, kGateMBSmall>), g, dim3(kThreads), 0, stream, J, h_q, h_s, partials,
+                           nmain, side, stage, J2, hq2, hs2, n2);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL((k_gate_up<F, FU, kGateMB>), g, dim3(kThreads), 0, stream, J, h_q, h_s, partials, nmain, side,
                        stage, J2, hq2, hs2, n2);
