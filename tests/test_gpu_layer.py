@@ -76,6 +76,8 @@ EDGE = [
     dict(M=70, H=256, E=3, k=2, I=128, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=256),  # >64 rows per expert
     dict(M=9, H=512, E=64, k=6, I=384, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=128, routed_scale=2.5),
     dict(M=130, H=128, E=2, k=1, I=128, bias="zipf:2.0"),               # one expert takes ~all rows
+    # an MXFP4 shared expert of five 32-row passes riding along both routed launches (I > 512)
+    dict(M=130, H=256, E=8, k=2, I=640, sfmt=synth.MXFP4, I_sh=640),
     # the clamped SwiGLU in routed and shared experts (few pairs, many pairs; MX, NV and bf16 shared)
     dict(M=9, H=512, E=64, k=6, I=384, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=256, swiglu_limit=0.4),
     dict(M=48, H=1024, E=32, k=8, I=256, wfmt=synth.MXFP4, sfmt=synth.MXFP4, I_sh=256, swiglu_limit=0.5),
