@@ -105,15 +105,20 @@ def test_layer_parity_edge(case):
     assert c["res_rel_l2"] <= REL_L2_MAX
 
 
-def _small_layer(seed=3):
-    sh = synth.custom_shape(M=24, H=512, E=12, k=3, I=256, wfmt=synth.MXFP4, sfmt=synth.MXFP4,
-                            I_sh=128, bias="zipf:1.2")
+def _small_layer(seed=3, a4=False):
+    if a4:  # NVFP4 experts on NVFP4 activations, NVFP4 shared expert
+        sh = synth.custom_shape(M=24, H=512, E=12, k=3, I=256, wfmt=synth.NVFP4, sfmt=synth.NVFP4,
+                                I_sh=128, bias="zipf:1.2", act_fmt=synth.ACT_NVFP4)
+    else:
+        sh = synth.custom_shape(M=24, H=512, E=12, k=3, I=256, wfmt=synth.MXFP4, sfmt=synth.MXFP4,
+                                I_sh=128, bias="zipf:1.2")
     inp = synth.make_inputs(sh, seed=seed, pool_rows=2048)
     return inp, staging.to_device(inp, DEV)
 
 
-def test_repeated_launches_bitwise_identical():
-    inp, d = _small_layer()
+@pytest.mark.parametrize("a4", [False, True])
+def test_repeated_launches_bitwise_identical(a4):
+    inp, d = _small_layer(a4=a4)
     first = LayerRun(d)
     ref = first.host()
     for i in range(400):
@@ -142,8 +147,9 @@ def test_row_permutation_invariance():
         assert np.array_equal(run["ids"], base["ids"][perm])
 
 
-def test_graph_replay_equals_eager():
-    inp, d = _small_layer(seed=5)
+@pytest.mark.parametrize("a4", [False, True])
+def test_graph_replay_equals_eager(a4):
+    inp, d = _small_layer(seed=5, a4=a4)
     run = LayerRun(d)
     eager = run.host()
     s = torch.cuda.Stream()
