@@ -26,7 +26,7 @@
  *     exception crosses the ABI.  moe_status_str() describes a code.
  *   - Limits (MOE_ERR_UNSUPPORTED otherwise): H % 128 == 0, I % 128 == 0,
  *     1 <= k <= min(E, 32), 1 <= E <= 1024, 1 <= M <= 4096, H <= 16384,
- *     I <= 8192, and a format pair this build implements.
+ *     I <= 8192, and a format pair the library implements.
  *
  * Number formats (the pages name them; their definitions are those of the
  * OCP Microscaling Formats v1.0 specification): E2M1 elements; MXFP4 = E2M1
