@@ -16,26 +16,60 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
 constexpr int kBucketThreads = 256;
 
-// Exclusive scan over kMaxE entries held 4 per thread (256 threads).
-__device__ inline void block_exclusive_scan(int* data, int* scratch, int& total) {
-    const int tid = threadIdx.x;
-    int v0 = data[4 * tid], v1 = data[4 * tid + 1], v2 = data[4 * tid + 2], v3 = data[4 * tid + 3];
-    int sum = v0 + v1 + v2 + v3;
-    scratch[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < kBucketThreads; off <<= 1) {
-        int add = tid >= off ? scratch[tid - off] : 0;
-        __syncthreads();
-        scratch[tid] += add;
-        __syncthreads();
+// Exclusive scans of three arrays of kMaxE entries at once (4 per thread of
+// 256): each wave scans its lanes' sums with shuffles, and the four wave
+// totals (in scratch, 12 ints) give each wave's base.  Two barriers.
+__device__ inline void block_exclusive_scan3(int* a, int* b, int* c, int* scratch, int& ta, int& tb, int& tc) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int va[4], vb[4], vc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        va[i] = a[4 * tid + i];
+        vb[i] = b[4 * tid + i];
+        vc[i] = c[4 * tid + i];
     }
-    const int incl = scratch[tid];
-    total = scratch[kBucketThreads - 1];
-    int base = incl - sum;
-    data[4 * tid] = base;
-    data[4 * tid + 1] = base + v0;
-    data[4 * tid + 2] = base + v0 + v1;
-    data[4 * tid + 3] = base + v0 + v1 + v2;
+    const int sa = va[0] + va[1] + va[2] + va[3], sb = vb[0] + vb[1] + vb[2] + vb[3],
+              sc = vc[0] + vc[1] + vc[2] + vc[3];
+    int ia = sa, ib = sb, ic = sc;  // inclusive scans over the wave's lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int xa = __shfl_up(ia, off, 64), xb = __shfl_up(ib, off, 64), xc = __shfl_up(ic, off, 64);
+        if (lane >= off) {
+            ia += xa;
+            ib += xb;
+            ic += xc;
+        }
+    }
+    if (lane == 63) {
+        scratch[3 * w] = ia;
+        scratch[3 * w + 1] = ib;
+        scratch[3 * w + 2] = ic;
+    }
+    __syncthreads();
+    int ba = 0, bb = 0, bc = 0;
+    ta = tb = tc = 0;
+#pragma unroll
+    for (int v = 0; v < kBucketThreads / 64; ++v) {
+        const int wa = scratch[3 * v], wb = scratch[3 * v + 1], wc = scratch[3 * v + 2];
+        if (v < w) {
+            ba += wa;
+            bb += wb;
+            bc += wc;
+        }
+        ta += wa;
+        tb += wb;
+        tc += wc;
+    }
+    int ea = ba + ia - sa, eb = bb + ib - sb, ec = bc + ic - sc;  // exclusive bases of the thread's entries
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[4 * tid + i] = ea;
+        b[4 * tid + i] = eb;
+        c[4 * tid + i] = ec;
+        ea += va[i];
+        eb += vb[i];
+        ec += vc[i];
+    }
     __syncthreads();
 }
 
@@ -71,7 +105,22 @@ __device__ inline void bucket_step(int M, int E, int k, const moe_routing& route
         s_run[e] = 0;
     }
     __syncthreads();
-    for (int p = tid; p < P; p += kBucketThreads) atomicAdd(&s_cnt[route.topk_ids[p]], 1);
+    // Pairs in placement chunks of R rows (R * k <= 256 pairs: pair r0 * k +
+    // tid).  The expert ids of a thread's first kIdRegs chunks stay in
+    // registers for the placement below.
+    const int R = bucket_chunk_rows(k);
+    const int W = bucket_words(k);
+    constexpr int kIdRegs = 16;
+    int idr[kIdRegs];
+#pragma unroll
+    for (int ci = 0; ci < kIdRegs; ++ci) {
+        const int p = ci * R * k + tid;
+        idr[ci] = tid < R * k && p < P ? route.topk_ids[p] : -1;
+    }
+#pragma unroll
+    for (int ci = 0; ci < kIdRegs; ++ci)
+        if (idr[ci] >= 0) atomicAdd(&s_cnt[idr[ci]], 1);
+    for (int p = kIdRegs * R * k + tid; p < P; p += kBucketThreads) atomicAdd(&s_cnt[route.topk_ids[p]], 1);
     __syncthreads();
     for (int e = tid; e < kMaxE; e += kBucketThreads) {
         const int c = s_cnt[e];
@@ -81,9 +130,7 @@ __device__ inline void bucket_step(int M, int E, int k, const moe_routing& route
     }
     __syncthreads();
     int tot_pairs, tot_tiles, tot_act;
-    block_exclusive_scan(s_off, s_scan, tot_pairs);
-    block_exclusive_scan(s_tile, s_scan, tot_tiles);
-    block_exclusive_scan(s_act, s_scan, tot_act);
+    block_exclusive_scan3(s_off, s_tile, s_act, s_scan, tot_pairs, tot_tiles, tot_act);
     for (int e = tid; e < E; e += kBucketThreads) {
         const int c = s_cnt[e];
         route.expert_offsets[e] = s_off[e];
@@ -107,16 +154,17 @@ __device__ inline void bucket_step(int M, int E, int k, const moe_routing& route
     // Stable placement: chunks of R rows; a bitmap per expert marks the chunk's
     // rows that chose it, and a pair's rank within its expert is the number of
     // earlier rows (previous chunks + lower bits of this chunk's bitmap).
-    const int R = bucket_chunk_rows(k);
-    const int W = bucket_words(k);
-    for (int r0 = 0; r0 < M; r0 += R) {
+    for (int r0 = 0, ci = 0; r0 < M; r0 += R, ++ci) {
         for (int w = tid; w < E * W; w += kBucketThreads) s_bm[w] = 0u;
         __syncthreads();
         const int p = r0 * k + tid;
         const bool valid = tid < R * k && p < P;
         int e = 0, rl = 0;
         if (valid) {
-            e = route.topk_ids[p];
+            int ev = 0;
+#pragma unroll
+            for (int cj = 0; cj < kIdRegs; ++cj) ev = cj == ci ? idr[cj] : ev;  // registers, no dynamic index
+            e = ci < kIdRegs ? ev : route.topk_ids[p];
             rl = p / k - r0;
             atomicOr(&s_bm[e * W + (rl >> 5)], 1u << (rl & 31));
         }
