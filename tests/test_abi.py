@@ -101,6 +101,9 @@ def test_layer_desc_validation(L):
         _desc(k=17),                                     # k > E
         _desc(E=1025),
         _desc(M=5000),
+        _desc(M=0),                                      # no rows
+        _desc(H=16384 + 128),                            # H above 16384
+        _desc(I=8192 + 128),                             # I above 8192
         _desc(w_router=None),
         _desc(gamma=None),
         _desc(w13=moe.moe_weights(moe.MOE_FMT_NVFP4, 0x1000, 0x1000, None)),  # NV without global

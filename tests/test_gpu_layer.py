@@ -69,6 +69,26 @@ def test_layer_parity_extra_workload(name):
     assert c["res_rel_l2"] <= REL_L2_MAX
 
 
+MAX_CASES = [
+    dict(M=3, H=16384, E=4, k=2, I=8192, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=256),  # largest H and I
+    dict(M=4096, H=256, E=4, k=1, I=128, sfmt=synth.MXFP4, I_sh=128),                   # largest M
+]
+
+
+@pytest.mark.parametrize("case", range(len(MAX_CASES)))
+def test_layer_parity_max_sizes(case):
+    sh = synth.custom_shape(**MAX_CASES[case])
+    inp = synth.make_inputs(sh, seed=300 + case, pool_rows=2048)
+    print(f"[layer max] {sh.name}", flush=True)
+    d = staging.to_device(inp, DEV)
+    run = LayerRun(d)
+    c = compare_layer(inp, run, sample_rows(sh.M, 8, seed=case))
+    print(f"  rel_l2={c['rel_l2']:.3e} max_abs={c['max_abs']:.3e}", flush=True)
+    assert c["ids_ok"]
+    assert c["rel_l2"] <= REL_L2_MAX and c["max_abs"] <= MAX_ABS_MAX
+    assert c["res_rel_l2"] <= REL_L2_MAX
+
+
 EDGE = [
     dict(M=1, H=128, E=1, k=1, I=128),                                  # smallest layer
     dict(M=5, H=256, E=4, k=4, I=128, bias="normal:0.05"),               # top-k = all experts
