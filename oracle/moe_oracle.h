@@ -11,14 +11,18 @@
  *   - number formats decoded through 16/256/256-entry tables built from the
  *     formats' closed-form definitions;
  *   - every sum in fp64;
- *   - every quantization point of the layer mirrored (activation MXFP8,
- *     SwiGLU-output MXFP8 requant, bf16 residual, bf16 output).
+ *   - every quantization point of the layer mirrored (activation MXFP8 or,
+ *     for NVFP4 experts on NVFP4 activations, NVFP4 with its static globals
+ *     and every code decision in fp32; the SwiGLU-output requant in the same
+ *     format; bf16 residual, bf16 output);
+ *   - the SwiGLU optionally clamped (orc_swiglu).
  *
  * Every function that cannot be pinned against something other than itself
  * says "parity unpinned" here; at present every exported function has a pin
- * in the CPU test suite (format tables exhaustively, encoders by brute force,
- * routing by full sort, expert GEMMs by dense mixtures and textbook cases,
- * finalize by closed forms).
+ * in the CPU test suite (format tables exhaustively, encoders by brute force
+ * or an independent fp32 derivation, routing by full sort, expert GEMMs by
+ * dense mixtures and textbook cases, the clamp by closed forms, finalize by
+ * closed forms).
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
