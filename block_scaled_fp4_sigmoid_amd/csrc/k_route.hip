@@ -130,27 +130,29 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
             const v8bf A1 = __builtin_bit_cast(v8bf, v4i{(int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]});
             const v8bf A2 = __builtin_bit_cast(v8bf, v4i{(int)p2[0], (int)p2[1], (int)p2[2], (int)p2[3]});
             const v8bf A3 = __builtin_bit_cast(v8bf, v4i{(int)p3[0], (int)p3[1], (int)p3[2], (int)p3[3]});
+            // every block runs its MFMAs (blocks past the rows multiply the
+            // zeros loaded for them): no branch between an MFMA and the reads
+            // of its accumulator
 #pragma unroll
             for (int j = 0; j < NBT; ++j) {
-                if (j < nb) {
-                    const v8bf b = __builtin_bit_cast(v8bf, xb[u][j]);
-                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, acc[j], 0, 0, 0);
-                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, b, acc[j], 0, 0, 0);
-                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3, b, acc[j], 0, 0, 0);
-                }
+                const v8bf b = __builtin_bit_cast(v8bf, xb[u][j]);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, b, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3, b, acc[j], 0, 0, 0);
             }
         }
     }
-    // lane holds D[4g + t][i]: expert te*16 + 4g + t, row r0 + 16j + i
+    // lane holds D[4g + t][i]: expert te*16 + 4g + t, row r0 + 16j + i; stores
+    // of rows past M or experts past E go to an offset past the buffer (dropped)
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(partials, (uint32_t)splits * (uint32_t)M * (uint32_t)E * 4u);
 #pragma unroll
     for (int j = 0; j < NBT; ++j) {
         const int r = r0 + j * 16 + i;
-        if (j < nb && r < M) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int ee = te * 16 + 4 * g + t;
-                if (ee < E) partials[((size_t)kc * M + r) * E + ee] = acc[j][t];
-            }
+        for (int t = 0; t < 4; ++t) {
+            const int ee = te * 16 + 4 * g + t;
+            const uint32_t off = (j < nb && r < M && ee < E) ? (((uint32_t)kc * M + r) * E + ee) * 4u : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][t]), rp, off, 0, 0);
         }
     }
 }

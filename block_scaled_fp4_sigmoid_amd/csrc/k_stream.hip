@@ -64,7 +64,6 @@ template <int F>
 constexpr bool kA4 = F == kFmtNV4;  // NVFP4 activations
 constexpr int kThreads = 256;
 constexpr int kPassRows = 32;           // activation rows per pass (two 16-row N-blocks)
-constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every record count
 
 #ifndef MOE_STREAM_TARGET_ITEMS
 #define MOE_STREAM_TARGET_ITEMS 256  // gate_up splits K until about this many items
@@ -213,10 +212,6 @@ __device__ __forceinline__ bool resolve_ids(const StreamJob& J, int slot, Tokens
 
 __device__ __forceinline__ bool resolve_item(const StreamJob& J, int slot, Tokens& t, int* list, int* tok) {
     return (J.ids && !J.dense) ? resolve_ids(J, slot, t, list, tok) : resolve(J, slot, t);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
 // ---- NVFP4 helpers ----------------------------------------------------------

@@ -25,6 +25,15 @@ constexpr int kMaxK = 32;
 constexpr int kMaxH = 16384;
 constexpr int kMaxI = 8192;
 
+// Routed calls address the per-pair buffers (y [M*k, H] fp32, bucket-order
+// activations) with 32-bit buffer offsets; the byte size of y must stay below
+// the out-of-range offset the kernels use for masked lanes (2^31).
+constexpr int64_t kMaxPairBytes = (int64_t{1} << 31) - (int64_t{1} << 20);
+
+int check_pair_bytes(int M, int k, int H) {
+    return (int64_t)M * k * H * 4 > kMaxPairBytes ? MOE_ERR_UNSUPPORTED : MOE_OK;
+}
+
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
 int check_dims(int M, int H, int E, int k) {
@@ -244,8 +253,10 @@ int moe_expert_gate_up(const moe_weights* w13, const uint8_t* a_q, const uint8_t
     }
     if (int st = check_fp4_weights(w13)) return st;
     if (!a_q || !a_s || !h_q || !h_s) return MOE_ERR_INVALID_ARG;
-    if (!dense)
+    if (!dense) {
         if (int st = check_routing(route)) return st;
+        if (int st = check_pair_bytes(M, k, H)) return st;
+    }
     ExpertJob job = dense ? dense_job(*w13, I, H, M) : routed_job(*w13, I, H, *route, M, E, k);
     job.swiglu_limit = swiglu_limit;
     const size_t need = gate_up_fp4_partials_bytes(job);
@@ -267,8 +278,10 @@ int moe_expert_down(const moe_weights* w2, const uint8_t* h_q, const uint8_t* h_
     }
     if (int st = check_fp4_weights(w2)) return st;
     if (!h_q || !h_s) return MOE_ERR_INVALID_ARG;
-    if (!dense)
+    if (!dense) {
         if (int st = check_routing(route)) return st;
+        if (int st = check_pair_bytes(M, k, H)) return st;
+    }
     const ExpertJob job = dense ? dense_job(*w2, H, I, M) : routed_job(*w2, H, I, *route, M, E, k);
     return hip_status(launch_down_fp4(job, h_q, h_s, y, stream));
 }
@@ -284,8 +297,10 @@ int moe_expert_gate_up_nvfp4a(const moe_weights* w13, const uint8_t* a_q, const 
     if (I < 128 || I % 128 != 0 || I > kMaxI) return MOE_ERR_UNSUPPORTED;
     if (w13->fmt != MOE_FMT_NVFP4) return MOE_ERR_UNSUPPORTED;
     if (int st = check_fp4_weights(w13)) return st;
-    if (!dense)
+    if (!dense) {
         if (int st = check_routing(route)) return st;
+        if (int st = check_pair_bytes(M, k, H)) return st;
+    }
     ExpertJob job = dense ? dense_job(*w13, I, H, M) : routed_job(*w13, I, H, *route, M, E, k);
     job.swiglu_limit = swiglu_limit;
     job.a_nvfp4 = true;
@@ -302,8 +317,10 @@ int moe_expert_down_nvfp4a(const moe_weights* w2, const uint8_t* h_q, const uint
     if (I < 128 || I % 128 != 0 || I > kMaxI) return MOE_ERR_UNSUPPORTED;
     if (w2->fmt != MOE_FMT_NVFP4) return MOE_ERR_UNSUPPORTED;
     if (int st = check_fp4_weights(w2)) return st;
-    if (!dense)
+    if (!dense) {
         if (int st = check_routing(route)) return st;
+        if (int st = check_pair_bytes(M, k, H)) return st;
+    }
     ExpertJob job = dense ? dense_job(*w2, H, I, M) : routed_job(*w2, H, I, *route, M, E, k);
     job.a_nvfp4 = true;
     job.a_globals = h_globals;
@@ -352,6 +369,7 @@ void set_a4(ExpertJob& j, const moe_layer_desc* d, bool shared, bool gate_up) {
 int check_desc(const moe_layer_desc* d) {
     if (!d) return MOE_ERR_INVALID_ARG;
     if (int st = check_dims(d->M, d->H, d->E, d->k)) return st;
+    if (int st = check_pair_bytes(d->M, d->k, d->H)) return st;
     if (d->I < 128 || d->I % 128 != 0 || d->I > kMaxI) return MOE_ERR_UNSUPPORTED;
     if (!d->w_router || !d->gamma) return MOE_ERR_INVALID_ARG;
     if (!(d->eps >= 0.0f)) return MOE_ERR_INVALID_ARG;

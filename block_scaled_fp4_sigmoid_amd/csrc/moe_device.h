@@ -73,6 +73,15 @@ __device__ __forceinline__ T load_agent(const T* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Raw buffer resource over [p, p + bytes): loads at offsets at or past `bytes`
+// return zeros and stores there are dropped, without a memory access.  Every
+// buffer the kernels address this way holds fewer than 2^31 bytes (the C ABI
+// refuses larger shapes), so kOOB is past every record count.
+constexpr uint32_t kOOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ v4i load16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
 __device__ __forceinline__ v4i load16_nt(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));

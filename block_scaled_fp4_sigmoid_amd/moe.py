@@ -145,6 +145,17 @@ def workspace(nbytes: int, device) -> torch.Tensor:
     return t
 
 
+def _call_workspace(nbytes: int, device, stream) -> torch.Tensor:
+    """A workspace for one call that the binding drops at return: allocated
+    from torch's caching allocator and marked as used by the call's stream, so
+    the block is not handed to another allocation before the kernels on that
+    stream are done with it."""
+    t = workspace(nbytes, device)
+    if stream is not None:
+        t.record_stream(stream)
+    return t
+
+
 @dataclass
 class Weights:
     """One projection of E experts in the canonical layout (see moe.h)."""
@@ -212,7 +223,7 @@ def route_topk(routing: Routing, x=None, logits_in=None, w_router=None, bias=Non
     dev = (x if x is not None else logits_in).device
     need = lib().moe_route_workspace_bytes(M, H, E, k)
     if ws is None:
-        ws = workspace(need, dev)
+        ws = _call_workspace(need, dev, stream)
     r = routing.c()
     rc = lib().moe_route_topk(_p(x), _p(logits_in), _p(w_router), _p(bias), M, H, E, k,
                               float(routed_scale), _p(logits_out), C.byref(r), _p(ws), ws.numel(),
@@ -248,7 +259,7 @@ def expert_gate_up(w13: Weights, M, H, I, E, k, routing: Optional[Routing] = Non
     dev = (a_q if a_q is not None else a_bf16).device
     need = lib().moe_gate_up_workspace_bytes(w13.fmt, M, H, I, E, k, int(dense))
     if ws is None and need:
-        ws = workspace(need, dev)
+        ws = _call_workspace(need, dev, stream)
     wc = w13.c()
     r = None if dense else routing.c()
     rc = lib().moe_expert_gate_up(C.byref(wc), _p(a_q), _p(a_s), _p(a_bf16),

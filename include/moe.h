@@ -26,7 +26,10 @@
  *     exception crosses the ABI.  moe_status_str() describes a code.
  *   - Limits (MOE_ERR_UNSUPPORTED otherwise): H % 128 == 0, I % 128 == 0,
  *     1 <= k <= min(E, 32), 1 <= E <= 1024, 1 <= M <= 4096, H <= 16384,
- *     I <= 8192, and a format pair the library implements.
+ *     I <= 8192, and a format pair the library implements; for routed expert
+ *     GEMMs and the layer also M*k*H*4 <= 2^31 - 2^20 (the fp32 output of
+ *     every (row, slot) pair stays under 2 GiB: the kernels address it with
+ *     32-bit buffer offsets).
  *
  * Number formats (the pages name them; their definitions are those of the
  * OCP Microscaling Formats v1.0 specification): E2M1 elements; MXFP4 = E2M1
@@ -241,8 +244,11 @@ int moe_quant_act_nvfp4(const uint16_t *x, int M, int K, float global, const moe
  *   GEMMs over 8-row tiles); sgl-nvidia-mega PR #33 appended table, row
  *   "shared act quant" (SiLU-and-mul fused with the down input's quant);
  *   SGLang Spark GB10 Optimizations, section 1 (NVFP4 K-groups of 16).
- * g = A W13[:I]^T, u = A W13[I:]^T with exact products and fp32 sums; h =
- * silu(g) * u in fp32.  swiglu_limit > 0 selects the clamped SwiGLU (README
+ * g = A W13[:I]^T, u = A W13[I:]^T with exact products summed in fp32,
+ * except that MXFP4 weights run on the scaled FP4 x FP8 matrix instruction,
+ * which adds the products of each 128-long K step with a reduced internal
+ * precision (measured: about 2^-13 of that step's sum of |products|) before
+ * the fp32 accumulation; h = silu(g) * u in fp32.  swiglu_limit > 0 selects the clamped SwiGLU (README
  * DeepSeek-V4.1 slot table, row "Shared expert gate_up (shared_ll)"): g is
  * capped from above at the limit and u clamped to [-limit, limit] before the
  * product; 0 is the plain SwiGLU; negative or NaN is MOE_ERR_INVALID_ARG.
@@ -269,7 +275,9 @@ int moe_expert_gate_up(const moe_weights *w13, const uint8_t *a_q, const uint8_t
  *   second block-scaled GEMM); README Qwen3.5 slot table, row "mkm" (FC2).
  * h is what moe_expert_gate_up wrote (MXFP8 h_q/h_s for FP4 weights, h_bf16
  * for BF16).  y: fp32 [M*k, H] indexed by pair id (route != NULL) or fp32
- * [M, H] by row (dense).  Exact products, fp32 sums. */
+ * [M, H] by row (dense).  Exact products summed in fp32; MXFP4 weights with
+ * the reduced-precision sum of each 128-long K step described at
+ * moe_expert_gate_up. */
 int moe_expert_down(const moe_weights *w2, const uint8_t *h_q, const uint8_t *h_s,
                     const uint16_t *h_bf16, const moe_routing *route, int M, int H, int I,
                     int E, int k, float *y, hipStream_t stream);

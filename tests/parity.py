@@ -13,6 +13,9 @@ DEV = "cuda"
 # Acceptance bars for the layer outputs against the oracle's fp64 values.
 REL_L2_MAX = 5e-3
 MAX_ABS_MAX = 3e-2
+# Router logits (fp32 products of bf16 x and fp32 weights, fp32 sums) against
+# the oracle's fp64 logits.
+LOGITS_ABS_MAX = 1e-5
 
 
 def bf16_to_f64(a) -> np.ndarray:
@@ -71,9 +74,13 @@ def sample_rows(M: int, n: int, seed: int = 0) -> np.ndarray:
 
 
 def compare_layer(inp, run: LayerRun, rows):
-    """Layer parity on sampled rows: ids bit-exact (oracle routed from the GPU
+    """Layer parity on sampled rows: the fused router launch's logits against
+    the oracle's fp64 logits, ids bit-exact (oracle routed from the GPU
     logits), out / residual_out within the bars."""
     h = run.host()
+    rows = np.asarray(rows)
+    ref_logits = orc.router_logits(np.ascontiguousarray(inp.x[rows]), inp.Wr)
+    logits_err = float(np.max(np.abs(h["logits"][rows].astype(np.float64) - ref_logits)))
     ref = oracle_rows(inp, rows, h["logits"])
     ids_ok = np.array_equal(h["ids"][rows], ref["ids"])
     w_rel = float(np.max(np.abs(h["w"][rows] - ref["w"]) / np.abs(ref["w"])))
@@ -84,4 +91,5 @@ def compare_layer(inp, run: LayerRun, rows):
     res_ref = bf16_to_f64(ref["resid_out"])
     res_l2 = rel_l2(res_got, res_ref)
     return dict(ids_ok=ids_ok, w_rel=w_rel, rel_l2=r_l2, max_abs=mabs, res_rel_l2=res_l2,
-                ids_gpu=h["ids"][rows], ids_ref=ref["ids"])
+                ids_gpu=h["ids"][rows], ids_ref=ref["ids"], logits_err=logits_err,
+                logits_ok=logits_err <= LOGITS_ABS_MAX)

@@ -211,3 +211,30 @@ def test_calls_refuse_before_enqueueing(L):
                                     None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_finalize_rmsnorm(0x1000, 0x1000, None, 0x1000, 0x1000, -1.0, 4, 128, 2, 0x1000,
                                   None, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_pair_output_size_limit(L):
+    """Routed calls whose fp32 per-pair output y [M*k, H] would reach 2 GiB are
+    refused (the kernels address it with 32-bit buffer offsets); the largest
+    accepted shapes sit just under the limit."""
+    limit = (1 << 31) - (1 << 20)
+    # M=4096, k=9, H=16384: 2.25 GiB of y -> refused; k=7 (1.75 GiB) accepted
+    assert 4096 * 9 * 16384 * 4 > limit and 4096 * 7 * 16384 * 4 <= limit
+    assert L.moe_layer_workspace_bytes(C.byref(_desc(M=4096, E=32, k=9, H=16384))) == 0
+    assert L.moe_layer_workspace_bytes(C.byref(_desc(M=4096, E=32, k=16, H=16384))) == 0
+    assert L.moe_layer_workspace_bytes(C.byref(_desc(M=4096, E=32, k=7, H=16384))) > 0
+    d = _desc(M=4096, E=32, k=9, H=16384)
+    rc = L.moe_layer(C.byref(d), 0x1000, 0x1000, 0x1000, None, None, None, None, 0x1000, 1 << 40, None)
+    assert rc == moe.MOE_ERR_UNSUPPORTED
+    r = moe.moe_routing(*([0x1000] * 11))
+    for fmt in (moe.MOE_FMT_MXFP4, moe.MOE_FMT_NVFP4):
+        w = moe.moe_weights(fmt, 0x1000, 0x1000, 0x1000)
+        assert L.moe_expert_down(C.byref(w), 0x1000, 0x1000, None, C.byref(r), 4096, 16384, 128, 32, 9,
+                                 0x1000, None) == moe.MOE_ERR_UNSUPPORTED
+        assert L.moe_expert_gate_up(C.byref(w), 0x1000, 0x1000, None, C.byref(r), 4096, 16384, 128, 32, 9,
+                                    0.0, 0x1000, 0x1000, None, 0x1000, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    nvw = moe.moe_weights(moe.MOE_FMT_NVFP4, 0x1000, 0x1000, 0x1000)
+    assert L.moe_expert_gate_up_nvfp4a(C.byref(nvw), 0x1000, 0x1000, 1.0, C.byref(r), 4096, 16384, 128, 32, 9,
+                                       0.0, 0x1000, 0x1000, 0x1000, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_down_nvfp4a(C.byref(nvw), 0x1000, 0x1000, 0x1000, C.byref(r), 4096, 16384, 128, 32, 9,
+                                    0x1000, None) == moe.MOE_ERR_UNSUPPORTED

@@ -84,6 +84,11 @@ ROUTE_CASES = [
     (5, 256, 7, 7, "normal:0.05", 1.0),  # k = E
     (100, 384, 3, 2, "none", 1.0),     # few experts, many rows per expert
     (37, 640, 1024, 32, "none", 1.0),  # largest E and k
+    (16, 7168, 384, 8, "none", 1.0),   # the decode workload's router
+    # the route step places rows in chunks of min(128, 256 / k) rows and keeps
+    # the first 16 chunks' expert ids in registers; these run past 16 chunks
+    (1024, 512, 64, 8, "zipf:1.0", 1.0),  # 32 chunks of 32 rows
+    (4096, 256, 4, 1, "none", 1.0),       # 32 chunks of 128 rows
 ]
 
 
