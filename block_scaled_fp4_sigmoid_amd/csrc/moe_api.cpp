@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "moe_internal.h"
@@ -130,6 +131,9 @@ const char* moe_status_str(int status) {
         case MOE_ERR_UNSUPPORTED: return "unsupported shape or format (see the limits in moe.h)";
         case MOE_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
         case MOE_ERR_HIP: return "a HIP launch failed";
+        case MOE_ERR_SCRATCH:
+            return "the layer needs more scratch than moe_layer_noalloc's static buffer holds "
+                   "(MOE_NOALLOC_SCRATCH_BYTES per device); use moe_layer with a workspace";
         default: return "unknown status";
     }
 }
@@ -595,3 +599,61 @@ int moe_layer(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residu
 }
 
 }  // extern "C"
+
+// ---- the layer without an allocation: a static scratch buffer per device ----
+
+static_assert(MOE_NOALLOC_SCRATCH_BYTES % 256 == 0, "the scratch is carved at 256-byte boundaries");
+
+// The scratch of moe_layer_noalloc.  In host code `scratch` names a host-side
+// stand-in, not device memory: the kernels get its device address, which
+// hipGetSymbolAddress resolves once per device (each device holds its own
+// copy of the array, at its own address, until the process ends).
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device; null until its first call
+
+// The scratch's device address on the current device, resolved on the first
+// call there (with that device current).
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return MOE_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return MOE_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_layer_noalloc(const moe_layer_desc* d, const uint16_t* x, const uint16_t* residual,
+                                 uint16_t* out, uint16_t* residual_out, float* logits_out,
+                                 int32_t* topk_ids_out, float* topk_w_out, hipStream_t stream) {
+    if (int st = check_desc(d)) return st;
+    if (!x || !residual || !out) return MOE_ERR_INVALID_ARG;
+    Carver c(nullptr);
+    carve_layer(c, d);
+    if (c.off > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (int st = scratch_address(&ws)) return st;
+    // every scratch region is written before it is read within the call (the
+    // workspace of moe_layer needs no initialization), so the previous call's
+    // contents are never seen
+    return moe_layer_mxfp8_out(d, x, residual, out, residual_out, nullptr, nullptr, logits_out, topk_ids_out,
+                               topk_w_out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
+}

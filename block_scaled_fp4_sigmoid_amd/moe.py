@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355.so")
 
 MOE_FMT_NONE, MOE_FMT_MXFP4, MOE_FMT_NVFP4, MOE_FMT_BF16 = 0, 1, 2, 3
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
+MOE_ERR_SCRATCH = 5
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTS = ["moe_status_str", "moe_abi_version", "moe_tile_capacity", "moe_packed_scale_bytes",
            "moe_pack_fp4", "moe_route_workspace_bytes",
@@ -26,7 +28,7 @@ EXPORTS = ["moe_status_str", "moe_abi_version", "moe_tile_capacity", "moe_packed
            "moe_expert_gate_up", "moe_expert_down", "moe_expert_gate_up_nvfp4a",
            "moe_expert_down_nvfp4a", "moe_finalize_rmsnorm",
            "moe_finalize_rmsnorm_mxfp8", "moe_layer_workspace_bytes", "moe_layer",
-           "moe_layer_mxfp8_out"]
+           "moe_layer_mxfp8_out", "moe_layer_noalloc"]
 
 
 class moe_weights(C.Structure):
@@ -104,6 +106,8 @@ def lib() -> C.CDLL:
         L.moe_layer_mxfp8_out.restype = i
         L.moe_layer_mxfp8_out.argtypes = [C.POINTER(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                           sz, vp]
+        L.moe_layer_noalloc.restype = i
+        L.moe_layer_noalloc.argtypes = [C.POINTER(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -356,3 +360,12 @@ class Layer:
                                        _p(out_q), _p(out_s), _p(logits_out), _p(topk_ids_out),
                                        _p(topk_w_out), _p(self.ws), self.ws.numel(), _stream(stream))
         _check(rc, "moe_layer_mxfp8_out")
+
+
+def layer_noalloc(layer: "Layer", x, residual, out, residual_out=None, logits_out=None, topk_ids_out=None,
+                  topk_w_out=None, stream=None):
+    """moe_layer_noalloc on the description of `layer` (its own workspace is
+    not used): the scratch is the library's static per-device buffer."""
+    rc = lib().moe_layer_noalloc(C.byref(layer.desc), _p(x), _p(residual), _p(out), _p(residual_out),
+                                 _p(logits_out), _p(topk_ids_out), _p(topk_w_out), _stream(stream))
+    _check(rc, "moe_layer_noalloc")

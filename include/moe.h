@@ -49,14 +49,15 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 
 enum moe_status {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shape */
     MOE_ERR_UNSUPPORTED = 2, /* outside the limits above or an unimplemented format */
     MOE_ERR_WORKSPACE = 3,   /* workspace null, too small or misaligned */
-    MOE_ERR_HIP = 4          /* a launch failed; the HIP error was cleared */
+    MOE_ERR_HIP = 4,         /* a launch failed; the HIP error was cleared */
+    MOE_ERR_SCRATCH = 5      /* moe_layer_noalloc: the layer needs more than its static scratch */
 };
 
 /* Weight formats. */
@@ -364,6 +365,27 @@ int moe_layer_mxfp8_out(const moe_layer_desc *desc, const uint16_t *x, const uin
                         uint16_t *out, uint16_t *residual_out, uint8_t *out_q, uint8_t *out_s,
                         float *logits_out, int32_t *topk_ids_out, float *topk_w_out, void *workspace,
                         size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_layer_noalloc — moe_layer without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).
+ * The scratch lives in a static device array of MOE_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) that the library holds on every device it runs on until the
+ * process ends.  The call allocates nothing and frees nothing; its first call
+ * on a device resolves the array's address there (so make it once outside
+ * capture), with that device current and `stream` belonging to it.
+ * Arguments and results as moe_layer.  A layer whose workspace
+ * (moe_layer_workspace_bytes) exceeds the array is refused with
+ * MOE_ERR_SCRATCH before anything is enqueued (every five-workload shape up
+ * to 48 rows fits; 384 rows at hidden 7168 and intermediate 2048 does not).
+ * Every call on a device shares that device's array, which keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that overlap
+ * in time on one device, on any streams, race and give wrong results. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_layer_noalloc(const moe_layer_desc *desc, const uint16_t *x, const uint16_t *residual,
+                      uint16_t *out, uint16_t *residual_out, float *logits_out, int32_t *topk_ids_out,
+                      float *topk_w_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -51,7 +51,7 @@ def test_probe_library_exports():
 
 
 def test_version_and_status_strings(L):
-    assert moe.abi_version() == 7
+    assert moe.abi_version() == 8
     for rc in range(5):
         assert len(moe.status_str(rc)) > 0
     assert "unknown" in moe.status_str(99)
@@ -238,3 +238,23 @@ def test_pair_output_size_limit(L):
                                        0.0, 0x1000, 0x1000, 0x1000, None) == moe.MOE_ERR_UNSUPPORTED
     assert L.moe_expert_down_nvfp4a(C.byref(nvw), 0x1000, 0x1000, 0x1000, C.byref(r), 4096, 16384, 128, 32, 9,
                                     0x1000, None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_noalloc_refusals(L):
+    """moe_layer_noalloc refuses, before any HIP call, an invalid description,
+    missing pointers, and a layer whose workspace exceeds its static scratch."""
+    assert L.moe_layer_noalloc(None, 0x1000, 0x1000, 0x1000, None, None, None, None, None) == moe.MOE_ERR_INVALID_ARG
+    d = _desc()
+    assert L.moe_layer_noalloc(C.byref(d), None, 0x1000, 0x1000, None, None, None, None, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_noalloc(C.byref(_desc(H=1000)), 0x1000, 0x1000, 0x1000, None, None, None, None,
+                               None) == moe.MOE_ERR_UNSUPPORTED
+    # the 384-row step at hidden 7168, intermediate 2048 needs about 107 MiB of workspace
+    wide = _desc(M=384, H=7168, E=256, k=8, I=2048)
+    assert L.moe_layer_workspace_bytes(C.byref(wide)) > moe.NOALLOC_SCRATCH_BYTES
+    assert L.moe_layer_noalloc(C.byref(wide), 0x1000, 0x1000, 0x1000, None, None, None, None,
+                               None) == moe.MOE_ERR_SCRATCH
+    assert b"static" in L.moe_status_str(moe.MOE_ERR_SCRATCH)
+    # a 16-row decode-sized layer fits
+    assert 0 < L.moe_layer_workspace_bytes(C.byref(_desc(M=16, H=7168, E=384, k=8, I=2048))) <= \
+        moe.NOALLOC_SCRATCH_BYTES
