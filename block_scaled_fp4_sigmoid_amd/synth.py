@@ -41,9 +41,10 @@ import numpy as np
 MXFP4 = 1
 NVFP4 = 2
 BF16 = 3
+FP8S = 4   # static per-tensor FP8: E4M3 weights, one fp32 weight scale, static input scales (shared expert)
 NONE = 0
 
-FMT_NAMES = {NONE: "none", MXFP4: "mxfp4", NVFP4: "nvfp4", BF16: "bf16"}
+FMT_NAMES = {NONE: "none", MXFP4: "mxfp4", NVFP4: "nvfp4", BF16: "bf16", FP8S: "fp8s"}
 # activation formats of the expert GEMMs
 ACT_MXFP8 = 0
 ACT_NVFP4 = 1
@@ -210,7 +211,8 @@ class Matrix:
 
     fmt MXFP4/NVFP4: ``packed`` [N, K/2] u8 (low nibble = even K), ``scales``
     [N, K/32] E8M0 (MX) or [N, K/16] E4M3 (NV), ``gscale`` fp32 (NV only).
-    fmt BF16: ``bf16`` [N, K] u16."""
+    fmt BF16: ``bf16`` [N, K] u16.
+    fmt FP8S: ``packed`` [N, K] E4M3 codes, ``gscale`` the fp32 weight scale."""
     fmt: int
     N: int
     K: int
@@ -263,6 +265,10 @@ class MoEInputs:
     x_gscale: float = 0.0
     h_gscale: Optional[np.ndarray] = None  # fp32 [E]
     sh_h_gscale: float = 0.0
+    # static-FP8 shared expert (sfmt FP8S): static input scales of its gate/up
+    # (the layer input) and of its down (h)
+    sh_in13: float = 0.0
+    sh_in2: float = 0.0
 
     @property
     def residual(self) -> np.ndarray:
@@ -300,10 +306,23 @@ def _pooled(rng, fmt, E, N, K, pool_rows, std=0.02) -> PooledExperts:
     return PooledExperts(fmt, E, N, K, packed, scales, idx, np.full(E, g, dtype=np.float32))
 
 
+def encode_fp8s(w: np.ndarray):
+    """Offline static-FP8 encoding of an fp32 matrix: one per-tensor scale
+    amax / 448 (fp32) and E4M3 elements nearest, saturating.
+    Returns (codes [N, K] u8, scale)."""
+    s = np.float32(max(float(np.abs(w).max()), 1e-30) / 448.0)
+    v = w.astype(np.float64) / np.float64(s)
+    codes = _nearest_code(np.abs(v), _E4M3_POS) | (np.signbit(v).astype(np.uint8) << 7)
+    return codes.astype(np.uint8), float(s)
+
+
 def _whole(rng, fmt, N, K, std=0.02) -> Matrix:
     w = (rng.standard_normal((N, K), dtype=np.float32) * np.float32(std))
     if fmt == BF16:
         return Matrix(BF16, N, K, bf16=_bf16_trunc(w))
+    if fmt == FP8S:
+        codes, sc = encode_fp8s(w)
+        return Matrix(FP8S, N, K, packed=codes, gscale=sc)
     g = nvfp4_global_for(w) if fmt == NVFP4 else np.float32(1.0)
     packed, scales = _encode(fmt, w, g)
     return Matrix(fmt, N, K, packed, scales, float(g))
@@ -326,9 +345,18 @@ def make_inputs(shape: Shape | str, seed: int = 1, pool_rows: int = POOL_ROWS) -
         sh13 = _whole(rng, shape.sfmt, 2 * shape.I_sh, H)
         sh2 = _whole(rng, shape.sfmt, H, shape.I_sh)
     inp = MoEInputs(shape, seed, x, Wr, bias, gamma, w13, w2, sh13, sh2)
+    if shape.sfmt == FP8S:
+        # Static input scales, as an FP8 checkpoint ships them (calibrated
+        # offline; no draw): the gate/up input's from this step's amax, the
+        # down input's from 16x the spread of h (gate and up each have a std
+        # of 0.02 sqrt(H) for N(0, 1) rows and N(0, 0.02) weights), so only
+        # rare outliers of h saturate.
+        xa = np.abs(bf16_to_f32(x)).max()
+        inp.sh_in13 = float(np.float32(xa) / np.float32(448))
+        inp.sh_in2 = float(np.float32(16.0 * (0.02 * np.sqrt(H)) ** 2) / np.float32(448))
     if shape.act_fmt == ACT_NVFP4:
         if shape.wfmt != NVFP4 or shape.sfmt == MXFP4:
-            raise ValueError("NVFP4 activations go with NVFP4 experts (shared: none, NVFP4 or bf16)")
+            raise ValueError("NVFP4 activations go with NVFP4 experts (shared: none, NVFP4, bf16 or FP8S)")
         # Static globals, as an NVFP4 checkpoint ships them (calibrated offline):
         # the input's from this step's own amax; each h's from the spread that
         # gate and up have for N(0, 1) rows and N(0, 0.02) weights (std

@@ -331,6 +331,11 @@ void orc_mat_row(const orc_mat *m, int K, int n, double *out)
             out[k] = orc_bf16_value(m->bf16[(size_t)n * K + k]);
         return;
     }
+    if (m->fmt == ORC_FP8S) {
+        for (int k = 0; k < K; ++k)
+            out[k] = T_E4M3[m->packed[(size_t)n * K + k]] * (double)m->gscale;
+        return;
+    }
     const uint8_t *row = m->packed + (size_t)n * (K / 2);
     for (int k = 0; k < K; ++k) {
         uint8_t byte = row[k / 2];
@@ -488,6 +493,73 @@ void orc_gate_up_bf16(const orc_mat *w13, int H, int I, const uint16_t *x_row, d
     for (int c = 0; c < H; ++c)
         a[c] = orc_bf16_value(x_row[c]);
     orc_gate_up(w13, H, I, a, limit, h);
+    free(a);
+}
+
+/* ---- the static-FP8 shared expert ----
+ * README Qwen3.5 slot table, row "route_shared (with route)": the shared
+ * expert's gate/up runs on static FP8; sgl-nvidia-mega PR #33, appended table,
+ * row "shared act quant": its SiLU-and-mul is fused with the static FP8
+ * quantization of the down projection's input, with the FP8 bytes and bf16
+ * outputs of the unfused path.  The pages define neither the format nor the
+ * rule.  Reading (the plainest FP8 linear with static per-tensor scales):
+ * weights are E4M3 codes with one fp32 scale per matrix (orc_mat_row);
+ * an input value v (bf16) is stored as the E4M3 code of the fp32 quotient
+ * v / s_in (one fp32 rounding, then round to nearest even, saturating at 448;
+ * NaN stays NaN); a linear's output is s_in * sum(code values * weights),
+ * rounded to bf16, its dtype; h = bf16(silu(g) * u) from those bf16 g, u;
+ * h is quantized with the down input's own static scale the same way. */
+uint8_t orc_fp8s_quant(float v, float s_in)
+{
+    const float q = v / s_in; /* the fp32 quotient decides the code */
+    return orc_e4m3_rne_sat((double)q);
+}
+
+/* gate/up of the static-FP8 shared expert on one bf16 row: h (bf16 bits, [I])
+ * and, when gu is not NULL, the bf16 outputs g (gu[0, I)) and u (gu[I, 2I)). */
+void orc_gate_up_fp8s(const orc_mat *w13, int H, int I, const uint16_t *x_row, float s_in, double limit,
+                      uint16_t *h, uint16_t *gu)
+{
+    tables();
+    double *a = (double *)malloc(sizeof(double) * H);
+    double *wrow = (double *)malloc(sizeof(double) * H);
+    for (int c = 0; c < H; ++c)
+        a[c] = T_E4M3[orc_fp8s_quant((float)orc_bf16_value(x_row[c]), s_in)];
+    for (int n = 0; n < I; ++n) {
+        double g = 0.0, u = 0.0;
+        orc_mat_row(w13, H, n, wrow);
+        for (int c = 0; c < H; ++c)
+            g += a[c] * wrow[c];
+        orc_mat_row(w13, H, I + n, wrow);
+        for (int c = 0; c < H; ++c)
+            u += a[c] * wrow[c];
+        const uint16_t gb = orc_bf16_rne(g * (double)s_in);
+        const uint16_t ub = orc_bf16_rne(u * (double)s_in);
+        if (gu) {
+            gu[n] = gb;
+            gu[I + n] = ub;
+        }
+        h[n] = orc_bf16_rne(orc_swiglu(orc_bf16_value(gb), orc_bf16_value(ub), limit));
+    }
+    free(a);
+    free(wrow);
+}
+
+/* down of the static-FP8 shared expert: h (bf16 bits, [I]) quantized with the
+ * down input's static scale (codes to hq when not NULL), y [H] in fp64. */
+void orc_down_fp8s(const orc_mat *w2, int H, int I, const uint16_t *h, float s_in, double *y, uint8_t *hq)
+{
+    tables();
+    double *a = (double *)malloc(sizeof(double) * I);
+    for (int n = 0; n < I; ++n) {
+        const uint8_t q = orc_fp8s_quant((float)orc_bf16_value(h[n]), s_in);
+        if (hq)
+            hq[n] = q;
+        a[n] = T_E4M3[q];
+    }
+    orc_down(w2, H, I, a, y);
+    for (int c = 0; c < H; ++c)
+        y[c] *= (double)s_in;
     free(a);
 }
 
@@ -655,6 +727,11 @@ static void expert_item(rows_job *J, int i, int j)
             h[n] = orc_bf16_value(orc_bf16_rne(h[n]));
         orc_down(&L->sh2, H, L->I_sh, h, ysh);
         free(h);
+    } else if (L->sfmt == ORC_FP8S) {
+        uint16_t *h = (uint16_t *)malloc(sizeof(uint16_t) * L->I_sh);
+        orc_gate_up_fp8s(&L->sh13, H, L->I_sh, L->x + (size_t)r * H, L->sh_in13, L->swiglu_limit, h, NULL);
+        orc_down_fp8s(&L->sh2, H, L->I_sh, h, L->sh_in2, ysh, NULL);
+        free(h);
     } else {
         expert_fp4(&L->sh13, &L->sh2, H, L->I_sh, a, L->swiglu_limit, L->act_fmt, L->sh_h_gscale, ysh, NULL,
                    NULL);
@@ -712,7 +789,9 @@ int orc_moe_rows(const orc_layer *L, const float *logits, const int32_t *rows, i
     if (!logits && !L->Wr)
         return -1;
     if (L->act_fmt == ORC_ACT_NVFP4 &&
-        (L->wfmt != ORC_NVFP4 || !L->h_gscale || (L->sfmt != ORC_NONE && L->sfmt != ORC_NVFP4 && L->sfmt != ORC_BF16)))
+        (L->wfmt != ORC_NVFP4 || !L->h_gscale || L->sfmt == ORC_MXFP4))
+        return -1;
+    if (L->sfmt == ORC_FP8S && !(L->sh_in13 > 0.0f && L->sh_in2 > 0.0f && isfinite(L->sh_in13) && isfinite(L->sh_in2)))
         return -1;
     for (int i = 0; i < nrows; ++i)
         if (rows[i] < 0 || rows[i] >= L->M)

@@ -14,7 +14,9 @@
  *   - every quantization point of the layer mirrored (activation MXFP8 or,
  *     for NVFP4 experts on NVFP4 activations, NVFP4 with its static globals
  *     and every code decision in fp32; the SwiGLU-output requant in the same
- *     format; bf16 residual, bf16 output);
+ *     format; the static-FP8 shared expert's input quant, bf16 gate/up
+ *     outputs, bf16 h and its static-FP8 requant; bf16 residual, bf16
+ *     output);
  *   - the SwiGLU optionally clamped (orc_swiglu).
  *
  * Every function that cannot be pinned against something other than itself
@@ -34,11 +36,13 @@
 extern "C" {
 #endif
 
-enum { ORC_NONE = 0, ORC_MXFP4 = 1, ORC_NVFP4 = 2, ORC_BF16 = 3 };
+enum { ORC_NONE = 0, ORC_MXFP4 = 1, ORC_NVFP4 = 2, ORC_BF16 = 3, ORC_FP8S = 4 };
 
 /* One weight matrix [N, K], canonical layout: packed FP4 [N, K/2] (low nibble
  * = even K), scales [N, K/32] E8M0 (MXFP4) or [N, K/16] E4M3 (NVFP4), plus an
- * fp32 per-tensor global (NVFP4); or bf16 [N, K]. */
+ * fp32 per-tensor global (NVFP4); or bf16 [N, K]; or (ORC_FP8S, shared expert
+ * only) E4M3 codes [N, K] in `packed` with the fp32 per-tensor weight scale in
+ * `gscale`. */
 /* Activation formats of the expert GEMMs. */
 enum { ORC_ACT_MXFP8 = 0, ORC_ACT_NVFP4 = 1 };
 
@@ -55,7 +59,7 @@ typedef struct {
 typedef struct {
     int M, H, E, k, I, I_sh;
     int wfmt;            /* ORC_MXFP4 or ORC_NVFP4 */
-    int sfmt;            /* ORC_NONE, ORC_MXFP4, ORC_NVFP4 or ORC_BF16 */
+    int sfmt;            /* ORC_NONE, ORC_MXFP4, ORC_NVFP4, ORC_BF16 or ORC_FP8S */
     double routed_scale;
     double eps;
     const uint16_t *x;         /* bf16 [M, H] */
@@ -71,6 +75,7 @@ typedef struct {
     float x_gscale;            /* NVFP4 activations: global of the layer input */
     const float *h_gscale;     /* NVFP4 activations: global of each routed expert's h [E] */
     float sh_h_gscale;         /* NVFP4 activations: global of the shared expert's h */
+    float sh_in13, sh_in2;     /* ORC_FP8S shared expert: static input scales of gate/up and down */
 } orc_layer;
 
 /* ---- formats ---- */
@@ -107,6 +112,12 @@ double orc_swiglu(double g, double u, double limit);
 void orc_gate_up(const orc_mat *w13, int H, int I, const double *a, double limit, double *h);
 void orc_gate_up_bf16(const orc_mat *w13, int H, int I, const uint16_t *x_row, double limit, double *h);
 void orc_down(const orc_mat *w2, int H, int I, const double *h, double *y);
+/* the static-FP8 shared expert (ORC_FP8S): the input quant of one value, the
+ * gate/up on a bf16 row (h and optionally g/u as bf16 bits), the down on h */
+uint8_t orc_fp8s_quant(float v, float s_in);
+void orc_gate_up_fp8s(const orc_mat *w13, int H, int I, const uint16_t *x_row, float s_in, double limit,
+                      uint16_t *h, uint16_t *gu);
+void orc_down_fp8s(const orc_mat *w2, int H, int I, const uint16_t *h, float s_in, double *y, uint8_t *hq);
 
 /* ---- finalize ---- */
 void orc_finalize_row(int H, int k, const double *y, const float *w, const double *y_sh,

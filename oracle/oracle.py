@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 SOURCES = [os.path.join(HERE, "moe_oracle.c")]
 
-ORC_NONE, ORC_MXFP4, ORC_NVFP4, ORC_BF16 = 0, 1, 2, 3
+ORC_NONE, ORC_MXFP4, ORC_NVFP4, ORC_BF16, ORC_FP8S = 0, 1, 2, 3, 4
 
 
 def build(force: bool = True) -> str:
@@ -47,7 +47,7 @@ class orc_layer(C.Structure):
                 ("w13", C.POINTER(orc_mat)), ("w2", C.POINTER(orc_mat)),
                 ("sh13", orc_mat), ("sh2", orc_mat), ("swiglu_limit", C.c_double),
                 ("act_fmt", C.c_int), ("x_gscale", C.c_float), ("h_gscale", C.c_void_p),
-                ("sh_h_gscale", C.c_float)]
+                ("sh_h_gscale", C.c_float), ("sh_in13", C.c_float), ("sh_in2", C.c_float)]
 
 
 _lib = None
@@ -91,6 +91,10 @@ def lib():
         L.orc_swiglu.restype = d
         L.orc_swiglu.argtypes = [d, d, d]
         L.orc_down.argtypes = [C.POINTER(orc_mat), C.c_int, C.c_int, vp, vp]
+        L.orc_fp8s_quant.restype = u8
+        L.orc_fp8s_quant.argtypes = [f32, f32]
+        L.orc_gate_up_fp8s.argtypes = [C.POINTER(orc_mat), C.c_int, C.c_int, vp, f32, d, vp, vp]
+        L.orc_down_fp8s.argtypes = [C.POINTER(orc_mat), C.c_int, C.c_int, vp, f32, vp, vp]
         L.orc_finalize_row.argtypes = [C.c_int, C.c_int, vp, vp, vp, vp, vp, d, vp, vp, vp]
         L.orc_moe_rows.argtypes = [C.POINTER(orc_layer), vp, vp, C.c_int, C.c_int] + [vp] * 9
         L.orc_moe_rows.restype = C.c_int
@@ -318,6 +322,31 @@ def down(m: Mat, H: int, I: int, h: np.ndarray) -> np.ndarray:
     return y
 
 
+def fp8s_quant(v: float, s_in: float) -> int:
+    """Static-FP8 code of one value: E4M3 of the fp32 quotient v / s_in."""
+    return int(lib().orc_fp8s_quant(float(v), float(s_in)))
+
+
+def gate_up_fp8s(m: Mat, H: int, I: int, x_row: np.ndarray, s_in: float, limit: float = 0.0):
+    """Static-FP8 shared gate/up on one bf16 row: (h bf16 bits [I], g/u bf16 bits [2I])."""
+    x_row = np.ascontiguousarray(x_row, np.uint16)
+    h = np.empty(I, np.uint16)
+    gu = np.empty(2 * I, np.uint16)
+    cm = m.c()
+    lib().orc_gate_up_fp8s(C.byref(cm), H, I, _p(x_row), float(s_in), float(limit), _p(h), _p(gu))
+    return h, gu
+
+
+def down_fp8s(m: Mat, H: int, I: int, h_bf16: np.ndarray, s_in: float):
+    """Static-FP8 shared down on bf16 h: (y fp64 [H], h codes [I])."""
+    h_bf16 = np.ascontiguousarray(h_bf16, np.uint16)
+    y = np.empty(H, np.float64)
+    hq = np.empty(I, np.uint8)
+    cm = m.c()
+    lib().orc_down_fp8s(C.byref(cm), H, I, _p(h_bf16), float(s_in), _p(y), _p(hq))
+    return y, hq
+
+
 def finalize_row(y, w, y_sh, residual, gamma, eps):
     y = np.ascontiguousarray(y, np.float64)
     k, H = y.shape
@@ -366,7 +395,8 @@ class Layer:
                            float(sh.routed_scale), float(sh.eps), _p(self.x), _p(self.x),
                            _p(self.gamma), _p(self.Wr), _p(self.bias), arr13, arr2,
                            self.sh13.c(), self.sh2.c(), float(sh.swiglu_limit), int(sh.act_fmt),
-                           float(inp.x_gscale), _p(self.h_g), float(inp.sh_h_gscale))
+                           float(inp.x_gscale), _p(self.h_g), float(inp.sh_h_gscale),
+                           float(inp.sh_in13), float(inp.sh_in2))
 
     def rows(self, rows, logits=None, nthreads=0, want_h=False):
         sh = self.inp.shape

@@ -12,7 +12,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
-PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_route.py", "tests/test_oracle_layer.py"]
+PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_route.py", "tests/test_oracle_layer.py",
+        "tests/test_oracle_fp8s.py"]
 
 MUTANTS = {
     "up rows read from the gate half": ("orc_mat_row(w13, H, I + n, wrow);", "orc_mat_row(w13, H, n, wrow);"),
@@ -70,6 +71,21 @@ MUTANTS = {
                                           "orc_nvfp4_quant_f32(hf, 1, I, 1.0f, q, s);"),
     "W4A4 shared h with a routed global": ("L->act_fmt, L->sh_h_gscale, ysh,", "L->act_fmt, L->h_gscale[0], ysh,"),
     "E4M3 not saturating": ("    if (r > 448.0)\n        r = 448.0;\n", ""),
+    "static FP8 multiplies by its scale": ("const float q = v / s_in;", "const float q = v * s_in;"),
+    "static FP8 quotient in fp64": ("return orc_e4m3_rne_sat((double)q);",
+                                    "(void)q;\n    return orc_e4m3_rne_sat((double)v / (double)s_in);"),
+    "static FP8 gate/up without its input scale": ("const uint16_t gb = orc_bf16_rne(g * (double)s_in);",
+                                                   "const uint16_t gb = orc_bf16_rne(g);"),
+    "static FP8 gate/up outputs not rounded to bf16": (
+        "h[n] = orc_bf16_rne(orc_swiglu(orc_bf16_value(gb), orc_bf16_value(ub), limit));",
+        "h[n] = orc_bf16_rne(orc_swiglu(g * (double)s_in, u * (double)s_in, limit));"),
+    "static FP8 down without its input scale": ("        y[c] *= (double)s_in;\n", ""),
+    "static FP8 weight scale dropped": ("out[k] = T_E4M3[m->packed[(size_t)n * K + k]] * (double)m->gscale;",
+                                        "out[k] = T_E4M3[m->packed[(size_t)n * K + k]];"),
+    "static FP8 shared input scales swapped": ("L->x + (size_t)r * H, L->sh_in13, L->swiglu_limit, h, NULL);",
+                                               "L->x + (size_t)r * H, L->sh_in2, L->swiglu_limit, h, NULL);"),
+    "clamp left out of the static FP8 shared expert": ("L->x + (size_t)r * H, L->sh_in13, L->swiglu_limit, h, NULL);",
+                                                       "L->x + (size_t)r * H, L->sh_in13, 0.0, h, NULL);"),
 }
 
 
