@@ -93,6 +93,8 @@ def expert_bytes(fmt, N, K):
         return 2 * N * K
     if fmt == synth.MXFP4:
         return N * K // 2 + N * K // 32
+    if fmt == synth.FP8S:
+        return N * K + 4
     return N * K // 2 + N * K // 16 + 4
 
 
@@ -395,7 +397,8 @@ def stage_workload(name, seed, copies_arg):
         copies_w.append(cw)
         layers.append(moe.Layer(s.M, s.H, s.E, s.k, s.I, s.I_sh, s.routed_scale, s.eps, cw[4], d.bias,
                                 cw[0], cw[1], cw[2], cw[3], d.gamma, s.swiglu_limit, s.act_fmt, d.x_global,
-                                d.h_globals, d.sh_h_global if s.sfmt == synth.NVFP4 else None))
+                                d.h_globals, d.sh_h_global if s.sfmt == synth.NVFP4 else None, d.sh_in_scale,
+                                d.sh_h_scale))
     torch.cuda.synchronize()
     log(f"[bench] {name}: U={U} unique experts, routed bytes {bm['routed'] / 1e6:.1f} MB, total "
         f"{bm['total'] / 1e6:.1f} MB, {copies} weight copies; staged in {time.time() - t0:.1f}s")

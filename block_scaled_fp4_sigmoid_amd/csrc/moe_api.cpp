@@ -37,6 +37,9 @@ int check_pair_bytes(int M, int k, int H) {
 
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
+// A static FP8 input scale: finite and positive.
+bool static_scale_ok(float s) { return s > 0.0f && s <= 3.4e38f; }
+
 int check_dims(int M, int H, int E, int k) {
     if (M < 1 || H < 1 || E < 1 || k < 1) return MOE_ERR_INVALID_ARG;
     if (M > kMaxM || E > kMaxE || k > std::min(E, kMaxK)) return MOE_ERR_UNSUPPORTED;
@@ -53,9 +56,10 @@ int check_routing(const moe_routing* r) {
 }
 
 int check_fp4_weights(const moe_weights* w) {
-    if (!w || !w->w || !w->scales) return MOE_ERR_INVALID_ARG;
-    if (w->fmt == MOE_FMT_NVFP4 && !w->global_scale) return MOE_ERR_INVALID_ARG;
+    if (!w) return MOE_ERR_INVALID_ARG;
     if (w->fmt != MOE_FMT_MXFP4 && w->fmt != MOE_FMT_NVFP4) return MOE_ERR_UNSUPPORTED;
+    if (!w->w || !w->scales) return MOE_ERR_INVALID_ARG;
+    if (w->fmt == MOE_FMT_NVFP4 && !w->global_scale) return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
@@ -228,6 +232,7 @@ size_t moe_gate_up_workspace_bytes(int fmt, int M, int H, int I, int E, int k, i
     if (check_dims(M, H, dense ? 1 : E, dense ? 1 : k) != MOE_OK) return 0;
     if (I < 128 || I % 128 != 0 || I > kMaxI) return 0;
     if (fmt == MOE_FMT_BF16) return dense ? gate_up_bf16_partials_bytes(M, H, I) : 0;
+    if (fmt == MOE_FMT_FP8S) return dense ? gate_up_fp8s_partials_bytes(M, H, I) : 0;
     if (fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_NVFP4) return 0;
     moe_weights w{};
     w.fmt = fmt;
@@ -331,6 +336,33 @@ int moe_expert_down_nvfp4a(const moe_weights* w2, const uint8_t* h_q, const uint
     return hip_status(launch_down_fp4(job, h_q, h_s, y, stream));
 }
 
+int moe_expert_gate_up_fp8s(const moe_weights* w13, const uint16_t* x, float s_in, float s_h, int M, int H, int I,
+                            float swiglu_limit, uint8_t* h_q, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    if (!w13 || !x || !h_q) return MOE_ERR_INVALID_ARG;
+    if (!static_scale_ok(s_in) || !static_scale_ok(s_h) || !(swiglu_limit >= 0.0f)) return MOE_ERR_INVALID_ARG;
+    if (int st = check_dims(M, H, 1, 1)) return st;
+    if (I < 128 || I % 128 != 0 || I > kMaxI) return MOE_ERR_UNSUPPORTED;
+    if (w13->fmt != MOE_FMT_FP8S) return MOE_ERR_UNSUPPORTED;
+    if (!w13->w || !w13->global_scale) return MOE_ERR_INVALID_ARG;
+    const size_t need = gate_up_fp8s_partials_bytes(M, H, I);
+    if (!workspace || !aligned256(workspace) || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    ExpertJob job = dense_job(*w13, I, H, M);
+    job.swiglu_limit = swiglu_limit;
+    return hip_status(launch_gate_up_fp8s(job, x, s_in, s_h, h_q, static_cast<float*>(workspace), stream));
+}
+
+int moe_expert_down_fp8s(const moe_weights* w2, const uint8_t* h_q, float s_h, int M, int H, int I, float* y,
+                         hipStream_t stream) {
+    if (!w2 || !h_q || !y) return MOE_ERR_INVALID_ARG;
+    if (!static_scale_ok(s_h)) return MOE_ERR_INVALID_ARG;
+    if (int st = check_dims(M, H, 1, 1)) return st;
+    if (I < 128 || I % 128 != 0 || I > kMaxI) return MOE_ERR_UNSUPPORTED;
+    if (w2->fmt != MOE_FMT_FP8S) return MOE_ERR_UNSUPPORTED;
+    if (!w2->w || !w2->global_scale) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_down_fp8s(dense_job(*w2, H, I, M), h_q, s_h, y, stream));
+}
+
 int moe_finalize_rmsnorm_mxfp8(const float* y, const float* topk_w, const float* y_sh,
                                const uint16_t* residual, const uint16_t* gamma, float eps, int M, int H,
                                int k, uint16_t* out, uint16_t* residual_out, uint8_t* out_q, uint8_t* out_s,
@@ -393,6 +425,9 @@ int check_desc(const moe_layer_desc* d) {
         if (d->I_sh < 128 || d->I_sh % 128 != 0 || d->I_sh > kMaxI) return MOE_ERR_UNSUPPORTED;
         if (sf == MOE_FMT_BF16) {
             if (!d->sh13.w || !d->sh2.w) return MOE_ERR_INVALID_ARG;
+        } else if (sf == MOE_FMT_FP8S) {
+            if (!d->sh13.w || !d->sh2.w || !d->sh13.global_scale || !d->sh2.global_scale) return MOE_ERR_INVALID_ARG;
+            if (!static_scale_ok(d->sh_in_scale) || !static_scale_ok(d->sh_h_scale)) return MOE_ERR_INVALID_ARG;
         } else {
             if (int st = check_fp4_weights(&d->sh13)) return st;
             if (int st = check_fp4_weights(&d->sh2)) return st;
@@ -421,6 +456,7 @@ LayerWs carve_layer(Carver& c, const moe_layer_desc* d) {
     const int T = moe_tile_capacity(M, E, k);
     const bool sh = d->sh13.fmt != MOE_FMT_NONE;
     const bool shb = d->sh13.fmt == MOE_FMT_BF16;
+    const bool sh8 = d->sh13.fmt == MOE_FMT_FP8S;
     L.route = carve_route(c, M, H, E);
     L.ids = c.take<int32_t>(P);
     L.w = c.take<float>(P);
@@ -444,7 +480,7 @@ LayerWs carve_layer(Carver& c, const moe_layer_desc* d) {
     L.hsq = L.hss = nullptr;
     L.hsb = nullptr;
     L.sh_part = nullptr;
-    if (sh && !shb) {
+    if (sh && !shb && !sh8) {
         L.hsq = c.take<uint8_t>((size_t)M * Ish);
         L.hss = c.take<uint8_t>((size_t)M * Ish / sdiv);
     }
@@ -452,13 +488,17 @@ LayerWs carve_layer(Carver& c, const moe_layer_desc* d) {
         L.hsb = c.take<uint16_t>((size_t)M * Ish);
         L.sh_part = c.take<float>(gate_up_bf16_partials_bytes(M, H, Ish) / sizeof(float));
     }
+    if (sh8) {  // static-FP8 h codes and the gate_up partial sums
+        L.hsq = c.take<uint8_t>((size_t)M * Ish);
+        L.sh_part = c.take<float>(gate_up_fp8s_partials_bytes(M, H, Ish) / sizeof(float));
+    }
     {
         moe_weights w = d->w13;
         moe_routing r{};
         L.part = c.take<float>(gate_up_fp4_partials_bytes(routed_job(w, I, H, r, M, E, k)) / sizeof(float));
     }
     L.sh_fpart = nullptr;
-    if (sh && !shb)
+    if (sh && !shb && !sh8)
         L.sh_fpart = c.take<float>(gate_up_fp4_partials_bytes(dense_job(d->sh13, Ish, H, M)) / sizeof(float));
     L.y = c.take<float>((size_t)P * H);
     L.ysh = sh ? c.take<float>((size_t)M * H) : nullptr;
@@ -505,23 +545,27 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
     r.num_active = L.num_active;
     r.active_offsets = L.act_off;
 
-    // A bf16 shared expert does not depend on the routing: its three stages
-    // run as extra workgroups of the router, top-k and bucketing launches.
-    const bool shb = sf == MOE_FMT_BF16;
+    // A bf16 or static-FP8 shared expert does not depend on the routing: its
+    // three stages run as extra workgroups of the router, top-k and
+    // bucketing (or gate_up) launches; the static-FP8 gate/up in the router
+    // launch (README Qwen3.5 slot table, row "route_shared"), its SiLU-and-mul
+    // with the static FP8 quant of the down input in the top-k launch (PR #33
+    // appended table, row "shared act quant").
+    const bool sh8 = sf == MOE_FMT_FP8S;
+    const bool shb = sf == MOE_FMT_BF16 || sh8;  // the shared expert rides as side stages
     ExpertJob sh_gu = dense_job(d->sh13, Ish, H, M);
     sh_gu.swiglu_limit = d->swiglu_limit;
     const bool a4 = d->act_fmt == MOE_ACT_NVFP4;
     const float xg4 = a4 ? d->x_global : 0.0f;
     if (sf == MOE_FMT_NVFP4) set_a4(sh_gu, d, true, true);
-    const Bf16Side s1 = shb ? bf16_side(sh_gu, Ish, H, M, x, L.sh_part, L.hsb, L.ysh,
-                                        kBf16GateUp)
-                            : no_side();
-    const Bf16Side s2 = shb ? bf16_side(sh_gu, Ish, H, M, x, L.sh_part, L.hsb, L.ysh,
-                                        kBf16Swiglu)
-                            : no_side();
-    const Bf16Side s3 = shb ? bf16_side(dense_job(d->sh2, H, Ish, M), Ish, H, M, x, L.sh_part, L.hsb, L.ysh,
-                                        kBf16Down)
-                            : no_side();
+    const ExpertJob sh_dn = dense_job(d->sh2, H, Ish, M);
+    const auto side = [&](const ExpertJob& j, float s_in, float s_out, int stage) {
+        return sh8 ? fp8s_side(j, Ish, H, M, x, L.sh_part, L.hsq, L.ysh, s_in, s_out, stage)
+                   : bf16_side(j, Ish, H, M, x, L.sh_part, L.hsb, L.ysh, stage);
+    };
+    const Bf16Side s1 = shb ? side(sh_gu, d->sh_in_scale, d->sh_h_scale, kBf16GateUp) : no_side();
+    const Bf16Side s2 = shb ? side(sh_gu, d->sh_in_scale, d->sh_h_scale, kBf16Swiglu) : no_side();
+    const Bf16Side s3 = shb ? side(sh_dn, d->sh_h_scale, 0.0f, kBf16Down) : no_side();
     const RouterPlan p = router_plan(M, H, E);
     const bool fp4_shared = sf != MOE_FMT_NONE && !shb;
     if (M * k <= kSmallPairs) {

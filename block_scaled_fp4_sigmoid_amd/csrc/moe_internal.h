@@ -27,6 +27,17 @@ struct Bf16Side {
     float* y;           // fp32 [M][H] (down output)
     int blocks;         // workgroups of the stage
     float limit;        // clamped SwiGLU limit (0: unclamped)
+    // static-FP8 shared expert (fp8 != 0): E4M3 weights w8 [N][K] with the
+    // per-tensor scale *wscale (device); gate_up quantizes x with the static
+    // input scale s_in and writes raw partial sums; the SwiGLU stage scales
+    // them by s_in * *wscale, rounds g, u and h to bf16 and writes h as E4M3
+    // codes hq [M][I] quantized with s_out; down reads hq with its static
+    // scale s_in and scales the sums by s_in * *wscale.
+    int fp8;
+    const uint8_t* w8;
+    const float* wscale;
+    float s_in, s_out;
+    uint8_t* hq;
 };
 enum Bf16Stage { kBf16None = 0, kBf16GateUp = 1, kBf16Swiglu = 2, kBf16Down = 3 };
 // An empty side: no extra workgroups.
@@ -161,6 +172,15 @@ hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8
 size_t gate_up_bf16_partials_bytes(int M, int H, int I);
 Bf16Side bf16_side(const ExpertJob& gate_up_or_down, int I, int H, int M, const uint16_t* x, float* part,
                    uint16_t* h, float* y, int stage);
+// The static-FP8 shared expert's stages (weights: job.w.w E4M3 codes,
+// job.w.global_scale the device weight scale).  gate_up: s_in = the input's
+// static scale, s_out = h's; down: s_in = h's.
+size_t gate_up_fp8s_partials_bytes(int M, int H, int I);
+Bf16Side fp8s_side(const ExpertJob& gate_up_or_down, int I, int H, int M, const uint16_t* x, float* part,
+                   uint8_t* hq, float* y, float s_in, float s_out, int stage);
+hipError_t launch_gate_up_fp8s(const ExpertJob& job, const uint16_t* x, float s_in, float s_h, uint8_t* hq,
+                               float* partials, hipStream_t stream);
+hipError_t launch_down_fp8s(const ExpertJob& job, const uint8_t* hq, float s_h, float* y, hipStream_t stream);
 hipError_t launch_gate_up_bf16(const ExpertJob& job, const uint16_t* a, uint16_t* h,
                                float* partials, hipStream_t stream);
 hipError_t launch_down_bf16(const ExpertJob& job, const uint16_t* h, float* y, hipStream_t stream);

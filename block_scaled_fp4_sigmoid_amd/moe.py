@@ -17,7 +17,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_mi355.so")
 
-MOE_FMT_NONE, MOE_FMT_MXFP4, MOE_FMT_NVFP4, MOE_FMT_BF16 = 0, 1, 2, 3
+MOE_FMT_NONE, MOE_FMT_MXFP4, MOE_FMT_NVFP4, MOE_FMT_BF16, MOE_FMT_FP8S = 0, 1, 2, 3, 4
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
 MOE_ERR_SCRATCH = 5
 NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -28,7 +28,7 @@ EXPORTS = ["moe_status_str", "moe_abi_version", "moe_tile_capacity", "moe_packed
            "moe_expert_gate_up", "moe_expert_down", "moe_expert_gate_up_nvfp4a",
            "moe_expert_down_nvfp4a", "moe_finalize_rmsnorm",
            "moe_finalize_rmsnorm_mxfp8", "moe_layer_workspace_bytes", "moe_layer",
-           "moe_layer_mxfp8_out", "moe_layer_noalloc"]
+           "moe_layer_mxfp8_out", "moe_layer_noalloc", "moe_expert_gate_up_fp8s", "moe_expert_down_fp8s"]
 
 
 class moe_weights(C.Structure):
@@ -49,7 +49,7 @@ class moe_layer_desc(C.Structure):
                 ("w13", moe_weights), ("w2", moe_weights), ("sh13", moe_weights),
                 ("sh2", moe_weights), ("gamma", C.c_void_p), ("swiglu_limit", C.c_float),
                 ("act_fmt", C.c_int), ("x_global", C.c_float), ("h_globals", C.c_void_p),
-                ("sh_h_global", C.c_void_p)]
+                ("sh_h_global", C.c_void_p), ("sh_in_scale", C.c_float), ("sh_h_scale", C.c_float)]
 
 
 _lib = None
@@ -106,6 +106,10 @@ def lib() -> C.CDLL:
         L.moe_layer_mxfp8_out.restype = i
         L.moe_layer_mxfp8_out.argtypes = [C.POINTER(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                           sz, vp]
+        L.moe_expert_gate_up_fp8s.restype = i
+        L.moe_expert_gate_up_fp8s.argtypes = [C.POINTER(moe_weights), vp, f, f, i, i, i, f, vp, vp, sz, vp]
+        L.moe_expert_down_fp8s.restype = i
+        L.moe_expert_down_fp8s.argtypes = [C.POINTER(moe_weights), vp, f, i, i, i, vp, vp]
         L.moe_layer_noalloc.restype = i
         L.moe_layer_noalloc.argtypes = [C.POINTER(moe_layer_desc), vp, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
@@ -307,6 +311,24 @@ def expert_down_nvfp4a(w2: Weights, M, H, I, E, k, h_q, h_s, h_globals, y, routi
     _check(rc, "moe_expert_down_nvfp4a")
 
 
+def expert_gate_up_fp8s(w13: Weights, M, H, I, x, s_in: float, s_h: float, h_q, swiglu_limit=0.0, ws=None,
+                        stream=None):
+    """The static-FP8 shared expert's gate_up: h codes [M, I] from bf16 x."""
+    need = lib().moe_gate_up_workspace_bytes(MOE_FMT_FP8S, M, H, I, 1, 1, 1)
+    if ws is None:
+        ws = _call_workspace(need, x.device, stream)
+    wc = w13.c()
+    rc = lib().moe_expert_gate_up_fp8s(C.byref(wc), _p(x), float(s_in), float(s_h), M, H, I, float(swiglu_limit),
+                                       _p(h_q), _p(ws), ws.numel(), _stream(stream))
+    _check(rc, "moe_expert_gate_up_fp8s")
+
+
+def expert_down_fp8s(w2: Weights, M, H, I, h_q, s_h: float, y, stream=None):
+    wc = w2.c()
+    rc = lib().moe_expert_down_fp8s(C.byref(wc), _p(h_q), float(s_h), M, H, I, _p(y), _stream(stream))
+    _check(rc, "moe_expert_down_fp8s")
+
+
 def finalize_rmsnorm(y, topk_w, y_sh, residual, gamma, eps, out, residual_out=None, stream=None,
                      out_q=None, out_s=None):
     """moe_finalize_rmsnorm; with out_q/out_s, moe_finalize_rmsnorm_mxfp8."""
@@ -328,14 +350,14 @@ class Layer:
 
     def __init__(self, M, H, E, k, I, I_sh, routed_scale, eps, w_router, router_bias,
                  w13: Weights, w2: Weights, sh13: Weights, sh2: Weights, gamma, swiglu_limit=0.0,
-                 act_fmt=0, x_global=0.0, h_globals=None, sh_h_global=None):
+                 act_fmt=0, x_global=0.0, h_globals=None, sh_h_global=None, sh_in_scale=0.0, sh_h_scale=0.0):
         _need_packed(w13, w2, sh13, sh2)
         self._keep = (w_router, router_bias, w13, w2, sh13, sh2, gamma, h_globals, sh_h_global)
         self.M, self.H, self.E, self.k = M, H, E, k
         self.desc = moe_layer_desc(M, H, E, k, I, I_sh, float(routed_scale), float(eps),
                                    _p(w_router), _p(router_bias), w13.c(), w2.c(), sh13.c(),
                                    sh2.c(), _p(gamma), float(swiglu_limit), int(act_fmt), float(x_global),
-                                   _p(h_globals), _p(sh_h_global))
+                                   _p(h_globals), _p(sh_h_global), float(sh_in_scale), float(sh_h_scale))
         self.ws_bytes = lib().moe_layer_workspace_bytes(C.byref(self.desc))
         if self.ws_bytes == 0:
             raise RuntimeError("moe_layer_workspace_bytes rejected the layer description")

@@ -16,7 +16,7 @@ import numpy as np
 import torch
 
 from . import synth
-from .moe import (MOE_FMT_BF16, MOE_FMT_NONE, Layer, Weights, pack_fp4)
+from .moe import (MOE_FMT_BF16, MOE_FMT_FP8S, MOE_FMT_NONE, Layer, Weights, pack_fp4)
 
 
 def _t(a: np.ndarray, device) -> torch.Tensor:
@@ -39,6 +39,8 @@ def matrix_on(m: Optional[synth.Matrix], device) -> Weights:
     if m.fmt == synth.BF16:
         return Weights(MOE_FMT_BF16, _t(m.bf16, device))
     g = torch.tensor([m.gscale], dtype=torch.float32, device=device)
+    if m.fmt == synth.FP8S:  # E4M3 codes [1, N, K] and the weight scale
+        return Weights(MOE_FMT_FP8S, _t(m.packed, device)[None], None, g)
     w = Weights(m.fmt, _t(m.packed, device)[None], _t(m.scales, device)[None], g)
     return pack_fp4(w)
 
@@ -63,13 +65,16 @@ class DeviceInputs:
     x_global: float = 0.0
     h_globals: Optional[torch.Tensor] = None     # fp32 [E]
     sh_h_global: Optional[torch.Tensor] = None   # fp32 [1]
+    # static-FP8 shared expert: the static input scales of its gate/up and down
+    sh_in_scale: float = 0.0
+    sh_h_scale: float = 0.0
 
     def layer(self) -> Layer:
         s = self.shape
         return Layer(s.M, s.H, s.E, s.k, s.I, s.I_sh, s.routed_scale, s.eps, self.Wr, self.bias,
                      self.w13, self.w2, self.sh13, self.sh2, self.gamma, s.swiglu_limit,
                      s.act_fmt, self.x_global, self.h_globals,
-                     self.sh_h_global if s.sfmt == synth.NVFP4 else None)
+                     self.sh_h_global if s.sfmt == synth.NVFP4 else None, self.sh_in_scale, self.sh_h_scale)
 
     def weight_bytes_per_expert(self) -> int:
         s = self.shape
@@ -92,4 +97,6 @@ def to_device(inp: synth.MoEInputs, device="cuda") -> DeviceInputs:
         float(inp.x_gscale),
         None if inp.h_gscale is None else _t(np.ascontiguousarray(inp.h_gscale, np.float32), device),
         None if inp.h_gscale is None else _t(np.array([inp.sh_h_gscale], np.float32), device),
+        float(inp.sh_in13),
+        float(inp.sh_in2),
     )

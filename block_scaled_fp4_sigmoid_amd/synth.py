@@ -172,14 +172,15 @@ WORKLOAD_ORDER = list(WORKLOADS)
 
 # Further workloads (not among the five): NVFP4 activations (W4A4) at the
 # pages' Qwen3.5 verify step of 7 rows with top-10 (README slot table, rows
-# "route" and "mkm"); the pages give no layer dimensions, so it takes the
-# skewed-routing workload's (hidden 4096, 512 experts, intermediate 512, bf16
+# "route" and "mkm"), with the static-FP8 shared expert of the same table
+# (row "route_shared"); the pages give no layer dimensions, so it takes the
+# skewed-routing workload's (hidden 4096, 512 experts, intermediate 512,
 # shared expert of 512) without the bias.
 EXTRA_WORKLOADS = {
     "verify7-m7-h4096-e512-k10-nvfp4-a4": Shape(
-        "verify7-m7-h4096-e512-k10-nvfp4-a4", 7, 4096, 512, 10, 512, NVFP4, BF16, 512, 1.0, "none",
+        "verify7-m7-h4096-e512-k10-nvfp4-a4", 7, 4096, 512, 10, 512, NVFP4, FP8S, 512, 1.0, "none",
         act_fmt=ACT_NVFP4,
-        desc="7-row verify step with top-10, NVFP4 experts on NVFP4 activations (W4A4), bf16 shared expert"),
+        desc="7-row verify step with top-10, NVFP4 experts on NVFP4 activations (W4A4), static-FP8 shared expert"),
 }
 WORKLOADS.update(EXTRA_WORKLOADS)
 

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 8
+#define MOE_ABI_VERSION 9
 
 enum moe_status {
     MOE_OK = 0,
@@ -65,7 +65,8 @@ enum moe_fmt {
     MOE_FMT_NONE = 0,  /* no shared expert */
     MOE_FMT_MXFP4 = 1, /* packed E2M1 + E8M0 per 32 along K */
     MOE_FMT_NVFP4 = 2, /* packed E2M1 + E4M3 per 16 along K + fp32 global per expert */
-    MOE_FMT_BF16 = 3   /* bf16 (shared expert only) */
+    MOE_FMT_BF16 = 3,  /* bf16 (shared expert only) */
+    MOE_FMT_FP8S = 4   /* static FP8: E4M3 + one fp32 scale per matrix (shared expert only) */
 };
 
 /* One projection of E experts (or of the shared expert, E = 1), each a
@@ -73,7 +74,9 @@ enum moe_fmt {
  *   MXFP4: w = packed [E, N, K/2] (two E2M1 per byte, low nibble first),
  *          scales = E8M0 [E, N, K/32], global unused;
  *   NVFP4: w = packed [E, N, K/2], scales = E4M3 [E, N, K/16], global = fp32 [E];
- *   BF16:  w = bf16 [E, N, K], scales and global unused.
+ *   BF16:  w = bf16 [E, N, K], scales and global unused;
+ *   FP8S:  w = E4M3 codes [E, N, K], scales unused, global = fp32 [E], the
+ *          per-tensor weight scale (value = E4M3(code) * global).
  * The expert GEMMs and moe_layer take FP4 weights in the load-order layout
  * that moe_pack_fp4 produces from the standard one (same values, other
  * places); bf16 weights are taken as they are.
@@ -145,6 +148,11 @@ typedef struct moe_layer_desc {
     float x_global;
     const float *h_globals;      /* [E] */
     const float *sh_h_global;    /* [1], or NULL without an NVFP4 shared expert */
+    /* Static-FP8 shared expert (sh13.fmt MOE_FMT_FP8S; any act_fmt): the
+     * static input scales of its gate/up (applied to the bf16 x) and of its
+     * down projection (applied to h), as moe_expert_gate_up_fp8s takes them. */
+    float sh_in_scale;
+    float sh_h_scale;
 } moe_layer_desc;
 
 const char *moe_status_str(int status);
@@ -305,6 +313,34 @@ int moe_expert_gate_up_nvfp4a(const moe_weights *w13, const uint8_t *a_q, const 
 int moe_expert_down_nvfp4a(const moe_weights *w2, const uint8_t *h_q, const uint8_t *h_s, const float *h_globals,
                            const moe_routing *route, int M, int H, int I, int E, int k, float *y,
                            hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_gate_up_fp8s / moe_expert_down_fp8s — the static-FP8 shared
+ * expert (dense over all M rows).
+ *   Pages: README Qwen3.5 slot table, row "route_shared (with route)" (the
+ *   shared expert's static-FP8 gate/up, which the layer runs in the router's
+ *   launch); sgl-nvidia-mega PR #33, appended table, row "shared act quant"
+ *   (its SiLU-and-mul fused with the static FP8 quantization of the down
+ *   projection's input).
+ * The pages fix no rule; the one implemented: an input value v (bf16) is the
+ * E4M3 code of the correctly rounded fp32 quotient v / s (round to nearest
+ * even, saturating at +-448, NaN kept NaN), s the input's static scale; a
+ * linear's output is s * the weight scale * the sum of the code products
+ * (exact products, fp32 sums).
+ * gate_up: w13 FP8S [1, 2I, H] (rows [0, I) gate, [I, 2I) up); x bf16 [M, H]
+ *   quantized with s_in; g and u rounded to bf16; h = bf16(silu(g) * u) (the
+ *   clamped form with swiglu_limit > 0, as moe_expert_gate_up); h_q uint8
+ *   [M, I] = E4M3 codes of h quantized with s_h.  Workspace:
+ *   moe_gate_up_workspace_bytes(MOE_FMT_FP8S, M, H, I, 1, 1, 1) bytes,
+ *   256-byte aligned, no initialization needed.
+ * down: w2 FP8S [1, H, I]; h_q as above with its scale s_h; y fp32 [M, H].
+ * s_in, s_h: finite and > 0 (else MOE_ERR_INVALID_ARG); weights must be
+ * MOE_FMT_FP8S (else MOE_ERR_UNSUPPORTED). */
+int moe_expert_gate_up_fp8s(const moe_weights *w13, const uint16_t *x, float s_in, float s_h, int M, int H, int I,
+                            float swiglu_limit, uint8_t *h_q, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+int moe_expert_down_fp8s(const moe_weights *w2, const uint8_t *h_q, float s_h, int M, int H, int I, float *y,
+                         hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_finalize_rmsnorm — top-k weighted sum of the expert outputs fused with

@@ -51,7 +51,7 @@ def test_probe_library_exports():
 
 
 def test_version_and_status_strings(L):
-    assert moe.abi_version() == 8
+    assert moe.abi_version() == 9
     for rc in range(5):
         assert len(moe.status_str(rc)) > 0
     assert "unknown" in moe.status_str(99)
@@ -258,3 +258,36 @@ def test_noalloc_refusals(L):
     # a 16-row decode-sized layer fits
     assert 0 < L.moe_layer_workspace_bytes(C.byref(_desc(M=16, H=7168, E=384, k=8, I=2048))) <= \
         moe.NOALLOC_SCRATCH_BYTES
+
+
+def test_static_fp8_shared_refusals(L):
+    """The static-FP8 shared expert: dense only, FP8S weights with their
+    scale, finite positive static scales; in the layer description too."""
+    f8 = moe.moe_weights(moe.MOE_FMT_FP8S, 0x1000, None, 0x1000)
+    assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_FP8S, 7, 4096, 512, 1, 1, 1) > 0
+    assert L.moe_gate_up_workspace_bytes(moe.MOE_FMT_FP8S, 7, 4096, 512, 64, 4, 0) == 0   # routed: no
+    gu = lambda w, s_in, s_h, ws=0x1000: L.moe_expert_gate_up_fp8s(C.byref(w), 0x1000, s_in, s_h, 7, 4096, 512, 0.0,
+                                                                   0x1000, ws, 1 << 30, None)
+    mx = moe.moe_weights(moe.MOE_FMT_MXFP4, 0x1000, 0x1000, None)
+    assert gu(mx, 0.1, 0.1) == moe.MOE_ERR_UNSUPPORTED
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert gu(f8, bad, 0.1) == moe.MOE_ERR_INVALID_ARG
+        assert gu(f8, 0.1, bad) == moe.MOE_ERR_INVALID_ARG
+        assert L.moe_expert_down_fp8s(C.byref(f8), 0x1000, bad, 7, 4096, 512, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
+    assert gu(moe.moe_weights(moe.MOE_FMT_FP8S, 0x1000, None, None), 0.1, 0.1) == moe.MOE_ERR_INVALID_ARG
+    assert gu(f8, 0.1, 0.1, ws=0x1010) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_expert_down_fp8s(C.byref(mx), 0x1000, 0.1, 7, 4096, 512, 0x1000, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_down_fp8s(C.byref(f8), 0x1000, 0.1, 7, 4096, 500, 0x1000, None) == moe.MOE_ERR_UNSUPPORTED
+    # FP8S routed experts are refused by the routed entry points
+    r = moe.moe_routing(*([0x1000] * 11))
+    assert L.moe_expert_down(C.byref(f8), 0x1000, 0x1000, None, C.byref(r), 4, 128, 128, 8, 2, 0x1000,
+                             None) == moe.MOE_ERR_UNSUPPORTED
+    ok = dict(I_sh=256, sh13=f8, sh2=f8, sh_in_scale=0.01, sh_h_scale=0.03)
+    assert L.moe_layer_workspace_bytes(C.byref(_desc(**ok))) > 0
+    nv = moe.moe_weights(moe.MOE_FMT_NVFP4, 0x1000, 0x1000, 0x1000)
+    a4 = dict(w13=nv, w2=nv, act_fmt=1, x_global=0.01, h_globals=0x1000)
+    assert L.moe_layer_workspace_bytes(C.byref(_desc(**dict(ok, **a4)))) > 0   # with NVFP4 activations
+    for bad in (dict(ok, sh_in_scale=0.0), dict(ok, sh_h_scale=float("nan")),
+                dict(ok, sh13=moe.moe_weights(moe.MOE_FMT_FP8S, 0x1000, None, None)),
+                dict(ok, sh2=moe.moe_weights(moe.MOE_FMT_FP8S, None, None, 0x1000))):
+        assert L.moe_layer_workspace_bytes(C.byref(_desc(**bad))) == 0

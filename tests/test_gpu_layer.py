@@ -112,6 +112,11 @@ EDGE = [
     dict(M=9, H=512, E=16, k=4, I=384, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=256, act_fmt=synth.ACT_NVFP4),
     dict(M=40, H=768, E=32, k=8, I=640, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=640, act_fmt=synth.ACT_NVFP4,
          swiglu_limit=0.6),
+    # the static-FP8 shared expert riding the router, top-k and gate_up launches (few pairs: W4A4 and
+    # MXFP8 activations) or the route step's launch (many pairs), with the clamp
+    dict(M=7, H=1024, E=64, k=10, I=256, wfmt=synth.NVFP4, sfmt=synth.FP8S, I_sh=256, act_fmt=synth.ACT_NVFP4),
+    dict(M=9, H=768, E=32, k=4, I=384, wfmt=synth.NVFP4, sfmt=synth.FP8S, I_sh=128),
+    dict(M=40, H=512, E=16, k=8, I=256, wfmt=synth.MXFP4, sfmt=synth.FP8S, I_sh=384, swiglu_limit=0.5),
 ]
 
 

@@ -317,6 +317,44 @@ def test_dense_bf16_expert_parity(M, H, I, limit):
     assert eq / (M * I) >= 0.99
 
 
+@pytest.mark.parametrize("M,H,I,limit", [(7, 4096, 512, 0.0), (48, 1024, 256, 0.0), (16, 7168, 2048, 0.0),
+                                         (70, 512, 256, 0.5)])
+def test_dense_fp8s_expert_parity(M, H, I, limit):
+    """The static-FP8 shared expert: h codes (SiLU-and-mul fused with the
+    static FP8 quant of the down input) against the oracle's codes, and y
+    against the oracle's down on the GPU's own codes (exact products, fp32
+    sums).  Codes can differ where the fp32 sums and the fp64 ones round g, u
+    or h to bf16 on either side of a midpoint."""
+    sh = synth.custom_shape(M=M, H=H, E=1, k=1, I=128, sfmt=synth.FP8S, I_sh=I)
+    inp = synth.make_inputs(sh, seed=19, pool_rows=64)
+    d = staging.to_device(inp, DEV)
+    hq = torch.full((M, I), 0x5a, dtype=torch.uint8, device=DEV)
+    moe.expert_gate_up_fp8s(d.sh13, M, H, I, d.x, inp.sh_in13, inp.sh_in2, hq, swiglu_limit=limit)
+    y = torch.empty((M, H), dtype=torch.float32, device=DEV)
+    moe.expert_down_fp8s(d.sh2, M, H, I, hq, inp.sh_in2, y)
+    torch.cuda.synchronize()
+    m13, m2 = orc.Mat.from_synth(inp.sh13), orc.Mat.from_synth(inp.sh2)
+    e4 = orc.e4m3_table()
+    W2abs = np.abs(orc.mat_dequant(m2, H, I))
+    sh_ = np.float64(np.float32(inp.sh_in2))
+    ghq, gy = np_of(hq), np_of(y)
+    eq, worst, l2 = 0, 0.0, 0.0
+    for r in range(M):
+        h, _ = orc.gate_up_fp8s(m13, H, I, inp.x[r], inp.sh_in13, limit)
+        _, hq_ref = orc.down_fp8s(m2, H, I, h, inp.sh_in2)
+        eq += int(np.sum(hq_ref == ghq[r]))
+        hv = e4[ghq[r]]
+        yr = orc.down(m2, H, I, hv) * sh_
+        # the fp8 matrix instruction adds its 32 products with a reduced
+        # internal precision: bound each output by 2^-12 of its sum of |products|
+        bound = 2.0 ** -12 * (W2abs @ np.abs(hv)) * sh_ + 1e-30
+        worst = max(worst, float(np.max(np.abs(gy[r] - yr) / bound)))
+        l2 = max(l2, rel_l2(gy[r], yr))
+    print(f"  h codes equal: {eq / (M * I):.5f}; y: rel_l2 {l2:.2e}, worst error / bound {worst:.3f}")
+    assert worst <= 1.0 and l2 < 2e-4
+    assert eq / (M * I) >= 0.99
+
+
 def test_finalize_parity():
     rng = np.random.default_rng(4)
     M, H, k = 19, 2048 + 128, 5
