@@ -80,6 +80,12 @@ constexpr int kPassRows = 32;           // activation rows per pass (two 16-row 
 #ifndef MOE_MIN_BLOCKS
 #define MOE_MIN_BLOCKS 2  // workgroups per CU the register budget must allow
 #endif
+#ifndef MOE_MX_LDS_ROWS
+#define MOE_MX_LDS_ROWS 2  // MXFP4 gate_up: passes of at least this many rows take the activation tile in LDS
+#endif
+#ifndef MOE_MX_DQ
+#define MOE_MX_DQ 2  // MXFP4 gate_up with the activation tile in LDS: weight ring depth in quads
+#endif
 #ifndef MOE_NV_DQ
 #define MOE_NV_DQ 2  // NVFP4 gate_up: weight ring depth in quads
 #endif
@@ -825,6 +831,189 @@ __device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const
     }
 }
 
+// ---- MXFP4: streaming with the MXFP8 activation tile of a quad in LDS --------
+// With many rows per expert a wave loads as many activation bytes per step as
+// weight bytes, and the four waves of a workgroup load the same rows (from the
+// cache).  Instead the workgroup loads the tile of a quad once: 16*NB rows x
+// 512 E4M3 codes and their 16 E8M0 scale bytes per row, a share per thread,
+// into one of two LDS buffers; the waves read their B operands from there and
+// the register ring holds weights only.  One barrier per quad, as in the
+// NVFP4 path.  A row's 32 chunks of 16 codes sit at chunk ch ^ (row & 15) of
+// its 512 bytes, so the 16 rows a wave's lanes read at one step fall on 16
+// different bank groups.
+constexpr int kTileRowMX = 512;                                  // code bytes per row and quad
+constexpr int kTileCodesMX = kPassRows * kTileRowMX;             // codes of one buffer (two N-blocks)
+constexpr int kTileScalesMX = kPassRows * 16;                    // the rows' scale bytes
+// + a dump area where threads without a scale dword store theirs: every
+// store of the tile is unconditional, so the loop body stays one basic block
+// (a branch there lets the compiler sink the MFMAs past the barriers)
+constexpr int kTileBytesMX = kTileCodesMX + kTileScalesMX + 4 * kThreads;
+
+template <int NB>
+struct ActShareMX {
+    v4i c[2 * NB];  // code chunks of the thread (16 codes each)
+    uint32_t s;     // a scale dword of the thread (threads below 64 * NB)
+};
+
+template <int NB>
+struct TileOffsMX {
+    uint32_t c[2 * NB];  // byte offsets in a_q of the thread's chunks at quad 0 (kOOB past the pass)
+    uint32_t s;          // byte offset in a_s of the thread's scale dword at quad 0 (kOOB: none)
+};
+
+// Chunk k of thread t is row (t + 256k) / 32, codes [16 ch, +16) of the quad,
+// ch = (t + 256k) % 32; thread t < 64 NB loads dword t % 4 of row t / 4's 16
+// scale bytes.  src as in make_coord.
+template <int NB>
+__device__ __forceinline__ TileOffsMX<NB> tile_offsets_mx(int K, int npass, const int* src) {
+    const int t = threadIdx.x;
+    TileOffsMX<NB> o;
+#pragma unroll
+    for (int k = 0; k < 2 * NB; ++k) {
+        const int li = t + kThreads * k, row = li >> 5, ch = li & 31;
+        const uint32_t r = row < npass ? (src ? (uint32_t)src[row] : (uint32_t)row) : 0u;
+        o.c[k] = row < npass ? r * (uint32_t)K + 16 * ch : kOOB;
+    }
+    const int srow = t >> 2;
+    const uint32_t rs = srow < npass ? (src ? (uint32_t)src[srow] : (uint32_t)srow) : 0u;
+    o.s = (t < 64 * NB && srow < npass) ? rs * (uint32_t)(K / 32) + 4 * (t & 3) : kOOB;
+    return o;
+}
+
+// Requests the thread's share of tile q (absolute quad); rows past the pass
+// and steps at or past s_end read zeros.
+template <int NB>
+__device__ __forceinline__ void tile_load_mx(ActShareMX<NB>& P, const Coord<kFmtMX, 1, NB>& c,
+                                             const TileOffsMX<NB>& o, int q, int s_end) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 2 * NB; ++k) {
+        const int ch = (t + kThreads * k) & 31;
+        const bool ok = o.c[k] != kOOB && 4 * q + (ch >> 3) < s_end;
+        P.c[k] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, ok ? o.c[k] + 512 * q : kOOB, 0, 0);
+    }
+    // dword t % 4 holds the scales of step 4q + t % 4
+    const bool oks = o.s != kOOB && 4 * q + (t & 3) < s_end;
+    P.s = __builtin_amdgcn_raw_buffer_load_b32(c.ras, oks ? o.s + 16 * q : kOOB, 0, 0);
+}
+
+template <int NB>
+__device__ __forceinline__ void tile_store_mx(const ActShareMX<NB>& P, uint8_t* buf) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 2 * NB; ++k) {
+        const int li = t + kThreads * k, row = li >> 5, ch = li & 31;
+        *reinterpret_cast<v4i*>(buf + row * kTileRowMX + 16 * (ch ^ (row & 15))) = P.c[k];
+    }
+    *reinterpret_cast<uint32_t*>(buf + kTileCodesMX + (t < 64 * NB ? 4 * t : kTileScalesMX + 4 * t)) = P.s;
+}
+
+// The lane's B operand of step u of the tile in buf for N-block j: row
+// 16j + i, codes [128u + 16g, +16) and [128u + 64 + 16g, +16) (the layout of
+// the FP8 operand of the scaled MFMA), and the row's scale dword of step u.
+template <int NB>
+__device__ __forceinline__ void tile_read_mx(const uint8_t* buf, int u, v8i (&B)[NB], uint32_t (&bs)[NB]) {
+    const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int row = 16 * j + i;
+        const uint8_t* p = buf + row * kTileRowMX;
+        const v4i c0 = *reinterpret_cast<const v4i*>(p + 16 * ((8 * u + g) ^ i));
+        const v4i c1 = *reinterpret_cast<const v4i*>(p + 16 * ((8 * u + 4 + g) ^ i));
+        B[j] = v8i{c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        bs[j] = *reinterpret_cast<const uint32_t*>(buf + kTileCodesMX + 16 * row + 4 * u);
+    }
+}
+
+template <int MB, int NB, int DQ>
+__device__ __forceinline__ void ringw_load_scales_mx(RingW<MB, DQ>& R, int v, const Coord<kFmtMX, MB, NB>& c, int q,
+                                                     int s_end) {
+    const bool okq = 4 * q < s_end;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        R.as[v][mb][0] = __builtin_amdgcn_raw_buffer_load_b32(c.rs, okq ? c.vs[mb] : kOOB, 256 * q, 0);
+}
+
+// The four steps of the quad in slot v, the B operands of step U given and
+// those of step U+1 read from the tile meanwhile; each step's weight slot is
+// refilled with quad qn right after its MFMAs.
+template <int MB, int NB, int DQ, int U>
+__device__ __forceinline__ void quadw_steps_mx(RingW<MB, DQ>& R, int v, const Coord<kFmtMX, MB, NB>& c, int qn,
+                                               int s_end, const uint8_t* tile, const v8i (&B)[NB],
+                                               const uint32_t (&bs)[NB], v4f (&acc)[MB][2]) {
+    if constexpr (U < 4) {
+        __builtin_amdgcn_sched_barrier(0);
+        v8i Bn[NB];
+        uint32_t bsn[NB];
+        if constexpr (U < 3) tile_read_mx<NB>(tile, U + 1, Bn, bsn);
+        const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const v4i a = R.a[v][U][mb];
+            const v8i A = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[j], acc[mb][j], 4, 0, U,
+                                                                              (int)R.as[v][mb][0], 0,
+                                                                              (int)(bs[j] >> (8 * g)));
+        }
+        if constexpr (U == 3) ringw_load_scales_mx<MB, NB, DQ>(R, v, c, qn, s_end);
+        ringw_load_step<MB, NB, DQ>(R, v, U, c, qn, s_end);
+        quadw_steps_mx<MB, NB, DQ, U + 1>(R, v, c, qn, s_end, tile, Bn, bsn, acc);
+    }
+}
+
+// An MXFP4 pass as stream_pass, with the activation tiles in LDS (tiles: two
+// kTileBytesMX buffers).  Every thread of the workgroup must call it with the
+// same arguments apart from the weight blocks (it has barriers).
+template <int MB, int NB, int DQ>
+__device__ __forceinline__ void stream_pass_lds_mx(const StreamJob& J, int e, const int (&wblk)[MB], int arow0,
+                                                   int npass, const int* src, int s0, int nst, v4f (&acc)[MB][2],
+                                                   uint8_t* tiles) {
+    static_assert(DQ % 2 == 0, "slots alternate between the two tile buffers");
+    const Coord<kFmtMX, MB, NB> c = make_coord<kFmtMX, MB, NB>(J, e, wblk, arow0, npass, src);
+    const TileOffsMX<NB> to = tile_offsets_mx<NB>(J.K, npass, src);
+    Coord<kFmtMX, 1, NB> ca;  // the activation resources, for the tile loads
+    ca.ra = c.ra;
+    ca.ras = c.ras;
+    const int q0 = s0 / 4, nq = (nst + 3) / 4, s_end = s0 + nst;
+    ActShareMX<NB> P;
+    tile_load_mx<NB>(P, ca, to, q0, s_end);
+    RingW<MB, DQ> R;
+#pragma unroll
+    for (int v = 0; v < DQ; ++v) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (u == 3) ringw_load_scales_mx<MB, NB, DQ>(R, v, c, q0 + v, s_end);
+            ringw_load_step<MB, NB, DQ>(R, v, u, c, q0 + v, s_end);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[mb][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();  // the previous pass's reads of the LDS are done
+    tile_store_mx<NB>(P, tiles);
+    __syncthreads();
+    for (int l0 = 0; l0 < nq; l0 += DQ) {
+#pragma unroll
+        for (int v = 0; v < DQ; ++v) {
+            const int q = q0 + l0 + v;  // the quad of slot v in this round
+            const uint8_t* tile = tiles + (v & 1) * kTileBytesMX;
+            v8i B[NB];
+            uint32_t bs[NB];
+            tile_read_mx<NB>(tile, 0, B, bs);
+            tile_load_mx<NB>(P, ca, to, q + 1, s_end);  // in flight over the quad's steps
+            quadw_steps_mx<MB, NB, DQ, 0>(R, v, c, q + DQ, s_end, tile, B, bs, acc);
+            // tile q+1 into the other buffer (its reads ended at the last barrier)
+            tile_store_mx<NB>(P, tiles + ((v + 1) & 1) * kTileBytesMX);
+            __syncthreads();
+        }
+    }
+}
+
 // Ring depth in quads for MB weight blocks and NB activation blocks: about
 // 32 loads of 16 bytes per lane in flight (the registers allow two quads
 // with two weight blocks and one activation block).
@@ -936,7 +1125,8 @@ __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS)
     // the activation tiles of two quads in the same LDS: the epilogue runs
     // after the pass's last barrier, when no wave reads a tile any more.
     constexpr int kGBytes = kPassRows * (2 * GCOLS + 1) * 4;
-    constexpr int kLdsBytes = kNVW<FMT> && 2 * kTileBytesH > kGBytes ? 2 * kTileBytesH : kGBytes;
+    constexpr int kTileLds = kNVW<FMT> ? 2 * kTileBytesH : 2 * kTileBytesMX;
+    constexpr int kLdsBytes = kTileLds > kGBytes ? kTileLds : kGBytes;
     __shared__ __align__(16) uint8_t sLds[kLdsBytes];
     float(*sG)[2 * GCOLS + 1] = reinterpret_cast<float(*)[2 * GCOLS + 1]>(sLds);
     __shared__ int s_smax[kPassRows];
@@ -964,9 +1154,10 @@ __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS)
             if constexpr (kNVW<FMT>)
                 stream_pass_lds<GMB, 2, MOE_NV_DQ, kA4<FMT>>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm, acc, sLds,
                                                              s_smax);
-            else
-                stream_pass<FMT, GMB, 2, ring_quads<FMT, GMB, 2>(), 4>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm,
-                                                                         acc);
+            else {
+                stream_pass_lds_mx<GMB, 2, MOE_MX_DQ>(J, tk.e, wblk, arow0, npass, src, s0, nst, acc, sLds);
+                sm[0] = sm[1] = 0;
+            }
             smax[0] = sm[0];
             smax[1] = sm[1];
         } else {
@@ -974,9 +1165,13 @@ __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS)
             if constexpr (kNVW<FMT>)
                 stream_pass_lds<GMB, 1, MOE_NV_DQ, kA4<FMT>>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm, acc, sLds,
                                                              s_smax);
-            else
+            else if (npass >= MOE_MX_LDS_ROWS) {  // uniform: every wave of the workgroup takes the same path
+                stream_pass_lds_mx<GMB, 1, MOE_MX_DQ>(J, tk.e, wblk, arow0, npass, src, s0, nst, acc, sLds);
+                sm[0] = 0;
+            } else {
                 stream_pass<FMT, GMB, 1, ring_quads<FMT, GMB, 1>(), 4>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm,
                                                                          acc);
+            }
             smax[0] = sm[0];
         }
         if constexpr (FUSED) {
