@@ -80,11 +80,11 @@ constexpr int kPassRows = 32;           // activation rows per pass (two 16-row 
 #ifndef MOE_MIN_BLOCKS
 #define MOE_MIN_BLOCKS 2  // workgroups per CU the register budget must allow
 #endif
-#ifndef MOE_MX_LDS_ROWS
-#define MOE_MX_LDS_ROWS 2  // MXFP4 gate_up: passes of at least this many rows take the activation tile in LDS
-#endif
 #ifndef MOE_MX_DQ
 #define MOE_MX_DQ 2  // MXFP4 gate_up with the activation tile in LDS: weight ring depth in quads
+#endif
+#ifndef MOE_MX_DOWN_DQ
+#define MOE_MX_DOWN_DQ 1  // MXFP4 down along K with the h tile in LDS: weight ring depth in quads (four blocks: one)
 #endif
 #ifndef MOE_NV_DQ
 #define MOE_NV_DQ 2  // NVFP4 gate_up: weight ring depth in quads
@@ -838,10 +838,10 @@ __device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const
 // 512 E4M3 codes and their 16 E8M0 scale bytes per row, a share per thread,
 // into one of two LDS buffers; the waves read their B operands from there and
 // the register ring holds weights only.  One barrier per quad, as in the
-// NVFP4 path.  A row's 32 chunks of 16 codes sit at chunk ch ^ (row & 15) of
-// its 512 bytes, so the 16 rows a wave's lanes read at one step fall on 16
-// different bank groups.
-constexpr int kTileRowMX = 512;                                  // code bytes per row and quad
+// NVFP4 path.  Rows are 528 bytes apart (512 codes + 16): the 16 rows a
+// wave's lanes read at one step start on 16 different bank groups, and a
+// lane's reads of the quad's steps are immediate offsets from one address.
+constexpr int kTileRowMX = 528;                                  // row stride of the codes (512 + 16)
 constexpr int kTileCodesMX = kPassRows * kTileRowMX;             // codes of one buffer (two N-blocks)
 constexpr int kTileScalesMX = kPassRows * 16;                    // the rows' scale bytes
 // + a dump area where threads without a scale dword store theirs: every
@@ -903,7 +903,7 @@ __device__ __forceinline__ void tile_store_mx(const ActShareMX<NB>& P, uint8_t* 
 #pragma unroll
     for (int k = 0; k < 2 * NB; ++k) {
         const int li = t + kThreads * k, row = li >> 5, ch = li & 31;
-        *reinterpret_cast<v4i*>(buf + row * kTileRowMX + 16 * (ch ^ (row & 15))) = P.c[k];
+        *reinterpret_cast<v4i*>(buf + row * kTileRowMX + 16 * ch) = P.c[k];
     }
     *reinterpret_cast<uint32_t*>(buf + kTileCodesMX + (t < 64 * NB ? 4 * t : kTileScalesMX + 4 * t)) = P.s;
 }
@@ -917,9 +917,9 @@ __device__ __forceinline__ void tile_read_mx(const uint8_t* buf, int u, v8i (&B)
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
         const int row = 16 * j + i;
-        const uint8_t* p = buf + row * kTileRowMX;
-        const v4i c0 = *reinterpret_cast<const v4i*>(p + 16 * ((8 * u + g) ^ i));
-        const v4i c1 = *reinterpret_cast<const v4i*>(p + 16 * ((8 * u + 4 + g) ^ i));
+        const uint8_t* p = buf + row * kTileRowMX + 16 * g;
+        const v4i c0 = *reinterpret_cast<const v4i*>(p + 128 * u);
+        const v4i c1 = *reinterpret_cast<const v4i*>(p + 128 * u + 64);
         B[j] = v8i{c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
         bs[j] = *reinterpret_cast<const uint32_t*>(buf + kTileCodesMX + 16 * row + 4 * u);
     }
@@ -970,7 +970,6 @@ template <int MB, int NB, int DQ>
 __device__ __forceinline__ void stream_pass_lds_mx(const StreamJob& J, int e, const int (&wblk)[MB], int arow0,
                                                    int npass, const int* src, int s0, int nst, v4f (&acc)[MB][2],
                                                    uint8_t* tiles) {
-    static_assert(DQ % 2 == 0, "slots alternate between the two tile buffers");
     const Coord<kFmtMX, MB, NB> c = make_coord<kFmtMX, MB, NB>(J, e, wblk, arow0, npass, src);
     const TileOffsMX<NB> to = tile_offsets_mx<NB>(J.K, npass, src);
     Coord<kFmtMX, 1, NB> ca;  // the activation resources, for the tile loads
@@ -994,21 +993,22 @@ __device__ __forceinline__ void stream_pass_lds_mx(const StreamJob& J, int e, co
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[mb][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    // the tile of quad q sits in buffer q & 1
     __syncthreads();  // the previous pass's reads of the LDS are done
-    tile_store_mx<NB>(P, tiles);
+    tile_store_mx<NB>(P, tiles + (q0 & 1) * kTileBytesMX);
     __syncthreads();
     for (int l0 = 0; l0 < nq; l0 += DQ) {
 #pragma unroll
         for (int v = 0; v < DQ; ++v) {
             const int q = q0 + l0 + v;  // the quad of slot v in this round
-            const uint8_t* tile = tiles + (v & 1) * kTileBytesMX;
+            const uint8_t* tile = tiles + (q & 1) * kTileBytesMX;
             v8i B[NB];
             uint32_t bs[NB];
             tile_read_mx<NB>(tile, 0, B, bs);
             tile_load_mx<NB>(P, ca, to, q + 1, s_end);  // in flight over the quad's steps
             quadw_steps_mx<MB, NB, DQ, 0>(R, v, c, q + DQ, s_end, tile, B, bs, acc);
             // tile q+1 into the other buffer (its reads ended at the last barrier)
-            tile_store_mx<NB>(P, tiles + ((v + 1) & 1) * kTileBytesMX);
+            tile_store_mx<NB>(P, tiles + ((q + 1) & 1) * kTileBytesMX);
             __syncthreads();
         }
     }
@@ -1154,7 +1154,7 @@ __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS)
             if constexpr (kNVW<FMT>)
                 stream_pass_lds<GMB, 2, MOE_NV_DQ, kA4<FMT>>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm, acc, sLds,
                                                              s_smax);
-            else {
+            else {  // MXFP4: the activation tile in LDS (measured faster from one row per pass up)
                 stream_pass_lds_mx<GMB, 2, MOE_MX_DQ>(J, tk.e, wblk, arow0, npass, src, s0, nst, acc, sLds);
                 sm[0] = sm[1] = 0;
             }
@@ -1165,12 +1165,9 @@ __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS)
             if constexpr (kNVW<FMT>)
                 stream_pass_lds<GMB, 1, MOE_NV_DQ, kA4<FMT>>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm, acc, sLds,
                                                              s_smax);
-            else if (npass >= MOE_MX_LDS_ROWS) {  // uniform: every wave of the workgroup takes the same path
+            else {
                 stream_pass_lds_mx<GMB, 1, MOE_MX_DQ>(J, tk.e, wblk, arow0, npass, src, s0, nst, acc, sLds);
                 sm[0] = 0;
-            } else {
-                stream_pass<FMT, GMB, 1, ring_quads<FMT, GMB, 1>(), 4>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm,
-                                                                         acc);
             }
             smax[0] = sm[0];
         }
@@ -1284,7 +1281,10 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_quant(const float* __restri
 // output rows are a multiple of 256 (each activation load serves twice the
 // weight rows; measured: wide down 478 -> 400 us), else two; NVFP4 two (four
 // would spill: its dequantization needs registers).
-constexpr int kDownMBWide = 4, kDownMB = 2;
+#ifndef MOE_DOWN_MB_WIDE
+#define MOE_DOWN_MB_WIDE 4
+#endif
+constexpr int kDownMBWide = MOE_DOWN_MB_WIDE, kDownMB = 2;
 
 template <int FMT, int MB>
 __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0, float* __restrict__ y0, int nmain,
@@ -1317,6 +1317,9 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0,
     const int nst = I / 128;
     const float gs = kNVW<FMT> ? J.gscale[tk.e] : 1.0f;
     const float fa4 = kA4<FMT> ? act_global(J, tk.e) * gs : 0.0f;  // NVFP4 h: its global x the weights'
+    // MXFP4: the h tiles in LDS (the NVFP4 formats stream h from registers)
+    __shared__ __align__(16) uint8_t sTile[FMT == kFmtMX ? 2 * kTileBytesMX : 16];
+    constexpr int kDownDQ = MB > 2 ? MOE_MX_DOWN_DQ : MOE_MX_DQ;  // ring quads the registers allow
 
     for (int t0 = 0; t0 < tk.n; t0 += kPassRows) {
         const int npass = min(kPassRows, tk.n - t0);
@@ -1331,7 +1334,12 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0,
         }
         v4f acc[MB][2];
         int smax[2] = {0, 0};
-        if (npass > 16) {
+        if constexpr (FMT == kFmtMX) {  // the workgroup shares the h tile in LDS
+            if (npass > 16)
+                stream_pass_lds_mx<MB, 2, kDownDQ>(J, tk.e, wblk, arow0, npass, nullptr, 0, nst, acc, sTile);
+            else
+                stream_pass_lds_mx<MB, 1, kDownDQ>(J, tk.e, wblk, arow0, npass, nullptr, 0, nst, acc, sTile);
+        } else if (npass > 16) {
             int sm[2];
             stream_pass<FMT, MB, 2, ring_quads<FMT, MB, 2>(), 4>(J, tk.e, wblk, arow0, npass, nullptr, 0,
                                                                                  nst, sm, acc);
