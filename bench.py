@@ -213,6 +213,47 @@ def traffic_summary(fetch_dir, write_dir, workload, command):
     return "\n".join(lines)
 
 
+def mfma_summary(pmc_dir, workload, command):
+    """MFMA activity of the routed gate_up and down (each launched on its own
+    by --profile-kernels) from one counter run of SQ_INSTS_MFMA,
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CU_CYCLES and GRBM_GUI_ACTIVE.  Every
+    MFMA of the MXFP4 expert kernels is the scaled 16x16x128 FP4 x FP8 one
+    (65536 FLOP); GRBM_GUI_ACTIVE is summed over the 8 XCDs."""
+    import csv
+    from block_scaled_fp4_sigmoid_amd import synth
+    s = synth.WORKLOADS[workload]
+    U = stored_unique(workload)
+    bm = byte_model(s, U) if U else None
+    vals = {}
+    with open(os.path.join(pmc_dir, "run_counter_collection.csv")) as fh:
+        for r in csv.DictReader(fh):
+            n = r["Kernel_Name"]
+            key = "gate_up" if "k_gate_up" in n else "down" if "k_down" in n else None
+            if key:
+                vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    lines = [f"# MFMA activity of the routed expert GEMMs, {workload}", "",
+             "Command (from the repository root, on one MI355X):", "", "```", command, "```", "",
+             "Each kernel launched on its own (`--profile-kernels`), rotating over the bench's weight copies. "
+             "Useful FLOP = 2 x pairs x N x K over the real rows; the rest of the issued FLOP pads each "
+             "expert's rows to 16-row MFMA tiles.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x "
+             "GRBM_GUI_ACTIVE / 8).", "",
+             "| kernel | dispatches | MFMA instr. | issued FLOP | useful FLOP | useful / issued | MFMA busy |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for key, useful in (("gate_up", bm and bm["gate_up_flop"]), ("down", bm and bm["down_flop"])):
+        c = vals.get(key)
+        if not c:
+            continue
+        mean = {k: float(np.mean(v)) for k, v in c.items()}
+        n = len(c.get("SQ_INSTS_MFMA", []))
+        issued = mean.get("SQ_INSTS_MFMA", 0.0) * 65536
+        busy = mean.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (1024 * mean.get("GRBM_GUI_ACTIVE", 1.0) / 8)
+        lines.append(f"| routed {key} | {n} | {mean.get('SQ_INSTS_MFMA', 0):.4g} | {issued:.4g} | "
+                     f"{useful if useful else float('nan'):.4g} | {useful / issued if useful and issued else float('nan'):.0%} | "
+                     f"{busy:.1%} |")
+    lines += ["", f"unique_experts: {U}", f"kernel_sources_sha256_16: {kernel_sources_sha()}", ""]
+    return "\n".join(lines)
+
+
 def _read_keys(path):
     vals = {}
     if not os.path.exists(path):
@@ -606,11 +647,16 @@ def main():
                     help="write the traffic summary of two rocprofv3 counter runs to stdout")
     ap.add_argument("--kernel-summary", nargs=2, metavar=("ROCPD_DB", "TITLE"),
                     help="write the summary of a rocprofv3 kernel trace to stdout")
+    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
+                    help="write the MFMA counter summary of a --profile-kernels counter run to stdout")
     ap.add_argument("--summary-command", default="", help="the commands to record in a summary")
     args = ap.parse_args()
     if args.traffic_summary:
         print(traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload,
                               args.summary_command))
+        return
+    if args.mfma_summary:
+        print(mfma_summary(args.mfma_summary, args.workload, args.summary_command))
         return
     if args.kernel_summary:
         print(kernel_summary(args.kernel_summary[0], args.kernel_summary[1], args.summary_command), end="")

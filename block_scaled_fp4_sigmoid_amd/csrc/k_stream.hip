@@ -1287,14 +1287,8 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_quant(const float* __restri
 constexpr int kDownMBWide = MOE_DOWN_MB_WIDE, kDownMB = 2;
 
 template <int FMT, int MB>
-__global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0, float* __restrict__ y0, int nmain,
-                                                                   moe_routing ride, int ride_E, StreamJob J2,
+__global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0, float* __restrict__ y0, StreamJob J2,
                                                                    float* __restrict__ y2, int n2) {
-    if ((int)blockIdx.x >= nmain) {  // the route step riding along (it writes only the routing arrays)
-        extern __shared__ __align__(16) uint8_t s_dyn[];
-        bucket_step(J0.M, ride_E, J0.k, ride, s_dyn);
-        return;
-    }
     // workgroups [0, n2) take items of a second job J2 (first: its few long
     // items would otherwise trail the launch), [n2, nmain) items of J0
     const bool second = (int)blockIdx.x < n2;  // uniform
@@ -1407,13 +1401,7 @@ __device__ __forceinline__ void rows_steps(v4f& acc, const v4i (&wa)[D][S], cons
 // 4 * bpw blocks); wave w takes blocks [w * bpw, (w + 1) * bpw) of the run.
 // Passes of 16 activation rows; a later pass reads the item's weights again.
 template <int FMT, int S, int D>
-__global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down_rows(StreamJob J, float* __restrict__ y,
-                                                                        int nmain, moe_routing ride, int ride_E) {
-    if ((int)blockIdx.x >= nmain) {  // the route step riding along (it writes only the routing arrays)
-        extern __shared__ __align__(16) uint8_t s_dyn[];
-        bucket_step(J.M, ride_E, J.k, ride, s_dyn);
-        return;
-    }
+__global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down_rows(StreamJob J, float* __restrict__ y) {
     const int H = J.N, K = J.K;
     const int bpw = J.span;
     const int item = blockIdx.x % J.nblk;
@@ -1541,6 +1529,9 @@ struct GatePlan {
 
 // Weight blocks per wave of a gate_up launch (see kGateMB).
 int gate_mb(const ExpertJob& j) {
+#ifdef MOE_GATE_MB_FORCE
+    return MOE_GATE_MB_FORCE;
+#endif
     return (long)grid_slots(j) * (j.N_out / (32 * kGateMB)) <= 256 ? kGateMBSmall : kGateMB;
 }
 
@@ -1677,27 +1668,8 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
 
 // Down by rows (K of at most one quad): blocks per wave and items per slot so
 // that about two workgroups per CU stream runs of equal length.
-// The route step rides along as one extra workgroup when ride != nullptr.
-struct DownRide {
-    moe_routing route;
-    int E;
-    int blocks;     // 0 or 1
-    size_t lds;     // dynamic LDS bytes of the launch
-};
-
-DownRide down_ride(const moe_routing* ride, int E, int k) {
-    DownRide d{};
-    if (ride) {
-        d.route = *ride;
-        d.E = E;
-        d.blocks = 1;
-        d.lds = bucket_lds_bytes(E, k);
-    }
-    return d;
-}
-
 template <int FMT, int S>
-hipError_t launch_down_rows_s(StreamJob J, int slots, float* y, const DownRide& dr, hipStream_t stream) {
+hipError_t launch_down_rows_s(StreamJob J, int slots, float* y, hipStream_t stream) {
     constexpr int D = 4;  // blocks in flight per wave (deeper rings measured slower)
     const int nbr = J.N / 16;
     int items = std::max(1, std::min(MOE_ROWS_TARGET_WGS / std::max(1, slots), nbr / (4 * D)));
@@ -1709,25 +1681,23 @@ hipError_t launch_down_rows_s(StreamJob J, int slots, float* y, const DownRide& 
     J.span = bpw;
     J.nblk = items;
     const int nmain = slots * items;
-    hipLaunchKernelGGL((k_down_rows<FMT, S, D>), dim3(nmain + dr.blocks), dim3(kThreads), dr.lds, stream, J, y, nmain,
-                       dr.route, dr.E);
+    hipLaunchKernelGGL((k_down_rows<FMT, S, D>), dim3(nmain), dim3(kThreads), 0, stream, J, y);
     return hipGetLastError();
 }
 
 template <int FMT>
-hipError_t launch_down_rows(const StreamJob& J, int slots, float* y, const DownRide& dr, hipStream_t stream) {
+hipError_t launch_down_rows(const StreamJob& J, int slots, float* y, hipStream_t stream) {
     switch (J.K / 128) {
-        case 1: return launch_down_rows_s<FMT, 1>(J, slots, y, dr, stream);
-        case 2: return launch_down_rows_s<FMT, 2>(J, slots, y, dr, stream);
-        case 3: return launch_down_rows_s<FMT, 3>(J, slots, y, dr, stream);
-        default: return launch_down_rows_s<FMT, 4>(J, slots, y, dr, stream);
+        case 1: return launch_down_rows_s<FMT, 1>(J, slots, y, stream);
+        case 2: return launch_down_rows_s<FMT, 2>(J, slots, y, stream);
+        case 3: return launch_down_rows_s<FMT, 3>(J, slots, y, stream);
+        default: return launch_down_rows_s<FMT, 4>(J, slots, y, stream);
     }
 }
 
 hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8_t* h_s, float* y,
-                           hipStream_t stream, const moe_routing* ride_route, int E, const SecondDown& second) {
+                           hipStream_t stream, const SecondDown& second) {
     StreamJob J = stream_job(job, job.N_out, h_q, h_s, out_rows_of(job));
-    const DownRide dr = down_ride(ride_route, E, job.k);
     // a second job rides along when both stream along K with the same format
     const bool fold = second.job && job.K > 512 && second.job->K > 512 && second.job->w.fmt == job.w.fmt &&
                       second.job->a_nvfp4 == job.a_nvfp4;
@@ -1736,9 +1706,9 @@ hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8
         if (e != hipSuccess) return e;
     }
     if (job.K <= 512)  // all of K in one quad: stream along the rows
-        return job.a_nvfp4                 ? launch_down_rows<kFmtNV4>(J, grid_slots(job), y, dr, stream)
-               : job.w.fmt == MOE_FMT_MXFP4 ? launch_down_rows<kFmtMX>(J, grid_slots(job), y, dr, stream)
-                                            : launch_down_rows<kFmtNV>(J, grid_slots(job), y, dr, stream);
+        return job.a_nvfp4                 ? launch_down_rows<kFmtNV4>(J, grid_slots(job), y, stream)
+               : job.w.fmt == MOE_FMT_MXFP4 ? launch_down_rows<kFmtMX>(J, grid_slots(job), y, stream)
+                                            : launch_down_rows<kFmtNV>(J, grid_slots(job), y, stream);
     const bool mx = job.w.fmt == MOE_FMT_MXFP4;
     const bool wide = mx && job.N_out % (64 * kDownMBWide) == 0;
     const int dmb = wide ? kDownMBWide : kDownMB;
@@ -1754,15 +1724,15 @@ hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8
     }
     float* y2 = fold ? second.y : y;
     const int nmain = n1 + n2;
-    const dim3 g(nmain + dr.blocks), b(kThreads);
+    const dim3 g(nmain), b(kThreads);
     if (wide)
-        hipLaunchKernelGGL((k_down<kFmtMX, kDownMBWide>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E, J2, y2, n2);
+        hipLaunchKernelGGL((k_down<kFmtMX, kDownMBWide>), g, b, 0, stream, J, y, J2, y2, n2);
     else if (mx)
-        hipLaunchKernelGGL((k_down<kFmtMX, kDownMB>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E, J2, y2, n2);
+        hipLaunchKernelGGL((k_down<kFmtMX, kDownMB>), g, b, 0, stream, J, y, J2, y2, n2);
     else if (job.a_nvfp4)
-        hipLaunchKernelGGL((k_down<kFmtNV4, kDownMB>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E, J2, y2, n2);
+        hipLaunchKernelGGL((k_down<kFmtNV4, kDownMB>), g, b, 0, stream, J, y, J2, y2, n2);
     else
-        hipLaunchKernelGGL((k_down<kFmtNV, kDownMB>), g, b, dr.lds, stream, J, y, nmain, dr.route, dr.E, J2, y2, n2);
+        hipLaunchKernelGGL((k_down<kFmtNV, kDownMB>), g, b, 0, stream, J, y, J2, y2, n2);
     return hipGetLastError();
 }
 

@@ -570,9 +570,11 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
     const bool fp4_shared = sf != MOE_FMT_NONE && !shb;
     if (M * k <= kSmallPairs) {
         // Five launches: (router + token-order MXFP8 of x) -> top-k -> gate_up
-        // (workgroups resolve their expert from the ids and gather token rows)
-        // -> down (the route step rides along) -> finalize.  The bf16 shared
-        // expert's stages ride along the first three.
+        // (workgroups resolve their expert from the ids, in the route step's
+        // order, and gather token rows; one per slot records it) -> down
+        // (slots from the record) -> finalize.  No bucket or 8-row tiles are
+        // materialized: nothing in these launches reads them.  The bf16 or
+        // static-FP8 shared expert's stages ride along the first three.
         hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, L.xqt, L.xst, s1,
                                               shb ? kBf16GateUp : kBf16None, stream, xg4);
         if (e == hipSuccess)
@@ -601,7 +603,7 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
         dn.active_offsets = rec.off;
         dn.bucket = rec.bkt;
         dn.count = rec.na;
-        if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream, &r, E, s_dn);
+        if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream, s_dn);
         if (e == hipSuccess)
             e = launch_finalize(L.y, r.topk_w, L.ysh, residual, d->gamma, d->eps, M, H, k, out, residual_out,
                                 out_q, out_s, stream);
@@ -628,7 +630,7 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
         e = launch_gate_up_fp4(gu, L.xqt, L.xst, L.hq, L.hs, L.part, stream, no_side(), kBf16None, s_gu);
     ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);
     set_a4(dn, d, false, false);
-    if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream, nullptr, 0, s_dn);
+    if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream, s_dn);
     if (e == hipSuccess)
         e = launch_finalize(L.y, r.topk_w, L.ysh, residual, d->gamma, d->eps, M, H, k, out, residual_out,
                             out_q, out_s, stream);

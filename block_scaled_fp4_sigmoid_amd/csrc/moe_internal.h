@@ -158,16 +158,14 @@ struct SecondDown {
     float* y = nullptr;
 };
 
-// A bf16 shared-expert stage may ride along the gate_up launch (side, stage),
-// and the route step along the down launch (ride_route != nullptr: it writes
-// the routing arrays from ride_route->topk_ids for E experts).
+// A bf16 or static-FP8 shared-expert stage may ride along the gate_up launch
+// (side, stage).
 size_t gate_up_fp4_partials_bytes(const ExpertJob& job);
 hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const uint8_t* a_s,
                               uint8_t* h_q, uint8_t* h_s, float* partials, hipStream_t stream,
                               const Bf16Side& side = Bf16Side{}, int stage = 0, const SecondJob& second = SecondJob{});
 hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8_t* h_s,
-                           float* y, hipStream_t stream, const moe_routing* ride_route = nullptr, int E = 0,
-                           const SecondDown& second = SecondDown{});
+                           float* y, hipStream_t stream, const SecondDown& second = SecondDown{});
 
 size_t gate_up_bf16_partials_bytes(int M, int H, int I);
 Bf16Side bf16_side(const ExpertJob& gate_up_or_down, int I, int H, int M, const uint16_t* x, float* part,
