@@ -206,40 +206,42 @@ __device__ __forceinline__ void take_if(Cand& dst, const Cand& src, bool c) {
     dst.id = c ? src.id : dst.id;
 }
 
-// The candidate of another lane through one DPP move (all three words);
-// lanes outside row_mask keep their own.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ Cand dpp_cand(const Cand& c) {
-    const int h = (int)(uint32_t)(c.key >> 32), l = (int)(uint32_t)c.key;
-    Cand o;
-    o.key = ((uint64_t)(uint32_t)__builtin_amdgcn_update_dpp(h, h, CTRL, ROW_MASK, 0xF, false) << 32) |
-            (uint32_t)__builtin_amdgcn_update_dpp(l, l, CTRL, ROW_MASK, 0xF, false);
-    o.id = __builtin_amdgcn_update_dpp(c.id, c.id, CTRL, ROW_MASK, 0xF, false);
-    return o;
-}
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void dpp_best(Cand& c) {
-    const Cand o = dpp_cand<CTRL, ROW_MASK>(c);
-    take_if(c, o, better(o, c));
+// Wave-wide max / min of a 32-bit value, returned uniform.  Inside each row
+// of 16 lanes four DPP exchanges (pair swap, quad half swap, half-row mirror,
+// row mirror) leave the row's result in every lane of the row; two row
+// broadcasts then carry it to lane 63 (rows 1 and 3 take lane 15 of the row
+// before them, rows 2 and 3 take lane 31).
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+    // lanes a move does not write take the identity (0 for max, ~0 for min),
+    // so each move folds into the max / min as one DPP instruction
+    constexpr int id = MAX ? 0 : -1;
+    auto step = [](uint32_t a, int b) { return MAX ? max(a, (uint32_t)b) : min(a, (uint32_t)b); };
+    v = step(v, __builtin_amdgcn_update_dpp(id, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    v = step(v, __builtin_amdgcn_update_dpp(id, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    v = step(v, __builtin_amdgcn_update_dpp(id, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = step(v, __builtin_amdgcn_update_dpp(id, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    v = step(v, __builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+    v = step(v, __builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Best candidate of the wave, returned uniform.  Inside each row of 16 lanes
-// four DPP exchanges (pair swap, quad half swap, half-row mirror, row mirror)
-// leave the row's best in every lane of the row; two row broadcasts then carry
-// it to lane 63 (rows 1 and 3 take lane 15 of the row before them, rows 2 and
-// 3 take lane 31).
-__device__ __forceinline__ Cand wave_best(Cand c) {
-    dpp_best<0xB1, 0xF>(c);   // quad_perm [1,0,3,2]
-    dpp_best<0x4E, 0xF>(c);   // quad_perm [2,3,0,1]
-    dpp_best<0x141, 0xF>(c);  // row_half_mirror
-    dpp_best<0x140, 0xF>(c);  // row_mirror
-    dpp_best<0x142, 0xA>(c);  // row_bcast:15
-    dpp_best<0x143, 0xC>(c);  // row_bcast:31
-    Cand w;
-    w.key = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(c.key >> 32), 63) << 32) |
-            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)c.key, 63);
-    w.id = __builtin_amdgcn_readlane(c.id, 63);
-    return w;
+// The lane holding the wave's best candidate (larger key, then smaller id),
+// uniform.  The high key words decide almost always: the max of the high
+// words, and the low words (then the ids) only among the lanes tied on it.
+__device__ __forceinline__ int wave_best_lane(const Cand& c) {
+    const uint32_t hi = (uint32_t)(c.key >> 32), lo = (uint32_t)c.key;
+    const uint32_t H = wave_reduce_u32<true>(hi);
+    uint64_t tied = __ballot(hi == H);
+    if (__popcll(tied) > 1) {  // uniform
+        const uint32_t L = wave_reduce_u32<true>(hi == H ? lo : 0u);
+        tied = __ballot(hi == H && lo == L);
+        if (__popcll(tied) > 1) {
+            const uint32_t id = wave_reduce_u32<false>((hi == H && lo == L) ? (uint32_t)c.id : 0xffffffffu);
+            tied = __ballot(hi == H && lo == L && (uint32_t)c.id == id);
+        }
+    }
+    return __ffsll((unsigned long long)tied) - 1;
 }
 
 // Top-k of one row by wave 0: lane l holds experts l + 64t (t < KT) sorted
@@ -272,12 +274,13 @@ __device__ int select_topk(const uint64_t* s_ord, int E, int k, int lane) {
             }
     int my_id = 0;
     for (int j = 0; j < k; ++j) {
-        const Cand w = wave_best(c[0]);
-        const bool mine = (w.id & 63) == lane;
+        const int wl = wave_best_lane(c[0]);
+        const int wid = __builtin_amdgcn_readlane(c[0].id, wl);
+        const bool mine = wl == lane;
 #pragma unroll
         for (int t = 0; t + 1 < KT; ++t) take_if(c[t], c[t + 1], mine);
         c[KT - 1].key = mine ? 0 : c[KT - 1].key;
-        my_id = lane == j ? w.id : my_id;
+        my_id = lane == j ? wid : my_id;
     }
     return my_id;
 }
