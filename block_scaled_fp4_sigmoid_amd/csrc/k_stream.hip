@@ -1286,7 +1286,16 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_quant(const float* __restri
 #endif
 constexpr int kDownMBWide = MOE_DOWN_MB_WIDE, kDownMB = 2;
 
-template <int FMT, int MB>
+// y of at least this many bytes is written with non-temporal stores (NTY).
+// Measured at 384 rows (88 MB of y): the cached stores left y's lines dirty
+// in the caches and their write-back landed in the next step's gate_up
+// (634.8 -> 613.6 us with NTY, the finalize 21.0 -> 24.6 us: y comes from
+// HBM); at 16 or fewer rows (y of 2-8 MB) the finalize's cache hits win.
+#ifndef MOE_NT_Y_BYTES
+#define MOE_NT_Y_BYTES (32u << 20)
+#endif
+
+template <int FMT, int MB, bool NTY>
 __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0, float* __restrict__ y0, StreamJob J2,
                                                                    float* __restrict__ y2, int n2) {
     // workgroups [0, n2) take items of a second job J2 (first: its few long
@@ -1354,7 +1363,11 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0,
                     v4f v = acc[mb][j];
                     if (FMT == kFmtNV) v = v * nv_row_factor(smax[j], gs);
                     if (kA4<FMT>) v = v * fa4;
-                    *reinterpret_cast<v4f*>(y + (size_t)orow[j] * H + f0 + 16 * mb + 4 * g) = v;
+                    v4f* dst = reinterpret_cast<v4f*>(y + (size_t)orow[j] * H + f0 + 16 * mb + 4 * g);
+                    if constexpr (NTY)
+                        __builtin_nontemporal_store(v, dst);
+                    else
+                        *dst = v;
                 }
             }
         }
@@ -1695,6 +1708,13 @@ hipError_t launch_down_rows(const StreamJob& J, int slots, float* y, hipStream_t
     }
 }
 
+template <int FMT, int MB, bool NTY>
+hipError_t launch_down_k(dim3 g, hipStream_t stream, const StreamJob& J, float* y, const StreamJob& J2, float* y2,
+                         int n2) {
+    hipLaunchKernelGGL((k_down<FMT, MB, NTY>), g, dim3(kThreads), 0, stream, J, y, J2, y2, n2);
+    return hipGetLastError();
+}
+
 hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8_t* h_s, float* y,
                            hipStream_t stream, const SecondDown& second) {
     StreamJob J = stream_job(job, job.N_out, h_q, h_s, out_rows_of(job));
@@ -1725,15 +1745,18 @@ hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8
     float* y2 = fold ? second.y : y;
     const int nmain = n1 + n2;
     const dim3 g(nmain), b(kThreads);
+    const bool nty = (size_t)out_rows_of(job) * job.N_out * sizeof(float) >= MOE_NT_Y_BYTES;
     if (wide)
-        hipLaunchKernelGGL((k_down<kFmtMX, kDownMBWide>), g, b, 0, stream, J, y, J2, y2, n2);
-    else if (mx)
-        hipLaunchKernelGGL((k_down<kFmtMX, kDownMB>), g, b, 0, stream, J, y, J2, y2, n2);
-    else if (job.a_nvfp4)
-        hipLaunchKernelGGL((k_down<kFmtNV4, kDownMB>), g, b, 0, stream, J, y, J2, y2, n2);
-    else
-        hipLaunchKernelGGL((k_down<kFmtNV, kDownMB>), g, b, 0, stream, J, y, J2, y2, n2);
-    return hipGetLastError();
+        return nty ? launch_down_k<kFmtMX, kDownMBWide, true>(g, stream, J, y, J2, y2, n2)
+                   : launch_down_k<kFmtMX, kDownMBWide, false>(g, stream, J, y, J2, y2, n2);
+    if (mx)
+        return nty ? launch_down_k<kFmtMX, kDownMB, true>(g, stream, J, y, J2, y2, n2)
+                   : launch_down_k<kFmtMX, kDownMB, false>(g, stream, J, y, J2, y2, n2);
+    if (job.a_nvfp4)
+        return nty ? launch_down_k<kFmtNV4, kDownMB, true>(g, stream, J, y, J2, y2, n2)
+                   : launch_down_k<kFmtNV4, kDownMB, false>(g, stream, J, y, J2, y2, n2);
+    return nty ? launch_down_k<kFmtNV, kDownMB, true>(g, stream, J, y, J2, y2, n2)
+               : launch_down_k<kFmtNV, kDownMB, false>(g, stream, J, y, J2, y2, n2);
 }
 
 }  // namespace moe
