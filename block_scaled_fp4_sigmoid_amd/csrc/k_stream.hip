@@ -1277,12 +1277,14 @@ __global__ __launch_bounds__(kThreads) void k_swiglu_quant(const float* __restri
 // Activations are h rows in bucket order; the output row of bucket position b
 // is its pair id bucket[b] (the token row for a dense expert).
 
-// 16-row weight blocks per wave in down along K: MXFP4 takes four when the
-// output rows are a multiple of 256 (each activation load serves twice the
-// weight rows; measured: wide down 478 -> 400 us), else two; NVFP4 two (four
-// would spill: its dequantization needs registers).
+// 16-row weight blocks per wave in down along K: two, with two quads of
+// weights in flight.  Four blocks (one quad in flight, the activation tile
+// serving twice the weight rows) measured slower once y of 384 rows is
+// written non-temporally: wide down 342 us with two against 359 with four,
+// decode 137 against 140.  NVFP4 two (four would spill: its dequantization
+// needs registers).
 #ifndef MOE_DOWN_MB_WIDE
-#define MOE_DOWN_MB_WIDE 4
+#define MOE_DOWN_MB_WIDE 2
 #endif
 constexpr int kDownMBWide = MOE_DOWN_MB_WIDE, kDownMB = 2;
 
