@@ -24,11 +24,19 @@ namespace moe {
 // group); each writes partial logits for its K chunk, which the top-k step
 // sums in chunk order (deterministic, no atomics).
 
+#ifndef MOE_ROUTER_UNITS
+#define MOE_ROUTER_UNITS 1024  // router waves to aim for: 16-expert tiles x K splits x row groups
+#endif
+#ifndef MOE_ROUTER_NBT
+#define MOE_ROUTER_NBT 4  // 16-row blocks per router wave above 16 rows
+#endif
+constexpr int kRouterNBT = MOE_ROUTER_NBT;
+
 RouterPlan router_plan(int M, int H, int E) {
     const int et = (E + 15) / 16;
-    const int rg = (M + 63) / 64;
+    const int rg = M <= 16 ? 1 : (M + 16 * kRouterNBT - 1) / (16 * kRouterNBT);  // row groups of the waves
     const int nsteps = H / 128;  // chunks are whole multiples of 4 K-steps of 32
-    const int want = std::max(1, 1024 / (et * rg));
+    const int want = std::max(1, MOE_ROUTER_UNITS / (et * rg));
     int splits = 1;
     for (int d = 1; d <= nsteps; ++d)
         if (nsteps % d == 0 && d <= want && d <= 32) splits = d;
@@ -47,8 +55,8 @@ __device__ __forceinline__ void split3(float w, uint32_t& b1, uint32_t& b2, uint
     b3 = __float_as_uint(w3) >> 16;
 }
 
-// U: K-steps of 32 whose loads are issued together (a chunk of 256 takes one
-// round of loads); NBT: 16-row blocks of the row group (1 when M <= 16).
+// U: K-steps of 32 per round of loads (two rounds in flight); NBT: 16-row
+// blocks of the row group (1 when M <= 16).
 template <int U, int NBT>
 __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restrict__ x,
                                                          const float* __restrict__ w_router,
@@ -82,7 +90,7 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
     const int e = te * 16 + i;
     const bool ev = e < E;
     const float* wrow = w_router + (size_t)(ev ? e : 0) * H;
-    const int r0 = rgi * 64;
+    const int r0 = rgi * 16 * NBT;
     const int nb = min(NBT, (M - r0 + 15) / 16);
     const uint16_t* xr[NBT];
     bool xv[NBT];
@@ -96,27 +104,32 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
 #pragma unroll
     for (int j = 0; j < NBT; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    const int kbeg = kc * kchunk;
-    for (int k0 = kbeg; k0 < kbeg + kchunk; k0 += 32 * U) {
+    // K rounds of U steps of 32, software-pipelined over two buffers: the
+    // loads of round r + 1 are in flight while round r's MFMAs run.  The
+    // chunk holds an even number of rounds (the launch picks U so that 64 U
+    // divides kchunk), and every load is unconditional: lanes past E or rows
+    // past M read row 0 and are zeroed by a select, so no branch separates an
+    // MFMA from the read of its accumulator.
+    struct Round {
         float4 wl[U][2];
         v4i xb[U][NBT];
+    };
+    auto load = [&](int k0, Round& R) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int kk = k0 + 32 * u + 8 * g;
-            if (ev) {
-                wl[u][0] = *reinterpret_cast<const float4*>(wrow + kk);
-                wl[u][1] = *reinterpret_cast<const float4*>(wrow + kk + 4);
-            } else {
-                wl[u][0] = wl[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+            R.wl[u][0] = *reinterpret_cast<const float4*>(wrow + kk);
+            R.wl[u][1] = *reinterpret_cast<const float4*>(wrow + kk + 4);
 #pragma unroll
-            for (int j = 0; j < NBT; ++j)
-                xb[u][j] = (j < nb && xv[j]) ? load16(xr[j] + kk) : v4i{0, 0, 0, 0};
+            for (int j = 0; j < NBT; ++j) R.xb[u][j] = load16(xr[j] + kk);
         }
+    };
+    auto compute = [&](const Round& R) {
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float wv[8] = {wl[u][0].x, wl[u][0].y, wl[u][0].z, wl[u][0].w,
-                                 wl[u][1].x, wl[u][1].y, wl[u][1].z, wl[u][1].w};
+            const float4 w0 = ev ? R.wl[u][0] : z, w1 = ev ? R.wl[u][1] : z;
+            const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
             uint32_t p1[4], p2[4], p3[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -130,18 +143,41 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
             const v8bf A1 = __builtin_bit_cast(v8bf, v4i{(int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]});
             const v8bf A2 = __builtin_bit_cast(v8bf, v4i{(int)p2[0], (int)p2[1], (int)p2[2], (int)p2[3]});
             const v8bf A3 = __builtin_bit_cast(v8bf, v4i{(int)p3[0], (int)p3[1], (int)p3[2], (int)p3[3]});
-            // every block runs its MFMAs (blocks past the rows multiply the
-            // zeros loaded for them): no branch between an MFMA and the reads
-            // of its accumulator
+            // every block runs its MFMAs (blocks past the rows multiply zeros)
 #pragma unroll
             for (int j = 0; j < NBT; ++j) {
-                const v8bf b = __builtin_bit_cast(v8bf, xb[u][j]);
+                const v8bf b = __builtin_bit_cast(v8bf, (j < nb && xv[j]) ? R.xb[u][j] : v4i{0, 0, 0, 0});
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, acc[j], 0, 0, 0);
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, b, acc[j], 0, 0, 0);
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3, b, acc[j], 0, 0, 0);
             }
         }
+    };
+    const int kbeg = kc * kchunk, kend = kbeg + kchunk;
+    constexpr int KR = 32 * U;  // K per round
+    Round RA, RB;
+    load(kbeg, RA);
+    // (scheduling barriers keep each round's loads behind the previous
+    // round's, so a round's MFMAs wait only for their own loads; the last
+    // pair of rounds is peeled, so no load is issued past the chunk)
+    int k0 = kbeg;
+    for (; k0 + 2 * KR < kend; k0 += 2 * KR) {
+        __builtin_amdgcn_sched_barrier(0);
+        load(k0 + KR, RB);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(RA);
+        __builtin_amdgcn_sched_barrier(0);
+        load(k0 + 2 * KR, RA);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(RB);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load(k0 + KR, RB);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(RA);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(RB);
+    __builtin_amdgcn_sched_barrier(0);
     // lane holds D[4g + t][i]: expert te*16 + 4g + t, row r0 + 16j + i; stores
     // of rows past M or experts past E go to an offset past the buffer (dropped)
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(partials, (uint32_t)splits * (uint32_t)M * (uint32_t)E * 4u);
@@ -165,15 +201,18 @@ hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int 
     const int nquant = xq ? (M * (H / (xg4 > 0.0f ? 16 : 32)) + 255) / 256 : 0;
     const int extra = stage1 == kBf16None ? 0 : side1.blocks;
     const dim3 g(blocks + nquant + extra), b(256);
-    const bool wide = plan.kchunk % 256 == 0, one = M <= 16;  // (four row blocks keep U = 4: registers)
+    // rounds of 128 K when a chunk holds pairs of them, else of 64 K (chunks
+    // are multiples of 128); four row blocks take rounds of 64 K (registers)
+    if (plan.kchunk % 128 != 0) return hipErrorInvalidValue;
+    const bool wide = plan.kchunk % 256 == 0, one = M <= 16;
     if (wide && one)
-        hipLaunchKernelGGL((k_router_partials<8, 1>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
-                           units, blocks, partials, nquant, xq, xs, xg4, side1, stage1);
-    else if (one)
         hipLaunchKernelGGL((k_router_partials<4, 1>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
                            units, blocks, partials, nquant, xq, xs, xg4, side1, stage1);
+    else if (one)
+        hipLaunchKernelGGL((k_router_partials<2, 1>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
+                           units, blocks, partials, nquant, xq, xs, xg4, side1, stage1);
     else
-        hipLaunchKernelGGL((k_router_partials<4, 4>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
+        hipLaunchKernelGGL((k_router_partials<2, kRouterNBT>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
                            units, blocks, partials, nquant, xq, xs, xg4, side1, stage1);
     return hipGetLastError();
 }
