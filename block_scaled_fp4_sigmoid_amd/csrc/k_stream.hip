@@ -1547,7 +1547,11 @@ int gate_mb(const ExpertJob& j) {
 #ifdef MOE_GATE_MB_FORCE
     return MOE_GATE_MB_FORCE;
 #endif
-    return (long)grid_slots(j) * (j.N_out / (32 * kGateMB)) <= 256 ? kGateMBSmall : kGateMB;
+    // one block when a two-block grid would not reach one workgroup per CU, or
+    // when it would spill just past one round of resident workgroups (two per
+    // CU): then half-size items shorten the tail
+    const long items = (long)grid_slots(j) * (j.N_out / (32 * kGateMB));
+    return items <= 256 || (items > 512 && items <= 768) ? kGateMBSmall : kGateMB;
 }
 
 GatePlan gate_plan(const ExpertJob& j, int gmb) {
