@@ -155,23 +155,26 @@ __device__ __forceinline__ bool resolve(const StreamJob& J, int slot, Tokens& t)
     return true;
 }
 
-// Slot -> (expert, bucket range) from the top-k ids, for P = M*k <= kThreads
-// pairs: the slot-th chosen expert in ascending id order, its bucket base
-// (the pairs with a smaller expert) and its pairs in ascending order (list,
-// LDS; tok[t] = list[t] / k), the order the route step writes.  One bitmap of
-// the chosen experts in LDS, a scan of its word counts in one wave, and one
-// ballot per wave for the pairs below and at the expert.  Every thread of the
-// workgroup calls it (it has barriers); the result is uniform.
-static_assert(kSmallPairs == kThreads, "one thread per pair resolves a slot");
+// Slot -> (expert, bucket range) from the top-k ids, for P = M*k <= kIdsPairs
+// pairs (two per thread: pairs tid and tid + kThreads): the slot-th chosen
+// expert in ascending id order, its bucket base (the pairs with a smaller
+// expert) and its pairs in ascending order (list, LDS; tok[t] = list[t] / k),
+// the order the route step writes.  One bitmap of the chosen experts in LDS,
+// a scan of its word counts in one wave, and per wave one ballot per pair set
+// for the pairs below and at the expert.  Every thread of the workgroup calls
+// it (it has barriers); the result is uniform.
+static_assert(kIdsPairs == 2 * kThreads, "two pairs per thread resolve a slot");
 __device__ __forceinline__ bool resolve_ids(const StreamJob& J, int slot, Tokens& t, int* list, int* tok) {
     __shared__ uint32_t s_bm[kMaxE / 32];
-    __shared__ int s_cnt[kThreads / 64][2];
+    __shared__ int s_cnt[kThreads / 64][3];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = J.M * J.k;
-    const int id = tid < P ? J.ids[tid] : -1;
+    const int id0 = tid < P ? J.ids[tid] : -1;
+    const int id1 = tid + kThreads < P ? J.ids[tid + kThreads] : -1;
     if (tid < kMaxE / 32) s_bm[tid] = 0u;
     __syncthreads();
-    if (id >= 0) atomicOr(&s_bm[id >> 5], 1u << (id & 31));
+    if (id0 >= 0) atomicOr(&s_bm[id0 >> 5], 1u << (id0 & 31));
+    if (id1 >= 0) atomicOr(&s_bm[id1 >> 5], 1u << (id1 & 31));
     __syncthreads();
     const uint32_t word = lane < kMaxE / 32 ? s_bm[lane] : 0u;
     int incl = __popc(word);  // inclusive count of chosen experts up to this word
@@ -188,30 +191,40 @@ __device__ __forceinline__ bool resolve_ids(const StreamJob& J, int slot, Tokens
     uint32_t bits = (uint32_t)__shfl((int)word, w, 64);
     for (int r = slot - before; r > 0; --r) bits &= bits - 1u;
     const int e = 32 * w + __ffs(bits) - 1;
-    const uint64_t lt = __ballot(id >= 0 && id < e), eq = __ballot(id == e);
+    const uint64_t lt0 = __ballot(id0 >= 0 && id0 < e), eq0 = __ballot(id0 == e);
+    const uint64_t lt1 = __ballot(id1 >= 0 && id1 < e), eq1 = __ballot(id1 == e);
     if (lane == 0) {
-        s_cnt[wave][0] = __popcll(lt);
-        s_cnt[wave][1] = __popcll(eq);
+        s_cnt[wave][0] = __popcll(lt0) + __popcll(lt1);
+        s_cnt[wave][1] = __popcll(eq0);
+        s_cnt[wave][2] = __popcll(eq1);
     }
     __syncthreads();
-    int base = 0, n = 0, pre = 0;
+    int base = 0, n0 = 0, n1 = 0, pre0 = 0, pre1 = 0;
 #pragma unroll
     for (int w2 = 0; w2 < kThreads / 64; ++w2) {
         base += s_cnt[w2][0];
-        pre += w2 < wave ? s_cnt[w2][1] : 0;
-        n += s_cnt[w2][1];
+        pre0 += w2 < wave ? s_cnt[w2][1] : 0;
+        pre1 += w2 < wave ? s_cnt[w2][2] : 0;
+        n0 += s_cnt[w2][1];
+        n1 += s_cnt[w2][2];
     }
-    if (id == e) {
-        const int pos = pre + __popcll(eq & ((1ull << lane) - 1ull));
+    const uint64_t below = (1ull << lane) - 1ull;
+    if (id0 == e) {
+        const int pos = pre0 + __popcll(eq0 & below);
         list[pos] = tid;
         tok[pos] = tid / J.k;
+    }
+    if (id1 == e) {  // pairs tid + kThreads follow all of the first set
+        const int pos = n0 + pre1 + __popcll(eq1 & below);
+        list[pos] = tid + kThreads;
+        tok[pos] = (tid + kThreads) / J.k;
     }
     __syncthreads();
     // uniform, but computed through lane exchanges: say so, or every buffer
     // load through the expert's resource becomes a readfirstlane loop
     t.e = __builtin_amdgcn_readfirstlane(e);
     t.base = __builtin_amdgcn_readfirstlane(base);
-    t.n = __builtin_amdgcn_readfirstlane(n);
+    t.n = __builtin_amdgcn_readfirstlane(n0 + n1);
     t.na = total;
     return true;
 }
@@ -1092,11 +1105,11 @@ __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS)
     const int blk = (bid / J.splits) % J.nblk;
     const int slot = bid / (J.splits * J.nblk);
     Tokens tk;
-    __shared__ int s_list[kThreads], s_tok[kThreads];
+    __shared__ int s_list[kIdsPairs], s_tok[kIdsPairs];
     if (!resolve_item(J, slot, tk, s_list, s_tok)) return;
     if (J.r_act && blk == 0 && ks == 0) {  // one workgroup per slot records it for the down launch
         const int t = threadIdx.x;
-        if (t < tk.n) J.r_bkt[tk.base + t] = s_list[t];
+        for (int u = t; u < tk.n; u += kThreads) J.r_bkt[tk.base + u] = s_list[u];
         if (t == 0) {
             J.r_act[slot] = tk.e;
             J.r_off[slot] = tk.base;
@@ -1311,7 +1324,7 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0,
     const int blk = bid % J.nblk;
     const int slot = bid / J.nblk;
     Tokens tk;
-    __shared__ int s_list[kThreads], s_tok[kThreads];
+    __shared__ int s_list[kIdsPairs], s_tok[kIdsPairs];
     if (!resolve_item(J, slot, tk, s_list, s_tok)) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int i = lane & 15, g = lane >> 4;
@@ -1422,7 +1435,7 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down_rows(StreamJo
     const int item = blockIdx.x % J.nblk;
     const int slot = blockIdx.x / J.nblk;
     Tokens tk;
-    __shared__ int s_list[kThreads], s_tok[kThreads];
+    __shared__ int s_list[kIdsPairs], s_tok[kIdsPairs];
     if (!resolve_item(J, slot, tk, s_list, s_tok)) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int i = lane & 15, g = lane >> 4;

@@ -568,7 +568,7 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
     const Bf16Side s3 = shb ? side(sh_dn, d->sh_h_scale, 0.0f, kBf16Down) : no_side();
     const RouterPlan p = router_plan(M, H, E);
     const bool fp4_shared = sf != MOE_FMT_NONE && !shb;
-    if (M * k <= kSmallPairs) {
+    if (M * k <= kIdsPairs) {
         // Five launches: (router + token-order MXFP8 of x) -> top-k -> gate_up
         // (workgroups resolve their expert from the ids, in the route step's
         // order, and gather token rows; one per slot records it) -> down

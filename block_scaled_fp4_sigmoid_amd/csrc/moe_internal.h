@@ -89,6 +89,9 @@ hipError_t launch_quant_pairs(const uint16_t* x, const int32_t* bucket, int k, i
 // The route step (after launch_topk) and launch_quant_pairs in one launch,
 // for M*k <= kSmallPairs pairs; side3 rides along.
 constexpr int kSmallPairs = 256;
+// Pairs up to which the fused layer's gate_up workgroups resolve their slot
+// from the top-k ids themselves (two per thread), with no route step.
+constexpr int kIdsPairs = 512;
 hipError_t launch_bucket_quant(int M, int E, int k, const moe_routing& route, const uint16_t* x, int K,
                                uint8_t* qp, uint8_t* sp, uint8_t* qt, uint8_t* st, const Bf16Side& side3,
                                int stage3, hipStream_t stream);
@@ -117,7 +120,7 @@ struct ExpertJob {
     int slots;              // U_max for routed, 1 for dense
     int k;                  // top-k (pair id -> row)
     int M;
-    // Small-pair routed path (M*k <= kSmallPairs): with ids != nullptr every
+    // Few-pair routed path (M*k <= kIdsPairs): with ids != nullptr every
     // workgroup resolves its slot from the top-k ids (no route step needed
     // before it).  With a_tok the gate_up activations are in token order
     // ([M][K]: pair p reads row p / k, the pairs of a pass gathered through

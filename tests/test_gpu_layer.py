@@ -101,22 +101,33 @@ EDGE = [
     dict(M=70, H=256, E=3, k=2, I=128, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=256),  # >64 rows per expert
     dict(M=9, H=512, E=64, k=6, I=384, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=128, routed_scale=2.5),
     dict(M=130, H=128, E=2, k=1, I=128, bias="zipf:2.0"),               # one expert takes ~all rows
-    # an MXFP4 shared expert of five 32-row passes riding along both routed launches (I > 512)
+    # the few-pairs path (slots resolved from the ids, two pairs per thread) with one expert
+    # taking more than 256 of its 500 pairs
+    dict(M=500, H=128, E=2, k=1, I=128, bias="zipf:2.0"),
+    # an MXFP4 shared expert of five 32-row passes riding along both routed launches (I > 512),
+    # with few pairs (260) and with many (520: the route step's launch)
     dict(M=130, H=256, E=8, k=2, I=640, sfmt=synth.MXFP4, I_sh=640),
+    dict(M=130, H=256, E=16, k=4, I=640, sfmt=synth.MXFP4, I_sh=640),
     # the clamped SwiGLU in routed and shared experts (few pairs, many pairs; MX, NV and bf16 shared)
     dict(M=9, H=512, E=64, k=6, I=384, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=256, swiglu_limit=0.4),
     dict(M=48, H=1024, E=32, k=8, I=256, wfmt=synth.MXFP4, sfmt=synth.MXFP4, I_sh=256, swiglu_limit=0.5),
     # NVFP4 activations (W4A4): the 7-row verify shape of the pages' Qwen3.5 row with top-10, bf16
-    # shared; few pairs with an NVFP4 shared expert; many pairs (bucketed launches), K-streamed down
+    # shared; few pairs with an NVFP4 shared expert; 320 pairs (two per thread) and 576 (bucketed
+    # launches), K-streamed down
     dict(M=7, H=1024, E=64, k=10, I=256, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=256, act_fmt=synth.ACT_NVFP4),
     dict(M=9, H=512, E=16, k=4, I=384, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=256, act_fmt=synth.ACT_NVFP4),
     dict(M=40, H=768, E=32, k=8, I=640, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=640, act_fmt=synth.ACT_NVFP4,
          swiglu_limit=0.6),
-    # the static-FP8 shared expert riding the router, top-k and gate_up launches (few pairs: W4A4 and
-    # MXFP8 activations) or the route step's launch (many pairs), with the clamp
+    dict(M=72, H=768, E=32, k=8, I=640, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=640, act_fmt=synth.ACT_NVFP4,
+         swiglu_limit=0.6),
+    # the static-FP8 shared expert riding the router, top-k and gate_up launches (up to 512 pairs:
+    # W4A4 and MXFP8 activations, 320 pairs) or the route step's launch (576 pairs), with the clamp
     dict(M=7, H=1024, E=64, k=10, I=256, wfmt=synth.NVFP4, sfmt=synth.FP8S, I_sh=256, act_fmt=synth.ACT_NVFP4),
     dict(M=9, H=768, E=32, k=4, I=384, wfmt=synth.NVFP4, sfmt=synth.FP8S, I_sh=128),
     dict(M=40, H=512, E=16, k=8, I=256, wfmt=synth.MXFP4, sfmt=synth.FP8S, I_sh=384, swiglu_limit=0.5),
+    dict(M=72, H=512, E=16, k=8, I=256, wfmt=synth.MXFP4, sfmt=synth.FP8S, I_sh=384, swiglu_limit=0.5),
+    # a bf16 shared expert with 576 pairs (its down rides the route step's launch)
+    dict(M=72, H=512, E=32, k=8, I=256, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=256),
 ]
 
 
