@@ -785,7 +785,6 @@ template <int MB, int NB, int DQ, bool A4>
 __device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const int (&wblk)[MB], int arow0,
                                                 int npass, const int* src, int s0, int nst, int (&smax)[NB],
                                                 v4f (&acc)[MB][2], uint8_t* tiles, int* rsmax) {
-    static_assert(DQ % 2 == 0, "slots alternate between the two tile buffers");
     constexpr int CF = A4 ? kFmtNV4 : kFmtNV;
     const Coord<CF, MB, NB> c = make_coord<CF, MB, NB>(J, e, wblk, arow0, npass, src);
     const TileOffs<NB> to = tile_offsets<NB, A4>(J.K, npass, src);
@@ -826,19 +825,19 @@ __device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[mb][j] = v4f{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
-    tile_store<NB, A4>(P, tiles, rsmax, npass);
+    tile_store<NB, A4>(P, tiles + (q0 & 1) * kTileBytesH, rsmax, npass);  // the tile of quad q sits in buffer q & 1
     __syncthreads();
     for (int l0 = 0; l0 < nq; l0 += DQ) {
 #pragma unroll
         for (int v = 0; v < DQ; ++v) {
             const int q = q0 + l0 + v;  // the quad of slot v in this round
-            const uint8_t* tile = tiles + (v & 1) * kTileBytesH;
+            const uint8_t* tile = tiles + (q & 1) * kTileBytesH;
             v8h B[NB][4];
             tile_read<NB>(tile, 0, B);
             tile_load<NB, A4>(P, ca, to, q + 1, s_end);  // in flight over the quad's steps
             quadw_steps<MB, NB, DQ, 0>(R, v, c, q + DQ, s_end, tile, B, acc);
             // tile q+1 into the other buffer (its reads ended at the last barrier)
-            tile_store<NB, A4>(P, tiles + ((v + 1) & 1) * kTileBytesH, rsmax, npass);
+            tile_store<NB, A4>(P, tiles + ((q + 1) & 1) * kTileBytesH, rsmax, npass);
             __syncthreads();
         }
     }

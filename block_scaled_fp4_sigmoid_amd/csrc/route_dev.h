@@ -73,8 +73,12 @@ __device__ inline void block_exclusive_scan3(int* a, int* b, int* c, int* scratc
     __syncthreads();
 }
 
-// Rows per placement chunk and bitmap words per expert of the route step.
-__host__ __device__ inline int bucket_chunk_rows(int k) { return 128 < kBucketThreads / k ? 128 : kBucketThreads / k; }
+// Pairs per thread in one placement chunk, rows per chunk and bitmap words
+// per expert of the route step.
+constexpr int kChunkPairsPerThread = 4;
+__host__ __device__ inline int bucket_chunk_rows(int k) {
+    return 128 < kChunkPairsPerThread * kBucketThreads / k ? 128 : kChunkPairsPerThread * kBucketThreads / k;
+}
 __host__ __device__ inline int bucket_words(int k) { return (bucket_chunk_rows(k) + 31) / 32; }
 
 // LDS bytes the route step needs: five per-expert int arrays, the scan
@@ -105,22 +109,28 @@ __device__ inline void bucket_step(int M, int E, int k, const moe_routing& route
         s_run[e] = 0;
     }
     __syncthreads();
-    // Pairs in placement chunks of R rows (R * k <= 256 pairs: pair r0 * k +
-    // tid).  The expert ids of a thread's first kIdRegs chunks stay in
-    // registers for the placement below.
+    // Pairs in placement chunks of R rows (R * k <= 4 * 256 pairs: pairs
+    // r0 * k + tid + 256 q, q < 4).  The expert ids of a thread's pairs in the
+    // first kIdChunks chunks stay in registers for the placement below.
     const int R = bucket_chunk_rows(k);
     const int W = bucket_words(k);
-    constexpr int kIdRegs = 16;
-    int idr[kIdRegs];
+    const int CP = R * k;  // pairs per chunk
+    constexpr int kIdChunks = 4;
+    int idr[kIdChunks][kChunkPairsPerThread];
 #pragma unroll
-    for (int ci = 0; ci < kIdRegs; ++ci) {
-        const int p = ci * R * k + tid;
-        idr[ci] = tid < R * k && p < P ? route.topk_ids[p] : -1;
-    }
+    for (int ci = 0; ci < kIdChunks; ++ci)
 #pragma unroll
-    for (int ci = 0; ci < kIdRegs; ++ci)
-        if (idr[ci] >= 0) atomicAdd(&s_cnt[idr[ci]], 1);
-    for (int p = kIdRegs * R * k + tid; p < P; p += kBucketThreads) atomicAdd(&s_cnt[route.topk_ids[p]], 1);
+        for (int q = 0; q < kChunkPairsPerThread; ++q) {
+            const int pc = tid + kBucketThreads * q;
+            const int p = ci * CP + pc;
+            idr[ci][q] = pc < CP && p < P ? route.topk_ids[p] : -1;
+        }
+#pragma unroll
+    for (int ci = 0; ci < kIdChunks; ++ci)
+#pragma unroll
+        for (int q = 0; q < kChunkPairsPerThread; ++q)
+            if (idr[ci][q] >= 0) atomicAdd(&s_cnt[idr[ci][q]], 1);
+    for (int p = kIdChunks * CP + tid; p < P; p += kBucketThreads) atomicAdd(&s_cnt[route.topk_ids[p]], 1);
     __syncthreads();
     for (int e = tid; e < kMaxE; e += kBucketThreads) {
         const int c = s_cnt[e];
@@ -157,23 +167,32 @@ __device__ inline void bucket_step(int M, int E, int k, const moe_routing& route
     for (int r0 = 0, ci = 0; r0 < M; r0 += R, ++ci) {
         for (int w = tid; w < E * W; w += kBucketThreads) s_bm[w] = 0u;
         __syncthreads();
-        const int p = r0 * k + tid;
-        const bool valid = tid < R * k && p < P;
-        int e = 0, rl = 0;
-        if (valid) {
-            int ev = 0;
+        int eq[kChunkPairsPerThread], rlq[kChunkPairsPerThread];
 #pragma unroll
-            for (int cj = 0; cj < kIdRegs; ++cj) ev = cj == ci ? idr[cj] : ev;  // registers, no dynamic index
-            e = ci < kIdRegs ? ev : route.topk_ids[p];
-            rl = p / k - r0;
-            atomicOr(&s_bm[e * W + (rl >> 5)], 1u << (rl & 31));
+        for (int q = 0; q < kChunkPairsPerThread; ++q) {
+            const int pc = tid + kBucketThreads * q;
+            const int p = r0 * k + pc;
+            eq[q] = -1;
+            rlq[q] = 0;
+            if (pc < CP && p < P) {
+                int ev = 0;
+#pragma unroll
+                for (int cj = 0; cj < kIdChunks; ++cj) ev = cj == ci ? idr[cj][q] : ev;  // registers, no dynamic index
+                eq[q] = ci < kIdChunks ? ev : route.topk_ids[p];
+                rlq[q] = p / k - r0;
+                atomicOr(&s_bm[eq[q] * W + (rlq[q] >> 5)], 1u << (rlq[q] & 31));
+            }
         }
         __syncthreads();
-        if (valid) {
-            int rank = 0;
-            for (int w = 0; w < (rl >> 5); ++w) rank += __popc(s_bm[e * W + w]);
-            rank += __popc(s_bm[e * W + (rl >> 5)] & ((1u << (rl & 31)) - 1u));
-            route.bucket[s_off[e] + s_run[e] + rank] = p;
+#pragma unroll
+        for (int q = 0; q < kChunkPairsPerThread; ++q) {
+            if (eq[q] >= 0) {
+                const int e = eq[q], rl = rlq[q];
+                int rank = 0;
+                for (int w = 0; w < (rl >> 5); ++w) rank += __popc(s_bm[e * W + w]);
+                rank += __popc(s_bm[e * W + (rl >> 5)] & ((1u << (rl & 31)) - 1u));
+                route.bucket[s_off[e] + s_run[e] + rank] = r0 * k + tid + kBucketThreads * q;
+            }
         }
         __syncthreads();
         for (int ee = tid; ee < E; ee += kBucketThreads) {

@@ -85,10 +85,16 @@ ROUTE_CASES = [
     (100, 384, 3, 2, "none", 1.0),     # few experts, many rows per expert
     (37, 640, 1024, 32, "none", 1.0),  # largest E and k
     (16, 7168, 384, 8, "none", 1.0),   # the decode workload's router
-    # the route step places rows in chunks of min(128, 256 / k) rows and keeps
-    # the first 16 chunks' expert ids in registers; these run past 16 chunks
-    (1024, 512, 64, 8, "zipf:1.0", 1.0),  # 32 chunks of 32 rows
+    # the router's K chunks in pairs of software-pipelined rounds: two pairs of
+    # 128-K rounds (M <= 16) and three pairs of 64-K rounds (M <= 16, chunks of 384)
+    (8, 8192, 1024, 8, "none", 1.0),
+    (12, 6144, 1024, 8, "normal:0.01", 1.0),
+    # the route step places rows in chunks of min(128, 1024 / k) rows (four
+    # pairs per thread) and keeps the first 4 chunks' expert ids in registers;
+    # these run past 4 chunks
+    (1024, 512, 64, 8, "zipf:1.0", 1.0),  # 8 chunks of 128 rows
     (4096, 256, 4, 1, "none", 1.0),       # 32 chunks of 128 rows
+    (600, 512, 64, 10, "zipf:1.0", 1.0),  # 6 chunks of 102 rows (the last ragged)
 ]
 
 
