@@ -666,12 +666,17 @@ __device__ __forceinline__ void tile_load(ActShare<NB>& P, const Coord<CF, 1, NB
 
 // Converts the thread's share of a tile to f16 and writes it into an LDS
 // buffer.  rsmax: the pass rows' smax (LDS).  Codes past the range are zero,
-// and so are their f16 values.
+// and so are their f16 values.  A wave whose two rows of a round are both
+// past the pass skips that round: those LDS rows keep stale values, which
+// reach only the MFMA output columns of rows past the pass (each output
+// column depends on its own B column only), and those are never stored.
 template <int NB, bool A4>
 __device__ __forceinline__ void tile_store(const ActShare<NB>& P, uint8_t* buf, const int* rsmax, int npass) {
     const int t = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
 #pragma unroll
     for (int k = 0; k < 2 * NB; ++k) {
+        if (8 * k + 2 * wave >= npass) continue;  // uniform: rows 8k + 2w, +1 of the wave
         const int li = t + kThreads * k, row = li >> 5, ch = li & 31;
         v8h h0, h1;
         if constexpr (A4) {
