@@ -12,7 +12,11 @@
 // [M][H/32] as the activation quant lays them out.
 //
 // One workgroup per row; each thread owns 8 consecutive columns per 8192
-// (four neighbouring lanes hold one 32-value block).
+// (four neighbouring lanes hold one 32-value block).  y is [M*k][H] by pair,
+// or grouped as the fused layer's down writes it (pair p's row at yrec[p]:
+// its first 128-column block at yrec[p].x floats, the next ones yrec[p].y * 128
+// floats further each); y_sh likewise [M][H] or grouped (rows 0..M-1 taken as
+// one expert's).
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "quant_dev.h"
@@ -30,7 +34,9 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restric
                                                           float eps, int H, int k,
                                                           uint16_t* out, uint16_t* residual_out,
                                                           uint8_t* __restrict__ out_q,
-                                                          uint8_t* __restrict__ out_s) {
+                                                          uint8_t* __restrict__ out_s,
+                                                          const int2* __restrict__ yrec, int ysh_grp,
+                                                          int M) {
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
     constexpr int kMaxChunks = 2;  // H <= 16384
@@ -39,6 +45,10 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restric
     uint32_t gw[kMaxChunks][4];
     float ss = 0.f;
     const float* wr = topk_w + (size_t)r * k;
+    // the row of y_sh: grouped, its group of min(16, M - g0) rows from row g0
+    const int g0 = r & ~(kYGroupRows - 1);
+    const size_t sh_row = ysh_grp ? (size_t)g0 * H + (r - g0) * kYBlockCols : (size_t)r * H;
+    const int sh_blk = ysh_grp ? min(kYGroupRows, M - g0) * kYBlockCols : kYBlockCols;
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
         const int col = c * kFinChunk + tid * 8;
@@ -48,8 +58,9 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restric
             const v4i gb = load16(gamma + col);
             float4 sa = {0.f, 0.f, 0.f, 0.f}, sb = sa;
             if (y_sh) {
-                sa = *reinterpret_cast<const float4*>(y_sh + (size_t)r * H + col);
-                sb = *reinterpret_cast<const float4*>(y_sh + (size_t)r * H + col + 4);
+                const float* ys = y_sh + sh_row + (size_t)(col / kYBlockCols) * sh_blk + col % kYBlockCols;
+                sa = *reinterpret_cast<const float4*>(ys);
+                sb = *reinterpret_cast<const float4*>(ys + 4);
             }
             gw[c][0] = (uint32_t)gb.x; gw[c][1] = (uint32_t)gb.y; gw[c][2] = (uint32_t)gb.z; gw[c][3] = (uint32_t)gb.w;
             float t[8];
@@ -69,7 +80,11 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restric
                 for (int u = 0; u < kBatch; ++u) {
                     const int j = j0 + u;
                     if (j < k) {
-                        const float* yr = y + ((size_t)r * k + j) * H + col;
+                        const size_t p = (size_t)r * k + j;
+                        int2 yp = {(int)(p * H), 1};  // by pair: one row per "group"
+                        if (yrec) yp = yrec[p];
+                        const float* yr = y + (size_t)yp.x + (size_t)(col / kYBlockCols) * (yp.y * kYBlockCols) +
+                                          col % kYBlockCols;
                         ya[u] = *reinterpret_cast<const float4*>(yr);
                         yb[u] = *reinterpret_cast<const float4*>(yr + 4);
                         wj[u] = wr[j];
@@ -134,9 +149,9 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restric
 hipError_t launch_finalize(const float* y, const float* topk_w, const float* y_sh,
                            const uint16_t* residual, const uint16_t* gamma, float eps, int M,
                            int H, int k, uint16_t* out, uint16_t* residual_out, uint8_t* out_q,
-                           uint8_t* out_s, hipStream_t stream) {
+                           uint8_t* out_s, hipStream_t stream, const int2* yrec, bool ysh_grouped) {
     hipLaunchKernelGGL(k_finalize, dim3(M), dim3(kFinThreads), 0, stream, y, topk_w, y_sh,
-                       residual, gamma, eps, H, k, out, residual_out, out_q, out_s);
+                       residual, gamma, eps, H, k, out, residual_out, out_q, out_s, yrec, ysh_grouped ? 1 : 0, M);
     return hipGetLastError();
 }
 

@@ -379,13 +379,13 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials
 }
 
 __global__ __launch_bounds__(kBucketThreads) void k_bucket(int M, int E, int k, moe_routing route, Bf16Side side,
-                                                          int stage) {
+                                                          int stage, int H, int2* yrec) {
     if (blockIdx.x > 0) {  // a bf16 shared-expert stage riding along
         bf16_side_block(side, stage, blockIdx.x - 1);
         return;
     }
     __shared__ __align__(16) uint8_t s_lds[kBucketLdsMax];
-    bucket_step(M, E, k, route, s_lds);
+    bucket_step(M, E, k, route, s_lds, H, yrec);
 }
 
 // Route step and the activation quant in one launch, for P = M*k <= 256 pairs.
@@ -451,12 +451,13 @@ hipError_t launch_topk(const float* partials, int splits, const float* bias, int
 hipError_t launch_topk_bucket(const float* partials, int splits, const float* bias, int M, int E,
                               int k, float routed_scale, float* logits_out,
                               const moe_routing& route, const Bf16Side& side2, int stage2,
-                              const Bf16Side& side3, int stage3, hipStream_t stream) {
+                              const Bf16Side& side3, int stage3, hipStream_t stream, int H, int2* yrec) {
     hipError_t e = launch_topk(partials, splits, bias, M, E, k, routed_scale, logits_out, route, side2, stage2,
                                stream);
     if (e != hipSuccess) return e;
     const int extra3 = stage3 == kBf16None ? 0 : side3.blocks;
-    hipLaunchKernelGGL(k_bucket, dim3(1 + extra3), dim3(kBucketThreads), 0, stream, M, E, k, route, side3, stage3);
+    hipLaunchKernelGGL(k_bucket, dim3(1 + extra3), dim3(kBucketThreads), 0, stream, M, E, k, route, side3, stage3,
+                       H, yrec);
     return hipGetLastError();
 }
 

@@ -64,6 +64,7 @@ template <int F>
 constexpr bool kA4 = F == kFmtNV4;  // NVFP4 activations
 constexpr int kThreads = 256;
 constexpr int kPassRows = 32;           // activation rows per pass (two 16-row N-blocks)
+static_assert(kPassRows % kYGroupRows == 0, "a pass holds whole grouped-y groups");
 
 #ifndef MOE_STREAM_TARGET_ITEMS
 #define MOE_STREAM_TARGET_ITEMS 256  // gate_up splits K until about this many items
@@ -120,6 +121,8 @@ struct StreamJob {
     // gate_up resolving from the ids: record the resolved slots here for the
     // down launch (active experts, bucket ranges, count, bucket), or nullptr
     int32_t *r_act, *r_off, *r_na, *r_bkt;
+    int2* r_yrec;           // and each pair's grouped-y row (ygroup_rec), or nullptr
+    int ygrp;               // down: write y grouped (ygroup_rec) instead of [out_rows][N]
     float limit;            // gate_up: clamped SwiGLU limit (0: unclamped)
     // NVFP4 activations: their global (ag, or age[e] per expert) and the
     // global of the h a gate_up writes (hg, or hge[e])
@@ -1113,7 +1116,10 @@ __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS)
     if (!resolve_item(J, slot, tk, s_list, s_tok)) return;
     if (J.r_act && blk == 0 && ks == 0) {  // one workgroup per slot records it for the down launch
         const int t = threadIdx.x;
-        for (int u = t; u < tk.n; u += kThreads) J.r_bkt[tk.base + u] = s_list[u];
+        for (int u = t; u < tk.n; u += kThreads) {
+            J.r_bkt[tk.base + u] = s_list[u];
+            if (J.r_yrec) J.r_yrec[s_list[u]] = ygroup_rec(tk.base, tk.n, u, K);
+        }
         if (t == 0) {
             J.r_act[slot] = tk.e;
             J.r_off[slot] = tk.base;
@@ -1377,12 +1383,18 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0,
         for (int j = 0; j < 2; ++j) {
             const int t = 16 * j + i;
             if (t < npass) {
+                // grouped y: block j of the pass is one group of min(16, npass - 16 j) rows
+                const int grows = min(kYGroupRows, npass - 16 * j);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
                     v4f v = acc[mb][j];
                     if (FMT == kFmtNV) v = v * nv_row_factor(smax[j], gs);
                     if (kA4<FMT>) v = v * fa4;
-                    v4f* dst = reinterpret_cast<v4f*>(y + (size_t)orow[j] * H + f0 + 16 * mb + 4 * g);
+                    const int col = f0 + 16 * mb + 4 * g;
+                    const size_t yo = J.ygrp ? (size_t)(arow0 + 16 * j) * H + (size_t)(col / kYBlockCols) * (grows * kYBlockCols) +
+                                                   i * kYBlockCols + col % kYBlockCols
+                                             : (size_t)orow[j] * H + col;
+                    v4f* dst = reinterpret_cast<v4f*>(y + yo);
                     if constexpr (NTY)
                         __builtin_nontemporal_store(v, dst);
                     else
@@ -1533,7 +1545,13 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down_rows(StreamJo
             }
             fac = nv_row_factor(smax, gs);
         }
-        const uint32_t ybase = okr ? (uint32_t)orow * (uint32_t)H * 4u + 16u * g : kOOB;
+        // y by pair: the lane's row; grouped: the pass is one group of npass rows
+        // whose 128-column blocks (eight 16-column weight blocks) are npass rows apart
+        const uint32_t ybase = okr ? (J.ygrp ? ((uint32_t)arow0 * (uint32_t)H + (uint32_t)i * kYBlockCols) * 4u
+                                             : (uint32_t)orow * (uint32_t)H * 4u) + 16u * g
+                                   : kOOB;
+        const uint32_t ygs = J.ygrp ? (uint32_t)npass * kYBlockCols * 4u : 8u * 64u;  // bytes per 8 weight blocks
+        static_assert(kYBlockCols == 8 * 16, "a y column block is eight 16-row weight blocks");
         for (int b0 = 0; b0 < nb; b0 += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
@@ -1541,7 +1559,8 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down_rows(StreamJo
                 v4f acc = {0.f, 0.f, 0.f, 0.f};
                 rows_steps<FMT, S, D, 0>(acc, wa, wsc, d, b, bs, B16, g);
                 const int blk = b0 + d;
-                const uint32_t vo = blk < nb ? ybase + (uint32_t)(rb0 + blk) * 64u : kOOB;
+                const uint32_t cb = (uint32_t)(rb0 + blk);
+                const uint32_t vo = blk < nb ? ybase + (cb >> 3) * ygs + (cb & 7u) * 64u : kOOB;
                 const v4f v = acc * fac;
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), ry, vo, 0, 0);
                 load_block(d, blk + D);
@@ -1617,6 +1636,8 @@ StreamJob stream_job(const ExpertJob& j, int N, const uint8_t* a_q, const uint8_
     s.r_off = j.record ? j.record->off : nullptr;
     s.r_na = j.record ? j.record->na : nullptr;
     s.r_bkt = j.record ? j.record->bkt : nullptr;
+    s.r_yrec = j.record ? j.record->yrec : nullptr;
+    s.ygrp = j.ygroup ? 1 : 0;
     if (s.a_tok) s.a_rows = (uint32_t)j.M;
     s.limit = j.swiglu_limit;
     s.ag = j.a_global;

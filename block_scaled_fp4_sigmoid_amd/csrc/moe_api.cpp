@@ -37,6 +37,16 @@ int check_pair_bytes(int M, int k, int H) {
 
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
+// The fused layer writes y grouped (ygroup_rec) from this many bytes of y on.
+// A down workgroup's writes then form one span per 16-row group instead of a
+// short run per row (384 rows, 88 MB of y: 1046 -> 1021 us per step); the
+// finalize pays one dependent load for each pair's row, about 1 us, more than
+// the down saves below a few MB (7 rows of top-10 at H 4096, 1.1 MB: +1 us).
+#ifndef MOE_Y_GROUP_BYTES
+#define MOE_Y_GROUP_BYTES (4u << 20)
+#endif
+bool y_grouped(int M, int k, int H) { return (int64_t)M * k * H * 4 >= (int64_t)MOE_Y_GROUP_BYTES; }
+
 // A static FP8 input scale: finite and positive.
 bool static_scale_ok(float s) { return s > 0.0f && s <= 3.4e38f; }
 
@@ -447,6 +457,7 @@ struct LayerWs {
     float* sh_fpart; // FP4 shared gate_up split-K partials
     float *y, *ysh;
     int32_t *r_act, *r_off, *r_na, *r_bkt;  // slots recorded by the few-pairs gate_up
+    int2* yrec;                             // each pair's row of the grouped y
 };
 
 LayerWs carve_layer(Carver& c, const moe_layer_desc* d) {
@@ -506,6 +517,7 @@ LayerWs carve_layer(Carver& c, const moe_layer_desc* d) {
     L.r_off = c.take<int32_t>(std::min(E, P) + 1);
     L.r_na = c.take<int32_t>(1);
     L.r_bkt = c.take<int32_t>(P);
+    L.yrec = c.take<int2>(P);
     return L;
 }
 
@@ -574,7 +586,9 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
         // order, and gather token rows; one per slot records it) -> down
         // (slots from the record) -> finalize.  No bucket or 8-row tiles are
         // materialized: nothing in these launches reads them.  The bf16 or
-        // static-FP8 shared expert's stages ride along the first three.
+        // static-FP8 shared expert's stages ride along the first three.  A
+        // large y is written grouped (ygroup_rec): gate_up's record gives the
+        // finalize each pair's row.
         hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, L.xqt, L.xst, s1,
                                               shb ? kBf16GateUp : kBf16None, stream, xg4);
         if (e == hipSuccess)
@@ -585,12 +599,14 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
         set_a4(gu, d, false, true);
         gu.ids = r.topk_ids;
         gu.a_tok = true;
-        const SlotRecord rec{L.r_act, L.r_off, L.r_na, L.r_bkt};
+        const bool yg = y_grouped(M, k, H);
+        const SlotRecord rec{L.r_act, L.r_off, L.r_na, L.r_bkt, yg ? L.yrec : nullptr};
         gu.record = &rec;
         // the FP4 shared expert rides along the routed launches
         const ExpertJob& sgu = sh_gu;
         ExpertJob sdn = dense_job(d->sh2, H, Ish, M);
         if (sf == MOE_FMT_NVFP4) set_a4(sdn, d, true, false);
+        sdn.ygroup = yg;
         const SecondJob s_gu = fp4_shared ? SecondJob{&sgu, L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart} : SecondJob{};
         const SecondDown s_dn = fp4_shared ? SecondDown{&sdn, L.hsq, L.hss, L.ysh} : SecondDown{};
         if (e == hipSuccess)
@@ -603,20 +619,24 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
         dn.active_offsets = rec.off;
         dn.bucket = rec.bkt;
         dn.count = rec.na;
+        dn.ygroup = yg;
         if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream, s_dn);
         if (e == hipSuccess)
             e = launch_finalize(L.y, r.topk_w, L.ysh, residual, d->gamma, d->eps, M, H, k, out, residual_out,
-                                out_q, out_s, stream);
+                                out_q, out_s, stream, yg ? L.yrec : nullptr, fp4_shared && yg);
         return hip_status(e);
     }
     // Six launches: (router + token-order MXFP8 of x) -> top-k -> route step
     // -> gate_up (gathers each pass's token rows through the bucket) -> down
-    // -> finalize.
+    // -> finalize.  A large y is written grouped: the route step gives the
+    // finalize each pair's row.
+    const bool yg = y_grouped(M, k, H);
     hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, L.xqt, L.xst, s1,
                                           shb ? kBf16GateUp : kBf16None, stream, xg4);
     if (e == hipSuccess)
         e = launch_topk_bucket(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale, logits_out, r,
-                               s2, shb ? kBf16Swiglu : kBf16None, s3, shb ? kBf16Down : kBf16None, stream);
+                               s2, shb ? kBf16Swiglu : kBf16None, s3, shb ? kBf16Down : kBf16None, stream, H,
+                               yg ? L.yrec : nullptr);
     ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
     gu.swiglu_limit = d->swiglu_limit;
     set_a4(gu, d, false, true);
@@ -624,16 +644,18 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
     const ExpertJob& sgu = sh_gu;
     ExpertJob sdn = dense_job(d->sh2, H, Ish, M);
     if (sf == MOE_FMT_NVFP4) set_a4(sdn, d, true, false);
+    sdn.ygroup = yg;
     const SecondJob s_gu = fp4_shared ? SecondJob{&sgu, L.xqt, L.xst, L.hsq, L.hss, L.sh_fpart} : SecondJob{};
     const SecondDown s_dn = fp4_shared ? SecondDown{&sdn, L.hsq, L.hss, L.ysh} : SecondDown{};
     if (e == hipSuccess)
         e = launch_gate_up_fp4(gu, L.xqt, L.xst, L.hq, L.hs, L.part, stream, no_side(), kBf16None, s_gu);
     ExpertJob dn = routed_job(d->w2, H, I, r, M, E, k);
     set_a4(dn, d, false, false);
+    dn.ygroup = yg;
     if (e == hipSuccess) e = launch_down_fp4(dn, L.hq, L.hs, L.y, stream, s_dn);
     if (e == hipSuccess)
         e = launch_finalize(L.y, r.topk_w, L.ysh, residual, d->gamma, d->eps, M, H, k, out, residual_out,
-                            out_q, out_s, stream);
+                            out_q, out_s, stream, yg ? L.yrec : nullptr, fp4_shared && yg);
     return hip_status(e);
 }
 

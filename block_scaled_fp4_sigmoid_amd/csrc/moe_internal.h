@@ -69,7 +69,8 @@ hipError_t launch_topk(const float* partials, int splits, const float* bias, int
 hipError_t launch_topk_bucket(const float* partials, int splits, const float* bias, int M, int E,
                               int k, float routed_scale, float* logits_out,
                               const moe_routing& route, const Bf16Side& side2, int stage2,
-                              const Bf16Side& side3, int stage3, hipStream_t stream);
+                              const Bf16Side& side3, int stage3, hipStream_t stream, int H = 0,
+                              int2* yrec = nullptr);
 
 // FP4 weights in the load-order layout (moe_pack_fp4).
 size_t packed_scale_bytes(int fmt, int E, int N, int K);
@@ -102,7 +103,25 @@ hipError_t launch_bucket_quant(int M, int E, int k, const moe_routing& route, co
 // count, and the bucket ([P]) in the route step's order.
 struct SlotRecord {
     int32_t *act, *off, *na, *bkt;
+    int2* yrec = nullptr;  // [P] grouped-y row of each pair (ygroup_rec), or nullptr
 };
+
+// The fused layer's per-pair down outputs y (fp32) are grouped: the bucket
+// rows of one expert split into groups of at most kYGroupRows (the rows of one
+// 16-row MFMA block of a down pass), and a group of n rows holds its column
+// blocks of kYBlockCols one after another, each [n][kYBlockCols].  A down
+// workgroup, which owns whole column blocks of a pass, then writes one
+// contiguous span per group instead of one short run per row.  Row u of an
+// expert whose n rows start at bucket row base: its first column block starts
+// ygroup_rec(...).x floats into y, and its column blocks are
+// ygroup_rec(...).y * kYBlockCols floats apart.  H is a multiple of
+// kYBlockCols, and y's size (< 2^31 bytes) keeps every offset in an int.
+constexpr int kYGroupRows = 16, kYBlockCols = 128;
+__host__ __device__ inline int2 ygroup_rec(int base, int n, int u, int H) {
+    const int g = u & ~(kYGroupRows - 1);
+    const int rows = n - g < kYGroupRows ? n - g : kYGroupRows;
+    return make_int2((base + g) * H + (u - g) * kYBlockCols, rows);
+}
 
 // Expert GEMM jobs.  A routed job covers slots [0, U_max) of the active-expert
 // list; a dense job is one expert over all M rows.
@@ -129,6 +148,7 @@ struct ExpertJob {
     bool a_tok = false;
     const SlotRecord* record = nullptr;  // gate_up with ids: record the resolved slots
     const int32_t* count = nullptr;      // active list whose entries past *count are stale
+    bool ygroup = false;                 // down: y grouped (ygroup_rec) instead of [rows][N_out]
     float swiglu_limit = 0.0f;           // gate_up: clamped SwiGLU limit (0: unclamped)
     // NVFP4 activations (NVFP4 weights only): the activations are NVFP4 codes
     // [rows][K/2] + E4M3 scales [rows][K/16] with global a_global, or
@@ -186,9 +206,13 @@ hipError_t launch_gate_up_bf16(const ExpertJob& job, const uint16_t* a, uint16_t
                                float* partials, hipStream_t stream);
 hipError_t launch_down_bf16(const ExpertJob& job, const uint16_t* h, float* y, hipStream_t stream);
 
+// y [M*k][H] by pair, or grouped when yrec != nullptr (pair p's row at
+// yrec[p]); y_sh [M][H], or grouped as a dense down writes it (rows 0..M-1 as
+// one expert's) when ysh_grouped.
 hipError_t launch_finalize(const float* y, const float* topk_w, const float* y_sh,
                            const uint16_t* residual, const uint16_t* gamma, float eps, int M,
                            int H, int k, uint16_t* out, uint16_t* residual_out, uint8_t* out_q,
-                           uint8_t* out_s, hipStream_t stream);
+                           uint8_t* out_s, hipStream_t stream, const int2* yrec = nullptr,
+                           bool ysh_grouped = false);
 
 }  // namespace moe

@@ -92,8 +92,10 @@ constexpr size_t kBucketLdsMax = (size_t)(5 * kMaxE + kBucketThreads) * 4 + (siz
 // Route step: one workgroup builds the expert buckets, 8-row tiles and the
 // active-expert list from topk_ids (in a launch after the top-k one, so the
 // ids written by the top-k workgroups are visible without a device-scope
-// fence).
-__device__ inline void bucket_step(int M, int E, int k, const moe_routing& route, uint8_t* lds) {
+// fence).  With yrec, also each pair's row of a grouped y of H columns
+// (ygroup_rec).
+__device__ inline void bucket_step(int M, int E, int k, const moe_routing& route, uint8_t* lds, int H = 0,
+                                   int2* yrec = nullptr) {
     const int tid = threadIdx.x;
 
     int* s_cnt = reinterpret_cast<int*>(lds);
@@ -191,7 +193,9 @@ __device__ inline void bucket_step(int M, int E, int k, const moe_routing& route
                 int rank = 0;
                 for (int w = 0; w < (rl >> 5); ++w) rank += __popc(s_bm[e * W + w]);
                 rank += __popc(s_bm[e * W + (rl >> 5)] & ((1u << (rl & 31)) - 1u));
-                route.bucket[s_off[e] + s_run[e] + rank] = r0 * k + tid + kBucketThreads * q;
+                const int pair = r0 * k + tid + kBucketThreads * q;
+                route.bucket[s_off[e] + s_run[e] + rank] = pair;
+                if (yrec) yrec[pair] = ygroup_rec(s_off[e], s_cnt[e], s_run[e] + rank, H);
             }
         }
         __syncthreads();

@@ -128,6 +128,15 @@ EDGE = [
     dict(M=72, H=512, E=16, k=8, I=256, wfmt=synth.MXFP4, sfmt=synth.FP8S, I_sh=384, swiglu_limit=0.5),
     # a bf16 shared expert with 576 pairs (its down rides the route step's launch)
     dict(M=72, H=512, E=32, k=8, I=256, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=256),
+    # y of 4 MiB or more is written grouped (16-row groups of an expert's rows, column blocks
+    # one after another): many pairs, K-streamed down with the MXFP4 shared expert riding (130
+    # rows: a 2-row last shared group); few pairs with the down by rows (NVFP4, its shared
+    # expert's down a launch of its own), K-streamed MXFP4 with few pairs, and W4A4 both ways
+    dict(M=130, H=1024, E=16, k=8, I=640, sfmt=synth.MXFP4, I_sh=640, bias="zipf:1.0"),
+    dict(M=60, H=2304, E=32, k=8, I=256, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=256),
+    dict(M=50, H=2688, E=16, k=8, I=640, sfmt=synth.MXFP4, I_sh=640),
+    dict(M=40, H=3584, E=16, k=8, I=640, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=640, act_fmt=synth.ACT_NVFP4),
+    dict(M=60, H=2304, E=32, k=8, I=256, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=256, act_fmt=synth.ACT_NVFP4),
 ]
 
 
