@@ -158,6 +158,24 @@ __device__ __forceinline__ bool resolve(const StreamJob& J, int slot, Tokens& t)
     return true;
 }
 
+// Item -> (slot, column block) of a dense job, whose slots are passes over
+// the same weights: the passes of one column block take consecutive items of
+// one XCD (a launch's workgroups go to the eight XCDs in turn), so they run
+// together there and the later ones find the weights in that XCD's L2.
+// Routed jobs (and a column-block count that is not a multiple of 8) keep
+// slot-major items.
+__device__ __forceinline__ void item_of(const StreamJob& J, int bid, int nblk, int& slot, int& blk) {
+    if (J.dense && nblk % 8 == 0) {
+        const int passes = (J.M + kPassRows - 1) / kPassRows;
+        const int q = bid >> 3;
+        slot = q % passes;
+        blk = (q / passes) * 8 + (bid & 7);
+    } else {
+        slot = bid / nblk;
+        blk = bid % nblk;
+    }
+}
+
 // Slot -> (expert, bucket range) from the top-k ids, for P = M*k <= kIdsPairs
 // pairs (two per thread: pairs tid and tid + kThreads): the slot-th chosen
 // expert in ascending id order, its bucket base (the pairs with a smaller
@@ -1109,8 +1127,8 @@ __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS)
     const int I = J.N / 2, K = J.K;
     constexpr int GCOLS = 32 * GMB;  // output columns per workgroup
     const int ks = bid % J.splits;
-    const int blk = (bid / J.splits) % J.nblk;
-    const int slot = bid / (J.splits * J.nblk);
+    int slot, blk;
+    item_of(J, bid / J.splits, J.nblk, slot, blk);
     Tokens tk;
     __shared__ int s_list[kIdsPairs], s_tok[kIdsPairs];
     if (!resolve_item(J, slot, tk, s_list, s_tok)) return;
@@ -1331,8 +1349,8 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0,
     const int bid = second ? (int)blockIdx.x : (int)blockIdx.x - n2;
     const int H = J.N, I = J.K;
     constexpr int RB = 64 * MB;
-    const int blk = bid % J.nblk;
-    const int slot = bid / J.nblk;
+    int slot, blk;
+    item_of(J, bid, J.nblk, slot, blk);
     Tokens tk;
     __shared__ int s_list[kIdsPairs], s_tok[kIdsPairs];
     if (!resolve_item(J, slot, tk, s_list, s_tok)) return;
@@ -1448,8 +1466,8 @@ template <int FMT, int S, int D>
 __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down_rows(StreamJob J, float* __restrict__ y) {
     const int H = J.N, K = J.K;
     const int bpw = J.span;
-    const int item = blockIdx.x % J.nblk;
-    const int slot = blockIdx.x / J.nblk;
+    int slot, item;
+    item_of(J, blockIdx.x, J.nblk, slot, item);
     Tokens tk;
     __shared__ int s_list[kIdsPairs], s_tok[kIdsPairs];
     if (!resolve_item(J, slot, tk, s_list, s_tok)) return;
