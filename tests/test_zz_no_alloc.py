@@ -27,14 +27,20 @@ def _noalloc_run(d):
 
 
 def test_noalloc_matches_layer_two_calls_second_smaller():
-    # first: the skewed-routing workload (48 rows, 480 pairs: the bucketed
-    # launch sequence, 14.8 MiB of scratch); second: the tiny workload (4 rows,
-    # 16 pairs: the few-pairs launches, 0.08 MiB)
-    names = ["skew-m48-h4096-e512-k10-nvfp4", "tiny-m4-h1024-e16-k4-mxfp4"]
-    staged = []
-    for n in names:
-        inp = synth.make_inputs(n, seed=synth.seed_of(n))
-        staged.append((n, staging.to_device(inp, DEV)))
+    # each call needs less scratch than the one before: the skewed-routing
+    # workload (48 rows, 480 pairs: the few-pairs launches, a grouped y of
+    # 7.5 MiB); 1040 pairs (the route step's launch sequence, a grouped y of
+    # 4.1 MiB, the MXFP4 shared expert riding along); the tiny workload (4 rows,
+    # 16 pairs, y by pair); then the first again over the smaller calls'
+    # leftovers in the shared scratch
+    skew = "skew-m48-h4096-e512-k10-nvfp4"
+    staged = [(skew, staging.to_device(synth.make_inputs(skew, seed=synth.seed_of(skew)), DEV))]
+    mid = synth.custom_shape(M=130, H=1024, E=16, k=8, I=640, sfmt=synth.MXFP4, I_sh=640, bias="zipf:1.0")
+    staged.append((mid.name, staging.to_device(synth.make_inputs(mid, seed=41, pool_rows=4096), DEV)))
+    tiny = "tiny-m4-h1024-e16-k4-mxfp4"
+    staged.append((tiny, staging.to_device(synth.make_inputs(tiny, seed=synth.seed_of(tiny)), DEV)))
+    sizes = [d.layer().ws_bytes for _, d in staged]
+    assert sizes[0] > sizes[1] > sizes[2], sizes
     for n, d in staged:
         print(f"[noalloc] {n}", flush=True)
         got = _noalloc_run(d)
