@@ -624,8 +624,12 @@ __device__ __forceinline__ void stream_pass(const StreamJob& J, int e, const int
 // LDS buffers; the waves read ready operands from there, and the register
 // ring holds weights only.  One barrier per quad: tile q+1 is written while
 // tile q is read, the barrier publishes it.
-constexpr int kTileRowH = 1040;                     // bytes per row: 512 f16 + 16 (staggers banks)
-constexpr int kTileBytesH = kPassRows * kTileRowH;  // one buffer, sized for two N-blocks
+constexpr int kTileRowH = 1040;  // bytes per row: 512 f16 + 16 (staggers banks)
+// one buffer of a pass of NB N-blocks
+template <int NB>
+constexpr int tile_bytes_h() {
+    return 16 * NB * kTileRowH;
+}
 
 template <int NB>
 struct ActShare {
@@ -804,10 +808,11 @@ __device__ __forceinline__ void quadw_steps(RingW<MB, DQ>& R, int v, const Coord
 }
 
 // An NVFP4 pass as stream_pass, with the activation tiles in LDS (tiles: two
-// kTileBytesH buffers; rsmax: kPassRows ints).  Every thread of the workgroup
+// tile_bytes_h<LB>() buffers, LB the N-blocks the layout is sized for; rsmax:
+// 16 * NB ints).  Every thread of the workgroup
 // must call it with the same arguments apart from the weight blocks (it has
 // barriers).
-template <int MB, int NB, int DQ, bool A4>
+template <int MB, int NB, int DQ, bool A4, int LB>
 __device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const int (&wblk)[MB], int arow0,
                                                 int npass, const int* src, int s0, int nst, int (&smax)[NB],
                                                 v4f (&acc)[MB][2], uint8_t* tiles, int* rsmax) {
@@ -851,19 +856,19 @@ __device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[mb][j] = v4f{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
-    tile_store<NB, A4>(P, tiles + (q0 & 1) * kTileBytesH, rsmax, npass);  // the tile of quad q sits in buffer q & 1
+    tile_store<NB, A4>(P, tiles + (q0 & 1) * tile_bytes_h<LB>(), rsmax, npass);  // the tile of quad q sits in buffer q & 1
     __syncthreads();
     for (int l0 = 0; l0 < nq; l0 += DQ) {
 #pragma unroll
         for (int v = 0; v < DQ; ++v) {
             const int q = q0 + l0 + v;  // the quad of slot v in this round
-            const uint8_t* tile = tiles + (q & 1) * kTileBytesH;
+            const uint8_t* tile = tiles + (q & 1) * tile_bytes_h<LB>();
             v8h B[NB][4];
             tile_read<NB>(tile, 0, B);
             tile_load<NB, A4>(P, ca, to, q + 1, s_end);  // in flight over the quad's steps
             quadw_steps<MB, NB, DQ, 0>(R, v, c, q + DQ, s_end, tile, B, acc);
             // tile q+1 into the other buffer (its reads ended at the last barrier)
-            tile_store<NB, A4>(P, tiles + ((q + 1) & 1) * kTileBytesH, rsmax, npass);
+            tile_store<NB, A4>(P, tiles + ((q + 1) & 1) * tile_bytes_h<LB>(), rsmax, npass);
             __syncthreads();
         }
     }
@@ -879,13 +884,23 @@ __device__ __forceinline__ void stream_pass_lds(const StreamJob& J, int e, const
 // NVFP4 path.  Rows are 528 bytes apart (512 codes + 16): the 16 rows a
 // wave's lanes read at one step start on 16 different bank groups, and a
 // lane's reads of the quad's steps are immediate offsets from one address.
-constexpr int kTileRowMX = 528;                                  // row stride of the codes (512 + 16)
-constexpr int kTileCodesMX = kPassRows * kTileRowMX;             // codes of one buffer (two N-blocks)
-constexpr int kTileScalesMX = kPassRows * 16;                    // the rows' scale bytes
-// + a dump area where threads without a scale dword store theirs: every
-// store of the tile is unconditional, so the loop body stays one basic block
-// (a branch there lets the compiler sink the MFMAs past the barriers)
-constexpr int kTileBytesMX = kTileCodesMX + kTileScalesMX + 4 * kThreads;
+constexpr int kTileRowMX = 528;  // row stride of the codes (512 + 16)
+// One buffer of a pass of NB N-blocks: the codes, the rows' scale bytes, and a
+// dump area where threads without a scale dword store theirs: every store of
+// the tile is unconditional, so the loop body stays one basic block (a branch
+// there lets the compiler sink the MFMAs past the barriers).
+template <int NB>
+constexpr int tile_codes_mx() {
+    return 16 * NB * kTileRowMX;
+}
+template <int NB>
+constexpr int tile_scales_mx() {
+    return 16 * NB * 16;
+}
+template <int NB>
+constexpr int tile_bytes_mx() {
+    return tile_codes_mx<NB>() + tile_scales_mx<NB>() + 4 * kThreads;
+}
 
 template <int NB>
 struct ActShareMX {
@@ -935,7 +950,8 @@ __device__ __forceinline__ void tile_load_mx(ActShareMX<NB>& P, const Coord<kFmt
     P.s = __builtin_amdgcn_raw_buffer_load_b32(c.ras, oks ? o.s + 16 * q : kOOB, 0, 0);
 }
 
-template <int NB>
+// LB: the N-blocks the buffer layout is sized for (the kernel's largest pass).
+template <int NB, int LB>
 __device__ __forceinline__ void tile_store_mx(const ActShareMX<NB>& P, uint8_t* buf) {
     const int t = threadIdx.x;
 #pragma unroll
@@ -943,13 +959,14 @@ __device__ __forceinline__ void tile_store_mx(const ActShareMX<NB>& P, uint8_t* 
         const int li = t + kThreads * k, row = li >> 5, ch = li & 31;
         *reinterpret_cast<v4i*>(buf + row * kTileRowMX + 16 * ch) = P.c[k];
     }
-    *reinterpret_cast<uint32_t*>(buf + kTileCodesMX + (t < 64 * NB ? 4 * t : kTileScalesMX + 4 * t)) = P.s;
+    *reinterpret_cast<uint32_t*>(buf + tile_codes_mx<LB>() + (t < 64 * NB ? 4 * t : tile_scales_mx<LB>() + 4 * t)) =
+        P.s;
 }
 
 // The lane's B operand of step u of the tile in buf for N-block j: row
 // 16j + i, codes [128u + 16g, +16) and [128u + 64 + 16g, +16) (the layout of
 // the FP8 operand of the scaled MFMA), and the row's scale dword of step u.
-template <int NB>
+template <int NB, int LB>
 __device__ __forceinline__ void tile_read_mx(const uint8_t* buf, int u, v8i (&B)[NB], uint32_t (&bs)[NB]) {
     const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -959,7 +976,7 @@ __device__ __forceinline__ void tile_read_mx(const uint8_t* buf, int u, v8i (&B)
         const v4i c0 = *reinterpret_cast<const v4i*>(p + 128 * u);
         const v4i c1 = *reinterpret_cast<const v4i*>(p + 128 * u + 64);
         B[j] = v8i{c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-        bs[j] = *reinterpret_cast<const uint32_t*>(buf + kTileCodesMX + 16 * row + 4 * u);
+        bs[j] = *reinterpret_cast<const uint32_t*>(buf + tile_codes_mx<LB>() + 16 * row + 4 * u);
     }
 }
 
@@ -975,7 +992,7 @@ __device__ __forceinline__ void ringw_load_scales_mx(RingW<MB, DQ>& R, int v, co
 // The four steps of the quad in slot v, the B operands of step U given and
 // those of step U+1 read from the tile meanwhile; each step's weight slot is
 // refilled with quad qn right after its MFMAs.
-template <int MB, int NB, int DQ, int U>
+template <int MB, int NB, int DQ, int LB, int U>
 __device__ __forceinline__ void quadw_steps_mx(RingW<MB, DQ>& R, int v, const Coord<kFmtMX, MB, NB>& c, int qn,
                                                int s_end, const uint8_t* tile, const v8i (&B)[NB],
                                                const uint32_t (&bs)[NB], v4f (&acc)[MB][2]) {
@@ -983,7 +1000,7 @@ __device__ __forceinline__ void quadw_steps_mx(RingW<MB, DQ>& R, int v, const Co
         __builtin_amdgcn_sched_barrier(0);
         v8i Bn[NB];
         uint32_t bsn[NB];
-        if constexpr (U < 3) tile_read_mx<NB>(tile, U + 1, Bn, bsn);
+        if constexpr (U < 3) tile_read_mx<NB, LB>(tile, U + 1, Bn, bsn);
         const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -997,14 +1014,14 @@ __device__ __forceinline__ void quadw_steps_mx(RingW<MB, DQ>& R, int v, const Co
         }
         if constexpr (U == 3) ringw_load_scales_mx<MB, NB, DQ>(R, v, c, qn, s_end);
         ringw_load_step<MB, NB, DQ>(R, v, U, c, qn, s_end);
-        quadw_steps_mx<MB, NB, DQ, U + 1>(R, v, c, qn, s_end, tile, Bn, bsn, acc);
+        quadw_steps_mx<MB, NB, DQ, LB, U + 1>(R, v, c, qn, s_end, tile, Bn, bsn, acc);
     }
 }
 
 // An MXFP4 pass as stream_pass, with the activation tiles in LDS (tiles: two
-// kTileBytesMX buffers).  Every thread of the workgroup must call it with the
+// tile_bytes_mx<LB>() buffers).  Every thread of the workgroup must call it with the
 // same arguments apart from the weight blocks (it has barriers).
-template <int MB, int NB, int DQ>
+template <int MB, int NB, int DQ, int LB>
 __device__ __forceinline__ void stream_pass_lds_mx(const StreamJob& J, int e, const int (&wblk)[MB], int arow0,
                                                    int npass, const int* src, int s0, int nst, v4f (&acc)[MB][2],
                                                    uint8_t* tiles) {
@@ -1033,20 +1050,20 @@ __device__ __forceinline__ void stream_pass_lds_mx(const StreamJob& J, int e, co
         for (int j = 0; j < 2; ++j) acc[mb][j] = v4f{0.f, 0.f, 0.f, 0.f};
     // the tile of quad q sits in buffer q & 1
     __syncthreads();  // the previous pass's reads of the LDS are done
-    tile_store_mx<NB>(P, tiles + (q0 & 1) * kTileBytesMX);
+    tile_store_mx<NB, LB>(P, tiles + (q0 & 1) * tile_bytes_mx<LB>());
     __syncthreads();
     for (int l0 = 0; l0 < nq; l0 += DQ) {
 #pragma unroll
         for (int v = 0; v < DQ; ++v) {
             const int q = q0 + l0 + v;  // the quad of slot v in this round
-            const uint8_t* tile = tiles + (q & 1) * kTileBytesMX;
+            const uint8_t* tile = tiles + (q & 1) * tile_bytes_mx<LB>();
             v8i B[NB];
             uint32_t bs[NB];
-            tile_read_mx<NB>(tile, 0, B, bs);
+            tile_read_mx<NB, LB>(tile, 0, B, bs);
             tile_load_mx<NB>(P, ca, to, q + 1, s_end);  // in flight over the quad's steps
-            quadw_steps_mx<MB, NB, DQ, 0>(R, v, c, q + DQ, s_end, tile, B, bs, acc);
+            quadw_steps_mx<MB, NB, DQ, LB, 0>(R, v, c, q + DQ, s_end, tile, B, bs, acc);
             // tile q+1 into the other buffer (its reads ended at the last barrier)
-            tile_store_mx<NB>(P, tiles + ((q + 1) & 1) * kTileBytesMX);
+            tile_store_mx<NB, LB>(P, tiles + ((q + 1) & 1) * tile_bytes_mx<LB>());
             __syncthreads();
         }
     }
@@ -1110,8 +1127,10 @@ constexpr int kGateMB = 2, kGateMBSmall = 1;
 // Workgroups [0, n2) take items of a second job J2 of the same format (the
 // FP4 shared expert riding along the routed experts; first, so its few long
 // items do not trail the launch), [n2, nmain) items of job J0, later ones a
-// bf16 shared-expert stage.
-template <int FMT, bool FUSED, int GMB>
+// bf16 shared-expert stage.  PR: rows per pass, 32 (two 16-row N-blocks) or 16
+// (one: at 16 or fewer token rows no expert has more, and the smaller tiles
+// and registers let a third workgroup onto each CU).
+template <int FMT, bool FUSED, int GMB, int PR>
 __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS) void k_gate_up(
     StreamJob J0, uint8_t* __restrict__ h_q0, uint8_t* __restrict__ h_s0, float* __restrict__ part, int nmain,
     Bf16Side side, int stage, StreamJob J2, uint8_t* __restrict__ h_q2, uint8_t* __restrict__ h_s2, int n2) {
@@ -1165,15 +1184,17 @@ __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS)
     // fused epilogue: gate [0, GCOLS), up [GCOLS, 2*GCOLS) per row.  NVFP4 keeps
     // the activation tiles of two quads in the same LDS: the epilogue runs
     // after the pass's last barrier, when no wave reads a tile any more.
-    constexpr int kGBytes = kPassRows * (2 * GCOLS + 1) * 4;
-    constexpr int kTileLds = kNVW<FMT> ? 2 * kTileBytesH : 2 * kTileBytesMX;
+    static_assert(PR == 16 || PR == 32, "passes of one or two 16-row N-blocks");
+    constexpr int NBX = PR / 16;
+    constexpr int kGBytes = PR * (2 * GCOLS + 1) * 4;
+    constexpr int kTileLds = kNVW<FMT> ? 2 * tile_bytes_h<NBX>() : 2 * tile_bytes_mx<NBX>();
     constexpr int kLdsBytes = kTileLds > kGBytes ? kTileLds : kGBytes;
     __shared__ __align__(16) uint8_t sLds[kLdsBytes];
     float(*sG)[2 * GCOLS + 1] = reinterpret_cast<float(*)[2 * GCOLS + 1]>(sLds);
-    __shared__ int s_smax[kPassRows];
+    __shared__ int s_smax[PR];
 
-    for (int t0 = 0; t0 < tk.n; t0 += kPassRows) {
-        const int npass = min(kPassRows, tk.n - t0);
+    for (int t0 = 0; t0 < tk.n; t0 += PR) {
+        const int npass = min(PR, tk.n - t0);
         const int arow0 = tk.base + t0;
         // token-ordered activations: gather the pass's rows (tokens resolved
         // with the slot, or read from the bucket here)
@@ -1190,13 +1211,16 @@ __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS)
         }
         v4f acc[GMB][2];
         int smax[2] = {0, 0};
-        if (npass > 16) {
+        // NB = 2 only where a pass can hold two N-blocks (the NB = 1 code is
+        // written out for both kernels so each compiles as its own)
+        if (NBX > 1 && npass > 16) {
             int sm[2];
+            constexpr int NB2 = NBX > 1 ? 2 : 1;
             if constexpr (kNVW<FMT>)
-                stream_pass_lds<GMB, 2, MOE_NV_DQ, kA4<FMT>>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm, acc, sLds,
-                                                             s_smax);
+                stream_pass_lds<GMB, NB2, MOE_NV_DQ, kA4<FMT>, NBX>(J, tk.e, wblk, arow0, npass, src, s0, nst,
+                                                               reinterpret_cast<int(&)[NB2]>(sm), acc, sLds, s_smax);
             else {  // MXFP4: the activation tile in LDS (measured faster from one row per pass up)
-                stream_pass_lds_mx<GMB, 2, MOE_MX_DQ>(J, tk.e, wblk, arow0, npass, src, s0, nst, acc, sLds);
+                stream_pass_lds_mx<GMB, NB2, MOE_MX_DQ, NBX>(J, tk.e, wblk, arow0, npass, src, s0, nst, acc, sLds);
                 sm[0] = sm[1] = 0;
             }
             smax[0] = sm[0];
@@ -1204,10 +1228,10 @@ __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS)
         } else {
             int sm[1];
             if constexpr (kNVW<FMT>)
-                stream_pass_lds<GMB, 1, MOE_NV_DQ, kA4<FMT>>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm, acc, sLds,
-                                                             s_smax);
+                stream_pass_lds<GMB, 1, MOE_NV_DQ, kA4<FMT>, NBX>(J, tk.e, wblk, arow0, npass, src, s0, nst, sm, acc,
+                                                                  sLds, s_smax);
             else {
-                stream_pass_lds_mx<GMB, 1, MOE_MX_DQ>(J, tk.e, wblk, arow0, npass, src, s0, nst, acc, sLds);
+                stream_pass_lds_mx<GMB, 1, MOE_MX_DQ, NBX>(J, tk.e, wblk, arow0, npass, src, s0, nst, acc, sLds);
                 sm[0] = 0;
             }
             smax[0] = sm[0];
@@ -1232,7 +1256,7 @@ __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS)
             __syncthreads();
             // SwiGLU + MXFP8 requant: 8 lanes per 32-column block, 4 columns each
             // (whole waves take part in every round, the row check is per lane).
-            for (int idx = threadIdx.x; idx < kPassRows * (GCOLS / 4); idx += kThreads) {
+            for (int idx = threadIdx.x; idx < PR * (GCOLS / 4); idx += kThreads) {
                 const int t = idx / (GCOLS / 4), q = idx % (GCOLS / 4);
                 float hv[4];
                 float fac = 1.0f;
@@ -1338,11 +1362,14 @@ constexpr int kDownMBWide = MOE_DOWN_MB_WIDE, kDownMB = 2;
 #define MOE_NT_Y_BYTES (32u << 20)
 #endif
 
-template <int FMT, int MB, bool NTY>
+template <int FMT, int MB, bool NTY, int PR>
 __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0, float* __restrict__ y0, StreamJob J2,
                                                                    float* __restrict__ y2, int n2) {
     // workgroups [0, n2) take items of a second job J2 (first: its few long
-    // items would otherwise trail the launch), [n2, nmain) items of J0
+    // items would otherwise trail the launch), [n2, nmain) items of J0.  PR:
+    // rows per pass, as in k_gate_up
+    static_assert(PR == 16 || PR == 32, "passes of one or two 16-row N-blocks");
+    constexpr int NBX = PR / 16;
     const bool second = (int)blockIdx.x < n2;  // uniform
     const StreamJob& J = second ? J2 : J0;
     float* __restrict__ y = second ? y2 : y0;
@@ -1364,11 +1391,11 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0,
     const float gs = kNVW<FMT> ? J.gscale[tk.e] : 1.0f;
     const float fa4 = kA4<FMT> ? act_global(J, tk.e) * gs : 0.0f;  // NVFP4 h: its global x the weights'
     // MXFP4: the h tiles in LDS (the NVFP4 formats stream h from registers)
-    __shared__ __align__(16) uint8_t sTile[FMT == kFmtMX ? 2 * kTileBytesMX : 16];
+    __shared__ __align__(16) uint8_t sTile[FMT == kFmtMX ? 2 * tile_bytes_mx<NBX>() : 16];
     constexpr int kDownDQ = MB > 2 ? MOE_MX_DOWN_DQ : MOE_MX_DQ;  // ring quads the registers allow
 
-    for (int t0 = 0; t0 < tk.n; t0 += kPassRows) {
-        const int npass = min(kPassRows, tk.n - t0);
+    for (int t0 = 0; t0 < tk.n; t0 += PR) {
+        const int npass = min(PR, tk.n - t0);
         const int arow0 = tk.base + t0;
         // output rows of the lane's activation rows: loaded before the ring so
         // they return first
@@ -1380,15 +1407,16 @@ __global__ __launch_bounds__(kThreads, MOE_MIN_BLOCKS) void k_down(StreamJob J0,
         }
         v4f acc[MB][2];
         int smax[2] = {0, 0};
+        constexpr int NB2 = NBX > 1 ? 2 : 1;  // NB = 2 only where a pass can hold two N-blocks
         if constexpr (FMT == kFmtMX) {  // the workgroup shares the h tile in LDS
-            if (npass > 16)
-                stream_pass_lds_mx<MB, 2, kDownDQ>(J, tk.e, wblk, arow0, npass, nullptr, 0, nst, acc, sTile);
+            if (NBX > 1 && npass > 16)
+                stream_pass_lds_mx<MB, NB2, kDownDQ, NBX>(J, tk.e, wblk, arow0, npass, nullptr, 0, nst, acc, sTile);
             else
-                stream_pass_lds_mx<MB, 1, kDownDQ>(J, tk.e, wblk, arow0, npass, nullptr, 0, nst, acc, sTile);
-        } else if (npass > 16) {
+                stream_pass_lds_mx<MB, 1, kDownDQ, NBX>(J, tk.e, wblk, arow0, npass, nullptr, 0, nst, acc, sTile);
+        } else if (NBX > 1 && npass > 16) {
             int sm[2];
-            stream_pass<FMT, MB, 2, ring_quads<FMT, MB, 2>(), 4>(J, tk.e, wblk, arow0, npass, nullptr, 0,
-                                                                                 nst, sm, acc);
+            stream_pass<FMT, MB, NB2, ring_quads<FMT, MB, NB2>(), 4>(J, tk.e, wblk, arow0, npass, nullptr, 0, nst,
+                                                                     reinterpret_cast<int(&)[NB2]>(sm), acc);
             smax[0] = sm[0];
             smax[1] = sm[1];
         } else {
@@ -1676,19 +1704,34 @@ size_t gate_up_fp4_partials_bytes(const ExpertJob& job) {
     return align_up((size_t)p.splits * out_rows_of(job) * 2 * job.N_out * sizeof(float));
 }
 
-// One gate_up launch with the kernel of gmb weight blocks per wave.
-template <int F, bool FU>
-hipError_t launch_gu(int gmb, dim3 g, hipStream_t stream, const StreamJob& J, uint8_t* h_q, uint8_t* h_s,
-                     float* partials, int nmain, const Bf16Side& side, int stage, const StreamJob& J2, uint8_t* hq2,
-                     uint8_t* hs2, int n2) {
+// Rows per pass of a launch: 16 when its jobs have at most 16 token rows (an
+// expert gets at most one row per token: one 16-row N-block per pass, with
+// half the LDS tiles and fewer registers, so three workgroups fit on a CU;
+// measured at 7 rows of NVFP4 activations 85.2 -> 80.8 us per step, decode
+// 423 -> 419 us), else 32.
+int pass_rows(const ExpertJob& j, const ExpertJob* j2) { return j.M <= 16 && (!j2 || j2->M <= 16) ? 16 : 32; }
+
+// One gate_up launch with the kernel of gmb weight blocks per wave and pr rows per pass.
+template <int F, bool FU, int PR>
+hipError_t launch_gu_pr(int gmb, dim3 g, hipStream_t stream, const StreamJob& J, uint8_t* h_q, uint8_t* h_s,
+                        float* partials, int nmain, const Bf16Side& side, int stage, const StreamJob& J2,
+                        uint8_t* hq2, uint8_t* hs2, int n2) {
     if (gmb == kGateMBSmall) {
-        hipLaunchKernelGGL((k_gate_up<F, FU, kGateMBSmall>), g, dim3(kThreads), 0, stream, J, h_q, h_s, partials,
+        hipLaunchKernelGGL((k_gate_up<F, FU, kGateMBSmall, PR>), g, dim3(kThreads), 0, stream, J, h_q, h_s, partials,
                            nmain, side, stage, J2, hq2, hs2, n2);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((k_gate_up<F, FU, kGateMB>), g, dim3(kThreads), 0, stream, J, h_q, h_s, partials, nmain, side,
-                       stage, J2, hq2, hs2, n2);
+    hipLaunchKernelGGL((k_gate_up<F, FU, kGateMB, PR>), g, dim3(kThreads), 0, stream, J, h_q, h_s, partials, nmain,
+                       side, stage, J2, hq2, hs2, n2);
     return hipGetLastError();
+}
+template <int F, bool FU>
+hipError_t launch_gu(int pr, int gmb, dim3 g, hipStream_t stream, const StreamJob& J, uint8_t* h_q, uint8_t* h_s,
+                     float* partials, int nmain, const Bf16Side& side, int stage, const StreamJob& J2, uint8_t* hq2,
+                     uint8_t* hs2, int n2) {
+    return pr == 16 ? launch_gu_pr<F, FU, 16>(gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2, hq2, hs2, n2)
+                    : launch_gu_pr<F, FU, 32>(gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2, hq2, hs2,
+                                              n2);
 }
 
 hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const uint8_t* a_s, uint8_t* h_q,
@@ -1723,17 +1766,21 @@ hipError_t launch_gate_up_fp4(const ExpertJob& job, const uint8_t* a_q, const ui
     uint8_t* hq2 = n2 ? second.h_q : h_q;
     uint8_t* hs2 = n2 ? second.h_s : h_s;
     const int nmain = blocks + n2;
+    const int pr = pass_rows(job, n2 ? second.job : nullptr);
     if (p.splits == 1) {
         if (job.a_nvfp4)
-            return launch_gu<kFmtNV4, true>(gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2, hq2, hs2, n2);
+            return launch_gu<kFmtNV4, true>(pr, gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2, hq2, hs2,
+                                            n2);
         if (mx)
-            return launch_gu<kFmtMX, true>(gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2, hq2, hs2, n2);
-        return launch_gu<kFmtNV, true>(gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2, hq2, hs2, n2);
+            return launch_gu<kFmtMX, true>(pr, gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2, hq2, hs2,
+                                           n2);
+        return launch_gu<kFmtNV, true>(pr, gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2, hq2, hs2,
+                                       n2);
     }
-    hipError_t e = mx ? launch_gu<kFmtMX, false>(gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2, hq2,
-                                                 hs2, n2)
-                      : launch_gu<kFmtNV, false>(gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2, hq2,
-                                                 hs2, n2);
+    hipError_t e = mx ? launch_gu<kFmtMX, false>(pr, gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2,
+                                                 hq2, hs2, n2)
+                      : launch_gu<kFmtNV, false>(pr, gmb, g, stream, J, h_q, h_s, partials, nmain, side, stage, J2,
+                                                 hq2, hs2, n2);
     if (e != hipSuccess) return e;
     const int threads = rows * (job.N_out / 32) * 8;
     hipLaunchKernelGGL(k_swiglu_quant, dim3((threads + kThreads - 1) / kThreads), dim3(kThreads), 0, stream,
@@ -1771,9 +1818,12 @@ hipError_t launch_down_rows(const StreamJob& J, int slots, float* y, hipStream_t
 }
 
 template <int FMT, int MB, bool NTY>
-hipError_t launch_down_k(dim3 g, hipStream_t stream, const StreamJob& J, float* y, const StreamJob& J2, float* y2,
-                         int n2) {
-    hipLaunchKernelGGL((k_down<FMT, MB, NTY>), g, dim3(kThreads), 0, stream, J, y, J2, y2, n2);
+hipError_t launch_down_k(int pr, dim3 g, hipStream_t stream, const StreamJob& J, float* y, const StreamJob& J2,
+                         float* y2, int n2) {
+    if (pr == 16)
+        hipLaunchKernelGGL((k_down<FMT, MB, NTY, 16>), g, dim3(kThreads), 0, stream, J, y, J2, y2, n2);
+    else
+        hipLaunchKernelGGL((k_down<FMT, MB, NTY, 32>), g, dim3(kThreads), 0, stream, J, y, J2, y2, n2);
     return hipGetLastError();
 }
 
@@ -1808,17 +1858,18 @@ hipError_t launch_down_fp4(const ExpertJob& job, const uint8_t* h_q, const uint8
     const int nmain = n1 + n2;
     const dim3 g(nmain), b(kThreads);
     const bool nty = (size_t)out_rows_of(job) * job.N_out * sizeof(float) >= MOE_NT_Y_BYTES;
+    const int pr = pass_rows(job, fold ? second.job : nullptr);
     if (wide)
-        return nty ? launch_down_k<kFmtMX, kDownMBWide, true>(g, stream, J, y, J2, y2, n2)
-                   : launch_down_k<kFmtMX, kDownMBWide, false>(g, stream, J, y, J2, y2, n2);
+        return nty ? launch_down_k<kFmtMX, kDownMBWide, true>(pr, g, stream, J, y, J2, y2, n2)
+                   : launch_down_k<kFmtMX, kDownMBWide, false>(pr, g, stream, J, y, J2, y2, n2);
     if (mx)
-        return nty ? launch_down_k<kFmtMX, kDownMB, true>(g, stream, J, y, J2, y2, n2)
-                   : launch_down_k<kFmtMX, kDownMB, false>(g, stream, J, y, J2, y2, n2);
+        return nty ? launch_down_k<kFmtMX, kDownMB, true>(pr, g, stream, J, y, J2, y2, n2)
+                   : launch_down_k<kFmtMX, kDownMB, false>(pr, g, stream, J, y, J2, y2, n2);
     if (job.a_nvfp4)
-        return nty ? launch_down_k<kFmtNV4, kDownMB, true>(g, stream, J, y, J2, y2, n2)
-                   : launch_down_k<kFmtNV4, kDownMB, false>(g, stream, J, y, J2, y2, n2);
-    return nty ? launch_down_k<kFmtNV, kDownMB, true>(g, stream, J, y, J2, y2, n2)
-               : launch_down_k<kFmtNV, kDownMB, false>(g, stream, J, y, J2, y2, n2);
+        return nty ? launch_down_k<kFmtNV4, kDownMB, true>(pr, g, stream, J, y, J2, y2, n2)
+                   : launch_down_k<kFmtNV4, kDownMB, false>(pr, g, stream, J, y, J2, y2, n2);
+    return nty ? launch_down_k<kFmtNV, kDownMB, true>(pr, g, stream, J, y, J2, y2, n2)
+               : launch_down_k<kFmtNV, kDownMB, false>(pr, g, stream, J, y, J2, y2, n2);
 }
 
 }  // namespace moe
