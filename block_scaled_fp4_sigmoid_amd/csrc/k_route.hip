@@ -40,7 +40,7 @@ RouterPlan router_plan(int M, int H, int E) {
     int splits = 1;
     for (int d = 1; d <= nsteps; ++d)
         if (nsteps % d == 0 && d <= want && d <= 32) splits = d;
-    return RouterPlan{splits, H / splits, rg};
+    return RouterPlan{splits, H / splits, rg, M <= 16 && splits > 1 ? (splits + 3) & ~3 : 0};
 }
 
 __device__ __forceinline__ void split3(float w, uint32_t& b1, uint32_t& b2, uint32_t& b3) {
@@ -60,7 +60,7 @@ __device__ __forceinline__ void split3(float w, uint32_t& b1, uint32_t& b2, uint
 template <int U, int NBT>
 __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restrict__ x,
                                                          const float* __restrict__ w_router,
-                                                         int M, int H, int E, int splits,
+                                                         int M, int H, int E, int splits, int sp,
                                                          int kchunk, int units, int nmain,
                                                          float* __restrict__ partials, int nquant,
                                                          uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
@@ -179,15 +179,18 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
     compute(RB);
     __builtin_amdgcn_sched_barrier(0);
     // lane holds D[4g + t][i]: expert te*16 + 4g + t, row r0 + 16j + i; stores
-    // of rows past M or experts past E go to an offset past the buffer (dropped)
-    const __amdgpu_buffer_rsrc_t rp = make_rsrc(partials, (uint32_t)splits * (uint32_t)M * (uint32_t)E * 4u);
+    // of rows past M or experts past E go to an offset past the buffer (dropped).
+    // Layout [splits][M][E], or [M][E][sp] (sp > 0)
+    const uint32_t nsl = (uint32_t)(sp ? sp : splits);
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(partials, nsl * (uint32_t)M * (uint32_t)E * 4u);
 #pragma unroll
     for (int j = 0; j < NBT; ++j) {
         const int r = r0 + j * 16 + i;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int ee = te * 16 + 4 * g + t;
-            const uint32_t off = (j < nb && r < M && ee < E) ? (((uint32_t)kc * M + r) * E + ee) * 4u : kOOB;
+            const uint32_t at = sp ? ((uint32_t)r * E + ee) * (uint32_t)sp + kc : ((uint32_t)kc * M + r) * E + ee;
+            const uint32_t off = (j < nb && r < M && ee < E) ? at * 4u : kOOB;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][t]), rp, off, 0, 0);
         }
     }
@@ -206,13 +209,13 @@ hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int 
     if (plan.kchunk % 128 != 0) return hipErrorInvalidValue;
     const bool wide = plan.kchunk % 256 == 0, one = M <= 16;
     if (wide && one)
-        hipLaunchKernelGGL((k_router_partials<4, 1>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
+        hipLaunchKernelGGL((k_router_partials<4, 1>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.sp, plan.kchunk,
                            units, blocks, partials, nquant, xq, xs, xg4, side1, stage1);
     else if (one)
-        hipLaunchKernelGGL((k_router_partials<2, 1>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
+        hipLaunchKernelGGL((k_router_partials<2, 1>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.sp, plan.kchunk,
                            units, blocks, partials, nquant, xq, xs, xg4, side1, stage1);
     else
-        hipLaunchKernelGGL((k_router_partials<2, kRouterNBT>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.kchunk,
+        hipLaunchKernelGGL((k_router_partials<2, kRouterNBT>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.sp, plan.kchunk,
                            units, blocks, partials, nquant, xq, xs, xg4, side1, stage1);
     return hipGetLastError();
 }
@@ -324,7 +327,7 @@ __device__ int select_topk(const uint64_t* s_ord, int E, int k, int lane) {
     return my_id;
 }
 
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials, int splits,
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials, int splits, int sp,
                                               const float* __restrict__ bias, int M, int E, int k,
                                               float routed_scale, float* __restrict__ logits_out,
                                               moe_routing route, Bf16Side side, int stage) {
@@ -341,10 +344,24 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += 256) {
-        // all partials of the expert in one round of loads (splits <= 32)
+        // all partials of the expert in one round of loads (splits <= 32):
+        // 16-byte loads in the expert-contiguous layout; summed in chunk order
         float p[32];
+        if (sp) {
+            const float* pe = partials + ((size_t)r * E + e) * sp;
 #pragma unroll
-        for (int u = 0; u < 32; ++u) p[u] = u < splits ? partials[((size_t)u * M + r) * E + e] : 0.f;
+            for (int q = 0; q < 8; ++q) {
+                const float4 v =
+                    4 * q < splits ? *reinterpret_cast<const float4*>(pe + 4 * q) : float4{0.f, 0.f, 0.f, 0.f};
+                p[4 * q] = v.x;
+                p[4 * q + 1] = v.y;
+                p[4 * q + 2] = v.z;
+                p[4 * q + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 32; ++u) p[u] = u < splits ? partials[((size_t)u * M + r) * E + e] : 0.f;
+        }
         float lg = p[0];
 #pragma unroll
         for (int u = 1; u < 32; ++u)
@@ -439,20 +456,20 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket_quant(int M, int E, i
     }
 }
 
-hipError_t launch_topk(const float* partials, int splits, const float* bias, int M, int E, int k,
+hipError_t launch_topk(const float* partials, int splits, int sp, const float* bias, int M, int E, int k,
                        float routed_scale, float* logits_out, const moe_routing& route, const Bf16Side& side2,
                        int stage2, hipStream_t stream) {
     const int extra2 = stage2 == kBf16None ? 0 : side2.blocks;
-    hipLaunchKernelGGL(k_topk, dim3(M + extra2), dim3(256), 0, stream, partials, splits, bias,
+    hipLaunchKernelGGL(k_topk, dim3(M + extra2), dim3(256), 0, stream, partials, splits, sp, bias,
                        M, E, k, routed_scale, logits_out, route, side2, stage2);
     return hipGetLastError();
 }
 
-hipError_t launch_topk_bucket(const float* partials, int splits, const float* bias, int M, int E,
+hipError_t launch_topk_bucket(const float* partials, int splits, int sp, const float* bias, int M, int E,
                               int k, float routed_scale, float* logits_out,
                               const moe_routing& route, const Bf16Side& side2, int stage2,
                               const Bf16Side& side3, int stage3, hipStream_t stream, int H, int2* yrec) {
-    hipError_t e = launch_topk(partials, splits, bias, M, E, k, routed_scale, logits_out, route, side2, stage2,
+    hipError_t e = launch_topk(partials, splits, sp, bias, M, E, k, routed_scale, logits_out, route, side2, stage2,
                                stream);
     if (e != hipSuccess) return e;
     const int extra3 = stage3 == kBf16None ? 0 : side3.blocks;

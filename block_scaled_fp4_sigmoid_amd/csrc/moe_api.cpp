@@ -99,7 +99,7 @@ struct RouteWs {
 RouteWs carve_route(Carver& c, int M, int H, int E) {
     RouteWs w;
     const RouterPlan p = router_plan(M, H, E);
-    w.partials = c.take<float>((size_t)p.splits * M * E);
+    w.partials = c.take<float>(router_partials_floats(p, M, E));
     return w;
 }
 
@@ -202,10 +202,10 @@ int moe_route_topk(const uint16_t* x, const float* logits_in, const float* w_rou
         e = launch_router_partials(x, w_router, M, H, E, p, w.partials, nullptr, nullptr, no_side(), kBf16None,
                                    stream);
         if (e == hipSuccess)
-            e = launch_topk_bucket(w.partials, p.splits, bias, M, E, k, routed_scale, logits_out, *route, no_side(),
+            e = launch_topk_bucket(w.partials, p.splits, p.sp, bias, M, E, k, routed_scale, logits_out, *route, no_side(),
                                    kBf16None, no_side(), kBf16None, stream);
     } else {
-        e = launch_topk_bucket(logits_in, 1, bias, M, E, k, routed_scale, nullptr, *route, no_side(), kBf16None,
+        e = launch_topk_bucket(logits_in, 1, 0, bias, M, E, k, routed_scale, nullptr, *route, no_side(), kBf16None,
                                no_side(), kBf16None, stream);
     }
     return hip_status(e);
@@ -592,7 +592,7 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
         hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, L.xqt, L.xst, s1,
                                               shb ? kBf16GateUp : kBf16None, stream, xg4);
         if (e == hipSuccess)
-            e = launch_topk(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale, logits_out, r, s2,
+            e = launch_topk(L.route.partials, p.splits, p.sp, d->router_bias, M, E, k, d->routed_scale, logits_out, r, s2,
                             shb ? kBf16Swiglu : kBf16None, stream);
         ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
         gu.swiglu_limit = d->swiglu_limit;
@@ -634,7 +634,7 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
     hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, L.xqt, L.xst, s1,
                                           shb ? kBf16GateUp : kBf16None, stream, xg4);
     if (e == hipSuccess)
-        e = launch_topk_bucket(L.route.partials, p.splits, d->router_bias, M, E, k, d->routed_scale, logits_out, r,
+        e = launch_topk_bucket(L.route.partials, p.splits, p.sp, d->router_bias, M, E, k, d->routed_scale, logits_out, r,
                                s2, shb ? kBf16Swiglu : kBf16None, s3, shb ? kBf16Down : kBf16None, stream, H,
                                yg ? L.yrec : nullptr);
     ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);

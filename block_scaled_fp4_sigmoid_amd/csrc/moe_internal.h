@@ -45,12 +45,21 @@ inline Bf16Side no_side() {
     Bf16Side s{};
     return s;
 }
+// The partial logits: split-major [splits][M][E] fp32 (sp = 0), or, at 16 or
+// fewer rows, expert-contiguous [M][E][sp] with sp = splits rounded up to a
+// multiple of 4 (an expert's partials of a row in whole 16-byte loads for the
+// top-k; at more rows the router's scattered 4-byte stores cost more).  One
+// split is the logits [M][E] either way.
 struct RouterPlan {
     int splits;     // K chunks whose partial logits the top-k step sums
     int kchunk;     // elements of H per chunk (multiple of 32)
     int row_groups; // groups of up to 64 rows
+    int sp;         // expert-contiguous slots per expert, or 0 (split-major)
 };
 RouterPlan router_plan(int M, int H, int E);
+inline size_t router_partials_floats(const RouterPlan& p, int M, int E) {
+    return (size_t)(p.sp ? p.sp : p.splits) * M * E;
+}
 
 // The routing launches optionally run one bf16 shared-expert stage each as
 // extra workgroups: side1 with the router, side2 with the top-k, side3 with
@@ -63,10 +72,10 @@ hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int 
                                   const RouterPlan& plan, float* partials, uint8_t* xq, uint8_t* xs,
                                   const Bf16Side& side1, int stage1, hipStream_t stream, float xg4 = 0.0f);
 // logits: the router partials (splits of them), or given logits (splits = 1).
-hipError_t launch_topk(const float* partials, int splits, const float* bias, int M, int E, int k,
+hipError_t launch_topk(const float* partials, int splits, int sp, const float* bias, int M, int E, int k,
                        float routed_scale, float* logits_out, const moe_routing& route, const Bf16Side& side2,
                        int stage2, hipStream_t stream);
-hipError_t launch_topk_bucket(const float* partials, int splits, const float* bias, int M, int E,
+hipError_t launch_topk_bucket(const float* partials, int splits, int sp, const float* bias, int M, int E,
                               int k, float routed_scale, float* logits_out,
                               const moe_routing& route, const Bf16Side& side2, int stage2,
                               const Bf16Side& side3, int stage3, hipStream_t stream, int H = 0,
