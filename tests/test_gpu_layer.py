@@ -137,6 +137,11 @@ EDGE = [
     dict(M=50, H=2688, E=16, k=8, I=640, sfmt=synth.MXFP4, I_sh=640),
     dict(M=40, H=3584, E=16, k=8, I=640, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=640, act_fmt=synth.ACT_NVFP4),
     dict(M=60, H=2304, E=32, k=8, I=256, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=256, act_fmt=synth.ACT_NVFP4),
+    # the 16-row-pass kernels (16 or fewer token rows) with one expert taking nearly every row, in
+    # both formats and K-streamed down; 17 rows take the 32-row kernels again
+    dict(M=16, H=512, E=8, k=2, I=640, sfmt=synth.MXFP4, I_sh=640, bias="zipf:3.0"),
+    dict(M=16, H=512, E=8, k=2, I=640, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=640, bias="zipf:3.0"),
+    dict(M=17, H=512, E=8, k=2, I=640, sfmt=synth.MXFP4, I_sh=640, bias="zipf:3.0"),
 ]
 
 
