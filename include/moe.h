@@ -326,7 +326,9 @@ int moe_expert_down_nvfp4a(const moe_weights *w2, const uint8_t *h_q, const uint
  * E4M3 code of the correctly rounded fp32 quotient v / s (round to nearest
  * even, saturating at +-448, NaN kept NaN), s the input's static scale; a
  * linear's output is s * the weight scale * the sum of the code products
- * (exact products, fp32 sums).
+ * (exact products; the FP8 matrix instruction adds each 32-long K step's
+ * products with a reduced internal precision before the fp32 accumulation,
+ * measured at rel-L2 about 4e-5 against fp32 sums).
  * gate_up: w13 FP8S [1, 2I, H] (rows [0, I) gate, [I, 2I) up); x bf16 [M, H]
  *   quantized with s_in; g and u rounded to bf16; h = bf16(silu(g) * u) (the
  *   clamped form with swiglu_limit > 0, as moe_expert_gate_up); h_q uint8
