@@ -56,8 +56,10 @@ __device__ __forceinline__ void split3(float w, uint32_t& b1, uint32_t& b2, uint
 }
 
 // U: K-steps of 32 per round of loads (two rounds in flight); NBT: 16-row
-// blocks of the row group (1 when M <= 16).
-template <int U, int NBT>
+// blocks of the row group (1 when M <= 16).  XS: the four waves of a
+// workgroup (four 16-expert tiles of the same K chunk and row group) share
+// each round's x tile through LDS instead of each loading it.
+template <int U, int NBT, bool XS>
 __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restrict__ x,
                                                          const float* __restrict__ w_router,
                                                          int M, int H, int E, int splits, int sp,
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int unit = blockIdx.x * 4 + wave;
-    if (unit >= units) return;
+    if (!XS && unit >= units) return;  // XS: every workgroup is full (units a multiple of 4)
     const int et = (E + 15) / 16;
     const int te = unit % et;
     const int kc = (unit / et) % splits;
@@ -110,9 +112,30 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
     // divides kchunk), and every load is unconditional: lanes past E or rows
     // past M read row 0 and are zeroed by a select, so no branch separates an
     // MFMA from the read of its accumulator.
+    // XS: the round's x tile, 16 NBT rows x 32 U values (bf16), rows padded by
+    // 16 bytes: 64 NBT U chunks of 16 bytes, chunk c = (row c / (4 U), part
+    // c % (4 U)), thread t loading chunks t, t + 256, ... (threads past the
+    // last chunk load none)
+    constexpr int kXRow = 64 * U + 16;  // bytes per tile row
+    constexpr int kXTile = 16 * NBT * kXRow;
+    constexpr int kXCh = 64 * NBT * U, kXN = (kXCh + 255) / 256;
+    __shared__ __align__(16) uint8_t sx[XS ? 2 * kXTile : 16];
+    const uint16_t* xrt[kXN];
+    int xso[kXN];
+    bool xct[kXN];
+#pragma unroll
+    for (int n = 0; n < kXN; ++n) {
+        const int c = threadIdx.x + 256 * n;
+        const int row = c / (4 * U), part = c % (4 * U);
+        const int r = r0 + row;
+        xct[n] = XS && c < kXCh;
+        xrt[n] = x + (size_t)(r < M ? r : 0) * H + 8 * part;
+        xso[n] = row * kXRow + 16 * part;
+    }
     struct Round {
         float4 wl[U][2];
-        v4i xb[U][NBT];
+        v4i xb[U][NBT];  // the lane's B operands (each wave loads them), or
+        v4i xt[kXN];     // the thread's chunks of the x tile (XS)
     };
     auto load = [&](int k0, Round& R) {
 #pragma unroll
@@ -120,8 +143,34 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
             const int kk = k0 + 32 * u + 8 * g;
             R.wl[u][0] = *reinterpret_cast<const float4*>(wrow + kk);
             R.wl[u][1] = *reinterpret_cast<const float4*>(wrow + kk + 4);
+            if constexpr (!XS) {
 #pragma unroll
-            for (int j = 0; j < NBT; ++j) R.xb[u][j] = load16(xr[j] + kk);
+                for (int j = 0; j < NBT; ++j) R.xb[u][j] = load16(xr[j] + kk);
+            }
+        }
+        if constexpr (XS) {
+#pragma unroll
+            for (int n = 0; n < kXN; ++n)
+                if (kXCh % 256 == 0 || xct[n]) R.xt[n] = load16(xrt[n] + k0);
+        }
+    };
+    // XS: the tile of a round into LDS buffer b (rows past M hold row 0's
+    // values; the MFMA inputs of those rows are zeroed below)
+    auto tile_store = [&](const Round& R, int b) {
+        if constexpr (XS) {
+#pragma unroll
+            for (int n = 0; n < kXN; ++n)
+                if (kXCh % 256 == 0 || xct[n]) *reinterpret_cast<v4i*>(sx + b * kXTile + xso[n]) = R.xt[n];
+        }
+    };
+    auto tile_read = [&](Round& R, int b) {
+        if constexpr (XS) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < NBT; ++j)
+                    R.xb[u][j] =
+                        *reinterpret_cast<const v4i*>(sx + b * kXTile + (16 * j + i) * kXRow + 64 * u + 16 * g);
         }
     };
     auto compute = [&](const Round& R) {
@@ -159,23 +208,46 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
     load(kbeg, RA);
     // (scheduling barriers keep each round's loads behind the previous
     // round's, so a round's MFMAs wait only for their own loads; the last
-    // pair of rounds is peeled, so no load is issued past the chunk)
+    // pair of rounds is peeled, so no load is issued past the chunk.  XS:
+    // round A's tile sits in LDS buffer 0, round B's in buffer 1; a tile is
+    // stored after the other buffer's round was read, one barrier each)
+    if constexpr (XS) {
+        tile_store(RA, 0);
+        __syncthreads();
+    }
     int k0 = kbeg;
     for (; k0 + 2 * KR < kend; k0 += 2 * KR) {
         __builtin_amdgcn_sched_barrier(0);
         load(k0 + KR, RB);
         __builtin_amdgcn_sched_barrier(0);
+        tile_read(RA, 0);
         compute(RA);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (XS) {
+            tile_store(RB, 1);
+            __syncthreads();
+        }
         load(k0 + 2 * KR, RA);
         __builtin_amdgcn_sched_barrier(0);
+        tile_read(RB, 1);
         compute(RB);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (XS) {
+            tile_store(RA, 0);
+            __syncthreads();
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     load(k0 + KR, RB);
     __builtin_amdgcn_sched_barrier(0);
+    tile_read(RA, 0);
     compute(RA);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (XS) {
+        tile_store(RB, 1);
+        __syncthreads();
+    }
+    tile_read(RB, 1);
     compute(RB);
     __builtin_amdgcn_sched_barrier(0);
     // lane holds D[4g + t][i]: expert te*16 + 4g + t, row r0 + 16j + i; stores
@@ -208,15 +280,19 @@ hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int 
     // are multiples of 128); four row blocks take rounds of 64 K (registers)
     if (plan.kchunk % 128 != 0) return hipErrorInvalidValue;
     const bool wide = plan.kchunk % 256 == 0, one = M <= 16;
+    // the four waves of a workgroup share an x tile when they hold four expert
+    // tiles of one K chunk and row group: E a multiple of 64
+    const bool share = ((E + 15) / 16) % 4 == 0;
+    auto run = [&](auto kern) {
+        hipLaunchKernelGGL(kern, g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.sp, plan.kchunk, units,
+                           blocks, partials, nquant, xq, xs, xg4, side1, stage1);
+    };
     if (wide && one)
-        hipLaunchKernelGGL((k_router_partials<4, 1>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.sp, plan.kchunk,
-                           units, blocks, partials, nquant, xq, xs, xg4, side1, stage1);
+        share ? run(k_router_partials<4, 1, true>) : run(k_router_partials<4, 1, false>);
     else if (one)
-        hipLaunchKernelGGL((k_router_partials<2, 1>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.sp, plan.kchunk,
-                           units, blocks, partials, nquant, xq, xs, xg4, side1, stage1);
+        share ? run(k_router_partials<2, 1, true>) : run(k_router_partials<2, 1, false>);
     else
-        hipLaunchKernelGGL((k_router_partials<2, kRouterNBT>), g, b, 0, stream, x, w_router, M, H, E, plan.splits, plan.sp, plan.kchunk,
-                           units, blocks, partials, nquant, xq, xs, xg4, side1, stage1);
+        share ? run(k_router_partials<2, kRouterNBT, true>) : run(k_router_partials<2, kRouterNBT, false>);
     return hipGetLastError();
 }
 
