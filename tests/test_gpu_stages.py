@@ -361,9 +361,15 @@ def test_dense_fp8s_expert_parity(M, H, I, limit):
     assert eq / (M * I) >= 0.99
 
 
-def test_finalize_parity():
-    rng = np.random.default_rng(4)
-    M, H, k = 19, 2048 + 128, 5
+@pytest.mark.parametrize("M,H,k", [
+    (19, 2048 + 128, 5),
+    # many rows; two column passes per thread at 8576 (the second ragged)
+    # and 16384 columns
+    (300, 8192 + 384, 3),
+    (260, 16384, 2),
+])
+def test_finalize_parity(M, H, k):
+    rng = np.random.default_rng(4 + M)
     y = rng.standard_normal((M * k, H)).astype(np.float32)
     w = rng.random((M, k)).astype(np.float32)
     ysh = rng.standard_normal((M, H)).astype(np.float32)
@@ -426,7 +432,7 @@ def test_pack_fp4_layout(fmt, N, K):
             assert ps[e, rb, q, l, 2 * u + h] == want
 
 
-@pytest.mark.parametrize("M,H", [(19, 2048 + 128), (3, 8192 + 384)])
+@pytest.mark.parametrize("M,H", [(19, 2048 + 128), (3, 8192 + 384), (257, 8192 + 384)])
 def test_finalize_mxfp8_next_input(M, H):
     """The finalize's MXFP8 of its own bf16 output equals the one-pass quant of
     that output byte for byte; out and residual_out equal the plain call's."""
