@@ -283,6 +283,26 @@ int moe_expert_gate_up(const moe_weights* w13, const uint8_t* a_q, const uint8_t
     return hip_status(launch_gate_up_fp4(job, a_q, a_s, h_q, h_s, static_cast<float*>(workspace), stream));
 }
 
+int moe_expert_gate_up_tok(const moe_weights* w13, const uint8_t* a_q, const uint8_t* a_s,
+                           const moe_routing* route, int M, int H, int I, int E, int k, float swiglu_limit,
+                           uint8_t* h_q, uint8_t* h_s, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+    if (!w13 || !route || !a_q || !a_s || !h_q || !h_s) return MOE_ERR_INVALID_ARG;
+    if (!(swiglu_limit >= 0.0f)) return MOE_ERR_INVALID_ARG;
+    if (int st = check_dims(M, H, E, k)) return st;
+    if (I < 128 || I % 128 != 0 || I > kMaxI) return MOE_ERR_UNSUPPORTED;
+    if (w13->fmt != MOE_FMT_MXFP4 && w13->fmt != MOE_FMT_NVFP4) return MOE_ERR_UNSUPPORTED;
+    if (int st = check_fp4_weights(w13)) return st;
+    if (int st = check_routing(route)) return st;
+    if (int st = check_pair_bytes(M, k, H)) return st;
+    ExpertJob job = routed_job(*w13, I, H, *route, M, E, k);
+    job.swiglu_limit = swiglu_limit;
+    job.a_tok = true;  // pass rows gather their tokens through the bucket
+    const size_t need = gate_up_fp4_partials_bytes(job);
+    if (need && (!workspace || !aligned256(workspace) || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+    return hip_status(launch_gate_up_fp4(job, a_q, a_s, h_q, h_s, static_cast<float*>(workspace), stream));
+}
+
 int moe_expert_down(const moe_weights* w2, const uint8_t* h_q, const uint8_t* h_s,
                     const uint16_t* h_bf16, const moe_routing* route, int M, int H, int I,
                     int E, int k, float* y, hipStream_t stream) {

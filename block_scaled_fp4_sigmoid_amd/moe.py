@@ -25,7 +25,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20
 EXPORTS = ["moe_status_str", "moe_abi_version", "moe_tile_capacity", "moe_packed_scale_bytes",
            "moe_pack_fp4", "moe_route_workspace_bytes",
            "moe_route_topk", "moe_quant_act_mxfp8", "moe_quant_act_nvfp4", "moe_gate_up_workspace_bytes",
-           "moe_expert_gate_up", "moe_expert_down", "moe_expert_gate_up_nvfp4a",
+           "moe_expert_gate_up", "moe_expert_gate_up_tok", "moe_expert_down", "moe_expert_gate_up_nvfp4a",
            "moe_expert_down_nvfp4a", "moe_finalize_rmsnorm",
            "moe_finalize_rmsnorm_mxfp8", "moe_layer_workspace_bytes", "moe_layer",
            "moe_layer_mxfp8_out", "moe_layer_noalloc", "moe_expert_gate_up_fp8s", "moe_expert_down_fp8s"]
@@ -86,6 +86,9 @@ def lib() -> C.CDLL:
         L.moe_expert_gate_up.restype = i
         L.moe_expert_gate_up.argtypes = [C.POINTER(moe_weights), vp, vp, vp, C.POINTER(moe_routing),
                                          i, i, i, i, i, f, vp, vp, vp, vp, sz, vp]
+        L.moe_expert_gate_up_tok.restype = i
+        L.moe_expert_gate_up_tok.argtypes = [C.POINTER(moe_weights), vp, vp, C.POINTER(moe_routing),
+                                             i, i, i, i, i, f, vp, vp, vp, sz, vp]
         L.moe_expert_down.restype = i
         L.moe_expert_down.argtypes = [C.POINTER(moe_weights), vp, vp, vp, C.POINTER(moe_routing),
                                       i, i, i, i, i, vp, vp]
@@ -275,6 +278,22 @@ def expert_gate_up(w13: Weights, M, H, I, E, k, routing: Optional[Routing] = Non
                                   _p(h_q), _p(h_s),
                                   _p(h_bf16), _p(ws), 0 if ws is None else ws.numel(), _stream(stream))
     _check(rc, "moe_expert_gate_up")
+
+
+def expert_gate_up_tok(w13: Weights, M, H, I, E, k, routing: Routing, a_q, a_s, h_q, h_s, ws=None, stream=None,
+                       swiglu_limit=0.0):
+    """Routed gate_up with the MXFP8 activations in token order [M, H]; h in
+    bucket order, as expert_gate_up writes it."""
+    _need_packed(w13)
+    need = lib().moe_gate_up_workspace_bytes(w13.fmt, M, H, I, E, k, 0)
+    if ws is None and need:
+        ws = _call_workspace(need, a_q.device, stream)
+    wc = w13.c()
+    r = routing.c()
+    rc = lib().moe_expert_gate_up_tok(C.byref(wc), _p(a_q), _p(a_s), C.byref(r), M, H, I, E, k,
+                                      float(swiglu_limit), _p(h_q), _p(h_s), _p(ws),
+                                      0 if ws is None else ws.numel(), _stream(stream))
+    _check(rc, "moe_expert_gate_up_tok")
 
 
 def expert_down(w2: Weights, M, H, I, E, k, y, routing: Optional[Routing] = None, h_q=None,

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 9
+#define MOE_ABI_VERSION 10
 
 enum moe_status {
     MOE_OK = 0,
@@ -277,6 +277,26 @@ int moe_expert_gate_up(const moe_weights *w13, const uint8_t *a_q, const uint8_t
                        const uint16_t *a_bf16, const moe_routing *route, int M, int H, int I,
                        int E, int k, float swiglu_limit, uint8_t *h_q, uint8_t *h_s, uint16_t *h_bf16,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_gate_up_tok — moe_expert_gate_up of routed FP4 experts with the
+ * MXFP8 activations in token order.
+ *   Pages: as moe_expert_gate_up (README Qwen3.5 slot table, row "mkm";
+ *   DeepSeek-V4.1 slot table, row "Routed experts (moe)": the expert GEMMs
+ *   read the step's input rows, quantized once by the one-pass MXFP8 quant).
+ * A is (a_q [M, H], a_s [M, H/32]) as moe_quant_act_mxfp8 writes it without a
+ * route: row r = token r.  Each pass of an expert's rows reads its rows'
+ * tokens through the bucket (bucket position b reads token bucket[b] / k), so
+ * the k rows that pick a token share one copy and no bucket-order copy
+ * (M*k rows) is written.  Everything else — route (required), weights, h in
+ * bucket order (h_q [M*k, I], h_s [M*k, I/32]), the clamped SwiGLU, the
+ * workspace (moe_gate_up_workspace_bytes(fmt, M, H, I, E, k, 0) bytes) and the
+ * errors — is that of moe_expert_gate_up, whose h bytes it reproduces exactly
+ * from the same activations. */
+int moe_expert_gate_up_tok(const moe_weights *w13, const uint8_t *a_q, const uint8_t *a_s,
+                           const moe_routing *route, int M, int H, int I, int E, int k,
+                           float swiglu_limit, uint8_t *h_q, uint8_t *h_s, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_expert_down — down GEMM y = h W2^T per routed pair (or per row, dense).

@@ -51,7 +51,7 @@ def test_probe_library_exports():
 
 
 def test_version_and_status_strings(L):
-    assert moe.abi_version() == 9
+    assert moe.abi_version() == 10
     for rc in range(5):
         assert len(moe.status_str(rc)) > 0
     assert "unknown" in moe.status_str(99)
@@ -197,6 +197,18 @@ def test_calls_refuse_before_enqueueing(L):
                                     None, 0x1000, 0x1000, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_expert_down(C.byref(w), None, None, 0x1000, None, 4, 128, 100, 1, 1, 0x1000,
                              None) == moe.MOE_ERR_UNSUPPORTED
+    # token-order gate_up: routed FP4 experts only, every pointer given
+    gut = lambda wt, rt, lim=0.0, a=0x1000: L.moe_expert_gate_up_tok(C.byref(wt), a, 0x1000, rt, 4, 128, 128, 8, 2,
+                                                                     lim, 0x1000, 0x1000, 0x1000, 1 << 20, None)
+    mx = moe.moe_weights(moe.MOE_FMT_MXFP4, 0x1000, 0x1000, None)
+    assert gut(w, C.byref(r)) == moe.MOE_ERR_UNSUPPORTED          # bf16 weights
+    assert gut(mx, None) == moe.MOE_ERR_INVALID_ARG               # no route
+    assert gut(mx, C.byref(r), a=None) == moe.MOE_ERR_INVALID_ARG
+    assert gut(mx, C.byref(r), lim=-1.0) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_gate_up_tok(C.byref(mx), 0x1000, 0x1000, C.byref(r), 4, 128, 100, 8, 2, 0.0, 0x1000,
+                                    0x1000, 0x1000, 1 << 20, None) == moe.MOE_ERR_UNSUPPORTED  # I % 128
+    assert L.moe_expert_gate_up_tok(C.byref(mx), 0x1000, 0x1000, C.byref(r_bad), 4, 128, 128, 8, 2, 0.0, 0x1000,
+                                    0x1000, 0x1000, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG  # routing array missing
     # W4A4: NVFP4 weights only, a positive activation global, the h globals given
     mx = moe.moe_weights(moe.MOE_FMT_MXFP4, 0x1000, 0x1000, None)
     nvw = moe.moe_weights(moe.MOE_FMT_NVFP4, 0x1000, 0x1000, 0x1000)

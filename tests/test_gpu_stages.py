@@ -213,7 +213,12 @@ def test_gate_up_routed_parity(wfmt, H, neg, limit):
     hq = torch.empty((P, I), dtype=torch.uint8, device=DEV)
     hs = torch.empty((P, I // 32), dtype=torch.uint8, device=DEV)
     moe.expert_gate_up(d.w13, M, H, I, E, k, routing=rt, a_q=xqp, a_s=xsp, h_q=hq, h_s=hs, swiglu_limit=limit)
+    # the same rows read in token order through the bucket: the same h bytes
+    hq2 = torch.full_like(hq, 0x5a)
+    hs2 = torch.full_like(hs, 0x5a)
+    moe.expert_gate_up_tok(d.w13, M, H, I, E, k, rt, xq, xs, hq2, hs2, swiglu_limit=limit)
     torch.cuda.synchronize()
+    assert torch.equal(hq2, hq) and torch.equal(hs2, hs)
     bucket, ids = np_of(rt.bucket), np_of(rt.topk_ids).ravel()
     a = orc.mxfp8_dequant(np_of(xq), np_of(xs))
     ghq, ghs = np_of(hq), np_of(hs)
@@ -263,6 +268,55 @@ def test_down_routed_parity(wfmt, I, neg, H):
         yr = orc.down(orc.Mat(m2.fmt, m2.packed, m2.scales, m2.gscale), H, I, hd[b])
         worst = max(worst, rel_l2(gy[p], yr))
     assert worst < 2e-3, worst
+
+
+@pytest.mark.parametrize("I", [256, 1536])
+def test_down_nvfp4_outlier_blocks(I):
+    """NVFP4 weights on MXFP8 activations whose blocks lie far below the row's
+    largest one.  The f16 operand of a value is its E4M3 code times
+    2^(its scale - the row's largest scale over the item's K range), which is
+    exact unless it falls below f16's smallest normal 2^-14 (then it is
+    rounded or flushed: an error of at most the value itself).  So each output
+    is within sum_n |W[c, n]| |a_n| [a_n < 2^-14 of the row's largest block
+    scale] of the exact fp64 sum, plus the summation's rounding; rows without
+    an outlier keep the ordinary accuracy.  I = 256 streams along the output rows, 1536
+    along K."""
+    sh, inp, d, rt, _, _ = _routed_setup(synth.NVFP4, H=512, seed=9, I=I)
+    M, H, E, k, I = sh.M, sh.H, sh.E, sh.k, sh.I
+    P, nb = M * k, I // 32
+    rng = np.random.default_rng(21)
+    codes = rng.integers(0, 256, (P, I)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3F            # no NaN codes
+    scales = (118 + rng.integers(0, 4, (P, nb))).astype(np.uint8)
+    jump = np.array([0, 12, 20, 40])[np.arange(P) % 4]   # binades of the one outlier block per row
+    scales[np.arange(P), rng.integers(0, nb, P)] += jump.astype(np.uint8)
+    hq = torch.from_numpy(codes).to(DEV)
+    hs = torch.from_numpy(scales).to(DEV)
+    y = torch.full((P, H), float("nan"), dtype=torch.float32, device=DEV)
+    moe.expert_down(d.w2, M, H, I, E, k, y, routing=rt, h_q=hq, h_s=hs)
+    torch.cuda.synchronize()
+    bucket, ids = np_of(rt.bucket), np_of(rt.topk_ids).ravel()
+    a = orc.mxfp8_dequant(codes, scales)
+    gy = np_of(y).astype(np.float64)
+    lossy_rows = 0
+    for b in range(P):
+        p = bucket[b]
+        m2 = inp.w2.expert(ids[p])
+        mat = orc.Mat(m2.fmt, m2.packed, m2.scales, m2.gscale)
+        W = orc.mat_dequant(mat, H, I)
+        yr = W @ a[b]
+        unit = 2.0 ** (int(scales[b].max()) - 127)
+        lost = np.where(np.abs(a[b]) < 2.0 ** -14 * unit, np.abs(a[b]), 0.0)
+        lossy_rows += int(np.any(lost > 0))
+        # the matrix instruction's sums: 2^-12 of the sum of |products| (the
+        # reduced internal precision bound used for the FP8 instruction)
+        bound = np.abs(W) @ lost + 2.0 ** -12 * (np.abs(W) @ np.abs(a[b]))
+        err = np.abs(gy[p] - yr)
+        assert np.all(err <= bound), (b, jump[b], float(np.max(err / bound)))
+        assert np.all(np.isfinite(gy[p]))
+        if jump[b] == 0:
+            assert rel_l2(gy[p], yr) < 5e-4
+    assert lossy_rows >= P // 4  # the 20- and 40-binade rows reach below f16's normal range
 
 
 @pytest.mark.parametrize("sfmt,M,limit", [(synth.MXFP4, 23, 0.0), (synth.NVFP4, 23, 0.0), (synth.MXFP4, 70, 0.0),
