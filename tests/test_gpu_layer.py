@@ -142,6 +142,10 @@ EDGE = [
     dict(M=16, H=512, E=8, k=2, I=640, sfmt=synth.MXFP4, I_sh=640, bias="zipf:3.0"),
     dict(M=16, H=512, E=8, k=2, I=640, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=640, bias="zipf:3.0"),
     dict(M=17, H=512, E=8, k=2, I=640, sfmt=synth.MXFP4, I_sh=640, bias="zipf:3.0"),
+    # the most experts and the largest top-k the limits allow, on both paths (128 pairs: slots
+    # resolved from the ids; 640 pairs: the route step)
+    dict(M=4, H=256, E=1024, k=32, I=128),
+    dict(M=20, H=256, E=1024, k=32, I=128, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=128),
 ]
 
 
