@@ -478,7 +478,15 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(int M, int E, int k, 
         return;
     }
     __shared__ __align__(16) uint8_t s_lds[kBucketLdsMax];
-    bucket_step(M, E, k, route, s_lds, H, yrec);
+    bucket_step<kBucketThreads>(M, E, k, route, s_lds, H, yrec);
+}
+
+// The route step alone in its launch: one workgroup of 1024 threads, which
+// places up to 384 rows in one chunk.
+__global__ __launch_bounds__(kBucketThreadsBig) void k_bucket_big(int M, int E, int k, moe_routing route, int H,
+                                                                 int2* yrec) {
+    __shared__ __align__(16) uint8_t s_lds[kBucketLdsBig];
+    bucket_step<kBucketThreadsBig>(M, E, k, route, s_lds, H, yrec);
 }
 
 // Route step and the activation quant in one launch, for P = M*k <= 256 pairs.
@@ -495,7 +503,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket_quant(int M, int E, i
                                                                 uint8_t* __restrict__ st, Bf16Side side, int stage) {
     if (blockIdx.x == 0) {
         __shared__ __align__(16) uint8_t s_lds[kBucketLdsMax];
-        bucket_step(M, E, k, route, s_lds);
+        bucket_step<kBucketThreads>(M, E, k, route, s_lds);
         return;
     }
     if ((int)blockIdx.x > nq) {
@@ -549,8 +557,11 @@ hipError_t launch_topk_bucket(const float* partials, int splits, int sp, const f
                                stream);
     if (e != hipSuccess) return e;
     const int extra3 = stage3 == kBf16None ? 0 : side3.blocks;
-    hipLaunchKernelGGL(k_bucket, dim3(1 + extra3), dim3(kBucketThreads), 0, stream, M, E, k, route, side3, stage3,
-                       H, yrec);
+    if (extra3 == 0)
+        hipLaunchKernelGGL(k_bucket_big, dim3(1), dim3(kBucketThreadsBig), 0, stream, M, E, k, route, H, yrec);
+    else
+        hipLaunchKernelGGL(k_bucket, dim3(1 + extra3), dim3(kBucketThreads), 0, stream, M, E, k, route, side3,
+                           stage3, H, yrec);
     return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
-// route_dev.h — the route step as a device function of one workgroup of
-// kBucketThreads threads, so it can run in a launch of its own or as an extra
-// workgroup of a later launch (it reads only topk_ids).
+// route_dev.h — the route step as a device function of one workgroup (of
+// kBucketThreads threads, so it can run as an extra workgroup of a later
+// launch, or of kBucketThreadsBig in a launch of its own; it reads only
+// topk_ids).
 //
 // Pages: SGLang-NVIDIA-Mega README, DeepSeek-V4.1 slot table, row "Routed
 // experts (moe)": each expert's rows are grouped into tiles of at most 8 rows,
@@ -15,21 +16,26 @@ namespace moe {
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
 constexpr int kBucketThreads = 256;
+constexpr int kBucketThreadsBig = 1024;
 
-// Exclusive scans of three arrays of kMaxE entries at once (4 per thread of
-// 256): each wave scans its lanes' sums with shuffles, and the four wave
-// totals (in scratch, 12 ints) give each wave's base.  Two barriers.
+// Exclusive scans of three arrays of kMaxE entries at once (kMaxE / NT per
+// thread): each wave scans its lanes' sums with shuffles, and the wave totals
+// (in scratch, 3 ints per wave) give each wave's base.  Two barriers.
+template <int NT>
 __device__ inline void block_exclusive_scan3(int* a, int* b, int* c, int* scratch, int& ta, int& tb, int& tc) {
+    constexpr int EPT = kMaxE / NT;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    int va[4], vb[4], vc[4];
+    int va[EPT], vb[EPT], vc[EPT];
+    int sa = 0, sb = 0, sc = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        va[i] = a[4 * tid + i];
-        vb[i] = b[4 * tid + i];
-        vc[i] = c[4 * tid + i];
+    for (int i = 0; i < EPT; ++i) {
+        va[i] = a[EPT * tid + i];
+        vb[i] = b[EPT * tid + i];
+        vc[i] = c[EPT * tid + i];
+        sa += va[i];
+        sb += vb[i];
+        sc += vc[i];
     }
-    const int sa = va[0] + va[1] + va[2] + va[3], sb = vb[0] + vb[1] + vb[2] + vb[3],
-              sc = vc[0] + vc[1] + vc[2] + vc[3];
     int ia = sa, ib = sb, ic = sc;  // inclusive scans over the wave's lanes
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -49,7 +55,7 @@ __device__ inline void block_exclusive_scan3(int* a, int* b, int* c, int* scratc
     int ba = 0, bb = 0, bc = 0;
     ta = tb = tc = 0;
 #pragma unroll
-    for (int v = 0; v < kBucketThreads / 64; ++v) {
+    for (int v = 0; v < NT / 64; ++v) {
         const int wa = scratch[3 * v], wb = scratch[3 * v + 1], wc = scratch[3 * v + 2];
         if (v < w) {
             ba += wa;
@@ -62,10 +68,10 @@ __device__ inline void block_exclusive_scan3(int* a, int* b, int* c, int* scratc
     }
     int ea = ba + ia - sa, eb = bb + ib - sb, ec = bc + ic - sc;  // exclusive bases of the thread's entries
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        a[4 * tid + i] = ea;
-        b[4 * tid + i] = eb;
-        c[4 * tid + i] = ec;
+    for (int i = 0; i < EPT; ++i) {
+        a[EPT * tid + i] = ea;
+        b[EPT * tid + i] = eb;
+        c[EPT * tid + i] = ec;
         ea += va[i];
         eb += vb[i];
         ec += vc[i];
@@ -74,19 +80,28 @@ __device__ inline void block_exclusive_scan3(int* a, int* b, int* c, int* scratc
 }
 
 // Pairs per thread in one placement chunk, rows per chunk and bitmap words
-// per expert of the route step.
+// per expert of the route step of NT threads.  NT = 1024 places up to 384
+// rows in one chunk (the 384-row step in one), with each word's count of
+// earlier rows precomputed per expert so a rank costs two LDS reads; NT = 256
+// places chunks of 128 rows and counts a rank's earlier words in a loop.
 constexpr int kChunkPairsPerThread = 4;
+template <int NT>
 __host__ __device__ inline int bucket_chunk_rows(int k) {
-    return 128 < kChunkPairsPerThread * kBucketThreads / k ? 128 : kChunkPairsPerThread * kBucketThreads / k;
+    constexpr int cap = NT == kBucketThreadsBig ? 384 : 128;
+    return cap < kChunkPairsPerThread * NT / k ? cap : kChunkPairsPerThread * NT / k;
 }
-__host__ __device__ inline int bucket_words(int k) { return (bucket_chunk_rows(k) + 31) / 32; }
+template <int NT>
+__host__ __device__ inline int bucket_words(int k) { return (bucket_chunk_rows<NT>(k) + 31) / 32; }
 
-// LDS bytes the route step needs: five per-expert int arrays, the scan
-// scratch, and the placement bitmaps.
-__host__ __device__ inline size_t bucket_lds_bytes(int E, int k) {
-    return (size_t)(5 * kMaxE + kBucketThreads) * 4 + (size_t)E * bucket_words(k) * 4;
+// LDS bytes the route step needs at most: five per-expert int arrays, the
+// scan scratch, the placement bitmaps (and for NT = 1024 the per-word counts).
+template <int NT>
+constexpr size_t bucket_lds_max() {
+    constexpr int W = (NT == kBucketThreadsBig ? 384 : 128) / 32;
+    return (size_t)(5 * kMaxE + NT) * 4 + (size_t)kMaxE * W * 4 * (NT == kBucketThreadsBig ? 2 : 1);
 }
-constexpr size_t kBucketLdsMax = (size_t)(5 * kMaxE + kBucketThreads) * 4 + (size_t)kMaxE * 4 * 4;
+constexpr size_t kBucketLdsMax = bucket_lds_max<kBucketThreads>();
+constexpr size_t kBucketLdsBig = bucket_lds_max<kBucketThreadsBig>();
 
 // ---------------------------------------------------------------------------
 // Route step: one workgroup builds the expert buckets, 8-row tiles and the
@@ -94,9 +109,12 @@ constexpr size_t kBucketLdsMax = (size_t)(5 * kMaxE + kBucketThreads) * 4 + (siz
 // ids written by the top-k workgroups are visible without a device-scope
 // fence).  With yrec, also each pair's row of a grouped y of H columns
 // (ygroup_rec).
+template <int NT>
 __device__ inline void bucket_step(int M, int E, int k, const moe_routing& route, uint8_t* lds, int H = 0,
                                    int2* yrec = nullptr) {
     const int tid = threadIdx.x;
+    constexpr bool kBig = NT == kBucketThreadsBig;
+    static_assert(!kBig || NT == kMaxE, "one expert per thread in the per-word counts");
 
     int* s_cnt = reinterpret_cast<int*>(lds);
     int* s_off = s_cnt + kMaxE;
@@ -104,18 +122,19 @@ __device__ inline void bucket_step(int M, int E, int k, const moe_routing& route
     int* s_act = s_tile + kMaxE;
     int* s_run = s_act + kMaxE;
     int* s_scan = s_run + kMaxE;
-    uint32_t* s_bm = reinterpret_cast<uint32_t*>(s_scan + kBucketThreads);  // E * bucket_words(k)
+    uint32_t* s_bm = reinterpret_cast<uint32_t*>(s_scan + NT);  // E * bucket_words(k)
     const int P = M * k;
-    for (int e = tid; e < kMaxE; e += kBucketThreads) {
+    const int R = bucket_chunk_rows<NT>(k);
+    const int W = bucket_words<NT>(k);
+    int* s_pre = reinterpret_cast<int*>(s_bm + E * W);  // kBig: earlier rows of the expert before each word
+    for (int e = tid; e < kMaxE; e += NT) {
         s_cnt[e] = 0;
         s_run[e] = 0;
     }
     __syncthreads();
-    // Pairs in placement chunks of R rows (R * k <= 4 * 256 pairs: pairs
-    // r0 * k + tid + 256 q, q < 4).  The expert ids of a thread's pairs in the
+    // Pairs in placement chunks of R rows (R * k <= 4 * NT pairs: pairs
+    // r0 * k + tid + NT q, q < 4).  The expert ids of a thread's pairs in the
     // first kIdChunks chunks stay in registers for the placement below.
-    const int R = bucket_chunk_rows(k);
-    const int W = bucket_words(k);
     const int CP = R * k;  // pairs per chunk
     constexpr int kIdChunks = 4;
     int idr[kIdChunks][kChunkPairsPerThread];
@@ -123,7 +142,7 @@ __device__ inline void bucket_step(int M, int E, int k, const moe_routing& route
     for (int ci = 0; ci < kIdChunks; ++ci)
 #pragma unroll
         for (int q = 0; q < kChunkPairsPerThread; ++q) {
-            const int pc = tid + kBucketThreads * q;
+            const int pc = tid + NT * q;
             const int p = ci * CP + pc;
             idr[ci][q] = pc < CP && p < P ? route.topk_ids[p] : -1;
         }
@@ -132,9 +151,9 @@ __device__ inline void bucket_step(int M, int E, int k, const moe_routing& route
 #pragma unroll
         for (int q = 0; q < kChunkPairsPerThread; ++q)
             if (idr[ci][q] >= 0) atomicAdd(&s_cnt[idr[ci][q]], 1);
-    for (int p = kIdChunks * CP + tid; p < P; p += kBucketThreads) atomicAdd(&s_cnt[route.topk_ids[p]], 1);
+    for (int p = kIdChunks * CP + tid; p < P; p += NT) atomicAdd(&s_cnt[route.topk_ids[p]], 1);
     __syncthreads();
-    for (int e = tid; e < kMaxE; e += kBucketThreads) {
+    for (int e = tid; e < kMaxE; e += NT) {
         const int c = s_cnt[e];
         s_off[e] = c;
         s_tile[e] = (c + 7) / 8;
@@ -142,8 +161,8 @@ __device__ inline void bucket_step(int M, int E, int k, const moe_routing& route
     }
     __syncthreads();
     int tot_pairs, tot_tiles, tot_act;
-    block_exclusive_scan3(s_off, s_tile, s_act, s_scan, tot_pairs, tot_tiles, tot_act);
-    for (int e = tid; e < E; e += kBucketThreads) {
+    block_exclusive_scan3<NT>(s_off, s_tile, s_act, s_scan, tot_pairs, tot_tiles, tot_act);
+    for (int e = tid; e < E; e += NT) {
         const int c = s_cnt[e];
         route.expert_offsets[e] = s_off[e];
         if (c > 0) {
@@ -162,17 +181,17 @@ __device__ inline void bucket_step(int M, int E, int k, const moe_routing& route
         *route.num_tiles = tot_tiles;
         *route.num_active = tot_act;
     }
-    for (int sl = tot_act + tid; sl <= min(E, P); sl += kBucketThreads) route.active_offsets[sl] = P;
+    for (int sl = tot_act + tid; sl <= min(E, P); sl += NT) route.active_offsets[sl] = P;
     // Stable placement: chunks of R rows; a bitmap per expert marks the chunk's
     // rows that chose it, and a pair's rank within its expert is the number of
     // earlier rows (previous chunks + lower bits of this chunk's bitmap).
     for (int r0 = 0, ci = 0; r0 < M; r0 += R, ++ci) {
-        for (int w = tid; w < E * W; w += kBucketThreads) s_bm[w] = 0u;
+        for (int w = tid; w < E * W; w += NT) s_bm[w] = 0u;
         __syncthreads();
         int eq[kChunkPairsPerThread], rlq[kChunkPairsPerThread];
 #pragma unroll
         for (int q = 0; q < kChunkPairsPerThread; ++q) {
-            const int pc = tid + kBucketThreads * q;
+            const int pc = tid + NT * q;
             const int p = r0 * k + pc;
             eq[q] = -1;
             rlq[q] = 0;
@@ -186,23 +205,41 @@ __device__ inline void bucket_step(int M, int E, int k, const moe_routing& route
             }
         }
         __syncthreads();
+        int chunk_rows = 0;  // kBig: the chunk's rows of expert tid
+        if constexpr (kBig) {
+            if (tid < E) {
+                for (int w = 0; w < W; ++w) {
+                    s_pre[tid * W + w] = chunk_rows;
+                    chunk_rows += __popc(s_bm[tid * W + w]);
+                }
+            }
+            __syncthreads();
+        }
 #pragma unroll
         for (int q = 0; q < kChunkPairsPerThread; ++q) {
             if (eq[q] >= 0) {
                 const int e = eq[q], rl = rlq[q];
                 int rank = 0;
-                for (int w = 0; w < (rl >> 5); ++w) rank += __popc(s_bm[e * W + w]);
+                if constexpr (kBig) {
+                    rank = s_pre[e * W + (rl >> 5)];
+                } else {
+                    for (int w = 0; w < (rl >> 5); ++w) rank += __popc(s_bm[e * W + w]);
+                }
                 rank += __popc(s_bm[e * W + (rl >> 5)] & ((1u << (rl & 31)) - 1u));
-                const int pair = r0 * k + tid + kBucketThreads * q;
+                const int pair = r0 * k + tid + NT * q;
                 route.bucket[s_off[e] + s_run[e] + rank] = pair;
                 if (yrec) yrec[pair] = ygroup_rec(s_off[e], s_cnt[e], s_run[e] + rank, H);
             }
         }
         __syncthreads();
-        for (int ee = tid; ee < E; ee += kBucketThreads) {
-            int c = 0;
-            for (int w = 0; w < W; ++w) c += __popc(s_bm[ee * W + w]);
-            s_run[ee] += c;
+        if constexpr (kBig) {
+            if (tid < E) s_run[tid] += chunk_rows;
+        } else {
+            for (int ee = tid; ee < E; ee += NT) {
+                int c = 0;
+                for (int w = 0; w < W; ++w) c += __popc(s_bm[ee * W + w]);
+                s_run[ee] += c;
+            }
         }
         __syncthreads();
     }
