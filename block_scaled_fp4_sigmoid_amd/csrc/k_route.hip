@@ -67,12 +67,19 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
                                                          float* __restrict__ partials, int nquant,
                                                          uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
                                                          float xg4, Bf16Side side, int stage) {
-    if ((int)blockIdx.x >= nmain + nquant) {  // a bf16 shared-expert stage riding along
-        bf16_side_block(side, stage, blockIdx.x - nmain - nquant);
+    // a bf16 shared-expert stage riding along: after the router and quant
+    // workgroups, or first when the grid exceeds two workgroups per CU (placed
+    // last it then ran in the launch's tail: skew 200.8 -> 198.7 us per step)
+    const int nside = (int)gridDim.x - nmain - nquant;
+    const bool side_first = (int)gridDim.x > 512;
+    const int sb = side_first ? (int)blockIdx.x : (int)blockIdx.x - nmain - nquant;
+    if (sb >= 0 && sb < nside) {
+        bf16_side_block(side, stage, sb);
         return;
     }
-    if ((int)blockIdx.x >= nmain) {  // x in token order: MXFP8 (256 blocks of 32 values), or
-        const int b = (blockIdx.x - nmain) * 256 + threadIdx.x;  // NVFP4 with global xg4 > 0 (of 16)
+    const int bx = side_first ? (int)blockIdx.x - nside : (int)blockIdx.x;
+    if (bx >= nmain) {  // x in token order: MXFP8 (256 blocks of 32 values), or
+        const int b = (bx - nmain) * 256 + threadIdx.x;  // NVFP4 with global xg4 > 0 (of 16)
         if (xg4 > 0.0f) {
             if (b < M * (H / 16)) quant_nvfp4_bf16x16(x + (size_t)b * 16, xg4, xq + (size_t)b * 8, xs + b);
         } else if (b < M * (H / 32)) {
@@ -82,7 +89,7 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
     }
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int unit = blockIdx.x * 4 + wave;
+    const int unit = bx * 4 + wave;
     if (!XS && unit >= units) return;  // XS: every workgroup is full (units a multiple of 4)
     const int et = (E + 15) / 16;
     const int te = unit % et;

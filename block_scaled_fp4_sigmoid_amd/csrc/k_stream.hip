@@ -1124,25 +1124,35 @@ __device__ __forceinline__ uint32_t mx_quant4_group8(const float hv[4], uint8_t&
 // larger, with one: 269 -> 347 us).  Output columns per workgroup: 32 * blocks.
 constexpr int kGateMB = 2, kGateMBSmall = 1;
 
-// Workgroups [0, n2) take items of a second job J2 of the same format (the
-// FP4 shared expert riding along the routed experts; first, so its few long
-// items do not trail the launch), [n2, nmain) items of job J0, later ones a
-// bf16 shared-expert stage.  PR: rows per pass, 32 (two 16-row N-blocks) or 16
+// Main workgroups [0, n2) take items of a second job J2 of the same format
+// (the FP4 shared expert riding along the routed experts; first, so its few
+// long items do not trail the launch), [n2, nmain) items of job J0; the rest
+// of the grid runs a bf16 shared-expert stage (before or after them).  PR: rows per pass, 32 (two 16-row N-blocks) or 16
 // (one: at 16 or fewer token rows no expert has more, and the smaller tiles
 // and registers let a third workgroup onto each CU).
 template <int FMT, bool FUSED, int GMB, int PR>
 __global__ __launch_bounds__(kThreads, kNVW<FMT> ? MOE_NV_MINB : MOE_MIN_BLOCKS) void k_gate_up(
     StreamJob J0, uint8_t* __restrict__ h_q0, uint8_t* __restrict__ h_s0, float* __restrict__ part, int nmain,
     Bf16Side side, int stage, StreamJob J2, uint8_t* __restrict__ h_q2, uint8_t* __restrict__ h_s2, int n2) {
-    if ((int)blockIdx.x >= nmain) {  // a bf16 shared-expert stage riding along
-        bf16_side_block(side, stage, blockIdx.x - nmain);
+    // A bf16 shared-expert stage riding along takes the workgroups after the
+    // main items, or, when the main items need more than one round of resident
+    // workgroups (over 768), the first ones: placed last they ran in the
+    // launch's tail (skew 203.1 -> 200.8 us per step); within one round they
+    // stay last, where they do not take the first issue slots from the routed
+    // items (verify, 512 items and 112 riders: 59.8 -> 60.5 us with them first).
+    const int nside = (int)gridDim.x - nmain;
+    const bool side_first = nmain > 768;
+    const int sb = side_first ? (int)blockIdx.x : (int)blockIdx.x - nmain;
+    if (sb >= 0 && sb < nside) {
+        bf16_side_block(side, stage, sb);
         return;
     }
-    const bool second = (int)blockIdx.x < n2;  // uniform
+    const int b0 = side_first ? (int)blockIdx.x - nside : (int)blockIdx.x;
+    const bool second = b0 < n2;  // uniform
     const StreamJob& J = second ? J2 : J0;
     uint8_t* __restrict__ h_q = second ? h_q2 : h_q0;
     uint8_t* __restrict__ h_s = second ? h_s2 : h_s0;
-    const int bid = second ? (int)blockIdx.x : (int)blockIdx.x - n2;
+    const int bid = second ? b0 : b0 - n2;
     const int I = J.N / 2, K = J.K;
     constexpr int GCOLS = 32 * GMB;  // output columns per workgroup
     const int ks = bid % J.splits;
