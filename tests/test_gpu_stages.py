@@ -89,12 +89,14 @@ ROUTE_CASES = [
     # 128-K rounds (M <= 16) and three pairs of 64-K rounds (M <= 16, chunks of 384)
     (8, 8192, 1024, 8, "none", 1.0),
     (12, 6144, 1024, 8, "normal:0.01", 1.0),
-    # the route step places rows in chunks of min(128, 1024 / k) rows (four
-    # pairs per thread) and keeps the first 4 chunks' expert ids in registers;
-    # these run past 4 chunks
-    (1024, 512, 64, 8, "zipf:1.0", 1.0),  # 8 chunks of 128 rows
-    (4096, 256, 4, 1, "none", 1.0),       # 32 chunks of 128 rows
-    (600, 512, 64, 10, "zipf:1.0", 1.0),  # 6 chunks of 102 rows (the last ragged)
+    # the route step of its own launch (1024 threads) places rows in chunks of
+    # min(384, 4096 / k) rows (four pairs per thread) and keeps the first 4
+    # chunks' expert ids in registers; the last three run past 4 chunks
+    (1024, 512, 64, 8, "zipf:1.0", 1.0),  # 3 chunks of 384 rows (the last ragged)
+    (600, 512, 64, 10, "zipf:1.0", 1.0),  # 2 chunks of 384 rows
+    (4096, 256, 4, 1, "none", 1.0),       # 11 chunks of 384 rows
+    (2000, 256, 64, 8, "zipf:1.0", 1.0),  # 6 chunks of 384 rows (the last 80)
+    (700, 128, 64, 32, "none", 1.0),      # 6 chunks of 128 rows (the last 60)
 ]
 
 
