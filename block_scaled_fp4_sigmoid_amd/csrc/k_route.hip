@@ -496,57 +496,6 @@ __global__ __launch_bounds__(kBucketThreadsBig) void k_bucket_big(int M, int E, 
     bucket_step<kBucketThreadsBig>(M, E, k, route, s_lds, H, yrec);
 }
 
-// Route step and the activation quant in one launch, for P = M*k <= 256 pairs.
-// Block 0 is the route step; blocks 1..nq quantize 256 blocks of 32 values
-// each: rows [0, P) in bucket order, rows [P, P + Mt) in token order; later
-// blocks run a bf16 shared-expert stage.  A quant block that touches bucket
-// rows places the P pairs itself (position of pair p = pairs with a smaller
-// expert + earlier pairs with the same expert, the bucket order the route step
-// writes), so it does not wait for block 0.
-__global__ __launch_bounds__(kBucketThreads) void k_bucket_quant(int M, int E, int k, moe_routing route,
-                                                                const uint16_t* __restrict__ x, int K, int nq,
-                                                                int Mt, uint8_t* __restrict__ qp,
-                                                                uint8_t* __restrict__ sp, uint8_t* __restrict__ qt,
-                                                                uint8_t* __restrict__ st, Bf16Side side, int stage) {
-    if (blockIdx.x == 0) {
-        __shared__ __align__(16) uint8_t s_lds[kBucketLdsMax];
-        bucket_step<kBucketThreads>(M, E, k, route, s_lds);
-        return;
-    }
-    if ((int)blockIdx.x > nq) {
-        bf16_side_block(side, stage, blockIdx.x - 1 - nq);
-        return;
-    }
-    __shared__ int s_ids[kBucketThreads], s_pair[kBucketThreads];
-    const int tid = threadIdx.x;
-    const int P = M * k, bpr = K / 32;
-    const int idx0 = (blockIdx.x - 1) * kBucketThreads;
-    if (idx0 / bpr < P) {  // block-uniform: the block has bucket rows
-        if (tid < P) s_ids[tid] = route.topk_ids[tid];
-        __syncthreads();
-        if (tid < P) {
-            const int e = s_ids[tid];
-            int before = 0;
-            for (int p = 0; p < P; ++p) {
-                const int ep = s_ids[p];
-                before += (ep < e) | ((ep == e) & (p < tid));
-            }
-            s_pair[before] = tid;
-        }
-        __syncthreads();
-    }
-    const int idx = idx0 + tid;
-    const int row = idx / bpr, blk = idx - row * bpr;
-    if (row >= P + Mt) return;
-    if (row < P) {
-        const int tok = s_pair[row] / k;
-        quant_block32(x + (size_t)tok * K + 32 * blk, qp + (size_t)row * K + 32 * blk, sp + (size_t)row * bpr + blk);
-    } else {
-        const int tok = row - P;
-        quant_block32(x + (size_t)tok * K + 32 * blk, qt + (size_t)tok * K + 32 * blk, st + (size_t)tok * bpr + blk);
-    }
-}
-
 hipError_t launch_topk(const float* partials, int splits, int sp, const float* bias, int M, int E, int k,
                        float routed_scale, float* logits_out, const moe_routing& route, const Bf16Side& side2,
                        int stage2, hipStream_t stream) {
@@ -569,20 +518,6 @@ hipError_t launch_topk_bucket(const float* partials, int splits, int sp, const f
     else
         hipLaunchKernelGGL(k_bucket, dim3(1 + extra3), dim3(kBucketThreads), 0, stream, M, E, k, route, side3,
                            stage3, H, yrec);
-    return hipGetLastError();
-}
-
-hipError_t launch_bucket_quant(int M, int E, int k, const moe_routing& route, const uint16_t* x, int K,
-                               uint8_t* qp, uint8_t* sp, uint8_t* qt, uint8_t* st, const Bf16Side& side3,
-                               int stage3, hipStream_t stream) {
-    static_assert(kSmallPairs == kBucketThreads, "one thread per pair places the pairs");
-    if (M * k > kSmallPairs) return hipErrorInvalidValue;
-    const int Mt = qt ? M : 0;
-    const long n = (long)(M * k + Mt) * (K / 32);
-    const int nq = (int)((n + kBucketThreads - 1) / kBucketThreads);
-    const int extra3 = stage3 == kBf16None ? 0 : side3.blocks;
-    hipLaunchKernelGGL(k_bucket_quant, dim3(1 + nq + extra3), dim3(kBucketThreads), 0, stream, M, E, k, route, x,
-                       K, nq, Mt, qp, sp, qt, st, side3, stage3);
     return hipGetLastError();
 }
 

@@ -96,16 +96,9 @@ hipError_t launch_quant_nvfp4(const uint16_t* x, const int32_t* bucket, int k, i
 // rows); with qt != nullptr also the M token-ordered rows into qt/st.
 hipError_t launch_quant_pairs(const uint16_t* x, const int32_t* bucket, int k, int M, int K, uint8_t* qp,
                               uint8_t* sp, uint8_t* qt, uint8_t* st, hipStream_t stream);
-// The route step (after launch_topk) and launch_quant_pairs in one launch,
-// for M*k <= kSmallPairs pairs; side3 rides along.
-constexpr int kSmallPairs = 256;
 // Pairs up to which the fused layer's gate_up workgroups resolve their slot
 // from the top-k ids themselves (two per thread), with no route step.
 constexpr int kIdsPairs = 512;
-hipError_t launch_bucket_quant(int M, int E, int k, const moe_routing& route, const uint16_t* x, int K,
-                               uint8_t* qp, uint8_t* sp, uint8_t* qt, uint8_t* st, const Bf16Side& side3,
-                               int stage3, hipStream_t stream);
-
 
 // Slots a gate_up resolved from the top-k ids, recorded for the down launch:
 // active experts ([min(E,P)]), their bucket ranges ([min(E,P) + 1]), their

@@ -146,12 +146,12 @@ EDGE = [
     # resolved from the ids; 640 pairs: the route step)
     dict(M=4, H=256, E=1024, k=32, I=128),
     dict(M=20, H=256, E=1024, k=32, I=128, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=128),
-    # the route step sharing its launch (256 threads: chunks of min(128, 1024 / k) rows, the
-    # first 4 chunks' ids in registers) past 4 chunks: with the bf16 shared down riding it,
-    # with the static-FP8 shared down, and quantizing NVFP4 activations in bucket order
+    # the route step sharing its launch with the shared expert's down (256 threads: chunks of
+    # min(128, 1024 / k) rows, the first 4 chunks' ids in registers) past 4 chunks: bf16 shared
+    # on MXFP8 and on NVFP4 activations, static-FP8 shared
     dict(M=600, H=256, E=32, k=8, I=128, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=128, bias="zipf:1.0"),
     dict(M=520, H=256, E=16, k=8, I=128, wfmt=synth.MXFP4, sfmt=synth.FP8S, I_sh=128),
-    dict(M=700, H=256, E=32, k=4, I=128, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=128, act_fmt=synth.ACT_NVFP4),
+    dict(M=600, H=256, E=32, k=8, I=128, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=128, act_fmt=synth.ACT_NVFP4),
 ]
 
 
