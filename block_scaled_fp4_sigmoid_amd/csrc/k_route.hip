@@ -410,6 +410,32 @@ __device__ int select_topk(const uint64_t* s_ord, int E, int k, int lane) {
     return my_id;
 }
 
+// Phases 2 and 3 of a row's top-k, by wave 0 (lane = its lane): the k slots
+// picked from the keys in LDS, then the weights, the chosen scores summed in
+// slot order.
+__device__ __forceinline__ void topk_write_row(const uint64_t* s_ord, const double* s_sc, int r, int E, int k,
+                                               float routed_scale, const moe_routing& route, int lane) {
+    int my_id;
+    if (E <= 256)
+        my_id = select_topk<4>(s_ord, E, k, lane);
+    else if (E <= 512)
+        my_id = select_topk<8>(s_ord, E, k, lane);
+    else
+        my_id = select_topk<16>(s_ord, E, k, lane);
+    const double my_sc = lane < k ? s_sc[my_id] : 0.0;
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) {
+        const uint64_t b = __double_as_longlong(my_sc);
+        const uint64_t v = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), j) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, j);
+        sum += __longlong_as_double((long long)v);
+    }
+    if (lane < k) {
+        route.topk_ids[(size_t)r * k + lane] = my_id;
+        route.topk_w[(size_t)r * k + lane] = (float)(((double)routed_scale * my_sc) / sum);
+    }
+}
+
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials, int splits, int sp,
                                               const float* __restrict__ bias, int M, int E, int k,
                                               float routed_scale, float* __restrict__ logits_out,
@@ -455,27 +481,84 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials
         s_ord[e] = ordered_key(sc + (bias ? (double)bias[e] : 0.0));
     }
     __syncthreads();
-    if (tid >= 64) return;
-    const int lane = tid;
-    int my_id;
-    if (E <= 256)
-        my_id = select_topk<4>(s_ord, E, k, lane);
-    else if (E <= 512)
-        my_id = select_topk<8>(s_ord, E, k, lane);
-    else
-        my_id = select_topk<16>(s_ord, E, k, lane);
-    const double my_sc = lane < k ? s_sc[my_id] : 0.0;
-    double sum = 0.0;
-    for (int j = 0; j < k; ++j) {
-        const uint64_t b = __double_as_longlong(my_sc);
-        const uint64_t v = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), j) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, j);
-        sum += __longlong_as_double((long long)v);
+    if (tid < 64) topk_write_row(s_ord, s_sc, r, E, k, routed_scale, route, tid);
+}
+
+// Router and top-k of one row in one workgroup, for routers small enough
+// that every row's workgroup reads all of W_r (E <= 64, E * H <= 32768: the
+// partial logits, their launch boundary and the top-k launch go away).  The
+// E2 = max(4, pow2(E)) expert slots of a row take T = 256 / E2 threads each;
+// thread (e, part) takes the 8-value chunks part, part + T, ... of H (x and
+// W_r rows read in 16- and 32-byte pieces), multiplies in fp64 (a bf16 x
+// fp32 product is exact there) and adds in fp64; the T partial sums meet in a
+// fixed butterfly, and the logit is their sum rounded once to fp32.  Blocks
+// past M quantize x in token order, as the router launch's quant blocks do.
+__global__ __launch_bounds__(256) void k_router_topk_row(const uint16_t* __restrict__ x,
+                                                         const float* __restrict__ w_router,
+                                                         const float* __restrict__ bias, int M, int H, int E,
+                                                         int k, float routed_scale, float* __restrict__ logits_out,
+                                                         moe_routing route, uint8_t* __restrict__ xq,
+                                                         uint8_t* __restrict__ xs, float xg4) {
+    if ((int)blockIdx.x >= M) {
+        const int b = ((int)blockIdx.x - M) * 256 + threadIdx.x;
+        if (xg4 > 0.0f) {
+            if (b < M * (H / 16)) quant_nvfp4_bf16x16(x + (size_t)b * 16, xg4, xq + (size_t)b * 8, xs + b);
+        } else if (b < M * (H / 32)) {
+            quant_block32(x + (size_t)b * 32, xq + (size_t)b * 32, xs + b);
+        }
+        return;
     }
-    if (lane < k) {
-        route.topk_ids[(size_t)r * k + lane] = my_id;
-        route.topk_w[(size_t)r * k + lane] = (float)(((double)routed_scale * my_sc) / sum);
+    __shared__ uint64_t s_ord[kSmallRouterE];
+    __shared__ double s_sc[kSmallRouterE];
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x;
+    int e2 = 4;
+    while (e2 < E) e2 <<= 1;
+    const int T = 256 / e2;  // a power of two, 4..64: a slot's threads sit in one wave
+    const int e = tid / T, part = tid % T;
+    const bool ev = e < E;
+    const uint16_t* xr = x + (size_t)r * H;
+    const float* wr = w_router + (size_t)(ev ? e : 0) * H;
+    // kB chunks per round of loads (E * H <= 32768 gives at most 32 per
+    // thread); chunks past H load chunk `part` again and are skipped; four
+    // accumulators (value pair i of a chunk) added in a fixed order
+    constexpr int kB = 8;
+    const int nch = H / 8;
+    double a[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int c0 = part; c0 < nch; c0 += kB * T) {
+        v4i xv[kB];
+        float4 w0[kB], w1[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int c = c0 + u * T < nch ? c0 + u * T : part;
+            xv[u] = load16(xr + 8 * c);
+            w0[u] = *reinterpret_cast<const float4*>(wr + 8 * c);
+            w1[u] = *reinterpret_cast<const float4*>(wr + 8 * c + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            if (c0 + u * T < nch) {
+                const uint32_t xw[4] = {(uint32_t)xv[u].x, (uint32_t)xv[u].y, (uint32_t)xv[u].z, (uint32_t)xv[u].w};
+                const float wv[8] = {w0[u].x, w0[u].y, w0[u].z, w0[u].w, w1[u].x, w1[u].y, w1[u].z, w1[u].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a[i] = fma((double)bf16_to_f32(xw[i] & 0xffffu), (double)wv[2 * i], a[i]);
+                    a[i] = fma((double)bf16_to_f32(xw[i] >> 16), (double)wv[2 * i + 1], a[i]);
+                }
+            }
+        }
     }
+    double acc = (a[0] + a[1]) + (a[2] + a[3]);
+    for (int off = 1; off < T; off <<= 1) acc += __shfl_xor(acc, off, 64);
+    if (part == 0 && ev) {
+        const float lg = (float)acc;
+        if (logits_out) logits_out[(size_t)r * E + e] = lg;
+        const double sc = 1.0 / (1.0 + exp(-(double)lg));
+        s_sc[e] = sc;
+        s_ord[e] = ordered_key(sc + (bias ? (double)bias[e] : 0.0));
+    }
+    __syncthreads();
+    if (tid < 64) topk_write_row(s_ord, s_sc, r, E, k, routed_scale, route, tid);
 }
 
 __global__ __launch_bounds__(kBucketThreads) void k_bucket(int M, int E, int k, moe_routing route, Bf16Side side,
@@ -518,6 +601,23 @@ hipError_t launch_topk_bucket(const float* partials, int splits, int sp, const f
     else
         hipLaunchKernelGGL(k_bucket, dim3(1 + extra3), dim3(kBucketThreads), 0, stream, M, E, k, route, side3,
                            stage3, H, yrec);
+    return hipGetLastError();
+}
+
+bool small_router(int M, int H, int E) { return M <= kSmallRouterRows && E <= kSmallRouterE && E * H <= 32768; }
+
+hipError_t launch_router_topk_row(const uint16_t* x, const float* w_router, const float* bias, int M, int H,
+                                  int E, int k, float routed_scale, float* logits_out, const moe_routing& route,
+                                  uint8_t* xq, uint8_t* xs, float xg4, hipStream_t stream) {
+    if (!small_router(M, H, E) || H % 32 != 0) return hipErrorInvalidValue;
+    const int nquant = xq ? (M * (H / (xg4 > 0.0f ? 16 : 32)) + 255) / 256 : 0;
+    hipLaunchKernelGGL(k_router_topk_row, dim3(M + nquant), dim3(256), 0, stream, x, w_router, bias, M, H, E, k,
+                       routed_scale, logits_out, route, xq, xs, xg4);
+    return hipGetLastError();
+}
+
+hipError_t launch_bucket(int M, int E, int k, const moe_routing& route, hipStream_t stream, int H, int2* yrec) {
+    hipLaunchKernelGGL(k_bucket_big, dim3(1), dim3(kBucketThreadsBig), 0, stream, M, E, k, route, H, yrec);
     return hipGetLastError();
 }
 

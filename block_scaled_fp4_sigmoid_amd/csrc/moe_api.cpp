@@ -599,9 +599,11 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
     const Bf16Side s2 = shb ? side(sh_gu, d->sh_in_scale, d->sh_h_scale, kBf16Swiglu) : no_side();
     const Bf16Side s3 = shb ? side(sh_dn, d->sh_h_scale, 0.0f, kBf16Down) : no_side();
     const RouterPlan p = router_plan(M, H, E);
+    const bool row_router = !shb && small_router(M, H, E);
     const bool fp4_shared = sf != MOE_FMT_NONE && !shb;
     if (M * k <= kIdsPairs) {
-        // Five launches: (router + token-order MXFP8 of x) -> top-k -> gate_up
+        // Five launches (four with a small router: router and top-k in one):
+        // (router + token-order MXFP8 of x) -> top-k -> gate_up
         // (workgroups resolve their expert from the ids, in the route step's
         // order, and gather token rows; one per slot records it) -> down
         // (slots from the record) -> finalize.  No bucket or 8-row tiles are
@@ -609,11 +611,18 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
         // static-FP8 shared expert's stages ride along the first three.  A
         // large y is written grouped (ygroup_rec): gate_up's record gives the
         // finalize each pair's row.
-        hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, L.xqt, L.xst, s1,
-                                              shb ? kBf16GateUp : kBf16None, stream, xg4);
-        if (e == hipSuccess)
-            e = launch_topk(L.route.partials, p.splits, p.sp, d->router_bias, M, E, k, d->routed_scale, logits_out, r, s2,
-                            shb ? kBf16Swiglu : kBf16None, stream);
+        // a small router and its top-k take one launch (no shared stage to carry)
+        hipError_t e;
+        if (row_router) {
+            e = launch_router_topk_row(x, d->w_router, d->router_bias, M, H, E, k, d->routed_scale, logits_out, r,
+                                       L.xqt, L.xst, xg4, stream);
+        } else {
+            e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, L.xqt, L.xst, s1,
+                                       shb ? kBf16GateUp : kBf16None, stream, xg4);
+            if (e == hipSuccess)
+                e = launch_topk(L.route.partials, p.splits, p.sp, d->router_bias, M, E, k, d->routed_scale, logits_out,
+                                r, s2, shb ? kBf16Swiglu : kBf16None, stream);
+        }
         ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
         gu.swiglu_limit = d->swiglu_limit;
         set_a4(gu, d, false, true);
@@ -646,17 +655,25 @@ int moe_layer_mxfp8_out(const moe_layer_desc* d, const uint16_t* x, const uint16
                                 out_q, out_s, stream, yg ? L.yrec : nullptr, fp4_shared && yg);
         return hip_status(e);
     }
-    // Six launches: (router + token-order MXFP8 of x) -> top-k -> route step
+    // Six launches (five with a small router): (router + token-order MXFP8
+    // of x) -> top-k -> route step
     // -> gate_up (gathers each pass's token rows through the bucket) -> down
     // -> finalize.  A large y is written grouped: the route step gives the
     // finalize each pair's row.
     const bool yg = y_grouped(M, k, H);
-    hipError_t e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, L.xqt, L.xst, s1,
-                                          shb ? kBf16GateUp : kBf16None, stream, xg4);
-    if (e == hipSuccess)
-        e = launch_topk_bucket(L.route.partials, p.splits, p.sp, d->router_bias, M, E, k, d->routed_scale, logits_out, r,
-                               s2, shb ? kBf16Swiglu : kBf16None, s3, shb ? kBf16Down : kBf16None, stream, H,
-                               yg ? L.yrec : nullptr);
+    hipError_t e;
+    if (row_router) {
+        e = launch_router_topk_row(x, d->w_router, d->router_bias, M, H, E, k, d->routed_scale, logits_out, r, L.xqt,
+                                   L.xst, xg4, stream);
+        if (e == hipSuccess) e = launch_bucket(M, E, k, r, stream, H, yg ? L.yrec : nullptr);
+    } else {
+        e = launch_router_partials(x, d->w_router, M, H, E, p, L.route.partials, L.xqt, L.xst, s1,
+                                   shb ? kBf16GateUp : kBf16None, stream, xg4);
+        if (e == hipSuccess)
+            e = launch_topk_bucket(L.route.partials, p.splits, p.sp, d->router_bias, M, E, k, d->routed_scale,
+                                   logits_out, r, s2, shb ? kBf16Swiglu : kBf16None, s3, shb ? kBf16Down : kBf16None,
+                                   stream, H, yg ? L.yrec : nullptr);
+    }
     ExpertJob gu = routed_job(d->w13, I, H, r, M, E, k);
     gu.swiglu_limit = d->swiglu_limit;
     set_a4(gu, d, false, true);

@@ -72,6 +72,16 @@ hipError_t launch_router_partials(const uint16_t* x, const float* w_router, int 
                                   const RouterPlan& plan, float* partials, uint8_t* xq, uint8_t* xs,
                                   const Bf16Side& side1, int stage1, hipStream_t stream, float xg4 = 0.0f);
 // logits: the router partials (splits of them), or given logits (splits = 1).
+// Router and top-k of each row in one workgroup, with the token-order quant
+// of x as extra workgroups, for small routers (small_router): no partials.
+constexpr int kSmallRouterE = 64;
+constexpr int kSmallRouterRows = 64;
+bool small_router(int M, int H, int E);
+hipError_t launch_router_topk_row(const uint16_t* x, const float* w_router, const float* bias, int M, int H,
+                                  int E, int k, float routed_scale, float* logits_out, const moe_routing& route,
+                                  uint8_t* xq, uint8_t* xs, float xg4, hipStream_t stream);
+// The route step alone in its launch (after the top-k ids are written).
+hipError_t launch_bucket(int M, int E, int k, const moe_routing& route, hipStream_t stream, int H, int2* yrec);
 hipError_t launch_topk(const float* partials, int splits, int sp, const float* bias, int M, int E, int k,
                        float routed_scale, float* logits_out, const moe_routing& route, const Bf16Side& side2,
                        int stage2, hipStream_t stream);

@@ -152,6 +152,11 @@ EDGE = [
     dict(M=600, H=256, E=32, k=8, I=128, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=128, bias="zipf:1.0"),
     dict(M=520, H=256, E=16, k=8, I=128, wfmt=synth.MXFP4, sfmt=synth.FP8S, I_sh=128),
     dict(M=600, H=256, E=32, k=8, I=128, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=128, act_fmt=synth.ACT_NVFP4),
+    # a small router (router and top-k in one launch, each row's workgroup reading all of W_r)
+    # followed by the route step: 600 pairs on MXFP8 activations, 640 on NVFP4 activations
+    # at the largest W_r that path takes (E * H = 32768, 64 rows)
+    dict(M=60, H=256, E=32, k=10, I=128, sfmt=synth.MXFP4, I_sh=128, bias="zipf:1.0"),
+    dict(M=64, H=512, E=64, k=10, I=128, wfmt=synth.NVFP4, sfmt=synth.NVFP4, I_sh=128, act_fmt=synth.ACT_NVFP4),
 ]
 
 
