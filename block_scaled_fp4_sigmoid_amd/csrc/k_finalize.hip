@@ -11,8 +11,10 @@
 // the one-pass quant rule applied to the bf16 out, codes [M][H] and scales
 // [M][H/32] as the activation quant lays them out.
 //
-// One workgroup per row; each thread owns 8 consecutive columns per 8192
-// (four neighbouring lanes hold one 32-value block).  y is [M*k][H] by pair,
+// One workgroup per row; each thread owns 8 consecutive columns per NT * 8
+// (four neighbouring lanes hold one 32-value block).  Up to H = 4096 a row
+// takes 512 threads, whose registers hold 16 pairs' loads at once (k <= 16 in
+// one round of loads); above, 1024 threads and rounds of 8 pairs.  y is [M*k][H] by pair,
 // or grouped as the fused layer's down writes it (pair p's row at yrec[p]:
 // its first 128-column block at yrec[p].x floats, the next ones yrec[p].y * 128
 // floats further each); y_sh likewise [M][H] or grouped (rows 0..M-1 taken as
@@ -23,10 +25,9 @@
 
 namespace moe {
 
-constexpr int kFinThreads = 1024;
-constexpr int kFinChunk = kFinThreads * 8;  // columns per pass of the workgroup
-
-__global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restrict__ y,
+// NT threads per row, KB pairs per round of loads, NC passes of NT * 8 columns
+template <int NT, int KB, int NC>
+__global__ __launch_bounds__(NT) void k_finalize(const float* __restrict__ y,
                                                           const float* __restrict__ topk_w,
                                                           const float* __restrict__ y_sh,
                                                           const uint16_t* residual,
@@ -39,8 +40,9 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restric
                                                           int M) {
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
-    constexpr int kMaxChunks = 2;  // H <= 16384
-    constexpr int kBatch = 8;      // slots whose loads are in flight together
+    constexpr int kFinChunk = NT * 8;  // columns per pass of the workgroup
+    constexpr int kMaxChunks = NC;     // H <= NC * NT * 8
+    constexpr int kBatch = KB;         // slots whose loads are in flight together
     float rv[kMaxChunks][8];
     uint32_t gw[kMaxChunks][4];
     float ss = 0.f;
@@ -116,12 +118,12 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const float* __restric
     }
     // fixed-order reduction: wave butterfly, then the wave sums in order
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-    __shared__ float s_part[kFinThreads / 64];
+    __shared__ float s_part[NT / 64];
     if ((tid & 63) == 0) s_part[tid >> 6] = ss;
     __syncthreads();
     float tot = 0.f;
 #pragma unroll
-    for (int w = 0; w < kFinThreads / 64; ++w) tot += s_part[w];
+    for (int w = 0; w < NT / 64; ++w) tot += s_part[w];
     const float inv = rsqrtf(tot / (float)H + eps);
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
@@ -150,8 +152,12 @@ hipError_t launch_finalize(const float* y, const float* topk_w, const float* y_s
                            const uint16_t* residual, const uint16_t* gamma, float eps, int M,
                            int H, int k, uint16_t* out, uint16_t* residual_out, uint8_t* out_q,
                            uint8_t* out_s, hipStream_t stream, const int2* yrec, bool ysh_grouped) {
-    hipLaunchKernelGGL(k_finalize, dim3(M), dim3(kFinThreads), 0, stream, y, topk_w, y_sh,
-                       residual, gamma, eps, H, k, out, residual_out, out_q, out_s, yrec, ysh_grouped ? 1 : 0, M);
+    if (H <= 512 * 8)
+        hipLaunchKernelGGL((k_finalize<512, 16, 1>), dim3(M), dim3(512), 0, stream, y, topk_w, y_sh, residual, gamma,
+                           eps, H, k, out, residual_out, out_q, out_s, yrec, ysh_grouped ? 1 : 0, M);
+    else
+        hipLaunchKernelGGL((k_finalize<1024, 8, 2>), dim3(M), dim3(1024), 0, stream, y, topk_w, y_sh, residual, gamma,
+                           eps, H, k, out, residual_out, out_q, out_s, yrec, ysh_grouped ? 1 : 0, M);
     return hipGetLastError();
 }
 
