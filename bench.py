@@ -266,9 +266,15 @@ def _read_keys(path):
     return vals
 
 
+def unique_path(workload):
+    """Where a counter run leaves the unique-expert count of its input for the
+    summary step that follows it (the in-tree build folder)."""
+    return os.path.join(ROOT, "_build", f"unique_{workload}.txt")
+
+
 def stored_unique(workload):
     """Unique experts of the workload's default input (written by --profile-kernels)."""
-    v = _read_keys(os.path.join(ROOT, "gpurun_out", f"unique_{workload}.txt")).get("unique_experts")
+    v = _read_keys(unique_path(workload)).get("unique_experts")
     return int(v) if v else None
 
 
@@ -624,8 +630,8 @@ def profile_kernels(name, seed, n, copies_arg):
     for i in range(n):
         alone.down(cw[i % copies][1])
     torch.cuda.synchronize()
-    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
-    with open(os.path.join(ROOT, "gpurun_out", f"unique_{name}.txt"), "w") as fh:
+    os.makedirs(os.path.dirname(unique_path(name)), exist_ok=True)
+    with open(unique_path(name), "w") as fh:
         fh.write(f"unique_experts: {alone.U}\n")
     log(f"[bench] {name}: routed gate_up and down launched {n} times each ({copies} weight copies, U={alone.U})")
 
