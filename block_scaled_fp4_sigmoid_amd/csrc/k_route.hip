@@ -436,6 +436,44 @@ __device__ __forceinline__ void topk_write_row(const uint64_t* s_ord, const doub
     }
 }
 
+// The partial logits of expert e of row r, all in one round of loads
+// (splits <= 32): 16-byte loads in the expert-contiguous layout (sp > 0), else
+// split-major.
+__device__ __forceinline__ void load_partials(const float* __restrict__ partials, int splits, int sp, int M, int E,
+                                              int r, int e, float (&p)[32]) {
+    if (sp) {
+        const float* pe = partials + ((size_t)r * E + e) * sp;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float4 v = 4 * q < splits ? *reinterpret_cast<const float4*>(pe + 4 * q) : float4{0.f, 0.f, 0.f, 0.f};
+            p[4 * q] = v.x;
+            p[4 * q + 1] = v.y;
+            p[4 * q + 2] = v.z;
+            p[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < 32; ++u) p[u] = u < splits ? partials[((size_t)u * M + r) * E + e] : 0.f;
+    }
+}
+
+// The logit (partials summed in chunk order), its fp64 score and key into LDS.
+__device__ __forceinline__ void score_expert(const float (&p)[32], int splits, const float* __restrict__ bias,
+                                             float* __restrict__ logits_out, int r, int E, int e, uint64_t* s_ord,
+                                             double* s_sc) {
+    float lg = p[0];
+#pragma unroll
+    for (int u = 1; u < 32; ++u)
+        if (u < splits) lg = lg + p[u];
+    if (logits_out) logits_out[(size_t)r * E + e] = lg;
+    const double sc = 1.0 / (1.0 + exp(-(double)lg));
+    s_sc[e] = sc;
+    s_ord[e] = ordered_key(sc + (bias ? (double)bias[e] : 0.0));
+}
+
+// NE experts per thread and pass: 2 above 256 experts, so their partials
+// arrive in one round of loads instead of one round per pass.
+template <int NE>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials, int splits, int sp,
                                               const float* __restrict__ bias, int M, int E, int k,
                                               float routed_scale, float* __restrict__ logits_out,
@@ -452,33 +490,14 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ partials
     __shared__ double s_sc[kMaxE];
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += 256) {
-        // all partials of the expert in one round of loads (splits <= 32):
-        // 16-byte loads in the expert-contiguous layout; summed in chunk order
-        float p[32];
-        if (sp) {
-            const float* pe = partials + ((size_t)r * E + e) * sp;
+    for (int e = tid; e < E; e += 256 * NE) {
+        float p[NE][32];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const float4 v =
-                    4 * q < splits ? *reinterpret_cast<const float4*>(pe + 4 * q) : float4{0.f, 0.f, 0.f, 0.f};
-                p[4 * q] = v.x;
-                p[4 * q + 1] = v.y;
-                p[4 * q + 2] = v.z;
-                p[4 * q + 3] = v.w;
-            }
-        } else {
+        for (int n = 0; n < NE; ++n)
+            if (e + 256 * n < E) load_partials(partials, splits, sp, M, E, r, e + 256 * n, p[n]);
 #pragma unroll
-            for (int u = 0; u < 32; ++u) p[u] = u < splits ? partials[((size_t)u * M + r) * E + e] : 0.f;
-        }
-        float lg = p[0];
-#pragma unroll
-        for (int u = 1; u < 32; ++u)
-            if (u < splits) lg = lg + p[u];
-        if (logits_out) logits_out[(size_t)r * E + e] = lg;
-        const double sc = 1.0 / (1.0 + exp(-(double)lg));
-        s_sc[e] = sc;
-        s_ord[e] = ordered_key(sc + (bias ? (double)bias[e] : 0.0));
+        for (int n = 0; n < NE; ++n)
+            if (e + 256 * n < E) score_expert(p[n], splits, bias, logits_out, r, E, e + 256 * n, s_ord, s_sc);
     }
     __syncthreads();
     if (tid < 64) topk_write_row(s_ord, s_sc, r, E, k, routed_scale, route, tid);
@@ -583,8 +602,12 @@ hipError_t launch_topk(const float* partials, int splits, int sp, const float* b
                        float routed_scale, float* logits_out, const moe_routing& route, const Bf16Side& side2,
                        int stage2, hipStream_t stream) {
     const int extra2 = stage2 == kBf16None ? 0 : side2.blocks;
-    hipLaunchKernelGGL(k_topk, dim3(M + extra2), dim3(256), 0, stream, partials, splits, sp, bias,
-                       M, E, k, routed_scale, logits_out, route, side2, stage2);
+    if (E > 256)
+        hipLaunchKernelGGL(k_topk<2>, dim3(M + extra2), dim3(256), 0, stream, partials, splits, sp, bias, M, E, k,
+                           routed_scale, logits_out, route, side2, stage2);
+    else
+        hipLaunchKernelGGL(k_topk<1>, dim3(M + extra2), dim3(256), 0, stream, partials, splits, sp, bias, M, E, k,
+                           routed_scale, logits_out, route, side2, stage2);
     return hipGetLastError();
 }
 
