@@ -187,9 +187,18 @@ def _small_layer(seed=3, a4=False):
     return inp, staging.to_device(inp, DEV)
 
 
-@pytest.mark.parametrize("a4", [False, True])
-def test_repeated_launches_bitwise_identical(a4):
-    inp, d = _small_layer(a4=a4)
+def _router_layer(seed):
+    """A router too large for one workgroup per row (partial logits, then the
+    top-k launch), with the bf16 shared expert's stages riding those launches."""
+    sh = synth.custom_shape(M=24, H=1024, E=128, k=6, I=256, wfmt=synth.NVFP4, sfmt=synth.BF16, I_sh=256,
+                            bias="zipf:1.2")
+    inp = synth.make_inputs(sh, seed=seed, pool_rows=2048)
+    return inp, staging.to_device(inp, DEV)
+
+
+@pytest.mark.parametrize("case", ["mx", "a4", "router"])
+def test_repeated_launches_bitwise_identical(case):
+    inp, d = _router_layer(seed=3) if case == "router" else _small_layer(a4=case == "a4")
     first = LayerRun(d)
     ref = first.host()
     for i in range(400):
@@ -218,9 +227,9 @@ def test_row_permutation_invariance():
         assert np.array_equal(run["ids"], base["ids"][perm])
 
 
-@pytest.mark.parametrize("a4", [False, True])
-def test_graph_replay_equals_eager(a4):
-    inp, d = _small_layer(seed=5, a4=a4)
+@pytest.mark.parametrize("case", ["mx", "a4", "router"])
+def test_graph_replay_equals_eager(case):
+    inp, d = _router_layer(seed=5) if case == "router" else _small_layer(seed=5, a4=case == "a4")
     run = LayerRun(d)
     eager = run.host()
     s = torch.cuda.Stream()
